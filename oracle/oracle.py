@@ -1,0 +1,273 @@
+"""ctypes front end of the CPU oracle (iq_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the bench's
+cpu_baseline leg.  The GPU library never imports or calls it.
+
+Arrays are numpy: inputs as float32 or uint16 (BF16 bits); codes uint8;
+scales float32 (per-tensor / per-row), uint8 (E8M0 / E4M3 block codes) or
+uint16 (FP16 group scales).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "iq_oracle.c")
+_LIB = os.path.join(_HERE, "libiq_oracle.so")
+
+FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5}
+GRANS = {"tensor": 0, "row": 1, "block": 2}
+F32, BF16 = 0, 1
+K_E4M3, K_E5M2, K_E2M1, K_F16 = 0, 1, 2, 3
+FLAG_MX_ROUND_NEAREST, FLAG_MX_ROUND_UP, FLAG_NV_SCALE_RNE = 1, 2, 4
+QMAX = {"int8": 127.0, "e4m3": 448.0, "e5m2": 57344.0, "mxfp4": 6.0, "nvfp4": 6.0, "int4": 7.0}
+
+
+def build() -> str:
+    """Compile libiq_oracle.so with gcc (always recompiles)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+           "-fno-fast-math", "-frounding-math", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("gran", ctypes.c_int), ("in_dtype", ctypes.c_int),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64),
+                ("flags", ctypes.c_uint32)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("n_zero_flush", ctypes.c_uint64),
+                ("n_saturated", ctypes.c_uint64), ("n_nonfinite", ctypes.c_uint64),
+                ("sum_x2", ctypes.c_double), ("sum_err2", ctypes.c_double),
+                ("sum_abs_err", ctypes.c_double), ("max_abs_err", ctypes.c_float),
+                ("reserved", ctypes.c_uint32)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, I64, F, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_uint32
+        sig = {
+            "iqo_bf16_to_f32": (F, [ctypes.c_uint16]),
+            "iqo_f32_to_bf16": (ctypes.c_uint16, [F]),
+            "iqo_fp_encode": (U32, [ctypes.c_int, F]),
+            "iqo_fp_decode": (F, [ctypes.c_int, U32]),
+            "iqo_int_encode": (ctypes.c_int, [F, ctypes.c_int]),
+            "iqo_e8m0_code": (ctypes.c_uint8, [F, U32]),
+            "iqo_e8m0_value": (F, [ctypes.c_uint8]),
+            "iqo_e4m3_ceil": (ctypes.c_uint8, [F]),
+            "iqo_fp_encode_n": (None, [ctypes.c_int, P, P, I64]),
+            "iqo_fp_decode_n": (None, [ctypes.c_int, P, P, I64]),
+            "iqo_int_encode_n": (None, [P, P, I64, ctypes.c_int]),
+            "iqo_block_size": (I64, [ctypes.c_int, ctypes.c_int]),
+            "iqo_check": (ctypes.c_int, [ctypes.POINTER(Desc)]),
+            "iqo_amax": (F, [ctypes.POINTER(Desc), P]),
+            "iqo_quantize_rows": (ctypes.c_int, [ctypes.POINTER(Desc), P, I64, I64, F, P, P, P, P,
+                                                 ctypes.POINTER(Stats)]),
+            "iqo_quantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, P, ctypes.POINTER(Stats)]),
+            "iqo_dequantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+# ---- scalar codecs ---------------------------------------------------------
+def fp_encode(kind: int, v: float) -> int:
+    return int(_load().iqo_fp_encode(kind, float(v)))
+
+
+def fp_decode(kind: int, code: int) -> float:
+    return float(_load().iqo_fp_decode(kind, int(code)))
+
+
+def fp_encode_array(kind: int, v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint32)
+    _load().iqo_fp_encode_n(kind, v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def fp_decode_array(kind: int, codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint32)
+    out = np.empty(c.shape, dtype=np.float32)
+    _load().iqo_fp_decode_n(kind, c.ctypes.data, out.ctypes.data, c.size)
+    return out
+
+
+def int_encode_array(v, qmax: int) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.int32)
+    _load().iqo_int_encode_n(v.ctypes.data, out.ctypes.data, v.size, int(qmax))
+    return out
+
+
+def int_encode(v: float, qmax: int) -> int:
+    return int(_load().iqo_int_encode(float(v), int(qmax)))
+
+
+def e8m0_code(A: float, flags: int = 0) -> int:
+    return int(_load().iqo_e8m0_code(float(A), int(flags)))
+
+
+def e8m0_value(code: int) -> float:
+    return float(_load().iqo_e8m0_value(int(code)))
+
+
+def e4m3_ceil(t: float) -> int:
+    return int(_load().iqo_e4m3_ceil(float(t)))
+
+
+def bf16_to_f32(b: int) -> float:
+    return float(_load().iqo_bf16_to_f32(int(b)))
+
+
+def f32_to_bf16(f: float) -> int:
+    return int(_load().iqo_f32_to_bf16(float(f)))
+
+
+def block_size(fmt: str, gran: str) -> int:
+    return int(_load().iqo_block_size(FORMATS[fmt], GRANS[gran]))
+
+
+# ---- layouts ---------------------------------------------------------------
+def codes_shape(fmt: str, rows: int, cols: int) -> tuple:
+    return (rows, cols // 2) if fmt in ("mxfp4", "nvfp4", "int4") else (rows, cols)
+
+
+def scales_spec(fmt: str, gran: str, rows: int, cols: int) -> tuple:
+    """(shape, numpy dtype) of the scales array."""
+    if fmt in ("int8", "e4m3", "e5m2"):
+        return ((1,) if gran == "tensor" else (rows,)), np.float32
+    if fmt == "mxfp4":
+        return (rows, cols // 32), np.uint8
+    if fmt == "nvfp4":
+        return (rows, cols // 16), np.uint8
+    return (rows, cols // 128), np.uint16
+
+
+def _desc(fmt, gran, x, cols=None, flags=0):
+    rows, ld = x.shape
+    cols = ld if cols is None else cols
+    in_dtype = F32 if x.dtype == np.float32 else BF16
+    if x.dtype not in (np.float32, np.uint16) or not x.flags.c_contiguous:
+        raise TypeError("x must be a C-contiguous float32 or uint16 (BF16) array")
+    d = Desc(FORMATS[fmt], GRANS[gran], in_dtype, rows, cols, ld, flags)
+    if _load().iqo_check(ctypes.byref(d)):
+        raise ValueError(f"illegal descriptor {fmt}/{gran} rows={rows} cols={cols} ld={ld}")
+    return d
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def amax(x: np.ndarray, cols: int | None = None, fmt: str = "e4m3", gran: str = "tensor") -> float:
+    d = _desc(fmt, gran, x, cols)
+    return float(_load().iqo_amax(ctypes.byref(d), _p(x)))
+
+
+def quantize(x: np.ndarray, fmt: str, gran: str, cols: int | None = None, flags: int = 0,
+             want_xhat: bool = True, threads: int = 1) -> dict:
+    """Quantize a whole [rows, ld] array; returns codes, scales, global_scale, xhat, stats.
+
+    threads > 1 splits rows across threads (the oracle itself is serial per
+    row range; ctypes releases the GIL).  Codes, scales and x^ do not depend
+    on the split; the double-precision sums may differ in the last bits.
+    """
+    d = _desc(fmt, gran, x, cols, flags)
+    rows, c = d.rows, d.cols
+    codes = np.zeros(codes_shape(fmt, rows, c), dtype=np.uint8)
+    sshape, sdt = scales_spec(fmt, gran, rows, c)
+    scales = np.zeros(sshape, dtype=sdt)
+    g = np.zeros(1, dtype=np.float32)
+    xhat = np.zeros((rows, c), dtype=np.float32) if want_xhat else None
+    L = _load()
+    tensor_amax = 0.0
+    if gran == "tensor" or fmt == "nvfp4":
+        tensor_amax = L.iqo_amax(ctypes.byref(d), _p(x))
+    parts = _split(rows, threads)
+    stats = [Stats() for _ in parts]
+
+    def run(i):
+        r0, r1 = parts[i]
+        rc = L.iqo_quantize_rows(ctypes.byref(d), _p(x), r0, r1, tensor_amax, _p(codes), _p(scales),
+                                 _p(g), _p(xhat), ctypes.byref(stats[i]))
+        if rc:
+            raise RuntimeError("iqo_quantize_rows failed")
+
+    if len(parts) == 1:
+        run(0)
+    else:
+        with ThreadPoolExecutor(len(parts)) as ex:
+            list(ex.map(run, range(len(parts))))
+    st = merge_stats([s.as_dict() for s in stats])
+    return {"codes": codes, "scales": scales, "global_scale": g, "xhat": xhat, "stats": st,
+            "tensor_amax": tensor_amax}
+
+
+def quantize_rows(x: np.ndarray, fmt: str, gran: str, row0: int, nrows: int, tensor_amax: float,
+                  cols: int | None = None, flags: int = 0) -> dict:
+    """Quantize only rows [row0, row0+nrows) of x, given the tensor absmax
+    (used by per-tensor formats and NVFP4).  x holds just those rows."""
+    d = _desc(fmt, gran, x, cols, flags)
+    rows, c = d.rows, d.cols
+    codes = np.zeros(codes_shape(fmt, rows, c), dtype=np.uint8)
+    sshape, sdt = scales_spec(fmt, gran, rows, c)
+    scales = np.zeros(sshape, dtype=sdt)
+    g = np.zeros(1, dtype=np.float32)
+    xhat = np.zeros((rows, c), dtype=np.float32)
+    st = Stats()
+    rc = _load().iqo_quantize_rows(ctypes.byref(d), _p(x), 0, rows, float(tensor_amax), _p(codes),
+                                   _p(scales), _p(g), _p(xhat), ctypes.byref(st))
+    if rc:
+        raise RuntimeError("iqo_quantize_rows failed")
+    return {"codes": codes, "scales": scales, "global_scale": g, "xhat": xhat, "stats": st.as_dict()}
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, gran: str, rows: int, cols: int,
+               global_scale: np.ndarray | None = None, out_dtype: int = F32) -> np.ndarray:
+    d = Desc(FORMATS[fmt], GRANS[gran], F32, rows, cols, cols, 0)
+    if _load().iqo_check(ctypes.byref(d)):
+        raise ValueError("illegal descriptor")
+    out = np.zeros((rows, cols), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    g = None if global_scale is None else np.ascontiguousarray(global_scale, dtype=np.float32)
+    rc = _load().iqo_dequantize(ctypes.byref(d), _p(np.ascontiguousarray(codes)),
+                                _p(np.ascontiguousarray(scales)), _p(g), _p(out), out_dtype)
+    if rc:
+        raise RuntimeError("iqo_dequantize failed")
+    return out
+
+
+def merge_stats(parts: list) -> dict:
+    out = {"n": 0, "n_zero_flush": 0, "n_saturated": 0, "n_nonfinite": 0, "sum_x2": 0.0,
+           "sum_err2": 0.0, "sum_abs_err": 0.0, "max_abs_err": 0.0}
+    for p in parts:
+        for k in ("n", "n_zero_flush", "n_saturated", "n_nonfinite", "sum_x2", "sum_err2", "sum_abs_err"):
+            out[k] += p[k]
+        out["max_abs_err"] = max(out["max_abs_err"], p["max_abs_err"])
+    return out
+
+
+def _split(rows: int, threads: int) -> list:
+    threads = max(1, min(threads, rows)) if rows else 1
+    return [(rows * t // threads, rows * (t + 1) // threads) for t in range(threads)]

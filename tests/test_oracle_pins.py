@@ -1,0 +1,529 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Every test here checks the oracle (oracle/iq_oracle.c) against something other
+than its own formulas: values printed on the pages (tests/golden/), closed-form
+error bounds, library routines (torch float8 casts, numpy float16 / rint,
+struct), and brute-force nearest-code search over tiny code tables.
+
+Pages: Lorn blog, post "浅谈低精度浮点数" (sections "IEEE 754 标准浮点数",
+"FP8", "FP4 / MXFP4 / NVFP4"), and post "Triton" (Puzzle 12, extract()).
+"""
+import math
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden_map, read_golden
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def bits_f32(u: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", u))[0]
+
+
+# ---- independent code tables ------------------------------------------------
+def torch_fp8_table(dtype) -> np.ndarray:
+    """Decode of all 256 FP8 codes by torch's float8 dtypes (library routine)."""
+    return torch.arange(256, dtype=torch.uint8).view(dtype).float().numpy()
+
+
+def e2m1_table() -> np.ndarray:
+    """The 16 E2M1 values from the page's printed value set (sign in bit 3)."""
+    pos = np.array([float(v) for v in read_golden("e2m1_values.txt")[0]], dtype=np.float32)
+    return np.concatenate([pos, -pos]).astype(np.float32)
+
+
+def brute_nearest(v: np.ndarray, table: np.ndarray, sign_bit: int, nan_code: int) -> np.ndarray:
+    """Nearest finite code by exhaustive scan, ties to the even code, sign kept,
+    saturating beyond the largest finite magnitude.  Independent of the oracle."""
+    v = np.asarray(v, dtype=np.float64)
+    mags = table[:sign_bit].astype(np.float64)
+    finite = np.nonzero(np.isfinite(mags))[0]
+    vals = mags[finite]
+    a = np.abs(v)
+    out = np.zeros(v.shape, dtype=np.int64)
+    for i in range(v.size):
+        ai = a.flat[i]
+        if np.isnan(ai):
+            out.flat[i] = nan_code
+            continue
+        if ai >= vals.max():
+            c = finite[np.argmax(vals)]
+        else:
+            d = np.abs(vals - ai)
+            best = np.nonzero(d == d.min())[0]
+            cands = finite[best]
+            c = cands[0] if len(cands) == 1 else [k for k in cands if k % 2 == 0][0]
+        out.flat[i] = c | (sign_bit if np.signbit(v.flat[i]) else 0)
+    return out
+
+
+# ---- P1: the 25.125 worked example ------------------------------------------
+def test_p1_worked_example_fields(O):
+    g = golden_map("fp32_worked_example.txt")
+    val = float(g["value"][0])
+    word = int(g["word"][0], 16)
+    assert f32_bits(val) == word
+    assert (word >> 31) == int(g["sign"][0])
+    assert ((word >> 23) & 0xFF) == int(g["exponent_field"][0])
+    assert format(word & 0x7FFFFF, "023b") == g["fraction_bits"][0]
+    # BF16 is the top half of the word: widening and narrowing are exact here.
+    assert O.bf16_to_f32(word >> 16) == val
+    assert O.f32_to_bf16(val) == word >> 16
+    # The MX exponent is floor(log2 A): 25.125 lies in [2^4, 2^5).
+    assert O.e8m0_code(val) == int(g["exponent_unbiased"][0]) - 2 + 127
+
+
+def test_p2_fp32_limits(O):
+    g = golden_map("fp32_limits.txt")
+    vmax, wmax = float(g["max_finite"][0]), int(g["max_finite"][1], 16)
+    vmin, wmin = float(g["min_normal"][0]), int(g["min_normal"][1], 16)
+    assert bits_f32(wmax) == pytest.approx(vmax, rel=1e-7)
+    assert bits_f32(wmin) == pytest.approx(vmin, rel=1e-7)
+    emax, emin = int(g["exponent_max"][0]), int(g["exponent_min"][0])
+    assert O.e8m0_code(bits_f32(wmax)) == emax - 2 + 127
+    assert O.e8m0_code(bits_f32(wmin)) == max(0, emin - 2 + 127)
+    assert O.e8m0_code(2.0 ** -124) == 1
+    assert O.bf16_to_f32(wmax >> 16) == bits_f32(wmax & 0xFFFF0000)
+
+
+# ---- P3, P4, P5: printed value sets and constants ----------------------------
+def test_p3_e2m1_value_set(O):
+    tab = e2m1_table()
+    got = O.fp_decode_array(O.K_E2M1, np.arange(16))
+    assert np.array_equal(got, tab)
+    assert np.array_equal(np.signbit(got), np.arange(16) >= 8)
+
+
+def test_p4_constants(O):
+    g = golden_map("format_constants.txt")
+    e4m3 = O.fp_decode_array(O.K_E4M3, np.arange(256))
+    assert O.fp_decode(O.K_E4M3, 0x7E) == float(g["e4m3_max"][0])
+    assert np.nanmax(e4m3) == float(g["e4m3_max"][0])
+    assert O.fp_decode(O.K_E2M1, 0x7) == float(g["e2m1_max"][0])
+    assert float(g["e2m1_max"][0]) * float(g["e4m3_max"][0]) == float(g["nvfp4_global_divisor"][0])
+    # the NVFP4 global scale is the tensor absmax over 6*448
+    for G in (2688.0, 448.0, 1000.0):
+        x = np.full((1, 16), 0.5, dtype=np.float32)
+        x[0, 3] = -G
+        r = O.quantize(x, "nvfp4", "block")
+        assert r["global_scale"][0] == np.float32(G) / np.float32(2688.0)
+    assert O.block_size("mxfp4", "block") == int(g["mxfp4_block"][0])
+    assert O.block_size("nvfp4", "block") == int(g["nvfp4_block"][0])
+
+
+def test_p5_samples_per_binade(O):
+    g = golden_map("format_constants.txt")
+    for kind, key in ((O.K_E5M2, "e5m2_values_in_2_4"), (O.K_E4M3, "e4m3_values_in_2_4")):
+        v = O.fp_decode_array(kind, np.arange(128))
+        assert len({float(t) for t in v if 2.0 <= t < 4.0}) == int(g[key][0])
+
+
+# ---- P12: exhaustive code tables and brute force -------------------------------
+FP8 = [("e4m3", 0, torch.float8_e4m3fn, 448.0, 3), ("e5m2", 1, torch.float8_e5m2, 57344.0, 2)]
+
+
+@pytest.mark.parametrize("name,kind,tdt,fmax,mbits", FP8)
+def test_p12_fp8_decode_matches_torch(O, name, kind, tdt, fmax, mbits):
+    ref = torch_fp8_table(tdt)
+    got = O.fp_decode_array(kind, np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+@pytest.mark.parametrize("name,kind,tdt,fmax,mbits", FP8)
+def test_p12_fp8_roundtrip_midpoints_saturation(O, name, kind, tdt, fmax, mbits):
+    ref = torch_fp8_table(tdt)
+    codes = np.arange(256)
+    finite = np.isfinite(ref)
+    # decode -> encode is the identity on every finite code (also -0 -> 0x80)
+    enc = O.fp_encode_array(kind, ref[finite])
+    assert np.array_equal(enc, codes[finite])
+    # midpoints between adjacent positive values go to the even code;
+    # one FP32 ulp either side goes to the nearer code
+    pos = sorted((float(ref[c]), c) for c in range(128) if np.isfinite(ref[c]))
+    for (a, ca), (b, cb) in zip(pos, pos[1:]):
+        m = np.float32((a + b) / 2)
+        assert float(m) == (a + b) / 2
+        even = ca if ca % 2 == 0 else cb
+        assert O.fp_encode(kind, m) == even
+        assert O.fp_encode(kind, -m) == even | 0x80
+        assert O.fp_encode(kind, np.nextafter(m, np.float32(np.inf))) == cb
+        assert O.fp_encode(kind, np.nextafter(m, np.float32(0))) == ca
+    # saturation beyond the largest finite value
+    maxc = int(codes[finite & (ref == fmax)][0])
+    for v in (fmax * 1.01, fmax * 1.0625, fmax * 1.2, 1e30, float("inf")):
+        assert O.fp_encode(kind, v) == maxc
+        assert O.fp_encode(kind, -v) == maxc | 0x80
+
+
+@pytest.mark.parametrize("name,kind,tdt,fmax,mbits", FP8)
+def test_p12_fp8_bruteforce_random(O, name, kind, tdt, fmax, mbits):
+    rng = np.random.default_rng(12)
+    ref = torch_fp8_table(tdt)
+    # random magnitudes over the whole format range plus subnormals and beyond max
+    e = rng.uniform(-20 if kind == 0 else -19, math.log2(fmax) + 2, 20000)
+    v = (np.exp2(e) * rng.choice([-1, 1], e.size)).astype(np.float32)
+    got = O.fp_encode_array(kind, v)
+    want = brute_nearest(v, ref, 0x80, 0x7F)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("name,kind,tdt,fmax,mbits", FP8)
+def test_p12_fp8_matches_torch_cast_in_range(O, name, kind, tdt, fmax, mbits):
+    """Third opinion: torch's float8 casts round to nearest even inside the
+    finite range (they do not saturate, so only |v| <= max is compared)."""
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(1_000_000) * rng.choice([1e-4, 1e-2, 1, 30, fmax / 4], 1_000_000)).astype(np.float32)
+    v = v[np.abs(v) <= fmax]
+    t = torch.from_numpy(v).to(tdt).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp_encode_array(kind, v), t.astype(np.uint32))
+
+
+def test_p12_e2m1_exhaustive(O):
+    tab = e2m1_table()
+    assert np.array_equal(O.fp_encode_array(O.K_E2M1, tab), np.arange(16))
+    pos = sorted((float(tab[c]), c) for c in range(8))
+    for (a, ca), (b, cb) in zip(pos, pos[1:]):
+        m = np.float32((a + b) / 2)
+        even = ca if ca % 2 == 0 else cb
+        assert O.fp_encode(O.K_E2M1, m) == even
+        assert O.fp_encode(O.K_E2M1, np.nextafter(m, np.float32(np.inf))) == cb
+        assert O.fp_encode(O.K_E2M1, np.nextafter(m, np.float32(0))) == ca
+    for v in (6.5, 7.0, 100.0, float("inf")):
+        assert O.fp_encode(O.K_E2M1, v) == 0x7
+        assert O.fp_encode(O.K_E2M1, -v) == 0xF
+    rng = np.random.default_rng(3)
+    v = (rng.uniform(-8, 8, 20000)).astype(np.float32)
+    assert np.array_equal(O.fp_encode_array(O.K_E2M1, v), brute_nearest(v, tab, 0x8, 0))
+
+
+def test_p12_e8m0_values(O):
+    for c in range(255):
+        assert O.e8m0_value(c) == math.ldexp(1.0, c - 127)
+    assert math.isnan(O.e8m0_value(255))
+
+
+def test_p12_f16_scale_matches_numpy(O):
+    """The INT4 group scale is FP16 by round to nearest even (numpy's cast),
+    saturated at 65504 instead of overflowing."""
+    rng = np.random.default_rng(5)
+    v = np.exp2(rng.uniform(-27, 17, 200000)).astype(np.float32)
+    got = O.fp_encode_array(O.K_F16, v)
+    want = v.astype(np.float16).view(np.uint16).astype(np.uint32)
+    big = v > 65504
+    want[big] = 0x7BFF
+    assert np.array_equal(got, want)
+    h = np.arange(0x7C00, dtype=np.uint16)
+    assert np.array_equal(O.fp_decode_array(O.K_F16, h), h.view(np.float16).astype(np.float32))
+
+
+# ---- P13: textbook reductions -------------------------------------------------
+def test_p13_int_path_is_rint_and_clip(O):
+    rng = np.random.default_rng(9)
+    v = np.concatenate([rng.uniform(-200, 200, 100000), np.arange(-140, 140) + 0.5,
+                        np.arange(-140, 140, dtype=np.float64)]).astype(np.float32)
+    for qmax in (127, 7):
+        want = np.clip(np.rint(v.astype(np.float64)), -qmax, qmax).astype(np.int32)
+        assert np.array_equal(O.int_encode_array(v, qmax), want)
+    assert O.int_encode(float("nan"), 127) == 0
+
+
+def test_p13_mx_scale_is_exponent_field(O):
+    rng = np.random.default_rng(11)
+    bits = rng.integers(1, 0x7F800000, 200000, dtype=np.uint32)
+    A = bits.view(np.float32)
+    for a, b in zip(A[:50000], bits[:50000]):
+        field = int(b) >> 23
+        e = field - 127 if field else (int(b) & 0x7FFFFF).bit_length() - 1 - 149
+        assert O.e8m0_code(float(a)) == min(254, max(0, e - 2 + 127))
+    assert O.e8m0_code(0.0) == 0
+
+
+def test_p13_e5m2_is_rounded_fp16(O):
+    """E5M2 has FP16's exponent layout, so encoding an FP16 value equals
+    rounding its bit pattern to the top byte, ties to even."""
+    h = np.arange(0x0400, 0x7C00, dtype=np.uint32)          # positive normal FP16
+    vals = h.astype(np.uint16).view(np.float16).astype(np.float32)
+    keep = vals <= 57344
+    h, vals = h[keep], vals[keep]
+    low = h & 0xFF
+    up = h >> 8
+    want = up + ((low > 0x80) | ((low == 0x80) & (up & 1) == 1))
+    assert np.array_equal(O.fp_encode_array(O.K_E5M2, vals), want)
+    assert np.array_equal(O.fp_encode_array(O.K_E5M2, -vals), want | 0x80)
+
+
+# ---- P6, P7, P8: error bounds of the FP8 section -------------------------------
+def test_p6_int8_bound(O, S):
+    x = S.make("c1")
+    r = O.quantize(x, "int8", "tensor")
+    alpha = float(np.max(np.abs(x)))
+    s = float(r["scales"][0])
+    assert s == float(np.float32(alpha) / np.float32(127.0))
+    x64 = x.astype(np.float64)
+    err = np.abs(x64 - r["xhat"].astype(np.float64))
+    g = golden_map("error_bounds.txt")
+    assert err.max() <= s / 2 * (1 + 2 ** -20)
+    assert err.max() <= alpha * float(g["int8_abs_err_over_alpha"][0]) * (1 + 2 ** -20)
+    q = r["codes"].view(np.int8).astype(np.float64)
+    assert np.abs(x64 / s - q).max() <= 0.5 + 1e-6
+
+
+@pytest.mark.parametrize("fmt,fmax,mbits,key", [("e4m3", 448.0, 3, "e4m3_rel_err"),
+                                                 ("e5m2", 57344.0, 2, "e5m2_rel_err")])
+def test_p7_fp8_relative_bound(O, fmt, fmax, mbits, key):
+    """Every BF16 value in the format's normal range, quantized with s = 1
+    (alpha = FMAX), has relative error below 2^-(M+1)."""
+    bound = float(golden_map("error_bounds.txt")[key][0])
+    assert bound == 2.0 ** -(mbits + 1)
+    bits = np.arange(0x0000, 0x7F80, dtype=np.uint16)
+    v = (bits.astype(np.uint32) << 16).view(np.float32)
+    min_normal = 2.0 ** -6 if fmt == "e4m3" else 2.0 ** -14
+    v = v[(v >= min_normal) & (v <= fmax)]
+    x = np.concatenate([v, -v, [fmax]]).astype(np.float32)[None, :]
+    cols = x.shape[1] - x.shape[1] % 16
+    x = np.ascontiguousarray(x[:, :cols])
+    x[0, 0] = fmax
+    r = O.quantize(x, fmt, "tensor")
+    assert r["scales"][0] == 1.0
+    # |v| == FMAX is on the grid: represented exactly, so not counted as saturated
+    assert r["stats"]["n_saturated"] == 0
+    rel = np.abs(x - r["xhat"]).astype(np.float64) / np.abs(x).astype(np.float64)
+    assert rel.max() < bound
+    assert rel.max() > 0.9 * bound / (1 + bound)
+
+
+def test_p8_int8_fp8_crossover(O, S):
+    """Binned by |x|/alpha, the worst relative error of per-tensor INT8 falls
+    below per-tensor E4M3's near |x| ~ 0.063 alpha and not far from it."""
+    x = S.make("c1")
+    alpha = float(np.max(np.abs(x)))
+    xi = O.quantize(x, "int8", "tensor")["xhat"]
+    xf = O.quantize(x, "e4m3", "tensor")["xhat"]
+    ax = np.abs(x.astype(np.float64))
+    nz = ax > 0
+    rel_i = np.abs(x - xi)[nz] / ax[nz]
+    rel_f = np.abs(x - xf)[nz] / ax[nz]
+    ratio = ax[nz] / alpha
+    edges = np.exp2(np.arange(-7.0, 0.01, 0.125))
+    worse = []
+    for lo, hi in zip(edges, edges[1:]):
+        m = (ratio >= lo) & (ratio < hi)
+        if m.sum() < 200:
+            continue
+        worse.append((np.sqrt(lo * hi), rel_i[m].max() > rel_f[m].max()))
+    above = [c for c, w in worse if not w]
+    below = [c for c, w in worse if w]
+    cross = min(above)
+    assert max(below) < cross
+    page = float(golden_map("error_bounds.txt")["int8_e4m3_crossover"][0])
+    assert 0.75 * page < cross < 1.35 * page
+    assert all(w for c, w in worse if c < 0.5 * page)
+    assert not any(w for c, w in worse if c > 2 * page)
+
+
+# ---- P9: MXFP4 ------------------------------------------------------------------
+def test_p9_mx_alignment_example(O):
+    """The page's example A/6 = 1.99 vs 2.01: round-up gives scales 2 and 4.
+    The default floor(log2 A) - 2 rule gives 2 for both."""
+    rows = read_golden("mx_alignment_example.txt")
+    for r in rows:
+        A = np.float32(float(r[1]) * 6)
+        assert O.e8m0_value(O.e8m0_code(float(A), O.FLAG_MX_ROUND_UP)) == float(r[3])
+        assert O.e8m0_value(O.e8m0_code(float(A))) == 2.0
+    # default rule with block maximum 12.06: s = 2, v = 6.03 saturates to 6
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 12.06
+    x[0, 1] = -1.0
+    r = O.quantize(x, "mxfp4", "block")
+    assert r["scales"][0, 0] == 128
+    assert r["xhat"][0, 0] == 12.0
+    assert r["stats"]["n_saturated"] == 1
+    assert r["codes"][0, 0] == 0x7 | (0x9 << 4)  # +6 low nibble, -1/2 = -0.5 (0x9) high nibble
+
+
+def test_p9_mx_bounds(O, S):
+    x = S.make("c3", nrows=256)
+    for flags in (0, O.FLAG_MX_ROUND_UP):
+        r = O.quantize(x, "mxfp4", "block", flags=flags)
+        xb = x_f32(S, x).reshape(-1, 32).astype(np.float64)
+        xh = r["xhat"].reshape(-1, 32).astype(np.float64)
+        s = np.exp2(r["scales"].reshape(-1).astype(np.float64) - 127)[:, None]
+        A = np.abs(xb).max(axis=1, keepdims=True)
+        v = xb / s
+        err = np.abs(xb - xh)
+        if flags == 0:
+            assert ((A / s >= 4) & (A / s < 8)).all()
+            inr = np.abs(v) <= 6
+            assert (err[inr] <= s.repeat(32, 1)[inr]).all()
+            top = np.abs(v) > 6
+            assert (np.abs(xh[top]) == 6 * s.repeat(32, 1)[top]).all()
+            assert (err[top] < 2 * s.repeat(32, 1)[top]).all()
+        else:
+            g = golden_map("error_bounds.txt")
+            rho = s / (A / 6)
+            assert ((rho >= 1) & (rho < 2)).all()
+            assert (err <= s).all()
+            assert (err.max(axis=1, keepdims=True) < A * float(g["mx_err_worst"][0])).all()
+            zt = np.where(xh == 0, np.abs(xb), 0).max(axis=1, keepdims=True)
+            assert (zt <= A * float(g["mx_zero_hi"][0])).all()
+            assert (zt <= 0.25 * s).all()
+        assert (np.where(np.abs(v) <= 0.25, xh, 0) == 0).all()
+
+
+def x_f32(S, x):
+    return S.bf16_to_f32(x) if x.dtype == np.uint16 else x
+
+
+# ---- P10: NVFP4 -----------------------------------------------------------------
+def test_p10_nv_bounds(O, S):
+    x = S.make("c4", nrows=128)
+    G = float(np.max(np.abs(x_f32(S, x))))
+    r = O.quantize(x, "nvfp4", "block")
+    g = golden_map("error_bounds.txt")
+    sb = r["scales"].reshape(-1)
+    assert sb.max() <= 0x7E
+    s_g = float(r["global_scale"][0])
+    assert s_g == float(np.float32(G) / np.float32(2688))
+    dec = O.fp_decode_array(O.K_E4M3, sb).astype(np.float64)
+    s_nv = (np.float32(s_g) * dec.astype(np.float32)).astype(np.float64)[:, None]
+    xb = x_f32(S, x).reshape(-1, 16).astype(np.float64)
+    xh = r["xhat"].reshape(-1, 16).astype(np.float64)
+    A = np.abs(xb).max(axis=1, keepdims=True)
+    t = (A / 6) / s_g
+    normal = (t >= 2.0 ** -6) & (t <= 448)
+    rho = (s_nv / (A / 6))[normal]
+    assert rho.min() >= 1 - 1e-6
+    assert rho.max() <= float(g["nv_rho_max"][0]) + 1e-6
+    err = np.abs(xb - xh)
+    nb = normal[:, 0]
+    assert (err[nb].max(axis=1) <= A[nb, 0] * float(g["nv_err"][0]) * (1 + 1e-6)).all()
+    zt = np.where(xh == 0, np.abs(xb), 0).max(axis=1)
+    assert (zt[nb] <= A[nb, 0] * float(g["nv_zero"][0])).all()
+
+
+def test_p10_e4m3_ceil_is_smallest_not_below(O):
+    """Rounding the block scale up: the smallest E4M3 value >= t, with the
+    E4M3 table taken from torch's decode."""
+    tab = torch_fp8_table(torch.float8_e4m3fn)
+    for c in range(0x7F):
+        v = np.float32(tab[c])
+        assert O.e4m3_ceil(v) == c
+        if c < 0x7E:
+            assert O.e4m3_ceil(np.nextafter(v, np.float32(np.inf))) == c + 1
+    assert O.e4m3_ceil(1e6) == 0x7E
+
+
+def test_p10_nv_aligned_block_is_exact(O):
+    """rho = 1 (the aligned case): G = 2688 gives s_global = 1, and a block
+    whose maximum is 6 gets t = 1 exactly, so E2M1 values come back exact."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 2688.0
+    vals = np.array([6, -3, 1.5, 0.5, -4, 2, 1, -6, 0, 3, 4, -0.5, 1.5, 2, -1, 6], np.float32)
+    x[0, 16:] = vals
+    r = O.quantize(x, "nvfp4", "block")
+    assert r["global_scale"][0] == 1.0
+    assert r["scales"][0, 1] == 0x38                     # E4M3 1.0
+    assert np.array_equal(r["xhat"][0, 16:], vals)
+
+
+# ---- P11: INT4 and the nibble order of Puzzle 12 ---------------------------------
+def test_p11_int4_bound_and_nibbles(O, S):
+    x = S.make("c5", nrows=64)
+    r = O.quantize(x, "int4", "block")
+    xb = x_f32(S, x).astype(np.float64)
+    sf = r["scales"].view(np.float16).astype(np.float64)                 # [rows, groups]
+    sfe = np.repeat(sf, 128, axis=1)
+    A = np.abs(xb).reshape(x.shape[0], -1, 128).max(axis=2)
+    assert np.allclose(sf, A / 7, rtol=2 ** -10)
+    q = r["xhat"].astype(np.float64) / sfe
+    assert np.array_equal(q, np.rint(q))
+    v = xb / sfe
+    assert (np.abs(v - q) <= 0.5 + 1e-6).all()
+    assert (np.abs(xb[q == 0]) <= sfe[q == 0] / 2 * (1 + 1e-6)).all()
+    g = golden_map("error_bounds.txt")
+    Ae = np.repeat(A, 128, axis=1)
+    assert (np.abs(xb - r["xhat"]) <= Ae * float(g["int4_err"][0]) * (1 + 1e-3)).all()
+    # Puzzle 12's extract(): element i of a packed 32-bit word is (w >> 4i) & 0xF
+    words = r["codes"].view("<u4")
+    for i in range(8):
+        nib = (words >> (4 * i)) & 0xF
+        assert np.array_equal(nib, (q[:, i::8].astype(np.int64) & 0xF))
+
+
+# ---- P14: statistics by brute force ------------------------------------------------
+@pytest.mark.parametrize("fmt,gran,cfg", [("e4m3", "row", "c2"), ("e5m2", "row", "c2"),
+                                          ("int8", "tensor", "c1"), ("mxfp4", "block", "c3"),
+                                          ("nvfp4", "block", "c4"), ("int4", "block", "c5")])
+def test_p14_stats_bruteforce(O, S, fmt, gran, cfg):
+    x = S.make(cfg, nrows=64)
+    x.reshape(-1)[::97] = 0          # exact zeros must not count as flushed
+    x.reshape(-1)[5::193] = 0x8000 if x.dtype == np.uint16 else np.float32(-0.0)
+    r = O.quantize(x, fmt, gran)
+    xf = x_f32(S, x)
+    x64 = xf.astype(np.float64)
+    xh = r["xhat"]
+    d = (xf - xh).astype(np.float64)
+    st = r["stats"]
+    assert st["n"] == x.size
+    assert st["n_nonfinite"] == 0
+    assert st["sum_x2"] == pytest.approx(np.sum(x64 * x64), rel=1e-12)
+    assert st["sum_err2"] == pytest.approx(np.sum(d * d), rel=1e-12)
+    assert st["sum_abs_err"] == pytest.approx(np.sum(np.abs(d)), rel=1e-12)
+    assert st["max_abs_err"] == np.float32(np.abs(d).max())
+    assert st["n_zero_flush"] == int(np.sum((xf != 0) & (xh == 0)))
+    assert st["n_zero_flush"] < int(np.sum(xh == 0))
+    # d = x - x^ is exact: recomputing in double gives the same values
+    assert np.array_equal(d, x64 - xh.astype(np.float64))
+
+
+def test_dequantize_reproduces_xhat(O, S):
+    for fmt, gran, cfg in [("e4m3", "row", "c2"), ("e5m2", "row", "c2"), ("int8", "tensor", "c1"),
+                           ("e4m3", "tensor", "c1"), ("mxfp4", "block", "c3"), ("nvfp4", "block", "c4"),
+                           ("int4", "block", "c5")]:
+        x = S.make(cfg, nrows=32)
+        r = O.quantize(x, fmt, gran)
+        rows, cols = x.shape
+        d = O.dequantize(r["codes"], r["scales"], fmt, gran, rows, cols, r["global_scale"])
+        assert np.array_equal(d.view(np.uint32), r["xhat"].view(np.uint32)), fmt
+        b = O.dequantize(r["codes"], r["scales"], fmt, gran, rows, cols, r["global_scale"], O.BF16)
+        assert np.array_equal(b, S.f32_to_bf16_bits(r["xhat"])), fmt
+
+
+# ---- readings where the pages are silent (parity unpinned; documented rules) ------
+def test_readings_special_values(O):
+    x = np.array([[0.0, -0.0, -1e-30, np.nan, np.inf, -np.inf, 1.0, -2.0] * 4], dtype=np.float32)
+    r = O.quantize(x, "e4m3", "row")
+    c = r["codes"][0]
+    assert r["scales"][0] == np.float32(2.0) / np.float32(448.0)   # absmax over finite values
+    assert c[0] == 0x00 and c[1] == 0x80 and c[2] == 0x80            # sign kept on zero
+    assert c[3] == 0x7F                                               # NaN -> NaN code
+    assert c[4] == 0x7E and c[5] == 0xFE                              # +-Inf saturate
+    st = r["stats"]
+    assert st["n_nonfinite"] == 12 and st["n"] == 32
+    assert st["n_saturated"] == 8                                     # the infinities
+    assert np.isfinite(st["sum_err2"])
+    z = O.quantize(np.zeros((2, 32), np.float32), "int8", "row")
+    assert (z["codes"] == 0).all() and (z["scales"] == 0).all() and (z["xhat"] == 0).all()
+    m = O.quantize(x, "mxfp4", "block")
+    nib = [(m["codes"][0, i // 2] >> (4 * (i % 2))) & 0xF for i in range(8)]
+    assert nib[3] == 0 and nib[4] == 0x7 and nib[5] == 0xF and nib[1] == 0x8
+
+
+def test_empty_and_invalid(O):
+    r = O.quantize(np.zeros((0, 32), np.float32), "e4m3", "row")
+    assert r["stats"]["n"] == 0
+    with pytest.raises(ValueError):
+        O.quantize(np.zeros((2, 48), np.float32), "mxfp4", "block")   # 48 % 32 != 0
+    with pytest.raises(ValueError):
+        O.quantize(np.zeros((2, 32), np.float32), "mxfp4", "row")
