@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Throughput of the quantization hot path on one MI355X.
+
+A step is one pass of the whole path over the activation workload
+(BF16 8192 x 8192, N(0,1) with 0.5 % outlier channels x200): per-row
+E4M3 quantize (absmax, scale, saturating RNE cast, pack, fused dequant and
+error statistics), the standalone dequantize of those codes to BF16, and
+the same two calls for E5M2.  `value` is the algorithmic bytes of the step
+(every input read once plus every output written once) divided by the
+timed wall time, inputs already resident in HBM.
+
+Buffers rotate over 4 sets so that no call reads data the previous calls
+touched within the last ~400 MB of traffic (the 256 MB memory-side cache
+cannot serve the timed reads).
+
+Also reported: the dominant kernel's HBM roofline, a per-format breakdown
+over the other workloads, a hand-written 16-byte copy kernel as the
+practical ceiling, and the CPU oracle timed on the host on a bounded sample.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantize GB/s (bytes in+out) and % of MI355X HBM peak, per format"
+NSETS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-format workloads")
+    ap.add_argument("--stream", action="store_true", help="add the 2 GiB streaming pass to the breakdown")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, copy)")
+    ap.add_argument("--reps", type=int, default=20, help="timed repetitions per breakdown entry")
+    return ap.parse_args()
+
+
+def to_device(x_np):
+    """numpy float32 / uint16 (BF16 bits) -> device tensor."""
+    import numpy as np
+    import torch
+    if x_np.dtype == np.uint16:
+        return torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(x_np).to("cuda:0")
+
+
+def algo_bytes(fmt, gran, rows, cols, in_elem):
+    """Bytes the method itself must move: x once, codes + scales once."""
+    n = rows * cols
+    codes = n // 2 if fmt in ("mxfp4", "nvfp4", "int4") else n
+    if fmt in ("int8", "e4m3", "e5m2"):
+        scales = 4 if gran == "tensor" else 4 * rows
+    elif fmt == "mxfp4":
+        scales = n // 32
+    elif fmt == "nvfp4":
+        scales = n // 16 + 4
+    else:
+        scales = 2 * (n // 128)
+    return n * in_elem + codes + scales, codes + scales
+
+
+def timed(fn, reps, stream):
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median_us": 1e3 * ms[len(ms) // 2], "p10_us": 1e3 * ms[len(ms) // 10],
+            "p90_us": 1e3 * ms[(9 * len(ms)) // 10], "mean_us": 1e3 * sum(ms) / len(ms)}
+
+
+class Workload:
+    """NSETS device copies of one synthetic input plus outputs per format."""
+
+    def __init__(self, name, formats, x_np=None):
+        import torch
+
+        from synth import synth
+        self.name = name
+        self.w = synth.WORKLOADS[name]
+        x_np = synth.make(name) if x_np is None else x_np
+        x0 = to_device(x_np)
+        self.xs = [x0] + [x0.clone() for _ in range(NSETS - 1)]
+        self.rows, self.cols = x_np.shape
+        self.in_elem = 2 if x_np.dtype.itemsize == 2 else 4
+        self.formats = formats
+        import int_quantization_amd as iq
+        self.iq = iq
+        self.ws = [iq.workspace_for(iq.desc_for(x0, *formats[0]), x0.device) for _ in range(NSETS)]
+        self.q = {}
+        for fmt, gran in formats:
+            self.q[(fmt, gran)] = [iq.quantize(x, fmt, gran, stats=True, workspace=w) for x, w in zip(self.xs, self.ws)]
+        out_dt = torch.bfloat16 if self.in_elem == 2 else torch.float32
+        self.out = [torch.empty((self.rows, self.cols), dtype=out_dt, device=x0.device) for _ in range(NSETS)]
+        torch.cuda.synchronize()
+
+    def quant(self, fmt, gran, i):
+        self.iq.quantize(self.xs[i], fmt, gran, workspace=self.ws[i], out=self.q[(fmt, gran)][i])
+
+    def dequant(self, fmt, gran, i, j):
+        self.iq.dequantize(self.q[(fmt, gran)][j], out=self.out[i])
+
+    def bytes(self, fmt, gran):
+        qb, code_b = algo_bytes(fmt, gran, self.rows, self.cols, self.in_elem)
+        dq = code_b + self.rows * self.cols * self.in_elem
+        return qb, dq
+
+
+def copy_ceiling(reps=20):
+    """GB/s (read + write) of the 16-byte copy kernel over 1 GiB."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "int_quantization_amd", "libiq_bench.so"))
+    lib.iqb_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = [torch.empty(n // 4, dtype=torch.float32, device="cuda:0") for _ in range(2)]
+    s = torch.cuda.current_stream()
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        k = [0]
+
+        def run():
+            rc = lib.iqb_copy(src.data_ptr(), dst[k[0] & 1].data_ptr(), n, grid, s.cuda_stream)
+            k[0] += 1
+            assert rc == 0
+
+        run()
+        t = timed(run, reps, s)
+        gbs = 2 * n / (t["median_us"] * 1e-6) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "grid": grid, "median_us": round(t["median_us"], 2)}
+    return best
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in ("int_quantization_amd/csrc/iq_kernels.hip", "int_quantization_amd/csrc/iq_launch.h"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(rows=2048):
+    """The oracle (unchanged) on the first `rows` rows of the activation
+    workload: the same two formats' quantize + dequantize, same byte count."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from synth import synth
+    threads = max(1, min(os.cpu_count() or 1, 16))   # the host share of one GPU
+    x = synth.make("c2", nrows=rows)
+    t0 = time.perf_counter()
+    total = 0
+    for fmt in ("e4m3", "e5m2"):
+        r = O.quantize(x, fmt, "row", threads=threads)
+        O.dequantize(r["codes"], r["scales"], fmt, "row", rows, x.shape[1], None, O.BF16)
+        qb, code_b = algo_bytes(fmt, "row", rows, x.shape[1], 2)
+        total += qb + code_b + x.size * 2
+    dt = time.perf_counter() - t0
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of 8192 rows of the activation workload (BF16 {rows}x8192): per-row E4M3 "
+                      f"and E5M2 quantize with x^ and statistics, then dequantize to BF16; "
+                      f"quantize rows split over {threads} threads, dequantize serial; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on one MI355X)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import int_quantization_amd as iq
+    iq.load_library()
+    stream = torch.cuda.current_stream()
+
+    if args.only:
+        return only(args)
+
+    # ---- the step: activation workload, E4M3 and E5M2 per row ---------------------
+    fmts = [("e4m3", "row"), ("e5m2", "row")]
+    W = Workload("c2", fmts)
+    step_bytes = 0
+    for f in fmts:
+        qb, dq = W.bytes(*f)
+        step_bytes += qb + dq
+    per_call = {f"{a}/{b}/{k}": [] for a, b in fmts for k in ("quantize", "dequantize")}
+    ev = []
+
+    def step(s, record):
+        i, j = s % NSETS, (s - 1) % NSETS
+        for f in fmts:
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+                W.quant(*f, i)
+                e[1].record(stream)
+                W.dequant(*f, i, j)
+                e[2].record(stream)
+                ev.append((f, e))
+            else:
+                W.quant(*f, i)
+                W.dequant(*f, i, j)
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for (a, b), e in ev:
+        per_call[f"{a}/{b}/quantize"].append(e[0].elapsed_time(e[1]) * 1e3)
+        per_call[f"{a}/{b}/dequantize"].append(e[1].elapsed_time(e[2]) * 1e3)
+    value = step_bytes * args.steps / elapsed / 1e9
+    avg = {k: sum(v) / len(v) for k, v in per_call.items()}
+
+    qb, _ = W.bytes("e4m3", "row")
+    dom_us = avg["e4m3/row/quantize"]
+    achieved = qb / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("c2_e4m3_row"),
+                "kernel": "iq_quantize E4M3 per-row (k_quant_row + stats finalize)",
+                "bytes_per_launch": qb, "avg_launch_us": round(dom_us, 2)}
+    calls = {k: {"avg_us": round(v, 2)} for k, v in avg.items()}
+    for a, b in fmts:
+        q, d = W.bytes(a, b)
+        calls[f"{a}/{b}/quantize"]["GB/s"] = round(q / (avg[f"{a}/{b}/quantize"] * 1e-6) / 1e9, 1)
+        calls[f"{a}/{b}/dequantize"]["GB/s"] = round(d / (avg[f"{a}/{b}/dequantize"] * 1e-6) / 1e9, 1)
+    del W
+    torch.cuda.empty_cache()
+
+    extra = {"calls": calls}
+    if not args.no_breakdown:
+        extra["copy_ceiling"] = copy_ceiling()
+        extra["per_format"] = breakdown(args)
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "activations BF16 8192x8192, N(0,1) with 0.5% outlier channels x200, seed 2; "
+                               "per-row E4M3 and E5M2: quantize (+fused dequant + error stats) and dequantize "
+                               "to BF16", "rows": 8192, "cols": 8192, "input": "bf16",
+                   "formats": ["e4m3/row", "e5m2/row"], "step_bytes": step_bytes, "buffer_sets": NSETS},
+        "roofline": roofline, "cpu_baseline": cpu, **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def breakdown(args):
+    import torch
+    res = {}
+    plan = [("c1", [("int8", "tensor"), ("e4m3", "tensor")]), ("c2", [("e4m3", "row"), ("e5m2", "row")]),
+            ("c3", [("mxfp4", "block")]), ("c4", [("nvfp4", "block")]), ("c5", [("int4", "block")])]
+    if args.stream:
+        from synth import synth
+        plan.append(("stream", list(synth.WORKLOADS["stream"].formats)))
+    stream = torch.cuda.current_stream()
+    for name, fmts in plan:
+        W = Workload(name, fmts)
+        for fmt, gran in fmts:
+            k = [0]
+
+            def q():
+                W.quant(fmt, gran, k[0] % NSETS)
+                k[0] += 1
+
+            def d():
+                W.dequant(fmt, gran, k[0] % NSETS, (k[0] + 1) % NSETS)
+                k[0] += 1
+
+            for _ in range(3):
+                q()
+            tq = timed(q, args.reps, stream)
+            td = timed(d, args.reps, stream)
+            qb, dq = W.bytes(fmt, gran)
+            gq = qb / (tq["median_us"] * 1e-6) / 1e9
+            gd = dq / (td["median_us"] * 1e-6) / 1e9
+            res[f"{name}:{fmt}/{gran}"] = {
+                "quantize_GBps": round(gq, 1), "quantize_frac_hbm": round(gq / HBM_PEAK_GBS, 4),
+                "quantize_us": round(tq["median_us"], 2), "quantize_p10_p90_us": [round(tq["p10_us"], 2), round(tq["p90_us"], 2)],
+                "dequantize_GBps": round(gd, 1), "dequantize_us": round(td["median_us"], 2), "bytes": qb}
+        del W
+        torch.cuda.empty_cache()
+    return res
+
+
+def only(args):
+    """Loop one call type (for rocprofv3 runs)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    if args.only == "copy":
+        print(json.dumps({"copy_ceiling": copy_ceiling(args.reps)}), flush=True)
+        return
+    name, fmt, gran = args.only.split(":")
+    W = Workload(name, [(fmt, gran)])
+    for s in range(args.warmup + args.steps):
+        W.quant(fmt, gran, s % NSETS)
+    for s in range(args.steps):
+        W.dequant(fmt, gran, s % NSETS, (s + 1) % NSETS)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "calls": args.warmup + args.steps}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * iq.h -- C ABI of libiq, block-scaled low-precision quantization on MI355X.
+ *
+ * The method (Lorn blog, post "浅谈低精度浮点数", sections "FP8" and
+ * "FP4 / MXFP4 / NVFP4"): a tensor x is represented as x^ = s * Q(x / s),
+ * where s is a scale derived from an absolute maximum (per tensor, per row,
+ * or per block along the contiguous dimension) and Q rounds onto a small
+ * code grid.  One call reads x once and, in the same pass, derives the
+ * scales, casts with saturating round-to-nearest-even, packs codes and
+ * scales, dequantizes in registers and reduces error statistics.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named x, codes, scales, global_scale, stats, xhat, workspace
+ *   and amax_out are DEVICE pointers (HIP device memory of the current
+ *   device).  The descriptor is a HOST pointer.  The caller allocates and
+ *   owns every buffer; the library allocates nothing, keeps no state
+ *   between calls, and never synchronizes.
+ * - All work is enqueued on `stream` (0 = the null stream).  Functions
+ *   return before the GPU finishes; outputs are valid after the caller
+ *   synchronizes with the stream.
+ * - Arguments are validated on the host before anything is enqueued.  On
+ *   any error nothing is enqueued and no output is touched.
+ * - x is row-major [rows, cols] with a row stride of ld_in >= cols elements.
+ *   The base address must be 16-byte aligned and ld_in * sizeof(element) a
+ *   multiple of 16.  codes, scales and xhat are dense row-major and 16-byte
+ *   aligned; workspace is 256-byte aligned.
+ * - rows == 0 or cols == 0 is legal: no codes or scales are written and the
+ *   statistics (if requested) are written as zeros.
+ *
+ * Code and scale layouts (element (r, c); K = cols):
+ *   INT8        codes  int8  [rows, K]   (two's complement, q in [-127, 127])
+ *   FP8 E4M3/E5M2 codes uint8 [rows, K]  (OCP E4M3: max 448, NaN 0x7F;
+ *                                         OCP E5M2: max 57344)
+ *   MXFP4       codes  uint8 [rows, K/2]  E2M1 nibbles; scales uint8 E8M0 [rows, K/32]
+ *   NVFP4       codes  uint8 [rows, K/2]  E2M1 nibbles; scales uint8 E4M3 [rows, K/16];
+ *               global_scale float32 [1]
+ *   INT4        codes  uint8 [rows, K/2]  two's-complement nibbles, q in [-7, 7];
+ *               scales float16 bits [rows, K/128]
+ *   INT8 / FP8 scales: float32 [1] per tensor, float32 [rows] per row.
+ *   4-bit codes: element 2t in bits 3:0 of byte t, element 2t+1 in bits 7:4
+ *   (the order of the packed-word extract() of the Triton post, Puzzle 12).
+ */
+#ifndef IQ_H
+#define IQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IQ_ABI_VERSION 1
+
+typedef enum {
+    IQ_OK = 0,
+    IQ_EINVAL = 1,       /* NULL required pointer, bad enum, bad shape, cols not a multiple of the block */
+    IQ_EALIGN = 2,       /* a pointer or the row stride breaks the alignment rules above */
+    IQ_EUNSUPPORTED = 3, /* legal but not supported: unknown flags, sizes beyond 2^31 chunks */
+    IQ_EHIP = 4          /* the HIP runtime reported an error when launching */
+} iq_status;
+
+typedef enum {
+    IQ_INT8 = 0,     /* symmetric, s = alpha / 127 ("FP8" section, INT8 quantizer) */
+    IQ_FP8_E4M3 = 1, /* s = alpha / 448 */
+    IQ_FP8_E5M2 = 2, /* s = alpha / 57344 */
+    IQ_MXFP4 = 3,    /* E2M1 codes, one E8M0 scale per 32 elements ("MXFP4") */
+    IQ_NVFP4 = 4,    /* E2M1 codes, one E4M3 scale per 16 + FP32 global scale ("NVFP4") */
+    IQ_INT4 = 5      /* symmetric, s = A / 7 per group of 128, FP16 scale ("INT4") */
+} iq_format;
+
+typedef enum { IQ_F32 = 0, IQ_BF16 = 1 } iq_dtype;
+
+typedef enum {
+    IQ_PER_TENSOR = 0, /* INT8 / FP8 */
+    IQ_PER_ROW = 1,    /* INT8 / FP8 */
+    IQ_PER_BLOCK = 2   /* MXFP4 (32), NVFP4 (16), INT4 (128): the only legal choice for those */
+} iq_gran;
+
+/* Rule variants (iq_desc.flags); 0 selects the default readings. */
+#define IQ_FLAG_MX_ROUND_NEAREST 0x1u /* MXFP4: E8M0 = 2^round(log2(A/6)) instead of 2^(floor(log2 A)-2) */
+#define IQ_FLAG_MX_ROUND_UP 0x2u      /* MXFP4: E8M0 = 2^ceil(log2(A/6)) */
+#define IQ_FLAG_NV_SCALE_RNE 0x4u     /* NVFP4: block scale to E4M3 by RNE instead of rounding up */
+
+typedef struct {
+    int32_t fmt;      /* iq_format */
+    int32_t gran;     /* iq_gran */
+    int32_t in_dtype; /* iq_dtype of x */
+    int32_t reserved0;
+    int64_t rows, cols;
+    int64_t ld_in;    /* row stride of x, in elements */
+    uint32_t flags;
+    uint32_t reserved1;
+} iq_desc;
+
+/* Error statistics of one iq_quantize call, written to device memory.
+ * n counts every element; sums, max_abs_err and n_zero_flush cover the
+ * finite inputs.  d = x - x^ (exact in FP32).  MSE = sum_err2 / (n - n_nonfinite).
+ *   n_saturated   elements with |x/s| above the grid's largest value
+ *   n_zero_flush  finite x != 0 whose x^ is 0 */
+typedef struct {
+    uint64_t n, n_zero_flush, n_saturated, n_nonfinite;
+    double sum_x2, sum_err2, sum_abs_err;
+    float max_abs_err;
+    uint32_t reserved;
+} iq_stats;
+
+/* Bytes of the codes / scales arrays for a descriptor (0 on an invalid one). */
+size_t iq_codes_bytes(const iq_desc* d);
+size_t iq_scales_bytes(const iq_desc* d);
+/* Bytes of device workspace iq_quantize / iq_amax need (>= 256). */
+size_t iq_workspace_bytes(const iq_desc* d);
+
+/*
+ * Quantize x (the whole hot path).  Sections "FP8" (x^ = s * round(x / s),
+ * s = alpha / 127; FP8 with its own grid) and "FP4 / MXFP4 / NVFP4"
+ * (MXFP4 x^ = s_mx * Q(x / s_mx); NVFP4 s_global = amax / (6 * 448),
+ * s_block = (block_amax / 6) / s_global; INT4 s = A / 7).
+ *   codes, scales    outputs, layouts above (required)
+ *   global_scale     NVFP4 output s_global (required for NVFP4, else ignored)
+ *   stats            optional output (NULL skips the statistics)
+ *   xhat             optional dequantized output [rows, cols] of xhat_dtype
+ *   workspace        iq_workspace_bytes(d) bytes of device scratch; the
+ *                    call overwrites it, concurrent calls need separate ones
+ */
+iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales,
+                      float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype,
+                      void* workspace, hipStream_t stream);
+
+/*
+ * Dequantize: x^ = s * decode(q), bit-identical to the x^ of iq_quantize.
+ * d->in_dtype and d->ld_in are ignored; xhat is dense [rows, cols] of
+ * xhat_dtype (BF16 output is the FP32 x^ rounded to nearest even).
+ */
+iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales,
+                        const float* global_scale, void* xhat, int32_t xhat_dtype,
+                        hipStream_t stream);
+
+/*
+ * Per-tensor absmax over the finite elements of x (the per-tensor "alpha"
+ * of section "FP8", the global amax of NVFP4), written to amax_out (device
+ * float32 [1]).  Only d->in_dtype, rows, cols and ld_in are used.
+ */
+iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace,
+                  hipStream_t stream);
+
+const char* iq_status_str(iq_status s);
+int iq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,243 @@
+"""Python binding of libiq (block-scaled quantization on MI355X).
+
+A thin ctypes layer over the C ABI declared in include/iq.h: the functions
+below carry the C names and only marshal arguments.  torch provides device
+memory (torch.empty) and the current HIP stream; every step of quantization
+runs in the HIP kernels of libiq.so.  There is no CPU fallback: importing
+works anywhere, but any call raises if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libiq.so")
+
+# iq_format / iq_gran / iq_dtype / iq_status values of include/iq.h
+FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5}
+GRANS = {"tensor": 0, "row": 1, "block": 2}
+IQ_F32, IQ_BF16 = 0, 1
+IQ_OK, IQ_EINVAL, IQ_EALIGN, IQ_EUNSUPPORTED, IQ_EHIP = 0, 1, 2, 3, 4
+FOUR_BIT = ("mxfp4", "nvfp4", "int4")
+
+
+class IQDesc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("gran", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_in", ctypes.c_int64), ("flags", ctypes.c_uint32), ("reserved1", ctypes.c_uint32)]
+
+
+class IQStats(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint64), ("n_zero_flush", ctypes.c_uint64),
+                ("n_saturated", ctypes.c_uint64), ("n_nonfinite", ctypes.c_uint64),
+                ("sum_x2", ctypes.c_double), ("sum_err2", ctypes.c_double),
+                ("sum_abs_err", ctypes.c_double), ("max_abs_err", ctypes.c_float),
+                ("reserved", ctypes.c_uint32)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libiq.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"libiq.so not found at {path}: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    D = ctypes.POINTER(IQDesc)
+    L.iq_codes_bytes.restype, L.iq_codes_bytes.argtypes = S, [D]
+    L.iq_scales_bytes.restype, L.iq_scales_bytes.argtypes = S, [D]
+    L.iq_workspace_bytes.restype, L.iq_workspace_bytes.argtypes = S, [D]
+    L.iq_quantize.restype = ctypes.c_int
+    L.iq_quantize.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.iq_dequantize.restype = ctypes.c_int
+    L.iq_dequantize.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
+    L.iq_amax.restype = ctypes.c_int
+    L.iq_amax.argtypes = [D, P, P, P, P]
+    L.iq_status_str.restype, L.iq_status_str.argtypes = ctypes.c_char_p, [ctypes.c_int]
+    L.iq_abi_version.restype, L.iq_abi_version.argtypes = ctypes.c_int, []
+    _lib = L
+    return L
+
+
+class IQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {iq_status_str(status)} ({status})")
+        self.status = status
+
+
+def _check(status: int, what: str) -> None:
+    if status != IQ_OK:
+        raise IQError(status, what)
+
+
+# ---- C entry points (same names, marshalling only) -------------------------
+def iq_abi_version() -> int:
+    return load_library().iq_abi_version()
+
+
+def iq_status_str(status: int) -> str:
+    return load_library().iq_status_str(status).decode()
+
+
+def iq_codes_bytes(d: IQDesc) -> int:
+    return load_library().iq_codes_bytes(ctypes.byref(d))
+
+
+def iq_scales_bytes(d: IQDesc) -> int:
+    return load_library().iq_scales_bytes(ctypes.byref(d))
+
+
+def iq_workspace_bytes(d: IQDesc) -> int:
+    return load_library().iq_workspace_bytes(ctypes.byref(d))
+
+
+def iq_quantize(d: IQDesc, x: int, codes: int, scales: int, global_scale: int | None, stats: int | None,
+                xhat: int | None, xhat_dtype: int, workspace: int, stream: int | None) -> int:
+    """Raw call with integer device addresses; returns the iq_status."""
+    return load_library().iq_quantize(ctypes.byref(d), x, codes, scales, global_scale, stats, xhat,
+                                      xhat_dtype, workspace, stream)
+
+
+def iq_dequantize(d: IQDesc, codes: int, scales: int, global_scale: int | None, xhat: int,
+                  xhat_dtype: int, stream: int | None) -> int:
+    return load_library().iq_dequantize(ctypes.byref(d), codes, scales, global_scale, xhat, xhat_dtype,
+                                        stream)
+
+
+def iq_amax(d: IQDesc, x: int, amax_out: int, workspace: int, stream: int | None) -> int:
+    return load_library().iq_amax(ctypes.byref(d), x, amax_out, workspace, stream)
+
+
+# ---- torch-facing helpers (allocation with torch.empty + the calls above) ---
+def _torch():
+    import torch
+    return torch
+
+
+def make_desc(fmt: str, gran: str, rows: int, cols: int, in_dtype: int = IQ_BF16, ld: int | None = None,
+              flags: int = 0) -> IQDesc:
+    return IQDesc(FORMATS[fmt], GRANS[gran], in_dtype, 0, rows, cols, cols if ld is None else ld, flags, 0)
+
+
+def desc_for(x, fmt: str, gran: str, cols: int | None = None, flags: int = 0) -> IQDesc:
+    """Descriptor of a 2-D CUDA/HIP tensor (float32 or bfloat16, unit column stride)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    if x.dtype == torch.float32:
+        dt = IQ_F32
+    elif x.dtype == torch.bfloat16:
+        dt = IQ_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    rows = x.shape[0]
+    c = x.shape[1] if cols is None else cols
+    ld = x.stride(0) if rows > 1 else c   # a single row is read at ld-independent offsets
+    return IQDesc(FORMATS[fmt], GRANS[gran], dt, 0, rows, c, ld, flags, 0)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def empty_outputs(d: IQDesc, device, fmt: str, gran: str):
+    """codes, scales, global_scale tensors for a descriptor (torch.empty)."""
+    torch = _torch()
+    rows, cols = d.rows, d.cols
+    codes = torch.empty((rows, cols // 2 if fmt in FOUR_BIT else cols), dtype=torch.uint8, device=device)
+    if fmt in ("int8", "e4m3", "e5m2"):
+        scales = torch.empty((1,) if gran == "tensor" else (rows,), dtype=torch.float32, device=device)
+    elif fmt == "mxfp4":
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+    elif fmt == "nvfp4":
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=device)
+    else:
+        scales = torch.empty((rows, cols // 128), dtype=torch.int16, device=device)
+    gscale = torch.empty((1,), dtype=torch.float32, device=device) if fmt == "nvfp4" else None
+    return codes, scales, gscale
+
+
+def workspace_for(d: IQDesc, device):
+    torch = _torch()
+    n = iq_workspace_bytes(d)
+    return torch.empty((n + 255) // 256 * 64, dtype=torch.float32, device=device)  # 256-byte aligned
+
+
+@dataclass
+class Quantized:
+    codes: object
+    scales: object
+    global_scale: object
+    xhat: object
+    stats_buf: object
+    fmt: str
+    gran: str
+    rows: int
+    cols: int
+
+    def stats(self) -> dict:
+        """Copy the statistics to the host (synchronizes with the device)."""
+        if self.stats_buf is None:
+            return None
+        raw = bytes(self.stats_buf.cpu().numpy().tobytes())
+        return IQStats.from_buffer_copy(raw).as_dict()
+
+
+def quantize(x, fmt: str, gran: str, *, stats: bool = True, xhat_dtype=None, cols: int | None = None,
+             flags: int = 0, workspace=None, out=None, stream=None) -> Quantized:
+    """Quantize a device tensor; outputs are allocated with torch.empty unless
+    `out` (a Quantized from a previous call of the same shape) is given."""
+    torch = _torch()
+    d = desc_for(x, fmt, gran, cols, flags)
+    if out is None:
+        codes, scales, gscale = empty_outputs(d, x.device, fmt, gran)
+        sbuf = torch.empty((64,), dtype=torch.uint8, device=x.device) if stats else None
+        xh = None
+        if xhat_dtype is not None:
+            xh = torch.empty((d.rows, d.cols), dtype=xhat_dtype, device=x.device)
+        out = Quantized(codes, scales, gscale, xh, sbuf, fmt, gran, d.rows, d.cols)
+    ws = workspace if workspace is not None else workspace_for(d, x.device)
+    xdt = IQ_F32
+    if out.xhat is not None:
+        xdt = IQ_F32 if out.xhat.dtype == torch.float32 else IQ_BF16
+    st = iq_quantize(d, x.data_ptr(), _ptr(out.codes), _ptr(out.scales), _ptr(out.global_scale),
+                     _ptr(out.stats_buf), _ptr(out.xhat), xdt, ws.data_ptr(), _stream(stream))
+    _check(st, "iq_quantize")
+    return out
+
+
+def dequantize(q: Quantized, out_dtype=None, out=None, stream=None):
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    d = make_desc(q.fmt, q.gran, q.rows, q.cols)
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    dt = IQ_F32 if out.dtype == torch.float32 else IQ_BF16
+    st = iq_dequantize(d, q.codes.data_ptr(), q.scales.data_ptr(), _ptr(q.global_scale), out.data_ptr(), dt,
+                       _stream(stream))
+    _check(st, "iq_dequantize")
+    return out
+
+
+def amax(x, workspace=None, stream=None):
+    torch = _torch()
+    d = desc_for(x, "e4m3", "tensor")
+    out = torch.empty((1,), dtype=torch.float32, device=x.device)
+    ws = workspace if workspace is not None else workspace_for(d, x.device)
+    _check(iq_amax(d, x.data_ptr(), out.data_ptr(), ws.data_ptr(), _stream(stream)), "iq_amax")
+    return out

@@ -1,0 +1,167 @@
+// C ABI of libiq: host-side validation, size queries, dispatch to the
+// kernel launchers.  Validation happens before any HIP call, so argument
+// errors are reported without touching the device.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/iq.h"
+#include "iq_launch.h"
+
+namespace {
+
+bool is_bf16_or_f32(int32_t t) { return t == IQ_F32 || t == IQ_BF16; }
+size_t elem_size(int32_t t) { return t == IQ_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool four_bit(int32_t f) { return f == IQ_MXFP4 || f == IQ_NVFP4 || f == IQ_INT4; }
+
+// Elements per scale along a row (0 = whole row or tensor); -1 if the
+// format / granularity pair is illegal.
+int64_t block_of(int32_t fmt, int32_t gran) {
+    switch (fmt) {
+    case IQ_INT8: case IQ_FP8_E4M3: case IQ_FP8_E5M2:
+        return (gran == IQ_PER_TENSOR || gran == IQ_PER_ROW) ? 0 : -1;
+    case IQ_MXFP4: return gran == IQ_PER_BLOCK ? 32 : -1;
+    case IQ_NVFP4: return gran == IQ_PER_BLOCK ? 16 : -1;
+    case IQ_INT4: return gran == IQ_PER_BLOCK ? 128 : -1;
+    default: return -1;
+    }
+}
+
+// Shape rules shared by every entry point.  cols must be a multiple of the
+// 8-element chunk (16 for the 4-bit formats' blocks anyway) and of the
+// block; the chunk count must fit 31 bits.
+iq_status check_shape(const iq_desc* d, bool need_in_dtype) {
+    if (!d) return IQ_EINVAL;
+    if (need_in_dtype && !is_bf16_or_f32(d->in_dtype)) return IQ_EINVAL;
+    int64_t b = block_of(d->fmt, d->gran);
+    if (b < 0) return IQ_EINVAL;
+    if (d->rows < 0 || d->cols < 0) return IQ_EINVAL;
+    if (d->cols % iqk::kChunk) return IQ_EINVAL;
+    if (b > 0 && d->cols % b) return IQ_EINVAL;
+    if (d->rows > 0 && d->cols > 0 && d->rows * (d->cols / iqk::kChunk) >= (int64_t)1 << 31)
+        return IQ_EUNSUPPORTED;
+    if (d->rows > ((int64_t)1 << 31) - 1) return IQ_EUNSUPPORTED;
+    if (d->flags != 0) return IQ_EUNSUPPORTED;  // rule variants are oracle-only for now
+    return IQ_OK;
+}
+
+iq_status check_input(const iq_desc* d, const void* x) {
+    if (d->ld_in < d->cols) return IQ_EINVAL;
+    if (d->rows > 0 && d->cols > 0) {
+        if (!x) return IQ_EINVAL;
+        if (!aligned(x, 16)) return IQ_EALIGN;
+        if ((d->ld_in * (int64_t)elem_size(d->in_dtype)) % 16) return IQ_EALIGN;
+    }
+    return IQ_OK;
+}
+
+size_t codes_bytes(const iq_desc* d) {
+    return (size_t)(d->rows * (four_bit(d->fmt) ? d->cols / 2 : d->cols));
+}
+
+size_t scales_bytes(const iq_desc* d) {
+    switch (d->fmt) {
+    case IQ_INT8: case IQ_FP8_E4M3: case IQ_FP8_E5M2:
+        return d->gran == IQ_PER_TENSOR ? 4 : (size_t)d->rows * 4;
+    case IQ_MXFP4: return (size_t)(d->rows * (d->cols / 32));
+    case IQ_NVFP4: return (size_t)(d->rows * (d->cols / 16));
+    default: return (size_t)(d->rows * (d->cols / 128)) * 2;
+    }
+}
+
+iq_status from_hip(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int iq_abi_version(void) { return IQ_ABI_VERSION; }
+
+const char* iq_status_str(iq_status s) {
+    switch (s) {
+    case IQ_OK: return "ok";
+    case IQ_EINVAL: return "invalid argument";
+    case IQ_EALIGN: return "misaligned pointer or row stride";
+    case IQ_EUNSUPPORTED: return "unsupported size or flags";
+    case IQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t iq_codes_bytes(const iq_desc* d) {
+    if (check_shape(d, false) != IQ_OK) return 0;
+    return codes_bytes(d);
+}
+
+size_t iq_scales_bytes(const iq_desc* d) {
+    if (check_shape(d, false) != IQ_OK) return 0;
+    return scales_bytes(d);
+}
+
+size_t iq_workspace_bytes(const iq_desc* d) {
+    (void)d;
+    return iqk::Workspace::kBytes;
+}
+
+iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales, float* global_scale,
+                      iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace, hipStream_t stream) {
+    iq_status st = check_shape(d, true);
+    if (st != IQ_OK) return st;
+    if ((st = check_input(d, x)) != IQ_OK) return st;
+    const bool empty = d->rows == 0 || d->cols == 0;
+    const bool needs_scale_slot = d->gran == IQ_PER_TENSOR || !empty;
+    if (!workspace) return IQ_EINVAL;
+    if (!empty && !codes) return IQ_EINVAL;
+    if (needs_scale_slot && !scales) return IQ_EINVAL;
+    if (d->fmt == IQ_NVFP4 && !global_scale) return IQ_EINVAL;
+    if (xhat && !is_bf16_or_f32(xhat_dtype)) return IQ_EINVAL;
+    if (!aligned(workspace, 256)) return IQ_EALIGN;
+    if (codes && !aligned(codes, 16)) return IQ_EALIGN;
+    if (scales && !aligned(scales, 4)) return IQ_EALIGN;
+    if (global_scale && !aligned(global_scale, 4)) return IQ_EALIGN;
+    if (stats && !aligned(stats, 8)) return IQ_EALIGN;
+    if (xhat && !aligned(xhat, 16)) return IQ_EALIGN;
+
+    iqk::QuantArgs a;
+    a.fmt = d->fmt; a.gran = d->gran; a.in_dtype = d->in_dtype;
+    a.rows = d->rows; a.cols = d->cols; a.ld = d->ld_in;
+    a.x = x; a.codes = codes; a.scales = scales; a.global_scale = global_scale;
+    a.stats = stats; a.xhat = xhat; a.xhat_dtype = xhat_dtype; a.workspace = workspace;
+    if (empty) { a.rows = 0; a.cols = 0; }
+    return from_hip(iqk::launch_quantize(a, stream));
+}
+
+iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales, const float* global_scale,
+                        void* xhat, int32_t xhat_dtype, hipStream_t stream) {
+    iq_status st = check_shape(d, false);
+    if (st != IQ_OK) return st;
+    if (!is_bf16_or_f32(xhat_dtype)) return IQ_EINVAL;
+    if (d->rows == 0 || d->cols == 0) return IQ_OK;
+    if (!codes || !scales || !xhat) return IQ_EINVAL;
+    if (d->fmt == IQ_NVFP4 && !global_scale) return IQ_EINVAL;
+    if (!aligned(codes, 16) || !aligned(xhat, 16) || !aligned(scales, 4)) return IQ_EALIGN;
+    if (global_scale && !aligned(global_scale, 4)) return IQ_EALIGN;
+    iqk::DequantArgs a;
+    a.fmt = d->fmt; a.gran = d->gran; a.rows = d->rows; a.cols = d->cols;
+    a.codes = codes; a.scales = scales; a.global_scale = global_scale;
+    a.xhat = xhat; a.xhat_dtype = xhat_dtype;
+    return from_hip(iqk::launch_dequantize(a, stream));
+}
+
+iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace, hipStream_t stream) {
+    if (!d) return IQ_EINVAL;
+    if (!is_bf16_or_f32(d->in_dtype)) return IQ_EINVAL;
+    if (d->rows < 0 || d->cols < 0 || d->cols % iqk::kChunk) return IQ_EINVAL;
+    if (d->rows > 0 && d->cols > 0 && d->rows * (d->cols / iqk::kChunk) >= (int64_t)1 << 31)
+        return IQ_EUNSUPPORTED;
+    iq_status st = check_input(d, x);
+    if (st != IQ_OK) return st;
+    if (!amax_out || !workspace) return IQ_EINVAL;
+    if (!aligned(workspace, 256)) return IQ_EALIGN;
+    if (!aligned(amax_out, 4)) return IQ_EALIGN;
+    const bool empty = d->rows == 0 || d->cols == 0;
+    return from_hip(iqk::launch_amax(d->in_dtype, empty ? 0 : d->rows, empty ? 0 : d->cols, d->ld_in, x,
+                                     amax_out, workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,1077 @@
+// Block-scaled quantization kernels for gfx950 (MI355X).
+//
+// Method: Lorn blog, post "浅谈低精度浮点数".
+//   section "FP8":  x^ = s * round(x / s), s = alpha / 127 (INT8); the FP8
+//                   quantizer uses the E4M3 / E5M2 grid with s = alpha / FMAX.
+//   section "FP4 / MXFP4 / NVFP4": MXFP4 x^ = s_mx * Q_E2M1(x / s_mx) with an
+//                   E8M0 scale per 32; NVFP4 s_global = amax / (6 * 448),
+//                   s_block = (block_amax / 6) / s_global cast to E4M3 per 16;
+//                   INT4 q in [-7, 7], s = A / 7 (per group of 128 here).
+//
+// Every kernel streams x once with 16-byte non-temporal loads: one "chunk"
+// is 8 consecutive elements of a row (one load for BF16, two for FP32), and
+// consecutive lanes own consecutive chunks, so each load instruction of a
+// wave covers a contiguous 1 KiB (BF16).  Block maxima are reduced across the
+// lanes that share a block with DPP (2 lanes NVFP4, 4 lanes MXFP4, 16 lanes
+// INT4); per-row maxima add one LDS step across the four waves of a
+// workgroup.  Codes are produced, decoded and compared with x in registers;
+// no MFMA is involved (nothing is contracted).
+//
+// Division x / s.  The pages define v = x / s.  The fast path computes the
+// correctly rounded binary32 quotient with one Markstein correction from a
+// per-unit reciprocal y = RN(1/s):
+//     q0 = x*y;  r = fma(s, q0, -x);  v = fma(-r, y, q0)
+// which equals RN(x/s) whenever |x| <= alpha, s >= 2^-64 and |x/s| >= 2^-20
+// (checked exhaustively over every BF16 x and every scale the BF16 inputs
+// can produce for INT8, FP8, INT4 and NVFP4, and on random FP32 inputs).
+// Below 2^-20 every grid rounds the quotient to a signed zero, which the
+// correction preserves.  Units with non-finite inputs, zero or tiny scales
+// take a slow path that uses the compiler's correctly rounded division.
+//
+// Hardware converts.  v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round to nearest
+// even on the OCP E4M3 / E5M2 grids and keep the sign of zero, but do not
+// saturate; the fast path never feeds them |v| beyond the midpoint above the
+// largest code (|v| <= FMAX * (1 + 2^-23)), and the slow path clamps first.
+// v_cvt_scalef32_pk_fp4_f32 divides by a power-of-two scale, rounds to
+// nearest even and saturates to +-6; NaN is patched to code 0 on the slow
+// path.  The decode converts are exact.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "iq_launch.h"
+
+namespace iqk {
+namespace {
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef short s2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------------------
+// Input chunks: 8 consecutive elements of one row.
+// ---------------------------------------------------------------------------
+template <int IN> struct Chunk;
+
+template <> struct Chunk<D_BF16> {
+    uint32_t w[4];
+    __device__ __forceinline__ void load(const void* base, int64_t elem) {
+        u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(static_cast<const uint16_t*>(base) + elem));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+    __device__ __forceinline__ void zero() { w[0] = w[1] = w[2] = w[3] = 0; }
+    // BF16 -> FP32 is exact: the BF16 bits are the top half of the FP32 word.
+    __device__ __forceinline__ float get(int i) const {
+        return (i & 1) ? as_f(w[i >> 1] & 0xFFFF0000u) : as_f(w[i >> 1] << 16);
+    }
+    // Absmax over finite elements, on the integer image of |x|: for BF16 bits
+    // a = |x| in [0, 0x7FFF], t = a + 0x80 is negative as int16 exactly when
+    // x is Inf or NaN, so a signed 16-bit max skips them.
+    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& nf) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t t = (w[k] & 0x7FFF7FFFu) + 0x00800080u;
+            s2v a = __builtin_bit_cast(s2v, m), b = __builtin_bit_cast(s2v, t);
+            m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+            nf |= t;
+        }
+    }
+    // Fold the packed state into (bits of the finite absmax, nonfinite flag).
+    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t nf, uint32_t& bits, uint32_t& flag) {
+        int lo = (int)(int16_t)(m & 0xFFFFu), hi = (int)(int16_t)(m >> 16);
+        int mx = lo > hi ? lo : hi;
+        bits = mx >= 0x80 ? (uint32_t)(mx - 0x80) << 16 : 0u;
+        flag = (nf & 0x80008000u) ? 1u : 0u;
+    }
+    static constexpr uint32_t kAbsInit = 0u;
+};
+
+template <> struct Chunk<D_F32> {
+    uint32_t w[8];
+    __device__ __forceinline__ void load(const void* base, int64_t elem) {
+        const u4v* p = reinterpret_cast<const u4v*>(static_cast<const float*>(base) + elem);
+        u4v a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = 0;
+    }
+    __device__ __forceinline__ float get(int i) const { return as_f(w[i]); }
+    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& nf) const {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t a = w[k] & 0x7FFFFFFFu;
+            bool fin = a < 0x7F800000u;
+            m = (fin && a > m) ? a : m;
+            nf |= fin ? 0u : 1u;
+        }
+    }
+    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t nf, uint32_t& bits, uint32_t& flag) {
+        bits = m;
+        flag = nf ? 1u : 0u;
+    }
+    static constexpr uint32_t kAbsInit = 0u;
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions.  DPP within rows of 16 lanes, shuffles across rows.
+// ---------------------------------------------------------------------------
+template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max / or over groups of G consecutive lanes (G = 2, 4 or 16); every lane of
+// the group receives the result.
+template <int G> __device__ __forceinline__ void group_reduce(uint32_t& m, uint32_t& f) {
+    m = umax(m, dpp<kQuadSwap1>(m)); f |= dpp<kQuadSwap1>(f);
+    if (G >= 4) { m = umax(m, dpp<kQuadSwap2>(m)); f |= dpp<kQuadSwap2>(f); }
+    if (G >= 16) {
+        m = umax(m, dpp<kRowHalfMirror>(m)); f |= dpp<kRowHalfMirror>(f);
+        m = umax(m, dpp<kRowMirror>(m)); f |= dpp<kRowMirror>(f);
+    }
+}
+
+__device__ __forceinline__ void wave_reduce_max_or(uint32_t& m, uint32_t& f) {
+    group_reduce<16>(m, f);
+    m = umax(m, (uint32_t)__shfl_xor((int)m, 16)); f |= (uint32_t)__shfl_xor((int)f, 16);
+    m = umax(m, (uint32_t)__shfl_xor((int)m, 32)); f |= (uint32_t)__shfl_xor((int)f, 32);
+}
+
+// ---------------------------------------------------------------------------
+// Error statistics.  Sums of the fast path run in FP32 over one unit of work
+// (at most a few dozen terms per lane) and are folded into FP64 per lane; the
+// slow path sums in FP64 directly, which also covers units whose absmax lies
+// outside [2^-40, 2^60] where FP32 squares would underflow or overflow.
+// Counters come from wave ballots, so they are only ever updated in
+// wave-uniform control flow (add8 below): every lane then holds the same,
+// complete count.  Lanes without data carry zeros and contribute nothing.
+// ---------------------------------------------------------------------------
+constexpr float kStatLo = 0x1p-40f;   // unit absmax range of the FP32 fast path
+constexpr float kStatHi = 0x1p60f;
+
+__device__ __forceinline__ bool stat_range(float a) { return a >= kStatLo && a <= kStatHi; }
+
+struct Stats {
+    double sx2 = 0, se2 = 0, sae = 0;
+    float mae = 0.f;
+    uint32_t nsat = 0, nzf = 0, nnf = 0;   // wave-uniform
+    float fx2 = 0.f, fe2 = 0.f, fae = 0.f; // FP32 accumulators of the current unit
+
+    __device__ __forceinline__ void fold() {
+        sx2 += (double)fx2; se2 += (double)fe2; sae += (double)fae;
+        fx2 = fe2 = fae = 0.f;
+    }
+    // Finite inputs in a well-scaled unit.
+    __device__ __forceinline__ void add_fast(float x, float v, float xh, float qmax) {
+        float d = x - xh;
+        fx2 = __builtin_fmaf(x, x, fx2);
+        fe2 = __builtin_fmaf(d, d, fe2);
+        fae += __builtin_fabsf(d);
+        mae = __builtin_fmaxf(mae, __builtin_fabsf(d));
+        nsat += __popcll(__ballot(__builtin_fabsf(v) > qmax));
+        nzf += __popcll(__ballot(x != 0.f && xh == 0.f));
+    }
+    // General case: non-finite inputs count but stay out of sums and maxima.
+    __device__ __forceinline__ void add_slow(float x, float v, float xh, float qmax) {
+        bool fin = __builtin_isfinite(x);
+        double d = fin ? (double)(x - xh) : 0.0;
+        double xs = fin ? (double)x : 0.0;
+        sx2 = __builtin_fma(xs, xs, sx2);
+        se2 = __builtin_fma(d, d, se2);
+        sae += __builtin_fabs(d);
+        mae = __builtin_fmaxf(mae, fin ? __builtin_fabsf(x - xh) : 0.f);
+        nsat += __popcll(__ballot(__builtin_fabsf(v) > qmax));
+        nzf += __popcll(__ballot(fin && x != 0.f && xh == 0.f));
+        nnf += __popcll(__ballot(!fin));
+    }
+    // One chunk, called in wave-uniform control flow; slow_lane marks lanes
+    // whose unit needs the general accumulation (the whole wave then uses it).
+    __device__ __forceinline__ void add8(bool slow_lane, const float (&x)[8], const float (&v)[8],
+                                         const float (&h)[8], float qmax) {
+        if (__ballot(slow_lane) == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) add_fast(x[i], v[i], h[i], qmax);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) add_slow(x[i], v[i], h[i], qmax);
+        }
+    }
+};
+
+// Reduce the workgroup's statistics and write its partial (thread 0).
+__device__ void write_partial(Stats& st, Partial* out) {
+    __shared__ double s_d[4][3];
+    __shared__ float s_m[4];
+    __shared__ uint32_t s_c[4][3];
+    st.fold();
+    double a = st.sx2, b = st.se2, c = st.sae;
+    float m = st.mae;
+    // The ballot counters were only updated in wave-uniform control flow:
+    // every lane holds the wave's count.
+    const uint32_t n0 = st.nsat, n1 = st.nzf, n2 = st.nnf;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        a += __shfl_xor(a, o); b += __shfl_xor(b, o); c += __shfl_xor(c, o);
+        m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) {
+        s_d[wave][0] = a; s_d[wave][1] = b; s_d[wave][2] = c; s_m[wave] = m;
+        s_c[wave][0] = n0; s_c[wave][1] = n1; s_c[wave][2] = n2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Partial p;
+        p.sum_x2 = ((s_d[0][0] + s_d[1][0]) + (s_d[2][0] + s_d[3][0]));
+        p.sum_err2 = ((s_d[0][1] + s_d[1][1]) + (s_d[2][1] + s_d[3][1]));
+        p.sum_abs_err = ((s_d[0][2] + s_d[1][2]) + (s_d[2][2] + s_d[3][2]));
+        p.max_abs_err = __builtin_fmaxf(__builtin_fmaxf(s_m[0], s_m[1]), __builtin_fmaxf(s_m[2], s_m[3]));
+        p.n_saturated = s_c[0][0] + s_c[1][0] + s_c[2][0] + s_c[3][0];
+        p.n_zero_flush = s_c[0][1] + s_c[1][1] + s_c[2][1] + s_c[3][1];
+        p.n_nonfinite = s_c[0][2] + s_c[1][2] + s_c[2][2] + s_c[3][2];
+        p.pad[0] = p.pad[1] = 0;
+        out[blockIdx.x] = p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grids and their constants.
+// ---------------------------------------------------------------------------
+template <int FMT> struct Fmt;
+template <> struct Fmt<F_INT8> { static constexpr float qmax = 127.f; };
+template <> struct Fmt<F_E4M3> { static constexpr float qmax = 448.f; };
+template <> struct Fmt<F_E5M2> { static constexpr float qmax = 57344.f; };
+template <> struct Fmt<F_MXFP4> { static constexpr float qmax = 6.f; };
+template <> struct Fmt<F_NVFP4> { static constexpr float qmax = 6.f; };
+template <> struct Fmt<F_INT4> { static constexpr float qmax = 7.f; };
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |v| < 2^22 to an integer (RNE)
+constexpr float kTinyScale = 0x1p-64f;  // smaller scales take the slow path
+
+__device__ __forceinline__ float markstein(float x, float s, float y) {
+    float q0 = x * y;
+    float r = __builtin_fmaf(s, q0, -x);
+    return __builtin_fmaf(-r, y, q0);
+}
+
+// FP8 pack / unpack (4 codes per 32-bit word, element 0 in the low byte).
+template <int FMT> __device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+    uint32_t w;
+    if (FMT == F_E4M3) {
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+    } else {
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+        w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, (int)w, true);
+    }
+    return w;
+}
+template <int FMT, bool HI> __device__ __forceinline__ f2v fp8_unpack2(uint32_t w) {
+    f2v r;
+    if (FMT == F_E4M3) {
+        auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+        r.x = d[0]; r.y = d[1];
+    } else {
+        auto d = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+        r.x = d[0]; r.y = d[1];
+    }
+    return r;
+}
+// Exact value of one E4M3 code (low byte of c).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+    return d[0];
+}
+
+// ---------------------------------------------------------------------------
+// x^ output of one chunk (FP32 or BF16 by round to nearest even).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_xhat(void* xhat, int dtype, int64_t elem, const float (&h)[8]) {
+    if (dtype == D_F32) {
+        u4v* p = reinterpret_cast<u4v*>(static_cast<float*>(xhat) + elem);
+        u4v a = {as_u(h[0]), as_u(h[1]), as_u(h[2]), as_u(h[3])};
+        u4v b = {as_u(h[4]), as_u(h[5]), as_u(h[6]), as_u(h[7])};
+        __builtin_nontemporal_store(a, p);
+        __builtin_nontemporal_store(b, p + 1);
+    } else {
+        u4v o;
+        uint32_t r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t w;
+            asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(w) : "v"(h[2 * k]), "v"(h[2 * k + 1]));
+            r[k] = w;
+        }
+        o.x = r[0]; o.y = r[1]; o.z = r[2]; o.w = r[3];
+        __builtin_nontemporal_store(o, reinterpret_cast<u4v*>(static_cast<uint16_t*>(xhat) + elem));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// INT8 / FP8 with a scale shared by the whole chunk (per row or per tensor).
+// `fast` must be wave-uniform.  Every lane computes (lanes without data hold
+// zeros); only lanes with `store` write 8 code bytes at codes8 and x^ in h.
+// ---------------------------------------------------------------------------
+template <int IN, int FMT, bool STATS>
+__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float s, float y, bool fast, bool store,
+                                                    uint8_t* codes8, float (&h)[8], Stats& st) {
+    constexpr float Q = Fmt<FMT>::qmax;
+    float x[8], v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
+    uint32_t w0, w1;
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s, y);
+        if (FMT == F_INT8) {
+            float t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                t[i] = v[i] + kMagic;        // |v| <= 127 * (1 + 2^-23): the sum is the RNE integer
+                h[i] = s * (t[i] - kMagic);  // (t - kMagic) is +0 for a zero code
+            }
+            uint32_t p0 = __builtin_amdgcn_perm(as_u(t[1]), as_u(t[0]), 0x0c0c0400u);
+            uint32_t p1 = __builtin_amdgcn_perm(as_u(t[3]), as_u(t[2]), 0x0c0c0400u);
+            uint32_t p2 = __builtin_amdgcn_perm(as_u(t[5]), as_u(t[4]), 0x0c0c0400u);
+            uint32_t p3 = __builtin_amdgcn_perm(as_u(t[7]), as_u(t[6]), 0x0c0c0400u);
+            w0 = p0 | (p1 << 16);
+            w1 = p2 | (p3 << 16);
+        } else {
+            w0 = fp8_pack4<FMT>(v[0], v[1], v[2], v[3]);
+            w1 = fp8_pack4<FMT>(v[4], v[5], v[6], v[7]);
+            f2v d0 = fp8_unpack2<FMT, false>(w0), d1 = fp8_unpack2<FMT, true>(w0);
+            f2v d2 = fp8_unpack2<FMT, false>(w1), d3 = fp8_unpack2<FMT, true>(w1);
+            h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
+            h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
+        }
+    } else {
+        // Slow path: correctly rounded division, explicit clamps and NaN codes.
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (s == 0.f) ? 0.f : x[i] / s;
+        if (FMT == F_INT8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -127.f), 127.f);
+                int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
+                c[i] = (uint32_t)qi & 0xFFu;
+                h[i] = s * (float)qi;
+            }
+        } else {
+            float cl[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cl[i] = __builtin_fminf(__builtin_fmaxf(v[i], -Q), Q);
+            uint32_t a = fp8_pack4<FMT>(cl[0], cl[1], cl[2], cl[3]);
+            uint32_t b = fp8_pack4<FMT>(cl[4], cl[5], cl[6], cl[7]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t byte = ((i < 4 ? a : b) >> (8 * (i & 3))) & 0xFFu;
+                if (__builtin_isnan(v[i])) byte = 0x7Fu;
+                if (s == 0.f) byte = 0u;
+                c[i] = byte;
+            }
+            uint32_t a2 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+            uint32_t b2 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            f2v d0 = fp8_unpack2<FMT, false>(a2), d1 = fp8_unpack2<FMT, true>(a2);
+            f2v d2 = fp8_unpack2<FMT, false>(b2), d3 = fp8_unpack2<FMT, true>(b2);
+            h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
+            h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
+        }
+        w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    }
+    if (store) {
+        u2v o = {w0, w1};
+        __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(codes8));
+    }
+    if (STATS) st.add8(!fast, x, v, h, Q);
+}
+
+// ---------------------------------------------------------------------------
+// Per-row INT8 / FP8: one workgroup owns one row at a time; the row stays in
+// registers between the absmax and the cast (CPT chunks per thread).
+// ---------------------------------------------------------------------------
+struct RowArgs {
+    const void* x;
+    int64_t ld;
+    int32_t rows, cpr;   // chunks per row
+    uint8_t* codes;
+    float* scales;
+    void* xhat;
+    int xhat_dtype;
+    Partial* partials;
+};
+
+template <int IN, int FMT, int CPT, bool STATS>
+__global__ __launch_bounds__(kThreads) void k_quant_row(RowArgs a) {
+    __shared__ uint32_t s_red[2][4][2];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t cols = (int64_t)a.cpr * kChunk;
+    Stats st;
+    int parity = 0;
+    for (int32_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
+        Chunk<IN> ch[CPT];
+        const void* xrow = a.x;
+        const int64_t base = (int64_t)row * a.ld;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            int c = tid + j * kThreads;
+            if (c < a.cpr) ch[j].load(xrow, base + (int64_t)c * kChunk);
+            else ch[j].zero();
+        }
+        uint32_t m = Chunk<IN>::kAbsInit, nf = 0;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) ch[j].absmax(m, nf);
+        uint32_t bits, flag;
+        Chunk<IN>::absmax_finish(m, nf, bits, flag);
+        wave_reduce_max_or(bits, flag);
+        if (lane == 0) { s_red[parity][wave][0] = bits; s_red[parity][wave][1] = flag; }
+        __syncthreads();
+        bits = umax(umax(s_red[parity][0][0], s_red[parity][1][0]), umax(s_red[parity][2][0], s_red[parity][3][0]));
+        flag = s_red[parity][0][1] | s_red[parity][1][1] | s_red[parity][2][1] | s_red[parity][3][1];
+        const float alpha = as_f(bits);
+        const float s = alpha / Fmt<FMT>::qmax;
+        if (tid == 0) a.scales[row] = s;
+        // fast: finite row with alpha in [2^-40, 2^60] (so s >= 2^-64)
+        const bool fast = flag == 0 && stat_range(alpha);
+        const float y = fast ? 1.0f / s : 0.f;
+        uint8_t* crow = a.codes + (int64_t)row * cols;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = tid + j * kThreads;
+            const bool valid = c < a.cpr;
+            float h[8];
+            quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, valid, crow + (int64_t)c * kChunk, h, st);
+            if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
+        }
+        if (STATS) st.fold();
+    }
+    if (STATS) write_partial(st, a.partials);
+}
+
+// Rows longer than kRowCptMax * kThreads chunks: absmax pass, then a second
+// pass that re-reads the row (from L2 for rows up to a few MiB).
+template <int IN, int FMT, bool STATS>
+__global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
+    __shared__ uint32_t s_red[2][4][2];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t cols = (int64_t)a.cpr * kChunk;
+    Stats st;
+    int parity = 0;
+    for (int32_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
+        const int64_t base = (int64_t)row * a.ld;
+        uint32_t m = Chunk<IN>::kAbsInit, nf = 0;
+        for (int c = tid; c < a.cpr; c += kThreads) {
+            Chunk<IN> ch;
+            ch.load(a.x, base + (int64_t)c * kChunk);
+            ch.absmax(m, nf);
+        }
+        uint32_t bits, flag;
+        Chunk<IN>::absmax_finish(m, nf, bits, flag);
+        wave_reduce_max_or(bits, flag);
+        if (lane == 0) { s_red[parity][wave][0] = bits; s_red[parity][wave][1] = flag; }
+        __syncthreads();
+        bits = umax(umax(s_red[parity][0][0], s_red[parity][1][0]), umax(s_red[parity][2][0], s_red[parity][3][0]));
+        flag = s_red[parity][0][1] | s_red[parity][1][1] | s_red[parity][2][1] | s_red[parity][3][1];
+        const float alpha = as_f(bits);
+        const float s = alpha / Fmt<FMT>::qmax;
+        if (tid == 0) a.scales[row] = s;
+        const bool fast = flag == 0 && stat_range(alpha);
+        const float y = fast ? 1.0f / s : 0.f;
+        uint8_t* crow = a.codes + (int64_t)row * cols;
+        // uniform trip count: lanes past the row end carry a zero chunk
+        for (int c0 = 0; c0 < a.cpr; c0 += kThreads) {
+            const int c = c0 + tid;
+            const bool valid = c < a.cpr;
+            Chunk<IN> ch;
+            if (valid) ch.load(a.x, base + (int64_t)c * kChunk);
+            else ch.zero();
+            float h[8];
+            quant_chunk_uniform<IN, FMT, STATS>(ch, s, y, fast, valid, crow + (int64_t)c * kChunk, h, st);
+            if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
+            if (STATS) st.fold();
+        }
+    }
+    if (STATS) write_partial(st, a.partials);
+}
+
+// ---------------------------------------------------------------------------
+// Flat kernels: chunks of the [rows, cols] tensor in row-major order; each
+// workgroup iteration covers kTileChunks consecutive chunks.
+// ---------------------------------------------------------------------------
+struct FlatGeom {
+    const void* x;
+    int64_t ld;
+    uint32_t nchunks, cpr;
+    int cpr_shift;   // log2(cpr) if cpr is a power of two, else -1
+    int contiguous;  // ld == cols
+    __device__ __forceinline__ int64_t elem(uint32_t g) const {
+        if (contiguous) return (int64_t)g * kChunk;
+        uint32_t row = cpr_shift >= 0 ? (g >> cpr_shift) : (g / cpr);
+        return (int64_t)row * ld + (int64_t)(g - row * cpr) * kChunk;
+    }
+};
+
+struct FlatArgs {
+    FlatGeom geo;
+    uint8_t* codes;
+    void* scales;
+    float* global_scale;
+    void* xhat;
+    int xhat_dtype;
+    const TensorInfo* info;  // per-tensor INT8/FP8 and NVFP4: absmax pre-pass result
+    Partial* partials;
+};
+
+// The functions below run on every lane of the wave (lanes past the end of
+// the tensor carry a zero chunk, `valid` false); only stores are predicated,
+// and the statistics are accumulated in wave-uniform control flow.
+
+// MXFP4: blocks of 32 = 4 chunks = 4 lanes.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
+template <int IN, bool STATS>
+__device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
+    uint32_t m = Chunk<IN>::kAbsInit, nf = 0, bits, flag;
+    ch.absmax(m, nf);
+    Chunk<IN>::absmax_finish(m, nf, bits, flag);
+    group_reduce<4>(bits, flag);
+    int E = 0;
+    if (bits) {
+        int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
+        E = e - 2 + 127;
+        E = E < 0 ? 0 : (E > 254 ? 254 : E);
+    }
+    const float sc = E ? as_f((uint32_t)E << 23) : as_f(0x00400000u);   // 2^(E-127), exact
+    if (valid && (g & 3u) == 0) static_cast<uint8_t*>(a.scales)[g >> 2] = (uint8_t)E;
+    float x[8], v[8], h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], sc, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
+    if (flag) {
+        // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (__builtin_isnan(x[i])) w &= ~(0xFu << (4 * i));
+    }
+    f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+    f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+    f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+    f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+    h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
+    if (valid) {
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
+        if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
+    }
+    if (STATS) {
+        // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
+        // when |x| > 6 * 2^(E-127) (both sides are exact near 6).  v carries
+        // 7 for saturated elements and 0 otherwise (NaN never saturates).
+        const float thr = 6.0f * sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_fabsf(x[i]) > thr ? 7.f : 0.f;
+        st.add8(flag || !stat_range(as_f(bits)), x, v, h, 6.f);
+    }
+}
+
+// Smallest E4M3 code whose value is >= t (t >= 0, finite), capped at 448.
+__device__ __forceinline__ uint32_t e4m3_ceil(float t) {
+    if (t > 448.f) return 0x7Eu;
+    uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xFFu;   // RNE
+    return e4m3_value(c) < t ? c + 1u : c;
+}
+
+// NVFP4: blocks of 16 = 2 chunks = 2 lanes.
+template <int IN, bool STATS>
+__device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, bool valid, float s_g, const FlatArgs& a, Stats& st) {
+    uint32_t m = Chunk<IN>::kAbsInit, nf = 0, bits, flag;
+    ch.absmax(m, nf);
+    Chunk<IN>::absmax_finish(m, nf, bits, flag);
+    group_reduce<2>(bits, flag);
+    uint32_t sb = 0;
+    float s_nv = 0.f;
+    if (s_g != 0.f) {
+        const float t = (as_f(bits) / 6.0f) / s_g;
+        sb = e4m3_ceil(t);
+        s_nv = s_g * e4m3_value(sb);
+    }
+    if (valid && (g & 1u) == 0) static_cast<uint8_t*>(a.scales)[g >> 1] = (uint8_t)sb;
+    const bool fast = !flag && s_nv >= kTinyScale && stat_range(as_f(bits));
+    float x[8], v[8], h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
+    uint32_t w = 0;
+    if (fast) {
+        const float y = 1.0f / s_nv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s_nv, y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (s_nv == 0.f) ? 0.f : x[i] / s_nv;
+    }
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+    if (!fast) {
+        if (s_nv == 0.f) w = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (__builtin_isnan(v[i])) w &= ~(0xFu << (4 * i));
+    }
+    f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    h[0] = s_nv * p0.x; h[1] = s_nv * p0.y; h[2] = s_nv * p1.x; h[3] = s_nv * p1.y;
+    h[4] = s_nv * p2.x; h[5] = s_nv * p2.y; h[6] = s_nv * p3.x; h[7] = s_nv * p3.y;
+    if (valid) {
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
+        if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
+    }
+    if (STATS) st.add8(!fast, x, v, h, 6.f);
+}
+
+// INT4: groups of 128 = 16 chunks = 16 lanes; FP16 scale fp16(A / 7), saturated.
+template <int IN, bool STATS>
+__device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
+    uint32_t m = Chunk<IN>::kAbsInit, nf = 0, bits, flag;
+    ch.absmax(m, nf);
+    Chunk<IN>::absmax_finish(m, nf, bits, flag);
+    group_reduce<16>(bits, flag);
+    const float s32 = as_f(bits) / 7.0f;
+    _Float16 hs = (_Float16)s32;                       // RNE
+    uint16_t s16 = s32 > 65504.f ? (uint16_t)0x7BFF : __builtin_bit_cast(uint16_t, hs);
+    const float sf = (float)__builtin_bit_cast(_Float16, s16);
+    if (valid && (g & 15u) == 0) static_cast<uint16_t*>(a.scales)[g >> 4] = s16;
+    // fast: finite inputs and a normal, unsaturated FP16 scale keep |x/sf| < 7.5
+    // (and put A = 7 sf inside the FP32 statistics range)
+    const bool fast = !flag && sf >= 0x1p-14f && s32 <= 65504.f;
+    float x[8], v[8], h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
+    uint32_t w = 0;
+    if (fast) {
+        const float y = 1.0f / sf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = markstein(x[i], sf, y);
+            float t = v[i] + kMagic;
+            w |= (as_u(t) & 0xFu) << (4 * i);
+            h[i] = sf * (t - kMagic);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = (sf == 0.f) ? 0.f : x[i] / sf;
+            float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -7.f), 7.f);
+            int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
+            w |= ((uint32_t)qi & 0xFu) << (4 * i);
+            h[i] = sf * (float)qi;
+        }
+    }
+    if (valid) {
+        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
+        if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
+    }
+    if (STATS) st.add8(!fast, x, v, h, 7.f);
+}
+
+template <int IN, int FMT, bool STATS>
+__global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
+    Stats st;
+    const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
+    // Per-tensor quantities from the absmax pre-pass (uniform over the grid).
+    float s = 0.f, y = 0.f;
+    bool fast = false;
+    if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2 || FMT == F_NVFP4) {
+        s = a.info->scale;
+        fast = a.info->nonfinite == 0 && stat_range(as_f(a.info->amax_bits));
+        if (fast && FMT != F_NVFP4) y = 1.0f / s;
+    }
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        Chunk<IN> ch[kTileChunksPerThread];
+        uint32_t g[kTileChunksPerThread];
+        bool valid[kTileChunksPerThread];
+#pragma unroll
+        for (int j = 0; j < kTileChunksPerThread; ++j) {
+            g[j] = tile * kTileChunks + j * kThreads + threadIdx.x;
+            valid[j] = g[j] < a.geo.nchunks;
+            if (valid[j]) ch[j].load(a.geo.x, a.geo.elem(g[j]));
+            else ch[j].zero();
+        }
+#pragma unroll
+        for (int j = 0; j < kTileChunksPerThread; ++j) {
+            if (FMT == F_MXFP4) {
+                quant_chunk_mx<IN, STATS>(ch[j], g[j], valid[j], a, st);
+            } else if (FMT == F_NVFP4) {
+                quant_chunk_nv<IN, STATS>(ch[j], g[j], valid[j], s, a, st);
+            } else if (FMT == F_INT4) {
+                quant_chunk_int4<IN, STATS>(ch[j], g[j], valid[j], a, st);
+            } else {
+                float h[8];
+                quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, valid[j], a.codes + (int64_t)g[j] * kChunk, h, st);
+                if (a.xhat && valid[j]) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g[j] * kChunk, h);
+            }
+        }
+        if (STATS) st.fold();
+    }
+    if (STATS) write_partial(st, a.partials);
+}
+
+// ---------------------------------------------------------------------------
+// Absmax pre-pass (per-tensor formats, the NVFP4 global scale, iq_amax).
+// ---------------------------------------------------------------------------
+template <int IN>
+__global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* partials) {
+    __shared__ uint32_t s_red[4][2];
+    const uint32_t ntiles = (geo.nchunks + kTileChunks - 1) / kTileChunks;
+    uint32_t m = Chunk<IN>::kAbsInit, nf = 0;
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        Chunk<IN> ch[kTileChunksPerThread];
+#pragma unroll
+        for (int j = 0; j < kTileChunksPerThread; ++j) {
+            uint32_t g = tile * kTileChunks + j * kThreads + threadIdx.x;
+            if (g < geo.nchunks) ch[j].load(geo.x, geo.elem(g));
+            else ch[j].zero();
+        }
+#pragma unroll
+        for (int j = 0; j < kTileChunksPerThread; ++j) ch[j].absmax(m, nf);
+    }
+    uint32_t bits, flag;
+    Chunk<IN>::absmax_finish(m, nf, bits, flag);
+    wave_reduce_max_or(bits, flag);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { s_red[wave][0] = bits; s_red[wave][1] = flag; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        partials[2 * blockIdx.x] = umax(umax(s_red[0][0], s_red[1][0]), umax(s_red[2][0], s_red[3][0]));
+        partials[2 * blockIdx.x + 1] = s_red[0][1] | s_red[1][1] | s_red[2][1] | s_red[3][1];
+    }
+}
+
+// Fold the absmax partials; derive the per-tensor scale (alpha / qmax) or the
+// NVFP4 global scale (amax / 2688); write them where the caller wants them.
+__global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* partials, int n, float qdiv,
+                                                            TensorInfo* info, float* scale_out, float* amax_out) {
+    uint32_t m = 0, f = 0;
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        m = umax(m, partials[2 * i]);
+        f |= partials[2 * i + 1];
+    }
+    __shared__ uint32_t s_red[4][2];
+    wave_reduce_max_or(m, f);
+    if ((threadIdx.x & 63) == 0) { s_red[threadIdx.x >> 6][0] = m; s_red[threadIdx.x >> 6][1] = f; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = umax(umax(s_red[0][0], s_red[1][0]), umax(s_red[2][0], s_red[3][0]));
+        f = s_red[0][1] | s_red[1][1] | s_red[2][1] | s_red[3][1];
+        float s = qdiv > 0.f ? as_f(m) / qdiv : 0.f;
+        if (info) { TensorInfo t; t.amax_bits = m; t.nonfinite = f; t.scale = s; t.pad = 0; *info = t; }
+        if (scale_out) *scale_out = s;
+        if (amax_out) *amax_out = as_f(m);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Statistics finalize: one workgroup, fixed summation order.
+// ---------------------------------------------------------------------------
+struct StatsOut {   // mirrors iq_stats
+    uint64_t n, n_zero_flush, n_saturated, n_nonfinite;
+    double sum_x2, sum_err2, sum_abs_err;
+    float max_abs_err;
+    uint32_t reserved;
+};
+
+__global__ __launch_bounds__(kThreads) void k_stats_finalize(const Partial* p, int n, uint64_t nelem, StatsOut* out) {
+    __shared__ double s_d[kThreads][3];
+    __shared__ float s_m[kThreads];
+    __shared__ uint64_t s_c[kThreads][3];
+    double a = 0, b = 0, c = 0;
+    float m = 0.f;
+    uint64_t c0 = 0, c1 = 0, c2 = 0;
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        a += p[i].sum_x2; b += p[i].sum_err2; c += p[i].sum_abs_err;
+        m = __builtin_fmaxf(m, p[i].max_abs_err);
+        c0 += p[i].n_saturated; c1 += p[i].n_zero_flush; c2 += p[i].n_nonfinite;
+    }
+    const int t = threadIdx.x;
+    s_d[t][0] = a; s_d[t][1] = b; s_d[t][2] = c; s_m[t] = m;
+    s_c[t][0] = c0; s_c[t][1] = c1; s_c[t][2] = c2;
+    __syncthreads();
+    for (int w = kThreads / 2; w >= 1; w >>= 1) {
+        if (t < w) {
+            s_d[t][0] += s_d[t + w][0]; s_d[t][1] += s_d[t + w][1]; s_d[t][2] += s_d[t + w][2];
+            s_m[t] = __builtin_fmaxf(s_m[t], s_m[t + w]);
+            s_c[t][0] += s_c[t + w][0]; s_c[t][1] += s_c[t + w][1]; s_c[t][2] += s_c[t + w][2];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        StatsOut o;
+        o.n = nelem; o.n_saturated = s_c[0][0]; o.n_zero_flush = s_c[0][1]; o.n_nonfinite = s_c[0][2];
+        o.sum_x2 = s_d[0][0]; o.sum_err2 = s_d[0][1]; o.sum_abs_err = s_d[0][2];
+        o.max_abs_err = s_m[0]; o.reserved = 0;
+        *out = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: codes + scales -> x^ (FP32 or BF16), x^ = s * decode(q).
+// ---------------------------------------------------------------------------
+struct DeqArgs {
+    uint32_t nchunks, cpr;
+    int cpr_shift;
+    const uint8_t* codes;
+    const void* scales;
+    const float* global_scale;
+    void* xhat;
+    int xhat_dtype;
+    int per_tensor;
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
+    const uint32_t ntiles = (a.nchunks + kTileChunks - 1) / kTileChunks;
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+#pragma unroll
+        for (int j = 0; j < kTileChunksPerThread; ++j) {
+            const uint32_t g = tile * kTileChunks + j * kThreads + threadIdx.x;
+            if (g >= a.nchunks) continue;
+            float h[8];
+            if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) {
+                const uint32_t row = a.per_tensor ? 0u : (a.cpr_shift >= 0 ? g >> a.cpr_shift : g / a.cpr);
+                const float s = static_cast<const float*>(a.scales)[row];
+                u2v c = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(a.codes) + g);
+                if (FMT == F_INT8) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        int q = (int)(int8_t)(((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu);
+                        h[i] = s * (float)q;
+                    }
+                } else {
+                    f2v d0 = fp8_unpack2<FMT, false>(c.x), d1 = fp8_unpack2<FMT, true>(c.x);
+                    f2v d2 = fp8_unpack2<FMT, false>(c.y), d3 = fp8_unpack2<FMT, true>(c.y);
+                    h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
+                    h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
+                }
+            } else {
+                const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.codes) + g);
+                if (FMT == F_MXFP4) {
+                    const uint32_t E = static_cast<const uint8_t*>(a.scales)[g >> 2];
+                    const float sc = E ? as_f(E << 23) : as_f(0x00400000u);
+                    f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+                    f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+                    f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+                    f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+                    h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
+                    if (E == 255u) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) h[i] = __builtin_nanf("");
+                    }
+                } else if (FMT == F_NVFP4) {
+                    const uint32_t sb = static_cast<const uint8_t*>(a.scales)[g >> 1];
+                    const float s_nv = a.global_scale[0] * e4m3_value(sb);
+                    f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+                    f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+                    f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+                    f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+                    h[0] = s_nv * p0.x; h[1] = s_nv * p0.y; h[2] = s_nv * p1.x; h[3] = s_nv * p1.y;
+                    h[4] = s_nv * p2.x; h[5] = s_nv * p2.y; h[6] = s_nv * p3.x; h[7] = s_nv * p3.y;
+                } else {
+                    const uint16_t s16 = static_cast<const uint16_t*>(a.scales)[g >> 4];
+                    const float sf = (float)__builtin_bit_cast(_Float16, s16);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        int q = (int)((w >> (4 * i)) & 0xFu);
+                        q = (q & 7) - (q & 8);
+                        h[i] = sf * (float)q;
+                    }
+                }
+            }
+            store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side helpers.
+// ---------------------------------------------------------------------------
+int ilog2_exact(uint32_t v) {
+    if (v == 0 || (v & (v - 1))) return -1;
+    int s = 0;
+    while ((1u << s) != v) ++s;
+    return s;
+}
+
+FlatGeom make_geom(const void* x, int64_t rows, int64_t cols, int64_t ld) {
+    FlatGeom g;
+    g.x = x;
+    g.ld = ld;
+    g.cpr = (uint32_t)(cols / kChunk);
+    g.nchunks = (uint32_t)(rows * (cols / kChunk));
+    g.cpr_shift = ilog2_exact(g.cpr);
+    g.contiguous = ld == cols;
+    return g;
+}
+
+int flat_grid(uint32_t nchunks) {
+    uint32_t tiles = (nchunks + kTileChunks - 1) / kTileChunks;
+    return (int)(tiles < (uint32_t)kMaxGrid ? (tiles ? tiles : 1) : kMaxGrid);
+}
+
+template <int IN, int FMT, bool STATS>
+hipError_t launch_row_t(const RowArgs& r, int grid, int cpt, hipStream_t s) {
+    switch (cpt) {
+    case 1: k_quant_row<IN, FMT, 1, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 2: k_quant_row<IN, FMT, 2, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 4: k_quant_row<IN, FMT, 4, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 8: k_quant_row<IN, FMT, 8, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    default: k_quant_row_long<IN, FMT, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    }
+    return hipGetLastError();
+}
+
+template <int IN, int FMT>
+hipError_t launch_row(const RowArgs& r, int grid, int cpt, bool stats, hipStream_t s) {
+    return stats ? launch_row_t<IN, FMT, true>(r, grid, cpt, s) : launch_row_t<IN, FMT, false>(r, grid, cpt, s);
+}
+
+template <int IN, int FMT>
+hipError_t launch_flat(const FlatArgs& f, int grid, bool stats, hipStream_t s) {
+    if (stats) k_quant_flat<IN, FMT, true><<<grid, kThreads, 0, s>>>(f);
+    else k_quant_flat<IN, FMT, false><<<grid, kThreads, 0, s>>>(f);
+    return hipGetLastError();
+}
+
+template <int IN>
+hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, int grid, bool stats, hipStream_t s) {
+    switch (fmt) {
+    case F_INT8: return launch_flat<IN, F_INT8>(f, grid, stats, s);
+    case F_E4M3: return launch_flat<IN, F_E4M3>(f, grid, stats, s);
+    case F_E5M2: return launch_flat<IN, F_E5M2>(f, grid, stats, s);
+    case F_MXFP4: return launch_flat<IN, F_MXFP4>(f, grid, stats, s);
+    case F_NVFP4: return launch_flat<IN, F_NVFP4>(f, grid, stats, s);
+    default: return launch_flat<IN, F_INT4>(f, grid, stats, s);
+    }
+}
+
+template <int IN>
+hipError_t launch_row_fmt(int fmt, const RowArgs& r, int grid, int cpt, bool stats, hipStream_t s) {
+    switch (fmt) {
+    case F_INT8: return launch_row<IN, F_INT8>(r, grid, cpt, stats, s);
+    case F_E4M3: return launch_row<IN, F_E4M3>(r, grid, cpt, stats, s);
+    default: return launch_row<IN, F_E5M2>(r, grid, cpt, stats, s);
+    }
+}
+
+hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, float qdiv, TensorInfo* info,
+                            float* scale_out, float* amax_out, hipStream_t s) {
+    uint32_t* part = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxOff);
+    const int grid = flat_grid(geo.nchunks);
+    if (geo.nchunks) {
+        if (in_dtype == D_BF16) k_amax<D_BF16><<<grid, kThreads, 0, s>>>(geo, part);
+        else k_amax<D_F32><<<grid, kThreads, 0, s>>>(geo, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    k_amax_finalize<<<1, kThreads, 0, s>>>(part, geo.nchunks ? grid : 0, qdiv, info, scale_out, amax_out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
+    char* ws = static_cast<char*>(q.workspace);
+    Partial* partials = reinterpret_cast<Partial*>(ws + Workspace::kPartialOff);
+    TensorInfo* info = reinterpret_cast<TensorInfo*>(ws + Workspace::kInfoOff);
+    const bool stats = q.stats != nullptr;
+    const int64_t nelem = q.rows * q.cols;
+    int grid = 0;
+    hipError_t e = hipSuccess;
+
+    if (q.gran == G_ROW) {
+        RowArgs r;
+        r.x = q.x; r.ld = q.ld; r.rows = (int32_t)q.rows; r.cpr = (int32_t)(q.cols / kChunk);
+        r.codes = static_cast<uint8_t*>(q.codes); r.scales = static_cast<float*>(q.scales);
+        r.xhat = q.xhat; r.xhat_dtype = q.xhat_dtype; r.partials = partials;
+        int per = (r.cpr + kThreads - 1) / kThreads;
+        int cpt = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
+        grid = (int)(q.rows < kMaxGrid ? q.rows : kMaxGrid);
+        if (nelem) {
+            e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, grid, cpt, stats, s)
+                                     : launch_row_fmt<D_F32>(q.fmt, r, grid, cpt, stats, s);
+        } else {
+            grid = 0;
+        }
+    } else {
+        FlatArgs f;
+        f.geo = make_geom(q.x, q.rows, q.cols, q.ld);
+        f.codes = static_cast<uint8_t*>(q.codes); f.scales = q.scales; f.global_scale = q.global_scale;
+        f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.info = info; f.partials = partials;
+        if (q.gran == G_TENSOR || q.fmt == F_NVFP4) {
+            float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
+            float* scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);
+            e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, scale_out, nullptr, s);
+            if (e != hipSuccess) return e;
+        }
+        grid = flat_grid(f.geo.nchunks);
+        if (nelem) {
+            e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, grid, stats, s)
+                                     : launch_flat_fmt<D_F32>(q.fmt, f, grid, stats, s);
+        } else {
+            grid = 0;
+        }
+    }
+    if (e != hipSuccess) return e;
+    if (stats) {
+        k_stats_finalize<<<1, kThreads, 0, s>>>(partials, grid, (uint64_t)nelem, static_cast<StatsOut*>(q.stats));
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
+    DeqArgs a;
+    a.cpr = (uint32_t)(d.cols / kChunk);
+    a.nchunks = (uint32_t)(d.rows * (d.cols / kChunk));
+    a.cpr_shift = ilog2_exact(a.cpr);
+    a.codes = static_cast<const uint8_t*>(d.codes);
+    a.scales = d.scales;
+    a.global_scale = d.global_scale;
+    a.xhat = d.xhat;
+    a.xhat_dtype = d.xhat_dtype;
+    a.per_tensor = d.gran == G_TENSOR;
+    if (a.nchunks == 0) return hipSuccess;
+    const int grid = flat_grid(a.nchunks);
+    switch (d.fmt) {
+    case F_INT8: k_dequant<F_INT8><<<grid, kThreads, 0, s>>>(a); break;
+    case F_E4M3: k_dequant<F_E4M3><<<grid, kThreads, 0, s>>>(a); break;
+    case F_E5M2: k_dequant<F_E5M2><<<grid, kThreads, 0, s>>>(a); break;
+    case F_MXFP4: k_dequant<F_MXFP4><<<grid, kThreads, 0, s>>>(a); break;
+    case F_NVFP4: k_dequant<F_NVFP4><<<grid, kThreads, 0, s>>>(a); break;
+    default: k_dequant<F_INT4><<<grid, kThreads, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, const void* x, float* amax_out,
+                       void* workspace, hipStream_t stream) {
+    FlatGeom geo = make_geom(x, rows, cols, ld);
+    return launch_amax_pass(in_dtype, geo, workspace, 0.f, nullptr, nullptr, amax_out, stream);
+}
+
+}  // namespace iqk

@@ -1,0 +1,77 @@
+// Internal interface between the C ABI (iq_api.cpp) and the kernel launchers
+// (iq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace iqk {
+
+// Formats and granularities use the public enum values of iq.h.
+enum { F_INT8 = 0, F_E4M3 = 1, F_E5M2 = 2, F_MXFP4 = 3, F_NVFP4 = 4, F_INT4 = 5 };
+enum { G_TENSOR = 0, G_ROW = 1, G_BLOCK = 2 };
+enum { D_F32 = 0, D_BF16 = 1 };
+
+constexpr int kThreads = 256;        // threads per workgroup of every streaming kernel
+constexpr int kChunk = 8;            // elements per chunk (one 16-byte BF16 load)
+constexpr int kTileChunksPerThread = 4;
+constexpr int kTileChunks = kThreads * kTileChunksPerThread;  // chunks per workgroup iteration
+constexpr int kMaxGrid = 2048;       // workgroups of the persistent streaming kernels
+constexpr int kRowCptMax = 8;        // register-resident row: up to 8 chunks per thread
+
+// Per-workgroup partial statistics, reduced by the finalize kernel in a fixed order.
+struct alignas(16) Partial {
+    double sum_x2, sum_err2, sum_abs_err;
+    float max_abs_err;
+    uint32_t n_saturated, n_zero_flush, n_nonfinite;
+    uint32_t pad[2];
+};
+static_assert(sizeof(Partial) == 48, "partial layout");
+
+// Workspace header written by the absmax finalize kernel.
+struct alignas(16) TensorInfo {
+    uint32_t amax_bits;   // absmax over finite elements (bits of a non-negative float)
+    uint32_t nonfinite;   // nonzero if any element is NaN or +-Inf
+    float scale;          // per-tensor scale (INT8/FP8) or NVFP4 global scale s_g
+    uint32_t pad;
+};
+
+struct Workspace {
+    static constexpr size_t kInfoOff = 0;
+    static constexpr size_t kAmaxOff = 256;                                  // uint2 per workgroup
+    static constexpr size_t kPartialOff = kAmaxOff + sizeof(uint32_t) * 2 * kMaxGrid;
+    static constexpr size_t kBytes = kPartialOff + sizeof(Partial) * kMaxGrid;
+};
+
+struct QuantArgs {
+    int fmt, gran, in_dtype;
+    int64_t rows, cols, ld;
+    const void* x;
+    void* codes;
+    void* scales;
+    float* global_scale;
+    void* stats;          // iq_stats*, may be null
+    void* xhat;           // may be null
+    int xhat_dtype;
+    void* workspace;
+};
+
+struct DequantArgs {
+    int fmt, gran;
+    int64_t rows, cols;
+    const void* codes;
+    const void* scales;
+    const float* global_scale;
+    void* xhat;
+    int xhat_dtype;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, const void* x,
+                       float* amax_out, void* workspace, hipStream_t stream);
+
+}  // namespace iqk

@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports what include/iq.h declares,
+matches the header's struct layouts, and rejects bad arguments on the host
+before anything is enqueued (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "iq.h")
+
+
+@pytest.fixture(scope="module")
+def iq():
+    import int_quantization_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from int_quantization_amd import build
+        build.build()
+    m.load_library()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(iq):
+    names = declared_functions()
+    assert set(names) >= {"iq_quantize", "iq_dequantize", "iq_amax", "iq_codes_bytes", "iq_scales_bytes",
+                          "iq_workspace_bytes", "iq_status_str", "iq_abi_version"}
+    lib = ctypes.CDLL(iq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", iq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (iq_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header(iq, tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "iq.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(iq_desc), offsetof(iq_desc, rows), offsetof(iq_desc, cols),
+         offsetof(iq_desc, ld_in), offsetof(iq_desc, flags), offsetof(iq_desc, in_dtype));
+  printf("%zu %zu %zu %zu\n", sizeof(iq_stats), offsetof(iq_stats, sum_x2), offsetof(iq_stats, max_abs_err),
+         offsetof(iq_stats, n_nonfinite));
+  return 0;
+}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    a, b = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")[:2]
+    D, S = iq.IQDesc, iq.IQStats
+    assert [int(v) for v in a.split()] == [ctypes.sizeof(D), D.rows.offset, D.cols.offset, D.ld_in.offset,
+                                            D.flags.offset, D.in_dtype.offset]
+    assert [int(v) for v in b.split()] == [ctypes.sizeof(S), S.sum_x2.offset, S.max_abs_err.offset,
+                                            S.n_nonfinite.offset]
+
+
+def test_version_and_status_strings(iq):
+    assert iq.iq_abi_version() == 1
+    for s in range(5):
+        assert iq.iq_status_str(s)
+    assert "unknown" in iq.iq_status_str(99)
+
+
+def test_size_queries(iq):
+    d = iq.make_desc("e4m3", "row", 8192, 8192)
+    assert iq.iq_codes_bytes(d) == 8192 * 8192
+    assert iq.iq_scales_bytes(d) == 8192 * 4
+    d = iq.make_desc("e4m3", "tensor", 1024, 4096, iq.IQ_F32)
+    assert iq.iq_scales_bytes(d) == 4
+    d = iq.make_desc("mxfp4", "block", 14336, 4096)
+    assert iq.iq_codes_bytes(d) == 14336 * 2048 and iq.iq_scales_bytes(d) == 14336 * 128
+    d = iq.make_desc("nvfp4", "block", 16384, 8192)
+    assert iq.iq_codes_bytes(d) == 16384 * 4096 and iq.iq_scales_bytes(d) == 16384 * 512
+    d = iq.make_desc("int4", "block", 28672, 8192)
+    assert iq.iq_codes_bytes(d) == 28672 * 4096 and iq.iq_scales_bytes(d) == 28672 * 64 * 2
+    assert iq.iq_workspace_bytes(d) >= 256
+    assert iq.iq_codes_bytes(iq.make_desc("mxfp4", "row", 4, 64)) == 0      # illegal pair
+    assert iq.iq_codes_bytes(iq.make_desc("int4", "block", 4, 96)) == 0     # 96 % 128
+
+
+FAKE = 0x10000  # a 256-byte aligned address that validation never dereferences
+
+
+def quant(iq, d, x=FAKE, codes=FAKE, scales=FAKE, gs=FAKE, stats=None, xhat=None, xdt=0, ws=FAKE):
+    return iq.iq_quantize(d, x, codes, scales, gs, stats, xhat, xdt, ws, None)
+
+
+def test_quantize_argument_errors(iq):
+    E, A, U = iq.IQ_EINVAL, iq.IQ_EALIGN, iq.IQ_EUNSUPPORTED
+    ok = dict(rows=4, cols=256)
+    assert quant(iq, iq.make_desc("mxfp4", "row", **ok)) == E              # MX is per-block only
+    assert quant(iq, iq.make_desc("e4m3", "block", **ok)) == E             # FP8 has no block variant
+    assert quant(iq, iq.IQDesc(9, 0, 1, 0, 4, 256, 256, 0, 0)) == E         # unknown format
+    assert quant(iq, iq.IQDesc(1, 1, 7, 0, 4, 256, 256, 0, 0)) == E         # unknown dtype
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 252)) == E              # cols % 8
+    assert quant(iq, iq.make_desc("mxfp4", "block", 4, 48)) == E            # cols % 32
+    assert quant(iq, iq.make_desc("nvfp4", "block", 4, 24)) == E            # cols % 16
+    assert quant(iq, iq.make_desc("int4", "block", 4, 192)) == E            # cols % 128
+    assert quant(iq, iq.make_desc("e4m3", "row", -1, 256)) == E
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256, ld=128)) == E      # ld < cols
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), x=None) == E
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), codes=None) == E
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), scales=None) == E
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), ws=None) == E
+    assert quant(iq, iq.make_desc("nvfp4", "block", 4, 256), gs=None) == E
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), xhat=FAKE, xdt=5) == E
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), x=FAKE + 8) == A
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256, ld=260)) == A     # 260 * 2 % 16
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256, iq.IQ_F32, ld=258)) == A
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), codes=FAKE + 4) == A
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), ws=FAKE + 128) == A
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), xhat=FAKE + 4) == A
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256), stats=FAKE + 4) == A
+    assert quant(iq, iq.make_desc("e4m3", "row", 4, 256, flags=1)) == U
+    assert quant(iq, iq.make_desc("e4m3", "row", 1 << 30, 1 << 20)) == U   # > 2^31 chunks
+
+
+def test_dequantize_and_amax_argument_errors(iq):
+    E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
+    d = iq.make_desc("nvfp4", "block", 4, 256)
+    assert iq.iq_dequantize(d, FAKE, FAKE, None, FAKE, 0, None) == E
+    assert iq.iq_dequantize(d, FAKE, FAKE, FAKE, FAKE, 3, None) == E
+    assert iq.iq_dequantize(d, FAKE + 2, FAKE, FAKE, FAKE, 0, None) == A
+    assert iq.iq_dequantize(iq.make_desc("mxfp4", "row", 4, 256), FAKE, FAKE, None, FAKE, 0, None) == E
+    assert iq.iq_dequantize(iq.make_desc("e4m3", "row", 0, 256), None, None, None, None, 0, None) == iq.IQ_OK
+    assert iq.iq_amax(iq.make_desc("e4m3", "tensor", 4, 256), FAKE, None, FAKE, None) == E
+    assert iq.iq_amax(iq.make_desc("e4m3", "tensor", 4, 256), FAKE + 2, FAKE, FAKE, None) == A
+    assert iq.iq_amax(iq.IQDesc(1, 0, 3, 0, 4, 256, 256, 0, 0), FAKE, FAKE, FAKE, None) == E
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import int_quantization_amd as m
+    with pytest.raises(OSError):
+        m._lib_backup = m._lib
+        try:
+            m._lib = None
+            m.load_library(str(tmp_path / "missing.so"))
+        finally:
+            m._lib = m._lib_backup

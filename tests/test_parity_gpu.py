@@ -1,0 +1,364 @@
+"""GPU parity: libiq (HIP, gfx950) against the CPU oracle, element by element.
+
+Codes, scales, the NVFP4 global scale and x^ must match bit for bit (any NaN
+matches any NaN); counts and the maximum error exactly; the summed
+statistics within 1e-6 relative.  Inputs come from the seeded generator in
+synth/ (shared by both sides); nothing here feeds GPU output to the oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from helpers import assert_bits_equal, assert_stats_match, to_device, widen
+
+pytestmark = pytest.mark.gpu
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+ALL = [("int8", "tensor"), ("e4m3", "tensor"), ("e5m2", "tensor"), ("int8", "row"), ("e4m3", "row"),
+       ("e5m2", "row"), ("mxfp4", "block"), ("nvfp4", "block"), ("int4", "block")]
+
+
+@pytest.fixture(scope="module")
+def iq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int_quantization_amd as m
+    m.load_library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def O():
+    from oracle import oracle
+    return oracle
+
+
+@pytest.fixture(scope="module")
+def S():
+    from synth import synth
+    return synth
+
+
+def run_gpu(iq, x_np, fmt, gran, cols=None, xhat="f32"):
+    import torch
+    x = to_device(x_np)
+    if cols is not None:
+        x = x[:, :cols]
+    xdt = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[xhat]
+    q = iq.quantize(x, fmt, gran, xhat_dtype=xdt)
+    torch.cuda.synchronize()
+    out = {"codes": q.codes.cpu().numpy(), "scales": q.scales.cpu().numpy(), "stats": q.stats(), "q": q}
+    if q.global_scale is not None:
+        out["global_scale"] = q.global_scale.cpu().numpy()
+    if q.xhat is not None:
+        out["xhat"] = (q.xhat.cpu().numpy() if q.xhat.dtype == torch.float32
+                       else q.xhat.cpu().view(torch.int16).numpy().view(np.uint16))
+    return out
+
+
+def compare(g, r, fmt, what, O=None, S=None, xhat="f32"):
+    assert_bits_equal(g["codes"], r["codes"], f"{what} codes")
+    gs = g["scales"]
+    if gs.dtype == np.int16:
+        gs = gs.view(np.uint16)
+    assert_bits_equal(gs, r["scales"], f"{what} scales")
+    if fmt == "nvfp4":
+        assert_bits_equal(g["global_scale"], r["global_scale"], f"{what} global scale")
+    if "xhat" in g and r.get("xhat") is not None:
+        want = r["xhat"]
+        if xhat == "bf16":
+            want = S.f32_to_bf16_bits(want)
+        assert_bits_equal(g["xhat"], want, f"{what} xhat")
+    assert_stats_match(g["stats"], r["stats"], what)
+
+
+def oracle_ref(O, x_np, fmt, gran, cols=None, want_xhat=True):
+    return O.quantize(x_np, fmt, gran, cols=cols, want_xhat=want_xhat, threads=THREADS)
+
+
+# ---- shapes spanning several tiles, ragged tails, padded rows -----------------
+SHAPES = [
+    (37, 8192, None),      # per-row: 4 chunks per thread
+    (5, 2072, None),       # per-row: 259 chunks, ragged over 256 threads
+    (3, 40000, None),      # per-row: long rows, two-pass kernel
+    (2100, 16, None),      # more rows than workgroups, 2 chunks per row
+    (33, 1024, 1056),      # padded rows (ld > cols), power-of-two chunks per row
+    (13, 384, 400),        # padded rows, non-power-of-two chunks per row
+    (1, 8192, None),
+]
+
+
+def make_input(S, dtype, rows, cols, ld, seed):
+    w = S.fill(rows, cols, dtype, sigma=1.0, outlier_axis=S.AXIS_COLS, outlier_frac=0.02,
+               outlier_factor=50.0, seed=seed, ld=ld or cols)
+    return w
+
+
+@pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_parity_shapes(iq, O, S, fmt, gran, dtype):
+    bs = O.block_size(fmt, gran)
+    for i, (rows, cols, ld) in enumerate(SHAPES):
+        if bs and cols % bs:
+            continue
+        x = make_input(S, dtype, rows, cols, ld, seed=100 + i)
+        g = run_gpu(iq, x, fmt, gran, cols=cols if ld else None)
+        r = oracle_ref(O, x, fmt, gran, cols=cols if ld else None)
+        compare(g, r, fmt, f"{fmt}/{gran}/{'bf16' if dtype else 'f32'} {rows}x{cols} ld={ld}", O)
+
+
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_parity_bf16_xhat(iq, O, S, fmt, gran):
+    x = make_input(S, 1, 64, 4096, None, seed=7)
+    g = run_gpu(iq, x, fmt, gran, xhat="bf16")
+    r = oracle_ref(O, x, fmt, gran)
+    compare(g, r, fmt, f"{fmt}/{gran} bf16 xhat", O, S, xhat="bf16")
+
+
+# ---- special values and degenerate units --------------------------------------
+def bf16_special_matrix(S, rows=16, cols=512, seed=3):
+    x = S.fill(rows, cols, 1, sigma=1.0, seed=seed)
+    rng = np.random.default_rng(seed)
+    x[0] = 0                                                       # all zero
+    x[1] = 0x8000                                                  # all -0
+    x[2] = rng.integers(1, 0x80, cols) | (rng.integers(0, 2, cols) << 15)   # BF16 subnormals
+    x[3] = S.f32_to_bf16_bits((rng.standard_normal(cols) * 1e-30).astype(np.float32))  # tiny scale
+    x[4] = S.f32_to_bf16_bits((rng.standard_normal(cols) * 1e30).astype(np.float32))   # huge values
+    x[5, ::37] = 0x7FC0                                            # NaN
+    x[6, ::41] = 0x7F80                                            # +Inf
+    x[6, 5::41] = 0xFF80                                           # -Inf
+    x[7, ::3] = 0x7F7F                                             # max finite
+    x[8, :] = 0x7FC0                                               # all NaN
+    x[9, 17] = 0xFFC1                                              # negative NaN with payload
+    x[10, :] = S.f32_to_bf16_bits((rng.standard_normal(cols) * 1e-38).astype(np.float32))
+    x[11, 3::7] = 0x8000
+    x[11, 4::7] = 0x0000
+    x[12, :] = S.f32_to_bf16_bits((rng.standard_normal(cols) * 2.0 ** -125).astype(np.float32))
+    x[13, 100:] = 0                                                # mostly zero
+    return x
+
+
+def f32_special_matrix(S, rows=16, cols=512, seed=4):
+    x = S.fill(rows, cols, 0, sigma=1.0, seed=seed)
+    rng = np.random.default_rng(seed)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2] = (rng.integers(1, 1 << 20, cols).astype(np.uint32) | (rng.integers(0, 2, cols).astype(np.uint32) << 31)).view(np.float32)
+    x[3] = (rng.standard_normal(cols) * 1e-30).astype(np.float32)
+    x[4] = (rng.standard_normal(cols) * 1e36).astype(np.float32)
+    x[5, ::37] = np.nan
+    x[6, ::41] = np.inf
+    x[6, 5::41] = -np.inf
+    x[7, ::3] = np.float32(3.4028235e38)
+    x[8, :] = np.nan
+    x[10, :] = (rng.standard_normal(cols) * 1e-41).astype(np.float32)
+    x[12, :] = (rng.standard_normal(cols) * 2.0 ** -126).astype(np.float32)
+    x[13, 100:] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_parity_special_values(iq, O, S, fmt, gran, dtype):
+    x = bf16_special_matrix(S) if dtype else f32_special_matrix(S)
+    if gran == "tensor" or fmt == "nvfp4":
+        # per-tensor scales: check with and without the non-finite rows
+        cases = [x, np.ascontiguousarray(np.delete(x, [5, 6, 8, 9], axis=0))]
+    else:
+        cases = [x]
+    for k, xc in enumerate(cases):
+        g = run_gpu(iq, xc, fmt, gran)
+        r = oracle_ref(O, xc, fmt, gran)
+        compare(g, r, fmt, f"{fmt}/{gran} special case {k}", O)
+
+
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_parity_ties(iq, O, S, fmt, gran):
+    """Inputs on the midpoints between grid values, where round-to-nearest-even decides."""
+    rows, cols = 4, 1024
+    x = np.zeros((rows, cols), np.float32)
+    rng = np.random.default_rng(5)
+    if fmt in ("int8",):
+        top, mids = 127.0, np.arange(-127, 127) + 0.5
+    elif fmt in ("e4m3", "e5m2"):
+        kind = O.K_E4M3 if fmt == "e4m3" else O.K_E5M2
+        vals = np.unique(O.fp_decode_array(kind, np.arange(0x7C if fmt == "e5m2" else 0x7F)))
+        mids = (vals[:-1] + vals[1:]) / 2
+        mids = np.concatenate([mids, -mids])
+        top = vals.max()
+    elif fmt == "int4":
+        top, mids = 7.0, np.arange(-7, 7) + 0.5
+    else:
+        vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+        mids = (vals[:-1] + vals[1:]) / 2
+        mids = np.concatenate([mids, -mids])
+        top = 6.0
+    for r in range(rows):
+        x[r] = rng.choice(mids, cols).astype(np.float32)
+        if fmt == "int4":
+            x[r, ::128] = top                    # every group's maximum gives s = 1
+        elif fmt == "mxfp4":
+            x[r, ::32] = 4.0                     # floor(log2 4) - 2 = 0: s = 1
+        elif fmt == "nvfp4":
+            x[r, ::16] = 6.0                     # block max 6
+        else:
+            x[r, 0] = top                        # alpha = top: s = 1
+    if fmt == "nvfp4":
+        x[0, 0] = 2688.0                         # s_global = 1, so t = 1 and s_nv = 1 elsewhere
+    for dtype in (0, 1):
+        xi = x if dtype == 0 else S.f32_to_bf16_bits(x)
+        g = run_gpu(iq, xi, fmt, gran)
+        rr = oracle_ref(O, xi, fmt, gran)
+        compare(g, rr, fmt, f"{fmt}/{gran} ties dtype {dtype}", O)
+
+
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_empty(iq, O, fmt, gran):
+    import torch
+    cols = 128
+    x = torch.zeros((0, cols), dtype=torch.bfloat16, device="cuda:0")
+    q = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32)
+    torch.cuda.synchronize()
+    st = q.stats()
+    assert st["n"] == 0 and st["sum_err2"] == 0.0 and st["n_saturated"] == 0
+    if gran == "tensor":
+        assert q.scales.cpu().item() == 0.0
+    if fmt == "nvfp4":
+        assert q.global_scale.cpu().item() == 0.0
+    d = iq.dequantize(q)
+    assert d.shape == (0, cols)
+
+
+def test_determinism(iq, S):
+    import torch
+    x = to_device(S.make("c4", nrows=512))
+    outs = []
+    for _ in range(2):
+        q = iq.quantize(x, "nvfp4", "block", xhat_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs.append((q.codes.cpu(), q.scales.cpu(), q.xhat.cpu(), q.stats()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][2].view(torch.int32), outs[1][2].view(torch.int32))
+    assert outs[0][3] == outs[1][3]
+
+
+# ---- dequantize (separate call) -------------------------------------------------
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_dequantize_parity(iq, O, S, fmt, gran):
+    import torch
+    x = make_input(S, 1, 48, 2048, None, seed=11)
+    q = iq.quantize(x_dev := to_device(x), fmt, gran, xhat_dtype=torch.float32)
+    for dt, odt in ((torch.float32, O.F32), (torch.bfloat16, O.BF16)):
+        d = iq.dequantize(q, dt)
+        torch.cuda.synchronize()
+        codes = q.codes.cpu().numpy()
+        scales = q.scales.cpu().numpy()
+        if scales.dtype == np.int16:
+            scales = scales.view(np.uint16)
+        gs = q.global_scale.cpu().numpy() if q.global_scale is not None else None
+        want = O.dequantize(codes, scales, fmt, gran, x.shape[0], x.shape[1], gs, odt)
+        got = d.cpu().numpy() if dt == torch.float32 else d.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert_bits_equal(got, want, f"{fmt}/{gran} dequantize {dt}")
+        if dt == torch.float32:
+            assert_bits_equal(got, q.xhat.cpu().numpy(), f"{fmt}/{gran} dequantize vs quantize x^")
+    del x_dev
+
+
+def test_amax(iq, O, S):
+    for dtype in (1, 0):
+        x = bf16_special_matrix(S) if dtype else f32_special_matrix(S)
+        a = iq.amax(to_device(x)).cpu().item()
+        assert np.float32(a) == np.float32(O.amax(x))
+
+
+# ---- division strategy: every BF16 input against many scales ---------------------
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "int8"])
+def test_bf16_division_sweep(iq, O, S, fmt):
+    """Rows [alpha, every BF16 value with |x| <= alpha]: the per-row scale is
+    alpha / FMAX, and every BF16 input passes the divide + cast path."""
+    allv = np.arange(0x10000, dtype=np.uint32)
+    fin = allv[((allv & 0x7FFF) < 0x7F80)].astype(np.uint16)
+    alphas = np.arange(0x0080, 0x7F80, 61, dtype=np.uint16)       # ~500 alphas over the normal range
+    mag = widen(fin)
+    cols = 66 * 1024
+    x = np.zeros((len(alphas), cols), np.uint16)
+    for i, a in enumerate(alphas):
+        av = widen(np.array([a], np.uint16))[0]
+        keep = fin[np.abs(mag) <= av]
+        row = np.concatenate([[a], keep])
+        x[i, :len(row)] = row
+    g = run_gpu(iq, x, fmt, "row", xhat=None)
+    r = O.quantize(x, fmt, "row", want_xhat=False, threads=THREADS)
+    assert_bits_equal(g["codes"], r["codes"], f"{fmt} sweep codes")
+    assert_bits_equal(g["scales"], r["scales"], f"{fmt} sweep scales")
+    assert_stats_match(g["stats"], r["stats"], f"{fmt} sweep")
+
+
+@pytest.mark.parametrize("fmt", ["int4", "nvfp4", "mxfp4"])
+def test_bf16_block_sweep(iq, O, S, fmt):
+    """Blocks whose maximum walks the BF16 range while the other elements take
+    every BF16 magnitude at or below it."""
+    B = {"int4": 128, "nvfp4": 16, "mxfp4": 32}[fmt]
+    rng = np.random.default_rng(17)
+    rows, cols = 256, 8192
+    nb = cols // B
+    tops = rng.integers(0x0080, 0x7F80, (rows, nb)).astype(np.uint32)
+    te = np.repeat(tops, B, axis=1)
+    mags = (rng.random((rows, cols)) * (te + 1)).astype(np.uint32)          # any BF16 magnitude <= top
+    signs = rng.integers(0, 2, (rows, cols)).astype(np.uint32) << 15
+    x = (np.minimum(mags, te) | signs).astype(np.uint16)
+    pos = rng.integers(0, B, (rows, nb)) + np.arange(nb) * B                 # one element per block = top
+    np.put_along_axis(x, pos, tops.astype(np.uint16), axis=1)
+    if fmt == "nvfp4":
+        x[0, 0] = 0x7F7F
+    g = run_gpu(iq, x, fmt, "block")
+    rr = oracle_ref(O, x, fmt, "block")
+    compare(g, rr, fmt, f"{fmt} block sweep", O)
+
+
+# ---- the five workloads at full size (the configuration the bench times) ----------
+FULL = [("c1", "int8", "tensor"), ("c1", "e4m3", "tensor"), ("c2", "e4m3", "row"), ("c2", "e5m2", "row"),
+        ("c3", "mxfp4", "block"), ("c4", "nvfp4", "block"), ("c5", "int4", "block")]
+
+
+@pytest.mark.parametrize("cfg,fmt,gran", FULL)
+def test_full_size_workloads(iq, O, S, cfg, fmt, gran):
+    x = S.make(cfg)
+    g = run_gpu(iq, x, fmt, gran, xhat=None)
+    r = O.quantize(x, fmt, gran, want_xhat=False, threads=THREADS)
+    compare(g, r, fmt, f"{cfg} {fmt}/{gran} full size", O)
+
+
+def test_stream_sampled_rows(iq, O, S):
+    """The 2 GiB streaming workload: every format on the GPU at full size,
+    oracle on sampled rows (given the oracle's own tensor absmax)."""
+    import torch
+    x = S.make("stream")
+    xd = to_device(x)
+    rows = x.shape[0]
+    sample = np.unique(np.concatenate([[0, 1, rows - 1], np.random.default_rng(1).integers(0, rows, 24)]))
+    G = O.amax(x)
+    for fmt, gran in S.WORKLOADS["stream"].formats:
+        q = iq.quantize(xd, fmt, gran, stats=True)
+        torch.cuda.synchronize()
+        codes = q.codes.cpu().numpy()
+        scales = q.scales.cpu().numpy()
+        if scales.dtype == np.int16:
+            scales = scales.view(np.uint16)
+        st = q.stats()
+        assert st["n"] == x.size and st["n_nonfinite"] == 0
+        for r0 in sample:
+            ref = O.quantize_rows(np.ascontiguousarray(x[r0:r0 + 1]), fmt, gran, 0, 1, G)
+            assert_bits_equal(codes[r0:r0 + 1], ref["codes"], f"stream {fmt}/{gran} row {r0} codes")
+            if gran == "row":
+                assert_bits_equal(scales[r0:r0 + 1], ref["scales"], f"stream {fmt} row {r0} scale")
+            elif gran == "tensor":
+                assert_bits_equal(scales, np.array([np.float32(G) / np.float32(O.QMAX[fmt])], np.float32),
+                                  f"stream {fmt} tensor scale")
+            else:
+                assert_bits_equal(scales[r0:r0 + 1], ref["scales"], f"stream {fmt} row {r0} scales")
+        del q
+    del xd
