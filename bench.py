@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, copy)")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per breakdown entry")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of graphs")
     return ap.parse_args()
 
 
@@ -222,51 +223,76 @@ def main():
     for f in fmts:
         qb, dq = W.bytes(*f)
         step_bytes += qb + dq
-    per_call = {f"{a}/{b}/{k}": [] for a, b in fmts for k in ("quantize", "dequantize")}
-    ev = []
 
-    def step(s, record):
-        i, j = s % NSETS, (s - 1) % NSETS
+    def step(i):
+        j = (i - 1) % NSETS
         for f in fmts:
-            if record:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                e[0].record(stream)
-                W.quant(*f, i)
-                e[1].record(stream)
-                W.dequant(*f, i, j)
-                e[2].record(stream)
-                ev.append((f, e))
-            else:
-                W.quant(*f, i)
-                W.dequant(*f, i, j)
+            W.quant(*f, i)
+            W.dequant(*f, i, j)
 
-    for s in range(args.warmup):
-        step(s, False)
+    for s in range(NSETS):   # eager warm-up: also fills the launch caches before capture
+        step(s)
+    torch.cuda.synchronize()
+    graphs = None
+    if not args.eager:
+        # One graph per buffer set (4 library calls, 6 kernels each); replaying
+        # them removes host launch overhead from the timed region.
+        graphs = []
+        for i in range(NSETS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(k):
+        if graphs is None:
+            step(k % NSETS)
+        else:
+            graphs[k % NSETS].replay()
+
+    for k in range(args.warmup):
+        run_step(k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.warmup, args.warmup + args.steps):
-        step(s, True)
+    for k in range(args.warmup, args.warmup + args.steps):
+        run_step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    for (a, b), e in ev:
-        per_call[f"{a}/{b}/quantize"].append(e[0].elapsed_time(e[1]) * 1e3)
-        per_call[f"{a}/{b}/dequantize"].append(e[1].elapsed_time(e[2]) * 1e3)
     value = step_bytes * args.steps / elapsed / 1e9
-    avg = {k: sum(v) / len(v) for k, v in per_call.items()}
 
+    # ---- per-call durations: graphs of 2*NSETS consecutive calls of one kind -------
+    calls = {}
+    per_call_graph = 2 * NSETS
+    for a, b in fmts:
+        for kind in ("quantize", "dequantize"):
+            def body():
+                for n in range(per_call_graph):
+                    if kind == "quantize":
+                        W.quant(a, b, n % NSETS)
+                    else:
+                        W.dequant(a, b, n % NSETS, (n + 1) % NSETS)
+            if graphs is None:
+                t = timed(body, 10, stream)
+            else:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    body()
+                g.replay()
+                t = timed(g.replay, 10, stream)
+            us = t["mean_us"] / per_call_graph
+            q, d = W.bytes(a, b)
+            calls[f"{a}/{b}/{kind}"] = {"avg_us": round(us, 2),
+                                        "GB/s": round((q if kind == "quantize" else d) / (us * 1e-6) / 1e9, 1)}
     qb, _ = W.bytes("e4m3", "row")
-    dom_us = avg["e4m3/row/quantize"]
+    dom_us = calls["e4m3/row/quantize"]["avg_us"]
     achieved = qb / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("c2_e4m3_row"),
-                "kernel": "iq_quantize E4M3 per-row (k_quant_row + stats finalize)",
-                "bytes_per_launch": qb, "avg_launch_us": round(dom_us, 2)}
-    calls = {k: {"avg_us": round(v, 2)} for k, v in avg.items()}
-    for a, b in fmts:
-        q, d = W.bytes(a, b)
-        calls[f"{a}/{b}/quantize"]["GB/s"] = round(q / (avg[f"{a}/{b}/quantize"] * 1e-6) / 1e9, 1)
-        calls[f"{a}/{b}/dequantize"]["GB/s"] = round(d / (avg[f"{a}/{b}/dequantize"] * 1e-6) / 1e9, 1)
-    del W
+                "kernel": "iq_quantize E4M3 per-row (k_quant_row + k_stats_finalize)",
+                "bytes_per_launch": qb, "avg_launch_us": dom_us,
+                "timing": "HIP events around a replayed graph of %d consecutive calls" % per_call_graph}
+    del graphs, W
     torch.cuda.empty_cache()
 
     extra = {"calls": calls}
@@ -282,10 +308,27 @@ def main():
         "config": {"workload": "activations BF16 8192x8192, N(0,1) with 0.5% outlier channels x200, seed 2; "
                                "per-row E4M3 and E5M2: quantize (+fused dequant + error stats) and dequantize "
                                "to BF16", "rows": 8192, "cols": 8192, "input": "bf16",
-                   "formats": ["e4m3/row", "e5m2/row"], "step_bytes": step_bytes, "buffer_sets": NSETS},
+                   "formats": ["e4m3/row", "e5m2/row"], "step_bytes": step_bytes, "buffer_sets": NSETS,
+                   "launch": "eager" if args.eager else "hip graph per step"},
         "roofline": roofline, "cpu_baseline": cpu, **extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_calls(body, n_calls, use_graph, reps, stream):
+    """Mean microseconds per call of `body` (which issues n_calls calls),
+    from HIP events around graph replays (or eager calls)."""
+    import torch
+    if not use_graph:
+        t = timed(body, reps, stream)
+        return t["mean_us"] / n_calls, t
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    t = timed(g.replay, reps, stream)
+    del g
+    return t["mean_us"] / n_calls, t
 
 
 def breakdown(args):
@@ -297,30 +340,29 @@ def breakdown(args):
         from synth import synth
         plan.append(("stream", list(synth.WORKLOADS["stream"].formats)))
     stream = torch.cuda.current_stream()
+    n = 2 * NSETS
     for name, fmts in plan:
         W = Workload(name, fmts)
         for fmt, gran in fmts:
-            k = [0]
-
             def q():
-                W.quant(fmt, gran, k[0] % NSETS)
-                k[0] += 1
+                for k in range(n):
+                    W.quant(fmt, gran, k % NSETS)
 
             def d():
-                W.dequant(fmt, gran, k[0] % NSETS, (k[0] + 1) % NSETS)
-                k[0] += 1
+                for k in range(n):
+                    W.dequant(fmt, gran, k % NSETS, (k + 1) % NSETS)
 
-            for _ in range(3):
-                q()
-            tq = timed(q, args.reps, stream)
-            td = timed(d, args.reps, stream)
+            q()
+            torch.cuda.synchronize()
+            uq, _ = time_calls(q, n, not args.eager, args.reps, stream)
+            ud, _ = time_calls(d, n, not args.eager, args.reps, stream)
             qb, dq = W.bytes(fmt, gran)
-            gq = qb / (tq["median_us"] * 1e-6) / 1e9
-            gd = dq / (td["median_us"] * 1e-6) / 1e9
+            gq = qb / (uq * 1e-6) / 1e9
+            gd = dq / (ud * 1e-6) / 1e9
             res[f"{name}:{fmt}/{gran}"] = {
                 "quantize_GBps": round(gq, 1), "quantize_frac_hbm": round(gq / HBM_PEAK_GBS, 4),
-                "quantize_us": round(tq["median_us"], 2), "quantize_p10_p90_us": [round(tq["p10_us"], 2), round(tq["p90_us"], 2)],
-                "dequantize_GBps": round(gd, 1), "dequantize_us": round(td["median_us"], 2), "bytes": qb}
+                "quantize_us": round(uq, 2), "dequantize_GBps": round(gd, 1), "dequantize_us": round(ud, 2),
+                "quantize_bytes": qb, "dequantize_bytes": dq}
         del W
         torch.cuda.empty_cache()
     return res

@@ -38,6 +38,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "iq_launch.h"
 
 namespace iqk {
@@ -51,6 +54,9 @@ typedef uint32_t u2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 
+__device__ __forceinline__ uint32_t umax16(uint32_t m) { return (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16); }
+__device__ __forceinline__ uint32_t umin16(uint32_t m) { return (m & 0xFFFFu) < (m >> 16) ? (m & 0xFFFFu) : (m >> 16); }
+
 // ---------------------------------------------------------------------------
 // Input chunks: 8 consecutive elements of one row.
 // ---------------------------------------------------------------------------
@@ -63,30 +69,51 @@ template <> struct Chunk<D_BF16> {
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     }
     __device__ __forceinline__ void zero() { w[0] = w[1] = w[2] = w[3] = 0; }
+    // From staged 16-byte words (word k at p[k * stride]).
+    __device__ __forceinline__ void set(const u4v* p, int stride) {
+        (void)stride;
+        const u4v v = p[0];
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
     // BF16 -> FP32 is exact: the BF16 bits are the top half of the FP32 word.
     __device__ __forceinline__ float get(int i) const {
         return (i & 1) ? as_f(w[i >> 1] & 0xFFFF0000u) : as_f(w[i >> 1] << 16);
     }
-    // Absmax over finite elements, on the integer image of |x|: for BF16 bits
-    // a = |x| in [0, 0x7FFF], t = a + 0x80 is negative as int16 exactly when
-    // x is Inf or NaN, so a signed 16-bit max skips them.
-    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& nf) const {
+    // Absmax on the integer image of |x| (BF16 bits a = |x| in [0, 0x7FFF],
+    // ordered like the magnitudes): m keeps the per-half maximum, z the
+    // per-half minimum.  A maximum >= 0x7F80 means an Inf or NaN is present
+    // (then absmax_finite recomputes the maximum over finite elements); a
+    // minimum of 0 means an exact zero is present.
+    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& z) const {
+        typedef unsigned short u2s __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            uint32_t t = (w[k] & 0x7FFF7FFFu) + 0x00800080u;
-            s2v a = __builtin_bit_cast(s2v, m), b = __builtin_bit_cast(s2v, t);
-            m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
-            nf |= t;
+            const u2s a = __builtin_bit_cast(u2s, w[k] & 0x7FFF7FFFu);
+            m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u2s, m), a));
+            z = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u2s, z), a));
         }
     }
-    // Fold the packed state into (bits of the finite absmax, nonfinite flag).
-    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t nf, uint32_t& bits, uint32_t& flag) {
-        int lo = (int)(int16_t)(m & 0xFFFFu), hi = (int)(int16_t)(m >> 16);
-        int mx = lo > hi ? lo : hi;
-        bits = mx >= 0x80 ? (uint32_t)(mx - 0x80) << 16 : 0u;
-        flag = (nf & 0x80008000u) ? 1u : 0u;
+    // Fold into (bits of the absmax, flags: bit 0 non-finite present, bit 1
+    // exact zero present).  With bit 0 set, bits is not meaningful.
+    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t z, uint32_t& bits, uint32_t& flag) {
+        const uint32_t mx = umax16(m), mn = umin16(z);
+        bits = mx << 16;
+        flag = (mx >= 0x7F80u ? 1u : 0u) | (mn == 0u ? 2u : 0u);
     }
-    static constexpr uint32_t kAbsInit = 0u;
+    // Maximum over the finite elements only: t = a + 0x80 is negative as
+    // int16 exactly for Inf and NaN, so a signed 16-bit max skips them.
+    __device__ __forceinline__ uint32_t absmax_finite() const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t t = (w[k] & 0x7FFF7FFFu) + 0x00800080u;
+            m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s2v, m), __builtin_bit_cast(s2v, t)));
+        }
+        const int lo = (int)(int16_t)(m & 0xFFFFu), hi = (int)(int16_t)(m >> 16);
+        const int mx = lo > hi ? lo : hi;
+        return mx >= 0x80 ? (uint32_t)(mx - 0x80) << 16 : 0u;
+    }
+    static constexpr uint32_t kMaxInit = 0u, kMinInit = 0xFFFFFFFFu;
 };
 
 template <> struct Chunk<D_F32> {
@@ -100,22 +127,83 @@ template <> struct Chunk<D_F32> {
 #pragma unroll
         for (int k = 0; k < 8; ++k) w[k] = 0;
     }
+    __device__ __forceinline__ void set(const u4v* p, int stride) {
+        const u4v a = p[0], b = p[stride];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
     __device__ __forceinline__ float get(int i) const { return as_f(w[i]); }
-    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& nf) const {
+    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& z) const {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            uint32_t a = w[k] & 0x7FFFFFFFu;
-            bool fin = a < 0x7F800000u;
-            m = (fin && a > m) ? a : m;
-            nf |= fin ? 0u : 1u;
+            const uint32_t a = w[k] & 0x7FFFFFFFu;
+            m = a > m ? a : m;
+            z = a < z ? a : z;
         }
     }
-    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t nf, uint32_t& bits, uint32_t& flag) {
+    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t z, uint32_t& bits, uint32_t& flag) {
         bits = m;
-        flag = nf ? 1u : 0u;
+        flag = (m >= 0x7F800000u ? 1u : 0u) | (z == 0u ? 2u : 0u);
     }
-    static constexpr uint32_t kAbsInit = 0u;
+    __device__ __forceinline__ uint32_t absmax_finite() const {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t a = w[k] & 0x7FFFFFFFu;
+            m = (a < 0x7F800000u && a > m) ? a : m;
+        }
+        return m;
+    }
+    static constexpr uint32_t kMaxInit = 0u, kMinInit = 0xFFFFFFFFu;
 };
+
+// ---------------------------------------------------------------------------
+// LDS staging.  A workgroup's staging area holds NW 16-byte words per thread,
+// word k of thread t at stage[k][t].  global_load_lds_dwordx4 copies one
+// word per lane from HBM into LDS without passing through VGPRs: a wave's
+// instruction lands its 64 lanes at consecutive words from the wave-uniform
+// base &stage[k][64 * wave].  Each lane later reads back only its own words,
+// so no barrier is needed between the copy and the read.  The kernels read
+// the current unit from LDS, then start the copy of their next unit into the
+// same words, and compute while that copy is in flight.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr unsigned kAuxNontemporal = 2;   // cache policy bits of the copy: streaming (nt)
+
+template <int NW> using Stage = u4v[NW][kThreads];
+
+__device__ __forceinline__ void dma_word(const void* src, u4v* wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)wave_base, 16, 0, kAuxNontemporal);
+}
+
+// The compiler does not track the copies' LDS writes against later LDS
+// reads, so both orderings are explicit:
+//   wait_staged:     the copies have landed (vmcnt(0)) before the unit is read;
+//   wait_lds_reads:  the reads have completed (lgkmcnt(0)) before the next
+//                    copies overwrite the same words.
+__device__ __forceinline__ void wait_staged() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+}
+
+template <int IN> struct ChunkWords { static constexpr int n = IN == D_BF16 ? 1 : 2; };
+
+// Start copying chunk `elem` (8 elements) of x into words [w0, w0 + n) of this thread.
+template <int IN, int NW>
+__device__ __forceinline__ void stage_chunk(Stage<NW>& st, int w0, const void* x, int64_t elem) {
+    const int wave = threadIdx.x >> 6;
+    const char* src = static_cast<const char*>(x) + elem * (IN == D_BF16 ? 2 : 4);
+#pragma unroll
+    for (int k = 0; k < ChunkWords<IN>::n; ++k) dma_word(src + 16 * k, &st[w0 + k][64 * wave]);
+}
+
+template <int IN, int NW>
+__device__ __forceinline__ void unstage_chunk(const Stage<NW>& st, int w0, Chunk<IN>& ch) {
+    ch.set(&st[w0][threadIdx.x], kThreads);
+}
 
 // ---------------------------------------------------------------------------
 // Cross-lane reductions.  DPP within rows of 16 lanes, shuffles across rows.
@@ -145,6 +233,18 @@ __device__ __forceinline__ void wave_reduce_max_or(uint32_t& m, uint32_t& f) {
     group_reduce<16>(m, f);
     m = umax(m, (uint32_t)__shfl_xor((int)m, 16)); f |= (uint32_t)__shfl_xor((int)f, 16);
     m = umax(m, (uint32_t)__shfl_xor((int)m, 32)); f |= (uint32_t)__shfl_xor((int)f, 32);
+}
+
+// Max / or over the 256 threads of a workgroup (4 waves, one LDS slot each).
+// Every thread returns the result; red must not be reused by the next call
+// before all threads passed this one (callers alternate two slots).
+__device__ __forceinline__ void row_reduce(uint32_t& m, uint32_t& f, uint32_t (&red)[4][2]) {
+    wave_reduce_max_or(m, f);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { red[wave][0] = m; red[wave][1] = f; }
+    __syncthreads();
+    m = umax(umax(red[0][0], red[1][0]), umax(red[2][0], red[3][0]));
+    f = red[0][1] | red[1][1] | red[2][1] | red[3][1];
 }
 
 // ---------------------------------------------------------------------------
@@ -179,7 +279,7 @@ struct Stats {
         fae += __builtin_fabsf(d);
         mae = __builtin_fmaxf(mae, __builtin_fabsf(d));
         nsat += __popcll(__ballot(__builtin_fabsf(v) > qmax));
-        nzf += __popcll(__ballot(x != 0.f && xh == 0.f));
+        nzf += __popcll(__ballot(x != 0.f) & __ballot(xh == 0.f));   // two compares into SGPR masks
     }
     // General case: non-finite inputs count but stay out of sums and maxima.
     __device__ __forceinline__ void add_slow(float x, float v, float xh, float qmax) {
@@ -194,19 +294,64 @@ struct Stats {
         nzf += __popcll(__ballot(fin && x != 0.f && xh == 0.f));
         nnf += __popcll(__ballot(!fin));
     }
-    // One chunk, called in wave-uniform control flow; slow_lane marks lanes
-    // whose unit needs the general accumulation (the whole wave then uses it).
-    __device__ __forceinline__ void add8(bool slow_lane, const float (&x)[8], const float (&v)[8],
-                                         const float (&h)[8], float qmax) {
+    // One chunk, called in wave-uniform control flow.
+    //   slow_lane  the lane's unit needs the general accumulation (the whole
+    //              wave then uses it for this chunk);
+    //   sat_lane   the lane's unit can contain saturated elements; when no
+    //              lane's can, the saturation compares are skipped;
+    //   saturation test: SAT_X ? |x| > thr : |v| > thr.
+    // Sum of squares of BF16 inputs: one v_dot2_f32_bf16 per pair of raw
+    // inputs (products of BF16 values are exact in FP32).
+    //   zero_lane  the lane's unit may hold exact zeros.  Zero inputs always
+    //              quantize to zero, so the flushed count is
+    //              #(x^ == 0) - #(x == 0), and the second term is only
+    //              counted when some lane's unit holds a zero.
+    template <int IN, bool SAT_X>
+    __device__ __forceinline__ void add8(const Chunk<IN>& ch, bool slow_lane, bool sat_lane, bool zero_lane,
+                                         const float (&x)[8], const float (&v)[8], const float (&h)[8], float thr) {
         if (__ballot(slow_lane) == 0) {
+            float d[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) add_fast(x[i], v[i], h[i], qmax);
+            for (int i = 0; i < 8; ++i) d[i] = x[i] - h[i];
+            if (IN == D_BF16) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                    const bf2 p = __builtin_bit_cast(bf2, ch.w[k]);
+                    fx2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, fx2, false);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) fx2 = __builtin_fmaf(x[i], x[i], fx2);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                fe2 = __builtin_fmaf(d[i], d[i], fe2);
+                fae += __builtin_fabsf(d[i]);
+                mae = __builtin_fmaxf(mae, __builtin_fabsf(d[i]));
+                nzf += __popcll(__ballot(h[i] == 0.f));
+            }
+            if (__ballot(zero_lane) != 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) nzf -= __popcll(__ballot(x[i] == 0.f));
+            }
+            if (__ballot(sat_lane) != 0) {
+                float t = thr;
+                asm volatile("" : "+v"(t));   // keep the compares inside this branch
+#pragma unroll
+                for (int i = 0; i < 8; ++i) nsat += __popcll(__ballot(__builtin_fabsf(SAT_X ? x[i] : v[i]) > t));
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) add_slow(x[i], v[i], h[i], qmax);
+            for (int i = 0; i < 8; ++i) add_slow(x[i], SAT_X ? x[i] : v[i], h[i], thr);
         }
     }
 };
+
+// Whether a unit with absmax A and scale s can hold elements with |x/s| > Q:
+// exactly when A > Q * s, whose sign the single rounding of fma(Q, s, -A)
+// preserves.
+__device__ __forceinline__ bool can_saturate(float A, float s, float Q) { return __builtin_fmaf(Q, s, -A) < 0.f; }
 
 // Reduce the workgroup's statistics and write its partial (thread 0).
 __device__ void write_partial(Stats& st, Partial* out) {
@@ -323,8 +468,8 @@ __device__ __forceinline__ void store_xhat(void* xhat, int dtype, int64_t elem, 
 // zeros); only lanes with `store` write 8 code bytes at codes8 and x^ in h.
 // ---------------------------------------------------------------------------
 template <int IN, int FMT, bool STATS>
-__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float s, float y, bool fast, bool store,
-                                                    uint8_t* codes8, float (&h)[8], Stats& st) {
+__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float alpha, float s, float y, bool fast,
+                                                    bool zeros, bool store, uint8_t* codes8, float (&h)[8], Stats& st) {
     constexpr float Q = Fmt<FMT>::qmax;
     float x[8], v[8];
 #pragma unroll
@@ -394,7 +539,7 @@ __device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float s
         u2v o = {w0, w1};
         __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(codes8));
     }
-    if (STATS) st.add8(!fast, x, v, h, Q);
+    if (STATS) st.add8<IN, false>(ch, !fast, !fast || can_saturate(alpha, s, Q), zeros, x, v, h, Q);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,49 +557,84 @@ struct RowArgs {
     Partial* partials;
 };
 
+template <int IN, int CPT>
+__device__ __forceinline__ void stage_row(Stage<CPT * ChunkWords<IN>::n>& st, const RowArgs& a, int32_t row) {
+    const int64_t base = (int64_t)row * a.ld;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        if (c < a.cpr) stage_chunk<IN, CPT * ChunkWords<IN>::n>(st, j * ChunkWords<IN>::n, a.x, base + (int64_t)c * kChunk);
+    }
+}
+
+template <int IN, int CPT>
+__device__ __forceinline__ void unstage_row(const Stage<CPT * ChunkWords<IN>::n>& st, const RowArgs& a,
+                                            Chunk<IN> (&ch)[CPT]) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        if ((int)threadIdx.x + j * kThreads < a.cpr) unstage_chunk<IN, CPT * ChunkWords<IN>::n>(st, j * ChunkWords<IN>::n, ch[j]);
+        else ch[j].zero();
+    }
+}
+
+// One row held in registers: absmax (lanes, then the four waves through
+// LDS), scale, cast, stores, statistics.
+template <int IN, int FMT, int CPT, bool STATS>
+__device__ __forceinline__ void quant_row(const Chunk<IN> (&ch)[CPT], const RowArgs& a, int32_t row,
+                                          uint32_t (&s_red)[2][4][2], int parity, Stats& st) {
+    const int tid = threadIdx.x;
+    const int64_t cols = (int64_t)a.cpr * kChunk;
+    uint32_t m = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) ch[j].absmax(m, z);
+    uint32_t bits, flag;
+    Chunk<IN>::absmax_finish(m, z, bits, flag);
+    row_reduce(bits, flag, s_red[parity]);
+    if (flag & 1u) {   // the row holds Inf or NaN: absmax over its finite elements
+        uint32_t f = 0, unused = 0;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) f = umax(f, ch[j].absmax_finite());
+        row_reduce(f, unused, s_red[parity ^ 1]);
+        bits = f;
+    }
+    const float alpha = as_f(bits);
+    const float s = alpha / Fmt<FMT>::qmax;
+    if (tid == 0) a.scales[row] = s;
+    // fast: finite row with alpha in [2^-40, 2^60] (so s >= 2^-64)
+    const bool fast = (flag & 1u) == 0 && stat_range(alpha);
+    const float y = fast ? 1.0f / s : 0.f;
+    uint8_t* crow = a.codes + (int64_t)row * cols;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + j * kThreads;
+        const bool valid = c < a.cpr;
+        float h[8];
+        quant_chunk_uniform<IN, FMT, STATS>(ch[j], alpha, s, y, fast, (flag & 2u) != 0, valid,
+                                            crow + (int64_t)c * kChunk, h, st);
+        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
+    }
+    if (STATS) st.fold();
+}
+
+// Per-row INT8 / FP8: a workgroup owns one row at a time and keeps it in
+// registers between the absmax and the cast (CPT chunks per thread).  The
+// next row streams into LDS while the current one is reduced, cast and stored.
 template <int IN, int FMT, int CPT, bool STATS>
 __global__ __launch_bounds__(kThreads) void k_quant_row(RowArgs a) {
     __shared__ uint32_t s_red[2][4][2];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int64_t cols = (int64_t)a.cpr * kChunk;
+    __shared__ Stage<CPT * ChunkWords<IN>::n> stage;
     Stats st;
+    const int32_t G = gridDim.x;
     int parity = 0;
-    for (int32_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
+    int32_t row = blockIdx.x;
+    if (row < a.rows) stage_row<IN, CPT>(stage, a, row);
+    for (; row < a.rows; row += G, parity ^= 1) {
         Chunk<IN> ch[CPT];
-        const void* xrow = a.x;
-        const int64_t base = (int64_t)row * a.ld;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            int c = tid + j * kThreads;
-            if (c < a.cpr) ch[j].load(xrow, base + (int64_t)c * kChunk);
-            else ch[j].zero();
-        }
-        uint32_t m = Chunk<IN>::kAbsInit, nf = 0;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) ch[j].absmax(m, nf);
-        uint32_t bits, flag;
-        Chunk<IN>::absmax_finish(m, nf, bits, flag);
-        wave_reduce_max_or(bits, flag);
-        if (lane == 0) { s_red[parity][wave][0] = bits; s_red[parity][wave][1] = flag; }
-        __syncthreads();
-        bits = umax(umax(s_red[parity][0][0], s_red[parity][1][0]), umax(s_red[parity][2][0], s_red[parity][3][0]));
-        flag = s_red[parity][0][1] | s_red[parity][1][1] | s_red[parity][2][1] | s_red[parity][3][1];
-        const float alpha = as_f(bits);
-        const float s = alpha / Fmt<FMT>::qmax;
-        if (tid == 0) a.scales[row] = s;
-        // fast: finite row with alpha in [2^-40, 2^60] (so s >= 2^-64)
-        const bool fast = flag == 0 && stat_range(alpha);
-        const float y = fast ? 1.0f / s : 0.f;
-        uint8_t* crow = a.codes + (int64_t)row * cols;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int c = tid + j * kThreads;
-            const bool valid = c < a.cpr;
-            float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, valid, crow + (int64_t)c * kChunk, h, st);
-            if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
-        }
-        if (STATS) st.fold();
+        wait_staged();
+        unstage_row<IN, CPT>(stage, a, ch);
+        wait_lds_reads();
+        if (row + G < a.rows) stage_row<IN, CPT>(stage, a, row + G);
+        quant_row<IN, FMT, CPT, STATS>(ch, a, row, s_red, parity, st);
     }
     if (STATS) write_partial(st, a.partials);
 }
@@ -464,29 +644,37 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(RowArgs a) {
 template <int IN, int FMT, bool STATS>
 __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
     __shared__ uint32_t s_red[2][4][2];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int64_t cols = (int64_t)a.cpr * kChunk;
     Stats st;
     int parity = 0;
     for (int32_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
         const int64_t base = (int64_t)row * a.ld;
-        uint32_t m = Chunk<IN>::kAbsInit, nf = 0;
+        uint32_t m = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
         for (int c = tid; c < a.cpr; c += kThreads) {
             Chunk<IN> ch;
             ch.load(a.x, base + (int64_t)c * kChunk);
-            ch.absmax(m, nf);
+            ch.absmax(m, z);
         }
         uint32_t bits, flag;
-        Chunk<IN>::absmax_finish(m, nf, bits, flag);
-        wave_reduce_max_or(bits, flag);
-        if (lane == 0) { s_red[parity][wave][0] = bits; s_red[parity][wave][1] = flag; }
-        __syncthreads();
-        bits = umax(umax(s_red[parity][0][0], s_red[parity][1][0]), umax(s_red[parity][2][0], s_red[parity][3][0]));
-        flag = s_red[parity][0][1] | s_red[parity][1][1] | s_red[parity][2][1] | s_red[parity][3][1];
+        Chunk<IN>::absmax_finish(m, z, bits, flag);
+        row_reduce(bits, flag, s_red[parity]);
+        if (flag & 1u) {   // Inf or NaN in the row: another pass for the finite absmax
+            uint32_t f = 0, unused = 0;
+            for (int c = tid; c < a.cpr; c += kThreads) {
+                Chunk<IN> ch;
+                ch.load(a.x, base + (int64_t)c * kChunk);
+                f = umax(f, ch.absmax_finite());
+            }
+            row_reduce(f, unused, s_red[parity ^ 1]);
+            bits = f;
+        }
+        // lanes past the row end carry zero chunks: count them as zeros too
+        const bool zeros = (flag & 2u) != 0 || (a.cpr % kThreads) != 0;
         const float alpha = as_f(bits);
         const float s = alpha / Fmt<FMT>::qmax;
         if (tid == 0) a.scales[row] = s;
-        const bool fast = flag == 0 && stat_range(alpha);
+        const bool fast = (flag & 1u) == 0 && stat_range(alpha);
         const float y = fast ? 1.0f / s : 0.f;
         uint8_t* crow = a.codes + (int64_t)row * cols;
         // uniform trip count: lanes past the row end carry a zero chunk
@@ -497,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
             if (valid) ch.load(a.x, base + (int64_t)c * kChunk);
             else ch.zero();
             float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch, s, y, fast, valid, crow + (int64_t)c * kChunk, h, st);
+            quant_chunk_uniform<IN, FMT, STATS>(ch, alpha, s, y, fast, zeros, valid, crow + (int64_t)c * kChunk, h, st);
             if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
             if (STATS) st.fold();
         }
@@ -537,13 +725,26 @@ struct FlatArgs {
 // the tensor carry a zero chunk, `valid` false); only stores are predicated,
 // and the statistics are accumulated in wave-uniform control flow.
 
+// Absmax of a block spread over G lanes (G = 2, 4, 16): bits of the finite
+// maximum and the flags of absmax_finish, on every lane of the group.
+template <int IN, int G>
+__device__ __forceinline__ void unit_absmax(const Chunk<IN>& ch, uint32_t& bits, uint32_t& flag) {
+    uint32_t m = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
+    ch.absmax(m, z);
+    Chunk<IN>::absmax_finish(m, z, bits, flag);
+    group_reduce<G>(bits, flag);
+    if (__ballot(flag & 1u) != 0) {   // some block of the wave holds Inf or NaN
+        uint32_t f = ch.absmax_finite(), unused = 0;
+        group_reduce<G>(f, unused);
+        if (flag & 1u) bits = f;
+    }
+}
+
 // MXFP4: blocks of 32 = 4 chunks = 4 lanes.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    uint32_t m = Chunk<IN>::kAbsInit, nf = 0, bits, flag;
-    ch.absmax(m, nf);
-    Chunk<IN>::absmax_finish(m, nf, bits, flag);
-    group_reduce<4>(bits, flag);
+    uint32_t bits, flag;
+    unit_absmax<IN, 4>(ch, bits, flag);
     int E = 0;
     if (bits) {
         int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
@@ -560,7 +761,7 @@ __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, 
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
-    if (flag) {
+    if (flag & 1u) {
         // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -577,12 +778,9 @@ __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, 
     }
     if (STATS) {
         // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
-        // when |x| > 6 * 2^(E-127) (both sides are exact near 6).  v carries
-        // 7 for saturated elements and 0 otherwise (NaN never saturates).
+        // when |x| > 6 * 2^(E-127) (both sides are exact near 6).
         const float thr = 6.0f * sc;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_fabsf(x[i]) > thr ? 7.f : 0.f;
-        st.add8(flag || !stat_range(as_f(bits)), x, v, h, 6.f);
+        st.add8<IN, true>(ch, (flag & 1u) || !stat_range(as_f(bits)), as_f(bits) > thr, (flag & 2u) != 0, x, v, h, thr);
     }
 }
 
@@ -596,10 +794,8 @@ __device__ __forceinline__ uint32_t e4m3_ceil(float t) {
 // NVFP4: blocks of 16 = 2 chunks = 2 lanes.
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, bool valid, float s_g, const FlatArgs& a, Stats& st) {
-    uint32_t m = Chunk<IN>::kAbsInit, nf = 0, bits, flag;
-    ch.absmax(m, nf);
-    Chunk<IN>::absmax_finish(m, nf, bits, flag);
-    group_reduce<2>(bits, flag);
+    uint32_t bits, flag;
+    unit_absmax<IN, 2>(ch, bits, flag);
     uint32_t sb = 0;
     float s_nv = 0.f;
     if (s_g != 0.f) {
@@ -608,7 +804,7 @@ __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, 
         s_nv = s_g * e4m3_value(sb);
     }
     if (valid && (g & 1u) == 0) static_cast<uint8_t*>(a.scales)[g >> 1] = (uint8_t)sb;
-    const bool fast = !flag && s_nv >= kTinyScale && stat_range(as_f(bits));
+    const bool fast = !(flag & 1u) && s_nv >= kTinyScale && stat_range(as_f(bits));
     float x[8], v[8], h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
@@ -641,16 +837,14 @@ __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, 
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
         if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
     }
-    if (STATS) st.add8(!fast, x, v, h, 6.f);
+    if (STATS) st.add8<IN, false>(ch, !fast, !fast || can_saturate(as_f(bits), s_nv, 6.f), (flag & 2u) != 0, x, v, h, 6.f);
 }
 
 // INT4: groups of 128 = 16 chunks = 16 lanes; FP16 scale fp16(A / 7), saturated.
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    uint32_t m = Chunk<IN>::kAbsInit, nf = 0, bits, flag;
-    ch.absmax(m, nf);
-    Chunk<IN>::absmax_finish(m, nf, bits, flag);
-    group_reduce<16>(bits, flag);
+    uint32_t bits, flag;
+    unit_absmax<IN, 16>(ch, bits, flag);
     const float s32 = as_f(bits) / 7.0f;
     _Float16 hs = (_Float16)s32;                       // RNE
     uint16_t s16 = s32 > 65504.f ? (uint16_t)0x7BFF : __builtin_bit_cast(uint16_t, hs);
@@ -658,7 +852,7 @@ __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g
     if (valid && (g & 15u) == 0) static_cast<uint16_t*>(a.scales)[g >> 4] = s16;
     // fast: finite inputs and a normal, unsaturated FP16 scale keep |x/sf| < 7.5
     // (and put A = 7 sf inside the FP32 statistics range)
-    const bool fast = !flag && sf >= 0x1p-14f && s32 <= 65504.f;
+    const bool fast = !(flag & 1u) && sf >= 0x1p-14f && s32 <= 65504.f;
     float x[8], v[8], h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
@@ -686,7 +880,7 @@ __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
         if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
     }
-    if (STATS) st.add8(!fast, x, v, h, 7.f);
+    if (STATS) st.add8<IN, false>(ch, !fast, !fast || can_saturate(as_f(bits), sf, 7.f), (flag & 2u) != 0, x, v, h, 7.f);
 }
 
 template <int IN, int FMT, bool STATS>
@@ -694,24 +888,39 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
     // Per-tensor quantities from the absmax pre-pass (uniform over the grid).
-    float s = 0.f, y = 0.f;
+    float s = 0.f, y = 0.f, alpha = 0.f;
     bool fast = false;
     if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2 || FMT == F_NVFP4) {
         s = a.info->scale;
+        alpha = as_f(a.info->amax_bits);
         fast = a.info->nonfinite == 0 && stat_range(as_f(a.info->amax_bits));
         if (fast && FMT != F_NVFP4) y = 1.0f / s;
     }
+    // The next tile streams into LDS while the current one is processed.
+    constexpr int NW = kTileChunksPerThread * ChunkWords<IN>::n;
+    __shared__ Stage<NW> stage;
+    auto stage_tile = [&](uint32_t tile) {
+#pragma unroll
+        for (int j = 0; j < kTileChunksPerThread; ++j) {
+            const uint32_t g = tile * kTileChunks + j * kThreads + threadIdx.x;
+            if (g < a.geo.nchunks) stage_chunk<IN, NW>(stage, j * ChunkWords<IN>::n, a.geo.x, a.geo.elem(g));
+        }
+    };
+    if (blockIdx.x < ntiles) stage_tile(blockIdx.x);
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         Chunk<IN> ch[kTileChunksPerThread];
         uint32_t g[kTileChunksPerThread];
         bool valid[kTileChunksPerThread];
+        wait_staged();
 #pragma unroll
         for (int j = 0; j < kTileChunksPerThread; ++j) {
             g[j] = tile * kTileChunks + j * kThreads + threadIdx.x;
             valid[j] = g[j] < a.geo.nchunks;
-            if (valid[j]) ch[j].load(a.geo.x, a.geo.elem(g[j]));
+            if (valid[j]) unstage_chunk<IN, NW>(stage, j * ChunkWords<IN>::n, ch[j]);
             else ch[j].zero();
         }
+        wait_lds_reads();
+        if (tile + gridDim.x < ntiles) stage_tile(tile + gridDim.x);
 #pragma unroll
         for (int j = 0; j < kTileChunksPerThread; ++j) {
             if (FMT == F_MXFP4) {
@@ -722,7 +931,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
                 quant_chunk_int4<IN, STATS>(ch[j], g[j], valid[j], a, st);
             } else {
                 float h[8];
-                quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, valid[j], a.codes + (int64_t)g[j] * kChunk, h, st);
+                quant_chunk_uniform<IN, FMT, STATS>(ch[j], alpha, s, y, fast, true, valid[j],
+                                                    a.codes + (int64_t)g[j] * kChunk, h, st);
                 if (a.xhat && valid[j]) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g[j] * kChunk, h);
             }
         }
@@ -738,7 +948,7 @@ template <int IN>
 __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* partials) {
     __shared__ uint32_t s_red[4][2];
     const uint32_t ntiles = (geo.nchunks + kTileChunks - 1) / kTileChunks;
-    uint32_t m = Chunk<IN>::kAbsInit, nf = 0;
+    uint32_t m = 0, raw = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         Chunk<IN> ch[kTileChunksPerThread];
 #pragma unroll
@@ -748,10 +958,14 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* parti
             else ch[j].zero();
         }
 #pragma unroll
-        for (int j = 0; j < kTileChunksPerThread; ++j) ch[j].absmax(m, nf);
+        for (int j = 0; j < kTileChunksPerThread; ++j) {
+            m = umax(m, ch[j].absmax_finite());
+            ch[j].absmax(raw, z);
+        }
     }
-    uint32_t bits, flag;
-    Chunk<IN>::absmax_finish(m, nf, bits, flag);
+    uint32_t bits = m, flag, unused;
+    Chunk<IN>::absmax_finish(raw, z, unused, flag);
+    flag &= 1u;
     wave_reduce_max_or(bits, flag);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) { s_red[wave][0] = bits; s_red[wave][1] = flag; }
@@ -795,35 +1009,46 @@ struct StatsOut {   // mirrors iq_stats
     uint32_t reserved;
 };
 
-__global__ __launch_bounds__(kThreads) void k_stats_finalize(const Partial* p, int n, uint64_t nelem, StatsOut* out) {
-    __shared__ double s_d[kThreads][3];
-    __shared__ float s_m[kThreads];
-    __shared__ uint64_t s_c[kThreads][3];
-    double a = 0, b = 0, c = 0;
-    float m = 0.f;
-    uint64_t c0 = 0, c1 = 0, c2 = 0;
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        a += p[i].sum_x2; b += p[i].sum_err2; c += p[i].sum_abs_err;
-        m = __builtin_fmaxf(m, p[i].max_abs_err);
-        c0 += p[i].n_saturated; c1 += p[i].n_zero_flush; c2 += p[i].n_nonfinite;
-    }
+constexpr int kFinThreads = 1024;
+static_assert(kMaxGrid <= 2 * kFinThreads, "finalize covers two partials per thread");
+
+__global__ __launch_bounds__(kFinThreads) void k_stats_finalize(const Partial* p, int n, uint64_t nelem, StatsOut* out) {
+    __shared__ double s_d[kFinThreads / 64][3];
+    __shared__ float s_m[kFinThreads / 64];
+    __shared__ uint64_t s_c[kFinThreads / 64][3];
     const int t = threadIdx.x;
-    s_d[t][0] = a; s_d[t][1] = b; s_d[t][2] = c; s_m[t] = m;
-    s_c[t][0] = c0; s_c[t][1] = c1; s_c[t][2] = c2;
-    __syncthreads();
-    for (int w = kThreads / 2; w >= 1; w >>= 1) {
-        if (t < w) {
-            s_d[t][0] += s_d[t + w][0]; s_d[t][1] += s_d[t + w][1]; s_d[t][2] += s_d[t + w][2];
-            s_m[t] = __builtin_fmaxf(s_m[t], s_m[t + w]);
-            s_c[t][0] += s_c[t + w][0]; s_c[t][1] += s_c[t + w][1]; s_c[t][2] += s_c[t + w][2];
-        }
-        __syncthreads();
+    // Two partials per thread, both loads issued before use; fixed order.
+    Partial z = {};
+    const Partial a0 = t < n ? p[t] : z;
+    const Partial a1 = t + kFinThreads < n ? p[t + kFinThreads] : z;
+    double a = a0.sum_x2 + a1.sum_x2, b = a0.sum_err2 + a1.sum_err2, c = a0.sum_abs_err + a1.sum_abs_err;
+    float m = __builtin_fmaxf(a0.max_abs_err, a1.max_abs_err);
+    uint64_t c0 = (uint64_t)a0.n_saturated + a1.n_saturated;
+    uint64_t c1 = (uint64_t)a0.n_zero_flush + a1.n_zero_flush;
+    uint64_t c2 = (uint64_t)a0.n_nonfinite + a1.n_nonfinite;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        a += __shfl_xor(a, o); b += __shfl_xor(b, o); c += __shfl_xor(c, o);
+        m = __builtin_fmaxf(m, __shfl_xor(m, o));
+        c0 += (uint64_t)__shfl_xor((unsigned long long)c0, o);
+        c1 += (uint64_t)__shfl_xor((unsigned long long)c1, o);
+        c2 += (uint64_t)__shfl_xor((unsigned long long)c2, o);
     }
+    const int w = t >> 6;
+    if ((t & 63) == 0) {
+        s_d[w][0] = a; s_d[w][1] = b; s_d[w][2] = c; s_m[w] = m;
+        s_c[w][0] = c0; s_c[w][1] = c1; s_c[w][2] = c2;
+    }
+    __syncthreads();
     if (t == 0) {
         StatsOut o;
-        o.n = nelem; o.n_saturated = s_c[0][0]; o.n_zero_flush = s_c[0][1]; o.n_nonfinite = s_c[0][2];
-        o.sum_x2 = s_d[0][0]; o.sum_err2 = s_d[0][1]; o.sum_abs_err = s_d[0][2];
-        o.max_abs_err = s_m[0]; o.reserved = 0;
+        o.n = nelem; o.n_saturated = 0; o.n_zero_flush = 0; o.n_nonfinite = 0;
+        o.sum_x2 = 0; o.sum_err2 = 0; o.sum_abs_err = 0; o.max_abs_err = 0.f; o.reserved = 0;
+        for (int k = 0; k < kFinThreads / 64; ++k) {
+            o.sum_x2 += s_d[k][0]; o.sum_err2 += s_d[k][1]; o.sum_abs_err += s_d[k][2];
+            o.max_abs_err = __builtin_fmaxf(o.max_abs_err, s_m[k]);
+            o.n_saturated += s_c[k][0]; o.n_zero_flush += s_c[k][1]; o.n_nonfinite += s_c[k][2];
+        }
         *out = o;
     }
 }
@@ -927,63 +1152,103 @@ FlatGeom make_geom(const void* x, int64_t rows, int64_t cols, int64_t ld) {
     return g;
 }
 
-int flat_grid(uint32_t nchunks) {
-    uint32_t tiles = (nchunks + kTileChunks - 1) / kTileChunks;
-    return (int)(tiles < (uint32_t)kMaxGrid ? (tiles ? tiles : 1) : kMaxGrid);
+// Workgroups that fit on the device at once for a kernel (occupancy x CUs),
+// capped by the partial slots of the workspace.  Persistent kernels launch
+// at most this many, so no workgroup waits for a second wave of residency.
+// Cached per (kernel, device); the cache is shared by host threads.
+int resident_slots(const void* kernel, int threads) {
+    static std::mutex mu;
+    static std::unordered_map<uint64_t, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return kMaxGrid;
+    const uint64_t key = reinterpret_cast<uint64_t>(kernel) * 64u + (uint64_t)dev;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || per <= 0) per = 1;
+    int slots = per * cus;
+    if (slots > kMaxGrid) slots = kMaxGrid;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[key] = slots;
+    return slots;
 }
+
+template <typename K> int grid_for(K kernel, uint64_t units) {
+    const int slots = resident_slots(reinterpret_cast<const void*>(kernel), kThreads);
+    if (units == 0) return 1;
+    return units < (uint64_t)slots ? (int)units : slots;
+}
+
+uint32_t tiles_of(uint32_t nchunks) { return (nchunks + kTileChunks - 1) / kTileChunks; }
 
 template <int IN, int FMT, bool STATS>
-hipError_t launch_row_t(const RowArgs& r, int grid, int cpt, hipStream_t s) {
+hipError_t launch_row_t(const RowArgs& r, int cpt, int& grid, hipStream_t s) {
+    const uint64_t rows = (uint64_t)r.rows;
     switch (cpt) {
-    case 1: k_quant_row<IN, FMT, 1, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    case 2: k_quant_row<IN, FMT, 2, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    case 4: k_quant_row<IN, FMT, 4, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    case 8: k_quant_row<IN, FMT, 8, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    default: k_quant_row_long<IN, FMT, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 1: grid = grid_for(k_quant_row<IN, FMT, 1, STATS>, rows); k_quant_row<IN, FMT, 1, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 2: grid = grid_for(k_quant_row<IN, FMT, 2, STATS>, rows); k_quant_row<IN, FMT, 2, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 4: grid = grid_for(k_quant_row<IN, FMT, 4, STATS>, rows); k_quant_row<IN, FMT, 4, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    case 8: grid = grid_for(k_quant_row<IN, FMT, 8, STATS>, rows); k_quant_row<IN, FMT, 8, STATS><<<grid, kThreads, 0, s>>>(r); break;
+    default: grid = grid_for(k_quant_row_long<IN, FMT, STATS>, rows); k_quant_row_long<IN, FMT, STATS><<<grid, kThreads, 0, s>>>(r); break;
     }
     return hipGetLastError();
 }
 
 template <int IN, int FMT>
-hipError_t launch_row(const RowArgs& r, int grid, int cpt, bool stats, hipStream_t s) {
-    return stats ? launch_row_t<IN, FMT, true>(r, grid, cpt, s) : launch_row_t<IN, FMT, false>(r, grid, cpt, s);
+hipError_t launch_row(const RowArgs& r, int cpt, bool stats, int& grid, hipStream_t s) {
+    return stats ? launch_row_t<IN, FMT, true>(r, cpt, grid, s) : launch_row_t<IN, FMT, false>(r, cpt, grid, s);
 }
 
 template <int IN, int FMT>
-hipError_t launch_flat(const FlatArgs& f, int grid, bool stats, hipStream_t s) {
-    if (stats) k_quant_flat<IN, FMT, true><<<grid, kThreads, 0, s>>>(f);
-    else k_quant_flat<IN, FMT, false><<<grid, kThreads, 0, s>>>(f);
+hipError_t launch_flat(const FlatArgs& f, bool stats, int& grid, hipStream_t s) {
+    const uint64_t tiles = tiles_of(f.geo.nchunks);
+    if (stats) {
+        grid = grid_for(k_quant_flat<IN, FMT, true>, tiles);
+        k_quant_flat<IN, FMT, true><<<grid, kThreads, 0, s>>>(f);
+    } else {
+        grid = grid_for(k_quant_flat<IN, FMT, false>, tiles);
+        k_quant_flat<IN, FMT, false><<<grid, kThreads, 0, s>>>(f);
+    }
     return hipGetLastError();
 }
 
 template <int IN>
-hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, int grid, bool stats, hipStream_t s) {
+hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, bool stats, int& grid, hipStream_t s) {
     switch (fmt) {
-    case F_INT8: return launch_flat<IN, F_INT8>(f, grid, stats, s);
-    case F_E4M3: return launch_flat<IN, F_E4M3>(f, grid, stats, s);
-    case F_E5M2: return launch_flat<IN, F_E5M2>(f, grid, stats, s);
-    case F_MXFP4: return launch_flat<IN, F_MXFP4>(f, grid, stats, s);
-    case F_NVFP4: return launch_flat<IN, F_NVFP4>(f, grid, stats, s);
-    default: return launch_flat<IN, F_INT4>(f, grid, stats, s);
+    case F_INT8: return launch_flat<IN, F_INT8>(f, stats, grid, s);
+    case F_E4M3: return launch_flat<IN, F_E4M3>(f, stats, grid, s);
+    case F_E5M2: return launch_flat<IN, F_E5M2>(f, stats, grid, s);
+    case F_MXFP4: return launch_flat<IN, F_MXFP4>(f, stats, grid, s);
+    case F_NVFP4: return launch_flat<IN, F_NVFP4>(f, stats, grid, s);
+    default: return launch_flat<IN, F_INT4>(f, stats, grid, s);
     }
 }
 
 template <int IN>
-hipError_t launch_row_fmt(int fmt, const RowArgs& r, int grid, int cpt, bool stats, hipStream_t s) {
+hipError_t launch_row_fmt(int fmt, const RowArgs& r, int cpt, bool stats, int& grid, hipStream_t s) {
     switch (fmt) {
-    case F_INT8: return launch_row<IN, F_INT8>(r, grid, cpt, stats, s);
-    case F_E4M3: return launch_row<IN, F_E4M3>(r, grid, cpt, stats, s);
-    default: return launch_row<IN, F_E5M2>(r, grid, cpt, stats, s);
+    case F_INT8: return launch_row<IN, F_INT8>(r, cpt, stats, grid, s);
+    case F_E4M3: return launch_row<IN, F_E4M3>(r, cpt, stats, grid, s);
+    default: return launch_row<IN, F_E5M2>(r, cpt, stats, grid, s);
     }
 }
 
 hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, float qdiv, TensorInfo* info,
                             float* scale_out, float* amax_out, hipStream_t s) {
     uint32_t* part = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxOff);
-    const int grid = flat_grid(geo.nchunks);
+    int grid = 0;
     if (geo.nchunks) {
-        if (in_dtype == D_BF16) k_amax<D_BF16><<<grid, kThreads, 0, s>>>(geo, part);
-        else k_amax<D_F32><<<grid, kThreads, 0, s>>>(geo, part);
+        if (in_dtype == D_BF16) {
+            grid = grid_for(k_amax<D_BF16>, tiles_of(geo.nchunks));
+            k_amax<D_BF16><<<grid, kThreads, 0, s>>>(geo, part);
+        } else {
+            grid = grid_for(k_amax<D_F32>, tiles_of(geo.nchunks));
+            k_amax<D_F32><<<grid, kThreads, 0, s>>>(geo, part);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1010,12 +1275,9 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         r.xhat = q.xhat; r.xhat_dtype = q.xhat_dtype; r.partials = partials;
         int per = (r.cpr + kThreads - 1) / kThreads;
         int cpt = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
-        grid = (int)(q.rows < kMaxGrid ? q.rows : kMaxGrid);
         if (nelem) {
-            e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, grid, cpt, stats, s)
-                                     : launch_row_fmt<D_F32>(q.fmt, r, grid, cpt, stats, s);
-        } else {
-            grid = 0;
+            e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, cpt, stats, grid, s)
+                                     : launch_row_fmt<D_F32>(q.fmt, r, cpt, stats, grid, s);
         }
     } else {
         FlatArgs f;
@@ -1028,17 +1290,14 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
             e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, scale_out, nullptr, s);
             if (e != hipSuccess) return e;
         }
-        grid = flat_grid(f.geo.nchunks);
         if (nelem) {
-            e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, grid, stats, s)
-                                     : launch_flat_fmt<D_F32>(q.fmt, f, grid, stats, s);
-        } else {
-            grid = 0;
+            e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, stats, grid, s)
+                                     : launch_flat_fmt<D_F32>(q.fmt, f, stats, grid, s);
         }
     }
     if (e != hipSuccess) return e;
     if (stats) {
-        k_stats_finalize<<<1, kThreads, 0, s>>>(partials, grid, (uint64_t)nelem, static_cast<StatsOut*>(q.stats));
+        k_stats_finalize<<<1, kFinThreads, 0, s>>>(partials, grid, (uint64_t)nelem, static_cast<StatsOut*>(q.stats));
         e = hipGetLastError();
     }
     return e;
@@ -1056,14 +1315,14 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
     a.xhat_dtype = d.xhat_dtype;
     a.per_tensor = d.gran == G_TENSOR;
     if (a.nchunks == 0) return hipSuccess;
-    const int grid = flat_grid(a.nchunks);
+    const uint64_t t = tiles_of(a.nchunks);
     switch (d.fmt) {
-    case F_INT8: k_dequant<F_INT8><<<grid, kThreads, 0, s>>>(a); break;
-    case F_E4M3: k_dequant<F_E4M3><<<grid, kThreads, 0, s>>>(a); break;
-    case F_E5M2: k_dequant<F_E5M2><<<grid, kThreads, 0, s>>>(a); break;
-    case F_MXFP4: k_dequant<F_MXFP4><<<grid, kThreads, 0, s>>>(a); break;
-    case F_NVFP4: k_dequant<F_NVFP4><<<grid, kThreads, 0, s>>>(a); break;
-    default: k_dequant<F_INT4><<<grid, kThreads, 0, s>>>(a); break;
+    case F_INT8: k_dequant<F_INT8><<<grid_for(k_dequant<F_INT8>, t), kThreads, 0, s>>>(a); break;
+    case F_E4M3: k_dequant<F_E4M3><<<grid_for(k_dequant<F_E4M3>, t), kThreads, 0, s>>>(a); break;
+    case F_E5M2: k_dequant<F_E5M2><<<grid_for(k_dequant<F_E5M2>, t), kThreads, 0, s>>>(a); break;
+    case F_MXFP4: k_dequant<F_MXFP4><<<grid_for(k_dequant<F_MXFP4>, t), kThreads, 0, s>>>(a); break;
+    case F_NVFP4: k_dequant<F_NVFP4><<<grid_for(k_dequant<F_NVFP4>, t), kThreads, 0, s>>>(a); break;
+    default: k_dequant<F_INT4><<<grid_for(k_dequant<F_INT4>, t), kThreads, 0, s>>>(a); break;
     }
     return hipGetLastError();
 }

@@ -362,3 +362,31 @@ def test_stream_sampled_rows(iq, O, S):
                 assert_bits_equal(scales[r0:r0 + 1], ref["scales"], f"stream {fmt} row {r0} scales")
         del q
     del xd
+
+
+# ---- graph capture: replays match eager calls -------------------------------------
+@pytest.mark.parametrize("fmt,gran", [("e4m3", "row"), ("e4m3", "tensor"), ("nvfp4", "block"), ("int4", "block")])
+def test_graph_replay_matches_eager(iq, S, fmt, gran):
+    """The library enqueues only kernels (no memset nodes), so a captured call
+    replays to the same bytes every time, also with eager work in between."""
+    import torch
+    x = to_device(S.make("c4", nrows=256))
+    ws = iq.workspace_for(iq.desc_for(x, fmt, gran), x.device)
+    ref = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    want = (ref.codes.cpu(), ref.scales.cpu(), ref.xhat.cpu(), ref.stats())
+    out = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32, workspace=ws)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.quantize(x, fmt, gran, workspace=ws, out=out)
+    for rep in range(4):
+        out.codes.zero_(); out.scales.zero_(); out.xhat.zero_(); out.stats_buf.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (out.codes.cpu(), out.scales.cpu(), out.xhat.cpu(), out.stats())
+        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1]), rep
+        assert torch.equal(got[2].view(torch.int32), want[2].view(torch.int32)), rep
+        assert got[3] == want[3], rep
+        iq.quantize(x, "mxfp4", "block", workspace=ws)     # eager work on the same workspace between replays
+        torch.cuda.synchronize()
