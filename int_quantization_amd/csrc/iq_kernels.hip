@@ -55,7 +55,8 @@ __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 
 __device__ __forceinline__ uint32_t umax16(uint32_t m) { return (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16); }
-__device__ __forceinline__ uint32_t umin16(uint32_t m) { return (m & 0xFFFFu) < (m >> 16) ? (m & 0xFFFFu) : (m >> 16); }
+
+constexpr uint32_t kNonFinite = 0x7F800000u;   // absmax bits at or above: Inf or NaN present
 
 // ---------------------------------------------------------------------------
 // Input chunks: 8 consecutive elements of one row.
@@ -79,26 +80,38 @@ template <> struct Chunk<D_BF16> {
     __device__ __forceinline__ float get(int i) const {
         return (i & 1) ? as_f(w[i >> 1] & 0xFFFF0000u) : as_f(w[i >> 1] << 16);
     }
-    // Absmax on the integer image of |x| (BF16 bits a = |x| in [0, 0x7FFF],
-    // ordered like the magnitudes): m keeps the per-half maximum, z the
-    // per-half minimum.  A maximum >= 0x7F80 means an Inf or NaN is present
-    // (then absmax_finite recomputes the maximum over finite elements); a
-    // minimum of 0 means an exact zero is present.
-    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& z) const {
+    // Absmax on the integer image of |x| (BF16 bits |x| in [0, 0x7FFF],
+    // ordered like the magnitudes): per-half maxima, combined as a tree.
+    __device__ __forceinline__ static uint32_t hmax(uint32_t a, uint32_t b) {
         typedef unsigned short u2s __attribute__((ext_vector_type(2)));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const u2s a = __builtin_bit_cast(u2s, w[k] & 0x7FFF7FFFu);
-            m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u2s, m), a));
-            z = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u2s, z), a));
-        }
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u2s, a), __builtin_bit_cast(u2s, b)));
     }
-    // Fold into (bits of the absmax, flags: bit 0 non-finite present, bit 1
-    // exact zero present).  With bit 0 set, bits is not meaningful.
-    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t z, uint32_t& bits, uint32_t& flag) {
-        const uint32_t mx = umax16(m), mn = umin16(z);
-        bits = mx << 16;
-        flag = (mx >= 0x7F80u ? 1u : 0u) | (mn == 0u ? 2u : 0u);
+    __device__ __forceinline__ uint32_t absmax_word() const {
+        const uint32_t a = hmax(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu);
+        const uint32_t b = hmax(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu);
+        return hmax(a, b);
+    }
+    __device__ __forceinline__ void absmax(uint32_t& m) const { m = hmax(m, absmax_word()); }
+    // FP32 bits of the maximum magnitude; kNonFinite or more means an Inf or
+    // NaN is present (absmax_finite then gives the maximum over the rest).
+    __device__ __forceinline__ static uint32_t absmax_bits(uint32_t m) { return umax16(m) << 16; }
+    __device__ __forceinline__ static uint32_t hmin(uint32_t a, uint32_t b) {
+        typedef unsigned short u2s __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u2s, a), __builtin_bit_cast(u2s, b)));
+    }
+    // Per-half maximum and minimum of |x| (the minimum is 0 iff an exact zero is present).
+    __device__ __forceinline__ void absmaxmin_word(uint32_t& mx, uint32_t& mn) const {
+        const uint32_t a0 = w[0] & 0x7FFF7FFFu, a1 = w[1] & 0x7FFF7FFFu, a2 = w[2] & 0x7FFF7FFFu, a3 = w[3] & 0x7FFF7FFFu;
+        mx = hmax(hmax(a0, a1), hmax(a2, a3));
+        mn = hmin(hmin(a0, a1), hmin(a2, a3));
+    }
+    __device__ __forceinline__ static bool has_zero(uint32_t mn) { return (mn & 0xFFFFu) == 0u || (mn >> 16) == 0u; }
+    // Number of nonzero elements: bit 15 of |x| + 0x7FFF (per half) is set iff |x| != 0.
+    __device__ __forceinline__ uint32_t nonzero_count() const {
+        uint32_t n = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) n += __builtin_popcount(((w[k] & 0x7FFF7FFFu) + 0x7FFF7FFFu) & 0x80008000u);
+        return n;
     }
     // Maximum over the finite elements only: t = a + 0x80 is negative as
     // int16 exactly for Inf and NaN, so a signed 16-bit max skips them.
@@ -113,7 +126,6 @@ template <> struct Chunk<D_BF16> {
         const int mx = lo > hi ? lo : hi;
         return mx >= 0x80 ? (uint32_t)(mx - 0x80) << 16 : 0u;
     }
-    static constexpr uint32_t kMaxInit = 0u, kMinInit = 0xFFFFFFFFu;
 };
 
 template <> struct Chunk<D_F32> {
@@ -132,17 +144,29 @@ template <> struct Chunk<D_F32> {
         w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
     }
     __device__ __forceinline__ float get(int i) const { return as_f(w[i]); }
-    __device__ __forceinline__ void absmax(uint32_t& m, uint32_t& z) const {
+    __device__ __forceinline__ static uint32_t hmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+    __device__ __forceinline__ uint32_t absmax_word() const {
+        uint32_t a[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t a = w[k] & 0x7FFFFFFFu;
-            m = a > m ? a : m;
-            z = a < z ? a : z;
-        }
+        for (int k = 0; k < 4; ++k) a[k] = hmax(w[2 * k] & 0x7FFFFFFFu, w[2 * k + 1] & 0x7FFFFFFFu);
+        return hmax(hmax(a[0], a[1]), hmax(a[2], a[3]));
     }
-    __device__ __forceinline__ static void absmax_finish(uint32_t m, uint32_t z, uint32_t& bits, uint32_t& flag) {
-        bits = m;
-        flag = (m >= 0x7F800000u ? 1u : 0u) | (z == 0u ? 2u : 0u);
+    __device__ __forceinline__ void absmax(uint32_t& m) const { m = hmax(m, absmax_word()); }
+    __device__ __forceinline__ static uint32_t absmax_bits(uint32_t m) { return m; }
+    __device__ __forceinline__ static uint32_t hmin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+    __device__ __forceinline__ void absmaxmin_word(uint32_t& mx, uint32_t& mn) const {
+        uint32_t a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = w[k] & 0x7FFFFFFFu;
+        mx = hmax(hmax(hmax(a[0], a[1]), hmax(a[2], a[3])), hmax(hmax(a[4], a[5]), hmax(a[6], a[7])));
+        mn = hmin(hmin(hmin(a[0], a[1]), hmin(a[2], a[3])), hmin(hmin(a[4], a[5]), hmin(a[6], a[7])));
+    }
+    __device__ __forceinline__ static bool has_zero(uint32_t mn) { return mn == 0u; }
+    __device__ __forceinline__ uint32_t nonzero_count() const {
+        uint32_t n = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) n += (w[k] & 0x7FFFFFFFu) != 0u ? 1u : 0u;
+        return n;
     }
     __device__ __forceinline__ uint32_t absmax_finite() const {
         uint32_t m = 0;
@@ -153,7 +177,6 @@ template <> struct Chunk<D_F32> {
         }
         return m;
     }
-    static constexpr uint32_t kMaxInit = 0u, kMinInit = 0xFFFFFFFFu;
 };
 
 // ---------------------------------------------------------------------------
@@ -169,7 +192,7 @@ template <> struct Chunk<D_F32> {
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr unsigned kAuxNontemporal = 2;   // cache policy bits of the copy: streaming (nt)
 
-template <int NW> using Stage = u4v[NW][kThreads];
+template <int NW, int NT = kThreads> using Stage = u4v[NW][NT];
 
 __device__ __forceinline__ void dma_word(const void* src, u4v* wave_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void*)wave_base, 16, 0, kAuxNontemporal);
@@ -192,25 +215,22 @@ __device__ __forceinline__ void wait_lds_reads() {
 template <int IN> struct ChunkWords { static constexpr int n = IN == D_BF16 ? 1 : 2; };
 
 // Start copying chunk `elem` (8 elements) of x into words [w0, w0 + n) of this thread.
-template <int IN, int NW>
-__device__ __forceinline__ void stage_chunk(Stage<NW>& st, int w0, const void* x, int64_t elem) {
+template <int IN, int NW, int NT = kThreads>
+__device__ __forceinline__ void stage_chunk(Stage<NW, NT>& st, int w0, const void* x, int64_t elem) {
     const int wave = threadIdx.x >> 6;
     const char* src = static_cast<const char*>(x) + elem * (IN == D_BF16 ? 2 : 4);
 #pragma unroll
     for (int k = 0; k < ChunkWords<IN>::n; ++k) dma_word(src + 16 * k, &st[w0 + k][64 * wave]);
 }
 
-template <int IN, int NW>
-__device__ __forceinline__ void unstage_chunk(const Stage<NW>& st, int w0, Chunk<IN>& ch) {
-    ch.set(&st[w0][threadIdx.x], kThreads);
+template <int IN, int NW, int NT = kThreads>
+__device__ __forceinline__ void unstage_chunk(const Stage<NW, NT>& st, int w0, Chunk<IN>& ch) {
+    ch.set(&st[w0][threadIdx.x], NT);
 }
 
 // ---------------------------------------------------------------------------
 // Cross-lane reductions.  DPP within rows of 16 lanes, shuffles across rows.
 // ---------------------------------------------------------------------------
-template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
@@ -218,33 +238,75 @@ constexpr int kRowMirror = 0x140;
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// max / or over groups of G consecutive lanes (G = 2, 4 or 16); every lane of
-// the group receives the result.
-template <int G> __device__ __forceinline__ void group_reduce(uint32_t& m, uint32_t& f) {
-    m = umax(m, dpp<kQuadSwap1>(m)); f |= dpp<kQuadSwap1>(f);
-    if (G >= 4) { m = umax(m, dpp<kQuadSwap2>(m)); f |= dpp<kQuadSwap2>(f); }
+// max(m, m of another lane); the DPP move starts from 0, the identity of an
+// unsigned max, so the compiler folds it into the max (one instruction).
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_max(uint32_t m) {
+    return umax(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, CTRL, 0xF, 0xF, false));
+}
+
+// Max over groups of G consecutive lanes (G = 2, 4 or 16); every lane of the
+// group receives the result.
+template <int G> __device__ __forceinline__ uint32_t group_max(uint32_t m) {
+    m = dpp_max<kQuadSwap1>(m);
+    if (G >= 4) m = dpp_max<kQuadSwap2>(m);
     if (G >= 16) {
-        m = umax(m, dpp<kRowHalfMirror>(m)); f |= dpp<kRowHalfMirror>(f);
-        m = umax(m, dpp<kRowMirror>(m)); f |= dpp<kRowMirror>(f);
+        m = dpp_max<kRowHalfMirror>(m);
+        m = dpp_max<kRowMirror>(m);
     }
+    return m;
 }
 
-__device__ __forceinline__ void wave_reduce_max_or(uint32_t& m, uint32_t& f) {
-    group_reduce<16>(m, f);
-    m = umax(m, (uint32_t)__shfl_xor((int)m, 16)); f |= (uint32_t)__shfl_xor((int)f, 16);
-    m = umax(m, (uint32_t)__shfl_xor((int)m, 32)); f |= (uint32_t)__shfl_xor((int)f, 32);
+// Max over the wave, wave-uniform (scalar) result.
+__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
+    m = group_max<16>(m);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
+    return umax(umax(a, b), umax(c, d));
 }
 
-// Max / or over the 256 threads of a workgroup (4 waves, one LDS slot each).
-// Every thread returns the result; red must not be reused by the next call
-// before all threads passed this one (callers alternate two slots).
-__device__ __forceinline__ void row_reduce(uint32_t& m, uint32_t& f, uint32_t (&red)[4][2]) {
-    wave_reduce_max_or(m, f);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { red[wave][0] = m; red[wave][1] = f; }
-    __syncthreads();
-    m = umax(umax(red[0][0], red[1][0]), umax(red[2][0], red[3][0]));
-    f = red[0][1] | red[1][1] | red[2][1] | red[3][1];
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global access of the wave (vmcnt(0)), which would stall
+// on the copy of the next unit issued just before; here only the LDS
+// traffic (lgkmcnt) has to be complete.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Max over the NWAVES waves of a workgroup (one LDS slot per wave beyond the
+// first).  Every thread returns the result; red must not be reused by the
+// next call before all threads passed this one (callers alternate two slots).
+// Max of m and OR of the per-lane flag f over the workgroup (two LDS words
+// per wave beyond the first), with the same slot discipline as block_max.
+template <int NWAVES>
+__device__ __forceinline__ uint32_t block_max_or(uint32_t m, bool f, bool& f_out, uint32_t (&red)[NWAVES][2]) {
+    m = wave_max(m);
+    uint32_t fl = __ballot(f) != 0 ? 1u : 0u;
+    if (NWAVES > 1) {
+        if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6][0] = m; red[threadIdx.x >> 6][1] = fl; }
+        asm volatile("" ::: "memory");
+        lds_barrier();
+        m = red[0][0]; fl = red[0][1];
+#pragma unroll
+        for (int k = 1; k < NWAVES; ++k) { m = umax(m, red[k][0]); fl |= red[k][1]; }
+        m = (uint32_t)__builtin_amdgcn_readfirstlane((int)m);     // uniform: keep in scalar registers
+        fl = (uint32_t)__builtin_amdgcn_readfirstlane((int)fl);
+    }
+    f_out = fl != 0;
+    return m;
+}
+
+template <int NWAVES> __device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t (&red)[NWAVES]) {
+    m = wave_max(m);
+    if (NWAVES == 1) return m;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    asm volatile("" ::: "memory");
+    lds_barrier();
+    m = red[0];
+#pragma unroll
+    for (int k = 1; k < NWAVES; ++k) m = umax(m, red[k]);
+    return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -253,8 +315,8 @@ __device__ __forceinline__ void row_reduce(uint32_t& m, uint32_t& f, uint32_t (&
 // slow path sums in FP64 directly, which also covers units whose absmax lies
 // outside [2^-40, 2^60] where FP32 squares would underflow or overflow.
 // Counters come from wave ballots, so they are only ever updated in
-// wave-uniform control flow (add8 below): every lane then holds the same,
-// complete count.  Lanes without data carry zeros and contribute nothing.
+// wave-uniform control flow: every lane then holds the same, complete count.
+// Lanes without data carry zeros and contribute nothing.
 // ---------------------------------------------------------------------------
 constexpr float kStatLo = 0x1p-40f;   // unit absmax range of the FP32 fast path
 constexpr float kStatHi = 0x1p60f;
@@ -265,85 +327,81 @@ struct Stats {
     double sx2 = 0, se2 = 0, sae = 0;
     float mae = 0.f;
     uint32_t nsat = 0, nzf = 0, nnf = 0;   // wave-uniform
+    uint32_t lzf = 0;                      // per lane: flushed elements counted from the codes
     float fx2 = 0.f, fe2 = 0.f, fae = 0.f; // FP32 accumulators of the current unit
 
     __device__ __forceinline__ void fold() {
         sx2 += (double)fx2; se2 += (double)fe2; sae += (double)fae;
         fx2 = fe2 = fae = 0.f;
     }
-    // Finite inputs in a well-scaled unit.
-    __device__ __forceinline__ void add_fast(float x, float v, float xh, float qmax) {
-        float d = x - xh;
-        fx2 = __builtin_fmaf(x, x, fx2);
-        fe2 = __builtin_fmaf(d, d, fe2);
-        fae += __builtin_fabsf(d);
-        mae = __builtin_fmaxf(mae, __builtin_fabsf(d));
-        nsat += __popcll(__ballot(__builtin_fabsf(v) > qmax));
-        nzf += __popcll(__ballot(x != 0.f) & __ballot(xh == 0.f));   // two compares into SGPR masks
-    }
-    // General case: non-finite inputs count but stay out of sums and maxima.
-    __device__ __forceinline__ void add_slow(float x, float v, float xh, float qmax) {
-        bool fin = __builtin_isfinite(x);
-        double d = fin ? (double)(x - xh) : 0.0;
-        double xs = fin ? (double)x : 0.0;
-        sx2 = __builtin_fma(xs, xs, sx2);
-        se2 = __builtin_fma(d, d, se2);
-        sae += __builtin_fabs(d);
-        mae = __builtin_fmaxf(mae, fin ? __builtin_fabsf(x - xh) : 0.f);
-        nsat += __popcll(__ballot(__builtin_fabsf(v) > qmax));
-        nzf += __popcll(__ballot(fin && x != 0.f && xh == 0.f));
-        nnf += __popcll(__ballot(!fin));
-    }
-    // One chunk, called in wave-uniform control flow.
-    //   slow_lane  the lane's unit needs the general accumulation (the whole
-    //              wave then uses it for this chunk);
-    //   sat_lane   the lane's unit can contain saturated elements; when no
-    //              lane's can, the saturation compares are skipped;
-    //   saturation test: SAT_X ? |x| > thr : |v| > thr.
+    // One chunk of the fast path (finite inputs, unit absmax in the FP32
+    // range), called in wave-uniform control flow with a wave-uniform `sat`:
+    // false when no lane's unit can hold |v| > thr, which skips the
+    // saturation compares (the test is |x| > thr with SAT_X, else |v| > thr).
     // Sum of squares of BF16 inputs: one v_dot2_f32_bf16 per pair of raw
     // inputs (products of BF16 values are exact in FP32).
-    //   zero_lane  the lane's unit may hold exact zeros.  Zero inputs always
-    //              quantize to zero, so the flushed count is
-    //              #(x^ == 0) - #(x == 0), and the second term is only
-    //              counted when some lane's unit holds a zero.
-    template <int IN, bool SAT_X>
-    __device__ __forceinline__ void add8(const Chunk<IN>& ch, bool slow_lane, bool sat_lane, bool zero_lane,
-                                         const float (&x)[8], const float (&v)[8], const float (&h)[8], float thr) {
-        if (__ballot(slow_lane) == 0) {
-            float d[8];
+    // With ZC the flushed count is taken here from the x^ values: zero inputs
+    // always quantize to zero, so it is #(x^ == 0) - #(x == 0), the second
+    // term only evaluated when some lane of the wave produced a zero.
+    // Without ZC the caller counts from the codes (count_flush).
+    template <int IN, bool SAT_X, bool ZC = true>
+    __device__ __forceinline__ void add8_fast(const Chunk<IN>& ch, bool sat, const float (&x)[8], const float (&v)[8],
+                                              const float (&h)[8], float thr) {
+        float d[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) d[i] = x[i] - h[i];
-            if (IN == D_BF16) {
+        for (int i = 0; i < 8; ++i) d[i] = x[i] - h[i];
+        if (IN == D_BF16) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-                    const bf2 p = __builtin_bit_cast(bf2, ch.w[k]);
-                    fx2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, fx2, false);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) fx2 = __builtin_fmaf(x[i], x[i], fx2);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                fe2 = __builtin_fmaf(d[i], d[i], fe2);
-                fae += __builtin_fabsf(d[i]);
-                mae = __builtin_fmaxf(mae, __builtin_fabsf(d[i]));
-                nzf += __popcll(__ballot(h[i] == 0.f));
-            }
-            if (__ballot(zero_lane) != 0) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) nzf -= __popcll(__ballot(x[i] == 0.f));
-            }
-            if (__ballot(sat_lane) != 0) {
-                float t = thr;
-                asm volatile("" : "+v"(t));   // keep the compares inside this branch
-#pragma unroll
-                for (int i = 0; i < 8; ++i) nsat += __popcll(__ballot(__builtin_fabsf(SAT_X ? x[i] : v[i]) > t));
+            for (int k = 0; k < 4; ++k) {
+                typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+                const bf2 p = __builtin_bit_cast(bf2, ch.w[k]);
+                fx2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, fx2, false);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) add_slow(x[i], SAT_X ? x[i] : v[i], h[i], thr);
+            for (int i = 0; i < 8; ++i) fx2 = __builtin_fmaf(x[i], x[i], fx2);
+        }
+        uint64_t zm = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            fe2 = __builtin_fmaf(d[i], d[i], fe2);
+            fae += __builtin_fabsf(d[i]);
+            mae = __builtin_fmaxf(mae, __builtin_fabsf(d[i]));
+            if (ZC) {
+                const uint64_t b = __ballot(h[i] == 0.f);
+                zm |= b;
+                nzf += __popcll(b);
+            }
+        }
+        if (ZC && zm != 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nzf -= __popcll(__ballot(x[i] == 0.f));
+        }
+        if (sat) {
+            float t = thr;
+            asm volatile("" : "+v"(t));   // keep the compares inside this branch
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nsat += __popcll(__ballot(__builtin_fabsf(SAT_X ? x[i] : v[i]) > t));
+        }
+    }
+    // Flushed elements of one chunk: nonzero inputs minus nonzero codes (a
+    // nonzero code always comes from a nonzero input).
+    __device__ __forceinline__ void count_flush(uint32_t nonzero_x, uint32_t nonzero_codes) { lzf += nonzero_x - nonzero_codes; }
+    // General case, wave-uniform call: non-finite inputs count but stay out
+    // of sums and maxima; vs is the value tested for |vs| > thr.
+    __device__ __forceinline__ void add8_slow(const float (&x)[8], const float (&vs)[8], const float (&h)[8], float thr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bool fin = __builtin_isfinite(x[i]);
+            const double d = fin ? (double)(x[i] - h[i]) : 0.0;
+            const double xs = fin ? (double)x[i] : 0.0;
+            sx2 = __builtin_fma(xs, xs, sx2);
+            se2 = __builtin_fma(d, d, se2);
+            sae += __builtin_fabs(d);
+            mae = __builtin_fmaxf(mae, fin ? __builtin_fabsf(x[i] - h[i]) : 0.f);
+            nsat += __popcll(__ballot(__builtin_fabsf(vs[i]) > thr));
+            nzf += __popcll(__ballot(fin && x[i] != 0.f && h[i] == 0.f));
+            nnf += __popcll(__ballot(!fin));
         }
     }
 };
@@ -353,40 +411,49 @@ struct Stats {
 // preserves.
 __device__ __forceinline__ bool can_saturate(float A, float s, float Q) { return __builtin_fmaf(Q, s, -A) < 0.f; }
 
-// Reduce the workgroup's statistics and write its partial (thread 0).
+// Reduce the workgroup's statistics (NWAVES waves) and write its partial.
+template <int NWAVES>
 __device__ void write_partial(Stats& st, Partial* out) {
-    __shared__ double s_d[4][3];
-    __shared__ float s_m[4];
-    __shared__ uint32_t s_c[4][3];
+    __shared__ double s_d[NWAVES][3];
+    __shared__ float s_m[NWAVES];
+    __shared__ uint32_t s_c[NWAVES][3];
     st.fold();
     double a = st.sx2, b = st.se2, c = st.sae;
     float m = st.mae;
     // The ballot counters were only updated in wave-uniform control flow:
-    // every lane holds the wave's count.
-    const uint32_t n0 = st.nsat, n1 = st.nzf, n2 = st.nnf;
+    // every lane holds the wave's count; lzf is per lane.
+    uint32_t lz = st.lzf;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         a += __shfl_xor(a, o); b += __shfl_xor(b, o); c += __shfl_xor(c, o);
         m = __builtin_fmaxf(m, __shfl_xor(m, o));
+        lz += (uint32_t)__shfl_xor((int)lz, o);
     }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) {
-        s_d[wave][0] = a; s_d[wave][1] = b; s_d[wave][2] = c; s_m[wave] = m;
-        s_c[wave][0] = n0; s_c[wave][1] = n1; s_c[wave][2] = n2;
+    const uint32_t n0 = st.nsat, n1 = st.nzf + lz, n2 = st.nnf;
+    Partial p;
+    if (NWAVES == 1) {
+        if (threadIdx.x != 0) return;
+        p.sum_x2 = a; p.sum_err2 = b; p.sum_abs_err = c; p.max_abs_err = m;
+        p.n_saturated = n0; p.n_zero_flush = n1; p.n_nonfinite = n2;
+    } else {
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (lane == 0) {
+            s_d[wave][0] = a; s_d[wave][1] = b; s_d[wave][2] = c; s_m[wave] = m;
+            s_c[wave][0] = n0; s_c[wave][1] = n1; s_c[wave][2] = n2;
+        }
+        __syncthreads();
+        if (threadIdx.x != 0) return;
+        p.sum_x2 = s_d[0][0]; p.sum_err2 = s_d[0][1]; p.sum_abs_err = s_d[0][2]; p.max_abs_err = s_m[0];
+        p.n_saturated = s_c[0][0]; p.n_zero_flush = s_c[0][1]; p.n_nonfinite = s_c[0][2];
+#pragma unroll
+        for (int k = 1; k < NWAVES; ++k) {
+            p.sum_x2 += s_d[k][0]; p.sum_err2 += s_d[k][1]; p.sum_abs_err += s_d[k][2];
+            p.max_abs_err = __builtin_fmaxf(p.max_abs_err, s_m[k]);
+            p.n_saturated += s_c[k][0]; p.n_zero_flush += s_c[k][1]; p.n_nonfinite += s_c[k][2];
+        }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        Partial p;
-        p.sum_x2 = ((s_d[0][0] + s_d[1][0]) + (s_d[2][0] + s_d[3][0]));
-        p.sum_err2 = ((s_d[0][1] + s_d[1][1]) + (s_d[2][1] + s_d[3][1]));
-        p.sum_abs_err = ((s_d[0][2] + s_d[1][2]) + (s_d[2][2] + s_d[3][2]));
-        p.max_abs_err = __builtin_fmaxf(__builtin_fmaxf(s_m[0], s_m[1]), __builtin_fmaxf(s_m[2], s_m[3]));
-        p.n_saturated = s_c[0][0] + s_c[1][0] + s_c[2][0] + s_c[3][0];
-        p.n_zero_flush = s_c[0][1] + s_c[1][1] + s_c[2][1] + s_c[3][1];
-        p.n_nonfinite = s_c[0][2] + s_c[1][2] + s_c[2][2] + s_c[3][2];
-        p.pad[0] = p.pad[1] = 0;
-        out[blockIdx.x] = p;
-    }
+    p.pad[0] = p.pad[1] = 0;
+    out[blockIdx.x] = p;
 }
 
 // ---------------------------------------------------------------------------
@@ -407,6 +474,12 @@ __device__ __forceinline__ float markstein(float x, float s, float y) {
     float q0 = x * y;
     float r = __builtin_fmaf(s, q0, -x);
     return __builtin_fmaf(-r, y, q0);
+}
+
+// Nonzero codes among the 4 bytes of w (INT8 / FP8: a code is zero iff its
+// low 7 bits are, -128 is never produced): bit 7 of (c & 0x7F) + 0x7F.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+    return __builtin_popcount(((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u);
 }
 
 // FP8 pack / unpack (4 codes per 32-bit word, element 0 in the low byte).
@@ -464,11 +537,104 @@ __device__ __forceinline__ void store_xhat(void* xhat, int dtype, int64_t elem, 
 
 // ---------------------------------------------------------------------------
 // INT8 / FP8 with a scale shared by the whole chunk (per row or per tensor).
-// `fast` must be wave-uniform.  Every lane computes (lanes without data hold
-// zeros); only lanes with `store` write 8 code bytes at codes8 and x^ in h.
+// `fast` and `sat` are wave-uniform: fast means a finite unit with absmax in
+// [2^-40, 2^60] (Markstein quotient, FP32 statistics), sat that some lane's
+// unit can saturate.  Every lane computes (lanes without data hold zeros);
+// only lanes with `store` write their 8 code bytes at codes8.  h receives x^.
 // ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ void cast_uniform_fast(const float (&x)[8], float s, float y, float (&v)[8], float (&h)[8],
+                                                  uint32_t& w0, uint32_t& w1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s, y);
+    if (FMT == F_INT8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            t[i] = v[i] + kMagic;        // |v| <= 127 * (1 + 2^-23): the sum is the RNE integer
+            h[i] = s * (t[i] - kMagic);  // (t - kMagic) is +0 for a zero code
+        }
+        const uint32_t p0 = __builtin_amdgcn_perm(as_u(t[1]), as_u(t[0]), 0x0c0c0400u);
+        const uint32_t p1 = __builtin_amdgcn_perm(as_u(t[3]), as_u(t[2]), 0x0c0c0400u);
+        const uint32_t p2 = __builtin_amdgcn_perm(as_u(t[5]), as_u(t[4]), 0x0c0c0400u);
+        const uint32_t p3 = __builtin_amdgcn_perm(as_u(t[7]), as_u(t[6]), 0x0c0c0400u);
+        w0 = p0 | (p1 << 16);
+        w1 = p2 | (p3 << 16);
+    } else {
+        w0 = fp8_pack4<FMT>(v[0], v[1], v[2], v[3]);
+        w1 = fp8_pack4<FMT>(v[4], v[5], v[6], v[7]);
+        const f2v d0 = fp8_unpack2<FMT, false>(w0), d1 = fp8_unpack2<FMT, true>(w0);
+        const f2v d2 = fp8_unpack2<FMT, false>(w1), d3 = fp8_unpack2<FMT, true>(w1);
+        h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
+        h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
+    }
+}
+
+// Slow path: correctly rounded division, explicit clamps and NaN codes.
+template <int FMT>
+__device__ __forceinline__ void cast_uniform_slow(const float (&x)[8], float s, float (&v)[8], float (&h)[8],
+                                               uint32_t& w0, uint32_t& w1) {
+    constexpr float Q = Fmt<FMT>::qmax;
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (s == 0.f) ? 0.f : x[i] / s;
+    if (FMT == F_INT8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -127.f), 127.f);
+            const int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
+            c[i] = (uint32_t)qi & 0xFFu;
+            h[i] = s * (float)qi;
+        }
+    } else {
+        float cl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cl[i] = __builtin_fminf(__builtin_fmaxf(v[i], -Q), Q);
+        const uint32_t a = fp8_pack4<FMT>(cl[0], cl[1], cl[2], cl[3]);
+        const uint32_t b = fp8_pack4<FMT>(cl[4], cl[5], cl[6], cl[7]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t byte = ((i < 4 ? a : b) >> (8 * (i & 3))) & 0xFFu;
+            if (__builtin_isnan(v[i])) byte = 0x7Fu;
+            if (s == 0.f) byte = 0u;
+            c[i] = byte;
+        }
+        const uint32_t a2 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        const uint32_t b2 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        const f2v d0 = fp8_unpack2<FMT, false>(a2), d1 = fp8_unpack2<FMT, true>(a2);
+        const f2v d2 = fp8_unpack2<FMT, false>(b2), d3 = fp8_unpack2<FMT, true>(b2);
+        h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
+        h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
+    }
+    w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+}
+
+// The common case of a unit: finite, absmax in the fast range, no exact
+// zeros and no lane of the wave able to saturate.  No flag tests.
 template <int IN, int FMT, bool STATS>
-__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float alpha, float s, float y, bool fast,
+__device__ __forceinline__ void quant_chunk_hot(const Chunk<IN>& ch, float s, float y, bool store, uint8_t* codes8,
+                                                float (&h)[8], Stats& st) {
+    constexpr float Q = Fmt<FMT>::qmax;
+    float x[8], v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
+    uint32_t w0, w1;
+    cast_uniform_fast<FMT>(x, s, y, v, h, w0, w1);
+    if (STATS) {
+        st.add8_fast<IN, false, false>(ch, false, x, v, h, Q);
+        st.count_flush(store ? 8u : 0u, nonzero_bytes(w0) + nonzero_bytes(w1));
+    }
+    if (store) {
+        const u2v o = {w0, w1};
+        __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(codes8));
+    }
+}
+
+// `zeros` (uniform): the unit may hold exact zeros; without it every lane
+// with `store` holds 8 nonzero inputs and lanes without data hold zeros.
+template <int IN, int FMT, bool STATS>
+__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float s, float y, bool fast, bool sat,
                                                     bool zeros, bool store, uint8_t* codes8, float (&h)[8], Stats& st) {
     constexpr float Q = Fmt<FMT>::qmax;
     float x[8], v[8];
@@ -476,75 +642,25 @@ __device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float a
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
     uint32_t w0, w1;
     if (fast) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s, y);
-        if (FMT == F_INT8) {
-            float t[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                t[i] = v[i] + kMagic;        // |v| <= 127 * (1 + 2^-23): the sum is the RNE integer
-                h[i] = s * (t[i] - kMagic);  // (t - kMagic) is +0 for a zero code
-            }
-            uint32_t p0 = __builtin_amdgcn_perm(as_u(t[1]), as_u(t[0]), 0x0c0c0400u);
-            uint32_t p1 = __builtin_amdgcn_perm(as_u(t[3]), as_u(t[2]), 0x0c0c0400u);
-            uint32_t p2 = __builtin_amdgcn_perm(as_u(t[5]), as_u(t[4]), 0x0c0c0400u);
-            uint32_t p3 = __builtin_amdgcn_perm(as_u(t[7]), as_u(t[6]), 0x0c0c0400u);
-            w0 = p0 | (p1 << 16);
-            w1 = p2 | (p3 << 16);
-        } else {
-            w0 = fp8_pack4<FMT>(v[0], v[1], v[2], v[3]);
-            w1 = fp8_pack4<FMT>(v[4], v[5], v[6], v[7]);
-            f2v d0 = fp8_unpack2<FMT, false>(w0), d1 = fp8_unpack2<FMT, true>(w0);
-            f2v d2 = fp8_unpack2<FMT, false>(w1), d3 = fp8_unpack2<FMT, true>(w1);
-            h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
-            h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
+        cast_uniform_fast<FMT>(x, s, y, v, h, w0, w1);
+        if (STATS) {
+            st.add8_fast<IN, false, false>(ch, sat, x, v, h, Q);
+            st.count_flush(zeros ? ch.nonzero_count() : (store ? 8u : 0u), nonzero_bytes(w0) + nonzero_bytes(w1));
         }
     } else {
-        // Slow path: correctly rounded division, explicit clamps and NaN codes.
-        uint32_t c[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (s == 0.f) ? 0.f : x[i] / s;
-        if (FMT == F_INT8) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -127.f), 127.f);
-                int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
-                c[i] = (uint32_t)qi & 0xFFu;
-                h[i] = s * (float)qi;
-            }
-        } else {
-            float cl[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cl[i] = __builtin_fminf(__builtin_fmaxf(v[i], -Q), Q);
-            uint32_t a = fp8_pack4<FMT>(cl[0], cl[1], cl[2], cl[3]);
-            uint32_t b = fp8_pack4<FMT>(cl[4], cl[5], cl[6], cl[7]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint32_t byte = ((i < 4 ? a : b) >> (8 * (i & 3))) & 0xFFu;
-                if (__builtin_isnan(v[i])) byte = 0x7Fu;
-                if (s == 0.f) byte = 0u;
-                c[i] = byte;
-            }
-            uint32_t a2 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            uint32_t b2 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-            f2v d0 = fp8_unpack2<FMT, false>(a2), d1 = fp8_unpack2<FMT, true>(a2);
-            f2v d2 = fp8_unpack2<FMT, false>(b2), d3 = fp8_unpack2<FMT, true>(b2);
-            h[0] = s * d0.x; h[1] = s * d0.y; h[2] = s * d1.x; h[3] = s * d1.y;
-            h[4] = s * d2.x; h[5] = s * d2.y; h[6] = s * d3.x; h[7] = s * d3.y;
-        }
-        w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        cast_uniform_slow<FMT>(x, s, v, h, w0, w1);
+        if (STATS) st.add8_slow(x, v, h, Q);
     }
     if (store) {
-        u2v o = {w0, w1};
+        const u2v o = {w0, w1};
         __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(codes8));
     }
-    if (STATS) st.add8<IN, false>(ch, !fast, !fast || can_saturate(alpha, s, Q), zeros, x, v, h, Q);
 }
 
 // ---------------------------------------------------------------------------
-// Per-row INT8 / FP8: one workgroup owns one row at a time; the row stays in
-// registers between the absmax and the cast (CPT chunks per thread).
+// Per-row INT8 / FP8.  A workgroup of NT threads (one wave for rows of up to
+// 1024 chunks, four waves for longer ones) owns one row at a time and keeps
+// it in registers between the absmax and the cast, CPT chunks per thread.
 // ---------------------------------------------------------------------------
 struct RowArgs {
     const void* x;
@@ -557,125 +673,157 @@ struct RowArgs {
     Partial* partials;
 };
 
-template <int IN, int CPT>
-__device__ __forceinline__ void stage_row(Stage<CPT * ChunkWords<IN>::n>& st, const RowArgs& a, int32_t row) {
-    const int64_t base = (int64_t)row * a.ld;
+template <int IN, int CPT, int NT>
+using RowStage = Stage<CPT * ChunkWords<IN>::n, NT>;
+
+// FULL: the row has exactly CPT * NT chunks (every lane holds data).  The
+// row address is scalar; each lane adds its own 32-bit byte offset, and
+// `wave` (uniform) selects the wave's LDS words.
+template <int IN, int CPT, int NT, bool FULL>
+__device__ __forceinline__ void stage_row(RowStage<IN, CPT, NT>& st, const RowArgs& a, int32_t row, int wave) {
+    constexpr int W = ChunkWords<IN>::n;
+    const char* rp = static_cast<const char*>(a.x) + (int64_t)row * a.ld * (IN == D_BF16 ? 2 : 4);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const int c = threadIdx.x + j * kThreads;
-        if (c < a.cpr) stage_chunk<IN, CPT * ChunkWords<IN>::n>(st, j * ChunkWords<IN>::n, a.x, base + (int64_t)c * kChunk);
+        const uint32_t c = threadIdx.x + j * NT;
+        if (FULL || (int)c < a.cpr) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) dma_word(rp + (c * 16u * W + 16u * k), &st[j * W + k][64 * wave]);
+        }
     }
 }
 
-template <int IN, int CPT>
-__device__ __forceinline__ void unstage_row(const Stage<CPT * ChunkWords<IN>::n>& st, const RowArgs& a,
-                                            Chunk<IN> (&ch)[CPT]) {
+template <int IN, int CPT, int NT, bool FULL>
+__device__ __forceinline__ void unstage_row(const RowStage<IN, CPT, NT>& st, const RowArgs& a, Chunk<IN> (&ch)[CPT]) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        if ((int)threadIdx.x + j * kThreads < a.cpr) unstage_chunk<IN, CPT * ChunkWords<IN>::n>(st, j * ChunkWords<IN>::n, ch[j]);
+        if (FULL || (int)threadIdx.x + j * NT < a.cpr) unstage_chunk<IN, CPT * ChunkWords<IN>::n, NT>(st, j * ChunkWords<IN>::n, ch[j]);
         else ch[j].zero();
     }
 }
 
-// One row held in registers: absmax (lanes, then the four waves through
-// LDS), scale, cast, stores, statistics.
-template <int IN, int FMT, int CPT, bool STATS>
-__device__ __forceinline__ void quant_row(const Chunk<IN> (&ch)[CPT], const RowArgs& a, int32_t row,
-                                          uint32_t (&s_red)[2][4][2], int parity, Stats& st) {
-    const int tid = threadIdx.x;
-    const int64_t cols = (int64_t)a.cpr * kChunk;
-    uint32_t m = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
+// Row scale and flags, uniform over the workgroup (sat: over the wave).
+struct RowScale {
+    float s, y;
+    bool fast, sat, zeros;
+};
+
+template <int IN, int FMT, int CPT, int NT>
+__device__ __forceinline__ RowScale row_scale(const Chunk<IN> (&ch)[CPT], uint32_t (&red)[2][NT / 64][2],
+                                              int parity) {
+    constexpr float Q = Fmt<FMT>::qmax;
+    uint32_t wm[CPT], wn[CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) ch[j].absmax(m, z);
-    uint32_t bits, flag;
-    Chunk<IN>::absmax_finish(m, z, bits, flag);
-    row_reduce(bits, flag, s_red[parity]);
-    if (flag & 1u) {   // the row holds Inf or NaN: absmax over its finite elements
-        uint32_t f = 0, unused = 0;
+    for (int j = 0; j < CPT; ++j) ch[j].absmaxmin_word(wm[j], wn[j]);
+#pragma unroll
+    for (int step = 1; step < CPT; step *= 2)
+#pragma unroll
+        for (int j = 0; j + step < CPT; j += 2 * step) {
+            wm[j] = Chunk<IN>::hmax(wm[j], wm[j + step]);
+            wn[j] = Chunk<IN>::hmin(wn[j], wn[j + step]);
+        }
+    const uint32_t lane_bits = Chunk<IN>::absmax_bits(wm[0]);
+    bool zeros;
+    uint32_t bits = block_max_or<NT / 64>(lane_bits, Chunk<IN>::has_zero(wn[0]), zeros, red[parity]);
+    const bool nonfinite = bits >= kNonFinite;
+    if (nonfinite) {   // the row holds Inf or NaN: absmax over its finite elements
+        uint32_t f = 0;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) f = umax(f, ch[j].absmax_finite());
-        row_reduce(f, unused, s_red[parity ^ 1]);
-        bits = f;
+        bool unused;
+        bits = block_max_or<NT / 64>(f, false, unused, red[parity ^ 1]);
     }
     const float alpha = as_f(bits);
-    const float s = alpha / Fmt<FMT>::qmax;
-    if (tid == 0) a.scales[row] = s;
+    RowScale r;
+    r.zeros = zeros;
+    r.s = alpha / Q;
     // fast: finite row with alpha in [2^-40, 2^60] (so s >= 2^-64)
-    const bool fast = (flag & 1u) == 0 && stat_range(alpha);
-    const float y = fast ? 1.0f / s : 0.f;
-    uint8_t* crow = a.codes + (int64_t)row * cols;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int c = tid + j * kThreads;
-        const bool valid = c < a.cpr;
-        float h[8];
-        quant_chunk_uniform<IN, FMT, STATS>(ch[j], alpha, s, y, fast, (flag & 2u) != 0, valid,
-                                            crow + (int64_t)c * kChunk, h, st);
-        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
-    }
-    if (STATS) st.fold();
+    r.fast = !nonfinite && stat_range(alpha);
+    r.y = r.fast ? 1.0f / r.s : 0.f;
+    // |v| > Q needs |x| > Q * s: only waves with such a lane test (per wave)
+    r.sat = !r.fast || __ballot(can_saturate(as_f(lane_bits), r.s, Q)) != 0;
+    return r;
 }
 
-// Per-row INT8 / FP8: a workgroup owns one row at a time and keeps it in
-// registers between the absmax and the cast (CPT chunks per thread).  The
-// next row streams into LDS while the current one is reduced, cast and stored.
-template <int IN, int FMT, int CPT, bool STATS>
-__global__ __launch_bounds__(kThreads) void k_quant_row(RowArgs a) {
-    __shared__ uint32_t s_red[2][4][2];
-    __shared__ Stage<CPT * ChunkWords<IN>::n> stage;
+// Per-row INT8 / FP8: the next row streams into LDS while the current one
+// is reduced, cast and stored.
+template <int IN, int FMT, int CPT, int NT, bool FULL, bool STATS>
+__global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
+    __shared__ uint32_t s_red[2][NT / 64][2];
+    __shared__ RowStage<IN, CPT, NT> stage;
     Stats st;
     const int32_t G = gridDim.x;
+    const int64_t cols = (int64_t)a.cpr * kChunk;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int parity = 0;
     int32_t row = blockIdx.x;
-    if (row < a.rows) stage_row<IN, CPT>(stage, a, row);
+    if (row < a.rows) stage_row<IN, CPT, NT, FULL>(stage, a, row, wave);
     for (; row < a.rows; row += G, parity ^= 1) {
         Chunk<IN> ch[CPT];
         wait_staged();
-        unstage_row<IN, CPT>(stage, a, ch);
+        unstage_row<IN, CPT, NT, FULL>(stage, a, ch);
         wait_lds_reads();
-        if (row + G < a.rows) stage_row<IN, CPT>(stage, a, row + G);
-        quant_row<IN, FMT, CPT, STATS>(ch, a, row, s_red, parity, st);
+        if (row + G < a.rows) stage_row<IN, CPT, NT, FULL>(stage, a, row + G, wave);
+        const auto r = row_scale<IN, FMT, CPT, NT>(ch, s_red, parity);
+        if (threadIdx.x == 0) a.scales[row] = r.s;
+        uint8_t* crow = a.codes + (int64_t)row * cols;
+        if (r.fast && !r.zeros && !r.sat && !a.xhat) {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const uint32_t c = threadIdx.x + j * NT;
+                float h[8];
+                quant_chunk_hot<IN, FMT, STATS>(ch[j], r.s, r.y, FULL || (int)c < a.cpr, crow + c * 8u, h, st);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const uint32_t c = threadIdx.x + j * NT;
+                const bool valid = FULL || (int)c < a.cpr;
+                float h[8];
+                quant_chunk_uniform<IN, FMT, STATS>(ch[j], r.s, r.y, r.fast, r.sat, r.zeros, valid, crow + c * 8u, h, st);
+                if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
+            }
+        }
+        if (STATS) st.fold();
     }
-    if (STATS) write_partial(st, a.partials);
+    if (STATS) write_partial<NT / 64>(st, a.partials);
 }
 
-// Rows longer than kRowCptMax * kThreads chunks: absmax pass, then a second
+// Rows longer than 2048 chunks: absmax pass, then a second
 // pass that re-reads the row (from L2 for rows up to a few MiB).
 template <int IN, int FMT, bool STATS>
 __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
-    __shared__ uint32_t s_red[2][4][2];
+    constexpr float Q = Fmt<FMT>::qmax;
+    __shared__ uint32_t s_red[2][kThreads / 64];
     const int tid = threadIdx.x;
     const int64_t cols = (int64_t)a.cpr * kChunk;
     Stats st;
     int parity = 0;
     for (int32_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
         const int64_t base = (int64_t)row * a.ld;
-        uint32_t m = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
+        uint32_t m = 0;
         for (int c = tid; c < a.cpr; c += kThreads) {
             Chunk<IN> ch;
             ch.load(a.x, base + (int64_t)c * kChunk);
-            ch.absmax(m, z);
+            ch.absmax(m);
         }
-        uint32_t bits, flag;
-        Chunk<IN>::absmax_finish(m, z, bits, flag);
-        row_reduce(bits, flag, s_red[parity]);
-        if (flag & 1u) {   // Inf or NaN in the row: another pass for the finite absmax
-            uint32_t f = 0, unused = 0;
+        uint32_t bits = block_max<kThreads / 64>(Chunk<IN>::absmax_bits(m), s_red[parity]);
+        const bool nonfinite = bits >= kNonFinite;
+        if (nonfinite) {   // Inf or NaN in the row: another pass for the finite absmax
+            uint32_t f = 0;
             for (int c = tid; c < a.cpr; c += kThreads) {
                 Chunk<IN> ch;
                 ch.load(a.x, base + (int64_t)c * kChunk);
                 f = umax(f, ch.absmax_finite());
             }
-            row_reduce(f, unused, s_red[parity ^ 1]);
-            bits = f;
+            bits = block_max<kThreads / 64>(f, s_red[parity ^ 1]);
         }
-        // lanes past the row end carry zero chunks: count them as zeros too
-        const bool zeros = (flag & 2u) != 0 || (a.cpr % kThreads) != 0;
         const float alpha = as_f(bits);
-        const float s = alpha / Fmt<FMT>::qmax;
+        const float s = alpha / Q;
         if (tid == 0) a.scales[row] = s;
-        const bool fast = (flag & 1u) == 0 && stat_range(alpha);
+        const bool fast = !nonfinite && stat_range(alpha);
         const float y = fast ? 1.0f / s : 0.f;
+        const bool sat = !fast || can_saturate(alpha, s, Q);
         uint8_t* crow = a.codes + (int64_t)row * cols;
         // uniform trip count: lanes past the row end carry a zero chunk
         for (int c0 = 0; c0 < a.cpr; c0 += kThreads) {
@@ -685,12 +833,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
             if (valid) ch.load(a.x, base + (int64_t)c * kChunk);
             else ch.zero();
             float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch, alpha, s, y, fast, zeros, valid, crow + (int64_t)c * kChunk, h, st);
+            quant_chunk_uniform<IN, FMT, STATS>(ch, s, y, fast, sat, true, valid, crow + (int64_t)c * kChunk, h, st);
             if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
             if (STATS) st.fold();
         }
     }
-    if (STATS) write_partial(st, a.partials);
+    if (STATS) write_partial<kThreads / 64>(st, a.partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -726,25 +874,25 @@ struct FlatArgs {
 // and the statistics are accumulated in wave-uniform control flow.
 
 // Absmax of a block spread over G lanes (G = 2, 4, 16): bits of the finite
-// maximum and the flags of absmax_finish, on every lane of the group.
+// maximum on every lane of the group; `nonfinite` if the block holds Inf/NaN.
 template <int IN, int G>
-__device__ __forceinline__ void unit_absmax(const Chunk<IN>& ch, uint32_t& bits, uint32_t& flag) {
-    uint32_t m = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
-    ch.absmax(m, z);
-    Chunk<IN>::absmax_finish(m, z, bits, flag);
-    group_reduce<G>(bits, flag);
-    if (__ballot(flag & 1u) != 0) {   // some block of the wave holds Inf or NaN
-        uint32_t f = ch.absmax_finite(), unused = 0;
-        group_reduce<G>(f, unused);
-        if (flag & 1u) bits = f;
+__device__ __forceinline__ uint32_t unit_absmax(const Chunk<IN>& ch, bool& nonfinite) {
+    uint32_t m = 0;
+    ch.absmax(m);
+    uint32_t bits = group_max<G>(Chunk<IN>::absmax_bits(m));
+    nonfinite = bits >= kNonFinite;
+    if (__ballot(nonfinite) != 0) {   // some block of the wave holds Inf or NaN
+        const uint32_t f = group_max<G>(ch.absmax_finite());
+        if (nonfinite) bits = f;
     }
+    return bits;
 }
 
 // MXFP4: blocks of 32 = 4 chunks = 4 lanes.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    uint32_t bits, flag;
-    unit_absmax<IN, 4>(ch, bits, flag);
+    bool nonfinite;
+    const uint32_t bits = unit_absmax<IN, 4>(ch, nonfinite);
     int E = 0;
     if (bits) {
         int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
@@ -761,16 +909,16 @@ __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, 
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
-    if (flag & 1u) {
+    if (nonfinite) {
         // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (__builtin_isnan(x[i])) w &= ~(0xFu << (4 * i));
     }
-    f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
-    f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
-    f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
-    f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+    const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+    const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+    const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+    const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
     h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
     if (valid) {
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
@@ -780,7 +928,8 @@ __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, 
         // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
         // when |x| > 6 * 2^(E-127) (both sides are exact near 6).
         const float thr = 6.0f * sc;
-        st.add8<IN, true>(ch, (flag & 1u) || !stat_range(as_f(bits)), as_f(bits) > thr, (flag & 2u) != 0, x, v, h, thr);
+        if (__ballot(nonfinite || !stat_range(as_f(bits))) == 0) st.add8_fast<IN, true>(ch, __ballot(as_f(bits) > thr) != 0, x, v, h, thr);
+        else st.add8_slow(x, x, h, thr);
     }
 }
 
@@ -791,11 +940,31 @@ __device__ __forceinline__ uint32_t e4m3_ceil(float t) {
     return e4m3_value(c) < t ? c + 1u : c;
 }
 
-// NVFP4: blocks of 16 = 2 chunks = 2 lanes.
+__device__ __forceinline__ uint32_t fp4_pack8(const float (&v)[8]) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+    return w;
+}
+
+__device__ __forceinline__ void fp4_unpack8(uint32_t w, float s, float (&h)[8]) {
+    const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    h[0] = s * p0.x; h[1] = s * p0.y; h[2] = s * p1.x; h[3] = s * p1.y;
+    h[4] = s * p2.x; h[5] = s * p2.y; h[6] = s * p3.x; h[7] = s * p3.y;
+}
+
+// NVFP4: blocks of 16 = 2 chunks = 2 lanes.  The wave takes the fast path
+// when every lane's block is finite with a scale in the fast range; the
+// slow path (correctly rounded division, patches) is exact for every lane.
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, bool valid, float s_g, const FlatArgs& a, Stats& st) {
-    uint32_t bits, flag;
-    unit_absmax<IN, 2>(ch, bits, flag);
+    bool nonfinite;
+    const uint32_t bits = unit_absmax<IN, 2>(ch, nonfinite);
     uint32_t sb = 0;
     float s_nv = 0.f;
     if (s_g != 0.f) {
@@ -804,47 +973,40 @@ __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, 
         s_nv = s_g * e4m3_value(sb);
     }
     if (valid && (g & 1u) == 0) static_cast<uint8_t*>(a.scales)[g >> 1] = (uint8_t)sb;
-    const bool fast = !(flag & 1u) && s_nv >= kTinyScale && stat_range(as_f(bits));
+    const bool fast = !nonfinite && s_nv >= kTinyScale && stat_range(as_f(bits));
     float x[8], v[8], h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
-    uint32_t w = 0;
-    if (fast) {
+    uint32_t w;
+    if (__ballot(!fast) == 0) {
         const float y = 1.0f / s_nv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s_nv, y);
+        w = fp4_pack8(v);
+        fp4_unpack8(w, s_nv, h);
+        if (STATS) st.add8_fast<IN, false>(ch, __ballot(can_saturate(as_f(bits), s_nv, 6.f)) != 0, x, v, h, 6.f);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (s_nv == 0.f) ? 0.f : x[i] / s_nv;
-    }
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
-    if (!fast) {
+        w = fp4_pack8(v);
         if (s_nv == 0.f) w = 0u;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (__builtin_isnan(v[i])) w &= ~(0xFu << (4 * i));
+        fp4_unpack8(w, s_nv, h);
+        if (STATS) st.add8_slow(x, v, h, 6.f);
     }
-    f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    h[0] = s_nv * p0.x; h[1] = s_nv * p0.y; h[2] = s_nv * p1.x; h[3] = s_nv * p1.y;
-    h[4] = s_nv * p2.x; h[5] = s_nv * p2.y; h[6] = s_nv * p3.x; h[7] = s_nv * p3.y;
     if (valid) {
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
         if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
     }
-    if (STATS) st.add8<IN, false>(ch, !fast, !fast || can_saturate(as_f(bits), s_nv, 6.f), (flag & 2u) != 0, x, v, h, 6.f);
 }
 
 // INT4: groups of 128 = 16 chunks = 16 lanes; FP16 scale fp16(A / 7), saturated.
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    uint32_t bits, flag;
-    unit_absmax<IN, 16>(ch, bits, flag);
+    bool nonfinite;
+    const uint32_t bits = unit_absmax<IN, 16>(ch, nonfinite);
     const float s32 = as_f(bits) / 7.0f;
     _Float16 hs = (_Float16)s32;                       // RNE
     uint16_t s16 = s32 > 65504.f ? (uint16_t)0x7BFF : __builtin_bit_cast(uint16_t, hs);
@@ -852,35 +1014,36 @@ __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g
     if (valid && (g & 15u) == 0) static_cast<uint16_t*>(a.scales)[g >> 4] = s16;
     // fast: finite inputs and a normal, unsaturated FP16 scale keep |x/sf| < 7.5
     // (and put A = 7 sf inside the FP32 statistics range)
-    const bool fast = !(flag & 1u) && sf >= 0x1p-14f && s32 <= 65504.f;
+    const bool fast = !nonfinite && sf >= 0x1p-14f && s32 <= 65504.f;
     float x[8], v[8], h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
     uint32_t w = 0;
-    if (fast) {
+    if (__ballot(!fast) == 0) {
         const float y = 1.0f / sf;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             v[i] = markstein(x[i], sf, y);
-            float t = v[i] + kMagic;
+            const float t = v[i] + kMagic;
             w |= (as_u(t) & 0xFu) << (4 * i);
             h[i] = sf * (t - kMagic);
         }
+        if (STATS) st.add8_fast<IN, false>(ch, __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0, x, v, h, 7.f);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             v[i] = (sf == 0.f) ? 0.f : x[i] / sf;
-            float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -7.f), 7.f);
-            int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
+            const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -7.f), 7.f);
+            const int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
             w |= ((uint32_t)qi & 0xFu) << (4 * i);
             h[i] = sf * (float)qi;
         }
+        if (STATS) st.add8_slow(x, v, h, 7.f);
     }
     if (valid) {
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
         if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
     }
-    if (STATS) st.add8<IN, false>(ch, !fast, !fast || can_saturate(as_f(bits), sf, 7.f), (flag & 2u) != 0, x, v, h, 7.f);
 }
 
 template <int IN, int FMT, bool STATS>
@@ -888,13 +1051,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
     // Per-tensor quantities from the absmax pre-pass (uniform over the grid).
-    float s = 0.f, y = 0.f, alpha = 0.f;
-    bool fast = false;
+    float s = 0.f, y = 0.f;
+    bool fast = false, sat = true, zeros = true;
     if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2 || FMT == F_NVFP4) {
         s = a.info->scale;
-        alpha = as_f(a.info->amax_bits);
-        fast = a.info->nonfinite == 0 && stat_range(as_f(a.info->amax_bits));
-        if (fast && FMT != F_NVFP4) y = 1.0f / s;
+        zeros = a.info->zeros != 0;
+        const float alpha = as_f(a.info->amax_bits);
+        fast = a.info->nonfinite == 0 && stat_range(alpha);
+        if (fast && FMT != F_NVFP4) {
+            y = 1.0f / s;
+            sat = can_saturate(alpha, s, Fmt<FMT>::qmax);
+        }
     }
     // The next tile streams into LDS while the current one is processed.
     constexpr int NW = kTileChunksPerThread * ChunkWords<IN>::n;
@@ -931,14 +1098,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
                 quant_chunk_int4<IN, STATS>(ch[j], g[j], valid[j], a, st);
             } else {
                 float h[8];
-                quant_chunk_uniform<IN, FMT, STATS>(ch[j], alpha, s, y, fast, true, valid[j],
+                quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, sat, zeros, valid[j],
                                                     a.codes + (int64_t)g[j] * kChunk, h, st);
                 if (a.xhat && valid[j]) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g[j] * kChunk, h);
             }
         }
         if (STATS) st.fold();
     }
-    if (STATS) write_partial(st, a.partials);
+    if (STATS) write_partial<kThreads / 64>(st, a.partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -946,33 +1113,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
 // ---------------------------------------------------------------------------
 template <int IN>
 __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* partials) {
-    __shared__ uint32_t s_red[4][2];
+    __shared__ uint32_t s_red[2][kThreads / 64][2];
     const uint32_t ntiles = (geo.nchunks + kTileChunks - 1) / kTileChunks;
-    uint32_t m = 0, raw = Chunk<IN>::kMaxInit, z = Chunk<IN>::kMinInit;
+    uint32_t m = 0, raw = 0, mn = 0xFFFFFFFFu;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         Chunk<IN> ch[kTileChunksPerThread];
+        bool valid[kTileChunksPerThread];
 #pragma unroll
         for (int j = 0; j < kTileChunksPerThread; ++j) {
             uint32_t g = tile * kTileChunks + j * kThreads + threadIdx.x;
-            if (g < geo.nchunks) ch[j].load(geo.x, geo.elem(g));
+            valid[j] = g < geo.nchunks;
+            if (valid[j]) ch[j].load(geo.x, geo.elem(g));
             else ch[j].zero();
         }
 #pragma unroll
         for (int j = 0; j < kTileChunksPerThread; ++j) {
             m = umax(m, ch[j].absmax_finite());
-            ch[j].absmax(raw, z);
+            uint32_t wx, wn;
+            ch[j].absmaxmin_word(wx, wn);
+            raw = Chunk<IN>::hmax(raw, wx);
+            if (valid[j]) mn = Chunk<IN>::hmin(mn, wn);
         }
     }
-    uint32_t bits = m, flag, unused;
-    Chunk<IN>::absmax_finish(raw, z, unused, flag);
-    flag &= 1u;
-    wave_reduce_max_or(bits, flag);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { s_red[wave][0] = bits; s_red[wave][1] = flag; }
-    __syncthreads();
+    bool nonfinite, zeros;
+    const uint32_t bits = block_max_or<kThreads / 64>(m, Chunk<IN>::absmax_bits(raw) >= kNonFinite, nonfinite, s_red[0]);
+    block_max_or<kThreads / 64>(0u, Chunk<IN>::has_zero(mn), zeros, s_red[1]);
     if (threadIdx.x == 0) {
-        partials[2 * blockIdx.x] = umax(umax(s_red[0][0], s_red[1][0]), umax(s_red[2][0], s_red[3][0]));
-        partials[2 * blockIdx.x + 1] = s_red[0][1] | s_red[1][1] | s_red[2][1] | s_red[3][1];
+        partials[2 * blockIdx.x] = bits;
+        partials[2 * blockIdx.x + 1] = (nonfinite ? 1u : 0u) | (zeros ? 2u : 0u);
     }
 }
 
@@ -980,20 +1148,22 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* parti
 // NVFP4 global scale (amax / 2688); write them where the caller wants them.
 __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* partials, int n, float qdiv,
                                                             TensorInfo* info, float* scale_out, float* amax_out) {
+    __shared__ uint32_t s_red[2][kThreads / 64][2];
     uint32_t m = 0, f = 0;
     for (int i = threadIdx.x; i < n; i += kThreads) {
         m = umax(m, partials[2 * i]);
         f |= partials[2 * i + 1];
     }
-    __shared__ uint32_t s_red[4][2];
-    wave_reduce_max_or(m, f);
-    if ((threadIdx.x & 63) == 0) { s_red[threadIdx.x >> 6][0] = m; s_red[threadIdx.x >> 6][1] = f; }
-    __syncthreads();
+    bool nonfinite, zeros;
+    m = block_max_or<kThreads / 64>(m, (f & 1u) != 0, nonfinite, s_red[0]);
+    block_max_or<kThreads / 64>(0u, (f & 2u) != 0, zeros, s_red[1]);
     if (threadIdx.x == 0) {
-        m = umax(umax(s_red[0][0], s_red[1][0]), umax(s_red[2][0], s_red[3][0]));
-        f = s_red[0][1] | s_red[1][1] | s_red[2][1] | s_red[3][1];
-        float s = qdiv > 0.f ? as_f(m) / qdiv : 0.f;
-        if (info) { TensorInfo t; t.amax_bits = m; t.nonfinite = f; t.scale = s; t.pad = 0; *info = t; }
+        const float s = qdiv > 0.f ? as_f(m) / qdiv : 0.f;
+        if (info) {
+            TensorInfo t;
+            t.amax_bits = m; t.nonfinite = nonfinite ? 1u : 0u; t.scale = s; t.zeros = zeros ? 1u : 0u;
+            *info = t;
+        }
         if (scale_out) *scale_out = s;
         if (amax_out) *amax_out = as_f(m);
     }
@@ -1009,31 +1179,43 @@ struct StatsOut {   // mirrors iq_stats
     uint32_t reserved;
 };
 
-constexpr int kFinThreads = 1024;
-static_assert(kMaxGrid <= 2 * kFinThreads, "finalize covers two partials per thread");
+constexpr int kFinThreads = 256;
+constexpr int kFinPer = kMaxGrid / kFinThreads;   // partials per thread
 
+// Sum over the 64 lanes with a fixed butterfly (the same order on every run).
+template <typename T> __device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Thread t folds partials t, t + 256, ... in that order (all loads issued
+// before the first add), then lanes and waves combine in a fixed pattern.
 __global__ __launch_bounds__(kFinThreads) void k_stats_finalize(const Partial* p, int n, uint64_t nelem, StatsOut* out) {
     __shared__ double s_d[kFinThreads / 64][3];
     __shared__ float s_m[kFinThreads / 64];
     __shared__ uint64_t s_c[kFinThreads / 64][3];
     const int t = threadIdx.x;
-    // Two partials per thread, both loads issued before use; fixed order.
-    Partial z = {};
-    const Partial a0 = t < n ? p[t] : z;
-    const Partial a1 = t + kFinThreads < n ? p[t + kFinThreads] : z;
-    double a = a0.sum_x2 + a1.sum_x2, b = a0.sum_err2 + a1.sum_err2, c = a0.sum_abs_err + a1.sum_abs_err;
-    float m = __builtin_fmaxf(a0.max_abs_err, a1.max_abs_err);
-    uint64_t c0 = (uint64_t)a0.n_saturated + a1.n_saturated;
-    uint64_t c1 = (uint64_t)a0.n_zero_flush + a1.n_zero_flush;
-    uint64_t c2 = (uint64_t)a0.n_nonfinite + a1.n_nonfinite;
+    Partial q[kFinPer];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        a += __shfl_xor(a, o); b += __shfl_xor(b, o); c += __shfl_xor(c, o);
-        m = __builtin_fmaxf(m, __shfl_xor(m, o));
-        c0 += (uint64_t)__shfl_xor((unsigned long long)c0, o);
-        c1 += (uint64_t)__shfl_xor((unsigned long long)c1, o);
-        c2 += (uint64_t)__shfl_xor((unsigned long long)c2, o);
+    for (int k = 0; k < kFinPer; ++k) {
+        const int i = t + k * kFinThreads;
+        if (i < n) q[k] = p[i];
+        else q[k] = Partial{};
     }
+    double a = 0.0, b = 0.0, c = 0.0;
+    float m = 0.f;
+    uint64_t c0 = 0, c1 = 0, c2 = 0;
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) {
+        a += q[k].sum_x2; b += q[k].sum_err2; c += q[k].sum_abs_err;
+        m = __builtin_fmaxf(m, q[k].max_abs_err);
+        c0 += q[k].n_saturated; c1 += q[k].n_zero_flush; c2 += q[k].n_nonfinite;
+    }
+    a = wave_sum(a); b = wave_sum(b); c = wave_sum(c);
+    c0 = wave_sum(c0); c1 = wave_sum(c1); c2 = wave_sum(c2);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
     const int w = t >> 6;
     if ((t & 63) == 0) {
         s_d[w][0] = a; s_d[w][1] = b; s_d[w][2] = c; s_m[w] = m;
@@ -1042,13 +1224,15 @@ __global__ __launch_bounds__(kFinThreads) void k_stats_finalize(const Partial* p
     __syncthreads();
     if (t == 0) {
         StatsOut o;
-        o.n = nelem; o.n_saturated = 0; o.n_zero_flush = 0; o.n_nonfinite = 0;
-        o.sum_x2 = 0; o.sum_err2 = 0; o.sum_abs_err = 0; o.max_abs_err = 0.f; o.reserved = 0;
-        for (int k = 0; k < kFinThreads / 64; ++k) {
-            o.sum_x2 += s_d[k][0]; o.sum_err2 += s_d[k][1]; o.sum_abs_err += s_d[k][2];
-            o.max_abs_err = __builtin_fmaxf(o.max_abs_err, s_m[k]);
-            o.n_saturated += s_c[k][0]; o.n_zero_flush += s_c[k][1]; o.n_nonfinite += s_c[k][2];
-        }
+        o.n = nelem;
+        o.sum_x2 = (s_d[0][0] + s_d[1][0]) + (s_d[2][0] + s_d[3][0]);
+        o.sum_err2 = (s_d[0][1] + s_d[1][1]) + (s_d[2][1] + s_d[3][1]);
+        o.sum_abs_err = (s_d[0][2] + s_d[1][2]) + (s_d[2][2] + s_d[3][2]);
+        o.max_abs_err = __builtin_fmaxf(__builtin_fmaxf(s_m[0], s_m[1]), __builtin_fmaxf(s_m[2], s_m[3]));
+        o.n_saturated = s_c[0][0] + s_c[1][0] + s_c[2][0] + s_c[3][0];
+        o.n_zero_flush = s_c[0][1] + s_c[1][1] + s_c[2][1] + s_c[3][1];
+        o.n_nonfinite = s_c[0][2] + s_c[1][2] + s_c[2][2] + s_c[3][2];
+        o.reserved = 0;
         *out = o;
     }
 }
@@ -1177,30 +1361,49 @@ int resident_slots(const void* kernel, int threads) {
     return slots;
 }
 
-template <typename K> int grid_for(K kernel, uint64_t units) {
-    const int slots = resident_slots(reinterpret_cast<const void*>(kernel), kThreads);
+template <int NT = kThreads, typename K> int grid_for(K kernel, uint64_t units) {
+    const int slots = resident_slots(reinterpret_cast<const void*>(kernel), NT);
     if (units == 0) return 1;
     return units < (uint64_t)slots ? (int)units : slots;
 }
 
 uint32_t tiles_of(uint32_t nchunks) { return (nchunks + kTileChunks - 1) / kTileChunks; }
 
+template <int IN, int FMT, int CPT, int NT, bool STATS>
+void launch_row_k(const RowArgs& r, int& grid, hipStream_t s) {
+    if (r.cpr == CPT * NT) {
+        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, true, STATS>, (uint64_t)r.rows);
+        k_quant_row<IN, FMT, CPT, NT, true, STATS><<<grid, NT, 0, s>>>(r);
+    } else {
+        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, false, STATS>, (uint64_t)r.rows);
+        k_quant_row<IN, FMT, CPT, NT, false, STATS><<<grid, NT, 0, s>>>(r);
+    }
+}
+
+// Rows of up to 256 chunks take a one-wave workgroup (no cross-wave
+// reduction); longer rows four waves (up to 8 chunks per lane), beyond that
+// the two-pass kernel.  At 1024 chunks per row four waves with 4 chunks per
+// lane measure faster than one wave with 16 (whose 200 VGPRs halve the
+// resident waves).
 template <int IN, int FMT, bool STATS>
-hipError_t launch_row_t(const RowArgs& r, int cpt, int& grid, hipStream_t s) {
-    const uint64_t rows = (uint64_t)r.rows;
-    switch (cpt) {
-    case 1: grid = grid_for(k_quant_row<IN, FMT, 1, STATS>, rows); k_quant_row<IN, FMT, 1, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    case 2: grid = grid_for(k_quant_row<IN, FMT, 2, STATS>, rows); k_quant_row<IN, FMT, 2, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    case 4: grid = grid_for(k_quant_row<IN, FMT, 4, STATS>, rows); k_quant_row<IN, FMT, 4, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    case 8: grid = grid_for(k_quant_row<IN, FMT, 8, STATS>, rows); k_quant_row<IN, FMT, 8, STATS><<<grid, kThreads, 0, s>>>(r); break;
-    default: grid = grid_for(k_quant_row_long<IN, FMT, STATS>, rows); k_quant_row_long<IN, FMT, STATS><<<grid, kThreads, 0, s>>>(r); break;
+hipError_t launch_row_t(const RowArgs& r, int& grid, hipStream_t s) {
+    const int cpr = r.cpr;
+    if (cpr <= 64) launch_row_k<IN, FMT, 1, 64, STATS>(r, grid, s);
+    else if (cpr <= 128) launch_row_k<IN, FMT, 2, 64, STATS>(r, grid, s);
+    else if (cpr <= 256) launch_row_k<IN, FMT, 4, 64, STATS>(r, grid, s);
+    else if (cpr <= 512) launch_row_k<IN, FMT, 2, kThreads, STATS>(r, grid, s);
+    else if (cpr <= 1024) launch_row_k<IN, FMT, 4, kThreads, STATS>(r, grid, s);
+    else if (cpr <= 2048) launch_row_k<IN, FMT, 8, kThreads, STATS>(r, grid, s);
+    else {
+        grid = grid_for(k_quant_row_long<IN, FMT, STATS>, (uint64_t)r.rows);
+        k_quant_row_long<IN, FMT, STATS><<<grid, kThreads, 0, s>>>(r);
     }
     return hipGetLastError();
 }
 
 template <int IN, int FMT>
-hipError_t launch_row(const RowArgs& r, int cpt, bool stats, int& grid, hipStream_t s) {
-    return stats ? launch_row_t<IN, FMT, true>(r, cpt, grid, s) : launch_row_t<IN, FMT, false>(r, cpt, grid, s);
+hipError_t launch_row(const RowArgs& r, bool stats, int& grid, hipStream_t s) {
+    return stats ? launch_row_t<IN, FMT, true>(r, grid, s) : launch_row_t<IN, FMT, false>(r, grid, s);
 }
 
 template <int IN, int FMT>
@@ -1229,11 +1432,11 @@ hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, bool stats, int& grid, hi
 }
 
 template <int IN>
-hipError_t launch_row_fmt(int fmt, const RowArgs& r, int cpt, bool stats, int& grid, hipStream_t s) {
+hipError_t launch_row_fmt(int fmt, const RowArgs& r, bool stats, int& grid, hipStream_t s) {
     switch (fmt) {
-    case F_INT8: return launch_row<IN, F_INT8>(r, cpt, stats, grid, s);
-    case F_E4M3: return launch_row<IN, F_E4M3>(r, cpt, stats, grid, s);
-    default: return launch_row<IN, F_E5M2>(r, cpt, stats, grid, s);
+    case F_INT8: return launch_row<IN, F_INT8>(r, stats, grid, s);
+    case F_E4M3: return launch_row<IN, F_E4M3>(r, stats, grid, s);
+    default: return launch_row<IN, F_E5M2>(r, stats, grid, s);
     }
 }
 
@@ -1273,11 +1476,9 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         r.x = q.x; r.ld = q.ld; r.rows = (int32_t)q.rows; r.cpr = (int32_t)(q.cols / kChunk);
         r.codes = static_cast<uint8_t*>(q.codes); r.scales = static_cast<float*>(q.scales);
         r.xhat = q.xhat; r.xhat_dtype = q.xhat_dtype; r.partials = partials;
-        int per = (r.cpr + kThreads - 1) / kThreads;
-        int cpt = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
         if (nelem) {
-            e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, cpt, stats, grid, s)
-                                     : launch_row_fmt<D_F32>(q.fmt, r, cpt, stats, grid, s);
+            e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, stats, grid, s)
+                                     : launch_row_fmt<D_F32>(q.fmt, r, stats, grid, s);
         }
     } else {
         FlatArgs f;

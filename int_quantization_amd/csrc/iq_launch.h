@@ -19,7 +19,6 @@ constexpr int kChunk = 8;            // elements per chunk (one 16-byte BF16 loa
 constexpr int kTileChunksPerThread = 4;
 constexpr int kTileChunks = kThreads * kTileChunksPerThread;  // chunks per workgroup iteration
 constexpr int kMaxGrid = 2048;       // workgroups of the persistent streaming kernels
-constexpr int kRowCptMax = 8;        // register-resident row: up to 8 chunks per thread
 
 // Per-workgroup partial statistics, reduced by the finalize kernel in a fixed order.
 struct alignas(16) Partial {
@@ -35,7 +34,7 @@ struct alignas(16) TensorInfo {
     uint32_t amax_bits;   // absmax over finite elements (bits of a non-negative float)
     uint32_t nonfinite;   // nonzero if any element is NaN or +-Inf
     float scale;          // per-tensor scale (INT8/FP8) or NVFP4 global scale s_g
-    uint32_t pad;
+    uint32_t zeros;       // nonzero if any element is an exact zero
 };
 
 struct Workspace {

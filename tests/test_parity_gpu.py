@@ -390,3 +390,32 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
         assert got[3] == want[3], rep
         iq.quantize(x, "mxfp4", "block", workspace=ws)     # eager work on the same workspace between replays
         torch.cuda.synchronize()
+
+
+# ---- one workspace across many calls ------------------------------------------------
+def test_workspace_reuse_across_calls(iq, O, S):
+    """One workspace serves a sequence of calls with different grids, formats,
+    the absmax pre-pass and calls without statistics in between; every call's
+    outputs and statistics still match the oracle."""
+    import torch
+    plan = [("c2", 96, "e4m3", "row"), ("c4", 128, "nvfp4", "block"), ("c1", 64, "int8", "tensor"),
+            ("c3", 64, "mxfp4", "block"), ("c5", 32, "int4", "block"), ("c2", 3, "e5m2", "row"),
+            ("c1", 1, "e4m3", "tensor"), ("c2", 96, "e4m3", "row")]
+    ws = None
+    for name, nrows, fmt, gran in plan:
+        x_np = S.make(name, nrows=nrows)
+        x = to_device(x_np)
+        if ws is None:
+            ws = iq.workspace_for(iq.desc_for(x, fmt, gran), x.device)
+        iq.quantize(x, fmt, gran, stats=False, workspace=ws)          # a call without statistics in between
+        a = iq.amax(x, workspace=ws)
+        q = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle_ref(O, x_np, fmt, gran)
+        what = f"{name}[{nrows}] {fmt}/{gran} on a shared workspace"
+        assert np.float32(a.cpu().item()) == np.float32(O.amax(x_np)), what
+        g = {"codes": q.codes.cpu().numpy(), "scales": q.scales.cpu().numpy(), "stats": q.stats(),
+             "xhat": q.xhat.cpu().numpy()}
+        if q.global_scale is not None:
+            g["global_scale"] = q.global_scale.cpu().numpy()
+        compare(g, ref, fmt, what)
