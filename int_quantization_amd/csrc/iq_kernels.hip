@@ -460,9 +460,9 @@ __device__ void write_partial(Stats& st, Partial* out) {
 // Grids and their constants.
 // ---------------------------------------------------------------------------
 template <int FMT> struct Fmt;
-template <> struct Fmt<F_INT8> { static constexpr float qmax = 127.f; };
-template <> struct Fmt<F_E4M3> { static constexpr float qmax = 448.f; };
-template <> struct Fmt<F_E5M2> { static constexpr float qmax = 57344.f; };
+template <> struct Fmt<F_INT8> { static constexpr float qmax = 127.f; static constexpr int iq = 127; };
+template <> struct Fmt<F_E4M3> { static constexpr float qmax = 448.f; static constexpr int iq = 448; };
+template <> struct Fmt<F_E5M2> { static constexpr float qmax = 57344.f; static constexpr int iq = 57344; };
 template <> struct Fmt<F_MXFP4> { static constexpr float qmax = 6.f; };
 template <> struct Fmt<F_NVFP4> { static constexpr float qmax = 6.f; };
 template <> struct Fmt<F_INT4> { static constexpr float qmax = 7.f; };
@@ -476,10 +476,29 @@ __device__ __forceinline__ float markstein(float x, float s, float y) {
     return __builtin_fmaf(-r, y, q0);
 }
 
+// a / Q for a constant Q by the same correction with the compile-time
+// reciprocal RN(1/Q).  Checked against the correctly rounded quotient for
+// every finite binary32 a: equal for Q = 7 and 127 everywhere, and for
+// Q = 6, 448, 2688 and 57344 whenever the quotient is a normal number (the
+// only differences have subnormal quotients); callers take the division
+// for quotients below kMarksteinMin.
+constexpr float kMarksteinMin = 0x1p-100f;
+template <int QI> __device__ __forceinline__ float div_const(float a) {
+    constexpr float Q = (float)QI, r = 1.0f / (float)QI;
+    const float q0 = a * r;
+    const float e = __builtin_fmaf(-Q, q0, a);
+    return __builtin_fmaf(e, r, q0);
+}
+
 // Nonzero codes among the 4 bytes of w (INT8 / FP8: a code is zero iff its
 // low 7 bits are, -128 is never produced): bit 7 of (c & 0x7F) + 0x7F.
 __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
     return __builtin_popcount(((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u);
+}
+// Nonzero codes among the 8 nibbles of w (E2M1 and INT4: a code is zero iff
+// its low 3 bits are; INT4 never produces -8).
+__device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w) {
+    return __builtin_popcount(((w & 0x77777777u) + 0x77777777u) & 0x88888888u);
 }
 
 // FP8 pack / unpack (4 codes per 32-bit word, element 0 in the low byte).
@@ -736,9 +755,10 @@ __device__ __forceinline__ RowScale row_scale(const Chunk<IN> (&ch)[CPT], uint32
     const float alpha = as_f(bits);
     RowScale r;
     r.zeros = zeros;
-    r.s = alpha / Q;
     // fast: finite row with alpha in [2^-40, 2^60] (so s >= 2^-64)
     r.fast = !nonfinite && stat_range(alpha);
+    // alpha / Q: the constant-divisor correction is exact for normal quotients
+    r.s = stat_range(alpha) ? div_const<Fmt<FMT>::iq>(alpha) : alpha / Q;
     r.y = r.fast ? 1.0f / r.s : 0.f;
     // |v| > Q needs |x| > Q * s: only waves with such a lane test (per wave)
     r.sat = !r.fast || __ballot(can_saturate(as_f(lane_bits), r.s, Q)) != 0;
@@ -876,9 +896,10 @@ struct FlatArgs {
 // Absmax of a block spread over G lanes (G = 2, 4, 16): bits of the finite
 // maximum on every lane of the group; `nonfinite` if the block holds Inf/NaN.
 template <int IN, int G>
-__device__ __forceinline__ uint32_t unit_absmax(const Chunk<IN>& ch, bool& nonfinite) {
-    uint32_t m = 0;
-    ch.absmax(m);
+__device__ __forceinline__ uint32_t unit_absmax(const Chunk<IN>& ch, bool& nonfinite, bool& chunk_zero) {
+    uint32_t m, mn;
+    ch.absmaxmin_word(m, mn);
+    chunk_zero = Chunk<IN>::has_zero(mn);
     uint32_t bits = group_max<G>(Chunk<IN>::absmax_bits(m));
     nonfinite = bits >= kNonFinite;
     if (__ballot(nonfinite) != 0) {   // some block of the wave holds Inf or NaN
@@ -888,11 +909,20 @@ __device__ __forceinline__ uint32_t unit_absmax(const Chunk<IN>& ch, bool& nonfi
     return bits;
 }
 
+// Flushed elements of a chunk with nibble codes w: nonzero inputs (8 for a
+// lane with data unless some lane of the wave holds an exact zero) minus
+// nonzero codes.
+template <int IN>
+__device__ __forceinline__ void count_flush_nibbles(Stats& st, const Chunk<IN>& ch, bool valid, bool chunk_zero, uint32_t w) {
+    const uint32_t nzx = __ballot(chunk_zero) != 0 ? ch.nonzero_count() : (valid ? 8u : 0u);
+    st.count_flush(nzx, nonzero_nibbles(w));
+}
+
 // MXFP4: blocks of 32 = 4 chunks = 4 lanes.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    bool nonfinite;
-    const uint32_t bits = unit_absmax<IN, 4>(ch, nonfinite);
+    bool nonfinite, chunk_zero;
+    const uint32_t bits = unit_absmax<IN, 4>(ch, nonfinite, chunk_zero);
     int E = 0;
     if (bits) {
         int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
@@ -928,8 +958,12 @@ __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, 
         // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
         // when |x| > 6 * 2^(E-127) (both sides are exact near 6).
         const float thr = 6.0f * sc;
-        if (__ballot(nonfinite || !stat_range(as_f(bits))) == 0) st.add8_fast<IN, true>(ch, __ballot(as_f(bits) > thr) != 0, x, v, h, thr);
-        else st.add8_slow(x, x, h, thr);
+        if (__ballot(nonfinite || !stat_range(as_f(bits))) == 0) {
+            st.add8_fast<IN, true, false>(ch, __ballot(as_f(bits) > thr) != 0, x, v, h, thr);
+            count_flush_nibbles<IN>(st, ch, valid, chunk_zero, w);
+        } else {
+            st.add8_slow(x, x, h, thr);
+        }
     }
 }
 
@@ -958,19 +992,44 @@ __device__ __forceinline__ void fp4_unpack8(uint32_t w, float s, float (&h)[8]) 
     h[4] = s * p2.x; h[5] = s * p2.y; h[6] = s * p3.x; h[7] = s * p3.y;
 }
 
+// Per-launch NVFP4 constants: the global scale, its reciprocal, and for every
+// E4M3 block code c the block scale s_g * value(c) with its correctly
+// rounded reciprocal (LDS, filled once per workgroup).
+struct NvConst {
+    float s_g, y_g;
+    bool g_fast;          // s_g >= kMarksteinMin: the block-scale quotient may use the correction
+    const f2v* tab;       // [128] {s_nv, 1 / s_nv}
+};
+
+// Block scale code: smallest E4M3 >= (A / 6) / s_g.  Both quotients come
+// from the correction step when they are normal and the global scale is
+// not tiny; other lanes (A tiny, block maxima far below the tensor's) take
+// the two divisions.
+__device__ __forceinline__ uint32_t nv_block_code(float A, const NvConst& k) {
+    const float t1 = div_const<6>(A);
+    const float t = markstein(t1, k.s_g, k.y_g);
+    const bool exact = A == 0.f || (t1 >= kMarksteinMin && t >= kMarksteinMin && t <= 0x1p120f);
+    float tt = t;
+    if (__ballot(!(exact && k.g_fast)) != 0) {
+        if (!(exact && k.g_fast)) tt = (A / 6.0f) / k.s_g;
+    }
+    return e4m3_ceil(tt);
+}
+
 // NVFP4: blocks of 16 = 2 chunks = 2 lanes.  The wave takes the fast path
 // when every lane's block is finite with a scale in the fast range; the
 // slow path (correctly rounded division, patches) is exact for every lane.
 template <int IN, bool STATS>
-__device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, bool valid, float s_g, const FlatArgs& a, Stats& st) {
-    bool nonfinite;
-    const uint32_t bits = unit_absmax<IN, 2>(ch, nonfinite);
+__device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, bool valid, const NvConst& k,
+                                               const FlatArgs& a, Stats& st) {
+    bool nonfinite, chunk_zero;
+    const uint32_t bits = unit_absmax<IN, 2>(ch, nonfinite, chunk_zero);
     uint32_t sb = 0;
-    float s_nv = 0.f;
-    if (s_g != 0.f) {
-        const float t = (as_f(bits) / 6.0f) / s_g;
-        sb = e4m3_ceil(t);
-        s_nv = s_g * e4m3_value(sb);
+    float s_nv = 0.f, y = 0.f;
+    if (k.s_g != 0.f) {
+        sb = nv_block_code(as_f(bits), k);
+        const f2v e = k.tab[sb];
+        s_nv = e.x; y = e.y;
     }
     if (valid && (g & 1u) == 0) static_cast<uint8_t*>(a.scales)[g >> 1] = (uint8_t)sb;
     const bool fast = !nonfinite && s_nv >= kTinyScale && stat_range(as_f(bits));
@@ -979,12 +1038,14 @@ __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, 
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
     uint32_t w;
     if (__ballot(!fast) == 0) {
-        const float y = 1.0f / s_nv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s_nv, y);
         w = fp4_pack8(v);
         fp4_unpack8(w, s_nv, h);
-        if (STATS) st.add8_fast<IN, false>(ch, __ballot(can_saturate(as_f(bits), s_nv, 6.f)) != 0, x, v, h, 6.f);
+        if (STATS) {
+            st.add8_fast<IN, false, false>(ch, __ballot(can_saturate(as_f(bits), s_nv, 6.f)) != 0, x, v, h, 6.f);
+            count_flush_nibbles<IN>(st, ch, valid, chunk_zero, w);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (s_nv == 0.f) ? 0.f : x[i] / s_nv;
@@ -1003,11 +1064,19 @@ __device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, 
 }
 
 // INT4: groups of 128 = 16 chunks = 16 lanes; FP16 scale fp16(A / 7), saturated.
+// rtab[f] = RN(1 / (1 + f / 1024)): the reciprocal of a normal FP16 scale
+// 2^e (1 + f / 1024) is rtab[f] * 2^-e exactly (a power-of-two scaling of a
+// normal binary32).
 template <int IN, bool STATS>
-__device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    bool nonfinite;
-    const uint32_t bits = unit_absmax<IN, 16>(ch, nonfinite);
-    const float s32 = as_f(bits) / 7.0f;
+__device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g, bool valid, const float* rtab,
+                                                 const FlatArgs& a, Stats& st) {
+    bool nonfinite, chunk_zero;
+    const uint32_t bits = unit_absmax<IN, 16>(ch, nonfinite, chunk_zero);
+    float s32 = div_const<7>(as_f(bits));              // the correctly rounded A / 7 for every finite A
+    // The FP32 quotient must be rounded to FP32 before the FP16 cast: without
+    // this barrier the compiler fuses the last fma with the cast into one
+    // fma with an FP16 result (a single rounding, different on FP16 ties).
+    asm volatile("" : "+v"(s32));
     _Float16 hs = (_Float16)s32;                       // RNE
     uint16_t s16 = s32 > 65504.f ? (uint16_t)0x7BFF : __builtin_bit_cast(uint16_t, hs);
     const float sf = (float)__builtin_bit_cast(_Float16, s16);
@@ -1020,15 +1089,22 @@ __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
     uint32_t w = 0;
     if (__ballot(!fast) == 0) {
-        const float y = 1.0f / sf;
+        const int ex = (int)((s16 >> 10) & 0x1Fu) - 15;
+        const float y = __builtin_amdgcn_ldexpf(rtab[s16 & 0x3FFu], -ex);
+        // x^ = sf * q = fma(sf, t, -sf * kMagic): sf * kMagic and sf * q are
+        // exact (11 + 2 and 11 + 3 significant bits), so the fma is exact.
+        const float sfm = sf * kMagic;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             v[i] = markstein(x[i], sf, y);
             const float t = v[i] + kMagic;
             w |= (as_u(t) & 0xFu) << (4 * i);
-            h[i] = sf * (t - kMagic);
+            h[i] = __builtin_fmaf(sf, t, -sfm);
         }
-        if (STATS) st.add8_fast<IN, false>(ch, __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0, x, v, h, 7.f);
+        if (STATS) {
+            st.add8_fast<IN, false, false>(ch, __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0, x, v, h, 7.f);
+            count_flush_nibbles<IN>(st, ch, valid, chunk_zero, w);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -1063,6 +1139,29 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
             sat = can_saturate(alpha, s, Fmt<FMT>::qmax);
         }
     }
+    // Reciprocal tables, filled once per workgroup with correctly rounded divisions.
+    __shared__ f2v s_nvtab[FMT == F_NVFP4 ? 128 : 1];
+    __shared__ float s_rtab[FMT == F_INT4 ? 1024 : 1];
+    NvConst nk;
+    nk.s_g = s; nk.y_g = 0.f; nk.g_fast = false; nk.tab = s_nvtab;
+    if (FMT == F_NVFP4) {
+        if (s != 0.f) {
+            nk.y_g = 1.0f / s;
+            nk.g_fast = s >= kMarksteinMin;
+        }
+        if (threadIdx.x < 128) {
+            const float sn = s * e4m3_value(threadIdx.x);
+            f2v e;
+            e.x = sn;
+            e.y = sn > 0.f ? 1.0f / sn : 0.f;
+            s_nvtab[threadIdx.x] = e;
+        }
+        __syncthreads();
+    }
+    if (FMT == F_INT4) {
+        for (int f = threadIdx.x; f < 1024; f += kThreads) s_rtab[f] = 1.0f / (1.0f + (float)f * 0x1p-10f);
+        __syncthreads();
+    }
     // The next tile streams into LDS while the current one is processed.
     constexpr int NW = kTileChunksPerThread * ChunkWords<IN>::n;
     __shared__ Stage<NW> stage;
@@ -1093,9 +1192,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
             if (FMT == F_MXFP4) {
                 quant_chunk_mx<IN, STATS>(ch[j], g[j], valid[j], a, st);
             } else if (FMT == F_NVFP4) {
-                quant_chunk_nv<IN, STATS>(ch[j], g[j], valid[j], s, a, st);
+                quant_chunk_nv<IN, STATS>(ch[j], g[j], valid[j], nk, a, st);
             } else if (FMT == F_INT4) {
-                quant_chunk_int4<IN, STATS>(ch[j], g[j], valid[j], a, st);
+                quant_chunk_int4<IN, STATS>(ch[j], g[j], valid[j], s_rtab, a, st);
             } else {
                 float h[8];
                 quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, sat, zeros, valid[j],

@@ -419,3 +419,43 @@ def test_workspace_reuse_across_calls(iq, O, S):
         if q.global_scale is not None:
             g["global_scale"] = q.global_scale.cpu().numpy()
         compare(g, ref, fmt, what)
+
+
+# ---- tiny magnitudes: global and block scales near the bottom of the range ------------
+@pytest.mark.parametrize("fmt,gran", ALL)
+@pytest.mark.parametrize("shift", [60, 100, 118, 126, 130])
+def test_tiny_magnitudes(iq, O, S, fmt, gran, shift):
+    """The activation workload scaled by 2^-shift (BF16, subnormals included):
+    quotients and scales that leave the normal range take the correctly
+    rounded divisions; every output still matches the oracle."""
+    x32 = S.bf16_to_f32(S.make("c2", nrows=48)) * np.float32(2.0 ** -shift)
+    x = S.f32_to_bf16_bits(x32.astype(np.float32))
+    g = run_gpu(iq, x, fmt, gran)
+    r = oracle_ref(O, x, fmt, gran)
+    compare(g, r, fmt, f"{fmt}/{gran} x 2^-{shift}", O)
+
+
+# ---- INT4: group maxima whose A / 7 is an exact FP16 tie ---------------------------------
+@pytest.mark.parametrize("dtype", [0, 1], ids=["f32", "bf16"])
+def test_int4_fp16_scale_ties(iq, O, S, dtype):
+    """Every group's maximum is 7 * m with m halfway between two FP16 values,
+    so A / 7 = m exactly and the FP16 scale is decided by ties-to-even after
+    the FP32 quotient (a fused fma-to-FP16 would round once and differ)."""
+    rng = np.random.default_rng(23)
+    rows, cols = 64, 1024
+    ng = cols // 128
+    k = rng.integers(0, 1024, (rows, ng))
+    e = rng.integers(-10, 12, (rows, ng))
+    m = (1.0 + (2 * k + 1) / 2048.0) * np.exp2(e)              # FP16 midpoints (12 significant bits)
+    A = (7.0 * m).astype(np.float32)                          # exact: 15 significant bits
+    if dtype:                                                 # BF16 keeps 8 bits: use maxima it can hold
+        A = S.bf16_to_f32(S.f32_to_bf16_bits(A))
+    x = (rng.standard_normal((rows, cols)) * 0.3).astype(np.float32) * np.repeat(A, 128, axis=1) / 4
+    x = np.clip(x, -np.repeat(A, 128, axis=1), np.repeat(A, 128, axis=1)).astype(np.float32)
+    pos = rng.integers(0, 128, (rows, ng)) + np.arange(ng) * 128
+    np.put_along_axis(x, pos, A * np.where(rng.random((rows, ng)) < 0.5, -1, 1).astype(np.float32), axis=1)
+    if dtype:
+        x = S.f32_to_bf16_bits(x)
+    g = run_gpu(iq, x, "int4", "block")
+    r = oracle_ref(O, x, "int4", "block")
+    compare(g, r, "int4", f"int4 FP16 scale ties ({'bf16' if dtype else 'f32'})", O)
