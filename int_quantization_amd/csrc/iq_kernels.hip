@@ -918,11 +918,58 @@ __device__ __forceinline__ void count_flush_nibbles(Stats& st, const Chunk<IN>& 
     st.count_flush(nzx, nonzero_nibbles(w));
 }
 
-// MXFP4: blocks of 32 = 4 chunks = 4 lanes.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
+// Absmax over chunks [k0, k0 + K) of the lane: FP32 bits of the finite
+// maximum, whether an Inf or NaN is present, whether an exact zero is.
+template <int IN, int K>
+__device__ __forceinline__ uint32_t lane_absmax(const Chunk<IN> (&ch)[kTileChunksPerThread], int k0, bool& nonfinite,
+                                                bool& zero) {
+    uint32_t m, mn;
+    ch[k0].absmaxmin_word(m, mn);
+#pragma unroll
+    for (int k = 1; k < K; ++k) {
+        uint32_t a, b;
+        ch[k0 + k].absmaxmin_word(a, b);
+        m = Chunk<IN>::hmax(m, a);
+        mn = Chunk<IN>::hmin(mn, b);
+    }
+    const uint32_t bits = Chunk<IN>::absmax_bits(m);
+    nonfinite = bits >= kNonFinite;
+    zero = Chunk<IN>::has_zero(mn);
+    return bits;
+}
+
+template <int IN, int K>
+__device__ __forceinline__ uint32_t lane_absmax_finite(const Chunk<IN> (&ch)[kTileChunksPerThread], int k0) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) f = umax(f, ch[k0 + k].absmax_finite());
+    return f;
+}
+
+// Store the 4 code words of the lane (one 16-byte store when all are valid).
+__device__ __forceinline__ void store_words4(uint8_t* codes, uint32_t g0, uint32_t nvalid, const uint32_t (&w)[4]) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(codes) + g0;
+    if (nvalid == 4) {
+        const u4v o = {w[0], w[1], w[2], w[3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<u4v*>(p));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if ((uint32_t)k < nvalid) __builtin_nontemporal_store(w[k], p + k);
+    }
+}
+
+// MXFP4: one block of 32 = the lane's 4 chunks.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
+// g0 is the lane's first chunk (a multiple of 4), nvalid its chunks with
+// data (0 or 4: the row length is a multiple of 32).
 template <int IN, bool STATS>
-__device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, bool valid, const FlatArgs& a, Stats& st) {
-    bool nonfinite, chunk_zero;
-    const uint32_t bits = unit_absmax<IN, 4>(ch, nonfinite, chunk_zero);
+__device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
+                                              const FlatArgs& a, Stats& st) {
+    bool nonfinite, zero;
+    uint32_t bits = lane_absmax<IN, 4>(ch, 0, nonfinite, zero);
+    if (__ballot(nonfinite) != 0) {
+        if (nonfinite) bits = lane_absmax_finite<IN, 4>(ch, 0);
+    }
     int E = 0;
     if (bits) {
         int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
@@ -930,41 +977,47 @@ __device__ __forceinline__ void quant_chunk_mx(const Chunk<IN>& ch, uint32_t g, 
         E = E < 0 ? 0 : (E > 254 ? 254 : E);
     }
     const float sc = E ? as_f((uint32_t)E << 23) : as_f(0x00400000u);   // 2^(E-127), exact
-    if (valid && (g & 3u) == 0) static_cast<uint8_t*>(a.scales)[g >> 2] = (uint8_t)E;
-    float x[8], v[8], h[8];
+    const bool valid = nvalid != 0;
+    if (valid) static_cast<uint8_t*>(a.scales)[g0 >> 2] = (uint8_t)E;
+    // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
+    // when |x| > 6 * 2^(E-127) (both sides are exact near 6).
+    const float thr = 6.0f * sc;
+    const bool slow = __ballot(nonfinite || !stat_range(as_f(bits))) != 0;
+    const bool sat = __ballot(as_f(bits) > thr) != 0;
+    uint32_t wq[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
-    uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], sc, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
-    if (nonfinite) {
-        // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
+    for (int k = 0; k < 4; ++k) {
+        float x[8], v[8], h[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (__builtin_isnan(x[i])) w &= ~(0xFu << (4 * i));
-    }
-    const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
-    const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
-    const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
-    const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
-    h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
-    if (valid) {
-        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
-        if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
-    }
-    if (STATS) {
-        // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
-        // when |x| > 6 * 2^(E-127) (both sides are exact near 6).
-        const float thr = 6.0f * sc;
-        if (__ballot(nonfinite || !stat_range(as_f(bits))) == 0) {
-            st.add8_fast<IN, true, false>(ch, __ballot(as_f(bits) > thr) != 0, x, v, h, thr);
-            count_flush_nibbles<IN>(st, ch, valid, chunk_zero, w);
-        } else {
-            st.add8_slow(x, x, h, thr);
+        for (int i = 0; i < 8; ++i) x[i] = ch[k].get(i);
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], sc, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
+        if (nonfinite) {
+            // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (__builtin_isnan(x[i])) w &= ~(0xFu << (4 * i));
         }
+        const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+        const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+        const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+        const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+        h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
+        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + k) * kChunk, h);
+        if (STATS) {
+            if (!slow) {
+                st.add8_fast<IN, true, false>(ch[k], sat, x, v, h, thr);
+                count_flush_nibbles<IN>(st, ch[k], valid, zero, w);
+            } else {
+                st.add8_slow(x, x, h, thr);
+            }
+        }
+        wq[k] = w;
     }
+    store_words4(a.codes, g0, nvalid, wq);
 }
 
 // Smallest E4M3 code whose value is >= t (t >= 0, finite), capped at 448.
@@ -1016,62 +1069,103 @@ __device__ __forceinline__ uint32_t nv_block_code(float A, const NvConst& k) {
     return e4m3_ceil(tt);
 }
 
-// NVFP4: blocks of 16 = 2 chunks = 2 lanes.  The wave takes the fast path
-// when every lane's block is finite with a scale in the fast range; the
-// slow path (correctly rounded division, patches) is exact for every lane.
+// NVFP4: blocks of 16 = 2 chunks; the lane holds blocks (0, 1) and (2, 3) of
+// its chunks.  The wave takes the fast path when every lane's blocks are
+// finite with scales in the fast range; the slow path (correctly rounded
+// division, patches) is exact for every lane.
 template <int IN, bool STATS>
-__device__ __forceinline__ void quant_chunk_nv(const Chunk<IN>& ch, uint32_t g, bool valid, const NvConst& k,
-                                               const FlatArgs& a, Stats& st) {
-    bool nonfinite, chunk_zero;
-    const uint32_t bits = unit_absmax<IN, 2>(ch, nonfinite, chunk_zero);
-    uint32_t sb = 0;
-    float s_nv = 0.f, y = 0.f;
+__device__ __forceinline__ void quant_lane_nv(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
+                                              const NvConst& k, const FlatArgs& a, Stats& st) {
+    bool nonfinite[2], zero[2];
+    uint32_t bits[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bits[b] = lane_absmax<IN, 2>(ch, 2 * b, nonfinite[b], zero[b]);
+    if (__ballot(nonfinite[0] || nonfinite[1]) != 0) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            if (nonfinite[b]) bits[b] = lane_absmax_finite<IN, 2>(ch, 2 * b);
+    }
+    uint32_t sb[2] = {0u, 0u};
+    float s_nv[2] = {0.f, 0.f}, y[2] = {0.f, 0.f};
     if (k.s_g != 0.f) {
-        sb = nv_block_code(as_f(bits), k);
-        const f2v e = k.tab[sb];
-        s_nv = e.x; y = e.y;
-    }
-    if (valid && (g & 1u) == 0) static_cast<uint8_t*>(a.scales)[g >> 1] = (uint8_t)sb;
-    const bool fast = !nonfinite && s_nv >= kTinyScale && stat_range(as_f(bits));
-    float x[8], v[8], h[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
-    uint32_t w;
-    if (__ballot(!fast) == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s_nv, y);
-        w = fp4_pack8(v);
-        fp4_unpack8(w, s_nv, h);
-        if (STATS) {
-            st.add8_fast<IN, false, false>(ch, __ballot(can_saturate(as_f(bits), s_nv, 6.f)) != 0, x, v, h, 6.f);
-            count_flush_nibbles<IN>(st, ch, valid, chunk_zero, w);
+        for (int b = 0; b < 2; ++b) {
+            sb[b] = nv_block_code(as_f(bits[b]), k);
+            const f2v e = k.tab[sb[b]];
+            s_nv[b] = e.x; y[b] = e.y;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (s_nv == 0.f) ? 0.f : x[i] / s_nv;
-        w = fp4_pack8(v);
-        if (s_nv == 0.f) w = 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (__builtin_isnan(v[i])) w &= ~(0xFu << (4 * i));
-        fp4_unpack8(w, s_nv, h);
-        if (STATS) st.add8_slow(x, v, h, 6.f);
     }
-    if (valid) {
-        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
-        if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
+    uint8_t* sc8 = static_cast<uint8_t*>(a.scales) + (g0 >> 1);
+    if (nvalid == 4) *reinterpret_cast<uint16_t*>(sc8) = (uint16_t)(sb[0] | (sb[1] << 8));
+    else if (nvalid >= 2) *sc8 = (uint8_t)sb[0];
+    bool fast = true, satl = false;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        fast = fast && !nonfinite[b] && s_nv[b] >= kTinyScale && stat_range(as_f(bits[b]));
+        satl = satl || can_saturate(as_f(bits[b]), s_nv[b], 6.f);
     }
+    const bool all_fast = __ballot(!fast) == 0;
+    const bool sat = __ballot(satl) != 0;
+    uint32_t wq[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float s = s_nv[c >> 1], yy = y[c >> 1];
+        const bool valid = (uint32_t)c < nvalid;
+        float x[8], v[8], h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = ch[c].get(i);
+        uint32_t w;
+        if (all_fast) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s, yy);
+            w = fp4_pack8(v);
+            fp4_unpack8(w, s, h);
+            if (STATS) {
+                st.add8_fast<IN, false, false>(ch[c], sat, x, v, h, 6.f);
+                count_flush_nibbles<IN>(st, ch[c], valid, zero[c >> 1], w);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = (s == 0.f) ? 0.f : x[i] / s;
+            w = fp4_pack8(v);
+            if (s == 0.f) w = 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (__builtin_isnan(v[i])) w &= ~(0xFu << (4 * i));
+            fp4_unpack8(w, s, h);
+            if (STATS) st.add8_slow(x, v, h, 6.f);
+        }
+        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+        wq[c] = w;
+    }
+    store_words4(a.codes, g0, nvalid, wq);
 }
 
-// INT4: groups of 128 = 16 chunks = 16 lanes; FP16 scale fp16(A / 7), saturated.
+// 8 INT4 codes from t = v + 1.5 * 2^23 (the low nibble of each t is the
+// two's-complement code): nibble pairs in the low byte, then bytes gathered.
+__device__ __forceinline__ uint32_t int4_pack8(const float (&t)[8]) {
+    uint32_t p[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = (as_u(t[2 * k + 1]) << 4) | (as_u(t[2 * k]) & 0xFu);
+    const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0c0c0400u);   // bytes {p0.b0, p1.b0, 0, 0}
+    const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x0c0c0400u);
+    return lo | (hi << 16);
+}
+
+// INT4: groups of 128 = 16 chunks = 4 lanes; FP16 scale fp16(A / 7), saturated.
 // rtab[f] = RN(1 / (1 + f / 1024)): the reciprocal of a normal FP16 scale
 // 2^e (1 + f / 1024) is rtab[f] * 2^-e exactly (a power-of-two scaling of a
 // normal binary32).
 template <int IN, bool STATS>
-__device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g, bool valid, const float* rtab,
-                                                 const FlatArgs& a, Stats& st) {
-    bool nonfinite, chunk_zero;
-    const uint32_t bits = unit_absmax<IN, 16>(ch, nonfinite, chunk_zero);
+__device__ __forceinline__ void quant_lane_int4(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
+                                                const float* rtab, const FlatArgs& a, Stats& st) {
+    bool nonfinite_l, zero;
+    uint32_t bits = group_max<4>(lane_absmax<IN, 4>(ch, 0, nonfinite_l, zero));
+    const bool nonfinite = group_max<4>(nonfinite_l ? 1u : 0u) != 0;
+    if (__ballot(nonfinite) != 0) {
+        const uint32_t f = group_max<4>(lane_absmax_finite<IN, 4>(ch, 0));
+        if (nonfinite) bits = f;
+    }
     float s32 = div_const<7>(as_f(bits));              // the correctly rounded A / 7 for every finite A
     // The FP32 quotient must be rounded to FP32 before the FP16 cast: without
     // this barrier the compiler fuses the last fma with the cast into one
@@ -1080,50 +1174,112 @@ __device__ __forceinline__ void quant_chunk_int4(const Chunk<IN>& ch, uint32_t g
     _Float16 hs = (_Float16)s32;                       // RNE
     uint16_t s16 = s32 > 65504.f ? (uint16_t)0x7BFF : __builtin_bit_cast(uint16_t, hs);
     const float sf = (float)__builtin_bit_cast(_Float16, s16);
-    if (valid && (g & 15u) == 0) static_cast<uint16_t*>(a.scales)[g >> 4] = s16;
+    if (nvalid != 0 && (g0 & 15u) == 0) static_cast<uint16_t*>(a.scales)[g0 >> 4] = s16;
     // fast: finite inputs and a normal, unsaturated FP16 scale keep |x/sf| < 7.5
     // (and put A = 7 sf inside the FP32 statistics range)
     const bool fast = !nonfinite && sf >= 0x1p-14f && s32 <= 65504.f;
-    float x[8], v[8], h[8];
+    const bool all_fast = __ballot(!fast) == 0;
+    const bool sat = __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0;
+    const int ex = (int)((s16 >> 10) & 0x1Fu) - 15;
+    const float y = all_fast ? __builtin_amdgcn_ldexpf(rtab[s16 & 0x3FFu], -ex) : 0.f;
+    // x^ = sf * q = fma(sf, t, -sf * kMagic): sf * kMagic and sf * q are
+    // exact (11 + 2 and 11 + 3 significant bits), so the fma is exact.
+    const float sfm = sf * kMagic;
+    uint32_t wq[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
-    uint32_t w = 0;
-    if (__ballot(!fast) == 0) {
-        const int ex = (int)((s16 >> 10) & 0x1Fu) - 15;
-        const float y = __builtin_amdgcn_ldexpf(rtab[s16 & 0x3FFu], -ex);
-        // x^ = sf * q = fma(sf, t, -sf * kMagic): sf * kMagic and sf * q are
-        // exact (11 + 2 and 11 + 3 significant bits), so the fma is exact.
-        const float sfm = sf * kMagic;
+    for (int c = 0; c < 4; ++c) {
+        const bool valid = (uint32_t)c < nvalid;
+        float x[8], v[8], h[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[i] = markstein(x[i], sf, y);
-            const float t = v[i] + kMagic;
-            w |= (as_u(t) & 0xFu) << (4 * i);
-            h[i] = __builtin_fmaf(sf, t, -sfm);
+        for (int i = 0; i < 8; ++i) x[i] = ch[c].get(i);
+        uint32_t w = 0;
+        if (all_fast) {
+            float t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[i] = markstein(x[i], sf, y);
+                t[i] = v[i] + kMagic;
+                h[i] = __builtin_fmaf(sf, t[i], -sfm);
+            }
+            w = int4_pack8(t);
+            if (STATS) {
+                st.add8_fast<IN, false, false>(ch[c], sat, x, v, h, 7.f);
+                count_flush_nibbles<IN>(st, ch[c], valid, zero, w);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[i] = (sf == 0.f) ? 0.f : x[i] / sf;
+                const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -7.f), 7.f);
+                const int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
+                w |= ((uint32_t)qi & 0xFu) << (4 * i);
+                h[i] = sf * (float)qi;
+            }
+            if (STATS) st.add8_slow(x, v, h, 7.f);
         }
-        if (STATS) {
-            st.add8_fast<IN, false, false>(ch, __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0, x, v, h, 7.f);
-            count_flush_nibbles<IN>(st, ch, valid, chunk_zero, w);
-        }
+        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+        wq[c] = w;
+    }
+    store_words4(a.codes, g0, nvalid, wq);
+}
+
+// ---------------------------------------------------------------------------
+// Flat tiles.  A workgroup iteration covers kTileChunks = 1024 consecutive
+// chunks; lane l of wave w owns the 4 consecutive chunks 256 w + 4 l + k of
+// the tile (32 elements: one MXFP4 block, two NVFP4 blocks, a quarter of an
+// INT4 group).  The HBM -> LDS copies keep each instruction on 1 KiB of
+// consecutive input: lane i of copy j fetches 16-byte word 64 j + unswz(i)
+// of the wave's region, so word o lands in column swz(o mod 64) of row
+// o / 64; a lane's reads of its own words then fall in distinct banks within
+// every group of 8 lanes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t swz(uint32_t o) { return (o & ~7u) | ((o + (o >> 3)) & 7u); }
+__device__ __forceinline__ uint32_t unswz(uint32_t i) { return (i & ~7u) | ((i - (i >> 3)) & 7u); }
+
+// Per-tensor constants of the flat kernel.
+struct FlatConst {
+    float s, y;
+    bool fast, sat, zeros;
+    NvConst nk;
+    const float* rtab;
+};
+
+// One tile's worth of the lane's chunks (wd: its 16-byte words from LDS).
+// FULL: every chunk of the tile holds data (no per-chunk validity selects).
+template <int IN, int FMT, bool STATS, bool FULL>
+__device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread * ChunkWords<IN>::n], uint32_t g0,
+                                          uint32_t nchunks, const FlatConst& k, const FlatArgs& a, Stats& st) {
+    constexpr int W = ChunkWords<IN>::n;
+    const uint32_t nvalid = FULL ? 4u : (g0 >= nchunks ? 0u : min(4u, nchunks - g0));
+    Chunk<IN> ch[kTileChunksPerThread];
+#pragma unroll
+    for (int c = 0; c < kTileChunksPerThread; ++c) {
+        if (FULL || (uint32_t)c < nvalid) ch[c].set(&wd[c * W], 1);
+        else ch[c].zero();
+    }
+    if (FMT == F_MXFP4) {
+        quant_lane_mx<IN, STATS>(ch, g0, nvalid, a, st);
+    } else if (FMT == F_NVFP4) {
+        quant_lane_nv<IN, STATS>(ch, g0, nvalid, k.nk, a, st);
+    } else if (FMT == F_INT4) {
+        quant_lane_int4<IN, STATS>(ch, g0, nvalid, k.rtab, a, st);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[i] = (sf == 0.f) ? 0.f : x[i] / sf;
-            const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -7.f), 7.f);
-            const int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
-            w |= ((uint32_t)qi & 0xFu) << (4 * i);
-            h[i] = sf * (float)qi;
+        for (int c = 0; c < kTileChunksPerThread; ++c) {
+            const bool valid = FULL || (uint32_t)c < nvalid;
+            float h[8];
+            quant_chunk_uniform<IN, FMT, STATS>(ch[c], k.s, k.y, k.fast, k.sat, k.zeros, valid,
+                                                a.codes + (int64_t)(g0 + c) * kChunk, h, st);
+            if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
         }
-        if (STATS) st.add8_slow(x, v, h, 7.f);
-    }
-    if (valid) {
-        __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(a.codes) + g);
-        if (a.xhat) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
     }
 }
 
 template <int IN, int FMT, bool STATS>
 __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
+    constexpr int W = ChunkWords<IN>::n;
+    constexpr int NW = kTileChunksPerThread * W;      // 16-byte words per lane = copies per wave and tile
+    static_assert(kTileChunksPerThread == 4, "lane layout assumes 4 chunks per lane");
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
     // Per-tensor quantities from the absmax pre-pass (uniform over the grid).
@@ -1162,46 +1318,48 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
         for (int f = threadIdx.x; f < 1024; f += kThreads) s_rtab[f] = 1.0f / (1.0f + (float)f * 0x1p-10f);
         __syncthreads();
     }
-    // The next tile streams into LDS while the current one is processed.
-    constexpr int NW = kTileChunksPerThread * ChunkWords<IN>::n;
     __shared__ Stage<NW> stage;
+    const uint32_t lane = threadIdx.x & 63u;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t dlane = unswz(lane);
+    const uint32_t esize = IN == D_BF16 ? 2u : 4u;
     auto stage_tile = [&](uint32_t tile) {
+        const uint32_t base = tile * kTileChunks + 256u * wave;
+        if (a.geo.contiguous) {
+            // word ow of the wave's region is the (base * W + ow)-th 16-byte word of x
+            const char* wp = static_cast<const char*>(a.geo.x) + (size_t)base * W * 16u;
 #pragma unroll
-        for (int j = 0; j < kTileChunksPerThread; ++j) {
-            const uint32_t g = tile * kTileChunks + j * kThreads + threadIdx.x;
-            if (g < a.geo.nchunks) stage_chunk<IN, NW>(stage, j * ChunkWords<IN>::n, a.geo.x, a.geo.elem(g));
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t ow = 64u * j + dlane;
+                if (base + ow / W < a.geo.nchunks) dma_word(wp + ow * 16u, &stage[j][64 * wave]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t ow = 64u * j + dlane;                // word of the wave's region
+                const uint32_t c = base + ow / W;
+                if (c < a.geo.nchunks)
+                    dma_word(static_cast<const char*>(a.geo.x) + a.geo.elem(c) * esize + 16u * (ow % W), &stage[j][64 * wave]);
+            }
         }
     };
     if (blockIdx.x < ntiles) stage_tile(blockIdx.x);
+    FlatConst fk;
+    fk.s = s; fk.y = y; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
+    const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        Chunk<IN> ch[kTileChunksPerThread];
-        uint32_t g[kTileChunksPerThread];
-        bool valid[kTileChunksPerThread];
+        const uint32_t g0 = tile * kTileChunks + 256u * wave + 4u * lane;   // the lane's first chunk
         wait_staged();
+        u4v wd[NW];
 #pragma unroll
-        for (int j = 0; j < kTileChunksPerThread; ++j) {
-            g[j] = tile * kTileChunks + j * kThreads + threadIdx.x;
-            valid[j] = g[j] < a.geo.nchunks;
-            if (valid[j]) unstage_chunk<IN, NW>(stage, j * ChunkWords<IN>::n, ch[j]);
-            else ch[j].zero();
+        for (int k = 0; k < NW; ++k) {
+            const uint32_t ow = NW * lane + k;
+            wd[k] = stage[ow >> 6][64 * wave + swz(ow & 63u)];
         }
         wait_lds_reads();
         if (tile + gridDim.x < ntiles) stage_tile(tile + gridDim.x);
-#pragma unroll
-        for (int j = 0; j < kTileChunksPerThread; ++j) {
-            if (FMT == F_MXFP4) {
-                quant_chunk_mx<IN, STATS>(ch[j], g[j], valid[j], a, st);
-            } else if (FMT == F_NVFP4) {
-                quant_chunk_nv<IN, STATS>(ch[j], g[j], valid[j], nk, a, st);
-            } else if (FMT == F_INT4) {
-                quant_chunk_int4<IN, STATS>(ch[j], g[j], valid[j], s_rtab, a, st);
-            } else {
-                float h[8];
-                quant_chunk_uniform<IN, FMT, STATS>(ch[j], s, y, fast, sat, zeros, valid[j],
-                                                    a.codes + (int64_t)g[j] * kChunk, h, st);
-                if (a.xhat && valid[j]) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g[j] * kChunk, h);
-            }
-        }
+        if (tile < full_tiles) flat_lane<IN, FMT, STATS, true>(wd, g0, a.geo.nchunks, fk, a, st);
+        else flat_lane<IN, FMT, STATS, false>(wd, g0, a.geo.nchunks, fk, a, st);
         if (STATS) st.fold();
     }
     if (STATS) write_partial<kThreads / 64>(st, a.partials);
