@@ -20,6 +20,8 @@ FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5}
 GRANS = {"tensor": 0, "row": 1, "block": 2}
 IQ_F32, IQ_BF16 = 0, 1
 IQ_OK, IQ_EINVAL, IQ_EALIGN, IQ_EUNSUPPORTED, IQ_EHIP = 0, 1, 2, 3, 4
+# iq_desc.flags: scale-rule variants (MXFP4 exponent rounding, NVFP4 block-scale rounding)
+IQ_FLAG_MX_ROUND_NEAREST, IQ_FLAG_MX_ROUND_UP, IQ_FLAG_NV_SCALE_RNE = 0x1, 0x2, 0x4
 FOUR_BIT = ("mxfp4", "nvfp4", "int4")
 
 

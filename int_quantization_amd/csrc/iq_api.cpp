@@ -27,6 +27,23 @@ int64_t block_of(int32_t fmt, int32_t gran) {
     }
 }
 
+// A rule variant applies to its own format only, and the two MXFP4
+// exponent rules exclude each other.
+bool flags_valid(const iq_desc* d) {
+    const uint32_t f = d->flags;
+    switch (d->fmt) {
+    case IQ_MXFP4:
+        return (f & ~(IQ_FLAG_MX_ROUND_NEAREST | IQ_FLAG_MX_ROUND_UP)) == 0 &&
+               f != (IQ_FLAG_MX_ROUND_NEAREST | IQ_FLAG_MX_ROUND_UP);
+    case IQ_NVFP4: return (f & ~IQ_FLAG_NV_SCALE_RNE) == 0;
+    default: return f == 0;
+    }
+}
+
+static_assert(iqk::R_MX_NEAREST == IQ_FLAG_MX_ROUND_NEAREST && iqk::R_MX_UP == IQ_FLAG_MX_ROUND_UP &&
+                  iqk::R_NV_RNE == IQ_FLAG_NV_SCALE_RNE,
+              "rule bits are the public flag values");
+
 // Shape rules shared by every entry point.  cols must be a multiple of the
 // 8-element chunk (16 for the 4-bit formats' blocks anyway) and of the
 // block; the chunk count must fit 31 bits.
@@ -41,7 +58,7 @@ iq_status check_shape(const iq_desc* d, bool need_in_dtype) {
     if (d->rows > 0 && d->cols > 0 && d->rows * (d->cols / iqk::kChunk) >= (int64_t)1 << 31)
         return IQ_EUNSUPPORTED;
     if (d->rows > ((int64_t)1 << 31) - 1) return IQ_EUNSUPPORTED;
-    if (d->flags != 0) return IQ_EUNSUPPORTED;  // rule variants are oracle-only for now
+    if (!flags_valid(d)) return IQ_EUNSUPPORTED;
     return IQ_OK;
 }
 
@@ -127,6 +144,7 @@ iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales
     a.rows = d->rows; a.cols = d->cols; a.ld = d->ld_in;
     a.x = x; a.codes = codes; a.scales = scales; a.global_scale = global_scale;
     a.stats = stats; a.xhat = xhat; a.xhat_dtype = xhat_dtype; a.workspace = workspace;
+    a.rule = d->flags;
     if (empty) { a.rows = 0; a.cols = 0; }
     return from_hip(iqk::launch_quantize(a, stream));
 }

@@ -887,6 +887,7 @@ struct FlatArgs {
     int xhat_dtype;
     const TensorInfo* info;  // per-tensor INT8/FP8 and NVFP4: absmax pre-pass result
     Partial* partials;
+    uint32_t rule;           // R_* scale-rule bits (MXFP4 exponent, NVFP4 block-scale rounding)
 };
 
 // The functions below run on every lane of the wave (lanes past the end of
@@ -959,9 +960,29 @@ __device__ __forceinline__ void store_words4(uint8_t* codes, uint32_t g0, uint32
     }
 }
 
-// MXFP4: one block of 32 = the lane's 4 chunks.  E8M0 = clamp(floor(log2 A) - 2 + 127, 0, 254).
-// g0 is the lane's first chunk (a multiple of 4), nvalid its chunks with
-// data (0 or 4: the row length is a multiple of 32).
+// First FP32 significand (bits 0..22) at or above 3*sqrt(2)/4 - 1: with
+// A = m * 2^e, m in [1, 2), round(log2(A / 6)) = e - 3 + [m >= 3*sqrt(2)/4]
+// (the half-way point 2^(k + 1/2) is irrational, so no FP32 value sits on it).
+constexpr uint32_t kMxNearestMant = 0x07C3B7u;
+
+// Unbiased E8M0 exponent of a block with finite absmax A = m * 2^e (bits of
+// a positive float), before the bias and clamp:
+//   default      floor(log2 A) - 2           = e - 2
+//   R_MX_NEAREST round(log2(A / 6))          = e - 3 + [m >= 3*sqrt(2)/4]
+//   R_MX_UP      ceil(log2(A / 6))           = e - 2 + [m > 3/2]
+// For subnormal A the raw fraction stands in for m: every rule then lands
+// below the clamp (e <= -127), whatever m is.
+__device__ __forceinline__ int mx_exponent(uint32_t bits, uint32_t rule) {
+    const int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
+    const uint32_t m = bits & 0x7FFFFFu;
+    if (rule & R_MX_NEAREST) return e - 3 + (m >= kMxNearestMant ? 1 : 0);
+    if (rule & R_MX_UP) return e - 2 + (m > 0x400000u ? 1 : 0);
+    return e - 2;
+}
+
+// MXFP4: one block of 32 = the lane's 4 chunks.  E8M0 = clamp(E + 127, 0, 254)
+// with E from mx_exponent.  g0 is the lane's first chunk (a multiple of 4),
+// nvalid its chunks with data (0 or 4: the row length is a multiple of 32).
 template <int IN, bool STATS>
 __device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
                                               const FlatArgs& a, Stats& st) {
@@ -972,8 +993,7 @@ __device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksP
     }
     int E = 0;
     if (bits) {
-        int e = (bits >> 23) ? (int)(bits >> 23) - 127 : (31 - __clz((int)bits)) - 149;
-        E = e - 2 + 127;
+        E = mx_exponent(bits, a.rule) + 127;
         E = E < 0 ? 0 : (E > 254 ? 254 : E);
     }
     const float sc = E ? as_f((uint32_t)E << 23) : as_f(0x00400000u);   // 2^(E-127), exact
@@ -1027,6 +1047,12 @@ __device__ __forceinline__ uint32_t e4m3_ceil(float t) {
     return e4m3_value(c) < t ? c + 1u : c;
 }
 
+// Nearest E4M3 code to t (t >= 0, finite), ties to even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+    if (t >= 448.f) return 0x7Eu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xFFu;
+}
+
 __device__ __forceinline__ uint32_t fp4_pack8(const float (&v)[8]) {
     uint32_t w = 0;
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
@@ -1051,10 +1077,12 @@ __device__ __forceinline__ void fp4_unpack8(uint32_t w, float s, float (&h)[8]) 
 struct NvConst {
     float s_g, y_g;
     bool g_fast;          // s_g >= kMarksteinMin: the block-scale quotient may use the correction
+    bool rne;             // block scale to the nearest E4M3 instead of the next one up
     const f2v* tab;       // [128] {s_nv, 1 / s_nv}
 };
 
-// Block scale code: smallest E4M3 >= (A / 6) / s_g.  Both quotients come
+// Block scale code: smallest E4M3 >= (A / 6) / s_g (k.rne: the nearest
+// E4M3, ties to even, saturating at 448).  Both quotients come
 // from the correction step when they are normal and the global scale is
 // not tiny; other lanes (A tiny, block maxima far below the tensor's) take
 // the two divisions.
@@ -1066,7 +1094,7 @@ __device__ __forceinline__ uint32_t nv_block_code(float A, const NvConst& k) {
     if (__ballot(!(exact && k.g_fast)) != 0) {
         if (!(exact && k.g_fast)) tt = (A / 6.0f) / k.s_g;
     }
-    return e4m3_ceil(tt);
+    return k.rne ? e4m3_rne(tt) : e4m3_ceil(tt);
 }
 
 // NVFP4: blocks of 16 = 2 chunks; the lane holds blocks (0, 1) and (2, 3) of
@@ -1299,7 +1327,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     __shared__ f2v s_nvtab[FMT == F_NVFP4 ? 128 : 1];
     __shared__ float s_rtab[FMT == F_INT4 ? 1024 : 1];
     NvConst nk;
-    nk.s_g = s; nk.y_g = 0.f; nk.g_fast = false; nk.tab = s_nvtab;
+    nk.s_g = s; nk.y_g = 0.f; nk.g_fast = false; nk.rne = (a.rule & R_NV_RNE) != 0; nk.tab = s_nvtab;
     if (FMT == F_NVFP4) {
         if (s != 0.f) {
             nk.y_g = 1.0f / s;
@@ -1742,6 +1770,7 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         f.geo = make_geom(q.x, q.rows, q.cols, q.ld);
         f.codes = static_cast<uint8_t*>(q.codes); f.scales = q.scales; f.global_scale = q.global_scale;
         f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.info = info; f.partials = partials;
+        f.rule = q.rule;
         if (q.gran == G_TENSOR || q.fmt == F_NVFP4) {
             float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
             float* scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);

@@ -13,6 +13,8 @@ namespace iqk {
 enum { F_INT8 = 0, F_E4M3 = 1, F_E5M2 = 2, F_MXFP4 = 3, F_NVFP4 = 4, F_INT4 = 5 };
 enum { G_TENSOR = 0, G_ROW = 1, G_BLOCK = 2 };
 enum { D_F32 = 0, D_BF16 = 1 };
+// Scale-rule variants, the public flag values.
+enum : uint32_t { R_MX_NEAREST = 0x1u, R_MX_UP = 0x2u, R_NV_RNE = 0x4u };
 
 constexpr int kThreads = 256;        // threads per workgroup of every streaming kernel
 constexpr int kChunk = 8;            // elements per chunk (one 16-byte BF16 load)
@@ -54,6 +56,7 @@ struct QuantArgs {
     void* stats;          // iq_stats*, may be null
     void* xhat;           // may be null
     int xhat_dtype;
+    uint32_t rule;        // R_* bits valid for fmt, 0 for the default rules
     void* workspace;
 };
 

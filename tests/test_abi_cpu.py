@@ -126,6 +126,31 @@ def test_quantize_argument_errors(iq):
     assert quant(iq, iq.make_desc("e4m3", "row", 1 << 30, 1 << 20)) == U   # > 2^31 chunks
 
 
+def test_rule_flags_validated_per_format(iq):
+    """A rule flag is accepted only with its own format; unknown bits and
+    both MXFP4 exponent rules at once are rejected before any launch."""
+    text = open(HEADER).read()
+    for name in ("IQ_FLAG_MX_ROUND_NEAREST", "IQ_FLAG_MX_ROUND_UP", "IQ_FLAG_NV_SCALE_RNE"):
+        v = int(re.search(name + r"\s+(0x[0-9a-fA-F]+)u", text).group(1), 16)
+        assert getattr(iq, name) == v, name
+    NEAR, UP, RNE = iq.IQ_FLAG_MX_ROUND_NEAREST, iq.IQ_FLAG_MX_ROUND_UP, iq.IQ_FLAG_NV_SCALE_RNE
+    U = iq.IQ_EUNSUPPORTED
+    legal = [("mxfp4", NEAR), ("mxfp4", UP), ("nvfp4", RNE)]
+    for fmt, f in legal:                                   # size queries share the shape check
+        assert iq.iq_scales_bytes(iq.make_desc(fmt, "block", 4, 256, flags=f)) > 0, (fmt, f)
+    illegal = [("mxfp4", NEAR | UP), ("mxfp4", RNE), ("mxfp4", 0x8), ("nvfp4", NEAR), ("nvfp4", UP),
+               ("nvfp4", RNE | 0x100), ("int4", RNE), ("int4", NEAR)]
+    for fmt, f in illegal:
+        d = iq.make_desc(fmt, "block", 4, 256, flags=f)
+        assert iq.iq_scales_bytes(d) == 0, (fmt, f)
+        assert quant(iq, d) == U, (fmt, f)
+        assert iq.iq_dequantize(d, FAKE, FAKE, FAKE, FAKE, 0, None) == U, (fmt, f)
+    for fmt in ("int8", "e4m3", "e5m2"):
+        for gran in ("tensor", "row"):
+            for f in (NEAR, UP, RNE):
+                assert quant(iq, iq.make_desc(fmt, gran, 4, 256, flags=f)) == U, (fmt, gran, f)
+
+
 def test_dequantize_and_amax_argument_errors(iq):
     E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
     d = iq.make_desc("nvfp4", "block", 4, 256)

@@ -385,6 +385,58 @@ def x_f32(S, x):
     return S.bf16_to_f32(x) if x.dtype == np.uint16 else x
 
 
+def mx_rule_exact(A: float, rule: str) -> int:
+    """E8M0 code of a block maximum A > 0 by exact rational arithmetic.
+    floor: the largest k with 2^k <= A, minus 2; nearest: the k closest to
+    log2(A/6), decided by (A/6)^2 >= 2^(2k+1); up: the least k with
+    6 * 2^k >= A.  Biased by 127 and clamped to [0, 254]."""
+    from fractions import Fraction
+    a = Fraction(A)
+    k = math.frexp(A)[1] - 1                       # 2^k <= A < 2^(k+1), exact for floats
+    assert Fraction(2) ** k <= a < Fraction(2) ** (k + 1)
+    if rule == "floor":
+        e = k - 2
+    else:
+        a6 = a / 6
+        j = k - 3                                  # 2^j <= A/6 < 2^(j+1) for one of j, j+1
+        while Fraction(2) ** (j + 1) <= a6:
+            j += 1
+        assert Fraction(2) ** j <= a6 < Fraction(2) ** (j + 1)
+        if rule == "nearest":
+            e = j + 1 if a6 * a6 >= Fraction(2) ** (2 * j + 1) else j
+        else:
+            e = j if a6 == Fraction(2) ** j else j + 1
+    return min(max(e + 127, 0), 254)
+
+
+def test_p9_mx_rule_variants_exact(O):
+    """The three MXFP4 exponent rules of the page against exact rational
+    arithmetic, for maxima over the whole FP32 range (subnormals included),
+    with significands at random and next to 3*sqrt(2)/4 and 3/2, where the
+    nearest and round-up rules change their answer."""
+    rng = np.random.default_rng(9)
+    mants = list(rng.integers(0, 1 << 23, 12)) + [0, 1, 0x07C3B5, 0x07C3B6, 0x07C3B7, 0x07C3B8,
+                                                   0x3FFFFF, 0x400000, 0x400001, 0x7FFFFF]
+    flags = {"floor": 0, "nearest": O.FLAG_MX_ROUND_NEAREST, "up": O.FLAG_MX_ROUND_UP}
+    for e in range(0, 255):
+        for m in mants:
+            u = (e << 23) | int(m)
+            if u == 0:
+                continue
+            A = bits_f32(u)
+            for rule, f in flags.items():
+                assert O.e8m0_code(A, f) == mx_rule_exact(A, rule), (hex(u), rule)
+    # saturation ranges: nearest keeps A/s below 6*sqrt(2), round-up at most 6
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0] = 8.4                                  # A/6 = 1.4 < sqrt(2): s = 1, v = 8.4 saturates
+    x[0, 32] = 6.0                                 # exact power-of-two boundary for round-up
+    r = O.quantize(x, "mxfp4", "block", flags=O.FLAG_MX_ROUND_NEAREST)
+    assert r["scales"][0, 0] == 127 and r["xhat"][0, 0] == 6.0 and r["stats"]["n_saturated"] == 1
+    r = O.quantize(x, "mxfp4", "block", flags=O.FLAG_MX_ROUND_UP)
+    assert r["scales"][0, 0] == 128 and r["scales"][0, 1] == 127
+    assert r["xhat"][0, 32] == 6.0 and r["stats"]["n_saturated"] == 0
+
+
 # ---- P10: NVFP4 -----------------------------------------------------------------
 def test_p10_nv_bounds(O, S):
     x = S.make("c4", nrows=128)
@@ -435,6 +487,53 @@ def test_p10_nv_aligned_block_is_exact(O):
     assert r["global_scale"][0] == 1.0
     assert r["scales"][0, 1] == 0x38                     # E4M3 1.0
     assert np.array_equal(r["xhat"][0, 16:], vals)
+
+
+def test_p10_nv_rne_block_scale_exact(O):
+    """Block scale by RNE (flag): with s_global = 1 each block's code is the
+    E4M3 value nearest to t = A/6 (torch's decode table, exhaustive search,
+    ties to the even code), for maxima on E4M3 values, on midpoints between
+    neighbours (below the smallest subnormal too) and a few FP32 steps off;
+    blocks that round to code 0 quantize to +0, and elements beyond
+    6 * s_block saturate."""
+    tab = torch_fp8_table(torch.float8_e4m3fn)[:0x7F].astype(np.float64)      # codes 0 .. 0x7E
+    order = np.argsort(tab, kind="stable")
+    vals = tab[order]
+    mids = (vals[:-1] + vals[1:]) / 2
+    targets = []
+    for t in np.concatenate([vals[1:], mids]):
+        a = np.float32(6.0 * t)
+        for k in (-2, -1, 0, 1, 2):
+            b = a
+            for _ in range(abs(k)):
+                b = np.nextafter(b, np.float32(np.inf) if k > 0 else np.float32(0))
+            if 0 < b <= 2688.0:
+                targets.append(b)
+    targets = np.array(targets, np.float32)
+    nb = len(targets) + 1
+    x = np.zeros((1, 16 * nb), np.float32)
+    x[0, 0] = 2688.0                                       # s_global = 1
+    x[0, 16::16] = targets
+    x[0, 17::16] = -targets                                # a second element equal in magnitude
+    x[0, 18::16] = targets * np.float32(0.3)
+    r = O.quantize(x, "nvfp4", "block", flags=O.FLAG_NV_SCALE_RNE)
+    assert r["global_scale"][0] == 1.0
+    for i, A in enumerate(targets):
+        t = float(np.float32(A) / np.float32(6.0))
+        d = np.abs(tab - t)
+        best = np.flatnonzero(d == d.min())
+        want = int(best[0]) if len(best) == 1 else int([c for c in best if c % 2 == 0][0])
+        got = int(r["scales"][0, i + 1])
+        assert got == want, (float(A), t, got, want)
+        s_nv = tab[got]
+        xh = r["xhat"][0, 16 * (i + 1): 16 * (i + 2)].astype(np.float64)
+        assert (np.abs(xh) <= 6 * s_nv).all()
+        if got == 0:
+            assert (xh == 0).all() and not np.signbit(xh).any()
+    # rounding up never lands below t; RNE does for about half the targets
+    up = O.quantize(x, "nvfp4", "block")
+    assert (tab[up["scales"][0, 1:]] >= (targets.astype(np.float64) / 6) * (1 - 2 ** -23)).all()
+    assert (r["scales"][0, 1:] != up["scales"][0, 1:]).any()
 
 
 # ---- P11: INT4 and the nibble order of Puzzle 12 ---------------------------------

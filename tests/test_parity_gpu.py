@@ -42,13 +42,13 @@ def S():
     return synth
 
 
-def run_gpu(iq, x_np, fmt, gran, cols=None, xhat="f32"):
+def run_gpu(iq, x_np, fmt, gran, cols=None, xhat="f32", flags=0):
     import torch
     x = to_device(x_np)
     if cols is not None:
         x = x[:, :cols]
     xdt = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[xhat]
-    q = iq.quantize(x, fmt, gran, xhat_dtype=xdt)
+    q = iq.quantize(x, fmt, gran, xhat_dtype=xdt, flags=flags)
     torch.cuda.synchronize()
     out = {"codes": q.codes.cpu().numpy(), "scales": q.scales.cpu().numpy(), "stats": q.stats(), "q": q}
     if q.global_scale is not None:
@@ -75,8 +75,8 @@ def compare(g, r, fmt, what, O=None, S=None, xhat="f32"):
     assert_stats_match(g["stats"], r["stats"], what)
 
 
-def oracle_ref(O, x_np, fmt, gran, cols=None, want_xhat=True):
-    return O.quantize(x_np, fmt, gran, cols=cols, want_xhat=want_xhat, threads=THREADS)
+def oracle_ref(O, x_np, fmt, gran, cols=None, want_xhat=True, flags=0):
+    return O.quantize(x_np, fmt, gran, cols=cols, flags=flags, want_xhat=want_xhat, threads=THREADS)
 
 
 # ---- shapes spanning several tiles, ragged tails, padded rows -----------------
@@ -297,8 +297,10 @@ def test_bf16_division_sweep(iq, O, S, fmt):
     assert_stats_match(g["stats"], r["stats"], f"{fmt} sweep")
 
 
-@pytest.mark.parametrize("fmt", ["int4", "nvfp4", "mxfp4"])
-def test_bf16_block_sweep(iq, O, S, fmt):
+@pytest.mark.parametrize("fmt,flags", [("int4", 0), ("nvfp4", 0), ("mxfp4", 0), ("nvfp4", 4), ("mxfp4", 1),
+                                       ("mxfp4", 2)], ids=["int4", "nvfp4", "mxfp4", "nvfp4-rne",
+                                                           "mxfp4-nearest", "mxfp4-up"])
+def test_bf16_block_sweep(iq, O, S, fmt, flags):
     """Blocks whose maximum walks the BF16 range while the other elements take
     every BF16 magnitude at or below it."""
     B = {"int4": 128, "nvfp4": 16, "mxfp4": 32}[fmt]
@@ -314,22 +316,24 @@ def test_bf16_block_sweep(iq, O, S, fmt):
     np.put_along_axis(x, pos, tops.astype(np.uint16), axis=1)
     if fmt == "nvfp4":
         x[0, 0] = 0x7F7F
-    g = run_gpu(iq, x, fmt, "block")
-    rr = oracle_ref(O, x, fmt, "block")
-    compare(g, rr, fmt, f"{fmt} block sweep", O)
+    g = run_gpu(iq, x, fmt, "block", flags=flags)
+    rr = oracle_ref(O, x, fmt, "block", flags=flags)
+    compare(g, rr, fmt, f"{fmt} block sweep flags={flags}", O)
 
 
 # ---- the five workloads at full size (the configuration the bench times) ----------
-FULL = [("c1", "int8", "tensor"), ("c1", "e4m3", "tensor"), ("c2", "e4m3", "row"), ("c2", "e5m2", "row"),
-        ("c3", "mxfp4", "block"), ("c4", "nvfp4", "block"), ("c5", "int4", "block")]
+FULL = [("c1", "int8", "tensor", 0), ("c1", "e4m3", "tensor", 0), ("c2", "e4m3", "row", 0),
+        ("c2", "e5m2", "row", 0), ("c3", "mxfp4", "block", 0), ("c4", "nvfp4", "block", 0),
+        ("c5", "int4", "block", 0), ("c3", "mxfp4", "block", 1), ("c3", "mxfp4", "block", 2),
+        ("c4", "nvfp4", "block", 4)]
 
 
-@pytest.mark.parametrize("cfg,fmt,gran", FULL)
-def test_full_size_workloads(iq, O, S, cfg, fmt, gran):
+@pytest.mark.parametrize("cfg,fmt,gran,flags", FULL)
+def test_full_size_workloads(iq, O, S, cfg, fmt, gran, flags):
     x = S.make(cfg)
-    g = run_gpu(iq, x, fmt, gran, xhat=None)
-    r = O.quantize(x, fmt, gran, want_xhat=False, threads=THREADS)
-    compare(g, r, fmt, f"{cfg} {fmt}/{gran} full size", O)
+    g = run_gpu(iq, x, fmt, gran, xhat=None, flags=flags)
+    r = O.quantize(x, fmt, gran, flags=flags, want_xhat=False, threads=THREADS)
+    compare(g, r, fmt, f"{cfg} {fmt}/{gran} flags={flags} full size", O)
 
 
 def test_stream_sampled_rows(iq, O, S):
@@ -459,3 +463,97 @@ def test_int4_fp16_scale_ties(iq, O, S, dtype):
     g = run_gpu(iq, x, "int4", "block")
     r = oracle_ref(O, x, "int4", "block")
     compare(g, r, "int4", f"int4 FP16 scale ties ({'bf16' if dtype else 'f32'})", O)
+
+
+# ---- scale-rule variants (iq_desc.flags) ------------------------------------------
+RULES = [("mxfp4", 1), ("mxfp4", 2), ("nvfp4", 4)]
+RULE_IDS = ["mx-nearest", "mx-up", "nv-rne"]
+
+
+@pytest.mark.parametrize("fmt,flags", RULES, ids=RULE_IDS)
+@pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
+def test_rule_variant_parity(iq, O, S, fmt, flags, dtype):
+    """Each rule variant over the multi-tile shapes, the special-value matrix
+    and the activation workload scaled toward the bottom of the range."""
+    bs = O.block_size(fmt, "block")
+    for i, (rows, cols, ld) in enumerate(SHAPES):
+        if cols % bs:
+            continue
+        x = make_input(S, dtype, rows, cols, ld, seed=300 + i)
+        c = cols if ld else None
+        g = run_gpu(iq, x, fmt, "block", cols=c, flags=flags)
+        r = oracle_ref(O, x, fmt, "block", cols=c, flags=flags)
+        compare(g, r, fmt, f"{fmt} flags={flags} {rows}x{cols} ld={ld}", O)
+    x = bf16_special_matrix(S) if dtype else f32_special_matrix(S)
+    cases = [x, np.ascontiguousarray(np.delete(x, [5, 6, 8, 9], axis=0))]
+    for k, xc in enumerate(cases):
+        g = run_gpu(iq, xc, fmt, "block", flags=flags)
+        r = oracle_ref(O, xc, fmt, "block", flags=flags)
+        compare(g, r, fmt, f"{fmt} flags={flags} special case {k}", O)
+    for shift in (100, 126, 130):
+        x32 = S.bf16_to_f32(S.make("c2", nrows=16)) * np.float32(2.0 ** -shift)
+        x = S.f32_to_bf16_bits(x32.astype(np.float32)) if dtype else x32.astype(np.float32)
+        g = run_gpu(iq, x, fmt, "block", flags=flags)
+        r = oracle_ref(O, x, fmt, "block", flags=flags)
+        compare(g, r, fmt, f"{fmt} flags={flags} x 2^-{shift}", O)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2], ids=["floor", "nearest", "up"])
+def test_mx_exponent_rule_boundaries(iq, O, S, flags):
+    """FP32 block maxima whose significand sits on, or next to, the point
+    where each exponent rule changes its answer (3*sqrt(2)/4 for the nearest
+    rule, 3/2 for the round-up rule, the binade ends for the default), with
+    exponents over the whole FP32 range, subnormals included."""
+    rng = np.random.default_rng(41)
+    rows, cols = 64, 2048
+    nb = cols // 32
+    mants = np.array([0x0, 0x1, 0x07C3B5, 0x07C3B6, 0x07C3B7, 0x07C3B8, 0x3FFFFF, 0x400000, 0x400001,
+                      0x7FFFFE, 0x7FFFFF], np.uint32)
+    m = rng.choice(mants, (rows, nb))
+    e = rng.integers(0, 255, (rows, nb)).astype(np.uint32)       # 0: subnormal maxima
+    e[:, :8] = np.arange(0, 8, dtype=np.uint32)                  # the bottom of the range on every row
+    e[:, 8:12] = np.arange(251, 255, dtype=np.uint32)            # and the top
+    m[e == 0] |= 1                                               # keep subnormal maxima nonzero
+    tops = ((e << 23) | m).astype(np.uint32).view(np.float32)
+    te = np.repeat(tops, 32, axis=1)
+    x = (te * rng.random((rows, cols)).astype(np.float32)).astype(np.float32)
+    x *= np.where(rng.random((rows, cols)) < 0.5, -1, 1).astype(np.float32)
+    pos = rng.integers(0, 32, (rows, nb)) + np.arange(nb) * 32
+    np.put_along_axis(x, pos, tops * np.where(rng.random((rows, nb)) < 0.5, -1, 1).astype(np.float32), axis=1)
+    g = run_gpu(iq, x, "mxfp4", "block", flags=flags)
+    r = oracle_ref(O, x, "mxfp4", "block", flags=flags)
+    compare(g, r, "mxfp4", f"mxfp4 exponent-rule boundaries flags={flags}", O)
+
+
+@pytest.mark.parametrize("flags", [0, 4], ids=["ceil", "rne"])
+def test_nv_block_scale_rounding(iq, O, S, flags):
+    """NVFP4 with s_global = 1 (tensor absmax 2688): each block's maximum is
+    6 t with t an E4M3 value, a midpoint between two neighbours (below the
+    smallest subnormal too), or a few FP32 steps off one, so the rounding
+    rule alone decides the block scale code, including code 0 for A > 0."""
+    rng = np.random.default_rng(43)
+    vals = np.asarray(O.fp_decode_array(O.K_E4M3, np.arange(0x7F)), np.float64)      # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    targets = []
+    for t in np.concatenate([vals[1:], mids]):
+        a = np.float32(6.0 * t)                                                       # exact
+        for k in (-2, -1, 0, 1, 2):
+            b = a
+            for _ in range(abs(k)):
+                b = np.nextafter(b, np.float32(np.inf) if k > 0 else np.float32(0))
+            if 0 < b <= 2688.0:
+                targets.append(b)
+    targets = np.array(targets, np.float32)
+    rows, cols = 64, 1024
+    nb = cols // 16
+    tops = rng.choice(targets, (rows, nb)).astype(np.float32)
+    tops[0, 0] = np.float32(2688.0)
+    te = np.repeat(tops, 16, axis=1)
+    x = (te * rng.random((rows, cols)).astype(np.float32)).astype(np.float32)
+    x *= np.where(rng.random((rows, cols)) < 0.5, -1, 1).astype(np.float32)
+    pos = rng.integers(0, 16, (rows, nb)) + np.arange(nb) * 16
+    np.put_along_axis(x, pos, tops, axis=1)
+    g = run_gpu(iq, x, "nvfp4", "block", flags=flags)
+    r = oracle_ref(O, x, "nvfp4", "block", flags=flags)
+    assert r["global_scale"][0] == np.float32(1.0)
+    compare(g, r, "nvfp4", f"nvfp4 block-scale rounding flags={flags}", O)
