@@ -11,8 +11,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Pointers named x, codes, scales, global_scale, stats, xhat, workspace
- *   and amax_out are DEVICE pointers (HIP device memory of the current
+ * - Pointers named x, codes, scales, global_scale, stats, xhat, workspace,
+ *   amax_in and amax_out are DEVICE pointers (HIP device memory of the current
  *   device).  The descriptor is a HOST pointer.  The caller allocates and
  *   owns every buffer; the library allocates nothing, keeps no state
  *   between calls, and never synchronizes.
@@ -146,6 +146,26 @@ iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales,
  */
 iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace,
                   hipStream_t stream);
+
+/*
+ * Static (calibrated) scaling: iq_quantize with the per-tensor absmax taken
+ * from *amax_in (device float32 [1], e.g. written by iq_amax over
+ * calibration data) instead of measured, so x is read once.  The scale is
+ * derived from it exactly as iq_quantize derives it from the measured one
+ * (section "FP8": s = alpha / FMAX; "NVFP4": s_global = amax / (6 * 448)).
+ *   Legal for INT8 / E4M3 / E5M2 per tensor and for NVFP4 (the global
+ *   scale; block scales still come from each block).  Any other
+ *   descriptor returns IQ_EINVAL.
+ *   Elements beyond alpha saturate and are counted in n_saturated; NaN and
+ *   +-Inf inputs are handled as in iq_quantize.
+ *   A NaN, negative or infinite *amax_in is taken as 0 (every code +0,
+ *   scale 0); -0 is taken as +0.
+ *   The other arguments, layouts, workspace rules and errors are those of
+ *   iq_quantize; amax_in must be 4-byte aligned (IQ_EALIGN otherwise).
+ */
+iq_status iq_quantize_static(const iq_desc* d, const void* x, const float* amax_in, void* codes,
+                             void* scales, float* global_scale, iq_stats* stats, void* xhat,
+                             int32_t xhat_dtype, void* workspace, hipStream_t stream);
 
 const char* iq_status_str(iq_status s);
 int iq_abi_version(void);

@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.iq_workspace_bytes.restype, L.iq_workspace_bytes.argtypes = S, [D]
     L.iq_quantize.restype = ctypes.c_int
     L.iq_quantize.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.iq_quantize_static.restype = ctypes.c_int
+    L.iq_quantize_static.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
     L.iq_dequantize.restype = ctypes.c_int
     L.iq_dequantize.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
     L.iq_amax.restype = ctypes.c_int
@@ -107,6 +109,14 @@ def iq_quantize(d: IQDesc, x: int, codes: int, scales: int, global_scale: int | 
     """Raw call with integer device addresses; returns the iq_status."""
     return load_library().iq_quantize(ctypes.byref(d), x, codes, scales, global_scale, stats, xhat,
                                       xhat_dtype, workspace, stream)
+
+
+def iq_quantize_static(d: IQDesc, x: int, amax_in: int, codes: int, scales: int, global_scale: int | None,
+                       stats: int | None, xhat: int | None, xhat_dtype: int, workspace: int,
+                       stream: int | None) -> int:
+    """Raw call with integer device addresses (amax_in: device float32 [1])."""
+    return load_library().iq_quantize_static(ctypes.byref(d), x, amax_in, codes, scales, global_scale, stats,
+                                             xhat, xhat_dtype, workspace, stream)
 
 
 def iq_dequantize(d: IQDesc, codes: int, scales: int, global_scale: int | None, xhat: int,
@@ -201,9 +211,11 @@ class Quantized:
 
 
 def quantize(x, fmt: str, gran: str, *, stats: bool = True, xhat_dtype=None, cols: int | None = None,
-             flags: int = 0, workspace=None, out=None, stream=None) -> Quantized:
+             flags: int = 0, workspace=None, out=None, stream=None, static_amax=None) -> Quantized:
     """Quantize a device tensor; outputs are allocated with torch.empty unless
-    `out` (a Quantized from a previous call of the same shape) is given."""
+    `out` (a Quantized from a previous call of the same shape) is given.
+    static_amax (a device float32 tensor of one element) selects static
+    scaling: iq_quantize_static with that absmax instead of the measured one."""
     torch = _torch()
     d = desc_for(x, fmt, gran, cols, flags)
     if out is None:
@@ -217,9 +229,17 @@ def quantize(x, fmt: str, gran: str, *, stats: bool = True, xhat_dtype=None, col
     xdt = IQ_F32
     if out.xhat is not None:
         xdt = IQ_F32 if out.xhat.dtype == torch.float32 else IQ_BF16
-    st = iq_quantize(d, x.data_ptr(), _ptr(out.codes), _ptr(out.scales), _ptr(out.global_scale),
-                     _ptr(out.stats_buf), _ptr(out.xhat), xdt, ws.data_ptr(), _stream(stream))
-    _check(st, "iq_quantize")
+    if static_amax is None:
+        st = iq_quantize(d, x.data_ptr(), _ptr(out.codes), _ptr(out.scales), _ptr(out.global_scale),
+                         _ptr(out.stats_buf), _ptr(out.xhat), xdt, ws.data_ptr(), _stream(stream))
+        _check(st, "iq_quantize")
+    else:
+        if static_amax.dtype != torch.float32 or static_amax.numel() != 1 or static_amax.device != x.device:
+            raise ValueError("static_amax must be one float32 on the input's device")
+        st = iq_quantize_static(d, x.data_ptr(), static_amax.data_ptr(), _ptr(out.codes), _ptr(out.scales),
+                                _ptr(out.global_scale), _ptr(out.stats_buf), _ptr(out.xhat), xdt,
+                                ws.data_ptr(), _stream(stream))
+        _check(st, "iq_quantize_static")
     return out
 
 

@@ -120,8 +120,13 @@ size_t iq_workspace_bytes(const iq_desc* d) {
     return iqk::Workspace::kBytes;
 }
 
-iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales, float* global_scale,
-                      iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+iq_status quantize_impl(const iq_desc* d, const void* x, const float* static_amax, void* codes, void* scales,
+                        float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace,
+                        hipStream_t stream) {
     iq_status st = check_shape(d, true);
     if (st != IQ_OK) return st;
     if ((st = check_input(d, x)) != IQ_OK) return st;
@@ -145,8 +150,30 @@ iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales
     a.x = x; a.codes = codes; a.scales = scales; a.global_scale = global_scale;
     a.stats = stats; a.xhat = xhat; a.xhat_dtype = xhat_dtype; a.workspace = workspace;
     a.rule = d->flags;
+    a.static_amax = static_amax;
     if (empty) { a.rows = 0; a.cols = 0; }
     return from_hip(iqk::launch_quantize(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales, float* global_scale,
+                      iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace, hipStream_t stream) {
+    return quantize_impl(d, x, nullptr, codes, scales, global_scale, stats, xhat, xhat_dtype, workspace, stream);
+}
+
+iq_status iq_quantize_static(const iq_desc* d, const void* x, const float* amax_in, void* codes, void* scales,
+                             float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype,
+                             void* workspace, hipStream_t stream) {
+    if (!d) return IQ_EINVAL;
+    if (!(d->gran == IQ_PER_TENSOR || d->fmt == IQ_NVFP4)) return IQ_EINVAL;   // no per-tensor scale to take
+    if (!amax_in) return IQ_EINVAL;
+    iq_status st = check_shape(d, true);
+    if (st != IQ_OK) return st;
+    if (!aligned(amax_in, 4)) return IQ_EALIGN;
+    return quantize_impl(d, x, amax_in, codes, scales, global_scale, stats, xhat, xhat_dtype, workspace, stream);
 }
 
 iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales, const float* global_scale,

@@ -1268,13 +1268,19 @@ __device__ __forceinline__ uint32_t unswz(uint32_t i) { return (i & ~7u) | ((i -
 struct FlatConst {
     float s, y;
     bool fast, sat, zeros;
+    uint32_t amax_bits;   // the per-tensor absmax the scale came from
     NvConst nk;
     const float* rtab;
 };
 
 // One tile's worth of the lane's chunks (wd: its 16-byte words from LDS).
 // FULL: every chunk of the tile holds data (no per-chunk validity selects).
-template <int IN, int FMT, bool STATS, bool FULL>
+// CHECK (per-tensor INT8 / FP8 with a caller-supplied absmax): nothing is
+// known of the data, so each wave takes the fast cast only when its inputs
+// are finite, within the absmax (no clamping beyond the rounding of s) and
+// not all below the FP32 statistics range; the exact-zero flag is the
+// wave's own.
+template <int IN, int FMT, bool STATS, bool FULL, bool CHECK>
 __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread * ChunkWords<IN>::n], uint32_t g0,
                                           uint32_t nchunks, const FlatConst& k, const FlatArgs& a, Stats& st) {
     constexpr int W = ChunkWords<IN>::n;
@@ -1292,18 +1298,25 @@ __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread *
     } else if (FMT == F_INT4) {
         quant_lane_int4<IN, STATS>(ch, g0, nvalid, k.rtab, a, st);
     } else {
+        bool fast = k.fast, zeros = k.zeros;
+        if (CHECK) {
+            bool nonfinite, zero;
+            const uint32_t m = lane_absmax<IN, kTileChunksPerThread>(ch, 0, nonfinite, zero);
+            fast = fast && __ballot(nonfinite || m > k.amax_bits) == 0 && __ballot(m >= as_u(kStatLo)) != 0;
+            zeros = __ballot(zero) != 0;
+        }
 #pragma unroll
         for (int c = 0; c < kTileChunksPerThread; ++c) {
             const bool valid = FULL || (uint32_t)c < nvalid;
             float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch[c], k.s, k.y, k.fast, k.sat, k.zeros, valid,
+            quant_chunk_uniform<IN, FMT, STATS>(ch[c], k.s, k.y, fast, k.sat, zeros, valid,
                                                 a.codes + (int64_t)(g0 + c) * kChunk, h, st);
             if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
         }
     }
 }
 
-template <int IN, int FMT, bool STATS>
+template <int IN, int FMT, bool STATS, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     constexpr int W = ChunkWords<IN>::n;
     constexpr int NW = kTileChunksPerThread * W;      // 16-byte words per lane = copies per wave and tile
@@ -1374,6 +1387,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     if (blockIdx.x < ntiles) stage_tile(blockIdx.x);
     FlatConst fk;
     fk.s = s; fk.y = y; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
+    fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? a.info->amax_bits : 0u;
     const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const uint32_t g0 = tile * kTileChunks + 256u * wave + 4u * lane;   // the lane's first chunk
@@ -1386,8 +1400,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
         }
         wait_lds_reads();
         if (tile + gridDim.x < ntiles) stage_tile(tile + gridDim.x);
-        if (tile < full_tiles) flat_lane<IN, FMT, STATS, true>(wd, g0, a.geo.nchunks, fk, a, st);
-        else flat_lane<IN, FMT, STATS, false>(wd, g0, a.geo.nchunks, fk, a, st);
+        if (tile < full_tiles) flat_lane<IN, FMT, STATS, true, CHECK>(wd, g0, a.geo.nchunks, fk, a, st);
+        else flat_lane<IN, FMT, STATS, false, CHECK>(wd, g0, a.geo.nchunks, fk, a, st);
         if (STATS) st.fold();
     }
     if (STATS) write_partial<kThreads / 64>(st, a.partials);
@@ -1451,6 +1465,23 @@ __global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* part
         }
         if (scale_out) *scale_out = s;
         if (amax_out) *amax_out = as_f(m);
+    }
+}
+
+// Static scaling: the per-tensor absmax comes from the caller.  A NaN,
+// negative or infinite value is taken as 0 and -0 as +0; the scale follows
+// as in k_amax_finalize.  Nothing is known of the data (the quantize kernel
+// checks it per wave), so the exact-zero flag is set.
+__global__ __launch_bounds__(64) void k_static_info(const float* amax_in, float qdiv, TensorInfo* info,
+                                                     float* scale_out) {
+    if (threadIdx.x == 0) {
+        float a = *amax_in;
+        a = (a >= 0.f && a <= 0x1.fffffep127f) ? __builtin_fabsf(a) : 0.f;
+        const float s = a / qdiv;
+        TensorInfo t;
+        t.amax_bits = as_u(a); t.nonfinite = 0u; t.scale = s; t.zeros = 1u;
+        *info = t;
+        *scale_out = s;
     }
 }
 
@@ -1691,28 +1722,33 @@ hipError_t launch_row(const RowArgs& r, bool stats, int& grid, hipStream_t s) {
     return stats ? launch_row_t<IN, FMT, true>(r, grid, s) : launch_row_t<IN, FMT, false>(r, grid, s);
 }
 
-template <int IN, int FMT>
-hipError_t launch_flat(const FlatArgs& f, bool stats, int& grid, hipStream_t s) {
-    const uint64_t tiles = tiles_of(f.geo.nchunks);
-    if (stats) {
-        grid = grid_for(k_quant_flat<IN, FMT, true>, tiles);
-        k_quant_flat<IN, FMT, true><<<grid, kThreads, 0, s>>>(f);
-    } else {
-        grid = grid_for(k_quant_flat<IN, FMT, false>, tiles);
-        k_quant_flat<IN, FMT, false><<<grid, kThreads, 0, s>>>(f);
-    }
+template <int IN, int FMT, bool STATS, bool CHECK>
+hipError_t launch_flat_one(const FlatArgs& f, int& grid, hipStream_t s) {
+    grid = grid_for(k_quant_flat<IN, FMT, STATS, CHECK>, tiles_of(f.geo.nchunks));
+    k_quant_flat<IN, FMT, STATS, CHECK><<<grid, kThreads, 0, s>>>(f);
     return hipGetLastError();
 }
 
+// check: per-tensor INT8 / FP8 with a caller-supplied absmax (the other
+// formats decide per block and need no data checks).
+template <int IN, int FMT>
+hipError_t launch_flat(const FlatArgs& f, bool stats, bool check, int& grid, hipStream_t s) {
+    constexpr bool kUniform = FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2;
+    if (kUniform && check)
+        return stats ? launch_flat_one<IN, FMT, true, kUniform>(f, grid, s)
+                     : launch_flat_one<IN, FMT, false, kUniform>(f, grid, s);
+    return stats ? launch_flat_one<IN, FMT, true, false>(f, grid, s) : launch_flat_one<IN, FMT, false, false>(f, grid, s);
+}
+
 template <int IN>
-hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, bool stats, int& grid, hipStream_t s) {
+hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, bool stats, bool check, int& grid, hipStream_t s) {
     switch (fmt) {
-    case F_INT8: return launch_flat<IN, F_INT8>(f, stats, grid, s);
-    case F_E4M3: return launch_flat<IN, F_E4M3>(f, stats, grid, s);
-    case F_E5M2: return launch_flat<IN, F_E5M2>(f, stats, grid, s);
-    case F_MXFP4: return launch_flat<IN, F_MXFP4>(f, stats, grid, s);
-    case F_NVFP4: return launch_flat<IN, F_NVFP4>(f, stats, grid, s);
-    default: return launch_flat<IN, F_INT4>(f, stats, grid, s);
+    case F_INT8: return launch_flat<IN, F_INT8>(f, stats, check, grid, s);
+    case F_E4M3: return launch_flat<IN, F_E4M3>(f, stats, check, grid, s);
+    case F_E5M2: return launch_flat<IN, F_E5M2>(f, stats, check, grid, s);
+    case F_MXFP4: return launch_flat<IN, F_MXFP4>(f, stats, check, grid, s);
+    case F_NVFP4: return launch_flat<IN, F_NVFP4>(f, stats, check, grid, s);
+    default: return launch_flat<IN, F_INT4>(f, stats, check, grid, s);
     }
 }
 
@@ -1774,12 +1810,18 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         if (q.gran == G_TENSOR || q.fmt == F_NVFP4) {
             float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
             float* scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);
-            e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, scale_out, nullptr, s);
+            if (q.static_amax) {
+                k_static_info<<<1, 64, 0, s>>>(q.static_amax, qdiv, info, scale_out);
+                e = hipGetLastError();
+            } else {
+                e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, scale_out, nullptr, s);
+            }
             if (e != hipSuccess) return e;
         }
+        const bool check = q.static_amax != nullptr;
         if (nelem) {
-            e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, stats, grid, s)
-                                     : launch_flat_fmt<D_F32>(q.fmt, f, stats, grid, s);
+            e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, stats, check, grid, s)
+                                     : launch_flat_fmt<D_F32>(q.fmt, f, stats, check, grid, s);
         }
     }
     if (e != hipSuccess) return e;

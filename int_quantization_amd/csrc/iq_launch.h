@@ -57,6 +57,7 @@ struct QuantArgs {
     void* xhat;           // may be null
     int xhat_dtype;
     uint32_t rule;        // R_* bits valid for fmt, 0 for the default rules
+    const float* static_amax;  // per-tensor / NVFP4: caller-supplied absmax (null: measured)
     void* workspace;
 };
 

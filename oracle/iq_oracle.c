@@ -423,6 +423,19 @@ int iqo_quantize(const iqo_desc* d, const void* x, uint8_t* codes, void* scales,
     return iqo_quantize_rows(d, x, 0, d->rows, amax, codes, scales, global_scale, xhat, st);
 }
 
+/* ---- static scaling: the absmax of "FP8" / "NVFP4" supplied by the caller -- */
+float iqo_static_amax(float amax_in) {
+    if (!(amax_in >= 0.0f) || isinf(amax_in)) return 0.0f;
+    return fabsf(amax_in);
+}
+
+int iqo_quantize_static(const iqo_desc* d, const void* x, float amax_in, uint8_t* codes, void* scales,
+                        float* global_scale, float* xhat, iqo_stats* st) {
+    if (iqo_check(d)) return -1;
+    if (!(d->gran == IQO_PER_TENSOR || d->fmt == IQO_NVFP4)) return -1;
+    return iqo_quantize_rows(d, x, 0, d->rows, iqo_static_amax(amax_in), codes, scales, global_scale, xhat, st);
+}
+
 /* ---- dequantization: x^ = s * decode(q), the same products as above ----- */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype) {

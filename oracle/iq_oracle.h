@@ -81,6 +81,12 @@ int iqo_quantize_rows(const iqo_desc* d, const void* x, int64_t r0, int64_t r1, 
 /* Whole tensor: absmax pre-pass when needed, then every row in order. */
 int iqo_quantize(const iqo_desc* d, const void* x, uint8_t* codes, void* scales,
                  float* global_scale, float* xhat, iqo_stats* st);
+/* Static (calibrated) scaling: the per-tensor absmax is the caller's value,
+ * taken as 0 when it is NaN, negative or infinite (and -0 as +0). */
+float iqo_static_amax(float amax_in);
+/* Whole tensor with a caller-supplied absmax (per-tensor formats, NVFP4). */
+int iqo_quantize_static(const iqo_desc* d, const void* x, float amax_in, uint8_t* codes, void* scales,
+                        float* global_scale, float* xhat, iqo_stats* st);
 /* Reconstruct xhat ([rows, cols], FP32 or BF16) from codes and scales. */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype);

@@ -82,6 +82,9 @@ def _load():
             "iqo_quantize_rows": (ctypes.c_int, [ctypes.POINTER(Desc), P, I64, I64, F, P, P, P, P,
                                                  ctypes.POINTER(Stats)]),
             "iqo_quantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, P, ctypes.POINTER(Stats)]),
+            "iqo_static_amax": (F, [F]),
+            "iqo_quantize_static": (ctypes.c_int, [ctypes.POINTER(Desc), P, F, P, P, P, P,
+                                                   ctypes.POINTER(Stats)]),
             "iqo_dequantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
@@ -187,12 +190,14 @@ def amax(x: np.ndarray, cols: int | None = None, fmt: str = "e4m3", gran: str = 
 
 
 def quantize(x: np.ndarray, fmt: str, gran: str, cols: int | None = None, flags: int = 0,
-             want_xhat: bool = True, threads: int = 1) -> dict:
+             want_xhat: bool = True, threads: int = 1, static_amax: float | None = None) -> dict:
     """Quantize a whole [rows, ld] array; returns codes, scales, global_scale, xhat, stats.
 
     threads > 1 splits rows across threads (the oracle itself is serial per
     row range; ctypes releases the GIL).  Codes, scales and x^ do not depend
     on the split; the double-precision sums may differ in the last bits.
+    static_amax: per-tensor formats and NVFP4 only; the absmax is the given
+    value (iqo_static_amax's rule) instead of the measured one.
     """
     d = _desc(fmt, gran, x, cols, flags)
     rows, c = d.rows, d.cols
@@ -203,7 +208,11 @@ def quantize(x: np.ndarray, fmt: str, gran: str, cols: int | None = None, flags:
     xhat = np.zeros((rows, c), dtype=np.float32) if want_xhat else None
     L = _load()
     tensor_amax = 0.0
-    if gran == "tensor" or fmt == "nvfp4":
+    if static_amax is not None:
+        if not (gran == "tensor" or fmt == "nvfp4"):
+            raise ValueError("static_amax needs a per-tensor format or NVFP4")
+        tensor_amax = L.iqo_static_amax(float(static_amax))
+    elif gran == "tensor" or fmt == "nvfp4":
         tensor_amax = L.iqo_amax(ctypes.byref(d), _p(x))
     parts = _split(rows, threads)
     stats = [Stats() for _ in parts]

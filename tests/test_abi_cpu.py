@@ -151,6 +151,29 @@ def test_rule_flags_validated_per_format(iq):
                 assert quant(iq, iq.make_desc(fmt, gran, 4, 256, flags=f)) == U, (fmt, gran, f)
 
 
+def test_quantize_static_argument_errors(iq):
+    """Static scaling takes a per-tensor absmax: per-row and per-block
+    descriptors (other than NVFP4) have none to take."""
+    E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
+
+    def qs(d, amax=FAKE, **kw):
+        a = dict(x=FAKE, codes=FAKE, scales=FAKE, gs=FAKE, stats=None, xhat=None, xdt=0, ws=FAKE)
+        a.update(kw)
+        return iq.iq_quantize_static(d, a["x"], amax, a["codes"], a["scales"], a["gs"], a["stats"], a["xhat"],
+                                     a["xdt"], a["ws"], None)
+    assert qs(iq.make_desc("e4m3", "row", 4, 256)) == E
+    assert qs(iq.make_desc("int8", "row", 4, 256)) == E
+    assert qs(iq.make_desc("mxfp4", "block", 4, 256)) == E
+    assert qs(iq.make_desc("int4", "block", 4, 256)) == E
+    assert qs(iq.make_desc("e4m3", "tensor", 4, 256), amax=None) == E
+    assert qs(iq.make_desc("nvfp4", "block", 4, 256), amax=None) == E
+    assert qs(iq.make_desc("e4m3", "tensor", 4, 256), amax=FAKE + 2) == A
+    assert qs(iq.make_desc("nvfp4", "block", 4, 256), gs=None) == E
+    assert qs(iq.make_desc("e4m3", "tensor", 4, 256), ws=None) == E
+    assert qs(iq.make_desc("e4m3", "tensor", 4, 252)) == E
+    assert qs(iq.make_desc("e4m3", "tensor", 4, 256, flags=1)) == iq.IQ_EUNSUPPORTED
+
+
 def test_dequantize_and_amax_argument_errors(iq):
     E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
     d = iq.make_desc("nvfp4", "block", 4, 256)

@@ -536,6 +536,67 @@ def test_p10_nv_rne_block_scale_exact(O):
     assert (r["scales"][0, 1:] != up["scales"][0, 1:]).any()
 
 
+# ---- static (calibrated) scaling: the absmax is given, not measured ---------------
+def test_static_scale_matches_measured_and_textbook(O, S):
+    """With alpha equal to the measured absmax, static scaling is the
+    dynamic path; with any alpha, INT8 codes are rint(x / s) clipped to
+    [-127, 127] (numpy), s = alpha / 127 in FP32, and the saturation count
+    is the number of |x / s| > 127."""
+    x = S.make("c1", nrows=64)
+    x32 = x_f32(S, x)
+    G = float(np.max(np.abs(x32)))
+    for fmt, gran in (("int8", "tensor"), ("e4m3", "tensor"), ("e5m2", "tensor"), ("nvfp4", "block")):
+        a = O.quantize(x, fmt, gran)
+        b = O.quantize(x, fmt, gran, static_amax=G)
+        for k in ("codes", "scales", "global_scale", "xhat"):
+            assert np.array_equal(a[k], b[k]), (fmt, k)
+        assert a["stats"] == b["stats"]
+    for alpha in (0.25 * G, G, 3.0 * G, 1e-3):
+        s = np.float32(np.float32(alpha) / np.float32(127.0))
+        r = O.quantize(x, "int8", "tensor", static_amax=alpha)
+        assert r["scales"][0] == s
+        v = x32 / s
+        q = np.clip(np.rint(v), -127, 127).astype(np.int8)
+        assert np.array_equal(r["codes"].view(np.int8), q)
+        assert np.array_equal(r["xhat"], (s * q.astype(np.float32)).astype(np.float32))
+        assert r["stats"]["n_saturated"] == int(np.count_nonzero(np.abs(v) > 127))
+
+
+def test_static_scale_fp8_saturates_to_torch_clamp(O, S):
+    """E4M3 / E5M2 with alpha below the data: codes equal torch's float8 cast
+    of clamp(x / s, -FMAX, FMAX) (torch's cast rounds to nearest even and
+    does not saturate, hence the clamp)."""
+    x = S.make("c1", nrows=32)
+    x32 = x_f32(S, x)
+    G = float(np.max(np.abs(x32)))
+    for fmt, tdt, fmax in (("e4m3", torch.float8_e4m3fn, 448.0), ("e5m2", torch.float8_e5m2, 57344.0)):
+        alpha = 0.1 * G
+        r = O.quantize(x, fmt, "tensor", static_amax=alpha)
+        s = np.float32(np.float32(alpha) / np.float32(fmax))
+        v = np.clip(x32 / s, -fmax, fmax).astype(np.float32)
+        want = torch.from_numpy(v).to(tdt).view(torch.uint8).numpy()
+        assert np.array_equal(r["codes"], want), fmt
+        assert r["stats"]["n_saturated"] == int(np.count_nonzero(np.abs(x32 / s) > fmax))
+
+
+def test_static_scale_invalid_alpha_is_zero(O, S):
+    """NaN, negative and infinite alphas are taken as 0 (every code +0,
+    scale 0, x^ = 0); -0 as +0."""
+    x = S.make("c1", nrows=8)
+    assert O._load().iqo_static_amax(float("nan")) == 0.0
+    assert O._load().iqo_static_amax(-1.0) == 0.0
+    assert O._load().iqo_static_amax(float("inf")) == 0.0
+    assert not math.copysign(1.0, O._load().iqo_static_amax(-0.0)) < 0
+    assert O._load().iqo_static_amax(2.5) == 2.5
+    for alpha in (float("nan"), -3.0, float("inf"), -0.0):
+        for fmt, gran in (("int8", "tensor"), ("e4m3", "tensor"), ("nvfp4", "block")):
+            r = O.quantize(x, fmt, gran, static_amax=alpha)
+            assert not r["codes"].any() and not r["scales"].any()
+            assert not r["xhat"].any() and not np.signbit(r["xhat"]).any()
+            if fmt == "nvfp4":
+                assert r["global_scale"][0] == 0.0 and not np.signbit(r["global_scale"][0])
+
+
 # ---- P11: INT4 and the nibble order of Puzzle 12 ---------------------------------
 def test_p11_int4_bound_and_nibbles(O, S):
     x = S.make("c5", nrows=64)

@@ -557,3 +557,132 @@ def test_nv_block_scale_rounding(iq, O, S, flags):
     r = oracle_ref(O, x, "nvfp4", "block", flags=flags)
     assert r["global_scale"][0] == np.float32(1.0)
     compare(g, r, "nvfp4", f"nvfp4 block-scale rounding flags={flags}", O)
+
+
+# ---- static (calibrated) scaling: iq_quantize_static -------------------------------
+STATIC = [("int8", "tensor"), ("e4m3", "tensor"), ("e5m2", "tensor"), ("nvfp4", "block")]
+
+
+def run_gpu_static(iq, x_np, fmt, gran, alpha, cols=None, xhat="f32"):
+    import torch
+    x = to_device(x_np)
+    if cols is not None:
+        x = x[:, :cols]
+    a = torch.tensor([alpha], dtype=torch.float32, device=x.device)
+    xdt = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[xhat]
+    q = iq.quantize(x, fmt, gran, xhat_dtype=xdt, static_amax=a)
+    torch.cuda.synchronize()
+    out = {"codes": q.codes.cpu().numpy(), "scales": q.scales.cpu().numpy(), "stats": q.stats(), "q": q}
+    if q.global_scale is not None:
+        out["global_scale"] = q.global_scale.cpu().numpy()
+    if q.xhat is not None:
+        out["xhat"] = q.xhat.cpu().numpy()
+    return out
+
+
+def static_alphas(G):
+    """Calibrated absmaxes around the data's own G: equal, below (clipping),
+    above, tiny, huge, and the invalid values taken as 0."""
+    return [G, 0.5 * G, 0.01 * G, 4.0 * G, 1e-30, 1e30, 0.0, -0.0, -1.0, float("nan"), float("inf")]
+
+
+@pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt,gran", STATIC)
+def test_static_parity(iq, O, S, fmt, gran, dtype):
+    """Every calibrated absmax on multi-tile and ragged shapes, and on the
+    special-value matrix (non-finite inputs, zeros, subnormals)."""
+    for i, (rows, cols, ld) in enumerate(SHAPES):
+        if cols % 16:
+            continue
+        x = make_input(S, dtype, rows, cols, ld, seed=500 + i)
+        c = cols if ld else None
+        G = float(O.quantize(x, fmt, gran, cols=c, want_xhat=False)["tensor_amax"])
+        for alpha in static_alphas(G):
+            g = run_gpu_static(iq, x, fmt, gran, alpha, cols=c)
+            r = O.quantize(x, fmt, gran, cols=c, static_amax=alpha, threads=THREADS)
+            compare(g, r, fmt, f"static {fmt}/{gran} {rows}x{cols} ld={ld} alpha={alpha!r}", O)
+    x = bf16_special_matrix(S) if dtype else f32_special_matrix(S)
+    for alpha in (1.0, 1e-30, 3e38, float("nan")):
+        g = run_gpu_static(iq, x, fmt, gran, alpha)
+        r = O.quantize(x, fmt, gran, static_amax=alpha, threads=THREADS)
+        compare(g, r, fmt, f"static {fmt}/{gran} special alpha={alpha!r}", O)
+
+
+@pytest.mark.parametrize("cfg,fmt,gran", [("c1", "int8", "tensor"), ("c1", "e4m3", "tensor"),
+                                          ("c4", "nvfp4", "block")])
+def test_static_full_size(iq, O, S, cfg, fmt, gran):
+    """The per-tensor workloads at full size with a calibrated absmax below
+    the data's (outlier columns clip)."""
+    x = S.make(cfg)
+    G = float(np.max(np.abs(S.bf16_to_f32(x) if x.dtype == np.uint16 else x)))
+    alpha = 0.3 * G
+    g = run_gpu_static(iq, x, fmt, gran, alpha, xhat=None)
+    r = O.quantize(x, fmt, gran, static_amax=alpha, want_xhat=False, threads=THREADS)
+    compare(g, r, fmt, f"static {cfg} {fmt}/{gran} full size", O)
+    assert r["stats"]["n_saturated"] > 0
+
+
+@pytest.mark.parametrize("fmt,gran", STATIC)
+def test_static_after_amax_equals_dynamic(iq, S, fmt, gran):
+    """iq_amax then iq_quantize_static on the same stream reproduces
+    iq_quantize bit for bit (codes, scales, x^ and statistics)."""
+    import torch
+    x = to_device(make_input(S, 1, 96, 4096, None, seed=61))
+    a = iq.amax(x)
+    qs = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32, static_amax=a)
+    qd = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(qs.codes, qd.codes) and torch.equal(qs.scales.view(torch.uint8), qd.scales.view(torch.uint8))
+    assert torch.equal(qs.xhat.view(torch.int32), qd.xhat.view(torch.int32))
+    if fmt == "nvfp4":
+        assert torch.equal(qs.global_scale, qd.global_scale)
+    assert qs.stats() == qd.stats()
+
+
+@pytest.mark.parametrize("fmt,gran", STATIC)
+def test_static_empty(iq, O, fmt, gran):
+    """An empty input still gets the scale derived from the supplied absmax."""
+    import torch
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda:0")
+    a = torch.tensor([254.0], dtype=torch.float32, device="cuda:0")
+    q = iq.quantize(x, fmt, gran, static_amax=a)
+    torch.cuda.synchronize()
+    r = O.quantize(np.zeros((0, 256), np.uint16), fmt, gran, static_amax=254.0)
+    st = q.stats()
+    assert st["n"] == 0 and st["sum_x2"] == 0.0
+    if gran == "tensor":
+        assert np.float32(q.scales.cpu().item()) == r["scales"][0]
+    else:
+        assert np.float32(q.global_scale.cpu().item()) == r["global_scale"][0]
+
+
+@pytest.mark.parametrize("fmt,gran", [("e4m3", "tensor"), ("nvfp4", "block")])
+def test_static_graph_replay(iq, S, fmt, gran):
+    """A captured iq_quantize_static (the calibrated mode a serving loop
+    captures) reads its absmax buffer at replay time: refilled before each
+    replay, it reproduces the eager bytes, with eager work in between."""
+    import torch
+    x = to_device(S.make("c4", nrows=256))
+    ws = iq.workspace_for(iq.desc_for(x, fmt, gran), x.device)
+    a = iq.amax(x)
+    ref = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32, workspace=ws, static_amax=a)
+    torch.cuda.synchronize()
+    want = (ref.codes.cpu(), ref.scales.cpu(), ref.xhat.cpu(), ref.stats())
+    a2 = torch.empty_like(a)
+    out = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32, workspace=ws, static_amax=a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.quantize(x, fmt, gran, workspace=ws, out=out, static_amax=a2)
+    for rep in range(3):
+        out.codes.zero_(); out.scales.zero_(); out.xhat.zero_(); out.stats_buf.zero_()
+        a2.copy_(a)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (out.codes.cpu(), out.scales.cpu(), out.xhat.cpu(), out.stats())
+        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1]), rep
+        assert torch.equal(got[2].view(torch.int32), want[2].view(torch.int32)), rep
+        assert got[3] == want[3], rep
+        a2.fill_(-1.0)                                       # invalid absmax: taken as 0 if replayed now
+        iq.quantize(x, "mxfp4", "block", workspace=ws)
+        torch.cuda.synchronize()
