@@ -29,7 +29,14 @@
  *   zero scale         a zero scale (all-zero unit) gives +0 codes and x^ = 0;
  *   absmax             over finite elements only; +-Inf saturates, NaN -> NaN code
  *                      (FP8: 0x7F) or +0 (E2M1, INT);
- *   nibble order       element 2t in bits 3:0 of byte t, element 2t+1 in bits 7:4.
+ *   nibble order       element 2t in bits 3:0 of byte t, element 2t+1 in bits 7:4;
+ *   asymmetric INT4    [TR] Puzzle 12 fixes the decoder x^ = sc*(w - sh) with
+ *                      unsigned 4-bit w and sh and a float sc per group; the
+ *                      encoder is the min-max one: range [lo, hi] widened to
+ *                      hold 0, sc = (hi - lo)/15 (binary32; an overflowing
+ *                      range is clamped to the largest float), sh = RNE(-lo/sc)
+ *                      in [0, 15], w = clamp(RNE(x/sc) + sh, 0, 15); groups of
+ *                      128, shifts two per byte.
  */
 #include "iq_oracle.h"
 
@@ -180,6 +187,7 @@ int64_t iqo_block_size(int fmt, int gran) {
     case IQO_MXFP4: return gran == IQO_PER_BLOCK ? 32 : -1;
     case IQO_NVFP4: return gran == IQO_PER_BLOCK ? 16 : -1;
     case IQO_INT4:  return gran == IQO_PER_BLOCK ? 128 : -1;
+    case IQO_INT4ZP: return gran == IQO_PER_BLOCK ? 128 : -1;
     default: return -1;
     }
 }
@@ -191,6 +199,7 @@ int iqo_check(const iqo_desc* d) {
     if (b < 0) return -1;
     if (d->rows < 0 || d->cols < 0 || d->ld < d->cols) return -1;
     if (b > 0 && d->cols % b) return -1;
+    if (d->fmt == IQO_INT4ZP && d->cols % 256) return -1; /* whole shift bytes per row */
     return 0;
 }
 
@@ -228,9 +237,9 @@ typedef struct {
 
 /* v is the scaled value x/s (0 when the scale is zero); qmax the largest
  * code magnitude of the grid, for the saturation count. */
-static void acc_elem(acc_t* a, float x, float v, float xh, float qmax) {
+static void acc_elem_sat(acc_t* a, float x, int saturated, float xh) {
     a->n++;
-    if (fabsf(v) > qmax) a->n_saturated++;
+    if (saturated) a->n_saturated++;
     if (!isfinite(x)) { a->n_nonfinite++; return; }
     float d = x - xh; /* exact: x and x^ are within a factor 2 (Sterbenz) or x^ = 0 */
     a->sum_x2 += (double)x * (double)x;
@@ -238,6 +247,10 @@ static void acc_elem(acc_t* a, float x, float v, float xh, float qmax) {
     a->sum_abs_err += fabs((double)d);
     if (fabsf(d) > a->max_abs_err) a->max_abs_err = fabsf(d);
     if (x != 0.0f && xh == 0.0f) a->n_zero_flush++;
+}
+
+static void acc_elem(acc_t* a, float x, float v, float xh, float qmax) {
+    acc_elem_sat(a, x, fabsf(v) > qmax, xh);
 }
 
 static void acc_add(acc_t* t, const acc_t* a) {
@@ -381,9 +394,102 @@ static void stats_out(iqo_stats* st, const acc_t* t) {
     st->sum_abs_err = t->sum_abs_err; st->max_abs_err = t->max_abs_err; st->reserved = 0;
 }
 
+/* [TR] Puzzle 12: asymmetric 4-bit codes.  The page gives the decoder
+ * x^ = sc * (w - sh) (w, sh unsigned 4-bit, sc a float per group); the
+ * encoder below is the min-max reading.  Over the group's finite elements,
+ * lo = min(0, min x) and hi = max(0, max x), so 0 is on the grid;
+ * sc = (hi - lo) / 15 in binary32 (clamped to the largest float if the
+ * range overflows); sh = RNE(-lo / sc) clamped to [0, 15]; each element
+ * takes q = RNE(x / sc) as the symmetric INT formats do and stores
+ * w = clamp(q + sh, 0, 15).  sc == 0 gives w = sh = 0 and x^ = 0.  NaN
+ * maps to w = sh (x^ = 0), +-Inf to 15 or 0.  Saturated: x/sc beyond the
+ * grid's ends, above 15 - sh or below -sh. */
+static uint8_t zp_code(float v, int sh) {
+    if (isnan(v)) return (uint8_t)sh;
+    double w = nearbyint((double)v) + (double)sh; /* v is finite or +-Inf */
+    if (w < 0.0) w = 0.0;
+    if (w > 15.0) w = 15.0;
+    return (uint8_t)w;
+}
+
+static void row_int4zp(const iqo_desc* d, const void* x, int64_t r, uint8_t* codes, float* scales,
+                       uint8_t* shifts, float* xhat, acc_t* a) {
+    int64_t ng = d->cols / 128;
+    uint8_t* rc = codes + r * (d->cols / 2);
+    uint8_t* rs = shifts + r * (ng / 2);
+    for (int64_t g = 0; g < ng; ++g) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t c = g * 128; c < g * 128 + 128; ++c) {
+            float v = load_x(d, x, r, c);
+            if (!isfinite(v)) continue;
+            if (v < lo) lo = v;
+            if (v > hi) hi = v;
+        }
+        float sc = (hi - lo) / 15.0f;
+        if (isinf(sc)) sc = 3.40282347e38f; /* largest binary32 */
+        int sh = 0;
+        if (sc != 0.0f) {
+            float z = nearbyintf(-lo / sc);
+            sh = z < 0.0f ? 0 : (z > 15.0f ? 15 : (int)z);
+        }
+        scales[r * ng + g] = sc;
+        put_nibble(rs, g, (uint32_t)sh);
+        for (int64_t c = g * 128; c < g * 128 + 128; ++c) {
+            float xv = load_x(d, x, r, c);
+            float v = 0.0f;
+            uint8_t w = (uint8_t)sh;
+            if (sc != 0.0f) {
+                v = xv / sc;
+                w = zp_code(v, sh);
+            }
+            put_nibble(rc, c, w);
+            float xh = sc * (float)((int)w - sh);
+            if (xhat) xhat[r * d->cols + c] = xh;
+            acc_elem_sat(a, xv, v > (float)(15 - sh) || v < (float)(-sh), xh);
+        }
+    }
+}
+
+int iqo_quantize_zp_rows(const iqo_desc* d, const void* x, int64_t r0, int64_t r1, uint8_t* codes,
+                         float* scales, uint8_t* shifts, float* xhat, iqo_stats* st) {
+    if (iqo_check(d) || d->fmt != IQO_INT4ZP || r0 < 0 || r1 > d->rows || r0 > r1) return -1;
+    if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+    acc_t total;
+    memset(&total, 0, sizeof total);
+    for (int64_t r = r0; r < r1; ++r) {
+        acc_t a;
+        memset(&a, 0, sizeof a);
+        row_int4zp(d, x, r, codes, scales, shifts, xhat, &a);
+        acc_add(&total, &a);
+    }
+    if (st) stats_out(st, &total);
+    return 0;
+}
+
+int iqo_dequantize_zp(const iqo_desc* d, const uint8_t* codes, const float* scales, const uint8_t* shifts,
+                      void* xhat, int xhat_dtype) {
+    if (iqo_check(d) || d->fmt != IQO_INT4ZP) return -1;
+    if (xhat_dtype != IQO_F32 && xhat_dtype != IQO_BF16) return -1;
+    if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+    int64_t ng = d->cols / 128;
+    for (int64_t r = 0; r < d->rows; ++r) {
+        for (int64_t c = 0; c < d->cols; ++c) {
+            uint8_t byte = codes[r * (d->cols / 2) + c / 2];
+            int w = (int)((c & 1) ? (byte >> 4) : (byte & 0xFu));
+            int64_t g = c / 128;
+            uint8_t sb = shifts[r * (ng / 2) + g / 2];
+            int sh = (int)((g & 1) ? (sb >> 4) : (sb & 0xFu));
+            float xh = scales[r * ng + g] * (float)(w - sh);
+            if (xhat_dtype == IQO_F32) ((float*)xhat)[r * d->cols + c] = xh;
+            else ((uint16_t*)xhat)[r * d->cols + c] = iqo_f32_to_bf16(xh);
+        }
+    }
+    return 0;
+}
+
 int iqo_quantize_rows(const iqo_desc* d, const void* x, int64_t r0, int64_t r1, float tensor_amax,
                       uint8_t* codes, void* scales, float* global_scale, float* xhat, iqo_stats* st) {
-    if (iqo_check(d) || r0 < 0 || r1 > d->rows || r0 > r1) return -1;
+    if (iqo_check(d) || d->fmt == IQO_INT4ZP || r0 < 0 || r1 > d->rows || r0 > r1) return -1;
     if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
     acc_t total;
     memset(&total, 0, sizeof total);
@@ -439,7 +545,7 @@ int iqo_quantize_static(const iqo_desc* d, const void* x, float amax_in, uint8_t
 /* ---- dequantization: x^ = s * decode(q), the same products as above ----- */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype) {
-    if (iqo_check(d)) return -1;
+    if (iqo_check(d) || d->fmt == IQO_INT4ZP) return -1;
     if (xhat_dtype != IQO_F32 && xhat_dtype != IQO_BF16) return -1;
     if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
     for (int64_t r = 0; r < d->rows; ++r) {

@@ -25,7 +25,8 @@ extern "C" {
 #endif
 
 /* Quantized formats. */
-enum { IQO_INT8 = 0, IQO_E4M3 = 1, IQO_E5M2 = 2, IQO_MXFP4 = 3, IQO_NVFP4 = 4, IQO_INT4 = 5 };
+enum { IQO_INT8 = 0, IQO_E4M3 = 1, IQO_E5M2 = 2, IQO_MXFP4 = 3, IQO_NVFP4 = 4, IQO_INT4 = 5,
+       IQO_INT4ZP = 6 /* unsigned 4-bit codes, per-group scale and 4-bit shift (Puzzle 12) */ };
 /* Scale granularity. */
 enum { IQO_PER_TENSOR = 0, IQO_PER_ROW = 1, IQO_PER_BLOCK = 2 };
 /* Element types of inputs and dequantized outputs. */
@@ -87,6 +88,13 @@ float iqo_static_amax(float amax_in);
 /* Whole tensor with a caller-supplied absmax (per-tensor formats, NVFP4). */
 int iqo_quantize_static(const iqo_desc* d, const void* x, float amax_in, uint8_t* codes, void* scales,
                         float* global_scale, float* xhat, iqo_stats* st);
+/* Asymmetric INT4 (IQO_INT4ZP, per block of 128; cols a multiple of 256):
+ * codes [rows, cols/2] unsigned nibbles, scales float [rows, cols/128],
+ * shifts [rows, cols/256] bytes, group 2t in bits 3:0.  Rows [r0, r1). */
+int iqo_quantize_zp_rows(const iqo_desc* d, const void* x, int64_t r0, int64_t r1, uint8_t* codes,
+                         float* scales, uint8_t* shifts, float* xhat, iqo_stats* st);
+int iqo_dequantize_zp(const iqo_desc* d, const uint8_t* codes, const float* scales, const uint8_t* shifts,
+                      void* xhat, int xhat_dtype);
 /* Reconstruct xhat ([rows, cols], FP32 or BF16) from codes and scales. */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype);

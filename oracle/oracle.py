@@ -20,12 +20,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "iq_oracle.c")
 _LIB = os.path.join(_HERE, "libiq_oracle.so")
 
-FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5}
+FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5, "int4zp": 6}
 GRANS = {"tensor": 0, "row": 1, "block": 2}
 F32, BF16 = 0, 1
 K_E4M3, K_E5M2, K_E2M1, K_F16 = 0, 1, 2, 3
 FLAG_MX_ROUND_NEAREST, FLAG_MX_ROUND_UP, FLAG_NV_SCALE_RNE = 1, 2, 4
 QMAX = {"int8": 127.0, "e4m3": 448.0, "e5m2": 57344.0, "mxfp4": 6.0, "nvfp4": 6.0, "int4": 7.0}
+FOUR_BIT = ("mxfp4", "nvfp4", "int4", "int4zp")
 
 
 def build() -> str:
@@ -83,6 +84,9 @@ def _load():
                                                  ctypes.POINTER(Stats)]),
             "iqo_quantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, P, ctypes.POINTER(Stats)]),
             "iqo_static_amax": (F, [F]),
+            "iqo_quantize_zp_rows": (ctypes.c_int, [ctypes.POINTER(Desc), P, I64, I64, P, P, P, P,
+                                                    ctypes.POINTER(Stats)]),
+            "iqo_dequantize_zp": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
             "iqo_quantize_static": (ctypes.c_int, [ctypes.POINTER(Desc), P, F, P, P, P, P,
                                                    ctypes.POINTER(Stats)]),
             "iqo_dequantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
@@ -154,7 +158,7 @@ def block_size(fmt: str, gran: str) -> int:
 
 # ---- layouts ---------------------------------------------------------------
 def codes_shape(fmt: str, rows: int, cols: int) -> tuple:
-    return (rows, cols // 2) if fmt in ("mxfp4", "nvfp4", "int4") else (rows, cols)
+    return (rows, cols // 2) if fmt in FOUR_BIT else (rows, cols)
 
 
 def scales_spec(fmt: str, gran: str, rows: int, cols: int) -> tuple:
@@ -165,7 +169,14 @@ def scales_spec(fmt: str, gran: str, rows: int, cols: int) -> tuple:
         return (rows, cols // 32), np.uint8
     if fmt == "nvfp4":
         return (rows, cols // 16), np.uint8
+    if fmt == "int4zp":
+        return (rows, cols // 128), np.float32
     return (rows, cols // 128), np.uint16
+
+
+def shifts_shape(rows: int, cols: int) -> tuple:
+    """Asymmetric INT4 shifts: two 4-bit values per byte, group 2t in bits 3:0."""
+    return (rows, cols // 256)
 
 
 def _desc(fmt, gran, x, cols=None, flags=0):
@@ -216,11 +227,16 @@ def quantize(x: np.ndarray, fmt: str, gran: str, cols: int | None = None, flags:
         tensor_amax = L.iqo_amax(ctypes.byref(d), _p(x))
     parts = _split(rows, threads)
     stats = [Stats() for _ in parts]
+    shifts = np.zeros(shifts_shape(rows, c), dtype=np.uint8) if fmt == "int4zp" else None
 
     def run(i):
         r0, r1 = parts[i]
-        rc = L.iqo_quantize_rows(ctypes.byref(d), _p(x), r0, r1, tensor_amax, _p(codes), _p(scales),
-                                 _p(g), _p(xhat), ctypes.byref(stats[i]))
+        if shifts is not None:
+            rc = L.iqo_quantize_zp_rows(ctypes.byref(d), _p(x), r0, r1, _p(codes), _p(scales), _p(shifts),
+                                        _p(xhat), ctypes.byref(stats[i]))
+        else:
+            rc = L.iqo_quantize_rows(ctypes.byref(d), _p(x), r0, r1, tensor_amax, _p(codes), _p(scales),
+                                     _p(g), _p(xhat), ctypes.byref(stats[i]))
         if rc:
             raise RuntimeError("iqo_quantize_rows failed")
 
@@ -230,8 +246,11 @@ def quantize(x: np.ndarray, fmt: str, gran: str, cols: int | None = None, flags:
         with ThreadPoolExecutor(len(parts)) as ex:
             list(ex.map(run, range(len(parts))))
     st = merge_stats([s.as_dict() for s in stats])
-    return {"codes": codes, "scales": scales, "global_scale": g, "xhat": xhat, "stats": st,
-            "tensor_amax": tensor_amax}
+    out = {"codes": codes, "scales": scales, "global_scale": g, "xhat": xhat, "stats": st,
+           "tensor_amax": tensor_amax}
+    if shifts is not None:
+        out["shifts"] = shifts
+    return out
 
 
 def quantize_rows(x: np.ndarray, fmt: str, gran: str, row0: int, nrows: int, tensor_amax: float,
@@ -246,19 +265,34 @@ def quantize_rows(x: np.ndarray, fmt: str, gran: str, row0: int, nrows: int, ten
     g = np.zeros(1, dtype=np.float32)
     xhat = np.zeros((rows, c), dtype=np.float32)
     st = Stats()
-    rc = _load().iqo_quantize_rows(ctypes.byref(d), _p(x), 0, rows, float(tensor_amax), _p(codes),
-                                   _p(scales), _p(g), _p(xhat), ctypes.byref(st))
+    out = {"codes": codes, "scales": scales, "global_scale": g, "xhat": xhat}
+    if fmt == "int4zp":
+        out["shifts"] = np.zeros(shifts_shape(rows, c), dtype=np.uint8)
+        rc = _load().iqo_quantize_zp_rows(ctypes.byref(d), _p(x), 0, rows, _p(codes), _p(scales),
+                                          _p(out["shifts"]), _p(xhat), ctypes.byref(st))
+    else:
+        rc = _load().iqo_quantize_rows(ctypes.byref(d), _p(x), 0, rows, float(tensor_amax), _p(codes),
+                                       _p(scales), _p(g), _p(xhat), ctypes.byref(st))
     if rc:
         raise RuntimeError("iqo_quantize_rows failed")
-    return {"codes": codes, "scales": scales, "global_scale": g, "xhat": xhat, "stats": st.as_dict()}
+    out["stats"] = st.as_dict()
+    return out
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, gran: str, rows: int, cols: int,
-               global_scale: np.ndarray | None = None, out_dtype: int = F32) -> np.ndarray:
+               global_scale: np.ndarray | None = None, out_dtype: int = F32,
+               shifts: np.ndarray | None = None) -> np.ndarray:
     d = Desc(FORMATS[fmt], GRANS[gran], F32, rows, cols, cols, 0)
     if _load().iqo_check(ctypes.byref(d)):
         raise ValueError("illegal descriptor")
     out = np.zeros((rows, cols), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    if fmt == "int4zp":
+        rc = _load().iqo_dequantize_zp(ctypes.byref(d), _p(np.ascontiguousarray(codes)),
+                                       _p(np.ascontiguousarray(scales, dtype=np.float32)),
+                                       _p(np.ascontiguousarray(shifts, dtype=np.uint8)), _p(out), out_dtype)
+        if rc:
+            raise RuntimeError("iqo_dequantize_zp failed")
+        return out
     g = None if global_scale is None else np.ascontiguousarray(global_scale, dtype=np.float32)
     rc = _load().iqo_dequantize(ctypes.byref(d), _p(np.ascontiguousarray(codes)),
                                 _p(np.ascontiguousarray(scales)), _p(g), _p(out), out_dtype)

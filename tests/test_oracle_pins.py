@@ -621,6 +621,117 @@ def test_p11_int4_bound_and_nibbles(O, S):
         assert np.array_equal(nib, (q[:, i::8].astype(np.int64) & 0xF))
 
 
+# ---- P15: asymmetric INT4 of Puzzle 12 (decoder printed, encoder read) ------------
+def puzzle12_extract(words: np.ndarray) -> np.ndarray:
+    """The page's extract(): value i of a 32-bit word is (word >> 4i) & 0xF."""
+    over = np.arange(8, dtype=np.uint32) * 4
+    return ((words[..., None] >> over) & np.uint32(0xF)).reshape(*words.shape[:-1], -1)
+
+
+def zp_input(S, rows=48, cols=1024, seed=71):
+    """Weight-like rows (c5 recipe), one group all positive, one all
+    negative, one all zero, one symmetric, one constant."""
+    x = S.bf16_to_f32(S.make("c5", nrows=rows))[:, :cols].copy()
+    x[0, 0:128] = np.abs(x[0, 0:128])
+    x[0, 128:256] = -np.abs(x[0, 128:256])
+    x[0, 256:384] = 0.0
+    x[1, 0:128] = np.linspace(-1, 1, 128, dtype=np.float32)
+    x[1, 128:256] = np.float32(0.37)
+    return np.ascontiguousarray(x.astype(np.float32))
+
+
+def test_p15_zp_decoder_is_puzzle12(O, S):
+    """Codes and shifts read as 32-bit words through the page's extract(),
+    decoded by its sc * (w - sh), give the oracle's x^ bit for bit."""
+    x = zp_input(S)
+    r = O.quantize(x, "int4zp", "block")
+    rows, cols = x.shape
+    assert (cols // 128) % 8 == 0                        # whole 32-bit words of shifts per row
+    w = puzzle12_extract(r["codes"].view("<u4")).astype(np.int32)                 # [rows, cols]
+    sh = puzzle12_extract(r["shifts"].view("<u4")).astype(np.int32)               # [rows, cols / 128]
+    assert sh.shape == (rows, cols // 128)
+    sc = r["scales"].astype(np.float32)
+    want = (np.repeat(sc, 128, axis=1) * (w - np.repeat(sh, 128, axis=1)).astype(np.float32)).astype(np.float32)
+    assert np.array_equal(r["xhat"], want)
+    d = O.dequantize(r["codes"], r["scales"], "int4zp", "block", rows, cols, shifts=r["shifts"])
+    assert np.array_equal(d, r["xhat"])
+
+
+def test_p15_zp_nearest_grid_point(O, S):
+    """Exhaustive search: each code is the grid point k in [-sh, 15 - sh]
+    nearest to v = x / sc (binary32 quotient), ties to even k; the scale
+    spans the range [min(0, x), max(0, x)] in 15 steps, and the shift puts
+    0 within half a step of -lo / sc."""
+    x = zp_input(S)
+    r = O.quantize(x, "int4zp", "block")
+    rows, cols = x.shape
+    ng = cols // 128
+    w = puzzle12_extract(r["codes"].view("<u4")).astype(np.int64)
+    sh = puzzle12_extract(r["shifts"].view("<u4")).astype(np.int64)
+    ks = np.arange(-15, 16)
+    for i in range(rows):
+        for g in range(ng):
+            xb = x[i, g * 128:(g + 1) * 128]
+            sc, s = np.float32(r["scales"][i, g]), int(sh[i, g])
+            lo, hi = min(0.0, float(xb.min())), max(0.0, float(xb.max()))
+            if hi == lo:
+                assert sc == 0 and s == 0 and not w[i, g * 128:(g + 1) * 128].any()
+                continue
+            assert abs(15 * float(sc) - (hi - lo)) <= (hi - lo) * 2.0 ** -23
+            assert abs(s - (-lo / float(sc))) <= 0.5 + 1e-6
+            v = (xb / sc).astype(np.float32).astype(np.float64)
+            grid = ks[(ks >= -s) & (ks <= 15 - s)]
+            dist = np.abs(v[:, None] - grid[None, :])
+            best = dist == dist.min(axis=1, keepdims=True)
+            pick = np.array([grid[b][0] if b.sum() == 1 else grid[b][grid[b] % 2 == 0][0] for b in best])
+            assert np.array_equal(w[i, g * 128:(g + 1) * 128] - s, pick), (i, g)
+
+
+def test_p15_zp_bounds_and_textbook_cases(O, S):
+    """|x - x^| <= sc/2 inside the grid and <= sc at its ends; an all-positive
+    group is unsigned 4-bit quantization (sh = 0, w = clip(rint(x / sc), 0, 15),
+    numpy); an all-negative group has sh = 15; an all-zero group has sc = 0;
+    the statistics' counts match brute force."""
+    x = zp_input(S)
+    r = O.quantize(x, "int4zp", "block")
+    rows, cols = x.shape
+    sh = puzzle12_extract(r["shifts"].view("<u4")).astype(np.int64)
+    sc = np.repeat(r["scales"].astype(np.float64), 128, axis=1)
+    shr = np.repeat(sh, 128, axis=1)
+    v = (x / np.repeat(r["scales"], 128, axis=1)).astype(np.float32).astype(np.float64)
+    err = np.abs(x.astype(np.float64) - r["xhat"].astype(np.float64))
+    inside = (v <= 15 - shr) & (v >= -shr)
+    assert (err[inside] <= sc[inside] * 0.5 * (1 + 2.0 ** -20)).all()
+    assert (err <= sc * (1 + 2.0 ** -20)).all()
+    assert sh[0, 0] == 0 and sh[0, 1] == 15 and r["scales"][0, 2] == 0.0 and sh[0, 2] == 0
+    s0 = np.float32(r["scales"][0, 0])
+    want = np.clip(np.rint(x[0, :128] / s0), 0, 15).astype(np.int64)
+    assert np.array_equal(puzzle12_extract(r["codes"][0:1, :64].copy().view("<u4"))[0], want)
+    st = r["stats"]
+    assert st["n_saturated"] == int(np.count_nonzero(~inside & (sc > 0)))
+    assert st["n_zero_flush"] == int(np.count_nonzero((x != 0) & (r["xhat"] == 0)))
+    assert st["n"] == x.size
+
+
+def test_p15_zp_special_values(O):
+    """NaN maps to w = sh (x^ = 0), +-Inf to the grid ends; a group whose
+    range overflows binary32 takes the largest float as its scale."""
+    x = np.zeros((2, 256), np.float32)
+    x[0, :128] = np.linspace(-2, 2, 128, dtype=np.float32)
+    x[0, 5], x[0, 6], x[0, 7] = np.nan, np.inf, -np.inf
+    x[1, 0], x[1, 1] = np.float32(3e38), np.float32(-3e38)
+    x[1, 128] = np.nan
+    r = O.quantize(x, "int4zp", "block")
+    w = puzzle12_extract(r["codes"].view("<u4"))
+    sh = np.stack([r["shifts"] & 0xF, r["shifts"] >> 4], axis=-1).reshape(2, -1)   # one byte per row
+    assert w[0, 5] == sh[0, 0] and r["xhat"][0, 5] == 0.0
+    assert w[0, 6] == 15 and w[0, 7] == 0
+    assert r["stats"]["n_nonfinite"] == 4
+    assert r["scales"][1, 0] == np.float32(3.4028235e38)
+    assert np.isfinite(r["xhat"][1]).all()
+    assert r["scales"][1, 1] == 0.0 and w[1, 128] == 0
+
+
 # ---- P14: statistics by brute force ------------------------------------------------
 @pytest.mark.parametrize("fmt,gran,cfg", [("e4m3", "row", "c2"), ("e5m2", "row", "c2"),
                                           ("int8", "tensor", "c1"), ("mxfp4", "block", "c3"),
