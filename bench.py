@@ -60,13 +60,15 @@ def to_device(x_np):
 def algo_bytes(fmt, gran, rows, cols, in_elem):
     """Bytes the method itself must move: x once, codes + scales once."""
     n = rows * cols
-    codes = n // 2 if fmt in ("mxfp4", "nvfp4", "int4") else n
+    codes = n // 2 if fmt in ("mxfp4", "nvfp4", "int4", "int4zp") else n
     if fmt in ("int8", "e4m3", "e5m2"):
         scales = 4 if gran == "tensor" else 4 * rows
     elif fmt == "mxfp4":
         scales = n // 32
     elif fmt == "nvfp4":
         scales = n // 16 + 4
+    elif fmt == "int4zp":
+        scales = 4 * (n // 128) + n // 256      # FP32 scale and a 4-bit shift per group
     else:
         scales = 2 * (n // 128)
     return n * in_elem + codes + scales, codes + scales

@@ -37,6 +37,9 @@
  *               global_scale float32 [1]
  *   INT4        codes  uint8 [rows, K/2]  two's-complement nibbles, q in [-7, 7];
  *               scales float16 bits [rows, K/128]
+ *   INT4_ZP     codes  uint8 [rows, K/2]  unsigned nibbles w in [0, 15];
+ *               scales float32 [rows, K/128]; shifts uint8 [rows, K/256]
+ *               (4-bit sh, group 2t in bits 3:0); K a multiple of 256
  *   INT8 / FP8 scales: float32 [1] per tensor, float32 [rows] per row.
  *   4-bit codes: element 2t in bits 3:0 of byte t, element 2t+1 in bits 7:4
  *   (the order of the packed-word extract() of the Triton post, Puzzle 12).
@@ -69,7 +72,9 @@ typedef enum {
     IQ_FP8_E5M2 = 2, /* s = alpha / 57344 */
     IQ_MXFP4 = 3,    /* E2M1 codes, one E8M0 scale per 32 elements ("MXFP4") */
     IQ_NVFP4 = 4,    /* E2M1 codes, one E4M3 scale per 16 + FP32 global scale ("NVFP4") */
-    IQ_INT4 = 5      /* symmetric, s = A / 7 per group of 128, FP16 scale ("INT4") */
+    IQ_INT4 = 5,     /* symmetric, s = A / 7 per group of 128, FP16 scale ("INT4") */
+    IQ_INT4_ZP = 6   /* asymmetric: unsigned codes, FP32 scale + 4-bit shift per group of 128
+                        (Triton post, Puzzle 12); only through iq_quantize_zp / iq_dequantize_zp */
 } iq_format;
 
 typedef enum { IQ_F32 = 0, IQ_BF16 = 1 } iq_dtype;
@@ -77,7 +82,7 @@ typedef enum { IQ_F32 = 0, IQ_BF16 = 1 } iq_dtype;
 typedef enum {
     IQ_PER_TENSOR = 0, /* INT8 / FP8 */
     IQ_PER_ROW = 1,    /* INT8 / FP8 */
-    IQ_PER_BLOCK = 2   /* MXFP4 (32), NVFP4 (16), INT4 (128): the only legal choice for those */
+    IQ_PER_BLOCK = 2   /* MXFP4 (32), NVFP4 (16), INT4 and INT4_ZP (128): the only legal choice for those */
 } iq_gran;
 
 /* Rule variants (iq_desc.flags); 0 selects the default readings. */
@@ -166,6 +171,38 @@ iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* worksp
 iq_status iq_quantize_static(const iq_desc* d, const void* x, const float* amax_in, void* codes,
                              void* scales, float* global_scale, iq_stats* stats, void* xhat,
                              int32_t xhat_dtype, void* workspace, hipStream_t stream);
+
+/*
+ * Asymmetric INT4, the format of the Triton post's Puzzle 12 ("Quantized
+ * Matrix Mult"): unsigned 4-bit codes w, and per group of 128 along the row
+ * an FP32 scale sc and a 4-bit shift sh, with x^ = sc * (w - sh).  The page
+ * prints this decoder only; the encoder is the min-max one:
+ *   lo = min(0, min x), hi = max(0, max x) over the group's finite elements;
+ *   sc = (hi - lo) / 15 in FP32 (the largest float if that overflows);
+ *   sh = round-half-even(-lo / sc), clamped to [0, 15];
+ *   w  = clamp(round-half-even(x / sc) + sh, 0, 15).
+ * sc == 0 gives w = sh = 0; NaN gives w = sh (x^ = 0), +-Inf the ends 15 / 0.
+ * n_saturated counts x / sc above 15 - sh or below -sh.
+ *   d->fmt must be IQ_INT4_ZP with IQ_PER_BLOCK and cols a multiple of 256
+ *   (IQ_EINVAL otherwise); d->flags must be 0.
+ *   codes   uint8 [rows, cols/2]: element 2t in bits 3:0 of byte t, i.e.
+ *           eight per little-endian 32-bit word, element i in bits
+ *           [4i, 4i+4) (the page's extract() order)
+ *   scales  float32 [rows, cols/128], 4-byte aligned
+ *   shifts  uint8 [rows, cols/256], group 2t in bits 3:0 of byte t (whole
+ *           32-bit words of eight shifts per row when cols % 1024 == 0)
+ * The other arguments, layouts, workspace rules and errors are those of
+ * iq_quantize.  iq_quantize and iq_dequantize reject IQ_INT4_ZP.
+ */
+iq_status iq_quantize_zp(const iq_desc* d, const void* x, void* codes, float* scales, uint8_t* shifts,
+                         iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace,
+                         hipStream_t stream);
+/* x^ = sc * (w - sh) from codes, scales and shifts laid out as above;
+ * otherwise as iq_dequantize. */
+iq_status iq_dequantize_zp(const iq_desc* d, const void* codes, const float* scales,
+                           const uint8_t* shifts, void* xhat, int32_t xhat_dtype, hipStream_t stream);
+/* Bytes of the shifts array for an IQ_INT4_ZP descriptor (0 otherwise). */
+size_t iq_shifts_bytes(const iq_desc* d);
 
 const char* iq_status_str(iq_status s);
 int iq_abi_version(void);

@@ -16,13 +16,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libiq.so")
 
 # iq_format / iq_gran / iq_dtype / iq_status values of include/iq.h
-FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5}
+FORMATS = {"int8": 0, "e4m3": 1, "e5m2": 2, "mxfp4": 3, "nvfp4": 4, "int4": 5, "int4zp": 6}
 GRANS = {"tensor": 0, "row": 1, "block": 2}
 IQ_F32, IQ_BF16 = 0, 1
 IQ_OK, IQ_EINVAL, IQ_EALIGN, IQ_EUNSUPPORTED, IQ_EHIP = 0, 1, 2, 3, 4
 # iq_desc.flags: scale-rule variants (MXFP4 exponent rounding, NVFP4 block-scale rounding)
 IQ_FLAG_MX_ROUND_NEAREST, IQ_FLAG_MX_ROUND_UP, IQ_FLAG_NV_SCALE_RNE = 0x1, 0x2, 0x4
-FOUR_BIT = ("mxfp4", "nvfp4", "int4")
+FOUR_BIT = ("mxfp4", "nvfp4", "int4", "int4zp")
 
 
 class IQDesc(ctypes.Structure):
@@ -62,6 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.iq_quantize.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
     L.iq_quantize_static.restype = ctypes.c_int
     L.iq_quantize_static.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.iq_quantize_zp.restype = ctypes.c_int
+    L.iq_quantize_zp.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.iq_dequantize_zp.restype = ctypes.c_int
+    L.iq_dequantize_zp.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
+    L.iq_shifts_bytes.restype, L.iq_shifts_bytes.argtypes = S, [D]
     L.iq_dequantize.restype = ctypes.c_int
     L.iq_dequantize.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
     L.iq_amax.restype = ctypes.c_int
@@ -117,6 +122,21 @@ def iq_quantize_static(d: IQDesc, x: int, amax_in: int, codes: int, scales: int,
     """Raw call with integer device addresses (amax_in: device float32 [1])."""
     return load_library().iq_quantize_static(ctypes.byref(d), x, amax_in, codes, scales, global_scale, stats,
                                              xhat, xhat_dtype, workspace, stream)
+
+
+def iq_quantize_zp(d: IQDesc, x: int, codes: int, scales: int, shifts: int, stats: int | None,
+                   xhat: int | None, xhat_dtype: int, workspace: int, stream: int | None) -> int:
+    return load_library().iq_quantize_zp(ctypes.byref(d), x, codes, scales, shifts, stats, xhat, xhat_dtype,
+                                         workspace, stream)
+
+
+def iq_dequantize_zp(d: IQDesc, codes: int, scales: int, shifts: int, xhat: int, xhat_dtype: int,
+                     stream: int | None) -> int:
+    return load_library().iq_dequantize_zp(ctypes.byref(d), codes, scales, shifts, xhat, xhat_dtype, stream)
+
+
+def iq_shifts_bytes(d: IQDesc) -> int:
+    return load_library().iq_shifts_bytes(ctypes.byref(d))
 
 
 def iq_dequantize(d: IQDesc, codes: int, scales: int, global_scale: int | None, xhat: int,
@@ -178,6 +198,8 @@ def empty_outputs(d: IQDesc, device, fmt: str, gran: str):
         scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
     elif fmt == "nvfp4":
         scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=device)
+    elif fmt == "int4zp":
+        scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=device)
     else:
         scales = torch.empty((rows, cols // 128), dtype=torch.int16, device=device)
     gscale = torch.empty((1,), dtype=torch.float32, device=device) if fmt == "nvfp4" else None
@@ -201,6 +223,7 @@ class Quantized:
     gran: str
     rows: int
     cols: int
+    shifts: object = None   # asymmetric INT4: uint8 [rows, cols / 256]
 
     def stats(self) -> dict:
         """Copy the statistics to the host (synchronizes with the device)."""
@@ -224,12 +247,20 @@ def quantize(x, fmt: str, gran: str, *, stats: bool = True, xhat_dtype=None, col
         xh = None
         if xhat_dtype is not None:
             xh = torch.empty((d.rows, d.cols), dtype=xhat_dtype, device=x.device)
-        out = Quantized(codes, scales, gscale, xh, sbuf, fmt, gran, d.rows, d.cols)
+        shifts = (torch.empty((d.rows, d.cols // 256), dtype=torch.uint8, device=x.device)
+                  if fmt == "int4zp" else None)
+        out = Quantized(codes, scales, gscale, xh, sbuf, fmt, gran, d.rows, d.cols, shifts)
     ws = workspace if workspace is not None else workspace_for(d, x.device)
     xdt = IQ_F32
     if out.xhat is not None:
         xdt = IQ_F32 if out.xhat.dtype == torch.float32 else IQ_BF16
-    if static_amax is None:
+    if fmt == "int4zp":
+        if static_amax is not None:
+            raise ValueError("static_amax needs a per-tensor format or NVFP4")
+        st = iq_quantize_zp(d, x.data_ptr(), _ptr(out.codes), _ptr(out.scales), _ptr(out.shifts),
+                            _ptr(out.stats_buf), _ptr(out.xhat), xdt, ws.data_ptr(), _stream(stream))
+        _check(st, "iq_quantize_zp")
+    elif static_amax is None:
         st = iq_quantize(d, x.data_ptr(), _ptr(out.codes), _ptr(out.scales), _ptr(out.global_scale),
                          _ptr(out.stats_buf), _ptr(out.xhat), xdt, ws.data_ptr(), _stream(stream))
         _check(st, "iq_quantize")
@@ -250,6 +281,11 @@ def dequantize(q: Quantized, out_dtype=None, out=None, stream=None):
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
     dt = IQ_F32 if out.dtype == torch.float32 else IQ_BF16
+    if q.fmt == "int4zp":
+        st = iq_dequantize_zp(d, q.codes.data_ptr(), q.scales.data_ptr(), _ptr(q.shifts), out.data_ptr(), dt,
+                              _stream(stream))
+        _check(st, "iq_dequantize_zp")
+        return out
     st = iq_dequantize(d, q.codes.data_ptr(), q.scales.data_ptr(), _ptr(q.global_scale), out.data_ptr(), dt,
                        _stream(stream))
     _check(st, "iq_dequantize")

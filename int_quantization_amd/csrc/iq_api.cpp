@@ -12,7 +12,7 @@ namespace {
 bool is_bf16_or_f32(int32_t t) { return t == IQ_F32 || t == IQ_BF16; }
 size_t elem_size(int32_t t) { return t == IQ_F32 ? 4 : 2; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-bool four_bit(int32_t f) { return f == IQ_MXFP4 || f == IQ_NVFP4 || f == IQ_INT4; }
+bool four_bit(int32_t f) { return f == IQ_MXFP4 || f == IQ_NVFP4 || f == IQ_INT4 || f == IQ_INT4_ZP; }
 
 // Elements per scale along a row (0 = whole row or tensor); -1 if the
 // format / granularity pair is illegal.
@@ -22,7 +22,7 @@ int64_t block_of(int32_t fmt, int32_t gran) {
         return (gran == IQ_PER_TENSOR || gran == IQ_PER_ROW) ? 0 : -1;
     case IQ_MXFP4: return gran == IQ_PER_BLOCK ? 32 : -1;
     case IQ_NVFP4: return gran == IQ_PER_BLOCK ? 16 : -1;
-    case IQ_INT4: return gran == IQ_PER_BLOCK ? 128 : -1;
+    case IQ_INT4: case IQ_INT4_ZP: return gran == IQ_PER_BLOCK ? 128 : -1;
     default: return -1;
     }
 }
@@ -55,6 +55,7 @@ iq_status check_shape(const iq_desc* d, bool need_in_dtype) {
     if (d->rows < 0 || d->cols < 0) return IQ_EINVAL;
     if (d->cols % iqk::kChunk) return IQ_EINVAL;
     if (b > 0 && d->cols % b) return IQ_EINVAL;
+    if (d->fmt == IQ_INT4_ZP && d->cols % 256) return IQ_EINVAL;   // whole shift bytes per row
     if (d->rows > 0 && d->cols > 0 && d->rows * (d->cols / iqk::kChunk) >= (int64_t)1 << 31)
         return IQ_EUNSUPPORTED;
     if (d->rows > ((int64_t)1 << 31) - 1) return IQ_EUNSUPPORTED;
@@ -82,6 +83,7 @@ size_t scales_bytes(const iq_desc* d) {
         return d->gran == IQ_PER_TENSOR ? 4 : (size_t)d->rows * 4;
     case IQ_MXFP4: return (size_t)(d->rows * (d->cols / 32));
     case IQ_NVFP4: return (size_t)(d->rows * (d->cols / 16));
+    case IQ_INT4_ZP: return (size_t)(d->rows * (d->cols / 128)) * 4;
     default: return (size_t)(d->rows * (d->cols / 128)) * 2;
     }
 }
@@ -120,13 +122,18 @@ size_t iq_workspace_bytes(const iq_desc* d) {
     return iqk::Workspace::kBytes;
 }
 
+size_t iq_shifts_bytes(const iq_desc* d) {
+    if (check_shape(d, false) != IQ_OK || d->fmt != IQ_INT4_ZP) return 0;
+    return (size_t)(d->rows * (d->cols / 256));
+}
+
 }  // extern "C"
 
 namespace {
 
 iq_status quantize_impl(const iq_desc* d, const void* x, const float* static_amax, void* codes, void* scales,
-                        float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace,
-                        hipStream_t stream) {
+                        float* global_scale, uint8_t* shifts, iq_stats* stats, void* xhat, int32_t xhat_dtype,
+                        void* workspace, hipStream_t stream) {
     iq_status st = check_shape(d, true);
     if (st != IQ_OK) return st;
     if ((st = check_input(d, x)) != IQ_OK) return st;
@@ -136,6 +143,7 @@ iq_status quantize_impl(const iq_desc* d, const void* x, const float* static_ama
     if (!empty && !codes) return IQ_EINVAL;
     if (needs_scale_slot && !scales) return IQ_EINVAL;
     if (d->fmt == IQ_NVFP4 && !global_scale) return IQ_EINVAL;
+    if (d->fmt == IQ_INT4_ZP && !empty && !shifts) return IQ_EINVAL;
     if (xhat && !is_bf16_or_f32(xhat_dtype)) return IQ_EINVAL;
     if (!aligned(workspace, 256)) return IQ_EALIGN;
     if (codes && !aligned(codes, 16)) return IQ_EALIGN;
@@ -147,12 +155,30 @@ iq_status quantize_impl(const iq_desc* d, const void* x, const float* static_ama
     iqk::QuantArgs a;
     a.fmt = d->fmt; a.gran = d->gran; a.in_dtype = d->in_dtype;
     a.rows = d->rows; a.cols = d->cols; a.ld = d->ld_in;
-    a.x = x; a.codes = codes; a.scales = scales; a.global_scale = global_scale;
+    a.x = x; a.codes = codes; a.scales = scales; a.global_scale = global_scale; a.shifts = shifts;
     a.stats = stats; a.xhat = xhat; a.xhat_dtype = xhat_dtype; a.workspace = workspace;
     a.rule = d->flags;
     a.static_amax = static_amax;
     if (empty) { a.rows = 0; a.cols = 0; }
     return from_hip(iqk::launch_quantize(a, stream));
+}
+
+iq_status dequantize_impl(const iq_desc* d, const void* codes, const void* scales, const float* global_scale,
+                          const uint8_t* shifts, void* xhat, int32_t xhat_dtype, hipStream_t stream) {
+    iq_status st = check_shape(d, false);
+    if (st != IQ_OK) return st;
+    if (!is_bf16_or_f32(xhat_dtype)) return IQ_EINVAL;
+    if (d->rows == 0 || d->cols == 0) return IQ_OK;
+    if (!codes || !scales || !xhat) return IQ_EINVAL;
+    if (d->fmt == IQ_NVFP4 && !global_scale) return IQ_EINVAL;
+    if (d->fmt == IQ_INT4_ZP && !shifts) return IQ_EINVAL;
+    if (!aligned(codes, 16) || !aligned(xhat, 16) || !aligned(scales, 4)) return IQ_EALIGN;
+    if (global_scale && !aligned(global_scale, 4)) return IQ_EALIGN;
+    iqk::DequantArgs a;
+    a.fmt = d->fmt; a.gran = d->gran; a.rows = d->rows; a.cols = d->cols;
+    a.codes = codes; a.scales = scales; a.global_scale = global_scale; a.shifts = shifts;
+    a.xhat = xhat; a.xhat_dtype = xhat_dtype;
+    return from_hip(iqk::launch_dequantize(a, stream));
 }
 
 }  // namespace
@@ -161,7 +187,15 @@ extern "C" {
 
 iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales, float* global_scale,
                       iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace, hipStream_t stream) {
-    return quantize_impl(d, x, nullptr, codes, scales, global_scale, stats, xhat, xhat_dtype, workspace, stream);
+    if (d && d->fmt == IQ_INT4_ZP) return IQ_EINVAL;   // shifts have no slot here: iq_quantize_zp
+    return quantize_impl(d, x, nullptr, codes, scales, global_scale, nullptr, stats, xhat, xhat_dtype, workspace,
+                         stream);
+}
+
+iq_status iq_quantize_zp(const iq_desc* d, const void* x, void* codes, float* scales, uint8_t* shifts,
+                         iq_stats* stats, void* xhat, int32_t xhat_dtype, void* workspace, hipStream_t stream) {
+    if (!d || d->fmt != IQ_INT4_ZP) return IQ_EINVAL;
+    return quantize_impl(d, x, nullptr, codes, scales, nullptr, shifts, stats, xhat, xhat_dtype, workspace, stream);
 }
 
 iq_status iq_quantize_static(const iq_desc* d, const void* x, const float* amax_in, void* codes, void* scales,
@@ -173,24 +207,20 @@ iq_status iq_quantize_static(const iq_desc* d, const void* x, const float* amax_
     iq_status st = check_shape(d, true);
     if (st != IQ_OK) return st;
     if (!aligned(amax_in, 4)) return IQ_EALIGN;
-    return quantize_impl(d, x, amax_in, codes, scales, global_scale, stats, xhat, xhat_dtype, workspace, stream);
+    return quantize_impl(d, x, amax_in, codes, scales, global_scale, nullptr, stats, xhat, xhat_dtype, workspace,
+                         stream);
 }
 
 iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales, const float* global_scale,
                         void* xhat, int32_t xhat_dtype, hipStream_t stream) {
-    iq_status st = check_shape(d, false);
-    if (st != IQ_OK) return st;
-    if (!is_bf16_or_f32(xhat_dtype)) return IQ_EINVAL;
-    if (d->rows == 0 || d->cols == 0) return IQ_OK;
-    if (!codes || !scales || !xhat) return IQ_EINVAL;
-    if (d->fmt == IQ_NVFP4 && !global_scale) return IQ_EINVAL;
-    if (!aligned(codes, 16) || !aligned(xhat, 16) || !aligned(scales, 4)) return IQ_EALIGN;
-    if (global_scale && !aligned(global_scale, 4)) return IQ_EALIGN;
-    iqk::DequantArgs a;
-    a.fmt = d->fmt; a.gran = d->gran; a.rows = d->rows; a.cols = d->cols;
-    a.codes = codes; a.scales = scales; a.global_scale = global_scale;
-    a.xhat = xhat; a.xhat_dtype = xhat_dtype;
-    return from_hip(iqk::launch_dequantize(a, stream));
+    if (d && d->fmt == IQ_INT4_ZP) return IQ_EINVAL;   // iq_dequantize_zp
+    return dequantize_impl(d, codes, scales, global_scale, nullptr, xhat, xhat_dtype, stream);
+}
+
+iq_status iq_dequantize_zp(const iq_desc* d, const void* codes, const float* scales, const uint8_t* shifts,
+                           void* xhat, int32_t xhat_dtype, hipStream_t stream) {
+    if (!d || d->fmt != IQ_INT4_ZP) return IQ_EINVAL;
+    return dequantize_impl(d, codes, scales, nullptr, shifts, xhat, xhat_dtype, stream);
 }
 
 iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace, hipStream_t stream) {

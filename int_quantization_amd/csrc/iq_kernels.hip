@@ -113,6 +113,30 @@ template <> struct Chunk<D_BF16> {
         for (int k = 0; k < 4; ++k) n += __builtin_popcount(((w[k] & 0x7FFF7FFFu) + 0x7FFF7FFFu) & 0x80008000u);
         return n;
     }
+    // Signed range on the bit images, per half: p collects the signed
+    // maximum (the largest positive x when one is present, since positive
+    // BF16 bits order like their values and negatives are negative int16),
+    // n the unsigned maximum (the most negative x when one is present: the
+    // sign bit makes it the largest, larger magnitudes larger still), mn the
+    // minimum of |x| (0 iff an exact zero is present).
+    static constexpr uint32_t kMagInit = 0x7FFF7FFFu;
+    __device__ __forceinline__ void range(uint32_t& p, uint32_t& n, uint32_t& mn) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s2v, p), __builtin_bit_cast(s2v, w[k])));
+            n = hmax(n, w[k]);
+            mn = hmin(mn, w[k] & 0x7FFF7FFFu);
+        }
+    }
+    // FP32 bits of max(0, max x) and of -min(0, min x) from range(); a value
+    // of kNonFinite or more means an Inf or NaN on that side.
+    __device__ __forceinline__ static void range_bits(uint32_t p, uint32_t n, uint32_t& pos, uint32_t& neg) {
+        const int a = (int)(int16_t)(p & 0xFFFFu), b = (int)(int16_t)(p >> 16);
+        const int m = a > b ? a : b;
+        pos = m > 0 ? (uint32_t)m << 16 : 0u;
+        const uint32_t u = umax16(n);
+        neg = (u & 0x8000u) ? (u & 0x7FFFu) << 16 : 0u;
+    }
     // Maximum over the finite elements only: t = a + 0x80 is negative as
     // int16 exactly for Inf and NaN, so a signed 16-bit max skips them.
     __device__ __forceinline__ uint32_t absmax_finite() const {
@@ -176,6 +200,20 @@ template <> struct Chunk<D_F32> {
             m = (a < 0x7F800000u && a > m) ? a : m;
         }
         return m;
+    }
+    // As for BF16, on whole words.
+    static constexpr uint32_t kMagInit = 0x7FFFFFFFu;
+    __device__ __forceinline__ void range(uint32_t& p, uint32_t& n, uint32_t& mn) const {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            p = (int)w[k] > (int)p ? w[k] : p;
+            n = w[k] > n ? w[k] : n;
+            mn = hmin(mn, w[k] & 0x7FFFFFFFu);
+        }
+    }
+    __device__ __forceinline__ static void range_bits(uint32_t p, uint32_t n, uint32_t& pos, uint32_t& neg) {
+        pos = (int)p > 0 ? p : 0u;
+        neg = (n & 0x80000000u) ? (n & 0x7FFFFFFFu) : 0u;
     }
 };
 
@@ -390,6 +428,13 @@ struct Stats {
     // General case, wave-uniform call: non-finite inputs count but stay out
     // of sums and maxima; vs is the value tested for |vs| > thr.
     __device__ __forceinline__ void add8_slow(const float (&x)[8], const float (&vs)[8], const float (&h)[8], float thr) {
+        bool sat[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sat[i] = __builtin_fabsf(vs[i]) > thr;
+        add8_slow_flags(x, sat, h);
+    }
+    // The same with the saturation of each element decided by the caller.
+    __device__ __forceinline__ void add8_slow_flags(const float (&x)[8], const bool (&sat)[8], const float (&h)[8]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const bool fin = __builtin_isfinite(x[i]);
@@ -399,7 +444,7 @@ struct Stats {
             se2 = __builtin_fma(d, d, se2);
             sae += __builtin_fabs(d);
             mae = __builtin_fmaxf(mae, fin ? __builtin_fabsf(x[i] - h[i]) : 0.f);
-            nsat += __popcll(__ballot(__builtin_fabsf(vs[i]) > thr));
+            nsat += __popcll(__ballot(sat[i]));
             nzf += __popcll(__ballot(fin && x[i] != 0.f && h[i] == 0.f));
             nnf += __popcll(__ballot(!fin));
         }
@@ -466,6 +511,7 @@ template <> struct Fmt<F_E5M2> { static constexpr float qmax = 57344.f; static c
 template <> struct Fmt<F_MXFP4> { static constexpr float qmax = 6.f; };
 template <> struct Fmt<F_NVFP4> { static constexpr float qmax = 6.f; };
 template <> struct Fmt<F_INT4> { static constexpr float qmax = 7.f; };
+template <> struct Fmt<F_INT4ZP> { static constexpr float qmax = 15.f; };   // codes 0..15
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |v| < 2^22 to an integer (RNE)
 constexpr float kTinyScale = 0x1p-64f;  // smaller scales take the slow path
@@ -499,6 +545,10 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
 // its low 3 bits are; INT4 never produces -8).
 __device__ __forceinline__ uint32_t nonzero_nibbles(uint32_t w) {
     return __builtin_popcount(((w & 0x77777777u) + 0x77777777u) & 0x88888888u);
+}
+// Nibbles of w with any of their 4 bits set.
+__device__ __forceinline__ uint32_t nonzero_nibbles_full(uint32_t w) {
+    return __builtin_popcount((((w & 0x77777777u) + 0x77777777u) | w) & 0x88888888u);
 }
 
 // FP8 pack / unpack (4 codes per 32-bit word, element 0 in the low byte).
@@ -888,6 +938,7 @@ struct FlatArgs {
     const TensorInfo* info;  // per-tensor INT8/FP8 and NVFP4: absmax pre-pass result
     Partial* partials;
     uint32_t rule;           // R_* scale-rule bits (MXFP4 exponent, NVFP4 block-scale rounding)
+    uint8_t* shifts;         // asymmetric INT4: packed 4-bit shifts
 };
 
 // The functions below run on every lane of the wave (lanes past the end of
@@ -1251,6 +1302,131 @@ __device__ __forceinline__ void quant_lane_int4(const Chunk<IN> (&ch)[kTileChunk
     store_words4(a.codes, g0, nvalid, wq);
 }
 
+// Signed range over the finite elements of the lane's chunks (the rare path
+// of groups holding Inf or NaN): FP32 bits of max(0, max x) and -min(0, min x).
+template <int IN>
+__device__ __forceinline__ void lane_range_finite(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t& pos,
+                                                  uint32_t& neg) {
+    float hi = 0.f, nlo = 0.f;
+#pragma unroll
+    for (int c = 0; c < kTileChunksPerThread; ++c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = ch[c].get(i);
+            if (__builtin_isfinite(x)) {
+                hi = __builtin_fmaxf(hi, x);
+                nlo = __builtin_fmaxf(nlo, -x);
+            }
+        }
+    }
+    pos = as_u(hi) & 0x7FFFFFFFu;   // both are >= 0; drop the sign a max of +-0 may leave
+    neg = as_u(nlo) & 0x7FFFFFFFu;
+}
+
+// Asymmetric INT4 (the Triton post, Puzzle 12: x^ = sc * (w - sh) with
+// unsigned 4-bit w and sh; the min-max encoder).  Groups of 128 = 16 chunks
+// = 4 lanes.  Over the group's finite elements lo = min(0, min x) and
+// hi = max(0, max x); sc = (hi - lo) / 15 (the largest float if that
+// overflows); sh = RNE(-lo / sc) clamped to [0, 15];
+// w = clamp(RNE(x / sc) + sh, 0, 15).  x / sc takes the correction step with
+// y = RN(1 / sc): it equals the division except for quotients below 2^-20,
+// which give the same code (checked on the CPU over random FP32 ranges and
+// every BF16 input of random BF16 ranges).  A code equal to sh is exactly a
+// zero x^, so flushed elements are counted from w ^ sh.  Saturated elements
+// (x / sc above 15 - sh or below -sh) sit at the ends of a group's range;
+// only waves where some group's hi or lo crosses are compared per element.
+template <int IN, bool STATS>
+__device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0,
+                                                  uint32_t nvalid, const FlatArgs& a, Stats& st) {
+    uint32_t p = 0, n = 0, mn = Chunk<IN>::kMagInit;
+#pragma unroll
+    for (int c = 0; c < kTileChunksPerThread; ++c) ch[c].range(p, n, mn);
+    uint32_t pos, neg;
+    Chunk<IN>::range_bits(p, n, pos, neg);
+    const bool zero = Chunk<IN>::has_zero(mn);
+    pos = group_max<4>(pos);
+    neg = group_max<4>(neg);
+    const bool nonfinite = pos >= kNonFinite || neg >= kNonFinite;
+    if (__ballot(nonfinite) != 0) {
+        uint32_t fp, fn;
+        lane_range_finite<IN>(ch, fp, fn);
+        fp = group_max<4>(fp);
+        fn = group_max<4>(fn);
+        if (nonfinite) { pos = fp; neg = fn; }
+    }
+    const float hi = as_f(pos), nlo = as_f(neg);          // lo = -nlo
+    float sc = (hi + nlo) / 15.0f;                        // (hi - lo) / 15
+    sc = sc > 0x1.fffffep127f ? 0x1.fffffep127f : sc;
+    int sh = 0;
+    if (sc != 0.f) sh = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(nlo / sc), 0.f), 15.f);
+    const int sh_next = __shfl_down(sh, 4);               // the next group's shift (4 lanes on)
+    if (nvalid != 0) {
+        if ((g0 & 15u) == 0) static_cast<float*>(a.scales)[g0 >> 4] = sc;
+        if ((g0 & 31u) == 0) a.shifts[g0 >> 5] = (uint8_t)(sh | (sh_next << 4));
+    }
+    const bool fast = !nonfinite && sc >= kTinyScale && stat_range(__builtin_fmaxf(hi, nlo));
+    const bool all_fast = __ballot(!fast) == 0;
+    const float thi = (float)(15 - sh), tlo = (float)(-sh);
+    const uint32_t shrep = (uint32_t)sh * 0x11111111u;
+    const float y = all_fast ? 1.0f / sc : 0.f;
+    const bool sat = all_fast && __ballot(markstein(hi, sc, y) > thi || markstein(-nlo, sc, y) < tlo) != 0;
+    // Fast path codes in the magic-number domain: (v + kMagic) is kMagic +
+    // RNE(v) (ties to an even q, as the rounding happens before the shift),
+    // adding sh is exact, and clamping to kMagic + [0, 15] leaves kMagic + w,
+    // whose low nibble is w; x^ = sc * (t - (kMagic + sh)) with an exact
+    // difference.
+    const float shf = (float)sh, magic_sh = kMagic + shf, wtop = kMagic + 15.f;
+    uint32_t wq[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const bool valid = (uint32_t)c < nvalid;
+        float x[8], h[8];
+        uint32_t w = 0;
+        if (all_fast) {
+            float v[8], t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = ch[c].get(i);
+                v[i] = markstein(x[i], sc, y);
+                t[i] = __builtin_amdgcn_fmed3f((v[i] + kMagic) + shf, kMagic, wtop);   // finite here
+                h[i] = sc * (t[i] - magic_sh);
+            }
+            w = int4_pack8(t);
+            if (STATS) {
+                st.add8_fast<IN, false, false>(ch[c], false, x, v, h, 0.f);
+                if (sat) {
+                    float th = thi;
+                    asm volatile("" : "+v"(th));   // keep the compares inside this branch
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) st.nsat += __popcll(__ballot(v[i] > th || v[i] < tlo));
+                }
+                const uint32_t nzx = __ballot(zero) != 0 ? ch[c].nonzero_count() : (valid ? 8u : 0u);
+                st.count_flush(nzx, nonzero_nibbles_full(w ^ shrep));   // w != sh: a nonzero x^
+            }
+        } else {
+            bool sv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = ch[c].get(i);
+                float v = 0.f;
+                int wi = sh;
+                if (sc != 0.f) {
+                    v = x[i] / sc;
+                    if (!__builtin_isnan(v))
+                        wi = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(v) + (float)sh, 0.f), 15.f);
+                }
+                sv[i] = v > thi || v < tlo;
+                h[i] = sc * (float)(wi - sh);
+                w |= (uint32_t)wi << (4 * i);
+            }
+            if (STATS) st.add8_slow_flags(x, sv, h);
+        }
+        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+        wq[c] = w;
+    }
+    store_words4(a.codes, g0, nvalid, wq);
+}
+
 // ---------------------------------------------------------------------------
 // Flat tiles.  A workgroup iteration covers kTileChunks = 1024 consecutive
 // chunks; lane l of wave w owns the 4 consecutive chunks 256 w + 4 l + k of
@@ -1297,6 +1473,8 @@ __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread *
         quant_lane_nv<IN, STATS>(ch, g0, nvalid, k.nk, a, st);
     } else if (FMT == F_INT4) {
         quant_lane_int4<IN, STATS>(ch, g0, nvalid, k.rtab, a, st);
+    } else if (FMT == F_INT4ZP) {
+        quant_lane_int4zp<IN, STATS>(ch, g0, nvalid, a, st);
     } else {
         bool fast = k.fast, zeros = k.zeros;
         if (CHECK) {
@@ -1562,6 +1740,7 @@ struct DeqArgs {
     const uint8_t* codes;
     const void* scales;
     const float* global_scale;
+    const uint8_t* shifts;
     void* xhat;
     int xhat_dtype;
     int per_tensor;
@@ -1615,6 +1794,11 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
                     f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
                     h[0] = s_nv * p0.x; h[1] = s_nv * p0.y; h[2] = s_nv * p1.x; h[3] = s_nv * p1.y;
                     h[4] = s_nv * p2.x; h[5] = s_nv * p2.y; h[6] = s_nv * p3.x; h[7] = s_nv * p3.y;
+                } else if (FMT == F_INT4ZP) {
+                    const float sc = static_cast<const float*>(a.scales)[g >> 4];
+                    const int sh = (int)((a.shifts[g >> 5] >> (4u * ((g >> 4) & 1u))) & 0xFu);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) h[i] = sc * (float)((int)((w >> (4 * i)) & 0xFu) - sh);
                 } else {
                     const uint16_t s16 = static_cast<const uint16_t*>(a.scales)[g >> 4];
                     const float sf = (float)__builtin_bit_cast(_Float16, s16);
@@ -1748,6 +1932,7 @@ hipError_t launch_flat_fmt(int fmt, const FlatArgs& f, bool stats, bool check, i
     case F_E5M2: return launch_flat<IN, F_E5M2>(f, stats, check, grid, s);
     case F_MXFP4: return launch_flat<IN, F_MXFP4>(f, stats, check, grid, s);
     case F_NVFP4: return launch_flat<IN, F_NVFP4>(f, stats, check, grid, s);
+    case F_INT4ZP: return launch_flat<IN, F_INT4ZP>(f, stats, check, grid, s);
     default: return launch_flat<IN, F_INT4>(f, stats, check, grid, s);
     }
 }
@@ -1807,6 +1992,7 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         f.codes = static_cast<uint8_t*>(q.codes); f.scales = q.scales; f.global_scale = q.global_scale;
         f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.info = info; f.partials = partials;
         f.rule = q.rule;
+        f.shifts = q.shifts;
         if (q.gran == G_TENSOR || q.fmt == F_NVFP4) {
             float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
             float* scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);
@@ -1840,6 +2026,7 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
     a.codes = static_cast<const uint8_t*>(d.codes);
     a.scales = d.scales;
     a.global_scale = d.global_scale;
+    a.shifts = d.shifts;
     a.xhat = d.xhat;
     a.xhat_dtype = d.xhat_dtype;
     a.per_tensor = d.gran == G_TENSOR;
@@ -1851,6 +2038,7 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
     case F_E5M2: k_dequant<F_E5M2><<<grid_for(k_dequant<F_E5M2>, t), kThreads, 0, s>>>(a); break;
     case F_MXFP4: k_dequant<F_MXFP4><<<grid_for(k_dequant<F_MXFP4>, t), kThreads, 0, s>>>(a); break;
     case F_NVFP4: k_dequant<F_NVFP4><<<grid_for(k_dequant<F_NVFP4>, t), kThreads, 0, s>>>(a); break;
+    case F_INT4ZP: k_dequant<F_INT4ZP><<<grid_for(k_dequant<F_INT4ZP>, t), kThreads, 0, s>>>(a); break;
     default: k_dequant<F_INT4><<<grid_for(k_dequant<F_INT4>, t), kThreads, 0, s>>>(a); break;
     }
     return hipGetLastError();

@@ -10,7 +10,7 @@
 namespace iqk {
 
 // Formats and granularities use the public enum values of iq.h.
-enum { F_INT8 = 0, F_E4M3 = 1, F_E5M2 = 2, F_MXFP4 = 3, F_NVFP4 = 4, F_INT4 = 5 };
+enum { F_INT8 = 0, F_E4M3 = 1, F_E5M2 = 2, F_MXFP4 = 3, F_NVFP4 = 4, F_INT4 = 5, F_INT4ZP = 6 };
 enum { G_TENSOR = 0, G_ROW = 1, G_BLOCK = 2 };
 enum { D_F32 = 0, D_BF16 = 1 };
 // Scale-rule variants, the public flag values.
@@ -53,6 +53,7 @@ struct QuantArgs {
     void* codes;
     void* scales;
     float* global_scale;
+    uint8_t* shifts;      // asymmetric INT4: packed 4-bit shifts (else null)
     void* stats;          // iq_stats*, may be null
     void* xhat;           // may be null
     int xhat_dtype;
@@ -67,6 +68,7 @@ struct DequantArgs {
     const void* codes;
     const void* scales;
     const float* global_scale;
+    const uint8_t* shifts;   // asymmetric INT4 only
     void* xhat;
     int xhat_dtype;
 };

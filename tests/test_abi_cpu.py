@@ -174,6 +174,36 @@ def test_quantize_static_argument_errors(iq):
     assert qs(iq.make_desc("e4m3", "tensor", 4, 256, flags=1)) == iq.IQ_EUNSUPPORTED
 
 
+def test_int4zp_sizes_and_argument_errors(iq):
+    """Asymmetric INT4 goes through its own entry points: FP32 scales per
+    128, one shift byte per two groups, cols a multiple of 256."""
+    E = iq.IQ_EINVAL
+    d = iq.make_desc("int4zp", "block", 28672, 8192)
+    assert iq.iq_codes_bytes(d) == 28672 * 4096
+    assert iq.iq_scales_bytes(d) == 28672 * 64 * 4
+    assert iq.iq_shifts_bytes(d) == 28672 * 32
+    assert iq.iq_shifts_bytes(iq.make_desc("int4", "block", 4, 256)) == 0
+    assert iq.iq_scales_bytes(iq.make_desc("int4zp", "block", 4, 384)) == 0       # 384 % 256
+    assert iq.iq_scales_bytes(iq.make_desc("int4zp", "row", 4, 256)) == 0         # per block only
+
+    def qz(d, **kw):
+        a = dict(x=FAKE, codes=FAKE, scales=FAKE, shifts=FAKE, stats=None, xhat=None, xdt=0, ws=FAKE)
+        a.update(kw)
+        return iq.iq_quantize_zp(d, a["x"], a["codes"], a["scales"], a["shifts"], a["stats"], a["xhat"],
+                                 a["xdt"], a["ws"], None)
+    ok = iq.make_desc("int4zp", "block", 4, 256)
+    assert quant(iq, ok) == E                                    # no slot for the shifts
+    assert iq.iq_dequantize(ok, FAKE, FAKE, FAKE, FAKE, 0, None) == E
+    assert qz(iq.make_desc("int4", "block", 4, 256)) == E
+    assert qz(iq.make_desc("int4zp", "block", 4, 384)) == E
+    assert qz(ok, shifts=None) == E
+    assert qz(ok, scales=FAKE + 2) == iq.IQ_EALIGN
+    assert qz(ok, codes=FAKE + 4) == iq.IQ_EALIGN
+    assert qz(iq.make_desc("int4zp", "block", 4, 256, flags=4)) == iq.IQ_EUNSUPPORTED
+    assert iq.iq_dequantize_zp(ok, FAKE, FAKE, None, FAKE, 0, None) == E
+    assert iq.iq_dequantize_zp(iq.make_desc("int4", "block", 4, 256), FAKE, FAKE, FAKE, FAKE, 0, None) == E
+
+
 def test_dequantize_and_amax_argument_errors(iq):
     E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
     d = iq.make_desc("nvfp4", "block", 4, 256)

@@ -17,7 +17,14 @@ pytestmark = pytest.mark.gpu
 THREADS = max(1, min(16, os.cpu_count() or 1))
 
 ALL = [("int8", "tensor"), ("e4m3", "tensor"), ("e5m2", "tensor"), ("int8", "row"), ("e4m3", "row"),
-       ("e5m2", "row"), ("mxfp4", "block"), ("nvfp4", "block"), ("int4", "block")]
+       ("e5m2", "row"), ("mxfp4", "block"), ("nvfp4", "block"), ("int4", "block"), ("int4zp", "block")]
+
+
+def fits(O, fmt, gran, cols):
+    """Whether a row length is legal for the format (asymmetric INT4 needs
+    whole shift bytes: cols a multiple of 256)."""
+    bs = O.block_size(fmt, gran)
+    return not (bs and cols % bs) and not (fmt == "int4zp" and cols % 256)
 
 
 @pytest.fixture(scope="module")
@@ -53,6 +60,8 @@ def run_gpu(iq, x_np, fmt, gran, cols=None, xhat="f32", flags=0):
     out = {"codes": q.codes.cpu().numpy(), "scales": q.scales.cpu().numpy(), "stats": q.stats(), "q": q}
     if q.global_scale is not None:
         out["global_scale"] = q.global_scale.cpu().numpy()
+    if q.shifts is not None:
+        out["shifts"] = q.shifts.cpu().numpy()
     if q.xhat is not None:
         out["xhat"] = (q.xhat.cpu().numpy() if q.xhat.dtype == torch.float32
                        else q.xhat.cpu().view(torch.int16).numpy().view(np.uint16))
@@ -67,6 +76,8 @@ def compare(g, r, fmt, what, O=None, S=None, xhat="f32"):
     assert_bits_equal(gs, r["scales"], f"{what} scales")
     if fmt == "nvfp4":
         assert_bits_equal(g["global_scale"], r["global_scale"], f"{what} global scale")
+    if fmt == "int4zp":
+        assert_bits_equal(g["shifts"], r["shifts"], f"{what} shifts")
     if "xhat" in g and r.get("xhat") is not None:
         want = r["xhat"]
         if xhat == "bf16":
@@ -100,9 +111,8 @@ def make_input(S, dtype, rows, cols, ld, seed):
 @pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
 @pytest.mark.parametrize("fmt,gran", ALL)
 def test_parity_shapes(iq, O, S, fmt, gran, dtype):
-    bs = O.block_size(fmt, gran)
     for i, (rows, cols, ld) in enumerate(SHAPES):
-        if bs and cols % bs:
+        if not fits(O, fmt, gran, cols):
             continue
         x = make_input(S, dtype, rows, cols, ld, seed=100 + i)
         g = run_gpu(iq, x, fmt, gran, cols=cols if ld else None)
@@ -218,7 +228,7 @@ def test_parity_ties(iq, O, S, fmt, gran):
 @pytest.mark.parametrize("fmt,gran", ALL)
 def test_empty(iq, O, fmt, gran):
     import torch
-    cols = 128
+    cols = 256
     x = torch.zeros((0, cols), dtype=torch.bfloat16, device="cuda:0")
     q = iq.quantize(x, fmt, gran, xhat_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -259,7 +269,8 @@ def test_dequantize_parity(iq, O, S, fmt, gran):
         if scales.dtype == np.int16:
             scales = scales.view(np.uint16)
         gs = q.global_scale.cpu().numpy() if q.global_scale is not None else None
-        want = O.dequantize(codes, scales, fmt, gran, x.shape[0], x.shape[1], gs, odt)
+        sh = q.shifts.cpu().numpy() if q.shifts is not None else None
+        want = O.dequantize(codes, scales, fmt, gran, x.shape[0], x.shape[1], gs, odt, shifts=sh)
         got = d.cpu().numpy() if dt == torch.float32 else d.cpu().view(torch.int16).numpy().view(np.uint16)
         assert_bits_equal(got, want, f"{fmt}/{gran} dequantize {dt}")
         if dt == torch.float32:
@@ -298,12 +309,12 @@ def test_bf16_division_sweep(iq, O, S, fmt):
 
 
 @pytest.mark.parametrize("fmt,flags", [("int4", 0), ("nvfp4", 0), ("mxfp4", 0), ("nvfp4", 4), ("mxfp4", 1),
-                                       ("mxfp4", 2)], ids=["int4", "nvfp4", "mxfp4", "nvfp4-rne",
-                                                           "mxfp4-nearest", "mxfp4-up"])
+                                       ("mxfp4", 2), ("int4zp", 0)],
+                         ids=["int4", "nvfp4", "mxfp4", "nvfp4-rne", "mxfp4-nearest", "mxfp4-up", "int4zp"])
 def test_bf16_block_sweep(iq, O, S, fmt, flags):
     """Blocks whose maximum walks the BF16 range while the other elements take
     every BF16 magnitude at or below it."""
-    B = {"int4": 128, "nvfp4": 16, "mxfp4": 32}[fmt]
+    B = {"int4": 128, "int4zp": 128, "nvfp4": 16, "mxfp4": 32}[fmt]
     rng = np.random.default_rng(17)
     rows, cols = 256, 8192
     nb = cols // B
@@ -325,7 +336,7 @@ def test_bf16_block_sweep(iq, O, S, fmt, flags):
 FULL = [("c1", "int8", "tensor", 0), ("c1", "e4m3", "tensor", 0), ("c2", "e4m3", "row", 0),
         ("c2", "e5m2", "row", 0), ("c3", "mxfp4", "block", 0), ("c4", "nvfp4", "block", 0),
         ("c5", "int4", "block", 0), ("c3", "mxfp4", "block", 1), ("c3", "mxfp4", "block", 2),
-        ("c4", "nvfp4", "block", 4)]
+        ("c4", "nvfp4", "block", 4), ("c5", "int4zp", "block", 0)]
 
 
 @pytest.mark.parametrize("cfg,fmt,gran,flags", FULL)
@@ -369,7 +380,8 @@ def test_stream_sampled_rows(iq, O, S):
 
 
 # ---- graph capture: replays match eager calls -------------------------------------
-@pytest.mark.parametrize("fmt,gran", [("e4m3", "row"), ("e4m3", "tensor"), ("nvfp4", "block"), ("int4", "block")])
+@pytest.mark.parametrize("fmt,gran", [("e4m3", "row"), ("e4m3", "tensor"), ("nvfp4", "block"), ("int4", "block"),
+                                      ("int4zp", "block")])
 def test_graph_replay_matches_eager(iq, S, fmt, gran):
     """The library enqueues only kernels (no memset nodes), so a captured call
     replays to the same bytes every time, also with eager work in between."""
@@ -686,3 +698,35 @@ def test_static_graph_replay(iq, S, fmt, gran):
         a2.fill_(-1.0)                                       # invalid absmax: taken as 0 if replayed now
         iq.quantize(x, "mxfp4", "block", workspace=ws)
         torch.cuda.synchronize()
+
+
+
+# ---- asymmetric INT4: groups at the edges of the encoder ----------------------------
+@pytest.mark.parametrize("dtype", [0, 1], ids=["f32", "bf16"])
+def test_int4zp_edge_groups(iq, O, S, dtype):
+    """Groups that are all positive, all negative, constant, all zero, a
+    single nonzero, spanning the whole float range (the scale clamps), with
+    code ties (sc a power of two, x on half steps) and a shift tie
+    (-lo / sc = 7.5), beside weight-like groups."""
+    rng = np.random.default_rng(29)
+    rows, cols = 32, 2048
+    x = S.bf16_to_f32(S.make("c5", nrows=rows))[:, :cols].astype(np.float32).copy()
+    x[0, 0:128] = np.abs(x[0, 0:128])
+    x[0, 128:256] = -np.abs(x[0, 128:256])
+    x[0, 256:384] = np.float32(0.75)
+    x[0, 384:512] = 0.0
+    x[0, 512:640] = 0.0
+    x[0, 600] = np.float32(-3.5)
+    x[1, 0:128] = np.float32(3e38) * np.where(rng.random(128) < 0.5, -1, 1).astype(np.float32)
+    x[1, 0], x[1, 1] = np.float32(3.3e38), np.float32(-3.3e38)
+    half = (np.arange(128) % 15).astype(np.float32) + np.float32(0.5)
+    x[2, 0:128] = half * np.float32(2.0 ** -5)              # lo = 0, hi = 14.5 * 2^-5
+    x[2, 127] = np.float32(15 * 2.0 ** -5)                  # hi = 15 * 2^-5: sc = 2^-5, ties at k + 0.5
+    x[3, 0:128] = np.linspace(-7.5, 7.5, 128, dtype=np.float32)   # sc = 1, -lo / sc = 7.5
+    x[3, 128:256] = np.round(np.linspace(-7.5, 7.5, 128) * 2) / 2
+    x[4, 0:256] = rng.standard_normal(256).astype(np.float32) * np.float32(2.0 ** -130)   # subnormal range
+    if dtype:
+        x = S.f32_to_bf16_bits(x)
+    g = run_gpu(iq, x, "int4zp", "block")
+    r = oracle_ref(O, x, "int4zp", "block")
+    compare(g, r, "int4zp", f"int4zp edge groups ({'bf16' if dtype else 'f32'})", O)
