@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--stream", action="store_true", help="add the 2 GiB streaming pass to the breakdown")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, copy)")
+                    help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, "
+                         "c4:nvfp4:block:static, copy)")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per breakdown entry")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of graphs")
     return ap.parse_args()
@@ -87,8 +88,14 @@ def timed(fn, reps, stream):
             "p90_us": 1e3 * ms[(9 * len(ms)) // 10], "mean_us": 1e3 * sum(ms) / len(ms)}
 
 
+# Call variants of the breakdown: rule flags, or static scaling with an
+# absmax computed once beforehand (the calibrated mode).
+VARIANTS = {"": {}, "mx-nearest": {"flags": 1}, "mx-up": {"flags": 2}, "nv-rne": {"flags": 4}, "static": None}
+
+
 class Workload:
-    """NSETS device copies of one synthetic input plus outputs per format."""
+    """NSETS device copies of one synthetic input plus outputs per format
+    (entries (fmt, gran) or (fmt, gran, variant))."""
 
     def __init__(self, name, formats, x_np=None):
         import torch
@@ -104,19 +111,26 @@ class Workload:
         self.formats = formats
         import int_quantization_amd as iq
         self.iq = iq
-        self.ws = [iq.workspace_for(iq.desc_for(x0, *formats[0]), x0.device) for _ in range(NSETS)]
+        self.ws = [iq.workspace_for(iq.desc_for(x0, *formats[0][:2]), x0.device) for _ in range(NSETS)]
+        self.amax = [iq.amax(x) for x in self.xs] if any(len(f) > 2 and f[2] == "static" for f in formats) else None
         self.q = {}
-        for fmt, gran in formats:
-            self.q[(fmt, gran)] = [iq.quantize(x, fmt, gran, stats=True, workspace=w) for x, w in zip(self.xs, self.ws)]
+        for spec in formats:
+            fmt, gran, var = (*spec, "")[:3]
+            self.q[(fmt, gran, var)] = [iq.quantize(x, fmt, gran, stats=True, workspace=w, **self._kw(var, i))
+                                        for i, (x, w) in enumerate(zip(self.xs, self.ws))]
         out_dt = torch.bfloat16 if self.in_elem == 2 else torch.float32
         self.out = [torch.empty((self.rows, self.cols), dtype=out_dt, device=x0.device) for _ in range(NSETS)]
         torch.cuda.synchronize()
 
-    def quant(self, fmt, gran, i):
-        self.iq.quantize(self.xs[i], fmt, gran, workspace=self.ws[i], out=self.q[(fmt, gran)][i])
+    def _kw(self, var, i):
+        return {"static_amax": self.amax[i]} if var == "static" else dict(VARIANTS[var])
 
-    def dequant(self, fmt, gran, i, j):
-        self.iq.dequantize(self.q[(fmt, gran)][j], out=self.out[i])
+    def quant(self, fmt, gran, i, var=""):
+        self.iq.quantize(self.xs[i], fmt, gran, workspace=self.ws[i], out=self.q[(fmt, gran, var)][i],
+                         **self._kw(var, i))
+
+    def dequant(self, fmt, gran, i, j, var=""):
+        self.iq.dequantize(self.q[(fmt, gran, var)][j], out=self.out[i])
 
     def bytes(self, fmt, gran):
         qb, code_b = algo_bytes(fmt, gran, self.rows, self.cols, self.in_elem)
@@ -336,8 +350,12 @@ def time_calls(body, n_calls, use_graph, reps, stream):
 def breakdown(args):
     import torch
     res = {}
-    plan = [("c1", [("int8", "tensor"), ("e4m3", "tensor")]), ("c2", [("e4m3", "row"), ("e5m2", "row")]),
-            ("c3", [("mxfp4", "block")]), ("c4", [("nvfp4", "block")]), ("c5", [("int4", "block")])]
+    plan = [("c1", [("int8", "tensor"), ("e4m3", "tensor"), ("int8", "tensor", "static"),
+                    ("e4m3", "tensor", "static")]),
+            ("c2", [("e4m3", "row"), ("e5m2", "row")]),
+            ("c3", [("mxfp4", "block"), ("mxfp4", "block", "mx-nearest"), ("mxfp4", "block", "mx-up")]),
+            ("c4", [("nvfp4", "block"), ("nvfp4", "block", "nv-rne"), ("nvfp4", "block", "static")]),
+            ("c5", [("int4", "block"), ("int4zp", "block")])]
     if args.stream:
         from synth import synth
         plan.append(("stream", list(synth.WORKLOADS["stream"].formats)))
@@ -345,14 +363,16 @@ def breakdown(args):
     n = 2 * NSETS
     for name, fmts in plan:
         W = Workload(name, fmts)
-        for fmt, gran in fmts:
+        for spec in fmts:
+            fmt, gran, var = (*spec, "")[:3]
+
             def q():
                 for k in range(n):
-                    W.quant(fmt, gran, k % NSETS)
+                    W.quant(fmt, gran, k % NSETS, var)
 
             def d():
                 for k in range(n):
-                    W.dequant(fmt, gran, k % NSETS, (k + 1) % NSETS)
+                    W.dequant(fmt, gran, k % NSETS, (k + 1) % NSETS, var)
 
             q()
             torch.cuda.synchronize()
@@ -361,7 +381,7 @@ def breakdown(args):
             qb, dq = W.bytes(fmt, gran)
             gq = qb / (uq * 1e-6) / 1e9
             gd = dq / (ud * 1e-6) / 1e9
-            res[f"{name}:{fmt}/{gran}"] = {
+            res[f"{name}:{fmt}/{gran}" + (f"/{var}" if var else "")] = {
                 "quantize_GBps": round(gq, 1), "quantize_frac_hbm": round(gq / HBM_PEAK_GBS, 4),
                 "quantize_us": round(uq, 2), "dequantize_GBps": round(gd, 1), "dequantize_us": round(ud, 2),
                 "quantize_bytes": qb, "dequantize_bytes": dq}
@@ -377,12 +397,13 @@ def only(args):
     if args.only == "copy":
         print(json.dumps({"copy_ceiling": copy_ceiling(args.reps)}), flush=True)
         return
-    name, fmt, gran = args.only.split(":")
-    W = Workload(name, [(fmt, gran)])
+    name, fmt, gran, *rest = args.only.split(":")
+    var = rest[0] if rest else ""
+    W = Workload(name, [(fmt, gran, var)])
     for s in range(args.warmup + args.steps):
-        W.quant(fmt, gran, s % NSETS)
+        W.quant(fmt, gran, s % NSETS, var)
     for s in range(args.steps):
-        W.dequant(fmt, gran, s % NSETS, (s + 1) % NSETS)
+        W.dequant(fmt, gran, s % NSETS, (s + 1) % NSETS, var)
     torch.cuda.synchronize()
     print(json.dumps({"only": args.only, "calls": args.warmup + args.steps}), flush=True)
 
