@@ -433,6 +433,19 @@ struct Stats {
         for (int i = 0; i < 8; ++i) sat[i] = __builtin_fabsf(vs[i]) > thr;
         add8_slow_flags(x, sat, h);
     }
+    // One element of the general case (wave-uniform call).
+    __device__ __forceinline__ void add1_slow(float x, bool sat, float h) {
+        const bool fin = __builtin_isfinite(x);
+        const double d = fin ? (double)(x - h) : 0.0;
+        const double xs = fin ? (double)x : 0.0;
+        sx2 = __builtin_fma(xs, xs, sx2);
+        se2 = __builtin_fma(d, d, se2);
+        sae += __builtin_fabs(d);
+        mae = __builtin_fmaxf(mae, fin ? __builtin_fabsf(x - h) : 0.f);
+        nsat += __popcll(__ballot(sat));
+        nzf += __popcll(__ballot(fin && x != 0.f && h == 0.f));
+        nnf += __popcll(__ballot(!fin));
+    }
     // The same with the saturation of each element decided by the caller.
     __device__ __forceinline__ void add8_slow_flags(const float (&x)[8], const bool (&sat)[8], const float (&h)[8]) {
 #pragma unroll
@@ -455,6 +468,7 @@ struct Stats {
 // exactly when A > Q * s, whose sign the single rounding of fma(Q, s, -A)
 // preserves.
 __device__ __forceinline__ bool can_saturate(float A, float s, float Q) { return __builtin_fmaf(Q, s, -A) < 0.f; }
+
 
 // Reduce the workgroup's statistics (NWAVES waves) and write its partial.
 template <int NWAVES>
@@ -505,13 +519,38 @@ __device__ void write_partial(Stats& st, Partial* out) {
 // Grids and their constants.
 // ---------------------------------------------------------------------------
 template <int FMT> struct Fmt;
-template <> struct Fmt<F_INT8> { static constexpr float qmax = 127.f; static constexpr int iq = 127; };
-template <> struct Fmt<F_E4M3> { static constexpr float qmax = 448.f; static constexpr int iq = 448; };
-template <> struct Fmt<F_E5M2> { static constexpr float qmax = 57344.f; static constexpr int iq = 57344; };
+// qmid: the midpoint between qmax and the next binary32 above it (qmax's
+// significand is even, so the midpoint itself rounds down to qmax).
+template <> struct Fmt<F_INT8> {
+    static constexpr float qmax = 127.f; static constexpr int iq = 127;
+    static constexpr double qmid = 127.0 + 0x1p-18;
+};
+template <> struct Fmt<F_E4M3> {
+    static constexpr float qmax = 448.f; static constexpr int iq = 448;
+    static constexpr double qmid = 448.0 + 0x1p-16;
+};
+template <> struct Fmt<F_E5M2> {
+    static constexpr float qmax = 57344.f; static constexpr int iq = 57344;
+    static constexpr double qmid = 57344.0 + 0x1p-9;
+};
 template <> struct Fmt<F_MXFP4> { static constexpr float qmax = 6.f; };
 template <> struct Fmt<F_NVFP4> { static constexpr float qmax = 6.f; };
 template <> struct Fmt<F_INT4> { static constexpr float qmax = 7.f; };
 template <> struct Fmt<F_INT4ZP> { static constexpr float qmax = 15.f; };   // codes 0..15
+
+// Saturation in the x domain: for s > 0 and the correctly rounded v = x / s,
+// |v| > Q exactly when x / s > qmid (the midpoint above Q rounds down to Q),
+// i.e. when |x| > T = RD(qmid * s).  The FP64 product is exact (25 + 24
+// significant bits).  Checked on the CPU for every grid against the
+// division, with x next to T and to Q * s over scales 2^-60 .. 2^60.
+__device__ __forceinline__ float rd_to_float(double p) {   // p >= 0
+    float f = (float)p;
+    if ((double)f > p) f = as_f(as_u(f) - 1u);
+    return f;
+}
+template <int FMT> __device__ __forceinline__ float sat_threshold(float s) {
+    return rd_to_float(Fmt<FMT>::qmid * (double)s);
+}
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |v| < 2^22 to an integer (RNE)
 constexpr float kTinyScale = 0x1p-64f;  // smaller scales take the slow path
@@ -679,20 +718,25 @@ __device__ __forceinline__ void cast_uniform_slow(const float (&x)[8], float s, 
     w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
 }
 
-// The common case of a unit: finite, absmax in the fast range, no exact
-// zeros and no lane of the wave able to saturate.  No flag tests.
-template <int IN, int FMT, bool STATS>
-__device__ __forceinline__ void quant_chunk_hot(const Chunk<IN>& ch, float s, float y, bool store, uint8_t* codes8,
-                                                float (&h)[8], Stats& st) {
-    constexpr float Q = Fmt<FMT>::qmax;
+// Fast path of a unit (finite, absmax in the fast range), wave-uniform
+// `sat` and `zeros`: `zeros` means the unit may hold exact zeros; without
+// it every lane with `store` holds 8 nonzero inputs and lanes without data
+// hold zeros.
+// T = sat_threshold(s): the saturation count compares |x| > T, so the
+// quotients are dead once converted.  SAT and ZEROS fixed at compile time
+// keep the unrolled chunks free of branches (runtime flags inside the
+// chunk loop cost about 30 VGPRs).
+template <int IN, int FMT, bool STATS, bool SAT, bool ZEROS>
+__device__ __forceinline__ void quant_chunk_fast_t(const Chunk<IN>& ch, float s, float y, float T, bool store,
+                                                   uint8_t* codes8, float (&h)[8], Stats& st) {
     float x[8], v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
     uint32_t w0, w1;
     cast_uniform_fast<FMT>(x, s, y, v, h, w0, w1);
     if (STATS) {
-        st.add8_fast<IN, false, false>(ch, false, x, v, h, Q);
-        st.count_flush(store ? 8u : 0u, nonzero_bytes(w0) + nonzero_bytes(w1));
+        st.add8_fast<IN, true, false>(ch, SAT, x, v, h, T);
+        st.count_flush(ZEROS ? ch.nonzero_count() : (store ? 8u : 0u), nonzero_bytes(w0) + nonzero_bytes(w1));
     }
     if (store) {
         const u2v o = {w0, w1};
@@ -700,30 +744,40 @@ __device__ __forceinline__ void quant_chunk_hot(const Chunk<IN>& ch, float s, fl
     }
 }
 
-// `zeros` (uniform): the unit may hold exact zeros; without it every lane
-// with `store` holds 8 nonzero inputs and lanes without data hold zeros.
 template <int IN, int FMT, bool STATS>
-__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float s, float y, bool fast, bool sat,
-                                                    bool zeros, bool store, uint8_t* codes8, float (&h)[8], Stats& st) {
+__device__ __forceinline__ void quant_chunk_fast(const Chunk<IN>& ch, float s, float y, bool sat, float T, bool zeros,
+                                                 bool store, uint8_t* codes8, float (&h)[8], Stats& st) {
+    if (sat) {
+        if (zeros) quant_chunk_fast_t<IN, FMT, STATS, true, true>(ch, s, y, T, store, codes8, h, st);
+        else quant_chunk_fast_t<IN, FMT, STATS, true, false>(ch, s, y, T, store, codes8, h, st);
+    } else {
+        if (zeros) quant_chunk_fast_t<IN, FMT, STATS, false, true>(ch, s, y, T, store, codes8, h, st);
+        else quant_chunk_fast_t<IN, FMT, STATS, false, false>(ch, s, y, T, store, codes8, h, st);
+    }
+}
+
+// General path: correctly rounded division, clamps, FP64 statistics.
+template <int IN, int FMT, bool STATS>
+__device__ __forceinline__ void quant_chunk_slow(const Chunk<IN>& ch, float s, bool store, uint8_t* codes8,
+                                                 float (&h)[8], Stats& st) {
     constexpr float Q = Fmt<FMT>::qmax;
     float x[8], v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ch.get(i);
     uint32_t w0, w1;
-    if (fast) {
-        cast_uniform_fast<FMT>(x, s, y, v, h, w0, w1);
-        if (STATS) {
-            st.add8_fast<IN, false, false>(ch, sat, x, v, h, Q);
-            st.count_flush(zeros ? ch.nonzero_count() : (store ? 8u : 0u), nonzero_bytes(w0) + nonzero_bytes(w1));
-        }
-    } else {
-        cast_uniform_slow<FMT>(x, s, v, h, w0, w1);
-        if (STATS) st.add8_slow(x, v, h, Q);
-    }
+    cast_uniform_slow<FMT>(x, s, v, h, w0, w1);
+    if (STATS) st.add8_slow(x, v, h, Q);
     if (store) {
         const u2v o = {w0, w1};
         __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(codes8));
     }
+}
+
+template <int IN, int FMT, bool STATS>
+__device__ __forceinline__ void quant_chunk_uniform(const Chunk<IN>& ch, float s, float y, bool fast, bool sat, float T,
+                                                    bool zeros, bool store, uint8_t* codes8, float (&h)[8], Stats& st) {
+    if (fast) quant_chunk_fast<IN, FMT, STATS>(ch, s, y, sat, T, zeros, store, codes8, h, st);
+    else quant_chunk_slow<IN, FMT, STATS>(ch, s, store, codes8, h, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -773,7 +827,7 @@ __device__ __forceinline__ void unstage_row(const RowStage<IN, CPT, NT>& st, con
 
 // Row scale and flags, uniform over the workgroup (sat: over the wave).
 struct RowScale {
-    float s, y;
+    float s, y, T;   // T: saturation threshold in the x domain
     bool fast, sat, zeros;
 };
 
@@ -810,14 +864,133 @@ __device__ __forceinline__ RowScale row_scale(const Chunk<IN> (&ch)[CPT], uint32
     // alpha / Q: the constant-divisor correction is exact for normal quotients
     r.s = stat_range(alpha) ? div_const<Fmt<FMT>::iq>(alpha) : alpha / Q;
     r.y = r.fast ? 1.0f / r.s : 0.f;
-    // |v| > Q needs |x| > Q * s: only waves with such a lane test (per wave)
-    r.sat = !r.fast || __ballot(can_saturate(as_f(lane_bits), r.s, Q)) != 0;
+    r.T = sat_threshold<FMT>(r.s);
+    // only waves holding a saturating element count per element
+    r.sat = !r.fast || __ballot(as_f(lane_bits) > r.T) != 0;
     return r;
 }
 
+// One element of the general path: correctly rounded division, clamps,
+// NaN codes (INT8: 0; FP8: 0x7F), a zero scale giving +0 codes.
+template <int FMT>
+__device__ __forceinline__ uint32_t cast1_slow(float x, float s, float& v, float& h) {
+    constexpr float Q = Fmt<FMT>::qmax;
+    v = (s == 0.f) ? 0.f : x / s;
+    if (FMT == F_INT8) {
+        const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v), -127.f), 127.f);
+        const int qi = __builtin_isnan(v) ? 0 : (int)q;
+        h = s * (float)qi;
+        return (uint32_t)qi & 0xFFu;
+    } else {
+        const float cl = __builtin_fminf(__builtin_fmaxf(v, -Q), Q);
+        uint32_t c = fp8_pack4<FMT>(cl, 0.f, 0.f, 0.f) & 0xFFu;
+        if (__builtin_isnan(v)) c = 0x7Fu;
+        if (s == 0.f) c = 0u;
+        h = s * fp8_unpack2<FMT, false>(c).x;
+        return c;
+    }
+}
+
+template <int IN> __device__ __forceinline__ float load_elem(const void* x, int64_t i) {
+    if (IN == D_BF16) return as_f((uint32_t)static_cast<const uint16_t*>(x)[i] << 16);
+    return static_cast<const float*>(x)[i];
+}
+
+__device__ __forceinline__ void store_xhat1(void* xhat, int dtype, int64_t i, float h) {
+    if (dtype == D_F32) {
+        static_cast<float*>(xhat)[i] = h;
+    } else {
+        uint32_t w;
+        asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(w) : "v"(h), "v"(h));
+        static_cast<uint16_t*>(xhat)[i] = (uint16_t)w;
+    }
+}
+
+// Rows that are not finite or whose absmax leaves [2^-40, 2^60]: element by
+// element, re-read from x, in rolled loops, so this rare case needs few
+// registers and does not lower the kernel's occupancy.  The loops are
+// uniform; lanes past the row end work on zeros and store nothing.
+template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS>
+__device__ __forceinline__ void quant_row_slow(const RowArgs& a, int32_t row, float s, uint8_t* crow, Stats& st) {
+    constexpr float Q = Fmt<FMT>::qmax;
+    const int64_t base = (int64_t)row * a.ld;
+    const int64_t cols = (int64_t)a.cpr * kChunk;
+#pragma unroll 1
+    for (int j = 0; j < CPT; ++j) {
+        const uint32_t c = threadIdx.x + j * NT;
+        const bool valid = FULL || (int)c < a.cpr;
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i) {
+            const float x = valid ? load_elem<IN>(a.x, base + (int64_t)c * kChunk + i) : 0.f;
+            float v, h;
+            const uint32_t code = cast1_slow<FMT>(x, s, v, h);
+            if (i < 4) w0 |= code << (8 * i);
+            else w1 |= code << (8 * (i - 4));
+            if (STATS) st.add1_slow(x, __builtin_fabsf(v) > Q, h);
+            if (XHAT && valid) store_xhat1(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk + i, h);
+        }
+        if (valid) {
+            const u2v o = {w0, w1};
+            __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(crow + c * 8u));
+        }
+    }
+}
+
+// Fast path of a staged row.  Saturated elements and exact zeros are
+// counted first, in the rare waves and rows that hold them, so that the
+// cast below is one branch-free body (flags inside the unrolled chunk loop
+// cost about 30 VGPRs).  Within the fast range only elements equal to the
+// row's absmax can exceed T (T > the float below alpha), so `r.sat` is set
+// in the waves holding the maximum when it saturates.  The cast counts zero
+// codes as flushed; zero inputs, which always give a zero code, are
+// subtracted here.
+template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS>
+__device__ __forceinline__ void quant_row_fast(const Chunk<IN> (&ch)[CPT], const RowArgs& a, int32_t row,
+                                               const RowScale& r, uint8_t* crow, Stats& st) {
+    const int64_t cols = (int64_t)a.cpr * kChunk;
+    if (STATS && r.sat) {
+        // |x| > T on the integer images of |x| (opaque copies, so that none
+        // of this is shared with, and hoisted for, the cast below)
+        const uint32_t tb = as_u(r.T);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+#pragma unroll
+            for (int k = 0; k < (int)(sizeof(ch[j].w) / 4); ++k) {
+                uint32_t w = ch[j].w[k];
+                asm volatile("" : "+v"(w));
+                if (IN == D_BF16) {
+                    st.nsat += __popcll(__ballot((w & 0x7FFFu) > (tb >> 16)));
+                    st.nsat += __popcll(__ballot(((w >> 16) & 0x7FFFu) > (tb >> 16)));
+                } else {
+                    st.nsat += __popcll(__ballot((w & 0x7FFFFFFFu) > tb));
+                }
+            }
+        }
+    }
+    if (STATS && r.zeros) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            Chunk<IN> cj = ch[j];   // opaque copy, as above
+#pragma unroll
+            for (int k = 0; k < (int)(sizeof(cj.w) / 4); ++k) asm volatile("" : "+v"(cj.w[k]));
+            if (FULL || (int)(threadIdx.x + j * NT) < a.cpr) st.lzf -= 8u - cj.nonzero_count();
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const uint32_t c = threadIdx.x + j * NT;
+        const bool valid = FULL || (int)c < a.cpr;
+        float h[8];
+        quant_chunk_fast_t<IN, FMT, STATS, false, false>(ch[j], r.s, r.y, r.T, valid, crow + c * 8u, h, st);
+        if (XHAT && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
+    }
+}
+
 // Per-row INT8 / FP8: the next row streams into LDS while the current one
-// is reduced, cast and stored.
-template <int IN, int FMT, int CPT, int NT, bool FULL, bool STATS>
+// is reduced, cast and stored.  XHAT: the x^ output is requested (a separate
+// instantiation, so the other one carries no x^ code).
+template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS>
 __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
     __shared__ uint32_t s_red[2][NT / 64][2];
     __shared__ RowStage<IN, CPT, NT> stage;
@@ -837,22 +1010,10 @@ __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
         const auto r = row_scale<IN, FMT, CPT, NT>(ch, s_red, parity);
         if (threadIdx.x == 0) a.scales[row] = r.s;
         uint8_t* crow = a.codes + (int64_t)row * cols;
-        if (r.fast && !r.zeros && !r.sat && !a.xhat) {
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                const uint32_t c = threadIdx.x + j * NT;
-                float h[8];
-                quant_chunk_hot<IN, FMT, STATS>(ch[j], r.s, r.y, FULL || (int)c < a.cpr, crow + c * 8u, h, st);
-            }
+        if (r.fast) {
+            quant_row_fast<IN, FMT, CPT, NT, FULL, XHAT, STATS>(ch, a, row, r, crow, st);
         } else {
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                const uint32_t c = threadIdx.x + j * NT;
-                const bool valid = FULL || (int)c < a.cpr;
-                float h[8];
-                quant_chunk_uniform<IN, FMT, STATS>(ch[j], r.s, r.y, r.fast, r.sat, r.zeros, valid, crow + c * 8u, h, st);
-                if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
-            }
+            quant_row_slow<IN, FMT, CPT, NT, FULL, XHAT, STATS>(a, row, r.s, crow, st);
         }
         if (STATS) st.fold();
     }
@@ -893,7 +1054,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
         if (tid == 0) a.scales[row] = s;
         const bool fast = !nonfinite && stat_range(alpha);
         const float y = fast ? 1.0f / s : 0.f;
-        const bool sat = !fast || can_saturate(alpha, s, Q);
+        const float T = sat_threshold<FMT>(s);
+        const bool sat = !fast || alpha > T;
         uint8_t* crow = a.codes + (int64_t)row * cols;
         // uniform trip count: lanes past the row end carry a zero chunk
         for (int c0 = 0; c0 < a.cpr; c0 += kThreads) {
@@ -903,7 +1065,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
             if (valid) ch.load(a.x, base + (int64_t)c * kChunk);
             else ch.zero();
             float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch, s, y, fast, sat, true, valid, crow + (int64_t)c * kChunk, h, st);
+            quant_chunk_uniform<IN, FMT, STATS>(ch, s, y, fast, sat, T, true, valid, crow + (int64_t)c * kChunk, h, st);
             if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)row * cols + (int64_t)c * kChunk, h);
             if (STATS) st.fold();
         }
@@ -1442,7 +1604,7 @@ __device__ __forceinline__ uint32_t unswz(uint32_t i) { return (i & ~7u) | ((i -
 
 // Per-tensor constants of the flat kernel.
 struct FlatConst {
-    float s, y;
+    float s, y, T;        // T: per-tensor saturation threshold in the x domain
     bool fast, sat, zeros;
     uint32_t amax_bits;   // the per-tensor absmax the scale came from
     NvConst nk;
@@ -1487,7 +1649,7 @@ __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread *
         for (int c = 0; c < kTileChunksPerThread; ++c) {
             const bool valid = FULL || (uint32_t)c < nvalid;
             float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch[c], k.s, k.y, fast, k.sat, zeros, valid,
+            quant_chunk_uniform<IN, FMT, STATS>(ch[c], k.s, k.y, fast, k.sat, k.T, zeros, valid,
                                                 a.codes + (int64_t)(g0 + c) * kChunk, h, st);
             if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
         }
@@ -1502,16 +1664,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
     // Per-tensor quantities from the absmax pre-pass (uniform over the grid).
-    float s = 0.f, y = 0.f;
+    float s = 0.f, y = 0.f, T = 0.f;
     bool fast = false, sat = true, zeros = true;
     if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2 || FMT == F_NVFP4) {
         s = a.info->scale;
         zeros = a.info->zeros != 0;
         const float alpha = as_f(a.info->amax_bits);
         fast = a.info->nonfinite == 0 && stat_range(alpha);
-        if (fast && FMT != F_NVFP4) {
-            y = 1.0f / s;
-            sat = can_saturate(alpha, s, Fmt<FMT>::qmax);
+        if constexpr (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) {
+            if (fast) {
+                y = 1.0f / s;
+                T = sat_threshold<FMT>(s);
+                sat = alpha > T;
+            }
         }
     }
     // Reciprocal tables, filled once per workgroup with correctly rounded divisions.
@@ -1564,7 +1729,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     };
     if (blockIdx.x < ntiles) stage_tile(blockIdx.x);
     FlatConst fk;
-    fk.s = s; fk.y = y; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
+    fk.s = s; fk.y = y; fk.T = T; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
     fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? a.info->amax_bits : 0u;
     const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -1719,13 +1884,14 @@ __global__ __launch_bounds__(kFinThreads) void k_stats_finalize(const Partial* p
     if (t == 0) {
         StatsOut o;
         o.n = nelem;
-        o.sum_x2 = (s_d[0][0] + s_d[1][0]) + (s_d[2][0] + s_d[3][0]);
-        o.sum_err2 = (s_d[0][1] + s_d[1][1]) + (s_d[2][1] + s_d[3][1]);
-        o.sum_abs_err = (s_d[0][2] + s_d[1][2]) + (s_d[2][2] + s_d[3][2]);
-        o.max_abs_err = __builtin_fmaxf(__builtin_fmaxf(s_m[0], s_m[1]), __builtin_fmaxf(s_m[2], s_m[3]));
-        o.n_saturated = s_c[0][0] + s_c[1][0] + s_c[2][0] + s_c[3][0];
-        o.n_zero_flush = s_c[0][1] + s_c[1][1] + s_c[2][1] + s_c[3][1];
-        o.n_nonfinite = s_c[0][2] + s_c[1][2] + s_c[2][2] + s_c[3][2];
+        o.sum_x2 = s_d[0][0]; o.sum_err2 = s_d[0][1]; o.sum_abs_err = s_d[0][2]; o.max_abs_err = s_m[0];
+        o.n_saturated = s_c[0][0]; o.n_zero_flush = s_c[0][1]; o.n_nonfinite = s_c[0][2];
+#pragma unroll
+        for (int k = 1; k < kFinThreads / 64; ++k) {   // waves in order
+            o.sum_x2 += s_d[k][0]; o.sum_err2 += s_d[k][1]; o.sum_abs_err += s_d[k][2];
+            o.max_abs_err = __builtin_fmaxf(o.max_abs_err, s_m[k]);
+            o.n_saturated += s_c[k][0]; o.n_zero_flush += s_c[k][1]; o.n_nonfinite += s_c[k][2];
+        }
         o.reserved = 0;
         *out = o;
     }
@@ -1869,14 +2035,18 @@ template <int NT = kThreads, typename K> int grid_for(K kernel, uint64_t units) 
 
 uint32_t tiles_of(uint32_t nchunks) { return (nchunks + kTileChunks - 1) / kTileChunks; }
 
+// With x^ requested the partial-row instantiation serves every row length.
 template <int IN, int FMT, int CPT, int NT, bool STATS>
 void launch_row_k(const RowArgs& r, int& grid, hipStream_t s) {
-    if (r.cpr == CPT * NT) {
-        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, true, STATS>, (uint64_t)r.rows);
-        k_quant_row<IN, FMT, CPT, NT, true, STATS><<<grid, NT, 0, s>>>(r);
+    if (r.xhat) {
+        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, false, true, STATS>, (uint64_t)r.rows);
+        k_quant_row<IN, FMT, CPT, NT, false, true, STATS><<<grid, NT, 0, s>>>(r);
+    } else if (r.cpr == CPT * NT) {
+        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, true, false, STATS>, (uint64_t)r.rows);
+        k_quant_row<IN, FMT, CPT, NT, true, false, STATS><<<grid, NT, 0, s>>>(r);
     } else {
-        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, false, STATS>, (uint64_t)r.rows);
-        k_quant_row<IN, FMT, CPT, NT, false, STATS><<<grid, NT, 0, s>>>(r);
+        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, false, false, STATS>, (uint64_t)r.rows);
+        k_quant_row<IN, FMT, CPT, NT, false, false, STATS><<<grid, NT, 0, s>>>(r);
     }
 }
 
