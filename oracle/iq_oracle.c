@@ -542,6 +542,37 @@ int iqo_quantize_static(const iqo_desc* d, const void* x, float amax_in, uint8_t
     return iqo_quantize_rows(d, x, 0, d->rows, iqo_static_amax(amax_in), codes, scales, global_scale, xhat, st);
 }
 
+/* ---- [TR] Puzzle 12: the dequantize-then-dot consumer -------------------- */
+/* z[j, k] = sum_l sc * (w - sh) * y[l, k], written out: sc * (w - sh) has at
+ * most 24 + 5 significant bits and y at most 24, so each product is exact in
+ * binary64; the sum over l runs in order. */
+int iqo_zp_gemm(const iqo_desc* d, const uint8_t* codes, const float* scales, const uint8_t* shifts,
+                const void* x, int x_dtype, int64_t n1, double* z, double* zabs) {
+    if (iqo_check(d) || d->fmt != IQO_INT4ZP || n1 < 0) return -1;
+    if (x_dtype != IQO_F32 && x_dtype != IQO_BF16) return -1;
+    const int64_t K = d->cols, ng = K / 128;
+    for (int64_t j = 0; j < d->rows; ++j) {
+        for (int64_t k = 0; k < n1; ++k) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t l = 0; l < K; ++l) {
+                uint8_t byte = codes[j * (K / 2) + l / 2];
+                int w = (int)((l & 1) ? (byte >> 4) : (byte & 0xFu));
+                int64_t g = l / 128;
+                uint8_t sb = shifts[j * (ng / 2) + g / 2];
+                int sh = (int)((g & 1) ? (sb >> 4) : (sb & 0xFu));
+                double y = x_dtype == IQO_F32 ? (double)((const float*)x)[k * K + l]
+                                              : (double)iqo_bf16_to_f32(((const uint16_t*)x)[k * K + l]);
+                double t = (double)scales[j * ng + g] * (double)(w - sh) * y;
+                acc += t;
+                mag += fabs(t);
+            }
+            z[j * n1 + k] = acc;
+            if (zabs) zabs[j * n1 + k] = mag;
+        }
+    }
+    return 0;
+}
+
 /* ---- dequantization: x^ = s * decode(q), the same products as above ----- */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype) {

@@ -95,6 +95,14 @@ int iqo_quantize_zp_rows(const iqo_desc* d, const void* x, int64_t r0, int64_t r
                          float* scales, uint8_t* shifts, float* xhat, iqo_stats* st);
 int iqo_dequantize_zp(const iqo_desc* d, const uint8_t* codes, const float* scales, const uint8_t* shifts,
                       void* xhat, int xhat_dtype);
+/* [TR] Puzzle 12: z[j, k] = sum_l sc[j, l/128] * (w[j, l] - sh[j, l/128]) * y[l, k]
+ * for the asymmetric INT4 weights of d (rows N0 = d->rows, K = d->cols) and
+ * activations given token-major, y[l, k] = x[k * K + l] (x: n1 rows of K,
+ * FP32 or BF16 by x_dtype).  Every product is exact in binary64 and the sum
+ * runs in l order in binary64; z and zabs (the sum of |terms|, the scale of
+ * any rounding bound) are [N0, n1] row-major. */
+int iqo_zp_gemm(const iqo_desc* d, const uint8_t* codes, const float* scales, const uint8_t* shifts,
+                const void* x, int x_dtype, int64_t n1, double* z, double* zabs);
 /* Reconstruct xhat ([rows, cols], FP32 or BF16) from codes and scales. */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype);

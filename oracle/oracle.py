@@ -87,6 +87,7 @@ def _load():
             "iqo_quantize_zp_rows": (ctypes.c_int, [ctypes.POINTER(Desc), P, I64, I64, P, P, P, P,
                                                     ctypes.POINTER(Stats)]),
             "iqo_dequantize_zp": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
+            "iqo_zp_gemm": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int, I64, P, P]),
             "iqo_quantize_static": (ctypes.c_int, [ctypes.POINTER(Desc), P, F, P, P, P, P,
                                                    ctypes.POINTER(Stats)]),
             "iqo_dequantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
@@ -314,3 +315,24 @@ def merge_stats(parts: list) -> dict:
 def _split(rows: int, threads: int) -> list:
     threads = max(1, min(threads, rows)) if rows else 1
     return [(rows * t // threads, rows * (t + 1) // threads) for t in range(threads)]
+
+
+def zp_gemm(codes: np.ndarray, scales: np.ndarray, shifts: np.ndarray, x: np.ndarray) -> tuple:
+    """Puzzle 12's z[j, k] = sum_l sc * (w - sh) * y[l, k] for asymmetric INT4
+    weights (N0 x K) and token-major activations x [n1, K] (float32 or BF16
+    bits); returns (z, zabs) as float64 [N0, n1]."""
+    n0 = codes.shape[0]
+    K = codes.shape[1] * 2
+    n1 = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("activations must be [n1, K]")
+    d = Desc(FORMATS["int4zp"], GRANS["block"], F32, n0, K, K, 0)
+    z = np.zeros((n0, n1), dtype=np.float64)
+    zabs = np.zeros((n0, n1), dtype=np.float64)
+    xd = F32 if x.dtype == np.float32 else BF16
+    rc = _load().iqo_zp_gemm(ctypes.byref(d), _p(np.ascontiguousarray(codes)),
+                             _p(np.ascontiguousarray(scales, dtype=np.float32)),
+                             _p(np.ascontiguousarray(shifts)), _p(np.ascontiguousarray(x)), xd, n1, _p(z), _p(zabs))
+    if rc:
+        raise RuntimeError("iqo_zp_gemm failed")
+    return z, zabs

@@ -732,6 +732,54 @@ def test_p15_zp_special_values(O):
     assert r["scales"][1, 1] == 0.0 and w[1, 128] == 0
 
 
+# ---- P16: Puzzle 12's dequantize-then-dot -------------------------------------------
+def zp_weights(O, S, n0=48, K=1024, seed=77):
+    w = (S.bf16_to_f32(S.make("c5", nrows=n0))[:, :K]).astype(np.float32).copy()
+    r = O.quantize(np.ascontiguousarray(w), "int4zp", "block")
+    return w, r
+
+
+def test_p16_zp_gemm_is_puzzle12(O, S):
+    """The oracle's loop against the page's own procedure: extract() the
+    32-bit words, reshape into groups, broadcast scale and offset, then a
+    dot with the activations (numpy, float64)."""
+    w, r = zp_weights(O, S)
+    n0, K = w.shape
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((24, K)) * 0.7).astype(np.float32)
+    z, zabs = O.zp_gemm(r["codes"], r["scales"], r["shifts"], x)
+    wq = puzzle12_extract(r["codes"].view("<u4")).astype(np.float64)                  # [n0, K]
+    sh = puzzle12_extract(r["shifts"].view("<u4")).astype(np.float64)                 # [n0, K/128]
+    G = K // 128
+    wd = r["scales"].astype(np.float64)[:, :, None] * (wq.reshape(n0, G, 128) - sh[:, :, None])
+    want = wd.reshape(n0, K) @ x.T.astype(np.float64)
+    assert np.all(np.abs(z - want) <= 1e-12 * zabs + 1e-300)
+    assert np.all(zabs >= np.abs(z))
+
+
+def test_p16_zp_gemm_identity_and_bound(O, S):
+    """Identity activations return the format's x^ exactly (sc * (w - sh)
+    rounded once to FP32); any activations give z within the quantization
+    bound of the unquantized product, |z - W y| <= sum_l sc_l |y_l|."""
+    w, r = zp_weights(O, S, n0=16, K=256)
+    n0, K = w.shape
+    eye = np.eye(K, dtype=np.float32)
+    z, _ = O.zp_gemm(r["codes"], r["scales"], r["shifts"], eye)
+    assert np.array_equal(z.astype(np.float32), r["xhat"])
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((8, K)).astype(np.float32)
+    z, _ = O.zp_gemm(r["codes"], r["scales"], r["shifts"], x)
+    exact = w.astype(np.float64) @ x.T.astype(np.float64)
+    sc = np.repeat(r["scales"].astype(np.float64), 128, axis=1)
+    bound = sc @ np.abs(x.T.astype(np.float64))
+    assert np.all(np.abs(z - exact) <= bound * (1 + 1e-9))
+    # BF16 activations read as the same values
+    xb = S.f32_to_bf16_bits(x)
+    zb, _ = O.zp_gemm(r["codes"], r["scales"], r["shifts"], xb)
+    z2, _ = O.zp_gemm(r["codes"], r["scales"], r["shifts"], S.bf16_to_f32(xb).astype(np.float32))
+    assert np.array_equal(zb, z2)
+
+
 # ---- P14: statistics by brute force ------------------------------------------------
 @pytest.mark.parametrize("fmt,gran,cfg", [("e4m3", "row", "c2"), ("e5m2", "row", "c2"),
                                           ("int8", "tensor", "c1"), ("mxfp4", "block", "c3"),
