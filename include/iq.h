@@ -204,6 +204,24 @@ iq_status iq_dequantize_zp(const iq_desc* d, const void* codes, const float* sca
 /* Bytes of the shifts array for an IQ_INT4_ZP descriptor (0 otherwise). */
 size_t iq_shifts_bytes(const iq_desc* d);
 
+/*
+ * The consumer of Puzzle 12 (Triton post, "Quantized Matrix Mult"):
+ *   z[j, k] = sum_l sc[j, l/128] * (w[j, l] - sh[j, l/128]) * y[l, k]
+ * with the IQ_INT4_ZP weights of d (N0 = d->rows, K = d->cols; codes,
+ * scales and shifts laid out as for iq_quantize_zp) and activations given
+ * token-major: x is [n1, K] row-major BF16 with x[k, l] = y[l, k].
+ *   z       output float32 [N0, n1] row-major, 4-byte aligned
+ *   x_dtype must be IQ_BF16 (IQ_EUNSUPPORTED otherwise): the products
+ *           (w - sh) * x are formed exactly on the BF16 matrix cores and
+ *           summed in FP32; each group's sum is scaled by sc with one fma.
+ * Accuracy: |z - exact| <= (K + 2) * 2^-24 * sum_l |sc (w - sh) y|.
+ * d->in_dtype and d->ld_in are ignored; codes and x 16-byte aligned.
+ * N0, n1 and K must fit 31 bits (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is
+ * legal and writes nothing.  No workspace.
+ */
+iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, const uint8_t* shifts,
+                     const void* x, int32_t x_dtype, int64_t n1, float* z, hipStream_t stream);
+
 const char* iq_status_str(iq_status s);
 int iq_abi_version(void);
 

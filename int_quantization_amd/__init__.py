@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.iq_dequantize_zp.restype = ctypes.c_int
     L.iq_dequantize_zp.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
     L.iq_shifts_bytes.restype, L.iq_shifts_bytes.argtypes = S, [D]
+    L.iq_zp_gemm.restype = ctypes.c_int
+    L.iq_zp_gemm.argtypes = [D, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P]
     L.iq_dequantize.restype = ctypes.c_int
     L.iq_dequantize.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
     L.iq_amax.restype = ctypes.c_int
@@ -137,6 +139,11 @@ def iq_dequantize_zp(d: IQDesc, codes: int, scales: int, shifts: int, xhat: int,
 
 def iq_shifts_bytes(d: IQDesc) -> int:
     return load_library().iq_shifts_bytes(ctypes.byref(d))
+
+
+def iq_zp_gemm(d: IQDesc, codes: int, scales: int, shifts: int, x: int, x_dtype: int, n1: int, z: int,
+               stream: int | None) -> int:
+    return load_library().iq_zp_gemm(ctypes.byref(d), codes, scales, shifts, x, x_dtype, n1, z, stream)
 
 
 def iq_dequantize(d: IQDesc, codes: int, scales: int, global_scale: int | None, xhat: int,
@@ -298,4 +305,23 @@ def amax(x, workspace=None, stream=None):
     out = torch.empty((1,), dtype=torch.float32, device=x.device)
     ws = workspace if workspace is not None else workspace_for(d, x.device)
     _check(iq_amax(d, x.data_ptr(), out.data_ptr(), ws.data_ptr(), _stream(stream)), "iq_amax")
+    return out
+
+
+def zp_gemm(q: "Quantized", x, out=None, stream=None):
+    """Puzzle 12's z[j, k] = sum_l sc (w - sh) y[l, k] for asymmetric INT4
+    weights q (from quantize(..., "int4zp", "block")) and token-major BF16
+    activations x [n1, K]; returns z float32 [N0, n1]."""
+    torch = _torch()
+    if q.fmt != "int4zp":
+        raise ValueError("zp_gemm needs asymmetric INT4 weights")
+    if x.dim() != 2 or x.shape[1] != q.cols or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous BF16 [n1, K] tensor")
+    n1 = x.shape[0]
+    if out is None:
+        out = torch.empty((q.rows, n1), dtype=torch.float32, device=x.device)
+    d = make_desc("int4zp", "block", q.rows, q.cols)
+    st = iq_zp_gemm(d, q.codes.data_ptr(), q.scales.data_ptr(), q.shifts.data_ptr(), x.data_ptr(), IQ_BF16, n1,
+                    out.data_ptr(), _stream(stream))
+    _check(st, "iq_zp_gemm")
     return out

@@ -1982,6 +1982,150 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The Puzzle 12 consumer on the matrix cores:
+//   z[j, k] = sum_g sc[j, g] * sum_{l in g} (w[j, l] - sh[j, g]) * x[k, l]
+// (Triton post, Puzzle 12; x token-major).  Within a group of 128, w - sh is
+// an integer in [-15, 15], exact in BF16, so v_mfma_f32_16x16x32_bf16 forms
+// exact products of it and the BF16 activations, summed in FP32; each group's
+// sum is scaled by sc and added with one fma.
+// A workgroup computes a 128 x 128 tile of z with 4 waves of 64 x 64 (4 x 4
+// MFMA tiles of 16 x 16).  Per group the activations stream into LDS by DMA
+// and each thread dequantizes half a weight row into LDS; both tiles keep
+// 16-byte slot c of row r at c ^ (r & 15), so the DMA stays coalesced and the
+// fragment reads (16 rows, one 16-byte slot each) hit distinct banks.
+// MFMA operand layout (16x16x32): lane l supplies row l % 16 of A and column
+// l % 16 of B with the same 8 consecutive k (a fixed slice per l / 16), and
+// receives D[4 (l / 16) + i][l % 16], i = 0..3.
+// ---------------------------------------------------------------------------
+constexpr int kGemmTile = 128;
+
+struct ZpGemmArgs {
+    const uint8_t* codes;    // [n0, K / 2]
+    const float* scales;     // [n0, K / 128]
+    const uint8_t* shifts;   // [n0, K / 256]
+    const uint16_t* x;       // [n1, K] BF16
+    float* z;                // [n0, n1]
+    int32_t n0, n1, K;
+    int32_t tiles_j, tiles_n, per_xcd;   // tile grid, tiles per XCD slice
+};
+
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// 8 weights (one code word, element i in bits 4i..4i+3) as BF16 w - sh: the
+// float 2^23 + w minus 2^23 + sh is exactly w - sh, whose BF16 is its upper half.
+__device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float base) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = as_f(0x4B000000u | ((w >> (4 * i)) & 0xFu)) - base;
+    u4v o;
+    o.x = __builtin_amdgcn_perm(as_u(f[1]), as_u(f[0]), 0x07060302u);
+    o.y = __builtin_amdgcn_perm(as_u(f[3]), as_u(f[2]), 0x07060302u);
+    o.z = __builtin_amdgcn_perm(as_u(f[5]), as_u(f[4]), 0x07060302u);
+    o.w = __builtin_amdgcn_perm(as_u(f[7]), as_u(f[6]), 0x07060302u);
+    return o;
+}
+
+__global__ __launch_bounds__(kThreads) void k_zp_gemm(ZpGemmArgs a) {
+    __shared__ u4v sA[kGemmTile * 16];   // weights (w - sh) BF16, swizzled rows of 128
+    __shared__ u4v sB[kGemmTile * 16];   // activations BF16, same layout
+    __shared__ float sS[kGemmTile];      // the group's scales of the tile's rows
+    // Tiles of one XCD slice are consecutive: neighbours share weight rows in that XCD's L2.
+    const uint32_t b = blockIdx.x;
+    const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
+    if (idx >= (uint32_t)(a.tiles_j * a.tiles_n)) return;
+    const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
+    const int j0 = jb * kGemmTile, t0 = nb * kGemmTile;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int ng = a.K / 128;
+    const int ldc = a.K / 2;             // code bytes per weight row
+    const u4v zero = {0u, 0u, 0u, 0u};
+    f4v acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    // this thread's half weight row for the dequantization
+    const int dr = t >> 1, dh = t & 1;
+    const int dj = j0 + dr;
+    for (int g = 0; g < ng; ++g) {
+        // activations: wave w copies rows 32 w .. 32 w + 31, four per instruction
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int row = wave * 32 + q * 4 + (lane >> 4);
+            const int c = (lane & 15) ^ (row & 15);
+            const int tok = t0 + row;
+            u4v* dst = &sB[(wave * 8 + q) * 64];
+            if (tok < a.n1) dma_word(a.x + (int64_t)tok * a.K + g * 128 + c * 8, dst);
+            else dst[lane] = zero;
+        }
+        // weights: 64 codes of row dr, k = g * 128 + dh * 64 ..
+        if (dj < a.n0) {
+            const u4v* cp = reinterpret_cast<const u4v*>(a.codes + (int64_t)dj * ldc + g * 64 + dh * 32);
+            const u4v c0 = cp[0], c1 = cp[1];
+            const uint32_t sb = a.shifts[(int64_t)dj * (ng / 2) + (g >> 1)];
+            const float base = 8388608.0f + (float)((sb >> (4 * (g & 1))) & 0xFu);
+            const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sA[dr * 16 + ((dh * 8 + q) ^ (dr & 15))] = dequant8_bf16(cw[q], base);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sA[dr * 16 + ((dh * 8 + q) ^ (dr & 15))] = zero;
+        }
+        if (t < kGemmTile) sS[t] = (j0 + t < a.n0) ? a.scales[(int64_t)(j0 + t) * ng + g] : 0.f;
+        wait_staged();
+        __syncthreads();
+        f4v accg[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) accg[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int slot = 4 * s + (lane >> 4);
+            bf8v af[4], bfr[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int r = wm * 64 + mt * 16 + (lane & 15);
+                af[mt] = __builtin_bit_cast(bf8v, sA[r * 16 + (slot ^ (r & 15))]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int r = wn * 64 + nt * 16 + (lane & 15);
+                bfr[nt] = __builtin_bit_cast(bf8v, sB[r * 16 + (slot ^ (r & 15))]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    accg[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], accg[mt][nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sc = sS[wm * 64 + mt * 16 + 4 * (lane >> 4) + i];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) acc[mt][nt][i] = __builtin_fmaf(sc, accg[mt][nt][i], acc[mt][nt][i]);
+            }
+        __syncthreads();   // the next group's copies overwrite the tiles
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
+                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side helpers.
 // ---------------------------------------------------------------------------
 int ilog2_exact(uint32_t v) {
@@ -2211,6 +2355,20 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
     case F_INT4ZP: k_dequant<F_INT4ZP><<<grid_for(k_dequant<F_INT4ZP>, t), kThreads, 0, s>>>(a); break;
     default: k_dequant<F_INT4><<<grid_for(k_dequant<F_INT4>, t), kThreads, 0, s>>>(a); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
+    if (g.n0 == 0 || g.n1 == 0) return hipSuccess;
+    ZpGemmArgs a;
+    a.codes = static_cast<const uint8_t*>(g.codes); a.scales = g.scales; a.shifts = g.shifts;
+    a.x = static_cast<const uint16_t*>(g.x); a.z = g.z;
+    a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
+    a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
+    a.tiles_n = (int32_t)((g.n1 + kGemmTile - 1) / kGemmTile);
+    const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
+    a.per_xcd = (int32_t)((tiles + 7) / 8);
+    k_zp_gemm<<<(unsigned)(8 * (int64_t)a.per_xcd), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

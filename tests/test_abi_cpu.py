@@ -204,6 +204,29 @@ def test_int4zp_sizes_and_argument_errors(iq):
     assert iq.iq_dequantize_zp(iq.make_desc("int4", "block", 4, 256), FAKE, FAKE, FAKE, FAKE, 0, None) == E
 
 
+def test_zp_gemm_argument_errors(iq):
+    """The Puzzle 12 consumer: asymmetric INT4 weights only, BF16 activations
+    only (FP32 is legal but unsupported), alignment, empty shapes."""
+    E, A, U = iq.IQ_EINVAL, iq.IQ_EALIGN, iq.IQ_EUNSUPPORTED
+    d = iq.make_desc("int4zp", "block", 64, 512)
+
+    def g(d, codes=FAKE, scales=FAKE, shifts=FAKE, x=FAKE, xdt=1, n1=32, z=FAKE):
+        return iq.iq_zp_gemm(d, codes, scales, shifts, x, xdt, n1, z, None)
+    assert g(iq.make_desc("int4", "block", 64, 512)) == E
+    assert g(iq.make_desc("int4zp", "block", 64, 384)) == E
+    assert g(d, xdt=0) == U
+    assert g(d, xdt=7) == E
+    assert g(d, n1=-1) == E
+    assert g(d, x=None) == E
+    assert g(d, shifts=None) == E
+    assert g(d, z=None) == E
+    assert g(d, x=FAKE + 8) == A
+    assert g(d, codes=FAKE + 4) == A
+    assert g(d, z=FAKE + 2) == A
+    assert g(d, n1=0, x=None, z=None) == iq.IQ_OK          # nothing to do: no launch
+    assert g(iq.make_desc("int4zp", "block", 0, 512), x=None, z=None) == iq.IQ_OK
+
+
 def test_dequantize_and_amax_argument_errors(iq):
     E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
     d = iq.make_desc("nvfp4", "block", 4, 256)

@@ -730,3 +730,66 @@ def test_int4zp_edge_groups(iq, O, S, dtype):
     g = run_gpu(iq, x, "int4zp", "block")
     r = oracle_ref(O, x, "int4zp", "block")
     compare(g, r, "int4zp", f"int4zp edge groups ({'bf16' if dtype else 'f32'})", O)
+
+
+# ---- Puzzle 12's consumer: dequantize-then-dot on the matrix cores ------------------
+def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
+    """Weights quantized by the oracle (asymmetric INT4), BF16 activations;
+    the GPU result against the oracle's exact sum, within the FP32 bound."""
+    import torch
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n0, K)) * 0.02).astype(np.float32)
+    w[:, :: 97] *= 30.0                                           # outlier columns
+    r = O.quantize(w, "int4zp", "block")
+    x = S.f32_to_bf16_bits((rng.standard_normal((n1, K)) * x_scale).astype(np.float32))
+    q = iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "int4zp", "block", n0, K,
+                     to_device(r["shifts"]))
+    z = iq.zp_gemm(q, to_device(x)).cpu().numpy()
+    zr, zabs = O.zp_gemm(r["codes"], r["scales"], r["shifts"], x)
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+    err = np.abs(z.astype(np.float64) - zr)
+    assert np.all(err <= bound), f"{n0}x{K}x{n1}: max err/bound {np.max(err / bound):.3g}"
+    return err, bound, zr
+
+
+@pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (32, 1024, 300), (1, 256, 1),
+                                     (257, 768, 129), (384, 2048, 256)])
+def test_zp_gemm_parity(iq, O, S, n0, K, n1):
+    err, bound, zr = zp_gemm_case(iq, O, S, n0, K, n1, seed=n0 + K + n1)
+    assert np.abs(zr).max() > 0
+    assert np.max(err / bound) < 0.05          # the bound is loose; a real fault is not small
+
+
+def test_zp_gemm_zero_and_empty(iq, O, S):
+    import torch
+    zp_gemm_case(iq, O, S, 64, 512, 40, seed=3, x_scale=0.0)
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    r = O.quantize(w, "int4zp", "block")
+    q = iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "int4zp", "block", 16, 256,
+                     to_device(r["shifts"]))
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda:0")
+    assert iq.zp_gemm(q, x).shape == (16, 0)
+
+
+def test_zp_gemm_full_size_sampled(iq, O, S):
+    """The c5 weight matrix (28672 x 8192, asymmetric INT4 from the oracle)
+    against 256 tokens of BF16 activations; rows sampled for the oracle."""
+    import torch
+    wx = S.make("c5")
+    r = O.quantize(wx, "int4zp", "block", want_xhat=False, threads=THREADS)
+    n0, K = 28672, 8192
+    n1 = 256
+    x = S.make("c2", nrows=n1)                                  # BF16 activations [256, 8192]
+    q = iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "int4zp", "block", n0, K,
+                     to_device(r["shifts"]))
+    z = iq.zp_gemm(q, to_device(x))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, n0, 997), [n0 - 1, 1, 128, 8191]]))
+    zs = z[torch.from_numpy(rows).cuda()].cpu().numpy()
+    zr, zabs = O.zp_gemm(np.ascontiguousarray(r["codes"][rows]), np.ascontiguousarray(r["scales"][rows]),
+                         np.ascontiguousarray(r["shifts"][rows]), x)
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+    err = np.abs(zs.astype(np.float64) - zr)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    assert np.max(err / bound) < 0.05
