@@ -1988,9 +1988,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
 // an integer in [-15, 15], exact in BF16, so v_mfma_f32_16x16x32_bf16 forms
 // exact products of it and the BF16 activations, summed in FP32; each group's
 // sum is scaled by sc and added with one fma.
-// A workgroup computes a 128 x 128 tile of z with 4 waves of 64 x 64 (4 x 4
-// MFMA tiles of 16 x 16).  Per group the activations stream into LDS by DMA
-// and each thread dequantizes half a weight row into LDS; both tiles keep
+// From 65 tokens on a workgroup computes a 128 x 64 WN tile of z with 2 WN
+// waves of 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per group the activations
+// stream into LDS by DMA and the threads dequantize the weight tile into
+// LDS, WN threads per row; both tiles keep
 // 16-byte slot c of row r at c ^ (r & 15), so the DMA stays coalesced and the
 // fragment reads (16 rows, one 16-byte slot each) hit distinct banks.
 // MFMA operand layout (16x16x32): lane l supplies row l % 16 of A and column
@@ -2012,12 +2013,20 @@ struct ZpGemmArgs {
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-// 8 weights (one code word, element i in bits 4i..4i+3) as BF16 w - sh: the
-// float 2^23 + w minus 2^23 + sh is exactly w - sh, whose BF16 is its upper half.
-__device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float base) {
+// 8 weights (one code word, element i in bits 4i..4i+3) as BF16 w - sh.
+// The even and the odd elements are masked into bytes once, each byte
+// converts to float exactly, and w - sh (an integer in [-15, 15]) is exact
+// in BF16: its upper half.  The asm keeps the compiler from splitting the
+// masks back into one bit-field extract per element.
+__device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float sh) {
+    uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    asm volatile("" : "+v"(ev), "+v"(od));
     float f[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = as_f(0x4B000000u | ((w >> (4 * i)) & 0xFu)) - base;
+    for (int b = 0; b < 4; ++b) {
+        f[2 * b] = (float)((ev >> (8 * b)) & 0xFFu) - sh;
+        f[2 * b + 1] = (float)((od >> (8 * b)) & 0xFFu) - sh;
+    }
     u4v o;
     o.x = __builtin_amdgcn_perm(as_u(f[1]), as_u(f[0]), 0x07060302u);
     o.y = __builtin_amdgcn_perm(as_u(f[3]), as_u(f[2]), 0x07060302u);
@@ -2026,19 +2035,156 @@ __device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float base) {
     return o;
 }
 
-__global__ __launch_bounds__(kThreads) void k_zp_gemm(ZpGemmArgs a) {
+// Few tokens (n1 <= 64): the weights are read once, so HBM and the
+// dequantization bound the time, not the matrix cores.  A workgroup takes a
+// stripe of 32 weight rows and 16 NT tokens; its 4 waves split the group
+// pairs (wave w takes pairs w, w + 4, ...) and dequantize their codes in
+// registers straight into MFMA operands (no LDS tile); the waves' partial sums
+// meet in LDS at the end, added in wave order.
+// The activations are operand A (rows = tokens) and the weights operand B
+// (columns = weight rows): lane l dequantizes weight row 16 f + l % 16 and
+// receives results of that same row (tokens 4 (l / 16) .. + 3), so its fold
+// takes one scale per group.  For MFMA step q of group g lane l holds the k
+// slice g * 128 + 32 (l / 16) + 8 q .. + 8: one code word of its 16-byte code
+// load, and one 16-byte activation load per token tile.
+// The codes, shifts and scales of the next pair load while a pair computes.
+// Rows past n0 and tokens past n1 read row n0 - 1 and token n1 - 1 instead:
+// such lanes only feed outputs that are never stored, and no load is
+// conditional.
+constexpr int kGemvRows = 32;
+
+struct GemvPair {
+    u4v c[2][2];      // codes [fragment][group of the pair]
+    uint32_t sb[2];   // shift byte per fragment
+    float sc[2][2];   // scale [fragment][group]
+};
+
+// With one token tile four waves per SIMD (at most 128 registers, no
+// spills) hold the whole grid of a 28672-row weight matrix at once: no
+// second, mostly idle round.
+template <int NT>
+__global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArgs a) {
+    __shared__ f4v red[4][2][NT][64];
+    const int j0 = (int)blockIdx.x * kGemvRows, t0 = (int)blockIdx.y * 16 * NT;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int rr = lane & 15, h = lane >> 4;
+    const int ng = a.K / 128, np = ng / 2;
+    const uint8_t* crow[2];
+    const uint8_t* srow[2];
+    const float* scrow[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
+        crow[f] = a.codes + j * (a.K / 2) + 16 * h;
+        srow[f] = a.shifts + j * np;
+        scrow[f] = a.scales + j * ng;
+    }
+    const u4v* xr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int64_t tok = min(t0 + 16 * nt + rr, a.n1 - 1);
+        xr[nt] = reinterpret_cast<const u4v*>(a.x + tok * a.K + 32 * h);
+    }
+    auto load_pair = [&](int p, GemvPair& w) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            w.c[f][0] = *reinterpret_cast<const u4v*>(crow[f] + p * 128);
+            w.c[f][1] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + 64);
+            w.sb[f] = srow[f][p];
+            w.sc[f][0] = scrow[f][2 * p];
+            w.sc[f][1] = scrow[f][2 * p + 1];
+        }
+    };
+    f4v acc[2][NT];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    auto compute_pair = [&](int p, const GemvPair& w) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int g = 2 * p + e;
+            u4v xw[NT][4];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xw[nt][q] = xr[nt][g * 16 + q];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const float sh = (float)((w.sb[f] >> (4 * e)) & 0xFu);
+                const uint32_t cw[4] = {w.c[f][e].x, w.c[f][e].y, w.c[f][e].z, w.c[f][e].w};
+                f4v accg[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) accg[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf8v bw = __builtin_bit_cast(bf8v, dequant8_bf16(cw[q], sh));
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        accg[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, xw[nt][q]), bw,
+                                                                           accg[nt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[f][nt][i] = __builtin_fmaf(w.sc[f][e], accg[nt][i], acc[f][nt][i]);
+            }
+        }
+    };
+    // two register sets in turn (a copy between them would wait for the loads)
+    if (wave < np) {
+        GemvPair pa, pb;
+        load_pair(wave, pa);
+        for (int p = wave; p < np; p += 8) {
+            load_pair(min(p + 4, np - 1), pb);
+            compute_pair(p, pa);
+            load_pair(min(p + 8, np - 1), pa);
+            if (p + 4 < np) compute_pair(p + 4, pb);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[wave][f][nt][lane] = acc[f][nt];
+    __syncthreads();
+    // thread (part = t / 64, lane) sums the (fragment, token tile) pairs
+    // congruent to part mod 4 and writes 4 tokens of row j0 + 16 f + lane % 16
+    const int part = t >> 6;
+#pragma unroll
+    for (int fi = 0; fi < 2 * NT; ++fi) {
+        if (fi % 4 != part) continue;
+        const int f = fi / NT, nt = fi % NT;
+        const int j = j0 + 16 * f + rr;
+        if (j >= a.n0) continue;
+        const f4v v = ((red[0][f][nt][lane] + red[1][f][nt][lane]) + red[2][f][nt][lane]) + red[3][f][nt][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + 16 * nt + 4 * h + i;
+            if (tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = v[i];
+        }
+    }
+}
+
+// WN waves along the tokens (a tile of 128 weight rows x 64 WN tokens,
+// 128 WN threads): the dequantization of a weight tile is shared by 64 WN
+// tokens, so a wider tile spends fewer VALU cycles per MFMA.
+template <int WN>
+__global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
+    constexpr int kTN = 64 * WN;             // tokens per tile
+    constexpr int kWords = 4 / WN;           // 16-byte code words per thread and group
     __shared__ u4v sA[kGemmTile * 16];   // weights (w - sh) BF16, swizzled rows of 128
-    __shared__ u4v sB[kGemmTile * 16];   // activations BF16, same layout
+    __shared__ u4v sB[kTN * 16];         // activations BF16, same layout
     __shared__ float sS[kGemmTile];      // the group's scales of the tile's rows
     // Tiles of one XCD slice are consecutive: neighbours share weight rows in that XCD's L2.
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= (uint32_t)(a.tiles_j * a.tiles_n)) return;
     const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
-    const int j0 = jb * kGemmTile, t0 = nb * kGemmTile;
+    const int j0 = jb * kGemmTile, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int ng = a.K / 128;
     const int ldc = a.K / 2;             // code bytes per weight row
     const u4v zero = {0u, 0u, 0u, 0u};
@@ -2047,8 +2193,8 @@ __global__ __launch_bounds__(kThreads) void k_zp_gemm(ZpGemmArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    // this thread's half weight row for the dequantization
-    const int dr = t >> 1, dh = t & 1;
+    // this thread's part of a weight row for the dequantization: 32 kWords codes
+    const int dr = t / WN, dp = t % WN;
     const int dj = j0 + dr;
     for (int g = 0; g < ng; ++g) {
         // activations: wave w copies rows 32 w .. 32 w + 31, four per instruction
@@ -2061,18 +2207,24 @@ __global__ __launch_bounds__(kThreads) void k_zp_gemm(ZpGemmArgs a) {
             if (tok < a.n1) dma_word(a.x + (int64_t)tok * a.K + g * 128 + c * 8, dst);
             else dst[lane] = zero;
         }
-        // weights: 64 codes of row dr, k = g * 128 + dh * 64 ..
+        // weights: codes of row dr, k = g * 128 + dp * 32 kWords ..
         if (dj < a.n0) {
-            const u4v* cp = reinterpret_cast<const u4v*>(a.codes + (int64_t)dj * ldc + g * 64 + dh * 32);
-            const u4v c0 = cp[0], c1 = cp[1];
-            const uint32_t sb = a.shifts[(int64_t)dj * (ng / 2) + (g >> 1)];
-            const float base = 8388608.0f + (float)((sb >> (4 * (g & 1))) & 0xFu);
-            const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const u4v* cp = reinterpret_cast<const u4v*>(a.codes + (int64_t)dj * ldc + g * 64 + dp * 16 * kWords);
+            u4v c[kWords];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sA[dr * 16 + ((dh * 8 + q) ^ (dr & 15))] = dequant8_bf16(cw[q], base);
+            for (int v = 0; v < kWords; ++v) c[v] = cp[v];
+            const uint32_t sb = a.shifts[(int64_t)dj * (ng / 2) + (g >> 1)];
+            const float sh = (float)((sb >> (4 * (g & 1))) & 0xFu);
+#pragma unroll
+            for (int v = 0; v < kWords; ++v) {
+                const uint32_t cw[4] = {c[v].x, c[v].y, c[v].z, c[v].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = dequant8_bf16(cw[q], sh);
+            }
         } else {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sA[dr * 16 + ((dh * 8 + q) ^ (dr & 15))] = zero;
+            for (int q = 0; q < 4 * kWords; ++q) sA[dr * 16 + ((dp * 4 * kWords + q) ^ (dr & 15))] = zero;
         }
         if (t < kGemmTile) sS[t] = (j0 + t < a.n0) ? a.scales[(int64_t)(j0 + t) * ng + g] : 0.f;
         wait_staged();
@@ -2358,17 +2510,31 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Token waves per workgroup: the 256-token tile from 256 tokens on.
+static int gemm_token_waves(int64_t n1) { return n1 >= 256 ? 4 : 2; }
+
 hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     if (g.n0 == 0 || g.n1 == 0) return hipSuccess;
     ZpGemmArgs a;
     a.codes = static_cast<const uint8_t*>(g.codes); a.scales = g.scales; a.shifts = g.shifts;
     a.x = static_cast<const uint16_t*>(g.x); a.z = g.z;
     a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
+    if (g.n1 <= 64) {
+        const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4;
+        const dim3 grid((unsigned)((g.n0 + kGemvRows - 1) / kGemvRows), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
+        if (nt == 1) k_zp_gemv<1><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 2) k_zp_gemv<2><<<grid, kThreads, 0, s>>>(a);
+        else k_zp_gemv<4><<<grid, kThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    const int wn = gemm_token_waves(g.n1);
     a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
-    a.tiles_n = (int32_t)((g.n1 + kGemmTile - 1) / kGemmTile);
+    a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
     a.per_xcd = (int32_t)((tiles + 7) / 8);
-    k_zp_gemm<<<(unsigned)(8 * (int64_t)a.per_xcd), kThreads, 0, s>>>(a);
+    const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
+    if (wn == 4) k_zp_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
+    else k_zp_gemm<2><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

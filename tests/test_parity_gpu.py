@@ -752,8 +752,11 @@ def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
     return err, bound, zr
 
 
+# n1 <= 64: the few-token kernel (1, 2 or 4 token tiles of 16); 65 .. 255: the
+# 128-token tile; from 256: the 256-token tile.
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (32, 1024, 300), (1, 256, 1),
-                                     (257, 768, 129), (384, 2048, 256)])
+                                     (257, 768, 129), (384, 2048, 256), (100, 512, 1), (64, 768, 16),
+                                     (300, 1024, 33), (48, 256, 64), (17, 2048, 50), (40, 512, 1100)])
 def test_zp_gemm_parity(iq, O, S, n0, K, n1):
     err, bound, zr = zp_gemm_case(iq, O, S, n0, K, n1, seed=n0 + K + n1)
     assert np.abs(zr).max() > 0
@@ -772,15 +775,20 @@ def test_zp_gemm_zero_and_empty(iq, O, S):
     assert iq.zp_gemm(q, x).shape == (16, 0)
 
 
-def test_zp_gemm_full_size_sampled(iq, O, S):
-    """The c5 weight matrix (28672 x 8192, asymmetric INT4 from the oracle)
-    against 256 tokens of BF16 activations; rows sampled for the oracle."""
+@pytest.fixture(scope="module")
+def c5_int4zp(O, S):
+    """The c5 weight matrix (28672 x 8192) as asymmetric INT4, by the oracle."""
+    return O.quantize(S.make("c5"), "int4zp", "block", want_xhat=False, threads=THREADS)
+
+
+@pytest.mark.parametrize("n1", [16, 256, 2048])
+def test_zp_gemm_full_size_sampled(iq, O, S, c5_int4zp, n1):
+    """The c5 weights against n1 tokens of BF16 activations (each of the
+    three kernels); rows sampled for the oracle."""
     import torch
-    wx = S.make("c5")
-    r = O.quantize(wx, "int4zp", "block", want_xhat=False, threads=THREADS)
+    r = c5_int4zp
     n0, K = 28672, 8192
-    n1 = 256
-    x = S.make("c2", nrows=n1)                                  # BF16 activations [256, 8192]
+    x = S.make("c2", nrows=n1)                                  # BF16 activations [n1, 8192]
     q = iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "int4zp", "block", n0, K,
                      to_device(r["shifts"]))
     z = iq.zp_gemm(q, to_device(x))
