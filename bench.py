@@ -14,7 +14,9 @@ touched within the last ~400 MB of traffic (the 256 MB memory-side cache
 cannot serve the timed reads).
 
 Also reported: the dominant kernel's HBM roofline, a per-format breakdown
-over the other workloads, a hand-written 16-byte copy kernel as the
+over the other workloads, Puzzle 12's dequantize-then-dot consumer over
+asymmetric INT4 weights at several token counts (against both the HBM and
+the BF16 matrix-core bound), a hand-written 16-byte copy kernel as the
 practical ceiling, and the CPU oracle timed on the host on a bounded sample.
 """
 import argparse
@@ -29,6 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0                # dense BF16 matrix-core peak
+GEMM_TOKENS = (1, 16, 64, 256, 2048)
 METRIC = "quantize GB/s (bytes in+out) and % of MI355X HBM peak, per format"
 NSETS = 4
 
@@ -43,7 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, "
-                         "c4:nvfp4:block:static, copy)")
+                         "c4:nvfp4:block:static, copy, zp_gemm:16)")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per breakdown entry")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of graphs")
     return ap.parse_args()
@@ -315,6 +319,7 @@ def main():
     if not args.no_breakdown:
         extra["copy_ceiling"] = copy_ceiling()
         extra["per_format"] = breakdown(args)
+        extra["zp_gemm"] = gemm_breakdown(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {
@@ -390,12 +395,86 @@ def breakdown(args):
     return res
 
 
+class GemmWorkload:
+    """Puzzle 12's consumer on the c5 weights (28672 x 8192 as asymmetric
+    INT4, quantized on the GPU) over NSETS copies, so that consecutive calls
+    read weights the memory-side cache does not hold."""
+
+    def __init__(self):
+        import int_quantization_amd as iq
+        from synth import synth
+        w = to_device(synth.make("c5"))
+        q = iq.quantize(w, "int4zp", "block", stats=False)
+        del w
+        self.q = [q] + [iq.Quantized(q.codes.clone(), q.scales.clone(), None, None, None, q.fmt, q.gran, q.rows,
+                                     q.cols, q.shifts.clone()) for _ in range(NSETS - 1)]
+        self.n0, self.K = q.rows, q.cols
+
+    def inputs(self, n1):
+        import torch
+        from synth import synth
+        x = to_device(synth.make("c2", nrows=n1))
+        xs = [x] + [x.clone() for _ in range(NSETS - 1)]
+        outs = [torch.empty((self.n0, n1), dtype=torch.float32, device="cuda") for _ in range(NSETS)]
+        return xs, outs
+
+    def call(self, i, xs, outs):
+        import int_quantization_amd as iq
+        iq.zp_gemm(self.q[i % NSETS], xs[i % NSETS], out=outs[i % NSETS])
+
+    def bytes_flops(self, n1):
+        n0, K = self.n0, self.K
+        b = n0 * K // 2 + n0 * (K // 128) * 4 + n0 * (K // 256) + n1 * K * 2 + n0 * n1 * 4
+        return b, 2.0 * n0 * K * n1
+
+
+def gemm_breakdown(args):
+    """Time iq_zp_gemm per token count; each entry gives both bounds (HBM
+    bytes, BF16 MFMA flops) and the fraction of the larger one reached."""
+    import torch
+    stream = torch.cuda.current_stream()
+    G = GemmWorkload()
+    res = {"weights": f"c5 {G.n0}x{G.K} asymmetric INT4 (group 128), {NSETS} copies", "x": "BF16 [n1, K]"}
+    n = 2 * NSETS
+    for n1 in GEMM_TOKENS:
+        xs, outs = G.inputs(n1)
+
+        def body():
+            for k in range(n):
+                G.call(k, xs, outs)
+
+        body()
+        torch.cuda.synchronize()
+        us, _ = time_calls(body, n, not args.eager, args.reps, stream)
+        b, fl = G.bytes_flops(n1)
+        t_hbm = b / (HBM_PEAK_GBS * 1e3)            # microseconds at the HBM peak
+        t_mfma = fl / (MFMA_BF16_PEAK_TFS * 1e6)     # microseconds at the MFMA peak
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        res[f"n1={n1}"] = {"avg_us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                           "TFLOP/s": round(fl / us / 1e6, 1), "bound": bound,
+                           "frac": round(max(t_hbm, t_mfma) / us, 4), "bytes": b, "flops": fl,
+                           "kernel": "k_zp_gemv" if n1 <= 64 else "k_zp_gemm"}
+        del xs, outs
+    del G
+    torch.cuda.empty_cache()
+    return res
+
+
 def only(args):
     """Loop one call type (for rocprofv3 runs)."""
     import torch
     stream = torch.cuda.current_stream()
     if args.only == "copy":
         print(json.dumps({"copy_ceiling": copy_ceiling(args.reps)}), flush=True)
+        return
+    if args.only.startswith("zp_gemm:"):
+        n1 = int(args.only.split(":")[1])
+        G = GemmWorkload()
+        xs, outs = G.inputs(n1)
+        for s in range(args.warmup + args.steps):
+            G.call(s, xs, outs)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "calls": args.warmup + args.steps}), flush=True)
         return
     name, fmt, gran, *rest = args.only.split(":")
     var = rest[0] if rest else ""
