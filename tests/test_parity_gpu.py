@@ -775,6 +775,62 @@ def test_zp_gemm_zero_and_empty(iq, O, S):
     assert iq.zp_gemm(q, x).shape == (16, 0)
 
 
+def zp_gemm_run(iq, O, S, n0, K, x, seed, w_scale=0.02):
+    """Random asymmetric INT4 weights (by the oracle) against the BF16 bits x;
+    returns the GPU result and the oracle's exact sum and sum of |terms|."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n0, K)) * w_scale).astype(np.float32)
+    r = O.quantize(w, "int4zp", "block")
+    q = iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "int4zp", "block", n0, K,
+                     to_device(r["shifts"]))
+    z = iq.zp_gemm(q, to_device(x)).cpu().numpy().astype(np.float64)
+    zr, zabs = O.zp_gemm(r["codes"], r["scales"], r["shifts"], x)
+    return z, zr, zabs
+
+
+@pytest.mark.parametrize("n1", [5, 130, 300])
+def test_zp_gemm_nonfinite_activations(iq, O, S, n1):
+    """NaN and +-Inf activations: the non-finite pattern (NaN, and Inf with its
+    sign; Inf times a zero weight is NaN) equals the oracle's FP64 sums, and
+    every finite output is within the FP32 bound."""
+    n0, K = 70, 512
+    rng = np.random.default_rng(n1)
+    x = S.f32_to_bf16_bits(rng.standard_normal((n1, K)).astype(np.float32))
+    x[0, 7] = 0x7F80                       # +Inf
+    x[1 % n1, 300] = 0xFF80                # -Inf
+    x[2 % n1, 100] = 0x7FC0                # NaN
+    x[3 % n1, 5] = 0x7F80
+    x[3 % n1, 6] = 0xFF80                  # +Inf and -Inf in one group
+    z, zr, zabs = zp_gemm_run(iq, O, S, n0, K, x, seed=11)
+    assert np.array_equal(np.isnan(z), np.isnan(zr))
+    assert np.array_equal(np.isposinf(z), np.isposinf(zr))
+    assert np.array_equal(np.isneginf(z), np.isneginf(zr))
+    fin = np.isfinite(zr)
+    assert (~fin).any() and fin.any()
+    err = np.abs(z[fin] - zr[fin])
+    assert np.all(err <= (K + 2) * 2.0 ** -24 * zabs[fin] + 1e-30)
+
+
+def test_zp_gemm_subnormal_activations(iq, O, S):
+    """A token whose activations are all BF16 subnormals (2^-133 .. 2^-127
+    in magnitude) beside ordinary tokens: its outputs too are within the
+    bound of the exact sums, i.e. the matrix cores keep subnormal inputs.
+    Weights near 1e4 keep those outputs normal FP32 numbers, and every
+    product and partial sum is a multiple of 2^-133, exact in FP32."""
+    n0, K, n1 = 40, 256, 20
+    rng = np.random.default_rng(5)
+    x = S.f32_to_bf16_bits(rng.standard_normal((n1, K)).astype(np.float32))
+    mant = rng.integers(1, 128, size=K).astype(np.uint16)
+    sign = (rng.integers(0, 2, size=K) << 15).astype(np.uint16)
+    x[4] = sign | mant                     # exponent field 0: subnormal
+    z, zr, zabs = zp_gemm_run(iq, O, S, n0, K, x, seed=12, w_scale=1e4)
+    assert np.abs(zr[:, 4]).max() > 1e-36
+    assert np.abs(zr[:, 4]).max() > 0
+    err = np.abs(z - zr)
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-300
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g} (token 4: {np.max(err[:, 4] / bound[:, 4]):.3g})"
+
+
 @pytest.fixture(scope="module")
 def c5_int4zp(O, S):
     """The c5 weight matrix (28672 x 8192) as asymmetric INT4, by the oracle."""
