@@ -36,7 +36,9 @@
  *                      hold 0, sc = (hi - lo)/15 (binary32; an overflowing
  *                      range is clamped to the largest float), sh = RNE(-lo/sc)
  *                      in [0, 15], w = clamp(RNE(x/sc) + sh, 0, 15); groups of
- *                      128, shifts two per byte.
+ *                      128, shifts two per byte;
+ *   FP4 GEMM           a product of two MXFP4 operands multiplies their
+ *                      dequantized values; the oracle forms that sum exactly.
  */
 #include "iq_oracle.h"
 
@@ -568,6 +570,37 @@ int iqo_zp_gemm(const iqo_desc* d, const uint8_t* codes, const float* scales, co
             }
             z[j * n1 + k] = acc;
             if (zabs) zabs[j * n1 + k] = mag;
+        }
+    }
+    return 0;
+}
+
+/* ---- FP4 GEMM over MXFP4 operands ---------------------------------------
+ * [LP] "FP4 / MXFP4 / NVFP4": an MXFP4 value is its E2M1 code times the
+ * block's power-of-two scale 2^(E - 127); a GEMM over two such operands
+ * multiplies those values.  Written out as the definition: one binary64
+ * product per k (exact: at most 2 significant bits each, exponents far
+ * inside the binary64 range) and a binary64 sum in k order. */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t K, int64_t r, int64_t k) {
+    uint8_t byte = codes[r * (K / 2) + k / 2];
+    uint32_t q = (k & 1) ? (uint32_t)(byte >> 4) : (uint32_t)(byte & 0xFu);
+    return (double)iqo_e8m0_value(scales[r * (K / 32) + k / 32]) * (double)iqo_fp_decode(IQO_K_E2M1, q);
+}
+
+int iqo_mx_gemm(const iqo_desc* d, const uint8_t* codes_w, const uint8_t* scales_w, const uint8_t* codes_a,
+                const uint8_t* scales_a, int64_t n1, double* z, double* zabs) {
+    if (iqo_check(d) || d->fmt != IQO_MXFP4 || d->gran != IQO_PER_BLOCK || n1 < 0) return -1;
+    const int64_t K = d->cols;
+    for (int64_t j = 0; j < d->rows; ++j) {
+        for (int64_t t = 0; t < n1; ++t) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double term = mx_value(codes_w, scales_w, K, j, k) * mx_value(codes_a, scales_a, K, t, k);
+                acc += term;
+                mag += fabs(term);
+            }
+            z[j * n1 + t] = acc;
+            if (zabs) zabs[j * n1 + t] = mag;
         }
     }
     return 0;

@@ -103,6 +103,14 @@ int iqo_dequantize_zp(const iqo_desc* d, const uint8_t* codes, const float* scal
  * any rounding bound) are [N0, n1] row-major. */
 int iqo_zp_gemm(const iqo_desc* d, const uint8_t* codes, const float* scales, const uint8_t* shifts,
                 const void* x, int x_dtype, int64_t n1, double* z, double* zabs);
+/* [LP] FP4 GEMM over two MXFP4 operands: z[j, t] = sum_k xw[j, k] * xa[t, k]
+ * with x = 2^(E - 127) * e2m1(code) the dequantized values of the weights
+ * (rows N0 = d->rows, K = d->cols, codes [N0, K/2], E8M0 scales [N0, K/32])
+ * and of the activations (codes [n1, K/2], scales [n1, K/32]).  Every
+ * product is exact in binary64 and the sum runs in k order in binary64; z
+ * and zabs (the sum of |terms|) are [N0, n1] row-major. */
+int iqo_mx_gemm(const iqo_desc* d, const uint8_t* codes_w, const uint8_t* scales_w, const uint8_t* codes_a,
+                const uint8_t* scales_a, int64_t n1, double* z, double* zabs);
 /* Reconstruct xhat ([rows, cols], FP32 or BF16) from codes and scales. */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype);

@@ -88,6 +88,7 @@ def _load():
                                                     ctypes.POINTER(Stats)]),
             "iqo_dequantize_zp": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
             "iqo_zp_gemm": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int, I64, P, P]),
+            "iqo_mx_gemm": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, I64, P, P]),
             "iqo_quantize_static": (ctypes.c_int, [ctypes.POINTER(Desc), P, F, P, P, P, P,
                                                    ctypes.POINTER(Stats)]),
             "iqo_dequantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
@@ -335,4 +336,23 @@ def zp_gemm(codes: np.ndarray, scales: np.ndarray, shifts: np.ndarray, x: np.nda
                              _p(np.ascontiguousarray(shifts)), _p(np.ascontiguousarray(x)), xd, n1, _p(z), _p(zabs))
     if rc:
         raise RuntimeError("iqo_zp_gemm failed")
+    return z, zabs
+
+
+def mx_gemm(codes_w: np.ndarray, scales_w: np.ndarray, codes_a: np.ndarray, scales_a: np.ndarray) -> tuple:
+    """FP4 GEMM over two MXFP4 operands: z[j, t] = sum_k xw[j, k] * xa[t, k]
+    of the dequantized weights (codes [N0, K/2], E8M0 scales [N0, K/32]) and
+    activations (codes [n1, K/2], scales [n1, K/32]); returns (z, zabs) as
+    float64 [N0, n1]."""
+    n0, K = codes_w.shape[0], codes_w.shape[1] * 2
+    n1 = codes_a.shape[0]
+    if codes_a.shape[1] * 2 != K or scales_w.shape != (n0, K // 32) or scales_a.shape != (n1, K // 32):
+        raise ValueError("operand shapes do not match")
+    d = Desc(FORMATS["mxfp4"], GRANS["block"], F32, n0, K, K, 0)
+    z = np.zeros((n0, n1), dtype=np.float64)
+    zabs = np.zeros((n0, n1), dtype=np.float64)
+    rc = _load().iqo_mx_gemm(ctypes.byref(d), _p(np.ascontiguousarray(codes_w)), _p(np.ascontiguousarray(scales_w)),
+                             _p(np.ascontiguousarray(codes_a)), _p(np.ascontiguousarray(scales_a)), n1, _p(z), _p(zabs))
+    if rc:
+        raise RuntimeError("iqo_mx_gemm failed")
     return z, zabs

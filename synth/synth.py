@@ -1,7 +1,8 @@
 """Seeded synthetic inputs (ctypes front end of synth.c).
 
 Holds the workload table: shapes, dtypes, value distributions and outlier
-structure of the five quantization workloads plus the 2 GiB streaming pass.
+structure of the five quantization workloads, the activations that the
+MXFP4 weights of c3 are multiplied with, and the 2 GiB streaming pass.
 Nothing here performs any quantization arithmetic; GPU tests, the bench and
 the CPU oracle all read the same bytes produced here.
 """
@@ -87,6 +88,8 @@ WORKLOADS = {
                    (("nvfp4", "block"),)),
     "c5": Workload("c5", 28672, 8192, BF16, 0.02, AXIS_ROWS, 0.01, 30.0, 5,
                    (("int4", "block"),)),
+    # activations for the c3 weights (K = 4096): the MXFP4 x MXFP4 product
+    "a3": Workload("a3", 8192, 4096, BF16, 1.0, AXIS_COLS, 0.005, 200.0, 7, (("mxfp4", "block"),)),
     "stream": Workload("stream", 65536, 16384, BF16, 1.0, AXIS_COLS, 0.005, 200.0, 6,
                        (("int8", "tensor"), ("e4m3", "tensor"), ("e4m3", "row"), ("e5m2", "row"),
                         ("mxfp4", "block"), ("nvfp4", "block"), ("int4", "block"))),

@@ -780,6 +780,60 @@ def test_p16_zp_gemm_identity_and_bound(O, S):
     assert np.array_equal(zb, z2)
 
 
+# ---- P17: FP4 GEMM over two MXFP4 operands -------------------------------------------
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])       # the page's E2M1 value set
+
+
+def mx_decode_numpy(codes, scales):
+    """Dequantize MXFP4 with numpy alone: element 2t in the low nibble,
+    E2M1 magnitude by the value table, bit 3 the sign, 2^(E - 127) per 32."""
+    lo, hi = codes & 0xF, codes >> 4
+    q = np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1).astype(np.int64)
+    v = E2M1_VALUES[q & 7] * np.where(q & 8, -1.0, 1.0)
+    return v * np.repeat(np.exp2(scales.astype(np.float64) - 127.0), 32, axis=1)
+
+
+def test_p17_mx_gemm_is_the_product_of_dequantized_operands(O, S):
+    """Weights (c3) and activations (a3) quantized to MXFP4 by the oracle:
+    the GEMM equals the float64 product of the operands decoded by numpy
+    from the page's value table, exactly (every partial sum is a dyadic
+    number well inside binary64), and equals the product of the oracle's
+    own x^."""
+    K = 512
+    w = np.ascontiguousarray(S.bf16_to_f32(S.make("c3", nrows=40))[:, :K])
+    a = np.ascontiguousarray(S.bf16_to_f32(S.make("a3", nrows=24))[:, :K])
+    rw, ra = O.quantize(w, "mxfp4", "block"), O.quantize(a, "mxfp4", "block")
+    z, zabs = O.mx_gemm(rw["codes"], rw["scales"], ra["codes"], ra["scales"])
+    want = mx_decode_numpy(rw["codes"], rw["scales"]) @ mx_decode_numpy(ra["codes"], ra["scales"]).T
+    assert np.array_equal(z, want)
+    assert np.array_equal(z, rw["xhat"].astype(np.float64) @ ra["xhat"].astype(np.float64).T)
+    assert np.all(zabs >= np.abs(z)) and np.abs(z).max() > 0
+
+
+def test_p17_mx_gemm_closed_forms(O):
+    """All-ones operands give K; a scale of 2^3 on the weights and -1 codes
+    on the activations give -8 K; a single nonzero pair gives its product."""
+    n0, n1, K = 3, 5, 256
+    ones_c = np.full((n0, K // 2), 0x22, dtype=np.uint8)             # E2M1 code 2 = 1.0 in both nibbles
+    unit = np.full((n0, K // 32), 127, dtype=np.uint8)
+    a_c = np.full((n1, K // 2), 0x22, dtype=np.uint8)
+    a_s = np.full((n1, K // 32), 127, dtype=np.uint8)
+    z, _ = O.mx_gemm(ones_c, unit, a_c, a_s)
+    assert np.all(z == K)
+    z, zabs = O.mx_gemm(ones_c, unit + 3, np.full((n1, K // 2), 0xAA, dtype=np.uint8), a_s)   # code 0xA = -1.0
+    assert np.all(z == -8.0 * K) and np.all(zabs == 8.0 * K)
+    wc = np.zeros((n0, K // 2), dtype=np.uint8)
+    ac = np.zeros((n1, K // 2), dtype=np.uint8)
+    wc[1, 100] = 0x70                    # element 201 of row 1: 6.0
+    ac[4, 100] = 0xD0                    # element 201 of token 4: -3.0
+    ws = unit.copy()
+    ws[1, 201 // 32] = 125               # 2^-2
+    z, _ = O.mx_gemm(wc, ws, ac, a_s)
+    want = np.zeros((n0, n1))
+    want[1, 4] = 6.0 * 0.25 * -3.0
+    assert np.array_equal(z, want)
+
+
 # ---- P14: statistics by brute force ------------------------------------------------
 @pytest.mark.parametrize("fmt,gran,cfg", [("e4m3", "row", "c2"), ("e5m2", "row", "c2"),
                                           ("int8", "tensor", "c1"), ("mxfp4", "block", "c3"),
