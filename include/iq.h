@@ -222,6 +222,27 @@ size_t iq_shifts_bytes(const iq_desc* d);
 iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, const uint8_t* shifts,
                      const void* x, int32_t x_dtype, int64_t n1, float* z, hipStream_t stream);
 
+/*
+ * FP4 GEMM over two MXFP4 operands (low-precision post, section "FP4 /
+ * MXFP4 / NVFP4": an MXFP4 value is its E2M1 code times the block scale
+ * 2^(E - 127), one E8M0 byte per 32 elements):
+ *   z[j, t] = sum_k xw[j, k] * xa[t, k]
+ * with the weights described by d (IQ_MXFP4, IQ_PER_BLOCK; N0 = d->rows,
+ * K = d->cols) and n1 activation rows of the same K, both laid out as
+ * iq_quantize writes MXFP4 (codes [rows, K/2], element 2t in the low
+ * nibble; scales [rows, K/32] E8M0 bytes).
+ *   z       output float32 [N0, n1] row-major, 4-byte aligned
+ * The matrix cores form every product exactly (with its two block scales)
+ * and sum in FP32: |z - exact| <= (K + 2) * 2^-24 * sum_k |xw xa|.
+ * K must be a multiple of 128 (IQ_EINVAL); codes 16-byte aligned, scales
+ * 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits
+ * (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is legal and writes nothing.
+ * d->in_dtype and d->ld_in are ignored.  No workspace; inputs are not
+ * modified.
+ */
+iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w, const void* codes_a,
+                     const void* scales_a, int64_t n1, float* z, hipStream_t stream);
+
 const char* iq_status_str(iq_status s);
 int iq_abi_version(void);
 

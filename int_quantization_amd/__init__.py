@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.iq_shifts_bytes.restype, L.iq_shifts_bytes.argtypes = S, [D]
     L.iq_zp_gemm.restype = ctypes.c_int
     L.iq_zp_gemm.argtypes = [D, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P]
+    L.iq_mx_gemm.restype = ctypes.c_int
+    L.iq_mx_gemm.argtypes = [D, P, P, P, P, ctypes.c_int64, P, P]
     L.iq_dequantize.restype = ctypes.c_int
     L.iq_dequantize.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
     L.iq_amax.restype = ctypes.c_int
@@ -144,6 +146,11 @@ def iq_shifts_bytes(d: IQDesc) -> int:
 def iq_zp_gemm(d: IQDesc, codes: int, scales: int, shifts: int, x: int, x_dtype: int, n1: int, z: int,
                stream: int | None) -> int:
     return load_library().iq_zp_gemm(ctypes.byref(d), codes, scales, shifts, x, x_dtype, n1, z, stream)
+
+
+def iq_mx_gemm(d: IQDesc, codes_w: int, scales_w: int, codes_a: int, scales_a: int, n1: int, z: int,
+               stream: int | None) -> int:
+    return load_library().iq_mx_gemm(ctypes.byref(d), codes_w, scales_w, codes_a, scales_a, n1, z, stream)
 
 
 def iq_dequantize(d: IQDesc, codes: int, scales: int, global_scale: int | None, xhat: int,
@@ -324,4 +331,23 @@ def zp_gemm(q: "Quantized", x, out=None, stream=None):
     st = iq_zp_gemm(d, q.codes.data_ptr(), q.scales.data_ptr(), q.shifts.data_ptr(), x.data_ptr(), IQ_BF16, n1,
                     out.data_ptr(), _stream(stream))
     _check(st, "iq_zp_gemm")
+    return out
+
+
+def mx_gemm(qw: "Quantized", qa: "Quantized", out=None, stream=None):
+    """FP4 GEMM z[j, t] = sum_k xw[j, k] xa[t, k] of two MXFP4 operands (from
+    quantize(..., "mxfp4", "block")), weights qw [N0, K] and activations
+    qa [n1, K]; returns z float32 [N0, n1]."""
+    torch = _torch()
+    if qw.fmt != "mxfp4" or qa.fmt != "mxfp4":
+        raise ValueError("mx_gemm needs two MXFP4 operands")
+    if qa.cols != qw.cols:
+        raise ValueError("operands disagree on K")
+    n1 = qa.rows
+    if out is None:
+        out = torch.empty((qw.rows, n1), dtype=torch.float32, device=qw.codes.device)
+    d = make_desc("mxfp4", "block", qw.rows, qw.cols)
+    st = iq_mx_gemm(d, qw.codes.data_ptr(), qw.scales.data_ptr(), qa.codes.data_ptr(), qa.scales.data_ptr(), n1,
+                    out.data_ptr(), _stream(stream))
+    _check(st, "iq_mx_gemm")
     return out

@@ -241,6 +241,25 @@ iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, c
     return from_hip(iqk::launch_zp_gemm(g, stream));
 }
 
+iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w, const void* codes_a,
+                     const void* scales_a, int64_t n1, float* z, hipStream_t stream) {
+    iq_status st = check_shape(d, false);
+    if (st != IQ_OK) return st;
+    if (d->fmt != IQ_MXFP4 || d->gran != IQ_PER_BLOCK || n1 < 0) return IQ_EINVAL;
+    if (d->cols % 128) return IQ_EINVAL;
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if (d->rows > lim || d->cols > lim || n1 > lim) return IQ_EUNSUPPORTED;
+    if (d->rows == 0 || d->cols == 0 || n1 == 0) return IQ_OK;
+    if (!codes_w || !scales_w || !codes_a || !scales_a || !z) return IQ_EINVAL;
+    if (!aligned(codes_w, 16) || !aligned(codes_a, 16) || !aligned(scales_w, 4) || !aligned(scales_a, 4) ||
+        !aligned(z, 4))
+        return IQ_EALIGN;
+    iqk::MxGemmLaunch g;
+    g.codes_w = codes_w; g.scales_w = scales_w; g.codes_a = codes_a; g.scales_a = scales_a; g.z = z;
+    g.n0 = d->rows; g.n1 = n1; g.K = d->cols;
+    return from_hip(iqk::launch_mx_gemm(g, stream));
+}
+
 iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace, hipStream_t stream) {
     if (!d) return IQ_EINVAL;
     if (!is_bf16_or_f32(d->in_dtype)) return IQ_EINVAL;

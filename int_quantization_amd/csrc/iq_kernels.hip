@@ -2278,6 +2278,160 @@ __global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// FP4 GEMM over two MXFP4 operands on gfx950's block-scaled matrix cores:
+//   z[j, t] = sum_k xw[j, k] * xa[t, k],  x = 2^(E - 127) * e2m1(code)
+// (low-precision post, "FP4 / MXFP4 / NVFP4": the MXFP4 value of a code).
+// v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands takes, per lane, 32
+// codes (16 bytes) of row l % 16 at k block l / 16 of a 128-deep step, and
+// one E8M0 scale byte for exactly those 32: the MXFP4 storage layout itself
+// (16 contiguous code bytes and one scale byte per block).  The products
+// are exact and summed in FP32, so no dequantization or per-block fold runs
+// on the VALU.
+// A workgroup computes a 128 x 128 tile of z with 4 waves of 64 x 64 (4 x 4
+// MFMA tiles).  Per pair of k steps the codes of both operands (16 KB
+// each) and their scale words (one 32-bit word of 4 E8M0 bytes per row and
+// step) are staged through registers into a double-buffered LDS tile: pair
+// p + 2 loads into registers while pair p computes, and is written to LDS
+// during pair p + 1 after that pair's first operands have been read.
+// (Direct global-to-LDS copies measured about 3x slower here.)  One
+// LDS-only barrier per pair: it must not wait for the register loads in
+// flight.  Code rows are 8 slots of 16 bytes, slot s of row r at s ^ (r & 7),
+// so the 8 lanes of each read phase hit 8 distinct 16-byte bank groups.  Rows past n0 and tokens past n1 read a clamped valid
+// index: they feed only outputs that are never stored.
+// ---------------------------------------------------------------------------
+struct MxGemmArgs {
+    const uint8_t* codes_w;    // [n0, K / 2]
+    const uint8_t* scales_w;   // [n0, K / 32]
+    const uint8_t* codes_a;    // [n1, K / 2]
+    const uint8_t* scales_a;   // [n1, K / 32]
+    float* z;                  // [n0, n1]
+    int32_t n0, n1, K;
+    int32_t tiles_j, tiles_n, per_xcd;
+};
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// One thread's share of a pair of k steps: 4 + 4 code words (a full
+// 128-byte line per row and wave instruction) and the two scale words of
+// one row.
+struct MxStage {
+    u4v w[4], x[4];
+    uint32_t s0, s1;
+};
+
+__global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
+    constexpr int T = 128;
+    __shared__ u4v sW[2][T * 8], sA[2][T * 8];            // codes of two steps, 128 bytes per row
+    __shared__ uint32_t sWs[2][T * 2], sAs[2][T * 2];     // two scale words per row
+    const uint32_t b = blockIdx.x;
+    const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
+    if (idx >= (uint32_t)(a.tiles_j * a.tiles_n)) return;
+    const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
+    const int j0 = jb * T, t0 = nb * T;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nks = a.K / 128, nit = (nks + 1) / 2;
+    const int64_t cstride = a.K / 2, sstride = a.K / 32;
+    // staging: thread t moves 16-byte slot t & 7 of code rows t / 8 + 32 i
+    // (i = 0..3) of both operands, and the scale words of row t & 127 of the
+    // weights (t < 128) or the activations (t >= 128)
+    const int r0 = t >> 3, slot = t & 7;
+    const uint8_t* gw[4];
+    const uint8_t* gx[4];
+    int lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 32 * i;
+        gw[i] = a.codes_w + (int64_t)min(j0 + row, a.n0 - 1) * cstride + slot * 16;
+        gx[i] = a.codes_a + (int64_t)min(t0 + row, a.n1 - 1) * cstride + slot * 16;
+        lw[i] = row * 8 + (slot ^ (row & 7));
+    }
+    const int srow = t & 127;
+    const uint8_t* gs = t < 128 ? a.scales_w + (int64_t)min(j0 + srow, a.n0 - 1) * sstride
+                                : a.scales_a + (int64_t)min(t0 + srow, a.n1 - 1) * sstride;
+    // step pair it covers steps 2 it and 2 it + 1 (the latter absent when
+    // nks is odd and it is the last pair: nothing past a row is read)
+    auto load_stage = [&](int it, MxStage& r) {
+        const bool both = 2 * it + 1 < nks;
+        if (both || slot < 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                r.w[i] = *reinterpret_cast<const u4v*>(gw[i] + it * 128);
+                r.x[i] = *reinterpret_cast<const u4v*>(gx[i] + it * 128);
+            }
+        }
+        r.s0 = *reinterpret_cast<const uint32_t*>(gs + it * 8);
+        if (both) r.s1 = *reinterpret_cast<const uint32_t*>(gs + it * 8 + 4);
+    };
+    auto store_stage = [&](const MxStage& r, int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sW[buf][lw[i]] = r.w[i];
+            sA[buf][lw[i]] = r.x[i];
+        }
+        uint32_t* sd = t < 128 ? &sWs[buf][2 * srow] : &sAs[buf][2 * srow];
+        sd[0] = r.s0;
+        sd[1] = r.s1;
+    };
+    const int kb = lane >> 4;                 // this lane's 32-k block of a step
+    f4v acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    auto mfma_step = [&](int buf, int half) {
+        v8i af[4], bf[4];
+        int sa[4], sb[4];
+        const int sl = half * 4 + kb;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = wm * 64 + m * 16 + (lane & 15);
+            const u4v c = sW[buf][r * 8 + (sl ^ (r & 7))];
+            af[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+            sa[m] = (int)((sWs[buf][2 * r + half] >> (8 * kb)) & 0xFFu);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = wn * 64 + m * 16 + (lane & 15);
+            const u4v c = sA[buf][r * 8 + (sl ^ (r & 7))];
+            bf[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+            sb[m] = (int)((sAs[buf][2 * r + half] >> (8 * kb)) & 0xFFu);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], bf[nt], acc[mt][nt], 4, 4, 0,
+                                                                               sa[mt], 0, sb[nt]);
+    };
+    MxStage ra = {}, rb = {};
+    load_stage(0, ra);
+    if (nit > 1) load_stage(1, rb);
+    store_stage(ra, 0);
+    // registers: rb holds pair it + 1, then receives pair it + 2
+    for (int it = 0; it < nit; ++it) {
+        const int buf = it & 1;
+        lds_barrier();                        // pair it is in LDS; pair it - 1's buffer is free
+        mfma_step(buf, 0);
+        if (it + 1 < nit) store_stage(rb, buf ^ 1);
+        if (it + 2 < nit) load_stage(it + 2, rb);
+        if (2 * it + 1 < nks) mfma_step(buf, 1);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
+                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side helpers.
 // ---------------------------------------------------------------------------
 int ilog2_exact(uint32_t v) {
@@ -2535,6 +2689,21 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
     if (wn == 4) k_zp_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
     else k_zp_gemm<2><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
+    if (g.n0 == 0 || g.n1 == 0) return hipSuccess;
+    MxGemmArgs a;
+    a.codes_w = static_cast<const uint8_t*>(g.codes_w); a.scales_w = static_cast<const uint8_t*>(g.scales_w);
+    a.codes_a = static_cast<const uint8_t*>(g.codes_a); a.scales_a = static_cast<const uint8_t*>(g.scales_a);
+    a.z = g.z;
+    a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
+    a.tiles_j = (int32_t)((g.n0 + 127) / 128);
+    a.tiles_n = (int32_t)((g.n1 + 127) / 128);
+    const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
+    a.per_xcd = (int32_t)((tiles + 7) / 8);
+    k_mx_gemm<<<(unsigned)(8 * (int64_t)a.per_xcd), kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -84,10 +84,22 @@ struct ZpGemmLaunch {
     int64_t n0, n1, K;
 };
 
+// FP4 GEMM: z [n0, n1] = MXFP4 weights [n0, K] times MXFP4 activations
+// [n1, K], transposed (codes K/2 bytes and E8M0 scales K/32 bytes per row).
+struct MxGemmLaunch {
+    const void* codes_w;
+    const void* scales_w;
+    const void* codes_a;
+    const void* scales_a;
+    float* z;
+    int64_t n0, n1, K;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t stream);
+hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t stream);
 hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, const void* x,
                        float* amax_out, void* workspace, hipStream_t stream);
 

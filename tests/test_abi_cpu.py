@@ -227,6 +227,28 @@ def test_zp_gemm_argument_errors(iq):
     assert g(iq.make_desc("int4zp", "block", 0, 512), x=None, z=None) == iq.IQ_OK
 
 
+def test_mx_gemm_argument_errors(iq):
+    """The FP4 GEMM: MXFP4 block descriptors only, K a multiple of 128,
+    alignment of codes (16 B), scales and z (4 B), empty shapes."""
+    E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
+    d = iq.make_desc("mxfp4", "block", 64, 512)
+
+    def g(d, cw=FAKE, sw=FAKE, ca=FAKE, sa=FAKE, n1=32, z=FAKE):
+        return iq.iq_mx_gemm(d, cw, sw, ca, sa, n1, z, None)
+    assert g(iq.make_desc("nvfp4", "block", 64, 512)) == E
+    assert g(iq.make_desc("mxfp4", "block", 64, 480)) == E          # K % 128 != 0
+    assert g(d, n1=-1) == E
+    for kw in ("cw", "sw", "ca", "sa", "z"):
+        assert g(d, **{kw: None}) == E, kw
+    assert g(d, cw=FAKE + 8) == A
+    assert g(d, ca=FAKE + 4) == A
+    assert g(d, sw=FAKE + 2) == A
+    assert g(d, sa=FAKE + 1) == A
+    assert g(d, z=FAKE + 2) == A
+    assert g(d, n1=0, ca=None, sa=None, z=None) == iq.IQ_OK         # nothing to do: no launch
+    assert g(iq.make_desc("mxfp4", "block", 0, 512), z=None) == iq.IQ_OK
+
+
 def test_dequantize_and_amax_argument_errors(iq):
     E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
     d = iq.make_desc("nvfp4", "block", 4, 256)

@@ -857,3 +857,70 @@ def test_zp_gemm_full_size_sampled(iq, O, S, c5_int4zp, n1):
     err = np.abs(zs.astype(np.float64) - zr)
     assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
     assert np.max(err / bound) < 0.05
+
+
+# ---- FP4 GEMM over two MXFP4 operands on the block-scaled matrix cores -------------
+def mx_operand(O, S, rows, K, seed, sigma, outlier_axis):
+    x = S.fill(rows, K, S.F32, sigma=sigma, outlier_axis=outlier_axis, outlier_frac=0.02, outlier_factor=30.0,
+               seed=seed, ld=K)
+    r = O.quantize(x, "mxfp4", "block", want_xhat=False)
+    return r
+
+
+def mx_gpu(iq, r, rows, K):
+    return iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "mxfp4", "block", rows, K)
+
+
+@pytest.mark.parametrize("n0,K,n1", [(128, 128, 128), (200, 256, 75), (1, 128, 1), (257, 384, 129),
+                                     (384, 1024, 256), (64, 512, 1100), (33, 4096, 40)])
+def test_mx_gemm_parity(iq, O, S, n0, K, n1):
+    """Weights and activations quantized to MXFP4 by the oracle; the GPU
+    product against the oracle's exact sum, within the FP32 bound."""
+    rw = mx_operand(O, S, n0, K, seed=n0 + K, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    ra = mx_operand(O, S, n1, K, seed=n1 + 3 * K, sigma=1.0, outlier_axis=S.AXIS_COLS)
+    z = iq.mx_gemm(mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, n1, K)).cpu().numpy().astype(np.float64)
+    zr, zabs = O.mx_gemm(rw["codes"], rw["scales"], ra["codes"], ra["scales"])
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+    err = np.abs(z - zr)
+    assert np.all(err <= bound), f"{n0}x{K}x{n1}: max err/bound {np.max(err / bound):.3g}"
+    assert np.abs(zr).max() > 0
+    assert np.max(err / bound) < 0.05
+
+
+def test_mx_gemm_zero_and_empty(iq, O, S):
+    import torch
+    n0, K = 64, 256
+    rw = mx_operand(O, S, n0, K, seed=9, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    ra = O.quantize(np.zeros((40, K), dtype=np.float32), "mxfp4", "block", want_xhat=False)
+    z = iq.mx_gemm(mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, 40, K)).cpu().numpy()
+    assert np.all(z == 0)
+    empty = iq.Quantized(torch.zeros((0, K // 2), dtype=torch.uint8, device="cuda:0"),
+                         torch.zeros((0, K // 32), dtype=torch.uint8, device="cuda:0"), None, None, None,
+                         "mxfp4", "block", 0, K)
+    assert iq.mx_gemm(mx_gpu(iq, rw, n0, K), empty).shape == (n0, 0)
+
+
+@pytest.fixture(scope="module")
+def c3_mxfp4(O, S):
+    """The c3 weight matrix (14336 x 4096) as MXFP4, by the oracle."""
+    return O.quantize(S.make("c3"), "mxfp4", "block", want_xhat=False, threads=THREADS)
+
+
+@pytest.mark.parametrize("n1", [16, 2048])
+def test_mx_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
+    """The c3 weights against n1 tokens of the a3 activations (both MXFP4
+    from the oracle); rows sampled for the oracle."""
+    import torch
+    rw = c3_mxfp4
+    n0, K = 14336, 4096
+    ra = O.quantize(S.make("a3", nrows=n1), "mxfp4", "block", want_xhat=False, threads=THREADS)
+    z = iq.mx_gemm(mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, n1, K))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, n0, 997), [n0 - 1, 1, 128, 8191]]))
+    zs = z[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    zr, zabs = O.mx_gemm(np.ascontiguousarray(rw["codes"][rows]), np.ascontiguousarray(rw["scales"][rows]),
+                         ra["codes"], ra["scales"])
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+    err = np.abs(zs - zr)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    assert np.max(err / bound) < 0.05
