@@ -16,7 +16,8 @@ cannot serve the timed reads).
 Also reported: the dominant kernel's HBM roofline, a per-format breakdown
 over the other workloads, Puzzle 12's dequantize-then-dot consumer over
 asymmetric INT4 weights at several token counts (against both the HBM and
-the BF16 matrix-core bound), a hand-written 16-byte copy kernel as the
+the BF16 matrix-core bound), the FP4 GEMM over two MXFP4 operands on the
+block-scaled matrix cores, a hand-written 16-byte copy kernel as the
 practical ceiling, and the CPU oracle timed on the host on a bounded sample.
 """
 import argparse
@@ -32,7 +33,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0                # dense BF16 matrix-core peak
+MFMA_FP4_PEAK_TFS = 10100.0                # dense FP4 matrix-core peak
 GEMM_TOKENS = (1, 16, 64, 256, 2048)
+MX_GEMM_TOKENS = (16, 256, 2048, 8192)
 METRIC = "quantize GB/s (bytes in+out) and % of MI355X HBM peak, per format"
 NSETS = 4
 
@@ -47,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, "
-                         "c4:nvfp4:block:static, copy, zp_gemm:16)")
+                         "c4:nvfp4:block:static, copy, zp_gemm:16, mx_gemm:2048)")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per breakdown entry")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of graphs")
     return ap.parse_args()
@@ -320,6 +323,7 @@ def main():
         extra["copy_ceiling"] = copy_ceiling()
         extra["per_format"] = breakdown(args)
         extra["zp_gemm"] = gemm_breakdown(args)
+        extra["mx_gemm"] = mx_gemm_breakdown(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {
@@ -460,12 +464,92 @@ def gemm_breakdown(args):
     return res
 
 
+class MxGemmWorkload:
+    """FP4 GEMM over two MXFP4 operands: the c3 weights (14336 x 4096,
+    quantized on the GPU) over NSETS copies, and the a3 activations quantized
+    on the GPU."""
+
+    def __init__(self):
+        import int_quantization_amd as iq
+        from synth import synth
+        w = to_device(synth.make("c3"))
+        q = iq.quantize(w, "mxfp4", "block", stats=False)
+        del w
+        self.q = [q] + [iq.Quantized(q.codes.clone(), q.scales.clone(), None, None, None, q.fmt, q.gran, q.rows,
+                                     q.cols) for _ in range(NSETS - 1)]
+        self.n0, self.K = q.rows, q.cols
+
+    def inputs(self, n1):
+        import torch
+        import int_quantization_amd as iq
+        from synth import synth
+        x = to_device(synth.make("a3", nrows=n1))
+        qa = iq.quantize(x, "mxfp4", "block", stats=False)
+        outs = [torch.empty((self.n0, n1), dtype=torch.float32, device="cuda") for _ in range(NSETS)]
+        return x, qa, outs
+
+    def call(self, i, qa, outs):
+        import int_quantization_amd as iq
+        iq.mx_gemm(self.q[i % NSETS], qa, out=outs[i % NSETS])
+
+    def bytes_flops(self, n1):
+        n0, K = self.n0, self.K
+        b = (n0 + n1) * (K // 2 + K // 32) + n0 * n1 * 4
+        return b, 2.0 * n0 * K * n1
+
+
+def mx_gemm_breakdown(args):
+    """Time iq_mx_gemm per token count against both bounds (HBM bytes, FP4
+    matrix-core flops), and the MXFP4 quantize of those activations."""
+    import torch
+    import int_quantization_amd as iq
+    stream = torch.cuda.current_stream()
+    G = MxGemmWorkload()
+    res = {"weights": f"c3 {G.n0}x{G.K} MXFP4, {NSETS} copies", "activations": "a3 BF16 [n1, 4096] -> MXFP4"}
+    n = 2 * NSETS
+    for n1 in MX_GEMM_TOKENS:
+        x, qa, outs = G.inputs(n1)
+
+        def body():
+            for k in range(n):
+                G.call(k, qa, outs)
+
+        def quant():
+            for k in range(n):
+                iq.quantize(x, "mxfp4", "block", stats=False, out=qa)
+
+        body()
+        torch.cuda.synchronize()
+        us, _ = time_calls(body, n, not args.eager, args.reps, stream)
+        uq, _ = time_calls(quant, n, not args.eager, args.reps, stream)
+        b, fl = G.bytes_flops(n1)
+        t_hbm = b / (HBM_PEAK_GBS * 1e3)
+        t_mfma = fl / (MFMA_FP4_PEAK_TFS * 1e6)
+        res[f"n1={n1}"] = {"avg_us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                           "TFLOP/s": round(fl / us / 1e6, 1), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                           "frac": round(max(t_hbm, t_mfma) / us, 4), "bytes": b, "flops": fl,
+                           "activation_quantize_us": round(uq, 2), "kernel": "k_mx_gemm"}
+        del x, qa, outs
+    del G
+    torch.cuda.empty_cache()
+    return res
+
+
 def only(args):
     """Loop one call type (for rocprofv3 runs)."""
     import torch
     stream = torch.cuda.current_stream()
     if args.only == "copy":
         print(json.dumps({"copy_ceiling": copy_ceiling(args.reps)}), flush=True)
+        return
+    if args.only.startswith("mx_gemm:"):
+        n1 = int(args.only.split(":")[1])
+        G = MxGemmWorkload()
+        _, qa, outs = G.inputs(n1)
+        for s in range(args.warmup + args.steps):
+            G.call(s, qa, outs)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "calls": args.warmup + args.steps}), flush=True)
         return
     if args.only.startswith("zp_gemm:"):
         n1 = int(args.only.split(":")[1])
