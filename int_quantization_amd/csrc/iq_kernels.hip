@@ -2431,6 +2431,121 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
         }
 }
 
+// Few tokens (n1 <= 64) for the FP4 GEMM: the weights stream once, so HBM
+// bounds the call.  A workgroup takes 32 weight rows and 16 NT tokens (16
+// rows per workgroup measured slower from 16 tokens on); its 4 waves split the
+// pairs of k steps (wave w takes pairs w, w + 4, ...) and load the MFMA
+// operands straight from memory into registers (no LDS tile); the waves'
+// partial sums meet in LDS at the end, added in wave order.  The
+// activations are operand A (rows = tokens) and the weights operand B
+// (columns = weight rows): lane l loads weight row 16 f + l % 16 and
+// receives results of that row for tokens 4 (l / 16) .. + 3.  The weights of
+// the next pair load while a pair computes (two register sets in turn).
+// Rows past n0 and tokens past n1 read a clamped valid index; a pair past
+// the last step (odd step count) reads nothing beyond a row.
+struct MxGemvPair {
+    u4v c[2][2];          // weight codes [fragment][step of the pair]
+    uint32_t s[2][2];     // weight scale words [fragment][step]
+};
+
+template <int NT>
+__global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
+    __shared__ f4v red[4][2][NT][64];
+    const int j0 = (int)blockIdx.x * 32, t0 = (int)blockIdx.y * 16 * NT;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int rr = lane & 15, h = lane >> 4;
+    const int nks = a.K / 128, np = (nks + 1) / 2;
+    const int64_t cstride = a.K / 2, sstride = a.K / 32;
+    const uint8_t* cw[2];
+    const uint8_t* sw[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
+        cw[f] = a.codes_w + j * cstride + 16 * h;
+        sw[f] = a.scales_w + j * sstride;
+    }
+    const uint8_t* cx[NT];
+    const uint8_t* sx[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int64_t tok = min(t0 + 16 * nt + rr, a.n1 - 1);
+        cx[nt] = a.codes_a + tok * cstride + 16 * h;
+        sx[nt] = a.scales_a + tok * sstride;
+    }
+    auto load_pair = [&](int p, MxGemvPair& w) {
+        const bool both = 2 * p + 1 < nks;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            w.c[f][0] = *reinterpret_cast<const u4v*>(cw[f] + p * 128);
+            w.s[f][0] = *reinterpret_cast<const uint32_t*>(sw[f] + p * 8);
+            if (both) {
+                w.c[f][1] = *reinterpret_cast<const u4v*>(cw[f] + p * 128 + 64);
+                w.s[f][1] = *reinterpret_cast<const uint32_t*>(sw[f] + p * 8 + 4);
+            }
+        }
+    };
+    f4v acc[2][NT];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    auto compute_pair = [&](int p, const MxGemvPair& w) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int ks = 2 * p + e;
+            if (ks >= nks) break;
+            v8i xa[NT];
+            int xs[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const u4v c = *reinterpret_cast<const u4v*>(cx[nt] + ks * 64);
+                xa[nt] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+                xs[nt] = (int)((*reinterpret_cast<const uint32_t*>(sx[nt] + ks * 4) >> (8 * h)) & 0xFFu);
+            }
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const u4v c = w.c[f][e];
+                const v8i wb = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+                const int ws = (int)((w.s[f][e] >> (8 * h)) & 0xFFu);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[f][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa[nt], wb, acc[f][nt], 4, 4, 0,
+                                                                                   xs[nt], 0, ws);
+            }
+        }
+    };
+    if (wave < np) {
+        MxGemvPair pa = {}, pb = {};
+        load_pair(wave, pa);
+        for (int p = wave; p < np; p += 8) {
+            load_pair(min(p + 4, np - 1), pb);
+            compute_pair(p, pa);
+            load_pair(min(p + 8, np - 1), pa);
+            if (p + 4 < np) compute_pair(p + 4, pb);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[wave][f][nt][lane] = acc[f][nt];
+    __syncthreads();
+    const int part = t >> 6;
+#pragma unroll
+    for (int fi = 0; fi < 2 * NT; ++fi) {
+        if (fi % 4 != part) continue;
+        const int f = fi / NT, nt = fi % NT;
+        const int j = j0 + 16 * f + rr;
+        if (j >= a.n0) continue;
+        const f4v v = ((red[0][f][nt][lane] + red[1][f][nt][lane]) + red[2][f][nt][lane]) + red[3][f][nt][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + 16 * nt + 4 * h + i;
+            if (tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = v[i];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side helpers.
 // ---------------------------------------------------------------------------
@@ -2699,6 +2814,14 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
     a.codes_a = static_cast<const uint8_t*>(g.codes_a); a.scales_a = static_cast<const uint8_t*>(g.scales_a);
     a.z = g.z;
     a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
+    if (g.n1 <= 64) {
+        const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4;
+        const dim3 grid((unsigned)((g.n0 + 31) / 32), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
+        if (nt == 1) k_mx_gemv<1><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 2) k_mx_gemv<2><<<grid, kThreads, 0, s>>>(a);
+        else k_mx_gemv<4><<<grid, kThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
     a.tiles_j = (int32_t)((g.n0 + 127) / 128);
     a.tiles_n = (int32_t)((g.n1 + 127) / 128);
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
