@@ -528,7 +528,8 @@ def mx_gemm_breakdown(args):
         res[f"n1={n1}"] = {"avg_us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
                            "TFLOP/s": round(fl / us / 1e6, 1), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
                            "frac": round(max(t_hbm, t_mfma) / us, 4), "bytes": b, "flops": fl,
-                           "activation_quantize_us": round(uq, 2), "kernel": "k_mx_gemm"}
+                           "activation_quantize_us": round(uq, 2),
+                           "kernel": "k_mx_gemv" if n1 <= 64 else "k_mx_gemm"}
         del x, qa, outs
     del G
     torch.cuda.empty_cache()

@@ -871,8 +871,11 @@ def mx_gpu(iq, r, rows, K):
     return iq.Quantized(to_device(r["codes"]), to_device(r["scales"]), None, None, None, "mxfp4", "block", rows, K)
 
 
+# n1 <= 64: the few-token kernel (1, 2 or 4 token tiles of 16); above, the
+# 128 x 128 tiles.  Odd step counts (K / 128) exercise the last half pair.
 @pytest.mark.parametrize("n0,K,n1", [(128, 128, 128), (200, 256, 75), (1, 128, 1), (257, 384, 129),
-                                     (384, 1024, 256), (64, 512, 1100), (33, 4096, 40)])
+                                     (384, 1024, 256), (64, 512, 1100), (33, 4096, 40), (50, 640, 24),
+                                     (70, 2048, 64)])
 def test_mx_gemm_parity(iq, O, S, n0, K, n1):
     """Weights and activations quantized to MXFP4 by the oracle; the GPU
     product against the oracle's exact sum, within the FP32 bound."""
