@@ -2287,16 +2287,16 @@ __global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
 // (16 contiguous code bytes and one scale byte per block).  The products
 // are exact and summed in FP32, so no dequantization or per-block fold runs
 // on the VALU.
-// A workgroup computes a 128 x 128 tile of z with 4 waves of 64 x 64 (4 x 4
-// MFMA tiles).  Per pair of k steps the codes of both operands (16 KB
-// each) and their scale words (one 32-bit word of 4 E8M0 bytes per row and
-// step) are staged through registers into a double-buffered LDS tile: pair
-// p + 2 loads into registers while pair p computes, and is written to LDS
-// during pair p + 1 after that pair's first operands have been read.
-// (Direct global-to-LDS copies measured about 3x slower here.)  One
-// LDS-only barrier per pair: it must not wait for the register loads in
-// flight.  Code rows are 8 slots of 16 bytes, slot s of row r at s ^ (r & 7),
-// so the 8 lanes of each read phase hit 8 distinct 16-byte bank groups.  Rows past n0 and tokens past n1 read a clamped valid
+// A workgroup computes a 128 x TN tile of z with 2 x 2 waves.  Per k step
+// the codes of both operands (64 bytes per row) and their scale words (one
+// 32-bit word of 4 E8M0 bytes per row) are staged through registers into a
+// double-buffered LDS tile: step k + 2 loads into registers while step k
+// computes, and is written to LDS during step k + 1 after that step's
+// operands have been read.  (Direct global-to-LDS copies measured about 3x
+// slower here.)  One LDS-only barrier per step: it must not wait for the
+// register loads in flight.  Code rows are 4 slots of 16 bytes, slot s of
+// row r at s ^ ((r >> 1) & 3), so the 8 lanes of each read phase hit 8
+// distinct 16-byte bank groups.  Rows past n0 and tokens past n1 read a clamped valid
 // index: they feed only outputs that are never stored.
 // ---------------------------------------------------------------------------
 struct MxGemmArgs {
@@ -2311,112 +2311,107 @@ struct MxGemmArgs {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// One thread's share of a pair of k steps: 4 + 4 code words (a full
-// 128-byte line per row and wave instruction) and the two scale words of
-// one row.
+// One thread's share of a k step: 2 + TN / 64 code words and up to two
+// scale words (weights row t for t < 128, activations row t for t < TN).
+template <int TN>
 struct MxStage {
-    u4v w[4], x[4];
-    uint32_t s0, s1;
+    u4v w[2], x[TN / 64];
+    uint32_t sw, sx;
 };
 
+// TN = 128 or 256 tokens per tile; each wave computes 64 weight rows x TN / 2
+// tokens, so the wider tile reads 12 KB of LDS per 32 MFMAs instead of 8 KB
+// per 16 (it pays from about a thousand tokens on).
+template <int TN>
 __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
-    constexpr int T = 128;
-    __shared__ u4v sW[2][T * 8], sA[2][T * 8];            // codes of two steps, 128 bytes per row
-    __shared__ uint32_t sWs[2][T * 2], sAs[2][T * 2];     // two scale words per row
+    constexpr int TM = 128, NX = TN / 64, NB = TN / 32;
+    __shared__ u4v sW[2][TM * 4], sA[2][TN * 4];          // codes, 64 bytes per row
+    __shared__ uint32_t sWs[2][TM], sAs[2][TN];           // scale words, 4 E8M0 bytes per row
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= (uint32_t)(a.tiles_j * a.tiles_n)) return;
     const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
-    const int j0 = jb * T, t0 = nb * T;
+    const int j0 = jb * TM, t0 = nb * TN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int nks = a.K / 128, nit = (nks + 1) / 2;
+    const int nks = a.K / 128;
     const int64_t cstride = a.K / 2, sstride = a.K / 32;
-    // staging: thread t moves 16-byte slot t & 7 of code rows t / 8 + 32 i
-    // (i = 0..3) of both operands, and the scale words of row t & 127 of the
-    // weights (t < 128) or the activations (t >= 128)
-    const int r0 = t >> 3, slot = t & 7;
-    const uint8_t* gw[4];
-    const uint8_t* gx[4];
-    int lw[4];
+    // staging: thread t moves 16-byte slot t & 3 of weight rows t / 4 + 64 i
+    // (i < 2) and activation rows t / 4 + 64 i (i < 4), and the scale words
+    // of weight row t (t < 128) and activation row t
+    const int r0 = t >> 2, slot = t & 3;
+    const uint8_t* gw[2];
+    const uint8_t* gx[NX];
+    int lw[2], lx[NX];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = r0 + 32 * i;
+    for (int i = 0; i < 2; ++i) {
+        const int row = r0 + 64 * i;
         gw[i] = a.codes_w + (int64_t)min(j0 + row, a.n0 - 1) * cstride + slot * 16;
-        gx[i] = a.codes_a + (int64_t)min(t0 + row, a.n1 - 1) * cstride + slot * 16;
-        lw[i] = row * 8 + (slot ^ (row & 7));
+        lw[i] = row * 4 + (slot ^ ((row >> 1) & 3));
     }
-    const int srow = t & 127;
-    const uint8_t* gs = t < 128 ? a.scales_w + (int64_t)min(j0 + srow, a.n0 - 1) * sstride
-                                : a.scales_a + (int64_t)min(t0 + srow, a.n1 - 1) * sstride;
-    // step pair it covers steps 2 it and 2 it + 1 (the latter absent when
-    // nks is odd and it is the last pair: nothing past a row is read)
-    auto load_stage = [&](int it, MxStage& r) {
-        const bool both = 2 * it + 1 < nks;
-        if (both || slot < 4) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                r.w[i] = *reinterpret_cast<const u4v*>(gw[i] + it * 128);
-                r.x[i] = *reinterpret_cast<const u4v*>(gx[i] + it * 128);
-            }
-        }
-        r.s0 = *reinterpret_cast<const uint32_t*>(gs + it * 8);
-        if (both) r.s1 = *reinterpret_cast<const uint32_t*>(gs + it * 8 + 4);
+    for (int i = 0; i < NX; ++i) {
+        const int row = r0 + 64 * i;
+        gx[i] = a.codes_a + (int64_t)min(t0 + row, a.n1 - 1) * cstride + slot * 16;
+        lx[i] = row * 4 + (slot ^ ((row >> 1) & 3));
+    }
+    const uint8_t* gsw = a.scales_w + (int64_t)min(j0 + (t & 127), a.n0 - 1) * sstride;
+    const uint8_t* gsx = a.scales_a + (int64_t)min(t0 + (t % TN), a.n1 - 1) * sstride;
+    auto load_stage = [&](int ks, MxStage<TN>& r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) r.w[i] = *reinterpret_cast<const u4v*>(gw[i] + ks * 64);
+#pragma unroll
+        for (int i = 0; i < NX; ++i) r.x[i] = *reinterpret_cast<const u4v*>(gx[i] + ks * 64);
+        if (t < TM) r.sw = *reinterpret_cast<const uint32_t*>(gsw + ks * 4);
+        if (t < TN) r.sx = *reinterpret_cast<const uint32_t*>(gsx + ks * 4);
     };
-    auto store_stage = [&](const MxStage& r, int buf) {
+    auto store_stage = [&](const MxStage<TN>& r, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sW[buf][lw[i]] = r.w[i];
-            sA[buf][lw[i]] = r.x[i];
-        }
-        uint32_t* sd = t < 128 ? &sWs[buf][2 * srow] : &sAs[buf][2 * srow];
-        sd[0] = r.s0;
-        sd[1] = r.s1;
+        for (int i = 0; i < 2; ++i) sW[buf][lw[i]] = r.w[i];
+#pragma unroll
+        for (int i = 0; i < NX; ++i) sA[buf][lx[i]] = r.x[i];
+        if (t < TM) sWs[buf][t] = r.sw;
+        if (t < TN) sAs[buf][t] = r.sx;
     };
     const int kb = lane >> 4;                 // this lane's 32-k block of a step
-    f4v acc[4][4];
+    f4v acc[4][NB];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    auto mfma_step = [&](int buf, int half) {
-        v8i af[4], bf[4];
-        int sa[4], sb[4];
-        const int sl = half * 4 + kb;
+        for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    MxStage<TN> ra = {}, rb = {};
+    load_stage(0, ra);
+    if (nks > 1) load_stage(1, rb);
+    store_stage(ra, 0);
+    // registers: rb holds step ks + 1, then receives step ks + 2
+    for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        lds_barrier();                        // step ks is in LDS; step ks - 1's buffer is free
+        v8i af[4], bf[NB];
+        int sa[4], sb[NB];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int r = wm * 64 + m * 16 + (lane & 15);
-            const u4v c = sW[buf][r * 8 + (sl ^ (r & 7))];
+            const u4v c = sW[buf][r * 4 + (kb ^ ((r >> 1) & 3))];
             af[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-            sa[m] = (int)((sWs[buf][2 * r + half] >> (8 * kb)) & 0xFFu);
+            sa[m] = (int)((sWs[buf][r] >> (8 * kb)) & 0xFFu);
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = wn * 64 + m * 16 + (lane & 15);
-            const u4v c = sA[buf][r * 8 + (sl ^ (r & 7))];
+        for (int m = 0; m < NB; ++m) {
+            const int r = wn * (TN / 2) + m * 16 + (lane & 15);
+            const u4v c = sA[buf][r * 4 + (kb ^ ((r >> 1) & 3))];
             bf[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-            sb[m] = (int)((sAs[buf][2 * r + half] >> (8 * kb)) & 0xFFu);
+            sb[m] = (int)((sAs[buf][r] >> (8 * kb)) & 0xFFu);
         }
+        if (ks + 1 < nks) store_stage(rb, buf ^ 1);
+        if (ks + 2 < nks) load_stage(ks + 2, rb);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < NB; ++nt)
                 acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], bf[nt], acc[mt][nt], 4, 4, 0,
                                                                                sa[mt], 0, sb[nt]);
-    };
-    MxStage ra = {}, rb = {};
-    load_stage(0, ra);
-    if (nit > 1) load_stage(1, rb);
-    store_stage(ra, 0);
-    // registers: rb holds pair it + 1, then receives pair it + 2
-    for (int it = 0; it < nit; ++it) {
-        const int buf = it & 1;
-        lds_barrier();                        // pair it is in LDS; pair it - 1's buffer is free
-        mfma_step(buf, 0);
-        if (it + 1 < nit) store_stage(rb, buf ^ 1);
-        if (it + 2 < nit) load_stage(it + 2, rb);
-        if (2 * it + 1 < nks) mfma_step(buf, 1);
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -2424,8 +2419,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
+            for (int nt = 0; nt < NB; ++nt) {
+                const int tok = t0 + wn * (TN / 2) + nt * 16 + (lane & 15);
                 if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
             }
         }
@@ -2822,11 +2817,14 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
         else k_mx_gemv<4><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
+    const int tn = g.n1 >= 1024 ? 256 : 128;
     a.tiles_j = (int32_t)((g.n0 + 127) / 128);
-    a.tiles_n = (int32_t)((g.n1 + 127) / 128);
+    a.tiles_n = (int32_t)((g.n1 + tn - 1) / tn);
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
     a.per_xcd = (int32_t)((tiles + 7) / 8);
-    k_mx_gemm<<<(unsigned)(8 * (int64_t)a.per_xcd), kThreads, 0, s>>>(a);
+    const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
+    if (tn == 256) k_mx_gemm<256><<<grid, kThreads, 0, s>>>(a);
+    else k_mx_gemm<128><<<grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
