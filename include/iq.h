@@ -216,7 +216,8 @@ size_t iq_shifts_bytes(const iq_desc* d);
  *           summed in FP32; each group's sum is scaled by sc with one fma.
  * Accuracy: |z - exact| <= (K + 2) * 2^-24 * sum_l |sc (w - sh) y|.
  * d->in_dtype and d->ld_in are ignored; codes and x 16-byte aligned.
- * N0, n1 and K must fit 31 bits (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is
+ * N0, n1 and K must fit 31 bits, and (N0/128)(n1/128) output tiles must
+ * stay below 2^31 (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is
  * legal and writes nothing.  No workspace.
  */
 iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, const uint8_t* shifts,
@@ -235,8 +236,8 @@ iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, c
  * The matrix cores form every product exactly (with its two block scales)
  * and sum in FP32: |z - exact| <= (K + 2) * 2^-24 * sum_k |xw xa|.
  * K must be a multiple of 128 (IQ_EINVAL); codes 16-byte aligned, scales
- * 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits
- * (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is legal and writes nothing.
+ * 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits, and
+ * (N0/128)(n1/128) output tiles must stay below 2^31 (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is legal and writes nothing.
  * d->in_dtype and d->ld_in are ignored.  No workspace; inputs are not
  * modified.
  */

@@ -232,6 +232,7 @@ iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, c
     if (x_dtype != IQ_BF16) return IQ_EUNSUPPORTED;
     const int64_t lim = ((int64_t)1 << 31) - 1;
     if (d->rows > lim || d->cols > lim || n1 > lim) return IQ_EUNSUPPORTED;
+    if (((d->rows + 127) / 128) * ((n1 + 127) / 128) > lim - 64) return IQ_EUNSUPPORTED;   // one launch's grid
     if (d->rows == 0 || d->cols == 0 || n1 == 0) return IQ_OK;
     if (!codes || !scales || !shifts || !x || !z) return IQ_EINVAL;
     if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(scales, 4) || !aligned(z, 4)) return IQ_EALIGN;
@@ -249,6 +250,7 @@ iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w
     if (d->cols % 128) return IQ_EINVAL;
     const int64_t lim = ((int64_t)1 << 31) - 1;
     if (d->rows > lim || d->cols > lim || n1 > lim) return IQ_EUNSUPPORTED;
+    if (((d->rows + 127) / 128) * ((n1 + 127) / 128) > lim - 64) return IQ_EUNSUPPORTED;   // one launch's grid
     if (d->rows == 0 || d->cols == 0 || n1 == 0) return IQ_OK;
     if (!codes_w || !scales_w || !codes_a || !scales_a || !z) return IQ_EINVAL;
     if (!aligned(codes_w, 16) || !aligned(codes_a, 16) || !aligned(scales_w, 4) || !aligned(scales_a, 4) ||

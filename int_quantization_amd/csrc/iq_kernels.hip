@@ -2008,6 +2008,7 @@ struct ZpGemmArgs {
     float* z;                // [n0, n1]
     int32_t n0, n1, K;
     int32_t tiles_j, tiles_n, per_xcd;   // tile grid, tiles per XCD slice
+    uint32_t tiles;                      // tiles_j * tiles_n (checked on the host)
 };
 
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
@@ -2179,7 +2180,7 @@ __global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
     // Tiles of one XCD slice are consecutive: neighbours share weight rows in that XCD's L2.
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
-    if (idx >= (uint32_t)(a.tiles_j * a.tiles_n)) return;
+    if (idx >= a.tiles) return;
     const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
     const int j0 = jb * kGemmTile, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
@@ -2307,6 +2308,7 @@ struct MxGemmArgs {
     float* z;                  // [n0, n1]
     int32_t n0, n1, K;
     int32_t tiles_j, tiles_n, per_xcd;
+    uint32_t tiles;            // tiles_j * tiles_n (checked on the host)
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -2329,7 +2331,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
     __shared__ uint32_t sWs[2][TM], sAs[2][TN];           // scale words, 4 E8M0 bytes per row
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
-    if (idx >= (uint32_t)(a.tiles_j * a.tiles_n)) return;
+    if (idx >= a.tiles) return;
     const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
     const int j0 = jb * TM, t0 = nb * TN;
     const int t = threadIdx.x, lane = t & 63;
@@ -2774,6 +2776,9 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Tiles of one launch: the grid (8 XCD slices, rounded up) stays below 2^31.
+constexpr int64_t kMaxGemmTiles = ((int64_t)1 << 31) - 64;
+
 // Token waves per workgroup: the 256-token tile from 256 tokens on.
 static int gemm_token_waves(int64_t n1) { return n1 >= 256 ? 4 : 2; }
 
@@ -2795,6 +2800,8 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
+    if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+    a.tiles = (uint32_t)tiles;
     a.per_xcd = (int32_t)((tiles + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
     if (wn == 4) k_zp_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
@@ -2821,6 +2828,8 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
     a.tiles_j = (int32_t)((g.n0 + 127) / 128);
     a.tiles_n = (int32_t)((g.n1 + tn - 1) / tn);
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
+    if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+    a.tiles = (uint32_t)tiles;
     a.per_xcd = (int32_t)((tiles + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
     if (tn == 256) k_mx_gemm<256><<<grid, kThreads, 0, s>>>(a);

@@ -246,6 +246,8 @@ def test_mx_gemm_argument_errors(iq):
     assert g(d, sa=FAKE + 1) == A
     assert g(d, z=FAKE + 2) == A
     assert g(d, n1=0, ca=None, sa=None, z=None) == iq.IQ_OK         # nothing to do: no launch
+    big = iq.make_desc("mxfp4", "block", (1 << 31) - 1, 512)
+    assert g(big, n1=(1 << 31) - 1) == iq.IQ_EUNSUPPORTED          # more output tiles than one launch holds
     assert g(iq.make_desc("mxfp4", "block", 0, 512), z=None) == iq.IQ_OK
 
 
