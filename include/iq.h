@@ -234,7 +234,9 @@ iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, c
  * nibble; scales [rows, K/32] E8M0 bytes).
  *   z       output float32 [N0, n1] row-major, 4-byte aligned
  * The matrix cores form every product exactly (with its two block scales)
- * and sum in FP32: |z - exact| <= (K + 2) * 2^-24 * sum_k |xw xa|.
+ * and sum in FP32: |z - exact| <= (K + 2) * 2^-24 * sum_k |xw xa|.  A scale
+ * byte of 255 (E8M0 NaN; iq_quantize never writes it) makes every output of
+ * its row or token NaN.
  * K must be a multiple of 128 (IQ_EINVAL); codes 16-byte aligned, scales
  * 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits, and
  * (N0/128)(n1/128) output tiles must stay below 2^31 (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is legal and writes nothing.

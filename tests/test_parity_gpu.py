@@ -903,6 +903,24 @@ def test_mx_gemm_zero_and_empty(iq, O, S):
     assert iq.mx_gemm(mx_gpu(iq, rw, n0, K), empty).shape == (n0, 0)
 
 
+@pytest.mark.parametrize("n1", [24, 300])
+def test_mx_gemm_nan_scale(iq, O, S, n1):
+    """E8M0 byte 255 is NaN: a weight row or a token with such a block scale
+    gives NaN outputs (NaN times zero included), as in the oracle; every
+    other output stays within the FP32 bound."""
+    n0, K = 40, 512
+    rw = mx_operand(O, S, n0, K, seed=21, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    ra = mx_operand(O, S, n1, K, seed=22, sigma=1.0, outlier_axis=S.AXIS_COLS)
+    rw["scales"][3, 2] = 255
+    ra["scales"][5, 0] = 255
+    z = iq.mx_gemm(mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, n1, K)).cpu().numpy().astype(np.float64)
+    zr, zabs = O.mx_gemm(rw["codes"], rw["scales"], ra["codes"], ra["scales"])
+    assert np.isnan(zr[3]).all() and np.isnan(zr[:, 5]).all()
+    assert np.array_equal(np.isnan(z), np.isnan(zr))
+    fin = np.isfinite(zr)
+    assert np.all(np.abs(z[fin] - zr[fin]) <= (K + 2) * 2.0 ** -24 * zabs[fin] + 1e-30)
+
+
 @pytest.fixture(scope="module")
 def c3_mxfp4(O, S):
     """The c3 weight matrix (14336 x 4096) as MXFP4, by the oracle."""
