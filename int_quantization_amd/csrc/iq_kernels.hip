@@ -2436,13 +2436,15 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
 // partial sums meet in LDS at the end, added in wave order.  The
 // activations are operand A (rows = tokens) and the weights operand B
 // (columns = weight rows): lane l loads weight row 16 f + l % 16 and
-// receives results of that row for tokens 4 (l / 16) .. + 3.  The weights of
-// the next pair load while a pair computes (two register sets in turn).
+// receives results of that row for tokens 4 (l / 16) .. + 3.
 // Rows past n0 and tokens past n1 read a clamped valid index; a pair past
 // the last step (odd step count) reads nothing beyond a row.
+template <int NT>
 struct MxGemvPair {
     u4v c[2][2];          // weight codes [fragment][step of the pair]
     uint32_t s[2][2];     // weight scale words [fragment][step]
+    u4v x[2][NT];         // activation codes [step][token tile]
+    uint32_t xs[2][NT];   // activation scale words [step][token tile]
 };
 
 template <int NT>
@@ -2470,15 +2472,20 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
         cx[nt] = a.codes_a + tok * cstride + 16 * h;
         sx[nt] = a.scales_a + tok * sstride;
     }
-    auto load_pair = [&](int p, MxGemvPair& w) {
+    auto load_pair = [&](int p, MxGemvPair<NT>& w) {
         const bool both = 2 * p + 1 < nks;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            w.c[f][0] = *reinterpret_cast<const u4v*>(cw[f] + p * 128);
-            w.s[f][0] = *reinterpret_cast<const uint32_t*>(sw[f] + p * 8);
-            if (both) {
-                w.c[f][1] = *reinterpret_cast<const u4v*>(cw[f] + p * 128 + 64);
-                w.s[f][1] = *reinterpret_cast<const uint32_t*>(sw[f] + p * 8 + 4);
+        for (int e = 0; e < 2; ++e) {
+            if (e == 1 && !both) break;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                w.c[f][e] = *reinterpret_cast<const u4v*>(cw[f] + p * 128 + e * 64);
+                w.s[f][e] = *reinterpret_cast<const uint32_t*>(sw[f] + p * 8 + e * 4);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                w.x[e][nt] = *reinterpret_cast<const u4v*>(cx[nt] + p * 128 + e * 64);
+                w.xs[e][nt] = *reinterpret_cast<const uint32_t*>(sx[nt] + p * 8 + e * 4);
             }
         }
     };
@@ -2487,7 +2494,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
     for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    auto compute_pair = [&](int p, const MxGemvPair& w) {
+    auto compute_pair = [&](int p, const MxGemvPair<NT>& w) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int ks = 2 * p + e;
@@ -2496,9 +2503,9 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
             int xs[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const u4v c = *reinterpret_cast<const u4v*>(cx[nt] + ks * 64);
+                const u4v c = w.x[e][nt];
                 xa[nt] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-                xs[nt] = (int)((*reinterpret_cast<const uint32_t*>(sx[nt] + ks * 4) >> (8 * h)) & 0xFFu);
+                xs[nt] = (int)((w.xs[e][nt] >> (8 * h)) & 0xFFu);
             }
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
@@ -2512,15 +2519,17 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
             }
         }
     };
-    if (wave < np) {
-        MxGemvPair pa = {}, pb = {};
-        load_pair(wave, pa);
-        for (int p = wave; p < np; p += 8) {
-            load_pair(min(p + 4, np - 1), pb);
-            compute_pair(p, pa);
-            load_pair(min(p + 8, np - 1), pa);
-            if (p + 4 < np) compute_pair(p + 4, pb);
-        }
+    // The wave's pairs in chunks of kMxChunk, every load of a chunk issued
+    // before any of its math: enough bytes in flight per CU to stream the
+    // weights at HBM rate when each wave owns only a few pairs.
+    constexpr int kMxChunk = NT == 4 ? 2 : 4;
+    for (int p0 = wave; p0 < np; p0 += 4 * kMxChunk) {
+        MxGemvPair<NT> pr[kMxChunk];
+#pragma unroll
+        for (int c = 0; c < kMxChunk; ++c) load_pair(min(p0 + 4 * c, np - 1), pr[c]);
+#pragma unroll
+        for (int c = 0; c < kMxChunk; ++c)
+            if (p0 + 4 * c < np) compute_pair(p0 + 4 * c, pr[c]);
     }
 #pragma unroll
     for (int f = 0; f < 2; ++f)
