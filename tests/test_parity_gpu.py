@@ -408,6 +408,40 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("n1", [16, 300])
+def test_gemm_graph_replay_matches_eager(iq, O, S, n1):
+    """Both GEMMs (their few-token and their tiled kernels) add in a fixed
+    order, so a captured call replays to the eager call's exact bits, also
+    with eager work in between."""
+    import torch
+    K = 512
+    rzp = O.quantize((S.bf16_to_f32(S.make("c5", nrows=96))[:, :K]).copy(), "int4zp", "block")
+    qzp = iq.Quantized(to_device(rzp["codes"]), to_device(rzp["scales"]), None, None, None, "int4zp", "block",
+                       96, K, to_device(rzp["shifts"]))
+    x = to_device(S.make("c2", nrows=n1)[:, :K].copy())
+    rw = mx_operand(O, S, 96, K, seed=31, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    ra = mx_operand(O, S, n1, K, seed=32, sigma=1.0, outlier_axis=S.AXIS_COLS)
+    qw, qa = mx_gpu(iq, rw, 96, K), mx_gpu(iq, ra, n1, K)
+    want_zp, want_mx = iq.zp_gemm(qzp, x), iq.mx_gemm(qw, qa)
+    torch.cuda.synchronize()
+    want_zp, want_mx = want_zp.cpu(), want_mx.cpu()
+    out_zp = torch.empty((96, n1), dtype=torch.float32, device="cuda:0")
+    out_mx = torch.empty((96, n1), dtype=torch.float32, device="cuda:0")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.zp_gemm(qzp, x, out=out_zp)
+        iq.mx_gemm(qw, qa, out=out_mx)
+    for rep in range(4):
+        out_zp.zero_(); out_mx.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_zp.cpu().view(torch.int32), want_zp.view(torch.int32)), rep
+        assert torch.equal(out_mx.cpu().view(torch.int32), want_mx.view(torch.int32)), rep
+        iq.mx_gemm(qw, qa)                                   # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ---- one workspace across many calls ------------------------------------------------
 def test_workspace_reuse_across_calls(iq, O, S):
     """One workspace serves a sequence of calls with different grids, formats,
