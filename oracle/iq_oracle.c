@@ -606,6 +606,31 @@ int iqo_mx_gemm(const iqo_desc* d, const uint8_t* codes_w, const uint8_t* scales
     return 0;
 }
 
+/* The same weights against unquantized activations: one binary64 product
+ * per k (the MXFP4 value has at most 2 significant bits, a BF16 or FP32
+ * activation at most 24) and a binary64 sum in k order. */
+int iqo_mxw_gemm(const iqo_desc* d, const uint8_t* codes_w, const uint8_t* scales_w, const void* x, int x_dtype,
+                 int64_t n1, double* z, double* zabs) {
+    if (iqo_check(d) || d->fmt != IQO_MXFP4 || d->gran != IQO_PER_BLOCK || n1 < 0) return -1;
+    if (x_dtype != IQO_F32 && x_dtype != IQO_BF16) return -1;
+    const int64_t K = d->cols;
+    for (int64_t j = 0; j < d->rows; ++j) {
+        for (int64_t t = 0; t < n1; ++t) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double y = x_dtype == IQO_F32 ? (double)((const float*)x)[t * K + k]
+                                              : (double)iqo_bf16_to_f32(((const uint16_t*)x)[t * K + k]);
+                double term = mx_value(codes_w, scales_w, K, j, k) * y;
+                acc += term;
+                mag += fabs(term);
+            }
+            z[j * n1 + t] = acc;
+            if (zabs) zabs[j * n1 + t] = mag;
+        }
+    }
+    return 0;
+}
+
 /* ---- dequantization: x^ = s * decode(q), the same products as above ----- */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype) {

@@ -111,6 +111,13 @@ int iqo_zp_gemm(const iqo_desc* d, const uint8_t* codes, const float* scales, co
  * and zabs (the sum of |terms|) are [N0, n1] row-major. */
 int iqo_mx_gemm(const iqo_desc* d, const uint8_t* codes_w, const uint8_t* scales_w, const uint8_t* codes_a,
                 const uint8_t* scales_a, int64_t n1, double* z, double* zabs);
+/* [LP] MXFP4 weights against activations kept in BF16 or FP32:
+ * z[j, t] = sum_k xw[j, k] * y[t, k] with xw the dequantized weights of d
+ * (as for iqo_mx_gemm) and y token-major [n1, K] (x_dtype IQO_F32 or
+ * IQO_BF16).  Exact binary64 products, binary64 sum in k order; z and zabs
+ * [N0, n1] row-major. */
+int iqo_mxw_gemm(const iqo_desc* d, const uint8_t* codes_w, const uint8_t* scales_w, const void* x, int x_dtype,
+                 int64_t n1, double* z, double* zabs);
 /* Reconstruct xhat ([rows, cols], FP32 or BF16) from codes and scales. */
 int iqo_dequantize(const iqo_desc* d, const uint8_t* codes, const void* scales,
                    const float* global_scale, void* xhat, int xhat_dtype);

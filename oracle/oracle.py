@@ -89,6 +89,7 @@ def _load():
             "iqo_dequantize_zp": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
             "iqo_zp_gemm": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int, I64, P, P]),
             "iqo_mx_gemm": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, I64, P, P]),
+            "iqo_mxw_gemm": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, ctypes.c_int, I64, P, P]),
             "iqo_quantize_static": (ctypes.c_int, [ctypes.POINTER(Desc), P, F, P, P, P, P,
                                                    ctypes.POINTER(Stats)]),
             "iqo_dequantize": (ctypes.c_int, [ctypes.POINTER(Desc), P, P, P, P, ctypes.c_int]),
@@ -355,4 +356,23 @@ def mx_gemm(codes_w: np.ndarray, scales_w: np.ndarray, codes_a: np.ndarray, scal
                              _p(np.ascontiguousarray(codes_a)), _p(np.ascontiguousarray(scales_a)), n1, _p(z), _p(zabs))
     if rc:
         raise RuntimeError("iqo_mx_gemm failed")
+    return z, zabs
+
+
+def mxw_gemm(codes_w: np.ndarray, scales_w: np.ndarray, x: np.ndarray) -> tuple:
+    """MXFP4 weights (codes [N0, K/2], E8M0 scales [N0, K/32]) against
+    token-major activations x [n1, K] (float32 or BF16 bits):
+    z[j, t] = sum_k xw[j, k] * x[t, k]; returns (z, zabs) as float64 [N0, n1]."""
+    n0, K = codes_w.shape[0], codes_w.shape[1] * 2
+    n1 = x.shape[0]
+    if x.shape[1] != K or scales_w.shape != (n0, K // 32):
+        raise ValueError("operand shapes do not match")
+    d = Desc(FORMATS["mxfp4"], GRANS["block"], F32, n0, K, K, 0)
+    z = np.zeros((n0, n1), dtype=np.float64)
+    zabs = np.zeros((n0, n1), dtype=np.float64)
+    xd = F32 if x.dtype == np.float32 else BF16
+    rc = _load().iqo_mxw_gemm(ctypes.byref(d), _p(np.ascontiguousarray(codes_w)), _p(np.ascontiguousarray(scales_w)),
+                              _p(np.ascontiguousarray(x)), xd, n1, _p(z), _p(zabs))
+    if rc:
+        raise RuntimeError("iqo_mxw_gemm failed")
     return z, zabs

@@ -834,6 +834,24 @@ def test_p17_mx_gemm_closed_forms(O):
     assert np.array_equal(z, want)
 
 
+def test_p17_mxw_gemm_is_the_product_with_dequantized_weights(O, S):
+    """MXFP4 weights (c3) against BF16 and FP32 activations: the float64
+    product of the numpy-decoded weights with the activations (within the
+    float64 rounding of numpy's own sum order), identity activations return
+    the weights' x^ exactly, and BF16 bits read as their FP32 values."""
+    K = 512
+    w = np.ascontiguousarray(S.bf16_to_f32(S.make("c3", nrows=24))[:, :K])
+    rw = O.quantize(w, "mxfp4", "block")
+    xb = np.ascontiguousarray(S.make("a3", nrows=20)[:, :K])
+    z, zabs = O.mxw_gemm(rw["codes"], rw["scales"], xb)
+    want = mx_decode_numpy(rw["codes"], rw["scales"]) @ S.bf16_to_f32(xb).astype(np.float64).T
+    assert np.all(np.abs(z - want) <= 1e-13 * zabs + 1e-300) and np.abs(z).max() > 0
+    z2, _ = O.mxw_gemm(rw["codes"], rw["scales"], S.bf16_to_f32(xb).astype(np.float32))
+    assert np.array_equal(z, z2)
+    eye, _ = O.mxw_gemm(rw["codes"], rw["scales"], np.eye(K, dtype=np.float32))
+    assert np.array_equal(eye.astype(np.float32), rw["xhat"])
+
+
 # ---- P14: statistics by brute force ------------------------------------------------
 @pytest.mark.parametrize("fmt,gran,cfg", [("e4m3", "row", "c2"), ("e5m2", "row", "c2"),
                                           ("int8", "tensor", "c1"), ("mxfp4", "block", "c3"),
