@@ -246,6 +246,28 @@ iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, c
 iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w, const void* codes_a,
                      const void* scales_a, int64_t n1, float* z, hipStream_t stream);
 
+/*
+ * MXFP4 weights against BF16 activations (low-precision post, section
+ * "FP4 / MXFP4 / NVFP4": the weight values are E2M1 codes times the block
+ * scale 2^(E - 127)):
+ *   z[j, t] = sum_k xw[j, k] * x[t, k]
+ * with the weights described by d (IQ_MXFP4, IQ_PER_BLOCK; N0 = d->rows,
+ * K = d->cols; laid out as iq_quantize writes MXFP4) and x token-major
+ * [n1, K] row-major.
+ *   z       output float32 [N0, n1] row-major, 4-byte aligned
+ *   x_dtype must be IQ_BF16 (IQ_EUNSUPPORTED otherwise).  Each weight is
+ *           exact in BF16, so the BF16 matrix cores form exact products,
+ *           summed in FP32: |z - exact| <= (K + 2) * 2^-24 * sum_k |xw x|.
+ *           A scale byte of 255 (E8M0 NaN) makes its row's outputs NaN.
+ * K must be a multiple of 128 (IQ_EINVAL); codes and x 16-byte aligned,
+ * scales 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits, and
+ * (N0/128)(n1/128) output tiles must stay below 2^31 (IQ_EUNSUPPORTED).
+ * n1 == 0 or N0 == 0 is legal and writes nothing.  d->in_dtype and d->ld_in
+ * are ignored.  No workspace.
+ */
+iq_status iq_mxw_gemm(const iq_desc* d, const void* codes, const void* scales, const void* x, int32_t x_dtype,
+                      int64_t n1, float* z, hipStream_t stream);
+
 const char* iq_status_str(iq_status s);
 int iq_abi_version(void);
 

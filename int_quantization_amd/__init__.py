@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.iq_zp_gemm.argtypes = [D, P, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P]
     L.iq_mx_gemm.restype = ctypes.c_int
     L.iq_mx_gemm.argtypes = [D, P, P, P, P, ctypes.c_int64, P, P]
+    L.iq_mxw_gemm.restype = ctypes.c_int
+    L.iq_mxw_gemm.argtypes = [D, P, P, P, ctypes.c_int32, ctypes.c_int64, P, P]
     L.iq_dequantize.restype = ctypes.c_int
     L.iq_dequantize.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
     L.iq_amax.restype = ctypes.c_int
@@ -151,6 +153,11 @@ def iq_zp_gemm(d: IQDesc, codes: int, scales: int, shifts: int, x: int, x_dtype:
 def iq_mx_gemm(d: IQDesc, codes_w: int, scales_w: int, codes_a: int, scales_a: int, n1: int, z: int,
                stream: int | None) -> int:
     return load_library().iq_mx_gemm(ctypes.byref(d), codes_w, scales_w, codes_a, scales_a, n1, z, stream)
+
+
+def iq_mxw_gemm(d: IQDesc, codes: int, scales: int, x: int, x_dtype: int, n1: int, z: int,
+                stream: int | None) -> int:
+    return load_library().iq_mxw_gemm(ctypes.byref(d), codes, scales, x, x_dtype, n1, z, stream)
 
 
 def iq_dequantize(d: IQDesc, codes: int, scales: int, global_scale: int | None, xhat: int,
@@ -350,4 +357,23 @@ def mx_gemm(qw: "Quantized", qa: "Quantized", out=None, stream=None):
     st = iq_mx_gemm(d, qw.codes.data_ptr(), qw.scales.data_ptr(), qa.codes.data_ptr(), qa.scales.data_ptr(), n1,
                     out.data_ptr(), _stream(stream))
     _check(st, "iq_mx_gemm")
+    return out
+
+
+def mxw_gemm(qw: "Quantized", x, out=None, stream=None):
+    """MXFP4 weights qw [N0, K] (from quantize(..., "mxfp4", "block")) against
+    token-major BF16 activations x [n1, K]: z[j, t] = sum_k xw[j, k] x[t, k];
+    returns z float32 [N0, n1]."""
+    torch = _torch()
+    if qw.fmt != "mxfp4":
+        raise ValueError("mxw_gemm needs MXFP4 weights")
+    if x.dim() != 2 or x.shape[1] != qw.cols or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous BF16 [n1, K] tensor")
+    n1 = x.shape[0]
+    if out is None:
+        out = torch.empty((qw.rows, n1), dtype=torch.float32, device=x.device)
+    d = make_desc("mxfp4", "block", qw.rows, qw.cols)
+    st = iq_mxw_gemm(d, qw.codes.data_ptr(), qw.scales.data_ptr(), x.data_ptr(), IQ_BF16, n1, out.data_ptr(),
+                     _stream(stream))
+    _check(st, "iq_mxw_gemm")
     return out

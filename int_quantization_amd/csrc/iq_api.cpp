@@ -262,6 +262,26 @@ iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w
     return from_hip(iqk::launch_mx_gemm(g, stream));
 }
 
+iq_status iq_mxw_gemm(const iq_desc* d, const void* codes, const void* scales, const void* x, int32_t x_dtype,
+                      int64_t n1, float* z, hipStream_t stream) {
+    iq_status st = check_shape(d, false);
+    if (st != IQ_OK) return st;
+    if (d->fmt != IQ_MXFP4 || d->gran != IQ_PER_BLOCK || n1 < 0) return IQ_EINVAL;
+    if (d->cols % 128) return IQ_EINVAL;
+    if (!is_bf16_or_f32(x_dtype)) return IQ_EINVAL;
+    if (x_dtype != IQ_BF16) return IQ_EUNSUPPORTED;
+    const int64_t lim = ((int64_t)1 << 31) - 1;
+    if (d->rows > lim || d->cols > lim || n1 > lim) return IQ_EUNSUPPORTED;
+    if (((d->rows + 127) / 128) * ((n1 + 127) / 128) > lim - 64) return IQ_EUNSUPPORTED;   // one launch's grid
+    if (d->rows == 0 || d->cols == 0 || n1 == 0) return IQ_OK;
+    if (!codes || !scales || !x || !z) return IQ_EINVAL;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(scales, 4) || !aligned(z, 4)) return IQ_EALIGN;
+    iqk::MxwGemmLaunch g;
+    g.codes = codes; g.scales = scales; g.x = x; g.z = z;
+    g.n0 = d->rows; g.n1 = n1; g.K = d->cols;
+    return from_hip(iqk::launch_mxw_gemm(g, stream));
+}
+
 iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace, hipStream_t stream) {
     if (!d) return IQ_EINVAL;
     if (!is_bf16_or_f32(d->in_dtype)) return IQ_EINVAL;

@@ -2553,6 +2553,247 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 weights against BF16 activations (W4A16):
+//   z[j, t] = sum_k xw[j, k] * x[t, k],  xw = 2^(E - 127) * e2m1(code)
+// (low-precision post, "FP4 / MXFP4 / NVFP4").  A 16-byte code word is one
+// block of 32 (one E8M0 scale); v_cvt_scalef32_pk_bf16_fp4 turns two codes
+// into two BF16 weights scaled by the block's power of two, exactly (an
+// E2M1 value times a power of two has at most 2 significant bits).  The BF16
+// matrix cores then form exact products with the activations and sum in
+// FP32: no per-block fold, and 0.5 VALU instructions per weight.  E8M0 255
+// (NaN) gives NaN weights.  The kernels are the asymmetric INT4 consumer's
+// (LDS tiles from 65 tokens, registers only below) with this dequantization.
+// ---------------------------------------------------------------------------
+struct MxwGemmArgs {
+    const uint8_t* codes;      // [n0, K / 2]
+    const uint8_t* scales;     // [n0, K / 32] E8M0
+    const uint16_t* x;         // [n1, K] BF16
+    float* z;                  // [n0, n1]
+    int32_t n0, n1, K;
+    int32_t tiles_j, tiles_n, per_xcd;
+    uint32_t tiles;            // tiles_j * tiles_n (checked on the host)
+};
+
+// 8 weights of one code word (element 2t in the low nibble of byte t) as
+// BF16 times the block scale sc (a power of two; NaN for E8M0 255).
+__device__ __forceinline__ u4v mx_bf16x8(uint32_t w, float sc, bool nan) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    u4v o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+    if (nan) o = u4v{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    return o;
+}
+__device__ __forceinline__ float e8m0_scale(uint32_t E) {
+    return E ? as_f(E << 23) : as_f(0x00400000u);   // 2^(E - 127); 2^-127 is an FP32 subnormal
+}
+
+template <int WN>
+__global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
+    constexpr int kTN = 64 * WN;             // tokens per tile
+    constexpr int kWords = 4 / WN;           // 16-byte code words (scale blocks) per thread and step
+    constexpr int kX = 8;                    // 16-byte activation words per thread and step
+    __shared__ u4v sA[kGemmTile * 16];   // weights BF16, swizzled rows of 128
+    __shared__ u4v sB[kTN * 16];         // activations BF16, same layout
+    const uint32_t b = blockIdx.x;
+    const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
+    if (idx >= a.tiles) return;
+    const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
+    const int j0 = jb * kGemmTile, t0 = nb * kTN;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int nks = a.K / 128;
+    const int ldc = a.K / 2, lds_ = a.K / 32;
+    f4v acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    // staging: thread t moves 16-byte slot t & 15 of token rows t / 16 + 8 WN i
+    // (i < 8), and the code words of weight row t / WN (blocks dp * kWords ..)
+    const int xr0 = t >> 4, xs = t & 15;
+    const uint16_t* gx[kX];
+    int lx[kX];
+#pragma unroll
+    for (int i = 0; i < kX; ++i) {
+        const int row = xr0 + 8 * WN * i;
+        gx[i] = a.x + (int64_t)min(t0 + row, a.n1 - 1) * a.K + xs * 8;
+        lx[i] = row * 16 + (xs ^ (row & 15));
+    }
+    const int dr = t / WN, dp = t % WN;
+    const int64_t dj = min(j0 + dr, a.n0 - 1);
+    const u4v* gc = reinterpret_cast<const u4v*>(a.codes + dj * ldc + dp * 16 * kWords);
+    const uint8_t* gs = a.scales + dj * lds_ + dp * kWords;
+    u4v rx[kX], rc[kWords];
+    uint32_t rs[kWords];
+    auto load_step = [&](int ks) {
+#pragma unroll
+        for (int i = 0; i < kX; ++i) rx[i] = *reinterpret_cast<const u4v*>(gx[i] + ks * 128);
+#pragma unroll
+        for (int v = 0; v < kWords; ++v) {
+            rc[v] = gc[ks * 4 + v];
+            rs[v] = gs[ks * 4 + v];
+        }
+    };
+    load_step(0);
+    for (int ks = 0; ks < nks; ++ks) {
+        __syncthreads();                     // every wave is done with the previous step's tiles
+#pragma unroll
+        for (int i = 0; i < kX; ++i) sB[lx[i]] = rx[i];
+#pragma unroll
+        for (int v = 0; v < kWords; ++v) {
+            const float sc = e8m0_scale(rs[v]);
+            const uint32_t cw[4] = {rc[v].x, rc[v].y, rc[v].z, rc[v].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = mx_bf16x8(cw[q], sc, rs[v] == 255u);
+        }
+        if (ks + 1 < nks) load_step(ks + 1);     // lands during this step's MFMAs
+        lds_barrier();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int slot = 4 * s + (lane >> 4);
+            bf8v af[4], bfr[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int r = wm * 64 + mt * 16 + (lane & 15);
+                af[mt] = __builtin_bit_cast(bf8v, sA[r * 16 + (slot ^ (r & 15))]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int r = wn * 64 + nt * 16 + (lane & 15);
+                bfr[nt] = __builtin_bit_cast(bf8v, sB[r * 16 + (slot ^ (r & 15))]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
+                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+            }
+        }
+}
+
+// Few tokens (n1 <= 64): the asymmetric INT4 consumer's register-only kernel
+// with this dequantization.  Lane l holds weight row 16 f + l % 16 and, for
+// MFMA step q of 128-deep step g, k = 128 g + 32 (l / 16) + 8 q .. + 8: one
+// word of its 16-byte code load, whose block scale is byte 4 g + l / 16 of
+// the row.  A step past the last one (odd step count) reads nothing.
+struct MxwPair {
+    u4v c[2][2];          // codes [fragment][step of the pair]
+    uint32_t s[2][2];     // the row's 4 scale bytes of the step [fragment][step]
+};
+
+template <int NT>
+__global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmArgs a) {
+    __shared__ f4v red[4][2][NT][64];
+    const int j0 = (int)blockIdx.x * 32, t0 = (int)blockIdx.y * 16 * NT;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int rr = lane & 15, h = lane >> 4;
+    const int nks = a.K / 128, np = (nks + 1) / 2;
+    const uint8_t* crow[2];
+    const uint8_t* srow[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
+        crow[f] = a.codes + j * (a.K / 2) + 16 * h;
+        srow[f] = a.scales + j * (a.K / 32);
+    }
+    const u4v* xr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int64_t tok = min(t0 + 16 * nt + rr, a.n1 - 1);
+        xr[nt] = reinterpret_cast<const u4v*>(a.x + tok * a.K + 32 * h);
+    }
+    auto load_pair = [&](int p, MxwPair& w) {
+        const bool both = 2 * p + 1 < nks;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            if (e == 1 && !both) break;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                w.c[f][e] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + e * 64);
+                w.s[f][e] = *reinterpret_cast<const uint32_t*>(srow[f] + p * 8 + e * 4);
+            }
+        }
+    };
+    f4v acc[2][NT];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    auto compute_pair = [&](int p, const MxwPair& w) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int g = 2 * p + e;
+            if (g >= nks) break;
+            u4v xw[NT][4];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xw[nt][q] = xr[nt][g * 16 + q];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const uint32_t E = (w.s[f][e] >> (8 * h)) & 0xFFu;
+                const float sc = e8m0_scale(E);
+                const uint32_t cw[4] = {w.c[f][e].x, w.c[f][e].y, w.c[f][e].z, w.c[f][e].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf8v bw = __builtin_bit_cast(bf8v, mx_bf16x8(cw[q], sc, E == 255u));
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[f][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, xw[nt][q]), bw,
+                                                                              acc[f][nt], 0, 0, 0);
+                }
+            }
+        }
+    };
+    if (wave < np) {
+        MxwPair pa = {}, pb = {};
+        load_pair(wave, pa);
+        for (int p = wave; p < np; p += 8) {
+            load_pair(min(p + 4, np - 1), pb);
+            compute_pair(p, pa);
+            load_pair(min(p + 8, np - 1), pa);
+            if (p + 4 < np) compute_pair(p + 4, pb);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[wave][f][nt][lane] = acc[f][nt];
+    __syncthreads();
+    const int part = t >> 6;
+#pragma unroll
+    for (int fi = 0; fi < 2 * NT; ++fi) {
+        if (fi % 4 != part) continue;
+        const int f = fi / NT, nt = fi % NT;
+        const int j = j0 + 16 * f + rr;
+        if (j >= a.n0) continue;
+        const f4v v = ((red[0][f][nt][lane] + red[1][f][nt][lane]) + red[2][f][nt][lane]) + red[3][f][nt][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + 16 * nt + 4 * h + i;
+            if (tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = v[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side helpers.
 // ---------------------------------------------------------------------------
 int ilog2_exact(uint32_t v) {
@@ -2843,6 +3084,33 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
     if (tn == 256) k_mx_gemm<256><<<grid, kThreads, 0, s>>>(a);
     else k_mx_gemm<128><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
+    if (g.n0 == 0 || g.n1 == 0) return hipSuccess;
+    MxwGemmArgs a;
+    a.codes = static_cast<const uint8_t*>(g.codes); a.scales = static_cast<const uint8_t*>(g.scales);
+    a.x = static_cast<const uint16_t*>(g.x); a.z = g.z;
+    a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
+    if (g.n1 <= 64) {
+        const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4;
+        const dim3 grid((unsigned)((g.n0 + 31) / 32), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
+        if (nt == 1) k_mxw_gemv<1><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 2) k_mxw_gemv<2><<<grid, kThreads, 0, s>>>(a);
+        else k_mxw_gemv<4><<<grid, kThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    const int wn = gemm_token_waves(g.n1);
+    a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
+    a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
+    const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
+    if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+    a.tiles = (uint32_t)tiles;
+    a.per_xcd = (int32_t)((tiles + 7) / 8);
+    const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
+    if (wn == 4) k_mxw_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
+    else k_mxw_gemm<2><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

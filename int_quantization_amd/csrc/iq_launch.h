@@ -95,11 +95,21 @@ struct MxGemmLaunch {
     int64_t n0, n1, K;
 };
 
+// MXFP4 weights [n0, K] times token-major BF16 activations x [n1, K], transposed.
+struct MxwGemmLaunch {
+    const void* codes;
+    const void* scales;
+    const void* x;
+    float* z;
+    int64_t n0, n1, K;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t stream);
 hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t stream);
+hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t stream);
 hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, const void* x,
                        float* amax_out, void* workspace, hipStream_t stream);
 

@@ -251,6 +251,28 @@ def test_mx_gemm_argument_errors(iq):
     assert g(iq.make_desc("mxfp4", "block", 0, 512), z=None) == iq.IQ_OK
 
 
+def test_mxw_gemm_argument_errors(iq):
+    """MXFP4 weights against BF16 activations: MXFP4 block descriptors only,
+    K a multiple of 128, BF16 activations only, alignment, empty shapes."""
+    E, A, U = iq.IQ_EINVAL, iq.IQ_EALIGN, iq.IQ_EUNSUPPORTED
+    d = iq.make_desc("mxfp4", "block", 64, 512)
+
+    def g(d, codes=FAKE, scales=FAKE, x=FAKE, xdt=1, n1=32, z=FAKE):
+        return iq.iq_mxw_gemm(d, codes, scales, x, xdt, n1, z, None)
+    assert g(iq.make_desc("int4", "block", 64, 512)) == E
+    assert g(iq.make_desc("mxfp4", "block", 64, 480)) == E
+    assert g(d, xdt=0) == U
+    assert g(d, xdt=7) == E
+    assert g(d, n1=-1) == E
+    for kw in ("codes", "scales", "x", "z"):
+        assert g(d, **{kw: None}) == E, kw
+    assert g(d, codes=FAKE + 8) == A
+    assert g(d, x=FAKE + 4) == A
+    assert g(d, scales=FAKE + 2) == A
+    assert g(d, z=FAKE + 2) == A
+    assert g(d, n1=0, x=None, z=None) == iq.IQ_OK
+
+
 def test_dequantize_and_amax_argument_errors(iq):
     E, A = iq.IQ_EINVAL, iq.IQ_EALIGN
     d = iq.make_desc("nvfp4", "block", 4, 256)

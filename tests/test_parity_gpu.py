@@ -410,7 +410,7 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
 
 @pytest.mark.parametrize("n1", [16, 300])
 def test_gemm_graph_replay_matches_eager(iq, O, S, n1):
-    """Both GEMMs (their few-token and their tiled kernels) add in a fixed
+    """The GEMMs (their few-token and their tiled kernels) add in a fixed
     order, so a captured call replays to the eager call's exact bits, also
     with eager work in between."""
     import torch
@@ -422,22 +422,25 @@ def test_gemm_graph_replay_matches_eager(iq, O, S, n1):
     rw = mx_operand(O, S, 96, K, seed=31, sigma=0.02, outlier_axis=S.AXIS_ROWS)
     ra = mx_operand(O, S, n1, K, seed=32, sigma=1.0, outlier_axis=S.AXIS_COLS)
     qw, qa = mx_gpu(iq, rw, 96, K), mx_gpu(iq, ra, n1, K)
-    want_zp, want_mx = iq.zp_gemm(qzp, x), iq.mx_gemm(qw, qa)
+    want_zp, want_mx, want_w = iq.zp_gemm(qzp, x), iq.mx_gemm(qw, qa), iq.mxw_gemm(qw, x)
     torch.cuda.synchronize()
-    want_zp, want_mx = want_zp.cpu(), want_mx.cpu()
+    want_zp, want_mx, want_w = want_zp.cpu(), want_mx.cpu(), want_w.cpu()
     out_zp = torch.empty((96, n1), dtype=torch.float32, device="cuda:0")
     out_mx = torch.empty((96, n1), dtype=torch.float32, device="cuda:0")
+    out_w = torch.empty((96, n1), dtype=torch.float32, device="cuda:0")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         iq.zp_gemm(qzp, x, out=out_zp)
         iq.mx_gemm(qw, qa, out=out_mx)
+        iq.mxw_gemm(qw, x, out=out_w)
     for rep in range(4):
-        out_zp.zero_(); out_mx.zero_()
+        out_zp.zero_(); out_mx.zero_(); out_w.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_zp.cpu().view(torch.int32), want_zp.view(torch.int32)), rep
         assert torch.equal(out_mx.cpu().view(torch.int32), want_mx.view(torch.int32)), rep
+        assert torch.equal(out_w.cpu().view(torch.int32), want_w.view(torch.int32)), rep
         iq.mx_gemm(qw, qa)                                   # eager work between replays
         torch.cuda.synchronize()
 
@@ -975,6 +978,64 @@ def test_mx_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
     zs = z[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     zr, zabs = O.mx_gemm(np.ascontiguousarray(rw["codes"][rows]), np.ascontiguousarray(rw["scales"][rows]),
                          ra["codes"], ra["scales"])
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+    err = np.abs(zs - zr)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    assert np.max(err / bound) < 0.05
+
+
+# ---- MXFP4 weights against BF16 activations (W4A16) ---------------------------------
+def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
+    rw = mx_operand(O, S, n0, K, seed=seed, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    if nan_row is not None:
+        rw["scales"][nan_row, 1] = 255
+    rng = np.random.default_rng(seed + 1)
+    x = S.f32_to_bf16_bits(rng.standard_normal((n1, K)).astype(np.float32))
+    z = iq.mxw_gemm(mx_gpu(iq, rw, n0, K), to_device(x)).cpu().numpy().astype(np.float64)
+    zr, zabs = O.mxw_gemm(rw["codes"], rw["scales"], x)
+    return z, zr, zabs
+
+
+# n1 <= 64: the few-token kernel (1, 2 or 4 token tiles); 65 .. 255: 128-token
+# tiles; from 256: 256-token tiles.  Odd step counts (K / 128) included.
+@pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (257, 384, 129), (40, 512, 300),
+                                     (64, 1024, 1100), (1, 128, 1), (33, 640, 24), (70, 2048, 64), (50, 384, 16)])
+def test_mxw_gemm_parity(iq, O, S, n0, K, n1):
+    z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=n0 + 7 * K + n1)
+    bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+    err = np.abs(z - zr)
+    assert np.all(err <= bound), f"{n0}x{K}x{n1}: max err/bound {np.max(err / bound):.3g}"
+    assert np.abs(zr).max() > 0 and np.max(err / bound) < 0.05
+
+
+@pytest.mark.parametrize("n1", [24, 300])
+def test_mxw_gemm_nan_scale_and_empty(iq, O, S, n1):
+    """E8M0 255 on one weight block: that row's outputs are NaN, as in the
+    oracle; other outputs within the bound; no tokens writes nothing."""
+    import torch
+    n0, K = 40, 512
+    z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=5, nan_row=3)
+    assert np.isnan(zr[3]).all() and np.array_equal(np.isnan(z), np.isnan(zr))
+    fin = np.isfinite(zr)
+    assert np.all(np.abs(z[fin] - zr[fin]) <= (K + 2) * 2.0 ** -24 * zabs[fin] + 1e-30)
+    rw = mx_operand(O, S, n0, K, seed=6, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    x0 = torch.zeros((0, K), dtype=torch.bfloat16, device="cuda:0")
+    assert iq.mxw_gemm(mx_gpu(iq, rw, n0, K), x0).shape == (n0, 0)
+
+
+@pytest.mark.parametrize("n1", [16, 2048])
+def test_mxw_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
+    """The c3 weights (MXFP4 from the oracle) against n1 BF16 tokens of a3;
+    rows sampled for the oracle."""
+    import torch
+    rw = c3_mxfp4
+    n0, K = 14336, 4096
+    x = S.make("a3", nrows=n1)
+    z = iq.mxw_gemm(mx_gpu(iq, rw, n0, K), to_device(x))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, n0, 997), [n0 - 1, 1, 128, 8191]]))
+    zs = z[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    zr, zabs = O.mxw_gemm(np.ascontiguousarray(rw["codes"][rows]), np.ascontiguousarray(rw["scales"][rows]), x)
     bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
     err = np.abs(zs - zr)
     assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
