@@ -1990,10 +1990,11 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
 // sum is scaled by sc and added with one fma.
 // From 65 tokens on a workgroup computes a 128 x 64 WN tile of z with 2 WN
 // waves of 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per group the activations
-// stream into LDS by DMA and the threads dequantize the weight tile into
-// LDS, WN threads per row; both tiles keep
-// 16-byte slot c of row r at c ^ (r & 15), so the DMA stays coalesced and the
-// fragment reads (16 rows, one 16-byte slot each) hit distinct banks.
+// and codes of the next group load into registers during the MFMAs (direct
+// global-to-LDS copies were the bottleneck), then the activations are
+// written and the weights dequantized into LDS, WN threads per row.  Both
+// tiles keep 16-byte slot c of row r at c ^ (r & 15), so the fragment reads
+// (16 rows, one 16-byte slot each) hit distinct banks.
 // MFMA operand layout (16x16x32): lane l supplies row l % 16 of A and column
 // l % 16 of B with the same 8 consecutive k (a fixed slice per l / 16), and
 // receives D[4 (l / 16) + i][l % 16], i = 0..3.
@@ -2171,9 +2172,10 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
 // 128 WN threads): the dequantization of a weight tile is shared by 64 WN
 // tokens, so a wider tile spends fewer VALU cycles per MFMA.
 template <int WN>
-__global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
+__global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
     constexpr int kTN = 64 * WN;             // tokens per tile
     constexpr int kWords = 4 / WN;           // 16-byte code words per thread and group
+    constexpr int kX = 8;                    // 16-byte activation words per thread and group
     __shared__ u4v sA[kGemmTile * 16];   // weights (w - sh) BF16, swizzled rows of 128
     __shared__ u4v sB[kTN * 16];         // activations BF16, same layout
     __shared__ float sS[kGemmTile];      // the group's scales of the tile's rows
@@ -2188,48 +2190,55 @@ __global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
     const int wm = wave / WN, wn = wave % WN;
     const int ng = a.K / 128;
     const int ldc = a.K / 2;             // code bytes per weight row
-    const u4v zero = {0u, 0u, 0u, 0u};
     f4v acc[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    // this thread's part of a weight row for the dequantization: 32 kWords codes
+    // staging: thread t moves 16-byte slot t & 15 of token rows t / 16 + 8 WN i
+    // (i < 8), the codes of weight row t / WN (32 kWords from dp * 32 kWords)
+    // with the row's shift byte, and (t < 128) the scale of row t
+    const int xr0 = t >> 4, xs = t & 15;
+    const uint16_t* gx[kX];
+    int lx[kX];
+#pragma unroll
+    for (int i = 0; i < kX; ++i) {
+        const int row = xr0 + 8 * WN * i;
+        gx[i] = a.x + (int64_t)min(t0 + row, a.n1 - 1) * a.K + xs * 8;
+        lx[i] = row * 16 + (xs ^ (row & 15));
+    }
     const int dr = t / WN, dp = t % WN;
-    const int dj = j0 + dr;
+    const int64_t dj = min(j0 + dr, a.n0 - 1);
+    const u4v* gc = reinterpret_cast<const u4v*>(a.codes + dj * ldc + dp * 16 * kWords);
+    const uint8_t* gsh = a.shifts + dj * (ng / 2);
+    const float* gsc = a.scales + (int64_t)min(j0 + (t & (kGemmTile - 1)), a.n0 - 1) * ng;
+    u4v rx[kX], rc[kWords];
+    uint32_t rsb = 0;
+    float rsc = 0.f;
+    auto load_group = [&](int g) {
+#pragma unroll
+        for (int i = 0; i < kX; ++i) rx[i] = *reinterpret_cast<const u4v*>(gx[i] + g * 128);
+#pragma unroll
+        for (int v = 0; v < kWords; ++v) rc[v] = gc[g * 4 + v];
+        rsb = gsh[g >> 1];
+        if (t < kGemmTile) rsc = gsc[g];
+    };
+    load_group(0);
     for (int g = 0; g < ng; ++g) {
-        // activations: wave w copies rows 32 w .. 32 w + 31, four per instruction
+        __syncthreads();                     // every wave is done with the previous group's tiles
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int row = wave * 32 + q * 4 + (lane >> 4);
-            const int c = (lane & 15) ^ (row & 15);
-            const int tok = t0 + row;
-            u4v* dst = &sB[(wave * 8 + q) * 64];
-            if (tok < a.n1) dma_word(a.x + (int64_t)tok * a.K + g * 128 + c * 8, dst);
-            else dst[lane] = zero;
+        for (int i = 0; i < kX; ++i) sB[lx[i]] = rx[i];
+        const float sh = (float)((rsb >> (4 * (g & 1))) & 0xFu);
+#pragma unroll
+        for (int v = 0; v < kWords; ++v) {
+            const uint32_t cw[4] = {rc[v].x, rc[v].y, rc[v].z, rc[v].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = dequant8_bf16(cw[q], sh);
         }
-        // weights: codes of row dr, k = g * 128 + dp * 32 kWords ..
-        if (dj < a.n0) {
-            const u4v* cp = reinterpret_cast<const u4v*>(a.codes + (int64_t)dj * ldc + g * 64 + dp * 16 * kWords);
-            u4v c[kWords];
-#pragma unroll
-            for (int v = 0; v < kWords; ++v) c[v] = cp[v];
-            const uint32_t sb = a.shifts[(int64_t)dj * (ng / 2) + (g >> 1)];
-            const float sh = (float)((sb >> (4 * (g & 1))) & 0xFu);
-#pragma unroll
-            for (int v = 0; v < kWords; ++v) {
-                const uint32_t cw[4] = {c[v].x, c[v].y, c[v].z, c[v].w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = dequant8_bf16(cw[q], sh);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4 * kWords; ++q) sA[dr * 16 + ((dp * 4 * kWords + q) ^ (dr & 15))] = zero;
-        }
-        if (t < kGemmTile) sS[t] = (j0 + t < a.n0) ? a.scales[(int64_t)(j0 + t) * ng + g] : 0.f;
-        wait_staged();
-        __syncthreads();
+        if (t < kGemmTile) sS[t] = rsc;
+        if (g + 1 < ng) load_group(g + 1);   // lands during this group's MFMAs
+        lds_barrier();
         f4v accg[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -2263,7 +2272,6 @@ __global__ __launch_bounds__(128 * WN) void k_zp_gemm(ZpGemmArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) acc[mt][nt][i] = __builtin_fmaf(sc, accg[mt][nt][i], acc[mt][nt][i]);
             }
-        __syncthreads();   // the next group's copies overwrite the tiles
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
