@@ -17,7 +17,8 @@ Also reported: the dominant kernel's HBM roofline, a per-format breakdown
 over the other workloads, Puzzle 12's dequantize-then-dot consumer over
 asymmetric INT4 weights at several token counts (against both the HBM and
 the BF16 matrix-core bound), the FP4 GEMM over two MXFP4 operands on the
-block-scaled matrix cores, a hand-written 16-byte copy kernel as the
+block-scaled matrix cores, MXFP4 weights against BF16 activations, a
+hand-written 16-byte copy kernel as the
 practical ceiling, and the CPU oracle timed on the host on a bounded sample.
 """
 import argparse
@@ -329,6 +330,7 @@ def main():
         extra["per_format"] = breakdown(args)
         extra["zp_gemm"] = gemm_breakdown(args)
         extra["mx_gemm"] = mx_gemm_breakdown(args)
+        extra["mxw_gemm"] = mxw_gemm_breakdown(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {
@@ -536,6 +538,42 @@ def mx_gemm_breakdown(args):
                            "activation_quantize_us": round(uq, 2),
                            "kernel": "k_mx_gemv" if n1 <= 64 else "k_mx_gemm"}
         del x, qa, outs
+    del G
+    torch.cuda.empty_cache()
+    return res
+
+
+def mxw_gemm_breakdown(args):
+    """Time iq_mxw_gemm (the c3 weights as MXFP4 over NSETS copies against a3
+    activations kept in BF16) per token count against both bounds (HBM
+    bytes, BF16 matrix-core flops)."""
+    import torch
+    import int_quantization_amd as iq
+    from synth import synth
+    stream = torch.cuda.current_stream()
+    G = MxGemmWorkload()
+    res = {"weights": f"c3 {G.n0}x{G.K} MXFP4, {NSETS} copies", "activations": "a3 BF16 [n1, 4096]"}
+    n = 2 * NSETS
+    for n1 in MX_GEMM_TOKENS:
+        x = to_device(synth.make("a3", nrows=n1))
+        outs = [torch.empty((G.n0, n1), dtype=torch.float32, device="cuda") for _ in range(NSETS)]
+
+        def body():
+            for k in range(n):
+                iq.mxw_gemm(G.q[k % NSETS], x, out=outs[k % NSETS])
+
+        body()
+        torch.cuda.synchronize()
+        us, _ = time_calls(body, n, not args.eager, args.reps, stream)
+        b = G.n0 * (G.K // 2 + G.K // 32) + n1 * G.K * 2 + G.n0 * n1 * 4
+        fl = 2.0 * G.n0 * G.K * n1
+        t_hbm = b / (HBM_PEAK_GBS * 1e3)
+        t_mfma = fl / (MFMA_BF16_PEAK_TFS * 1e6)
+        res[f"n1={n1}"] = {"avg_us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
+                           "TFLOP/s": round(fl / us / 1e6, 1), "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+                           "frac": round(max(t_hbm, t_mfma) / us, 4), "bytes": b, "flops": fl,
+                           "kernel": "k_mxw_gemv" if n1 <= 64 else "k_mxw_gemm"}
+        del x, outs
     del G
     torch.cuda.empty_cache()
     return res
