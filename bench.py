@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one call type in a loop (e.g. c2:e4m3:row, c5:int4:block, "
-                         "c4:nvfp4:block:static, copy, zp_gemm:16, mx_gemm:2048)")
+                         "c4:nvfp4:block:static, copy, zp_gemm:16, mx_gemm:2048, mxw_gemm:2048)")
     ap.add_argument("--reps", type=int, default=20, help="timed repetitions per breakdown entry")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of graphs")
     return ap.parse_args()
@@ -585,6 +585,18 @@ def only(args):
     stream = torch.cuda.current_stream()
     if args.only == "copy":
         print(json.dumps({"copy_ceiling": copy_ceiling(args.reps)}), flush=True)
+        return
+    if args.only.startswith("mxw_gemm:"):
+        import int_quantization_amd as iq
+        from synth import synth
+        n1 = int(args.only.split(":")[1])
+        G = MxGemmWorkload()
+        x = to_device(synth.make("a3", nrows=n1))
+        outs = [torch.empty((G.n0, n1), dtype=torch.float32, device="cuda") for _ in range(NSETS)]
+        for s in range(args.warmup + args.steps):
+            iq.mxw_gemm(G.q[s % NSETS], x, out=outs[s % NSETS])
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "calls": args.warmup + args.steps}), flush=True)
         return
     if args.only.startswith("mx_gemm:"):
         n1 = int(args.only.split(":")[1])
