@@ -2008,8 +2008,9 @@ struct ZpGemmArgs {
     const uint16_t* x;       // [n1, K] BF16
     float* z;                // [n0, n1]
     int32_t n0, n1, K;
-    int32_t tiles_j, tiles_n, per_xcd;   // tile grid, tiles per XCD slice
-    uint32_t tiles;                      // tiles_j * tiles_n (checked on the host)
+    int32_t tiles_j, tiles_n, per_xcd;   // tile grid, work items per XCD slice
+    uint32_t tiles;                      // tiles_j * tiles_n * ksplit (checked on the host)
+    int32_t ksplit;                      // 1, or 2: k halves added atomically into a zeroed z
 };
 
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
@@ -2037,7 +2038,7 @@ __device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float sh) {
     return o;
 }
 
-// Few tokens (n1 <= 64): the weights are read once, so HBM and the
+// Few tokens (n1 <= 32): the weights are read once, so HBM and the
 // dequantization bound the time, not the matrix cores.  A workgroup takes a
 // stripe of 32 weight rows and 16 NT tokens; its 4 waves split the group
 // pairs (wave w takes pairs w, w + 4, ...) and dequantize their codes in
@@ -2171,6 +2172,11 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
 // WN waves along the tokens (a tile of 128 weight rows x 64 WN tokens,
 // 128 WN threads): the dequantization of a weight tile is shared by 64 WN
 // tokens, so a wider tile spends fewer VALU cycles per MFMA.
+// A grid too small to give every CU two groups in flight splits k in two
+// halves (ksplit = 2): each work item sums its half and adds it atomically
+// into z, which a fill kernel zeroed first.  With exactly two addends on a
+// +0 start the sum is a + b, rounded once, in either order, so the result
+// does not depend on which half lands first.
 template <int WN>
 __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
     constexpr int kTN = 64 * WN;             // tokens per tile
@@ -2183,12 +2189,16 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
-    const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
+    const uint32_t tile = idx / (uint32_t)a.ksplit;
+    const int half = (int)(idx % (uint32_t)a.ksplit);
+    const int jb = (int)(tile / (uint32_t)a.tiles_n), nb = (int)(tile % (uint32_t)a.tiles_n);
     const int j0 = jb * kGemmTile, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int ng = a.K / 128;
+    // the groups [g0, g1) of this work item's part of k
+    const int g0 = (int)((int64_t)half * ng / a.ksplit), g1 = (int)((int64_t)(half + 1) * ng / a.ksplit);
     const int ldc = a.K / 2;             // code bytes per weight row
     f4v acc[4][4];
 #pragma unroll
@@ -2223,8 +2233,8 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
         rsb = gsh[g >> 1];
         if (t < kGemmTile) rsc = gsc[g];
     };
-    load_group(0);
-    for (int g = 0; g < ng; ++g) {
+    if (g0 < g1) load_group(g0);
+    for (int g = g0; g < g1; ++g) {
         __syncthreads();                     // every wave is done with the previous group's tiles
 #pragma unroll
         for (int i = 0; i < kX; ++i) sB[lx[i]] = rx[i];
@@ -2237,7 +2247,7 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
                 sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = dequant8_bf16(cw[q], sh);
         }
         if (t < kGemmTile) sS[t] = rsc;
-        if (g + 1 < ng) load_group(g + 1);   // lands during this group's MFMAs
+        if (g + 1 < g1) load_group(g + 1);   // lands during this group's MFMAs
         lds_barrier();
         f4v accg[4][4];
 #pragma unroll
@@ -2281,7 +2291,10 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
-                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+                if (j < a.n0 && tok < a.n1) {
+                    if (a.ksplit > 1) unsafeAtomicAdd(a.z + (int64_t)j * a.n1 + tok, acc[mt][nt][i]);
+                    else a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+                }
             }
         }
 }
@@ -2570,7 +2583,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
 // matrix cores then form exact products with the activations and sum in
 // FP32: no per-block fold, and 0.5 VALU instructions per weight.  E8M0 255
 // (NaN) gives NaN weights.  The kernels are the asymmetric INT4 consumer's
-// (LDS tiles from 65 tokens, registers only below) with this dequantization.
+// (LDS tiles from 65 tokens with k split in halves when the tile grid is
+// small, registers only below) with this dequantization.
 // ---------------------------------------------------------------------------
 struct MxwGemmArgs {
     const uint8_t* codes;      // [n0, K / 2]
@@ -2579,7 +2593,8 @@ struct MxwGemmArgs {
     float* z;                  // [n0, n1]
     int32_t n0, n1, K;
     int32_t tiles_j, tiles_n, per_xcd;
-    uint32_t tiles;            // tiles_j * tiles_n (checked on the host)
+    uint32_t tiles;            // tiles_j * tiles_n * ksplit (checked on the host)
+    int32_t ksplit;            // 1, or 2: k halves added atomically into a zeroed z
 };
 
 // 8 weights of one code word (element 2t in the low nibble of byte t) as
@@ -2608,12 +2623,15 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
-    const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
+    const uint32_t tile = idx / (uint32_t)a.ksplit;
+    const int half = (int)(idx % (uint32_t)a.ksplit);
+    const int jb = (int)(tile / (uint32_t)a.tiles_n), nb = (int)(tile % (uint32_t)a.tiles_n);
     const int j0 = jb * kGemmTile, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int nks = a.K / 128;
+    const int k0 = (int)((int64_t)half * nks / a.ksplit), k1 = (int)((int64_t)(half + 1) * nks / a.ksplit);
     const int ldc = a.K / 2, lds_ = a.K / 32;
     f4v acc[4][4];
 #pragma unroll
@@ -2646,8 +2664,8 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
             rs[v] = gs[ks * 4 + v];
         }
     };
-    load_step(0);
-    for (int ks = 0; ks < nks; ++ks) {
+    if (k0 < k1) load_step(k0);
+    for (int ks = k0; ks < k1; ++ks) {
         __syncthreads();                     // every wave is done with the previous step's tiles
 #pragma unroll
         for (int i = 0; i < kX; ++i) sB[lx[i]] = rx[i];
@@ -2659,7 +2677,7 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
             for (int q = 0; q < 4; ++q)
                 sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = mx_bf16x8(cw[q], sc, rs[v] == 255u);
         }
-        if (ks + 1 < nks) load_step(ks + 1);     // lands during this step's MFMAs
+        if (ks + 1 < k1) load_step(ks + 1);     // lands during this step's MFMAs
         lds_barrier();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -2690,7 +2708,10 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
-                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+                if (j < a.n0 && tok < a.n1) {
+                    if (a.ksplit > 1) unsafeAtomicAdd(a.z + (int64_t)j * a.n1 + tok, acc[mt][nt][i]);
+                    else a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+                }
             }
         }
 }
@@ -3038,7 +3059,17 @@ hipError_t launch_dequantize(const DequantArgs& d, hipStream_t s) {
 constexpr int64_t kMaxGemmTiles = ((int64_t)1 << 31) - 64;
 
 // Token waves per workgroup: the 256-token tile from 256 tokens on.
-static int gemm_token_waves(int64_t n1) { return n1 >= 256 ? 4 : 2; }
+// 256-token tiles from 1024 tokens on, and below that wherever they pad no
+// more token rows than 128-token tiles do.
+static int gemm_token_waves(int64_t n1) {
+    const int64_t pad4 = (n1 + 255) / 256 * 256 - n1, pad2 = (n1 + 127) / 128 * 128 - n1;
+    return n1 >= 1024 || (n1 >= 256 && pad4 == pad2) ? 4 : 2;
+}
+
+__global__ void k_zero_f32(float* z, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        z[i] = 0.f;
+}
 
 hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     if (g.n0 == 0 || g.n1 == 0) return hipSuccess;
@@ -3046,22 +3077,29 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     a.codes = static_cast<const uint8_t*>(g.codes); a.scales = g.scales; a.shifts = g.shifts;
     a.x = static_cast<const uint16_t*>(g.x); a.z = g.z;
     a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
-    if (g.n1 <= 64) {
-        const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4;
+    if (g.n1 <= 32) {
+        const int nt = g.n1 <= 16 ? 1 : 2;
         const dim3 grid((unsigned)((g.n0 + kGemvRows - 1) / kGemvRows), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
         if (nt == 1) k_zp_gemv<1><<<grid, kThreads, 0, s>>>(a);
-        else if (nt == 2) k_zp_gemv<2><<<grid, kThreads, 0, s>>>(a);
-        else k_zp_gemv<4><<<grid, kThreads, 0, s>>>(a);
+        else k_zp_gemv<2><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
     const int wn = gemm_token_waves(g.n1);
     a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
-    if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
-    a.tiles = (uint32_t)tiles;
-    a.per_xcd = (int32_t)((tiles + 7) / 8);
+    // resident workgroups per CU: two of 256 threads, one of 512 (registers)
+    const int64_t slots = 256 * (wn == 4 ? 1 : 2);
+    a.ksplit = (2 * tiles <= slots && g.K >= 256) ? 2 : 1;
+    const int64_t items = tiles * a.ksplit;
+    if (items > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+    a.tiles = (uint32_t)items;
+    a.per_xcd = (int32_t)((items + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
+    if (a.ksplit > 1) {
+        const int64_t nz = g.n0 * g.n1;
+        k_zero_f32<<<(unsigned)std::min<int64_t>((nz + 255) / 256, 4096), 256, 0, s>>>(a.z, nz);
+    }
     if (wn == 4) k_zp_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
     else k_zp_gemm<2><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
@@ -3109,14 +3147,21 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
         else k_mxw_gemv<4><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
-    const int wn = gemm_token_waves(g.n1);
+    const int wn = g.n1 >= 256 ? 4 : 2;
     a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
-    if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
-    a.tiles = (uint32_t)tiles;
-    a.per_xcd = (int32_t)((tiles + 7) / 8);
+    const int64_t slots = 256 * (wn == 4 ? 1 : 2);
+    a.ksplit = (2 * tiles <= slots && g.K >= 256) ? 2 : 1;
+    const int64_t items = tiles * a.ksplit;
+    if (items > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+    a.tiles = (uint32_t)items;
+    a.per_xcd = (int32_t)((items + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
+    if (a.ksplit > 1) {
+        const int64_t nz = g.n0 * g.n1;
+        k_zero_f32<<<(unsigned)std::min<int64_t>((nz + 255) / 256, 4096), 256, 0, s>>>(a.z, nz);
+    }
     if (wn == 4) k_mxw_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
     else k_mxw_gemm<2><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();

@@ -789,11 +789,13 @@ def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
     return err, bound, zr
 
 
-# n1 <= 64: the few-token kernel (1, 2 or 4 token tiles of 16); 65 .. 255: the
-# 128-token tile; from 256: the 256-token tile.
+# n1 <= 32: the few-token kernel (1 or 2 token tiles of 16); above: 128- or
+# 256-token tiles, whose k is split in two halves added atomically when the
+# tile grid is small (every tiled case here; K = 256 gives each half one group).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (32, 1024, 300), (1, 256, 1),
                                      (257, 768, 129), (384, 2048, 256), (100, 512, 1), (64, 768, 16),
-                                     (300, 1024, 33), (48, 256, 64), (17, 2048, 50), (40, 512, 1100)])
+                                     (300, 1024, 33), (48, 256, 64), (17, 2048, 50), (40, 512, 1100),
+                                     (70, 256, 40), (96, 768, 100), (33, 512, 24)])
 def test_zp_gemm_parity(iq, O, S, n0, K, n1):
     err, bound, zr = zp_gemm_case(iq, O, S, n0, K, n1, seed=n0 + K + n1)
     assert np.abs(zr).max() > 0
@@ -874,10 +876,11 @@ def c5_int4zp(O, S):
     return O.quantize(S.make("c5"), "int4zp", "block", want_xhat=False, threads=THREADS)
 
 
-@pytest.mark.parametrize("n1", [16, 256, 2048])
+@pytest.mark.parametrize("n1", [16, 64, 256, 384, 2048])
 def test_zp_gemm_full_size_sampled(iq, O, S, c5_int4zp, n1):
-    """The c5 weights against n1 tokens of BF16 activations (each of the
-    three kernels); rows sampled for the oracle."""
+    """The c5 weights against n1 tokens of BF16 activations (the few-token
+    kernel, the 128-token tile with k split in halves, and the 128- and
+    256-token tiles whole); rows sampled for the oracle."""
     import torch
     r = c5_int4zp
     n0, K = 28672, 8192
@@ -997,9 +1000,12 @@ def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
 
 
 # n1 <= 64: the few-token kernel (1, 2 or 4 token tiles); 65 .. 255: 128-token
-# tiles; from 256: 256-token tiles.  Odd step counts (K / 128) included.
+# tiles; from 256: 256-token tiles.  Odd step counts (K / 128) included.  The
+# tiled cases' grids are small, so k is split in halves (one step each for
+# K = 256, 1 and 2 steps for K = 384), except for K = 128 (one step).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (257, 384, 129), (40, 512, 300),
-                                     (64, 1024, 1100), (1, 128, 1), (33, 640, 24), (70, 2048, 64), (50, 384, 16)])
+                                     (64, 1024, 1100), (1, 128, 1), (33, 640, 24), (70, 2048, 64), (50, 384, 16),
+                                     (80, 128, 90)])
 def test_mxw_gemm_parity(iq, O, S, n0, K, n1):
     z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=n0 + 7 * K + n1)
     bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
@@ -1023,10 +1029,11 @@ def test_mxw_gemm_nan_scale_and_empty(iq, O, S, n1):
     assert iq.mxw_gemm(mx_gpu(iq, rw, n0, K), x0).shape == (n0, 0)
 
 
-@pytest.mark.parametrize("n1", [16, 2048])
+@pytest.mark.parametrize("n1", [16, 128, 2048])
 def test_mxw_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
-    """The c3 weights (MXFP4 from the oracle) against n1 BF16 tokens of a3;
-    rows sampled for the oracle."""
+    """The c3 weights (MXFP4 from the oracle) against n1 BF16 tokens of a3
+    (few-token kernel; 128-token tiles with k split in halves; 256-token
+    tiles whole); rows sampled for the oracle."""
     import torch
     rw = c3_mxfp4
     n0, K = 14336, 4096
