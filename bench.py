@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0                # dense BF16 matrix-core peak
 MFMA_FP4_PEAK_TFS = 10100.0                # dense FP4 matrix-core peak
 GEMM_TOKENS = (1, 16, 64, 256, 2048)
-MX_GEMM_TOKENS = (16, 256, 2048, 8192)
+MX_GEMM_TOKENS = (16, 128, 256, 2048, 8192)
 METRIC = "quantize GB/s (bytes in+out) and % of MI355X HBM peak, per format"
 NSETS = 4
 
@@ -464,7 +464,7 @@ def gemm_breakdown(args):
         res[f"n1={n1}"] = {"avg_us": round(us, 2), "GB/s": round(b / us / 1e3, 1),
                            "TFLOP/s": round(fl / us / 1e6, 1), "bound": bound,
                            "frac": round(max(t_hbm, t_mfma) / us, 4), "bytes": b, "flops": fl,
-                           "kernel": "k_zp_gemv" if n1 <= 64 else "k_zp_gemm"}
+                           "kernel": "k_zp_gemv" if n1 <= 32 else "k_zp_gemm"}
         del xs, outs
     del G
     torch.cuda.empty_cache()

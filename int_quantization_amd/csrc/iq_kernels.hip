@@ -2050,7 +2050,10 @@ __device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float sh) {
 // takes one scale per group.  For MFMA step q of group g lane l holds the k
 // slice g * 128 + 32 (l / 16) + 8 q .. + 8: one code word of its 16-byte code
 // load, and one 16-byte activation load per token tile.
-// The codes, shifts and scales of the next pair load while a pair computes.
+// The codes of the next pair load while a pair computes; a pair's
+// activations load just before (loads complete in order, so a wait for them
+// leaves the codes in flight).  Scales and shift bytes come from LDS: read
+// per lane from memory, 16 rows apart, they cost a fifth of the call.
 // Rows past n0 and tokens past n1 read row n0 - 1 and token n1 - 1 instead:
 // such lanes only feed outputs that are never stored, and no load is
 // conditional.
@@ -2058,30 +2061,33 @@ constexpr int kGemvRows = 32;
 
 struct GemvPair {
     u4v c[2][2];      // codes [fragment][group of the pair]
-    uint32_t sb[2];   // shift byte per fragment
-    float sc[2][2];   // scale [fragment][group]
 };
+
+// Scales and shift bytes of the workgroup's 32 rows reach LDS in chunks of
+// up to kGemvChunk pairs of groups, with coalesced loads (row-contiguous in
+// memory), before the waves work through the chunk.  Rows are padded so the
+// 16 rows that a wave's lanes read sit in distinct banks.
+constexpr int kGemvChunk = 32;
 
 // With one token tile four waves per SIMD (at most 128 registers, no
 // spills) hold the whole grid of a 28672-row weight matrix at once: no
-// second, mostly idle round.
+// second, mostly idle round.  A second register set of activations (one
+// pair ahead) costs that occupancy and measured slower.
 template <int NT>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArgs a) {
     __shared__ f4v red[4][2][NT][64];
+    __shared__ float s_sc[kGemvRows][2 * kGemvChunk + 1];
+    __shared__ uint8_t s_sh[kGemvRows][kGemvChunk + 4];
     const int j0 = (int)blockIdx.x * kGemvRows, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int rr = lane & 15, h = lane >> 4;
     const int ng = a.K / 128, np = ng / 2;
     const uint8_t* crow[2];
-    const uint8_t* srow[2];
-    const float* scrow[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
         crow[f] = a.codes + j * (a.K / 2) + 16 * h;
-        srow[f] = a.shifts + j * np;
-        scrow[f] = a.scales + j * ng;
     }
     const u4v* xr[NT];
 #pragma unroll
@@ -2094,28 +2100,30 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
         for (int f = 0; f < 2; ++f) {
             w.c[f][0] = *reinterpret_cast<const u4v*>(crow[f] + p * 128);
             w.c[f][1] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + 64);
-            w.sb[f] = srow[f][p];
-            w.sc[f][0] = scrow[f][2 * p];
-            w.sc[f][1] = scrow[f][2 * p + 1];
         }
+    };
+    auto load_x = [&](int p, u4v (&xw)[2][NT][4]) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xw[e][nt][q] = xr[nt][(2 * p + e) * 16 + q];
     };
     f4v acc[2][NT];
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    auto compute_pair = [&](int p, const GemvPair& w) {
+    // pc: the pair's index within the staged chunk
+    auto compute_pair = [&](int pc, const GemvPair& w, const u4v (&xp)[2][NT][4]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int g = 2 * p + e;
-            u4v xw[NT][4];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) xw[nt][q] = xr[nt][g * 16 + q];
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
-                const float sh = (float)((w.sb[f] >> (4 * e)) & 0xFu);
+                const int r = 16 * f + rr;
+                const float sh = (float)((s_sh[r][pc] >> (4 * e)) & 0xFu);
+                const float sc = s_sc[r][2 * pc + e];
                 const uint32_t cw[4] = {w.c[f][e].x, w.c[f][e].y, w.c[f][e].z, w.c[f][e].w};
                 f4v accg[NT];
 #pragma unroll
@@ -2125,25 +2133,44 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
                     const bf8v bw = __builtin_bit_cast(bf8v, dequant8_bf16(cw[q], sh));
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        accg[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, xw[nt][q]), bw,
+                        accg[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, xp[e][nt][q]), bw,
                                                                            accg[nt], 0, 0, 0);
                 }
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[f][nt][i] = __builtin_fmaf(w.sc[f][e], accg[nt][i], acc[f][nt][i]);
+                    for (int i = 0; i < 4; ++i) acc[f][nt][i] = __builtin_fmaf(sc, accg[nt][i], acc[f][nt][i]);
             }
         }
     };
-    // two register sets in turn (a copy between them would wait for the loads)
-    if (wave < np) {
-        GemvPair pa, pb;
-        load_pair(wave, pa);
-        for (int p = wave; p < np; p += 8) {
-            load_pair(min(p + 4, np - 1), pb);
-            compute_pair(p, pa);
-            load_pair(min(p + 8, np - 1), pa);
-            if (p + 4 < np) compute_pair(p + 4, pb);
+    for (int p0 = 0; p0 < np; p0 += kGemvChunk) {
+        const int p1 = min(np, p0 + kGemvChunk), cp = p1 - p0;
+        __syncthreads();                         // the previous chunk's scales are no longer read
+        for (int i = t; i < kGemvRows * 2 * cp; i += kThreads) {
+            const int r = i / (2 * cp), gg = i - r * (2 * cp);
+            s_sc[r][gg] = a.scales[(int64_t)min(j0 + r, a.n0 - 1) * ng + 2 * p0 + gg];
+        }
+        for (int i = t; i < kGemvRows * cp; i += kThreads) {
+            const int r = i / cp, pp = i - r * cp;
+            s_sh[r][pp] = a.shifts[(int64_t)min(j0 + r, a.n0 - 1) * np + p0 + pp];
+        }
+        __syncthreads();
+        if (p0 + wave < p1) {
+            // the activations of a pair load before the next pair's codes, so
+            // waiting for them leaves that prefetch in flight
+            GemvPair pa, pb;
+            u4v xw[2][NT][4];
+            load_pair(p0 + wave, pa);
+            for (int p = p0 + wave; p < p1; p += 8) {
+                load_x(p, xw);
+                asm volatile("" ::: "memory");
+                load_pair(min(p + 4, p1 - 1), pb);
+                compute_pair(p - p0, pa, xw);
+                load_x(min(p + 4, p1 - 1), xw);
+                asm volatile("" ::: "memory");
+                load_pair(min(p + 8, p1 - 1), pa);
+                if (p + 4 < p1) compute_pair(p + 4 - p0, pb, xw);
+            }
         }
     }
 #pragma unroll
@@ -2723,24 +2750,25 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
 // the row.  A step past the last one (odd step count) reads nothing.
 struct MxwPair {
     u4v c[2][2];          // codes [fragment][step of the pair]
-    uint32_t s[2][2];     // the row's 4 scale bytes of the step [fragment][step]
 };
 
+// Scale words (4 E8M0 bytes per row and step) reach LDS in chunks of up to
+// kGemvChunk pairs of steps, as for the asymmetric INT4 kernel; so do the
+// load orders (a pair's activations before the next pair's codes).
 template <int NT>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmArgs a) {
     __shared__ f4v red[4][2][NT][64];
+    __shared__ uint32_t s_sw[32][2 * kGemvChunk + 1];
     const int j0 = (int)blockIdx.x * 32, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int rr = lane & 15, h = lane >> 4;
     const int nks = a.K / 128, np = (nks + 1) / 2;
     const uint8_t* crow[2];
-    const uint8_t* srow[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
         crow[f] = a.codes + j * (a.K / 2) + 16 * h;
-        srow[f] = a.scales + j * (a.K / 32);
     }
     const u4v* xr[NT];
 #pragma unroll
@@ -2754,10 +2782,17 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
         for (int e = 0; e < 2; ++e) {
             if (e == 1 && !both) break;
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                w.c[f][e] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + e * 64);
-                w.s[f][e] = *reinterpret_cast<const uint32_t*>(srow[f] + p * 8 + e * 4);
-            }
+            for (int f = 0; f < 2; ++f) w.c[f][e] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + e * 64);
+        }
+    };
+    auto load_x = [&](int p, u4v (&xw)[2][NT][4]) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            if (2 * p + e >= nks) break;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xw[e][nt][q] = xr[nt][(2 * p + e) * 16 + q];
         }
     };
     f4v acc[2][NT];
@@ -2765,19 +2800,14 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
     for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    auto compute_pair = [&](int p, const MxwPair& w) {
+    // pc: the pair's index within the staged chunk
+    auto compute_pair = [&](int p, int pc, const MxwPair& w, const u4v (&xp)[2][NT][4]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int g = 2 * p + e;
-            if (g >= nks) break;
-            u4v xw[NT][4];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) xw[nt][q] = xr[nt][g * 16 + q];
+            if (2 * p + e >= nks) break;
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
-                const uint32_t E = (w.s[f][e] >> (8 * h)) & 0xFFu;
+                const uint32_t E = (s_sw[16 * f + rr][2 * pc + e] >> (8 * h)) & 0xFFu;
                 const float sc = e8m0_scale(E);
                 const uint32_t cw[4] = {w.c[f][e].x, w.c[f][e].y, w.c[f][e].z, w.c[f][e].w};
 #pragma unroll
@@ -2785,20 +2815,36 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
                     const bf8v bw = __builtin_bit_cast(bf8v, mx_bf16x8(cw[q], sc, E == 255u));
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        acc[f][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, xw[nt][q]), bw,
+                        acc[f][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, xp[e][nt][q]), bw,
                                                                               acc[f][nt], 0, 0, 0);
                 }
             }
         }
     };
-    if (wave < np) {
-        MxwPair pa = {}, pb = {};
-        load_pair(wave, pa);
-        for (int p = wave; p < np; p += 8) {
-            load_pair(min(p + 4, np - 1), pb);
-            compute_pair(p, pa);
-            load_pair(min(p + 8, np - 1), pa);
-            if (p + 4 < np) compute_pair(p + 4, pb);
+    for (int p0 = 0; p0 < np; p0 += kGemvChunk) {
+        const int p1 = min(np, p0 + kGemvChunk);
+        const int cs = min(2 * p1, nks) - 2 * p0;   // steps in the chunk
+        __syncthreads();                            // the previous chunk's scales are no longer read
+        for (int i = t; i < 32 * cs; i += kThreads) {
+            const int r = i / cs, ss = i - r * cs;
+            s_sw[r][ss] = *reinterpret_cast<const uint32_t*>(a.scales + (int64_t)min(j0 + r, a.n0 - 1) * (a.K / 32) +
+                                                              4 * (2 * p0 + ss));
+        }
+        __syncthreads();
+        if (p0 + wave < p1) {
+            MxwPair pa = {}, pb = {};
+            u4v xw[2][NT][4] = {};
+            load_pair(p0 + wave, pa);
+            for (int p = p0 + wave; p < p1; p += 8) {
+                load_x(p, xw);
+                asm volatile("" ::: "memory");
+                load_pair(min(p + 4, p1 - 1), pb);
+                compute_pair(p, p - p0, pa, xw);
+                load_x(min(p + 4, p1 - 1), xw);
+                asm volatile("" ::: "memory");
+                load_pair(min(p + 8, p1 - 1), pa);
+                if (p + 4 < p1) compute_pair(p + 4, p + 4 - p0, pb, xw);
+            }
         }
     }
 #pragma unroll
@@ -3066,10 +3112,18 @@ static int gemm_token_waves(int64_t n1) {
     return n1 >= 1024 || (n1 >= 256 && pad4 == pad2) ? 4 : 2;
 }
 
+// z[0 .. n) = +0 (z 4-byte aligned): 16-byte stores from the first 16-byte
+// boundary, single floats for the up to 3 before it and after the last.
 __global__ void k_zero_f32(float* z, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        z[i] = 0.f;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t head = std::min<int64_t>(n, (int64_t)((16u - ((uint32_t)(uintptr_t)z & 15u)) & 15u) / 4);
+    const int64_t nv = (n - head) / 4, tail0 = head + 4 * nv;
+    u4v* zv = reinterpret_cast<u4v*>(z + head);
+    for (int64_t i = tid; i < nv; i += stride) zv[i] = u4v{0u, 0u, 0u, 0u};
+    if (tid < head) z[tid] = 0.f;
+    if (tid < n - tail0) z[tail0 + tid] = 0.f;
 }
+static unsigned zero_grid(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n / 4 + 255) / 256, 2048)); }
 
 hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     if (g.n0 == 0 || g.n1 == 0) return hipSuccess;
@@ -3098,7 +3152,7 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
     if (a.ksplit > 1) {
         const int64_t nz = g.n0 * g.n1;
-        k_zero_f32<<<(unsigned)std::min<int64_t>((nz + 255) / 256, 4096), 256, 0, s>>>(a.z, nz);
+        k_zero_f32<<<zero_grid(nz), 256, 0, s>>>(a.z, nz);
     }
     if (wn == 4) k_zp_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
     else k_zp_gemm<2><<<grid, 256, 0, s>>>(a);
@@ -3160,7 +3214,7 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
     if (a.ksplit > 1) {
         const int64_t nz = g.n0 * g.n1;
-        k_zero_f32<<<(unsigned)std::min<int64_t>((nz + 255) / 256, 4096), 256, 0, s>>>(a.z, nz);
+        k_zero_f32<<<zero_grid(nz), 256, 0, s>>>(a.z, nz);
     }
     if (wn == 4) k_mxw_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
     else k_mxw_gemm<2><<<grid, 256, 0, s>>>(a);

@@ -408,6 +408,32 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_gemm_split_output_offsets(iq, O, S, off):
+    """A call whose k is split zeroes z first, with 16-byte stores from the
+    first 16-byte boundary and single floats around them: an output 4, 8 or
+    12 bytes past a boundary gets the bits of an aligned output, and the
+    floats just before and after it keep their values."""
+    import torch
+    n0, K, n1 = 96, 512, 100                       # one tile: both GEMMs split k
+    rzp = O.quantize((S.bf16_to_f32(S.make("c5", nrows=n0))[:, :K]).copy(), "int4zp", "block")
+    qzp = iq.Quantized(to_device(rzp["codes"]), to_device(rzp["scales"]), None, None, None, "int4zp", "block",
+                       n0, K, to_device(rzp["shifts"]))
+    qw = mx_gpu(iq, mx_operand(O, S, n0, K, seed=41, sigma=0.02, outlier_axis=S.AXIS_ROWS), n0, K)
+    x = to_device(S.make("c2", nrows=n1)[:, :K].copy())
+    sentinel = 0x7FC0BEEF
+    for name, call in (("zp", lambda out=None: iq.zp_gemm(qzp, x, out=out)),
+                       ("mxw", lambda out=None: iq.mxw_gemm(qw, x, out=out))):
+        want = call().cpu()
+        buf = torch.full((n0 * n1 + 8,), sentinel, dtype=torch.int32, device="cuda:0")
+        out = buf[off:off + n0 * n1].view(torch.float32).view(n0, n1)
+        call(out)
+        torch.cuda.synchronize()
+        b = buf.cpu()
+        assert torch.equal(b[off:off + n0 * n1], want.view(torch.int32).reshape(-1)), name
+        assert bool((b[:off] == sentinel).all()) and bool((b[off + n0 * n1:] == sentinel).all()), name
+
+
 @pytest.mark.parametrize("n1", [16, 300])
 def test_gemm_graph_replay_matches_eager(iq, O, S, n1):
     """The GEMMs (their few-token and their tiled kernels) add in a fixed
