@@ -2490,14 +2490,19 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
 template <int NT>
 struct MxGemvPair {
     u4v c[2][2];          // weight codes [fragment][step of the pair]
-    uint32_t s[2][2];     // weight scale words [fragment][step]
     u4v x[2][NT];         // activation codes [step][token tile]
-    uint32_t xs[2][NT];   // activation scale words [step][token tile]
 };
 
+constexpr int kMxGemvChunk = 32;   // pairs of steps whose scale words one LDS chunk holds
+
+// The scale words (4 E8M0 bytes per row and step) of the workgroup's 32
+// weight rows and 16 NT tokens reach LDS in chunks, with coalesced loads:
+// read per lane, 16 rows apart, they cost more than the codes' streaming.
 template <int NT>
 __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
     __shared__ f4v red[4][2][NT][64];
+    __shared__ uint32_t s_sw[32][2 * kMxGemvChunk + 1];
+    __shared__ uint32_t s_sx[16 * NT][2 * kMxGemvChunk + 1];
     const int j0 = (int)blockIdx.x * 32, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -2505,20 +2510,16 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
     const int nks = a.K / 128, np = (nks + 1) / 2;
     const int64_t cstride = a.K / 2, sstride = a.K / 32;
     const uint8_t* cw[2];
-    const uint8_t* sw[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
         cw[f] = a.codes_w + j * cstride + 16 * h;
-        sw[f] = a.scales_w + j * sstride;
     }
     const uint8_t* cx[NT];
-    const uint8_t* sx[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int64_t tok = min(t0 + 16 * nt + rr, a.n1 - 1);
         cx[nt] = a.codes_a + tok * cstride + 16 * h;
-        sx[nt] = a.scales_a + tok * sstride;
     }
     auto load_pair = [&](int p, MxGemvPair<NT>& w) {
         const bool both = 2 * p + 1 < nks;
@@ -2526,15 +2527,9 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
         for (int e = 0; e < 2; ++e) {
             if (e == 1 && !both) break;
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                w.c[f][e] = *reinterpret_cast<const u4v*>(cw[f] + p * 128 + e * 64);
-                w.s[f][e] = *reinterpret_cast<const uint32_t*>(sw[f] + p * 8 + e * 4);
-            }
+            for (int f = 0; f < 2; ++f) w.c[f][e] = *reinterpret_cast<const u4v*>(cw[f] + p * 128 + e * 64);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                w.x[e][nt] = *reinterpret_cast<const u4v*>(cx[nt] + p * 128 + e * 64);
-                w.xs[e][nt] = *reinterpret_cast<const uint32_t*>(sx[nt] + p * 8 + e * 4);
-            }
+            for (int nt = 0; nt < NT; ++nt) w.x[e][nt] = *reinterpret_cast<const u4v*>(cx[nt] + p * 128 + e * 64);
         }
     };
     f4v acc[2][NT];
@@ -2542,7 +2537,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
     for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    auto compute_pair = [&](int p, const MxGemvPair<NT>& w) {
+    // pc: the pair's index within the staged chunk
+    auto compute_pair = [&](int p, int pc, const MxGemvPair<NT>& w) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int ks = 2 * p + e;
@@ -2553,13 +2549,13 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
             for (int nt = 0; nt < NT; ++nt) {
                 const u4v c = w.x[e][nt];
                 xa[nt] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-                xs[nt] = (int)((w.xs[e][nt] >> (8 * h)) & 0xFFu);
+                xs[nt] = (int)((s_sx[16 * nt + rr][2 * pc + e] >> (8 * h)) & 0xFFu);
             }
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
                 const u4v c = w.c[f][e];
                 const v8i wb = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-                const int ws = (int)((w.s[f][e] >> (8 * h)) & 0xFFu);
+                const int ws = (int)((s_sw[16 * f + rr][2 * pc + e] >> (8 * h)) & 0xFFu);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     acc[f][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa[nt], wb, acc[f][nt], 4, 4, 0,
@@ -2571,13 +2567,29 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
     // before any of its math: enough bytes in flight per CU to stream the
     // weights at HBM rate when each wave owns only a few pairs.
     constexpr int kMxChunk = NT == 4 ? 2 : 4;
-    for (int p0 = wave; p0 < np; p0 += 4 * kMxChunk) {
-        MxGemvPair<NT> pr[kMxChunk];
+    for (int c0 = 0; c0 < np; c0 += kMxGemvChunk) {
+        const int c1 = min(np, c0 + kMxGemvChunk);
+        const int cs = min(2 * c1, nks) - 2 * c0;   // steps in the staged chunk
+        __syncthreads();                            // the previous chunk's scales are no longer read
+        for (int i = t; i < 32 * cs; i += kThreads) {
+            const int r = i / cs, ss = i - r * cs;
+            s_sw[r][ss] = *reinterpret_cast<const uint32_t*>(a.scales_w + min(j0 + r, a.n0 - 1) * sstride +
+                                                              4 * (2 * c0 + ss));
+        }
+        for (int i = t; i < 16 * NT * cs; i += kThreads) {
+            const int r = i / cs, ss = i - r * cs;
+            s_sx[r][ss] = *reinterpret_cast<const uint32_t*>(a.scales_a + min(t0 + r, a.n1 - 1) * sstride +
+                                                              4 * (2 * c0 + ss));
+        }
+        __syncthreads();
+        for (int p0 = c0 + wave; p0 < c1; p0 += 4 * kMxChunk) {
+            MxGemvPair<NT> pr[kMxChunk];
 #pragma unroll
-        for (int c = 0; c < kMxChunk; ++c) load_pair(min(p0 + 4 * c, np - 1), pr[c]);
+            for (int c = 0; c < kMxChunk; ++c) load_pair(min(p0 + 4 * c, c1 - 1), pr[c]);
 #pragma unroll
-        for (int c = 0; c < kMxChunk; ++c)
-            if (p0 + 4 * c < np) compute_pair(p0 + 4 * c, pr[c]);
+            for (int c = 0; c < kMxChunk; ++c)
+                if (p0 + 4 * c < c1) compute_pair(p0 + 4 * c, p0 + 4 * c - c0, pr[c]);
+        }
     }
 #pragma unroll
     for (int f = 0; f < 2; ++f)
