@@ -2073,11 +2073,15 @@ constexpr int kGemvChunk = 32;
 // spills) hold the whole grid of a 28672-row weight matrix at once: no
 // second, mostly idle round.  A second register set of activations (one
 // pair ahead) costs that occupancy and measured slower.
-template <int NT>
+// X1 (a single token): the chunk's slice of the one activation row joins
+// the scales in LDS (16 KB), so no activation load waits behind the codes.
+template <int NT, bool X1>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArgs a) {
+    static_assert(!X1 || NT == 1, "one token, one token tile");
     __shared__ f4v red[4][2][NT][64];
     __shared__ float s_sc[kGemvRows][2 * kGemvChunk + 1];
     __shared__ uint8_t s_sh[kGemvRows][kGemvChunk + 4];
+    __shared__ u4v s_x[X1 ? 2 * kGemvChunk * 16 : 1];
     const int j0 = (int)blockIdx.x * kGemvRows, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -2102,13 +2106,14 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
             w.c[f][1] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + 64);
         }
     };
-    auto load_x = [&](int p, u4v (&xw)[2][NT][4]) {
+    auto load_x = [&](int p, int pc, u4v (&xw)[2][NT][4]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xw[e][nt][q] = xr[nt][(2 * p + e) * 16 + q];
+                for (int q = 0; q < 4; ++q)
+                    xw[e][nt][q] = X1 ? s_x[(2 * pc + e) * 16 + 4 * h + q] : xr[nt][(2 * p + e) * 16 + q];
     };
     f4v acc[2][NT];
 #pragma unroll
@@ -2154,6 +2159,10 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
             const int r = i / cp, pp = i - r * cp;
             s_sh[r][pp] = a.shifts[(int64_t)min(j0 + r, a.n0 - 1) * np + p0 + pp];
         }
+        if (X1) {
+            const u4v* xg = reinterpret_cast<const u4v*>(a.x) + (int64_t)(2 * p0) * 16;
+            for (int i = t; i < 2 * cp * 16; i += kThreads) s_x[i] = xg[i];
+        }
         __syncthreads();
         if (p0 + wave < p1) {
             // the activations of a pair load before the next pair's codes, so
@@ -2162,11 +2171,11 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
             u4v xw[2][NT][4];
             load_pair(p0 + wave, pa);
             for (int p = p0 + wave; p < p1; p += 8) {
-                load_x(p, xw);
+                load_x(p, p - p0, xw);
                 asm volatile("" ::: "memory");
                 load_pair(min(p + 4, p1 - 1), pb);
                 compute_pair(p - p0, pa, xw);
-                load_x(min(p + 4, p1 - 1), xw);
+                load_x(min(p + 4, p1 - 1), min(p + 4, p1 - 1) - p0, xw);
                 asm volatile("" ::: "memory");
                 load_pair(min(p + 8, p1 - 1), pa);
                 if (p + 4 < p1) compute_pair(p + 4 - p0, pb, xw);
@@ -2766,11 +2775,14 @@ struct MxwPair {
 
 // Scale words (4 E8M0 bytes per row and step) reach LDS in chunks of up to
 // kGemvChunk pairs of steps, as for the asymmetric INT4 kernel; so do the
-// load orders (a pair's activations before the next pair's codes).
-template <int NT>
+// load order (a pair's activations before the next pair's codes) and, with
+// X1 (a single token), the activation row's slice.
+template <int NT, bool X1>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmArgs a) {
+    static_assert(!X1 || NT == 1, "one token, one token tile");
     __shared__ f4v red[4][2][NT][64];
     __shared__ uint32_t s_sw[32][2 * kGemvChunk + 1];
+    __shared__ u4v s_x[X1 ? 2 * kGemvChunk * 16 : 1];
     const int j0 = (int)blockIdx.x * 32, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -2797,14 +2809,15 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
             for (int f = 0; f < 2; ++f) w.c[f][e] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + e * 64);
         }
     };
-    auto load_x = [&](int p, u4v (&xw)[2][NT][4]) {
+    auto load_x = [&](int p, int pc, u4v (&xw)[2][NT][4]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             if (2 * p + e >= nks) break;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xw[e][nt][q] = xr[nt][(2 * p + e) * 16 + q];
+                for (int q = 0; q < 4; ++q)
+                    xw[e][nt][q] = X1 ? s_x[(2 * pc + e) * 16 + 4 * h + q] : xr[nt][(2 * p + e) * 16 + q];
         }
     };
     f4v acc[2][NT];
@@ -2842,17 +2855,21 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
             s_sw[r][ss] = *reinterpret_cast<const uint32_t*>(a.scales + (int64_t)min(j0 + r, a.n0 - 1) * (a.K / 32) +
                                                               4 * (2 * p0 + ss));
         }
+        if (X1) {
+            const u4v* xg = reinterpret_cast<const u4v*>(a.x) + (int64_t)(2 * p0) * 16;
+            for (int i = t; i < cs * 16; i += kThreads) s_x[i] = xg[i];
+        }
         __syncthreads();
         if (p0 + wave < p1) {
             MxwPair pa = {}, pb = {};
             u4v xw[2][NT][4] = {};
             load_pair(p0 + wave, pa);
             for (int p = p0 + wave; p < p1; p += 8) {
-                load_x(p, xw);
+                load_x(p, p - p0, xw);
                 asm volatile("" ::: "memory");
                 load_pair(min(p + 4, p1 - 1), pb);
                 compute_pair(p, p - p0, pa, xw);
-                load_x(min(p + 4, p1 - 1), xw);
+                load_x(min(p + 4, p1 - 1), min(p + 4, p1 - 1) - p0, xw);
                 asm volatile("" ::: "memory");
                 load_pair(min(p + 8, p1 - 1), pa);
                 if (p + 4 < p1) compute_pair(p + 4, p + 4 - p0, pb, xw);
@@ -3146,8 +3163,9 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     if (g.n1 <= 32) {
         const int nt = g.n1 <= 16 ? 1 : 2;
         const dim3 grid((unsigned)((g.n0 + kGemvRows - 1) / kGemvRows), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
-        if (nt == 1) k_zp_gemv<1><<<grid, kThreads, 0, s>>>(a);
-        else k_zp_gemv<2><<<grid, kThreads, 0, s>>>(a);
+        if (g.n1 == 1) k_zp_gemv<1, true><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 1) k_zp_gemv<1, false><<<grid, kThreads, 0, s>>>(a);
+        else k_zp_gemv<2, false><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
     const int wn = gemm_token_waves(g.n1);
@@ -3208,9 +3226,10 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
     if (g.n1 <= 64) {
         const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4;
         const dim3 grid((unsigned)((g.n0 + 31) / 32), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
-        if (nt == 1) k_mxw_gemv<1><<<grid, kThreads, 0, s>>>(a);
-        else if (nt == 2) k_mxw_gemv<2><<<grid, kThreads, 0, s>>>(a);
-        else k_mxw_gemv<4><<<grid, kThreads, 0, s>>>(a);
+        if (g.n1 == 1) k_mxw_gemv<1, true><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 1) k_mxw_gemv<1, false><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 2) k_mxw_gemv<2, false><<<grid, kThreads, 0, s>>>(a);
+        else k_mxw_gemv<4, false><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
     const int wn = g.n1 >= 256 ? 4 : 2;

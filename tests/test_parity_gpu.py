@@ -821,7 +821,8 @@ def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (32, 1024, 300), (1, 256, 1),
                                      (257, 768, 129), (384, 2048, 256), (100, 512, 1), (64, 768, 16),
                                      (300, 1024, 33), (48, 256, 64), (17, 2048, 50), (40, 512, 1100),
-                                     (70, 256, 40), (96, 768, 100), (33, 512, 24)])
+                                     (70, 256, 40), (96, 768, 100), (33, 512, 24),
+                                     (40, 16896, 1), (40, 16896, 7), (24, 16896, 40)])
 def test_zp_gemm_parity(iq, O, S, n0, K, n1):
     err, bound, zr = zp_gemm_case(iq, O, S, n0, K, n1, seed=n0 + K + n1)
     assert np.abs(zr).max() > 0
@@ -902,7 +903,7 @@ def c5_int4zp(O, S):
     return O.quantize(S.make("c5"), "int4zp", "block", want_xhat=False, threads=THREADS)
 
 
-@pytest.mark.parametrize("n1", [16, 64, 256, 384, 2048])
+@pytest.mark.parametrize("n1", [1, 16, 64, 256, 384, 2048])
 def test_zp_gemm_full_size_sampled(iq, O, S, c5_int4zp, n1):
     """The c5 weights against n1 tokens of BF16 activations (the few-token
     kernel, the 128-token tile with k split in halves, and the 128- and
@@ -938,10 +939,11 @@ def mx_gpu(iq, r, rows, K):
 
 
 # n1 <= 64: the few-token kernel (1, 2 or 4 token tiles of 16); above, the
-# 128 x 128 tiles.  Odd step counts (K / 128) exercise the last half pair.
+# 128 x 128 tiles.  Odd step counts (K / 128) exercise the last half pair;
+# K = 8320 (65 steps) takes two LDS chunks of scale words, the second one step.
 @pytest.mark.parametrize("n0,K,n1", [(128, 128, 128), (200, 256, 75), (1, 128, 1), (257, 384, 129),
                                      (384, 1024, 256), (64, 512, 1100), (33, 4096, 40), (50, 640, 24),
-                                     (70, 2048, 64)])
+                                     (70, 2048, 64), (24, 8320, 3), (24, 8320, 50)])
 def test_mx_gemm_parity(iq, O, S, n0, K, n1):
     """Weights and activations quantized to MXFP4 by the oracle; the GPU
     product against the oracle's exact sum, within the FP32 bound."""
@@ -1031,7 +1033,7 @@ def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
 # K = 256, 1 and 2 steps for K = 384), except for K = 128 (one step).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (257, 384, 129), (40, 512, 300),
                                      (64, 1024, 1100), (1, 128, 1), (33, 640, 24), (70, 2048, 64), (50, 384, 16),
-                                     (80, 128, 90)])
+                                     (80, 128, 90), (24, 8320, 1), (24, 8320, 20), (24, 8320, 70)])
 def test_mxw_gemm_parity(iq, O, S, n0, K, n1):
     z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=n0 + 7 * K + n1)
     bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
@@ -1055,7 +1057,7 @@ def test_mxw_gemm_nan_scale_and_empty(iq, O, S, n1):
     assert iq.mxw_gemm(mx_gpu(iq, rw, n0, K), x0).shape == (n0, 0)
 
 
-@pytest.mark.parametrize("n1", [16, 128, 2048])
+@pytest.mark.parametrize("n1", [1, 16, 128, 2048])
 def test_mxw_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
     """The c3 weights (MXFP4 from the oracle) against n1 BF16 tokens of a3
     (few-token kernel; 128-token tiles with k split in halves; 256-token
