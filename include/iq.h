@@ -219,6 +219,11 @@ size_t iq_shifts_bytes(const iq_desc* d);
  * N0, n1 and K must fit 31 bits, and (N0/128)(n1/128) output tiles must
  * stay below 2^31 (IQ_EUNSUPPORTED).  n1 == 0 or N0 == 0 is
  * legal and writes nothing.  No workspace.
+ * Grids too small to fill the GPU (from 33 tokens, below about one tile
+ * per CU) split K in two halves: the call zeroes z with a kernel of its own,
+ * then each half adds its FP32 sum atomically.  Two addends on a +0 start
+ * give a + b rounded once in either order, so every call returns the same
+ * bits; z must not be touched by other work until the call completes.
  */
 iq_status iq_zp_gemm(const iq_desc* d, const void* codes, const float* scales, const uint8_t* shifts,
                      const void* x, int32_t x_dtype, int64_t n1, float* z, hipStream_t stream);
@@ -263,7 +268,9 @@ iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w
  * scales 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits, and
  * (N0/128)(n1/128) output tiles must stay below 2^31 (IQ_EUNSUPPORTED).
  * n1 == 0 or N0 == 0 is legal and writes nothing.  d->in_dtype and d->ld_in
- * are ignored.  No workspace.
+ * are ignored.  No workspace.  From 65 tokens, grids too small to fill the
+ * GPU split K in two halves as iq_zp_gemm does (z zeroed, two atomic adds,
+ * the same bits on every call).
  */
 iq_status iq_mxw_gemm(const iq_desc* d, const void* codes, const void* scales, const void* x, int32_t x_dtype,
                       int64_t n1, float* z, hipStream_t stream);
