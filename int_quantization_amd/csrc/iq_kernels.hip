@@ -2040,7 +2040,9 @@ __device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float sh) {
 
 // Few tokens (n1 <= 32): the weights are read once, so HBM and the
 // dequantization bound the time, not the matrix cores.  A workgroup takes a
-// stripe of 32 weight rows and 16 NT tokens; its 4 waves split the group
+// stripe of 16 FR weight rows (FR = 2 fragments up to 8 tokens, 4 above,
+// where one activation load then feeds twice the MFMAs) and 16 NT tokens;
+// its 4 waves split the group
 // pairs (wave w takes pairs w, w + 4, ...) and dequantize their codes in
 // registers straight into MFMA operands (no LDS tile); the waves' partial sums
 // meet in LDS at the end, added in wave order.
@@ -2057,39 +2059,39 @@ __device__ __forceinline__ u4v dequant8_bf16(uint32_t w, float sh) {
 // Rows past n0 and tokens past n1 read row n0 - 1 and token n1 - 1 instead:
 // such lanes only feed outputs that are never stored, and no load is
 // conditional.
-constexpr int kGemvRows = 32;
-
-struct GemvPair {
-    u4v c[2][2];      // codes [fragment][group of the pair]
+template <int FR> struct GemvPair {
+    u4v c[FR][2];      // codes [fragment][group of the pair]
 };
 
-// Scales and shift bytes of the workgroup's 32 rows reach LDS in chunks of
+// Scales and shift bytes of the workgroup's rows reach LDS in chunks of
 // up to kGemvChunk pairs of groups, with coalesced loads (row-contiguous in
 // memory), before the waves work through the chunk.  Rows are padded so the
 // 16 rows that a wave's lanes read sit in distinct banks.
 constexpr int kGemvChunk = 32;
 
-// With one token tile four waves per SIMD (at most 128 registers, no
-// spills) hold the whole grid of a 28672-row weight matrix at once: no
-// second, mostly idle round.  A second register set of activations (one
-// pair ahead) costs that occupancy and measured slower.
+// With one token tile and FR = 2, four waves per SIMD (at most 128
+// registers, no spills) hold the whole grid of a 28672-row weight matrix at
+// once: no second, mostly idle round; FR = 4 takes three.  A second register
+// set of activations (one pair ahead) costs that occupancy and measured
+// slower.
 // X1 (a single token): the chunk's slice of the one activation row joins
 // the scales in LDS (16 KB), so no activation load waits behind the codes.
-template <int NT, bool X1>
-__global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArgs a) {
+template <int NT, bool X1, int FR>
+__global__ __launch_bounds__(kThreads, NT == 1 ? (FR == 2 ? 4 : 3) : 1) void k_zp_gemv(ZpGemmArgs a) {
+    constexpr int kRows = 16 * FR;
     static_assert(!X1 || NT == 1, "one token, one token tile");
-    __shared__ f4v red[4][2][NT][64];
-    __shared__ float s_sc[kGemvRows][2 * kGemvChunk + 1];
-    __shared__ uint8_t s_sh[kGemvRows][kGemvChunk + 4];
+    __shared__ f4v red[4][FR][NT][64];
+    __shared__ float s_sc[kRows][2 * kGemvChunk + 1];
+    __shared__ uint8_t s_sh[kRows][kGemvChunk + 4];
     __shared__ u4v s_x[X1 ? 2 * kGemvChunk * 16 : 1];
-    const int j0 = (int)blockIdx.x * kGemvRows, t0 = (int)blockIdx.y * 16 * NT;
+    const int j0 = (int)blockIdx.x * kRows, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int rr = lane & 15, h = lane >> 4;
     const int ng = a.K / 128, np = ng / 2;
-    const uint8_t* crow[2];
+    const uint8_t* crow[FR];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < FR; ++f) {
         const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
         crow[f] = a.codes + j * (a.K / 2) + 16 * h;
     }
@@ -2099,9 +2101,9 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
         const int64_t tok = min(t0 + 16 * nt + rr, a.n1 - 1);
         xr[nt] = reinterpret_cast<const u4v*>(a.x + tok * a.K + 32 * h);
     }
-    auto load_pair = [&](int p, GemvPair& w) {
+    auto load_pair = [&](int p, GemvPair<FR>& w) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < FR; ++f) {
             w.c[f][0] = *reinterpret_cast<const u4v*>(crow[f] + p * 128);
             w.c[f][1] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + 64);
         }
@@ -2115,17 +2117,17 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
                 for (int q = 0; q < 4; ++q)
                     xw[e][nt][q] = X1 ? s_x[(2 * pc + e) * 16 + 4 * h + q] : xr[nt][(2 * p + e) * 16 + q];
     };
-    f4v acc[2][NT];
+    f4v acc[FR][NT];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
     // pc: the pair's index within the staged chunk
-    auto compute_pair = [&](int pc, const GemvPair& w, const u4v (&xp)[2][NT][4]) {
+    auto compute_pair = [&](int pc, const GemvPair<FR>& w, const u4v (&xp)[2][NT][4]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
+            for (int f = 0; f < FR; ++f) {
                 const int r = 16 * f + rr;
                 const float sh = (float)((s_sh[r][pc] >> (4 * e)) & 0xFu);
                 const float sc = s_sc[r][2 * pc + e];
@@ -2151,11 +2153,11 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
     for (int p0 = 0; p0 < np; p0 += kGemvChunk) {
         const int p1 = min(np, p0 + kGemvChunk), cp = p1 - p0;
         __syncthreads();                         // the previous chunk's scales are no longer read
-        for (int i = t; i < kGemvRows * 2 * cp; i += kThreads) {
+        for (int i = t; i < kRows * 2 * cp; i += kThreads) {
             const int r = i / (2 * cp), gg = i - r * (2 * cp);
             s_sc[r][gg] = a.scales[(int64_t)min(j0 + r, a.n0 - 1) * ng + 2 * p0 + gg];
         }
-        for (int i = t; i < kGemvRows * cp; i += kThreads) {
+        for (int i = t; i < kRows * cp; i += kThreads) {
             const int r = i / cp, pp = i - r * cp;
             s_sh[r][pp] = a.shifts[(int64_t)min(j0 + r, a.n0 - 1) * np + p0 + pp];
         }
@@ -2167,7 +2169,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
         if (p0 + wave < p1) {
             // the activations of a pair load before the next pair's codes, so
             // waiting for them leaves that prefetch in flight
-            GemvPair pa, pb;
+            GemvPair<FR> pa, pb;
             u4v xw[2][NT][4];
             load_pair(p0 + wave, pa);
             for (int p = p0 + wave; p < p1; p += 8) {
@@ -2183,7 +2185,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
         }
     }
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) red[wave][f][nt][lane] = acc[f][nt];
     __syncthreads();
@@ -2191,7 +2193,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_zp_gemv(ZpGemmArg
     // congruent to part mod 4 and writes 4 tokens of row j0 + 16 f + lane % 16
     const int part = t >> 6;
 #pragma unroll
-    for (int fi = 0; fi < 2 * NT; ++fi) {
+    for (int fi = 0; fi < FR * NT; ++fi) {
         if (fi % 4 != part) continue;
         const int f = fi / NT, nt = fi % NT;
         const int j = j0 + 16 * f + rr;
@@ -3161,11 +3163,12 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
     a.x = static_cast<const uint16_t*>(g.x); a.z = g.z;
     a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
     if (g.n1 <= 32) {
-        const int nt = g.n1 <= 16 ? 1 : 2;
-        const dim3 grid((unsigned)((g.n0 + kGemvRows - 1) / kGemvRows), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
-        if (g.n1 == 1) k_zp_gemv<1, true><<<grid, kThreads, 0, s>>>(a);
-        else if (nt == 1) k_zp_gemv<1, false><<<grid, kThreads, 0, s>>>(a);
-        else k_zp_gemv<2, false><<<grid, kThreads, 0, s>>>(a);
+        const int nt = g.n1 <= 16 ? 1 : 2, fr = g.n1 <= 8 ? 2 : 4;
+        const dim3 grid((unsigned)((g.n0 + 16 * fr - 1) / (16 * fr)), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
+        if (g.n1 == 1) k_zp_gemv<1, true, 2><<<grid, kThreads, 0, s>>>(a);
+        else if (fr == 2) k_zp_gemv<1, false, 2><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 1) k_zp_gemv<1, false, 4><<<grid, kThreads, 0, s>>>(a);
+        else k_zp_gemv<2, false, 4><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
     const int wn = gemm_token_waves(g.n1);

@@ -815,14 +815,16 @@ def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
     return err, bound, zr
 
 
-# n1 <= 32: the few-token kernel (1 or 2 token tiles of 16); above: 128- or
+# n1 <= 32: the few-token kernel (1 or 2 token tiles of 16, stripes of 32
+# weight rows up to 8 tokens and of 64 above); above: 128- or
 # 256-token tiles, whose k is split in two halves added atomically when the
 # tile grid is small (every tiled case here; K = 256 gives each half one group).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (32, 1024, 300), (1, 256, 1),
                                      (257, 768, 129), (384, 2048, 256), (100, 512, 1), (64, 768, 16),
                                      (300, 1024, 33), (48, 256, 64), (17, 2048, 50), (40, 512, 1100),
                                      (70, 256, 40), (96, 768, 100), (33, 512, 24),
-                                     (40, 16896, 1), (40, 16896, 7), (24, 16896, 40)])
+                                     (40, 16896, 1), (40, 16896, 7), (24, 16896, 40), (100, 512, 9),
+                                     (130, 16896, 12), (70, 768, 31)])
 def test_zp_gemm_parity(iq, O, S, n0, K, n1):
     err, bound, zr = zp_gemm_case(iq, O, S, n0, K, n1, seed=n0 + K + n1)
     assert np.abs(zr).max() > 0
