@@ -2771,28 +2771,30 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
 // MFMA step q of 128-deep step g, k = 128 g + 32 (l / 16) + 8 q .. + 8: one
 // word of its 16-byte code load, whose block scale is byte 4 g + l / 16 of
 // the row.  A step past the last one (odd step count) reads nothing.
-struct MxwPair {
-    u4v c[2][2];          // codes [fragment][step of the pair]
+template <int FR> struct MxwPair {
+    u4v c[FR][2];          // codes [fragment][step of the pair]
 };
 
 // Scale words (4 E8M0 bytes per row and step) reach LDS in chunks of up to
 // kGemvChunk pairs of steps, as for the asymmetric INT4 kernel; so do the
-// load order (a pair's activations before the next pair's codes) and, with
-// X1 (a single token), the activation row's slice.
-template <int NT, bool X1>
-__global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmArgs a) {
+// load order (a pair's activations before the next pair's codes), the
+// stripes of 16 FR rows (FR = 4 from 9 to 32 tokens) and, with X1 (a single
+// token), the activation row's slice.
+template <int NT, bool X1, int FR>
+__global__ __launch_bounds__(kThreads, NT == 1 ? (FR == 2 ? 4 : 3) : 1) void k_mxw_gemv(MxwGemmArgs a) {
+    constexpr int kRows = 16 * FR;
     static_assert(!X1 || NT == 1, "one token, one token tile");
-    __shared__ f4v red[4][2][NT][64];
-    __shared__ uint32_t s_sw[32][2 * kGemvChunk + 1];
+    __shared__ f4v red[4][FR][NT][64];
+    __shared__ uint32_t s_sw[kRows][2 * kGemvChunk + 1];
     __shared__ u4v s_x[X1 ? 2 * kGemvChunk * 16 : 1];
-    const int j0 = (int)blockIdx.x * 32, t0 = (int)blockIdx.y * 16 * NT;
+    const int j0 = (int)blockIdx.x * kRows, t0 = (int)blockIdx.y * 16 * NT;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int rr = lane & 15, h = lane >> 4;
     const int nks = a.K / 128, np = (nks + 1) / 2;
-    const uint8_t* crow[2];
+    const uint8_t* crow[FR];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < FR; ++f) {
         const int64_t j = min(j0 + 16 * f + rr, a.n0 - 1);
         crow[f] = a.codes + j * (a.K / 2) + 16 * h;
     }
@@ -2802,13 +2804,13 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
         const int64_t tok = min(t0 + 16 * nt + rr, a.n1 - 1);
         xr[nt] = reinterpret_cast<const u4v*>(a.x + tok * a.K + 32 * h);
     }
-    auto load_pair = [&](int p, MxwPair& w) {
+    auto load_pair = [&](int p, MxwPair<FR>& w) {
         const bool both = 2 * p + 1 < nks;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             if (e == 1 && !both) break;
 #pragma unroll
-            for (int f = 0; f < 2; ++f) w.c[f][e] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + e * 64);
+            for (int f = 0; f < FR; ++f) w.c[f][e] = *reinterpret_cast<const u4v*>(crow[f] + p * 128 + e * 64);
         }
     };
     auto load_x = [&](int p, int pc, u4v (&xw)[2][NT][4]) {
@@ -2822,18 +2824,18 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
                     xw[e][nt][q] = X1 ? s_x[(2 * pc + e) * 16 + 4 * h + q] : xr[nt][(2 * p + e) * 16 + q];
         }
     };
-    f4v acc[2][NT];
+    f4v acc[FR][NT];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[f][nt] = f4v{0.f, 0.f, 0.f, 0.f};
     // pc: the pair's index within the staged chunk
-    auto compute_pair = [&](int p, int pc, const MxwPair& w, const u4v (&xp)[2][NT][4]) {
+    auto compute_pair = [&](int p, int pc, const MxwPair<FR>& w, const u4v (&xp)[2][NT][4]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             if (2 * p + e >= nks) break;
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
+            for (int f = 0; f < FR; ++f) {
                 const uint32_t E = (s_sw[16 * f + rr][2 * pc + e] >> (8 * h)) & 0xFFu;
                 const float sc = e8m0_scale(E);
                 const uint32_t cw[4] = {w.c[f][e].x, w.c[f][e].y, w.c[f][e].z, w.c[f][e].w};
@@ -2852,7 +2854,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
         const int p1 = min(np, p0 + kGemvChunk);
         const int cs = min(2 * p1, nks) - 2 * p0;   // steps in the chunk
         __syncthreads();                            // the previous chunk's scales are no longer read
-        for (int i = t; i < 32 * cs; i += kThreads) {
+        for (int i = t; i < kRows * cs; i += kThreads) {
             const int r = i / cs, ss = i - r * cs;
             s_sw[r][ss] = *reinterpret_cast<const uint32_t*>(a.scales + (int64_t)min(j0 + r, a.n0 - 1) * (a.K / 32) +
                                                               4 * (2 * p0 + ss));
@@ -2863,7 +2865,7 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
         }
         __syncthreads();
         if (p0 + wave < p1) {
-            MxwPair pa = {}, pb = {};
+            MxwPair<FR> pa = {}, pb = {};
             u4v xw[2][NT][4] = {};
             load_pair(p0 + wave, pa);
             for (int p = p0 + wave; p < p1; p += 8) {
@@ -2879,13 +2881,13 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 4 : 1) void k_mxw_gemv(MxwGemmA
         }
     }
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) red[wave][f][nt][lane] = acc[f][nt];
     __syncthreads();
     const int part = t >> 6;
 #pragma unroll
-    for (int fi = 0; fi < 2 * NT; ++fi) {
+    for (int fi = 0; fi < FR * NT; ++fi) {
         if (fi % 4 != part) continue;
         const int f = fi / NT, nt = fi % NT;
         const int j = j0 + 16 * f + rr;
@@ -3227,12 +3229,13 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
     a.x = static_cast<const uint16_t*>(g.x); a.z = g.z;
     a.n0 = (int32_t)g.n0; a.n1 = (int32_t)g.n1; a.K = (int32_t)g.K;
     if (g.n1 <= 64) {
-        const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4;
-        const dim3 grid((unsigned)((g.n0 + 31) / 32), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
-        if (g.n1 == 1) k_mxw_gemv<1, true><<<grid, kThreads, 0, s>>>(a);
-        else if (nt == 1) k_mxw_gemv<1, false><<<grid, kThreads, 0, s>>>(a);
-        else if (nt == 2) k_mxw_gemv<2, false><<<grid, kThreads, 0, s>>>(a);
-        else k_mxw_gemv<4, false><<<grid, kThreads, 0, s>>>(a);
+        const int nt = g.n1 <= 16 ? 1 : g.n1 <= 32 ? 2 : 4, fr = (g.n1 <= 8 || nt == 4) ? 2 : 4;
+        const dim3 grid((unsigned)((g.n0 + 16 * fr - 1) / (16 * fr)), (unsigned)((g.n1 + 16 * nt - 1) / (16 * nt)));
+        if (g.n1 == 1) k_mxw_gemv<1, true, 2><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 1 && fr == 2) k_mxw_gemv<1, false, 2><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 1) k_mxw_gemv<1, false, 4><<<grid, kThreads, 0, s>>>(a);
+        else if (nt == 2) k_mxw_gemv<2, false, 4><<<grid, kThreads, 0, s>>>(a);
+        else k_mxw_gemv<4, false, 2><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
     const int wn = g.n1 >= 256 ? 4 : 2;

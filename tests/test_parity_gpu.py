@@ -1035,7 +1035,8 @@ def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
 # K = 256, 1 and 2 steps for K = 384), except for K = 128 (one step).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (257, 384, 129), (40, 512, 300),
                                      (64, 1024, 1100), (1, 128, 1), (33, 640, 24), (70, 2048, 64), (50, 384, 16),
-                                     (80, 128, 90), (24, 8320, 1), (24, 8320, 20), (24, 8320, 70)])
+                                     (80, 128, 90), (24, 8320, 1), (24, 8320, 20), (24, 8320, 70),
+                                     (70, 1024, 12), (130, 384, 8)])
 def test_mxw_gemm_parity(iq, O, S, n0, K, n1):
     z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=n0 + 7 * K + n1)
     bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
