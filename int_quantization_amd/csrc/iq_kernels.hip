@@ -2207,6 +2207,42 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? (FR == 2 ? 4 : 3) : 1) void k_z
     }
 }
 
+// Split-k epilogue for outputs whose rows do not start on 64-byte
+// boundaries (n1 not a multiple of 16): each wave's 64 x 64 block of sums
+// (rows mt 16 + 4 (lane / 16) + i, tokens nt 16 + lane % 16 of acc[mt][nt][i])
+// goes through LDS, four waves at a time, and is added one row per atomic
+// instruction: 64 floats, 256 contiguous bytes, where the direct form adds
+// four 64-byte pieces of four rows and touches twice the cache lines.  The
+// column swizzle (by row / 4) keeps the writes and the reads free of bank
+// conflicts.  Called by every wave of the workgroup; blk needs 64 KB.
+template <int NWAVES>
+__device__ __forceinline__ void atomic_add_rows(const f4v (&acc)[4][4], float* blk, int wave, int lane, float* z,
+                                                int32_t n0, int32_t n1, int row0, int tok0) {
+    for (int w0 = 0; w0 < NWAVES; w0 += 4) {
+        __syncthreads();
+        float* mine = blk + (wave - w0) * 64 * 64;
+        if (wave >= w0 && wave < w0 + 4) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        mine[(mt * 16 + 4 * (lane >> 4) + i) * 64 + ((nt * 16 + (lane & 15)) ^ ((lane >> 4) << 4))] =
+                            acc[mt][nt][i];
+        }
+        __syncthreads();
+        if (wave >= w0 && wave < w0 + 4) {
+            const int tok = tok0 + lane;
+            for (int r = 0; r < 64; ++r) {
+                const int j = row0 + r;
+                if (j < n0 && tok < n1)
+                    unsafeAtomicAdd(z + (int64_t)j * n1 + tok, mine[r * 64 + (lane ^ (((r >> 2) & 3) << 4))]);
+            }
+        }
+    }
+}
+
 // WN waves along the tokens (a tile of 128 weight rows x 64 WN tokens,
 // 128 WN threads): the dequantization of a weight tile is shared by 64 WN
 // tokens, so a wider tile spends fewer VALU cycles per MFMA.
@@ -2220,9 +2256,10 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
     constexpr int kTN = 64 * WN;             // tokens per tile
     constexpr int kWords = 4 / WN;           // 16-byte code words per thread and group
     constexpr int kX = 8;                    // 16-byte activation words per thread and group
-    __shared__ u4v sA[kGemmTile * 16];   // weights (w - sh) BF16, swizzled rows of 128
-    __shared__ u4v sB[kTN * 16];         // activations BF16, same layout
-    __shared__ float sS[kGemmTile];      // the group's scales of the tile's rows
+    __shared__ u4v tiles[(kGemmTile + kTN) * 16];
+    u4v* const sA = tiles;                   // weights (w - sh) BF16, swizzled rows of 128
+    u4v* const sB = tiles + kGemmTile * 16;  // activations BF16, same layout
+    __shared__ float sS[kGemmTile];          // the group's scales of the tile's rows
     // Tiles of one XCD slice are consecutive: neighbours share weight rows in that XCD's L2.
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
@@ -2320,6 +2357,12 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) acc[mt][nt][i] = __builtin_fmaf(sc, accg[mt][nt][i], acc[mt][nt][i]);
             }
+    }
+    static_assert((kGemmTile + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
+    if (a.ksplit > 1 && (a.n1 & 15)) {
+        atomic_add_rows<2 * WN>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
+                                t0 + wn * 64);
+        return;
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -2668,8 +2711,9 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
     constexpr int kTN = 64 * WN;             // tokens per tile
     constexpr int kWords = 4 / WN;           // 16-byte code words (scale blocks) per thread and step
     constexpr int kX = 8;                    // 16-byte activation words per thread and step
-    __shared__ u4v sA[kGemmTile * 16];   // weights BF16, swizzled rows of 128
-    __shared__ u4v sB[kTN * 16];         // activations BF16, same layout
+    __shared__ u4v tiles[(kGemmTile + kTN) * 16];
+    u4v* const sA = tiles;                   // weights BF16, swizzled rows of 128
+    u4v* const sB = tiles + kGemmTile * 16;  // activations BF16, same layout
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
@@ -2749,6 +2793,12 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
                 for (int nt = 0; nt < 4; ++nt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
         }
+    }
+    static_assert((kGemmTile + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
+    if (a.ksplit > 1 && (a.n1 & 15)) {
+        atomic_add_rows<2 * WN>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
+                                t0 + wn * 64);
+        return;
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)

@@ -905,11 +905,12 @@ def c5_int4zp(O, S):
     return O.quantize(S.make("c5"), "int4zp", "block", want_xhat=False, threads=THREADS)
 
 
-@pytest.mark.parametrize("n1", [1, 16, 64, 256, 384, 2048])
+@pytest.mark.parametrize("n1", [1, 16, 50, 64, 256, 384, 2048])
 def test_zp_gemm_full_size_sampled(iq, O, S, c5_int4zp, n1):
     """The c5 weights against n1 tokens of BF16 activations (the few-token
-    kernel, the 128-token tile with k split in halves, and the 128- and
-    256-token tiles whole); rows sampled for the oracle."""
+    kernel, the 128-token tile with k split in halves, added row by row at
+    50 tokens and directly at 64, and the 128- and 256-token tiles whole);
+    rows sampled for the oracle."""
     import torch
     r = c5_int4zp
     n0, K = 28672, 8192
@@ -1060,7 +1061,7 @@ def test_mxw_gemm_nan_scale_and_empty(iq, O, S, n1):
     assert iq.mxw_gemm(mx_gpu(iq, rw, n0, K), x0).shape == (n0, 0)
 
 
-@pytest.mark.parametrize("n1", [1, 16, 128, 2048])
+@pytest.mark.parametrize("n1", [1, 16, 128, 255, 2048])
 def test_mxw_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
     """The c3 weights (MXFP4 from the oracle) against n1 BF16 tokens of a3
     (few-token kernel; 128-token tiles with k split in halves; 256-token
