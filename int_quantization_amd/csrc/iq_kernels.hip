@@ -2551,7 +2551,7 @@ constexpr int kMxGemvChunk = 32;   // pairs of steps whose scale words one LDS c
 
 // The scale words (4 E8M0 bytes per row and step) of the workgroup's 32
 // weight rows and 16 NT tokens reach LDS in chunks, with coalesced loads:
-// read per lane, 16 rows apart, they cost more than the codes' streaming.
+// read per lane, 16 rows apart, they cost about a fifth of the call.
 template <int NT>
 __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
     __shared__ f4v red[4][2][NT][64];
