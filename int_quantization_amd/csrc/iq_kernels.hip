@@ -1988,7 +1988,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
 // an integer in [-15, 15], exact in BF16, so v_mfma_f32_16x16x32_bf16 forms
 // exact products of it and the BF16 activations, summed in FP32; each group's
 // sum is scaled by sc and added with one fma.
-// From 65 tokens on a workgroup computes a 128 x 64 WN tile of z with 2 WN
+// From 33 tokens on a workgroup computes a 128 x 64 WN tile of z with 2 WN
 // waves of 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per group the activations
 // and codes of the next group load into registers during the MFMAs (direct
 // global-to-LDS copies were the bottleneck), then the activations are
