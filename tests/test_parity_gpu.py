@@ -824,7 +824,8 @@ def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
                                      (300, 1024, 33), (48, 256, 64), (17, 2048, 50), (40, 512, 1100),
                                      (70, 256, 40), (96, 768, 100), (33, 512, 24),
                                      (40, 16896, 1), (40, 16896, 7), (24, 16896, 40), (100, 512, 9),
-                                     (130, 16896, 12), (70, 768, 31)])
+                                     (130, 16896, 12), (70, 768, 31), (1, 256, 12), (1, 256, 24), (5, 512, 40),
+                                     (3, 512, 300)])
 def test_zp_gemm_parity(iq, O, S, n0, K, n1):
     err, bound, zr = zp_gemm_case(iq, O, S, n0, K, n1, seed=n0 + K + n1)
     assert np.abs(zr).max() > 0
@@ -1037,7 +1038,8 @@ def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (257, 384, 129), (40, 512, 300),
                                      (64, 1024, 1100), (1, 128, 1), (33, 640, 24), (70, 2048, 64), (50, 384, 16),
                                      (80, 128, 90), (24, 8320, 1), (24, 8320, 20), (24, 8320, 70),
-                                     (70, 1024, 12), (130, 384, 8)])
+                                     (70, 1024, 12), (130, 384, 8), (1, 384, 12), (2, 256, 24), (5, 640, 70),
+                                     (3, 512, 300)])
 def test_mxw_gemm_parity(iq, O, S, n0, K, n1):
     z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=n0 + 7 * K + n1)
     bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
