@@ -2390,7 +2390,8 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
 // (16 contiguous code bytes and one scale byte per block).  The products
 // are exact and summed in FP32, so no dequantization or per-block fold runs
 // on the VALU.
-// A workgroup computes a 128 x TN tile of z with 2 x 2 waves.  Per k step
+// A workgroup computes a TM x TN tile of z with 4 waves: 2 x 2 of 64 x TN/2
+// for TM = 128, 1 x 4 of 64 x TN/4 for TM = 64 (small grids).  Per k step
 // the codes of both operands (64 bytes per row) and their scale words (one
 // 32-bit word of 4 E8M0 bytes per row) are staged through registers into a
 // double-buffered LDS tile: step k + 2 loads into registers while step k
@@ -2417,18 +2418,19 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 // One thread's share of a k step: 2 + TN / 64 code words and up to two
 // scale words (weights row t for t < 128, activations row t for t < TN).
-template <int TN>
+template <int TN, int TM>
 struct MxStage {
-    u4v w[2], x[TN / 64];
+    u4v w[TM / 64], x[TN / 64];
     uint32_t sw, sx;
 };
 
 // TN = 128 or 256 tokens per tile; each wave computes 64 weight rows x TN / 2
 // tokens, so the wider tile reads 12 KB of LDS per 32 MFMAs instead of 8 KB
 // per 16 (it pays from about a thousand tokens on).
-template <int TN>
+template <int TN, int TM>
 __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
-    constexpr int TM = 128, NX = TN / 64, NB = TN / 32;
+    // TM / 64 waves along the weight rows, the other 4 / (TM / 64) along the tokens
+    constexpr int WM = TM / 64, WT = 4 / WM, NX = TN / 64, NB = TN / (16 * WT);
     __shared__ u4v sW[2][TM * 4], sA[2][TN * 4];          // codes, 64 bytes per row
     __shared__ uint32_t sWs[2][TM], sAs[2][TN];           // scale words, 4 E8M0 bytes per row
     const uint32_t b = blockIdx.x;
@@ -2438,18 +2440,18 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
     const int j0 = jb * TM, t0 = nb * TN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WT, wn = wave % WT;
     const int nks = a.K / 128;
     const int64_t cstride = a.K / 2, sstride = a.K / 32;
     // staging: thread t moves 16-byte slot t & 3 of weight rows t / 4 + 64 i
     // (i < 2) and activation rows t / 4 + 64 i (i < 4), and the scale words
     // of weight row t (t < 128) and activation row t
     const int r0 = t >> 2, slot = t & 3;
-    const uint8_t* gw[2];
+    const uint8_t* gw[WM];
     const uint8_t* gx[NX];
-    int lw[2], lx[NX];
+    int lw[WM], lx[NX];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WM; ++i) {
         const int row = r0 + 64 * i;
         gw[i] = a.codes_w + (int64_t)min(j0 + row, a.n0 - 1) * cstride + slot * 16;
         lw[i] = row * 4 + (slot ^ ((row >> 1) & 3));
@@ -2460,19 +2462,19 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
         gx[i] = a.codes_a + (int64_t)min(t0 + row, a.n1 - 1) * cstride + slot * 16;
         lx[i] = row * 4 + (slot ^ ((row >> 1) & 3));
     }
-    const uint8_t* gsw = a.scales_w + (int64_t)min(j0 + (t & 127), a.n0 - 1) * sstride;
+    const uint8_t* gsw = a.scales_w + (int64_t)min(j0 + (t % TM), a.n0 - 1) * sstride;
     const uint8_t* gsx = a.scales_a + (int64_t)min(t0 + (t % TN), a.n1 - 1) * sstride;
-    auto load_stage = [&](int ks, MxStage<TN>& r) {
+    auto load_stage = [&](int ks, MxStage<TN, TM>& r) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) r.w[i] = *reinterpret_cast<const u4v*>(gw[i] + ks * 64);
+        for (int i = 0; i < WM; ++i) r.w[i] = *reinterpret_cast<const u4v*>(gw[i] + ks * 64);
 #pragma unroll
         for (int i = 0; i < NX; ++i) r.x[i] = *reinterpret_cast<const u4v*>(gx[i] + ks * 64);
         if (t < TM) r.sw = *reinterpret_cast<const uint32_t*>(gsw + ks * 4);
         if (t < TN) r.sx = *reinterpret_cast<const uint32_t*>(gsx + ks * 4);
     };
-    auto store_stage = [&](const MxStage<TN>& r, int buf) {
+    auto store_stage = [&](const MxStage<TN, TM>& r, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) sW[buf][lw[i]] = r.w[i];
+        for (int i = 0; i < WM; ++i) sW[buf][lw[i]] = r.w[i];
 #pragma unroll
         for (int i = 0; i < NX; ++i) sA[buf][lx[i]] = r.x[i];
         if (t < TM) sWs[buf][t] = r.sw;
@@ -2484,7 +2486,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    MxStage<TN> ra = {}, rb = {};
+    MxStage<TN, TM> ra = {}, rb = {};
     load_stage(0, ra);
     if (nks > 1) load_stage(1, rb);
     store_stage(ra, 0);
@@ -2503,7 +2505,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
         }
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
-            const int r = wn * (TN / 2) + m * 16 + (lane & 15);
+            const int r = wn * (TN / WT) + m * 16 + (lane & 15);
             const u4v c = sA[buf][r * 4 + (kb ^ ((r >> 1) & 3))];
             bf[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
             sb[m] = (int)((sAs[buf][r] >> (8 * kb)) & 0xFFu);
@@ -2524,7 +2526,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
             const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
 #pragma unroll
             for (int nt = 0; nt < NB; ++nt) {
-                const int tok = t0 + wn * (TN / 2) + nt * 16 + (lane & 15);
+                const int tok = t0 + wn * (TN / WT) + nt * 16 + (lane & 15);
                 if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
             }
         }
@@ -3260,15 +3262,20 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
         return hipGetLastError();
     }
     const int tn = g.n1 >= 1024 ? 256 : 128;
-    a.tiles_j = (int32_t)((g.n0 + 127) / 128);
+    // 64-row tiles where 128-row tiles would fill at most half of the CUs
+    // (14336 rows up to 128 tokens: 23.2 -> 19.7 us at 65); with more tiles
+    // they measured slower
+    const int tm = (tn == 128 && 2 * ((g.n0 + 127) / 128) * ((g.n1 + 127) / 128) <= 256) ? 64 : 128;
+    a.tiles_j = (int32_t)((g.n0 + tm - 1) / tm);
     a.tiles_n = (int32_t)((g.n1 + tn - 1) / tn);
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
     if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
     a.tiles = (uint32_t)tiles;
     a.per_xcd = (int32_t)((tiles + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
-    if (tn == 256) k_mx_gemm<256><<<grid, kThreads, 0, s>>>(a);
-    else k_mx_gemm<128><<<grid, kThreads, 0, s>>>(a);
+    if (tn == 256) k_mx_gemm<256, 128><<<grid, kThreads, 0, s>>>(a);
+    else if (tm == 64) k_mx_gemm<128, 64><<<grid, kThreads, 0, s>>>(a);
+    else k_mx_gemm<128, 128><<<grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

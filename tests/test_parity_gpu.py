@@ -943,11 +943,13 @@ def mx_gpu(iq, r, rows, K):
 
 
 # n1 <= 64: the few-token kernel (1, 2 or 4 token tiles of 16); above, the
-# 128 x 128 tiles.  Odd step counts (K / 128) exercise the last half pair;
+# 128 x 128 tiles, 64 x 128 where the grid is small (each such case here; 1100
+# tokens take 128 x 256 tiles).  Odd step counts (K / 128) exercise the last half pair;
 # K = 8320 (65 steps) takes two LDS chunks of scale words, the second one step.
 @pytest.mark.parametrize("n0,K,n1", [(128, 128, 128), (200, 256, 75), (1, 128, 1), (257, 384, 129),
                                      (384, 1024, 256), (64, 512, 1100), (33, 4096, 40), (50, 640, 24),
-                                     (70, 2048, 64), (24, 8320, 3), (24, 8320, 50)])
+                                     (70, 2048, 64), (24, 8320, 3), (24, 8320, 50), (100, 384, 65), (5, 512, 128),
+                                     (130, 4096, 100)])
 def test_mx_gemm_parity(iq, O, S, n0, K, n1):
     """Weights and activations quantized to MXFP4 by the oracle; the GPU
     product against the oracle's exact sum, within the FP32 bound."""
@@ -999,7 +1001,7 @@ def c3_mxfp4(O, S):
     return O.quantize(S.make("c3"), "mxfp4", "block", want_xhat=False, threads=THREADS)
 
 
-@pytest.mark.parametrize("n1", [16, 2048])
+@pytest.mark.parametrize("n1", [16, 128, 2048])
 def test_mx_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
     """The c3 weights against n1 tokens of the a3 activations (both MXFP4
     from the oracle); rows sampled for the oracle."""
