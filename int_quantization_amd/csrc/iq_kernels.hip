@@ -2678,8 +2678,9 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
 // matrix cores then form exact products with the activations and sum in
 // FP32: no per-block fold, and 0.5 VALU instructions per weight.  E8M0 255
 // (NaN) gives NaN weights.  The kernels are the asymmetric INT4 consumer's
-// (LDS tiles from 65 tokens with k split in halves when the tile grid is
-// small, registers only below) with this dequantization.
+// (LDS tiles from 65 tokens, registers only below) with this
+// dequantization; small grids of 128-token tiles take 64-row tiles (TM = 64,
+// 1 x 4 waves of 64 x 32) and the rest of the small grids split k.
 // ---------------------------------------------------------------------------
 struct MxwGemmArgs {
     const uint8_t* codes;      // [n0, K / 2]
@@ -2708,32 +2709,35 @@ __device__ __forceinline__ float e8m0_scale(uint32_t E) {
     return E ? as_f(E << 23) : as_f(0x00400000u);   // 2^(E - 127); 2^-127 is an FP32 subnormal
 }
 
-template <int WN>
+template <int WN, int TM>
 __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
     constexpr int kTN = 64 * WN;             // tokens per tile
-    constexpr int kWords = 4 / WN;           // 16-byte code words (scale blocks) per thread and step
+    constexpr int WR = TM / 64, WT = 2 * WN / WR;   // waves along rows and along tokens
+    constexpr int NB = kTN / WT / 16;        // 16-token MFMA blocks per wave
+    constexpr int TPR = 128 * WN / TM;       // staging threads per weight row
+    constexpr int kWords = 4 / TPR;          // 16-byte code words (scale blocks) per thread and step
     constexpr int kX = 8;                    // 16-byte activation words per thread and step
-    __shared__ u4v tiles[(kGemmTile + kTN) * 16];
+    __shared__ u4v tiles[(TM + kTN) * 16];
     u4v* const sA = tiles;                   // weights BF16, swizzled rows of 128
-    u4v* const sB = tiles + kGemmTile * 16;  // activations BF16, same layout
+    u4v* const sB = tiles + TM * 16;         // activations BF16, same layout
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
     const uint32_t tile = idx / (uint32_t)a.ksplit;
     const int half = (int)(idx % (uint32_t)a.ksplit);
     const int jb = (int)(tile / (uint32_t)a.tiles_n), nb = (int)(tile % (uint32_t)a.tiles_n);
-    const int j0 = jb * kGemmTile, t0 = nb * kTN;
+    const int j0 = jb * TM, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / WT, wn = wave % WT;
     const int nks = a.K / 128;
     const int k0 = (int)((int64_t)half * nks / a.ksplit), k1 = (int)((int64_t)(half + 1) * nks / a.ksplit);
     const int ldc = a.K / 2, lds_ = a.K / 32;
-    f4v acc[4][4];
+    f4v acc[4][NB];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
     // staging: thread t moves 16-byte slot t & 15 of token rows t / 16 + 8 WN i
     // (i < 8), and the code words of weight row t / WN (blocks dp * kWords ..)
     const int xr0 = t >> 4, xs = t & 15;
@@ -2745,7 +2749,7 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
         gx[i] = a.x + (int64_t)min(t0 + row, a.n1 - 1) * a.K + xs * 8;
         lx[i] = row * 16 + (xs ^ (row & 15));
     }
-    const int dr = t / WN, dp = t % WN;
+    const int dr = t / TPR, dp = t % TPR;
     const int64_t dj = min(j0 + dr, a.n0 - 1);
     const u4v* gc = reinterpret_cast<const u4v*>(a.codes + dj * ldc + dp * 16 * kWords);
     const uint8_t* gs = a.scales + dj * lds_ + dp * kWords;
@@ -2778,29 +2782,31 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int slot = 4 * s + (lane >> 4);
-            bf8v af[4], bfr[4];
+            bf8v af[4], bfr[NB];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int r = wm * 64 + mt * 16 + (lane & 15);
                 af[mt] = __builtin_bit_cast(bf8v, sA[r * 16 + (slot ^ (r & 15))]);
             }
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int r = wn * 64 + nt * 16 + (lane & 15);
+            for (int nt = 0; nt < NB; ++nt) {
+                const int r = wn * (kTN / WT) + nt * 16 + (lane & 15);
                 bfr[nt] = __builtin_bit_cast(bf8v, sB[r * 16 + (slot ^ (r & 15))]);
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < NB; ++nt)
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
         }
     }
-    static_assert((kGemmTile + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
-    if (a.ksplit > 1 && (a.n1 & 15)) {
-        atomic_add_rows<2 * WN>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
-                                t0 + wn * 64);
-        return;
+    if constexpr (NB == 4) {
+        static_assert((TM + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
+        if (a.ksplit > 1 && (a.n1 & 15)) {
+            atomic_add_rows<2 * WN>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
+                                    t0 + wn * 64);
+            return;
+        }
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -2808,8 +2814,8 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
+            for (int nt = 0; nt < NB; ++nt) {
+                const int tok = t0 + wn * (kTN / WT) + nt * 16 + (lane & 15);
                 if (j < a.n0 && tok < a.n1) {
                     if (a.ksplit > 1) unsafeAtomicAdd(a.z + (int64_t)j * a.n1 + tok, acc[mt][nt][i]);
                     else a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
@@ -3296,11 +3302,16 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
         return hipGetLastError();
     }
     const int wn = g.n1 >= 256 ? 4 : 2;
-    a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
+    // Grids of 128-row tiles too small for two workgroups per CU take 64-row
+    // tiles (1 x 4 waves of 64 x 32): twice the work items without the k
+    // split's fill kernel and atomics (14336 rows, 128 tokens: 52.4 -> 41.4 us)
+    const int64_t tiles128 = (int64_t)((g.n0 + 127) / 128) * ((g.n1 + 64 * wn - 1) / (64 * wn));
+    const int tm = (wn == 2 && 2 * tiles128 <= 512) ? 64 : 128;
+    a.tiles_j = (int32_t)((g.n0 + tm - 1) / tm);
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
     const int64_t slots = 256 * (wn == 4 ? 1 : 2);
-    a.ksplit = (2 * tiles <= slots && g.K >= 256) ? 2 : 1;
+    a.ksplit = (tm == 128 && 2 * tiles <= slots && g.K >= 256) ? 2 : 1;
     const int64_t items = tiles * a.ksplit;
     if (items > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
     a.tiles = (uint32_t)items;
@@ -3310,8 +3321,9 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
         const int64_t nz = g.n0 * g.n1;
         k_zero_f32<<<zero_grid(nz), 256, 0, s>>>(a.z, nz);
     }
-    if (wn == 4) k_mxw_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
-    else k_mxw_gemm<2><<<grid, 256, 0, s>>>(a);
+    if (wn == 4) k_mxw_gemm<4, 128><<<grid, 256 * 2, 0, s>>>(a);
+    else if (tm == 64) k_mxw_gemm<2, 64><<<grid, 256, 0, s>>>(a);
+    else k_mxw_gemm<2, 128><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -415,7 +415,7 @@ def test_gemm_split_output_offsets(iq, O, S, off):
     12 bytes past a boundary gets the bits of an aligned output, and the
     floats just before and after it keep their values."""
     import torch
-    n0, K, n1 = 96, 512, 100                       # one tile: both GEMMs split k
+    n0, K, n1 = 96, 512, 300                       # small grids of 128- and 256-token tiles: both split k
     rzp = O.quantize((S.bf16_to_f32(S.make("c5", nrows=n0))[:, :K]).copy(), "int4zp", "block")
     qzp = iq.Quantized(to_device(rzp["codes"]), to_device(rzp["scales"]), None, None, None, "int4zp", "block",
                        n0, K, to_device(rzp["shifts"]))
