@@ -268,10 +268,8 @@ iq_status iq_mx_gemm(const iq_desc* d, const void* codes_w, const void* scales_w
  * scales 4-byte aligned (IQ_EALIGN).  N0, n1 and K must fit 31 bits, and
  * (N0/128)(n1/128) output tiles must stay below 2^31 (IQ_EUNSUPPORTED).
  * n1 == 0 or N0 == 0 is legal and writes nothing.  d->in_dtype and d->ld_in
- * are ignored.  No workspace.  From 256 tokens, grids too small to fill
- * the GPU split K in two halves as iq_zp_gemm does (z zeroed, two atomic
- * adds, the same bits on every call); below, small grids use 64-row tiles
- * instead and write z directly.
+ * are ignored.  No workspace.  Grids too small to fill the GPU use 64-row
+ * tiles; K is never split and z is written directly, once.
  */
 iq_status iq_mxw_gemm(const iq_desc* d, const void* codes, const void* scales, const void* x, int32_t x_dtype,
                       int64_t n1, float* z, hipStream_t stream);

@@ -2679,8 +2679,8 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemv(MxGemmArgs a) {
 // FP32: no per-block fold, and 0.5 VALU instructions per weight.  E8M0 255
 // (NaN) gives NaN weights.  The kernels are the asymmetric INT4 consumer's
 // (LDS tiles from 65 tokens, registers only below) with this
-// dequantization; small grids of 128-token tiles take 64-row tiles (TM = 64,
-// 1 x 4 waves of 64 x 32) and the rest of the small grids split k.
+// dequantization; where the INT4 kernel splits k for small grids, these
+// take 64-row tiles (TM = 64, 1 x 4 waves of 64 x 32).
 // ---------------------------------------------------------------------------
 struct MxwGemmArgs {
     const uint8_t* codes;      // [n0, K / 2]
@@ -2689,8 +2689,7 @@ struct MxwGemmArgs {
     float* z;                  // [n0, n1]
     int32_t n0, n1, K;
     int32_t tiles_j, tiles_n, per_xcd;
-    uint32_t tiles;            // tiles_j * tiles_n * ksplit (checked on the host)
-    int32_t ksplit;            // 1, or 2: k halves added atomically into a zeroed z
+    uint32_t tiles;            // tiles_j * tiles_n (checked on the host)
 };
 
 // 8 weights of one code word (element 2t in the low nibble of byte t) as
@@ -2723,15 +2722,12 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
-    const uint32_t tile = idx / (uint32_t)a.ksplit;
-    const int half = (int)(idx % (uint32_t)a.ksplit);
-    const int jb = (int)(tile / (uint32_t)a.tiles_n), nb = (int)(tile % (uint32_t)a.tiles_n);
+    const int jb = (int)(idx / (uint32_t)a.tiles_n), nb = (int)(idx % (uint32_t)a.tiles_n);
     const int j0 = jb * TM, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WT, wn = wave % WT;
     const int nks = a.K / 128;
-    const int k0 = (int)((int64_t)half * nks / a.ksplit), k1 = (int)((int64_t)(half + 1) * nks / a.ksplit);
     const int ldc = a.K / 2, lds_ = a.K / 32;
     f4v acc[4][NB];
 #pragma unroll
@@ -2764,8 +2760,8 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
             rs[v] = gs[ks * 4 + v];
         }
     };
-    if (k0 < k1) load_step(k0);
-    for (int ks = k0; ks < k1; ++ks) {
+    load_step(0);
+    for (int ks = 0; ks < nks; ++ks) {
         __syncthreads();                     // every wave is done with the previous step's tiles
 #pragma unroll
         for (int i = 0; i < kX; ++i) sB[lx[i]] = rx[i];
@@ -2777,7 +2773,7 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
             for (int q = 0; q < 4; ++q)
                 sA[dr * 16 + ((dp * 4 * kWords + 4 * v + q) ^ (dr & 15))] = mx_bf16x8(cw[q], sc, rs[v] == 255u);
         }
-        if (ks + 1 < k1) load_step(ks + 1);     // lands during this step's MFMAs
+        if (ks + 1 < nks) load_step(ks + 1);     // lands during this step's MFMAs
         lds_barrier();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -2800,14 +2796,6 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
                     acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
         }
     }
-    if constexpr (NB == 4) {
-        static_assert((TM + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
-        if (a.ksplit > 1 && (a.n1 & 15)) {
-            atomic_add_rows<2 * WN>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
-                                    t0 + wn * 64);
-            return;
-        }
-    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -2816,10 +2804,7 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NB; ++nt) {
                 const int tok = t0 + wn * (kTN / WT) + nt * 16 + (lane & 15);
-                if (j < a.n0 && tok < a.n1) {
-                    if (a.ksplit > 1) unsafeAtomicAdd(a.z + (int64_t)j * a.n1 + tok, acc[mt][nt][i]);
-                    else a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
-                }
+                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
             }
         }
 }
@@ -3301,26 +3286,24 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
         else k_mxw_gemv<4, false, 2><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
-    const int wn = g.n1 >= 256 ? 4 : 2;
-    // Grids of 128-row tiles too small for two workgroups per CU take 64-row
+    // Grids of 128 x 128 tiles too small for two workgroups per CU take 64-row
     // tiles (1 x 4 waves of 64 x 32): twice the work items without the k
-    // split's fill kernel and atomics (14336 rows, 128 tokens: 52.4 -> 41.4 us)
-    const int64_t tiles128 = (int64_t)((g.n0 + 127) / 128) * ((g.n1 + 64 * wn - 1) / (64 * wn));
+    // split's fill kernel and atomics (14336 rows, 128 tokens: 52.4 -> 41.4 us;
+    // 256 tokens: 66.3 -> 60.6 us against 256-token tiles with the split)
+    const int64_t rows128 = (g.n0 + 127) / 128;
+    const bool small = 2 * rows128 * ((g.n1 + 127) / 128) <= 512;
+    const int wn = (g.n1 >= 256 && !small) ? 4 : 2;
+    const int64_t tiles128 = rows128 * ((g.n1 + 64 * wn - 1) / (64 * wn));
     const int tm = (wn == 2 && 2 * tiles128 <= 512) ? 64 : 128;
     a.tiles_j = (int32_t)((g.n0 + tm - 1) / tm);
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
+    // (a grid of 256-token tiles small enough to want a k split always has
+    // 128 x 128 tiles few enough for this form, so no split is needed)
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
-    const int64_t slots = 256 * (wn == 4 ? 1 : 2);
-    a.ksplit = (tm == 128 && 2 * tiles <= slots && g.K >= 256) ? 2 : 1;
-    const int64_t items = tiles * a.ksplit;
-    if (items > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
-    a.tiles = (uint32_t)items;
-    a.per_xcd = (int32_t)((items + 7) / 8);
+    if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+    a.tiles = (uint32_t)tiles;
+    a.per_xcd = (int32_t)((tiles + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
-    if (a.ksplit > 1) {
-        const int64_t nz = g.n0 * g.n1;
-        k_zero_f32<<<zero_grid(nz), 256, 0, s>>>(a.z, nz);
-    }
     if (wn == 4) k_mxw_gemm<4, 128><<<grid, 256 * 2, 0, s>>>(a);
     else if (tm == 64) k_mxw_gemm<2, 64><<<grid, 256, 0, s>>>(a);
     else k_mxw_gemm<2, 128><<<grid, 256, 0, s>>>(a);

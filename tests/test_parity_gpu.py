@@ -410,12 +410,13 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
 
 @pytest.mark.parametrize("off", [1, 2, 3])
 def test_gemm_split_output_offsets(iq, O, S, off):
-    """A call whose k is split zeroes z first, with 16-byte stores from the
-    first 16-byte boundary and single floats around them: an output 4, 8 or
-    12 bytes past a boundary gets the bits of an aligned output, and the
-    floats just before and after it keep their values."""
+    """An INT4 call whose k is split zeroes z first, with 16-byte stores from
+    the first 16-byte boundary and single floats around them, then adds row
+    by row; the W4A16 call (64-row tiles) writes z directly.  Either way an
+    output 4, 8 or 12 bytes past a boundary gets the bits of an aligned
+    output, and the floats just before and after it keep their values."""
     import torch
-    n0, K, n1 = 96, 512, 300                       # small grids of 128- and 256-token tiles: both split k
+    n0, K, n1 = 96, 512, 300                       # small grid: INT4 splits k (128-token tiles)
     rzp = O.quantize((S.bf16_to_f32(S.make("c5", nrows=n0))[:, :K]).copy(), "int4zp", "block")
     qzp = iq.Quantized(to_device(rzp["codes"]), to_device(rzp["scales"]), None, None, None, "int4zp", "block",
                        n0, K, to_device(rzp["shifts"]))
