@@ -408,6 +408,28 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("n1", [1, 24, 64, 100, 256])
+def test_gemm_repeat_bit_identical(iq, O, S, n1):
+    """Every consumer path returns the same bits on every call: the INT4
+    k split (atomic adds, direct at 64 tokens and row by row at 100), the
+    W4A16 and FP4 64-row tiles and the few-token kernels, on a 1024-row
+    grid over five calls with other work between them."""
+    import torch
+    n0, K = 1024, 1024
+    rzp = O.quantize((S.bf16_to_f32(S.make("c5", nrows=n0))[:, :K]).copy(), "int4zp", "block")
+    qzp = iq.Quantized(to_device(rzp["codes"]), to_device(rzp["scales"]), None, None, None, "int4zp", "block",
+                       n0, K, to_device(rzp["shifts"]))
+    qw = mx_gpu(iq, mx_operand(O, S, n0, K, seed=51, sigma=0.02, outlier_axis=S.AXIS_ROWS), n0, K)
+    qa = mx_gpu(iq, mx_operand(O, S, n1, K, seed=52, sigma=1.0, outlier_axis=S.AXIS_COLS), n1, K)
+    x = to_device(S.make("c2", nrows=n1)[:, :K].copy())
+    calls = (lambda: iq.zp_gemm(qzp, x), lambda: iq.mxw_gemm(qw, x), lambda: iq.mx_gemm(qw, qa))
+    first = [c().cpu().view(torch.int32) for c in calls]
+    for rep in range(4):
+        iq.quantize(x, "e4m3", "row", stats=True)         # other work on the stream between the calls
+        for c, want in zip(calls, first):
+            assert torch.equal(c().cpu().view(torch.int32), want), rep
+
+
 @pytest.mark.parametrize("off", [1, 2, 3])
 def test_gemm_split_output_offsets(iq, O, S, off):
     """An INT4 call whose k is split zeroes z first, with 16-byte stores from
