@@ -2243,19 +2243,25 @@ __device__ __forceinline__ void atomic_add_rows(const f4v (&acc)[4][4], float* b
     }
 }
 
-// WN waves along the tokens (a tile of 128 weight rows x 64 WN tokens,
-// 128 WN threads): the dequantization of a weight tile is shared by 64 WN
-// tokens, so a wider tile spends fewer VALU cycles per MFMA.
+// A tile of 128 weight rows x TNX tokens with NW waves in 2 rows of NW / 2
+// (wave tiles 64 x TNX / (NW / 2)): 64 x 64 wave tiles for 128 and 256
+// tokens (4 and 8 waves), 64 x 32 for 64 tokens (4 waves).  The
+// dequantization of a weight tile is shared by all its tokens, so a wider
+// tile spends fewer VALU cycles per MFMA.
 // A grid too small to give every CU two groups in flight splits k in two
 // halves (ksplit = 2): each work item sums its half and adds it atomically
 // into z, which a fill kernel zeroed first.  With exactly two addends on a
 // +0 start the sum is a + b, rounded once, in either order, so the result
 // does not depend on which half lands first.
-template <int WN>
-__global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
-    constexpr int kTN = 64 * WN;             // tokens per tile
-    constexpr int kWords = 4 / WN;           // 16-byte code words per thread and group
-    constexpr int kX = 8;                    // 16-byte activation words per thread and group
+template <int TNX, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_zp_gemm(ZpGemmArgs a) {
+    constexpr int kTN = TNX;                 // tokens per tile
+    constexpr int NTH = 64 * NW;             // threads
+    constexpr int WT = NW / 2;               // waves along the tokens (2 along the rows)
+    constexpr int NB = kTN / WT / 16;        // 16-token MFMA blocks per wave
+    constexpr int TPR = NTH / kGemmTile;     // staging threads per weight row
+    constexpr int kWords = 4 / TPR;          // 16-byte code words per thread and group
+    constexpr int kX = kTN * 16 / NTH;       // 16-byte activation words per thread and group
     __shared__ u4v tiles[(kGemmTile + kTN) * 16];
     u4v* const sA = tiles;                   // weights (w - sh) BF16, swizzled rows of 128
     u4v* const sB = tiles + kGemmTile * 16;  // activations BF16, same layout
@@ -2270,29 +2276,29 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
     const int j0 = jb * kGemmTile, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / WT, wn = wave % WT;
     const int ng = a.K / 128;
     // the groups [g0, g1) of this work item's part of k
     const int g0 = (int)((int64_t)half * ng / a.ksplit), g1 = (int)((int64_t)(half + 1) * ng / a.ksplit);
     const int ldc = a.K / 2;             // code bytes per weight row
-    f4v acc[4][4];
+    f4v acc[4][NB];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    // staging: thread t moves 16-byte slot t & 15 of token rows t / 16 + 8 WN i
-    // (i < 8), the codes of weight row t / WN (32 kWords from dp * 32 kWords)
+        for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    // staging: thread t moves 16-byte slot t & 15 of token rows t / 16 + NTH / 16 i
+    // (i < kX), the codes of weight row t / TPR (32 kWords from dp * 32 kWords)
     // with the row's shift byte, and (t < 128) the scale of row t
     const int xr0 = t >> 4, xs = t & 15;
     const uint16_t* gx[kX];
     int lx[kX];
 #pragma unroll
     for (int i = 0; i < kX; ++i) {
-        const int row = xr0 + 8 * WN * i;
+        const int row = xr0 + NTH / 16 * i;
         gx[i] = a.x + (int64_t)min(t0 + row, a.n1 - 1) * a.K + xs * 8;
         lx[i] = row * 16 + (xs ^ (row & 15));
     }
-    const int dr = t / WN, dp = t % WN;
+    const int dr = t / TPR, dp = t % TPR;
     const int64_t dj = min(j0 + dr, a.n0 - 1);
     const u4v* gc = reinterpret_cast<const u4v*>(a.codes + dj * ldc + dp * 16 * kWords);
     const uint8_t* gsh = a.shifts + dj * (ng / 2);
@@ -2324,29 +2330,29 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
         if (t < kGemmTile) sS[t] = rsc;
         if (g + 1 < g1) load_group(g + 1);   // lands during this group's MFMAs
         lds_barrier();
-        f4v accg[4][4];
+        f4v accg[4][NB];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) accg[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NB; ++nt) accg[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int slot = 4 * s + (lane >> 4);
-            bf8v af[4], bfr[4];
+            bf8v af[4], bfr[NB];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const int r = wm * 64 + mt * 16 + (lane & 15);
                 af[mt] = __builtin_bit_cast(bf8v, sA[r * 16 + (slot ^ (r & 15))]);
             }
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int r = wn * 64 + nt * 16 + (lane & 15);
+            for (int nt = 0; nt < NB; ++nt) {
+                const int r = wn * (kTN / WT) + nt * 16 + (lane & 15);
                 bfr[nt] = __builtin_bit_cast(bf8v, sB[r * 16 + (slot ^ (r & 15))]);
             }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < NB; ++nt)
                     accg[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], accg[mt][nt], 0, 0, 0);
         }
 #pragma unroll
@@ -2355,14 +2361,16 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const float sc = sS[wm * 64 + mt * 16 + 4 * (lane >> 4) + i];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[mt][nt][i] = __builtin_fmaf(sc, accg[mt][nt][i], acc[mt][nt][i]);
+                for (int nt = 0; nt < NB; ++nt) acc[mt][nt][i] = __builtin_fmaf(sc, accg[mt][nt][i], acc[mt][nt][i]);
             }
     }
-    static_assert((kGemmTile + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
-    if (a.ksplit > 1 && (a.n1 & 15)) {
-        atomic_add_rows<2 * WN>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
+    if constexpr (NB == 4) {
+        static_assert((kGemmTile + kTN) * 16 * 16 >= 4 * 64 * 64 * 4, "four 64 x 64 blocks fit in the tiles");
+        if (a.ksplit > 1 && (a.n1 & 15)) {
+            atomic_add_rows<NW>(acc, reinterpret_cast<float*>(tiles), wave, lane, a.z, a.n0, a.n1, j0 + wm * 64,
                                 t0 + wn * 64);
-        return;
+            return;
+        }
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -2370,8 +2378,8 @@ __global__ __launch_bounds__(128 * WN, 2) void k_zp_gemm(ZpGemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int tok = t0 + wn * 64 + nt * 16 + (lane & 15);
+            for (int nt = 0; nt < NB; ++nt) {
+                const int tok = t0 + wn * (kTN / WT) + nt * 16 + (lane & 15);
                 if (j < a.n0 && tok < a.n1) {
                     if (a.ksplit > 1) unsafeAtomicAdd(a.z + (int64_t)j * a.n1 + tok, acc[mt][nt][i]);
                     else a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
@@ -3216,12 +3224,16 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
         else k_zp_gemv<2, false, 4><<<grid, kThreads, 0, s>>>(a);
         return hipGetLastError();
     }
-    const int wn = gemm_token_waves(g.n1);
+    // up to 64 tokens: 64-token tiles (2 x 2 waves of 64 x 32, 152 registers),
+    // which measured 77 us at 33-64 tokens against 104-110 us for 128-token
+    // tiles; wn 1 stands for them
+    const int wn = g.n1 <= 64 ? 1 : gemm_token_waves(g.n1);
     a.tiles_j = (int32_t)((g.n0 + kGemmTile - 1) / kGemmTile);
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
-    // resident workgroups per CU: two of 256 threads, one of 512 (registers)
-    const int64_t slots = 256 * (wn == 4 ? 1 : 2);
+    // resident workgroups per CU (registers): one with 256-token tiles, two
+    // with 128-token tiles, three with 64-token tiles
+    const int64_t slots = 256 * (wn == 4 ? 1 : wn == 2 ? 2 : 3);
     a.ksplit = (2 * tiles <= slots && g.K >= 256) ? 2 : 1;
     const int64_t items = tiles * a.ksplit;
     if (items > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
@@ -3232,8 +3244,9 @@ hipError_t launch_zp_gemm(const ZpGemmLaunch& g, hipStream_t s) {
         const int64_t nz = g.n0 * g.n1;
         k_zero_f32<<<zero_grid(nz), 256, 0, s>>>(a.z, nz);
     }
-    if (wn == 4) k_zp_gemm<4><<<grid, 256 * 2, 0, s>>>(a);
-    else k_zp_gemm<2><<<grid, 256, 0, s>>>(a);
+    if (wn == 4) k_zp_gemm<256, 8><<<grid, 256 * 2, 0, s>>>(a);
+    else if (wn == 2) k_zp_gemm<128, 4><<<grid, 256, 0, s>>>(a);
+    else k_zp_gemm<64, 4><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

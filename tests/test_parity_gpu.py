@@ -839,7 +839,8 @@ def zp_gemm_case(iq, O, S, n0, K, n1, seed, x_scale=1.0):
 
 
 # n1 <= 32: the few-token kernel (1 or 2 token tiles of 16, stripes of 32
-# weight rows up to 8 tokens and of 64 above); above: 128- or
+# weight rows up to 8 tokens and of 64 above); up to 64 tokens 64-token
+# tiles; above: 128- or
 # 256-token tiles, whose k is split in two halves added atomically when the
 # tile grid is small (every tiled case here; K = 256 gives each half one group).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (32, 1024, 300), (1, 256, 1),
