@@ -14,8 +14,10 @@
  * - Pointers named x, codes, scales, global_scale, stats, xhat, workspace,
  *   amax_in and amax_out are DEVICE pointers (HIP device memory of the current
  *   device).  The descriptor is a HOST pointer.  The caller allocates and
- *   owns every buffer; the library allocates nothing, keeps no state
- *   between calls, and never synchronizes.
+ *   owns every buffer; the library allocates nothing and never
+ *   synchronizes.  Between calls it keeps only a cache of occupancy queries
+ *   per kernel and device (host memory, guarded by a mutex), and the
+ *   workspace tickets it leaves at zero.
  * - All work is enqueued on `stream` (0 = the null stream).  Functions
  *   return before the GPU finishes; outputs are valid after the caller
  *   synchronizes with the stream.
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define IQ_ABI_VERSION 1
+#define IQ_ABI_VERSION 2
 
 typedef enum {
     IQ_OK = 0,
@@ -128,8 +130,13 @@ size_t iq_workspace_bytes(const iq_desc* d);
  *   global_scale     NVFP4 output s_global (required for NVFP4, else ignored)
  *   stats            optional output (NULL skips the statistics)
  *   xhat             optional dequantized output [rows, cols] of xhat_dtype
- *   workspace        iq_workspace_bytes(d) bytes of device scratch; the
- *                    call overwrites it, concurrent calls need separate ones
+ *   workspace        iq_workspace_bytes(d) bytes of device scratch, zero-filled
+ *                    before its first use (e.g. hipMemset once, or torch.zeros);
+ *                    every call leaves it ready for the next one.  The
+ *                    workgroups of a call count themselves on it to decide
+ *                    which one folds the partial statistics (and the
+ *                    per-tensor absmax), so concurrent calls need separate
+ *                    workspaces
  */
 iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales,
                       float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype,
@@ -137,8 +144,13 @@ iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales
 
 /*
  * Dequantize: x^ = s * decode(q), bit-identical to the x^ of iq_quantize.
+ * Sections "FP8" (x^ = s * round(x / s): the code's value times the scale)
+ * and "FP4 / MXFP4 / NVFP4" (MXFP4: E2M1 value times 2^(E - 127); NVFP4:
+ * E2M1 value times s_global times the E4M3 block scale; INT4: q times the
+ * FP16 group scale).
  * d->in_dtype and d->ld_in are ignored; xhat is dense [rows, cols] of
  * xhat_dtype (BF16 output is the FP32 x^ rounded to nearest even).
+ * No workspace.  Errors as for iq_quantize.
  */
 iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales,
                         const float* global_scale, void* xhat, int32_t xhat_dtype,
@@ -147,7 +159,8 @@ iq_status iq_dequantize(const iq_desc* d, const void* codes, const void* scales,
 /*
  * Per-tensor absmax over the finite elements of x (the per-tensor "alpha"
  * of section "FP8", the global amax of NVFP4), written to amax_out (device
- * float32 [1]).  Only d->in_dtype, rows, cols and ld_in are used.
+ * float32 [1]).  Only d->in_dtype, rows, cols and ld_in are used.  The
+ * workspace rules are those of iq_quantize (zero-filled before first use).
  */
 iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* workspace,
                   hipStream_t stream);

@@ -228,9 +228,45 @@ def empty_outputs(d: IQDesc, device, fmt: str, gran: str):
 
 
 def workspace_for(d: IQDesc, device):
+    """A zero-filled workspace (the library's tickets start at zero and every
+    call leaves them there); 256-byte aligned."""
     torch = _torch()
     n = iq_workspace_bytes(d)
-    return torch.empty((n + 255) // 256 * 64, dtype=torch.float32, device=device)  # 256-byte aligned
+    return torch.zeros((n + 255) // 256 * 64, dtype=torch.float32, device=device)
+
+
+def _check_buffer(t, nbytes: int, what: str, device, dtype=None):
+    """A caller-supplied device buffer must be contiguous, on the input's
+    device, of the expected dtype and hold at least nbytes."""
+    if t is None:
+        raise ValueError(f"{what} is missing")
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, the input on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _check_out(out: "Quantized", d: IQDesc, fmt: str, gran: str, device):
+    """A Quantized passed as `out` must match the descriptor of this call."""
+    torch = _torch()
+    if out.fmt != fmt or out.gran != gran or out.rows != d.rows or out.cols != d.cols:
+        raise ValueError("out was made for another format, granularity or shape")
+    _check_buffer(out.codes, iq_codes_bytes(d), "out.codes", device, torch.uint8)
+    _check_buffer(out.scales, iq_scales_bytes(d), "out.scales", device)
+    if fmt == "nvfp4":
+        _check_buffer(out.global_scale, 4, "out.global_scale", device, torch.float32)
+    if fmt == "int4zp":
+        _check_buffer(out.shifts, iq_shifts_bytes(d), "out.shifts", device, torch.uint8)
+    if out.stats_buf is not None:
+        _check_buffer(out.stats_buf, ctypes.sizeof(IQStats), "out.stats_buf", device)
+    if out.xhat is not None:
+        if out.xhat.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out.xhat must be float32 or bfloat16")
+        _check_buffer(out.xhat, d.rows * d.cols * out.xhat.element_size(), "out.xhat", device)
 
 
 @dataclass
@@ -271,7 +307,13 @@ def quantize(x, fmt: str, gran: str, *, stats: bool = True, xhat_dtype=None, col
         shifts = (torch.empty((d.rows, d.cols // 256), dtype=torch.uint8, device=x.device)
                   if fmt == "int4zp" else None)
         out = Quantized(codes, scales, gscale, xh, sbuf, fmt, gran, d.rows, d.cols, shifts)
-    ws = workspace if workspace is not None else workspace_for(d, x.device)
+    else:
+        _check_out(out, d, fmt, gran, x.device)
+    if workspace is None:
+        ws = workspace_for(d, x.device)
+    else:
+        _check_buffer(workspace, iq_workspace_bytes(d), "workspace", x.device)
+        ws = workspace
     xdt = IQ_F32
     if out.xhat is not None:
         xdt = IQ_F32 if out.xhat.dtype == torch.float32 else IQ_BF16
@@ -301,6 +343,16 @@ def dequantize(q: Quantized, out_dtype=None, out=None, stream=None):
     d = make_desc(q.fmt, q.gran, q.rows, q.cols)
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    elif out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (q.rows, q.cols):
+        raise ValueError("out must be a float32 or bfloat16 [rows, cols] tensor")
+    else:
+        _check_buffer(out, q.rows * q.cols * out.element_size(), "out", q.codes.device)
+    _check_buffer(q.codes, iq_codes_bytes(d), "codes", q.codes.device, torch.uint8)
+    _check_buffer(q.scales, iq_scales_bytes(d), "scales", q.codes.device)
+    if q.fmt == "nvfp4":
+        _check_buffer(q.global_scale, 4, "global_scale", q.codes.device, torch.float32)
+    if q.fmt == "int4zp":
+        _check_buffer(q.shifts, iq_shifts_bytes(d), "shifts", q.codes.device, torch.uint8)
     dt = IQ_F32 if out.dtype == torch.float32 else IQ_BF16
     if q.fmt == "int4zp":
         st = iq_dequantize_zp(d, q.codes.data_ptr(), q.scales.data_ptr(), _ptr(q.shifts), out.data_ptr(), dt,
@@ -317,8 +369,23 @@ def amax(x, workspace=None, stream=None):
     torch = _torch()
     d = desc_for(x, "e4m3", "tensor")
     out = torch.empty((1,), dtype=torch.float32, device=x.device)
-    ws = workspace if workspace is not None else workspace_for(d, x.device)
+    if workspace is None:
+        ws = workspace_for(d, x.device)
+    else:
+        _check_buffer(workspace, iq_workspace_bytes(d), "workspace", x.device)
+        ws = workspace
     _check(iq_amax(d, x.data_ptr(), out.data_ptr(), ws.data_ptr(), _stream(stream)), "iq_amax")
+    return out
+
+
+def _gemm_out(out, n0: int, n1: int, device):
+    """z float32 [n0, n1]: a new tensor, or the caller's after checks."""
+    torch = _torch()
+    if out is None:
+        return torch.empty((n0, n1), dtype=torch.float32, device=device)
+    if tuple(out.shape) != (n0, n1):
+        raise ValueError(f"out must be [{n0}, {n1}], got {tuple(out.shape)}")
+    _check_buffer(out, n0 * n1 * 4, "out", device, torch.float32)
     return out
 
 
@@ -332,9 +399,11 @@ def zp_gemm(q: "Quantized", x, out=None, stream=None):
     if x.dim() != 2 or x.shape[1] != q.cols or x.dtype != torch.bfloat16 or not x.is_contiguous():
         raise ValueError("x must be a contiguous BF16 [n1, K] tensor")
     n1 = x.shape[0]
-    if out is None:
-        out = torch.empty((q.rows, n1), dtype=torch.float32, device=x.device)
+    out = _gemm_out(out, q.rows, n1, x.device)
     d = make_desc("int4zp", "block", q.rows, q.cols)
+    _check_buffer(q.codes, iq_codes_bytes(d), "codes", x.device, torch.uint8)
+    _check_buffer(q.scales, iq_scales_bytes(d), "scales", x.device, torch.float32)
+    _check_buffer(q.shifts, iq_shifts_bytes(d), "shifts", x.device, torch.uint8)
     st = iq_zp_gemm(d, q.codes.data_ptr(), q.scales.data_ptr(), q.shifts.data_ptr(), x.data_ptr(), IQ_BF16, n1,
                     out.data_ptr(), _stream(stream))
     _check(st, "iq_zp_gemm")
@@ -351,9 +420,14 @@ def mx_gemm(qw: "Quantized", qa: "Quantized", out=None, stream=None):
     if qa.cols != qw.cols:
         raise ValueError("operands disagree on K")
     n1 = qa.rows
-    if out is None:
-        out = torch.empty((qw.rows, n1), dtype=torch.float32, device=qw.codes.device)
+    out = _gemm_out(out, qw.rows, n1, qw.codes.device)
     d = make_desc("mxfp4", "block", qw.rows, qw.cols)
+    da = make_desc("mxfp4", "block", qa.rows, qa.cols)
+    dev = qw.codes.device
+    _check_buffer(qw.codes, iq_codes_bytes(d), "weight codes", dev, torch.uint8)
+    _check_buffer(qw.scales, iq_scales_bytes(d), "weight scales", dev, torch.uint8)
+    _check_buffer(qa.codes, iq_codes_bytes(da), "activation codes", dev, torch.uint8)
+    _check_buffer(qa.scales, iq_scales_bytes(da), "activation scales", dev, torch.uint8)
     st = iq_mx_gemm(d, qw.codes.data_ptr(), qw.scales.data_ptr(), qa.codes.data_ptr(), qa.scales.data_ptr(), n1,
                     out.data_ptr(), _stream(stream))
     _check(st, "iq_mx_gemm")
@@ -370,9 +444,10 @@ def mxw_gemm(qw: "Quantized", x, out=None, stream=None):
     if x.dim() != 2 or x.shape[1] != qw.cols or x.dtype != torch.bfloat16 or not x.is_contiguous():
         raise ValueError("x must be a contiguous BF16 [n1, K] tensor")
     n1 = x.shape[0]
-    if out is None:
-        out = torch.empty((qw.rows, n1), dtype=torch.float32, device=x.device)
+    out = _gemm_out(out, qw.rows, n1, x.device)
     d = make_desc("mxfp4", "block", qw.rows, qw.cols)
+    _check_buffer(qw.codes, iq_codes_bytes(d), "weight codes", x.device, torch.uint8)
+    _check_buffer(qw.scales, iq_scales_bytes(d), "weight scales", x.device, torch.uint8)
     st = iq_mxw_gemm(d, qw.codes.data_ptr(), qw.scales.data_ptr(), x.data_ptr(), IQ_BF16, n1, out.data_ptr(),
                      _stream(stream))
     _check(st, "iq_mxw_gemm")

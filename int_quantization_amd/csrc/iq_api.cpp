@@ -44,6 +44,12 @@ static_assert(iqk::R_MX_NEAREST == IQ_FLAG_MX_ROUND_NEAREST && iqk::R_MX_UP == I
                   iqk::R_NV_RNE == IQ_FLAG_NV_SCALE_RNE,
               "rule bits are the public flag values");
 
+// Whether rows x cols fits the 31-bit chunk indices of the kernels.
+bool chunks_fit(int64_t rows, int64_t cols) {
+    if (rows > ((int64_t)1 << 31) - 1 || cols / iqk::kChunk > ((int64_t)1 << 31)) return false;
+    return rows == 0 || cols == 0 || rows * (cols / iqk::kChunk) < ((int64_t)1 << 31);
+}
+
 // Shape rules shared by every entry point.  cols must be a multiple of the
 // 8-element chunk (16 for the 4-bit formats' blocks anyway) and of the
 // block; the chunk count must fit 31 bits.
@@ -56,15 +62,20 @@ iq_status check_shape(const iq_desc* d, bool need_in_dtype) {
     if (d->cols % iqk::kChunk) return IQ_EINVAL;
     if (b > 0 && d->cols % b) return IQ_EINVAL;
     if (d->fmt == IQ_INT4_ZP && d->cols % 256) return IQ_EINVAL;   // whole shift bytes per row
-    if (d->rows > 0 && d->cols > 0 && d->rows * (d->cols / iqk::kChunk) >= (int64_t)1 << 31)
-        return IQ_EUNSUPPORTED;
-    if (d->rows > ((int64_t)1 << 31) - 1) return IQ_EUNSUPPORTED;
+    if (!chunks_fit(d->rows, d->cols)) return IQ_EUNSUPPORTED;
     if (!flags_valid(d)) return IQ_EUNSUPPORTED;
     return IQ_OK;
 }
 
+// The kernels index chunks with 32 bits and element offsets row * ld_in
+// with 64 bits: the chunk count must stay below 2^31 (chunks_fit) and
+// rows * ld_in at most 2^59 elements, so byte offsets stay far inside 64
+// bits.  Each factor is bounded before any product is formed.
 iq_status check_input(const iq_desc* d, const void* x) {
     if (d->ld_in < d->cols) return IQ_EINVAL;
+    if (d->ld_in > ((int64_t)1 << 40)) return IQ_EUNSUPPORTED;
+    int64_t span = 0;
+    if (__builtin_mul_overflow(d->rows, d->ld_in, &span) || span > ((int64_t)1 << 59)) return IQ_EUNSUPPORTED;
     if (d->rows > 0 && d->cols > 0) {
         if (!x) return IQ_EINVAL;
         if (!aligned(x, 16)) return IQ_EALIGN;
@@ -131,26 +142,35 @@ size_t iq_shifts_bytes(const iq_desc* d) {
 
 namespace {
 
-iq_status quantize_impl(const iq_desc* d, const void* x, const float* static_amax, void* codes, void* scales,
-                        float* global_scale, uint8_t* shifts, iq_stats* stats, void* xhat, int32_t xhat_dtype,
-                        void* workspace, hipStream_t stream) {
+// Every check of a quantize call except the workspace's.
+iq_status check_quantize(const iq_desc* d, const void* x, void* codes, void* scales, float* global_scale,
+                         uint8_t* shifts, iq_stats* stats, void* xhat, int32_t xhat_dtype) {
     iq_status st = check_shape(d, true);
     if (st != IQ_OK) return st;
     if ((st = check_input(d, x)) != IQ_OK) return st;
     const bool empty = d->rows == 0 || d->cols == 0;
     const bool needs_scale_slot = d->gran == IQ_PER_TENSOR || !empty;
-    if (!workspace) return IQ_EINVAL;
     if (!empty && !codes) return IQ_EINVAL;
     if (needs_scale_slot && !scales) return IQ_EINVAL;
     if (d->fmt == IQ_NVFP4 && !global_scale) return IQ_EINVAL;
     if (d->fmt == IQ_INT4_ZP && !empty && !shifts) return IQ_EINVAL;
     if (xhat && !is_bf16_or_f32(xhat_dtype)) return IQ_EINVAL;
-    if (!aligned(workspace, 256)) return IQ_EALIGN;
     if (codes && !aligned(codes, 16)) return IQ_EALIGN;
     if (scales && !aligned(scales, 4)) return IQ_EALIGN;
     if (global_scale && !aligned(global_scale, 4)) return IQ_EALIGN;
     if (stats && !aligned(stats, 8)) return IQ_EALIGN;
     if (xhat && !aligned(xhat, 16)) return IQ_EALIGN;
+    return IQ_OK;
+}
+
+iq_status quantize_impl(const iq_desc* d, const void* x, const float* static_amax, void* codes, void* scales,
+                        float* global_scale, uint8_t* shifts, iq_stats* stats, void* xhat, int32_t xhat_dtype,
+                        void* workspace, hipStream_t stream) {
+    iq_status st = check_quantize(d, x, codes, scales, global_scale, shifts, stats, xhat, xhat_dtype);
+    if (st != IQ_OK) return st;
+    if (!workspace) return IQ_EINVAL;
+    if (!aligned(workspace, 256)) return IQ_EALIGN;
+    const bool empty = d->rows == 0 || d->cols == 0;
 
     iqk::QuantArgs a;
     a.fmt = d->fmt; a.gran = d->gran; a.in_dtype = d->in_dtype;
@@ -286,8 +306,7 @@ iq_status iq_amax(const iq_desc* d, const void* x, float* amax_out, void* worksp
     if (!d) return IQ_EINVAL;
     if (!is_bf16_or_f32(d->in_dtype)) return IQ_EINVAL;
     if (d->rows < 0 || d->cols < 0 || d->cols % iqk::kChunk) return IQ_EINVAL;
-    if (d->rows > 0 && d->cols > 0 && d->rows * (d->cols / iqk::kChunk) >= (int64_t)1 << 31)
-        return IQ_EUNSUPPORTED;
+    if (!chunks_fit(d->rows, d->cols)) return IQ_EUNSUPPORTED;
     iq_status st = check_input(d, x);
     if (st != IQ_OK) return st;
     if (!amax_out || !workspace) return IQ_EINVAL;

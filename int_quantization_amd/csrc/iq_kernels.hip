@@ -464,18 +464,178 @@ struct Stats {
     }
 };
 
+// Fast-path sums of one chunk whose x^ is h (finite inputs, unit absmax in
+// the FP32 statistics range; wave-uniform call): d = x - h (exact),
+// sum d^2, sum |d|, max |d|, and sum x^2 (BF16: v_dot2 on the raw pairs).
+template <int IN>
+__device__ __forceinline__ void sums8(Stats& st, const Chunk<IN>& ch, const float (&x)[8], const float (&h)[8]) {
+    float d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = x[i] - h[i];
+    if (IN == D_BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            const bf2 p = __builtin_bit_cast(bf2, ch.w[k]);
+            st.fx2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, st.fx2, false);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.fx2 = __builtin_fmaf(x[i], x[i], st.fx2);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        st.fe2 = __builtin_fmaf(d[i], d[i], st.fe2);
+        st.fae += __builtin_fabsf(d[i]);
+        st.mae = __builtin_fmaxf(st.mae, __builtin_fabsf(d[i]));
+    }
+}
+
+// Saturated elements of a chunk, |x| > T (T >= 0, per lane), added to the
+// wave-uniform count (wave-uniform call).  Compared on the integer images
+// of |x| of an opaque copy of the raw words, so the compiler keeps this
+// pass apart from the cast.  For BF16, |x| > T exactly when the BF16 bits
+// of |x| exceed those of T truncated to BF16.
+template <int IN>
+__device__ __forceinline__ void count_above(Stats& st, const Chunk<IN>& ch, float T) {
+    const uint32_t tb = as_u(T);
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(ch.w) / 4); ++k) {
+        uint32_t w = ch.w[k];
+        asm volatile("" : "+v"(w));
+        if (IN == D_BF16) {
+            st.nsat += __popcll(__ballot((w & 0x7FFFu) > (tb >> 16)));
+            st.nsat += __popcll(__ballot(((w >> 16) & 0x7FFFu) > (tb >> 16)));
+        } else {
+            st.nsat += __popcll(__ballot((w & 0x7FFFFFFFu) > tb));
+        }
+    }
+}
+
+// Exact zero inputs of a valid chunk: they always give a zero code, which
+// the flushed count (zero codes of nonzero inputs) must not include.
+template <int IN>
+__device__ __forceinline__ void uncount_zero_inputs(Stats& st, const Chunk<IN>& ch, bool valid) {
+    Chunk<IN> c = ch;
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(c.w) / 4); ++k) asm volatile("" : "+v"(c.w[k]));
+    if (valid) st.lzf -= 8u - c.nonzero_count();
+}
+
 // Whether a unit with absmax A and scale s can hold elements with |x/s| > Q:
 // exactly when A > Q * s, whose sign the single rounding of fma(Q, s, -A)
 // preserves.
 __device__ __forceinline__ bool can_saturate(float A, float s, float Q) { return __builtin_fmaf(Q, s, -A) < 0.f; }
 
 
-// Reduce the workgroup's statistics (NWAVES waves) and write its partial.
+// ---------------------------------------------------------------------------
+// Statistics across workgroups.  Every workgroup of a launch reduces its own
+// statistics to one partial, publishes it and takes a ticket; the workgroup
+// that draws the last ticket folds all partials, in a fixed order, into the
+// output and sets the ticket back to zero.
+//   Publishing uses device-scope atomic exchanges, whose results the
+//   workgroup waits for: an exchange has been performed at device scope
+//   when its old value returns, so every partial is in place before its
+//   ticket is taken.  The ticket is a device-scope atomic add, and the
+//   folding workgroup reads the partials with device-scope atomic loads
+//   after its own ticket returned, i.e. after every other ticket.
+//   No cache writeback of the whole L2 is needed, which a release fence per
+//   workgroup would cost.
+// ---------------------------------------------------------------------------
+struct StatsOut {   // mirrors iq_stats
+    uint64_t n, n_zero_flush, n_saturated, n_nonfinite;
+    double sum_x2, sum_err2, sum_abs_err;
+    float max_abs_err;
+    uint32_t reserved;
+};
+
+struct StatsSink {
+    Partial* partials;   // one slot per workgroup
+    uint32_t* ticket;    // zero when the launch starts; zero again when it ends
+    StatsOut* out;       // may be null: the partials of an x^ call without statistics
+    uint64_t nelem;
+};
+
+// Sum over the 64 lanes with a fixed butterfly (the same order on every run).
+template <typename T> __device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Fold the n published partials (all NT threads of the last workgroup):
+// thread t folds partials t, t + NT, ... in that order, then lanes and
+// waves combine in a fixed pattern.  Deterministic for a given grid.
+template <int NT>
+__device__ void fold_partials(const StatsSink& sink, int n) {
+    constexpr int NW = NT / 64;
+    __shared__ double s_d[NW][3];
+    __shared__ float s_m[NW];
+    __shared__ uint64_t s_c[NW][3];
+    const int t = threadIdx.x;
+    double a = 0.0, b = 0.0, c = 0.0;
+    float m = 0.f;
+    uint64_t c0 = 0, c1 = 0, c2 = 0;
+    // loads go out four partials at a time, all issued before the first sum
+    constexpr int PER = kMaxGrid / NT, B = PER < 4 ? PER : 4;
+#pragma unroll
+    for (int k0 = 0; k0 < PER; k0 += B) {
+        uint64_t pw[B][5];
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            const int i = t + (k0 + k) * NT;
+            const uint64_t* q = reinterpret_cast<const uint64_t*>(sink.partials + (i < n ? i : 0));
+#pragma unroll
+            for (int f = 0; f < 5; ++f)
+                pw[k][f] = __hip_atomic_load(q + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            if (t + (k0 + k) * NT >= n) continue;
+            a += __builtin_bit_cast(double, pw[k][0]);
+            b += __builtin_bit_cast(double, pw[k][1]);
+            c += __builtin_bit_cast(double, pw[k][2]);
+            m = __builtin_fmaxf(m, as_f((uint32_t)pw[k][3]));
+            c0 += (uint32_t)(pw[k][3] >> 32);
+            c1 += (uint32_t)pw[k][4];
+            c2 += (uint32_t)(pw[k][4] >> 32);
+        }
+    }
+    a = wave_sum(a); b = wave_sum(b); c = wave_sum(c);
+    c0 = wave_sum(c0); c1 = wave_sum(c1); c2 = wave_sum(c2);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    const int w = t >> 6;
+    if ((t & 63) == 0) {
+        s_d[w][0] = a; s_d[w][1] = b; s_d[w][2] = c; s_m[w] = m;
+        s_c[w][0] = c0; s_c[w][1] = c1; s_c[w][2] = c2;
+    }
+    __syncthreads();
+    if (t == 0) {
+        StatsOut o;
+        o.n = sink.nelem;
+        o.sum_x2 = s_d[0][0]; o.sum_err2 = s_d[0][1]; o.sum_abs_err = s_d[0][2]; o.max_abs_err = s_m[0];
+        o.n_saturated = s_c[0][0]; o.n_zero_flush = s_c[0][1]; o.n_nonfinite = s_c[0][2];
+#pragma unroll
+        for (int k = 1; k < NW; ++k) {   // waves in order
+            o.sum_x2 += s_d[k][0]; o.sum_err2 += s_d[k][1]; o.sum_abs_err += s_d[k][2];
+            o.max_abs_err = __builtin_fmaxf(o.max_abs_err, s_m[k]);
+            o.n_saturated += s_c[k][0]; o.n_zero_flush += s_c[k][1]; o.n_nonfinite += s_c[k][2];
+        }
+        o.reserved = 0;
+        if (sink.out) *sink.out = o;
+        __hip_atomic_store(sink.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Reduce the workgroup's statistics (NWAVES waves) to its partial, publish
+// it, and fold all partials if this workgroup finishes last.
 template <int NWAVES>
-__device__ void write_partial(Stats& st, Partial* out) {
+__device__ void write_partial(Stats& st, const StatsSink& sink) {
     __shared__ double s_d[NWAVES][3];
     __shared__ float s_m[NWAVES];
     __shared__ uint32_t s_c[NWAVES][3];
+    __shared__ uint32_t s_last;
     st.fold();
     double a = st.sx2, b = st.se2, c = st.sae;
     float m = st.mae;
@@ -489,30 +649,46 @@ __device__ void write_partial(Stats& st, Partial* out) {
         lz += (uint32_t)__shfl_xor((int)lz, o);
     }
     const uint32_t n0 = st.nsat, n1 = st.nzf + lz, n2 = st.nnf;
-    Partial p;
-    if (NWAVES == 1) {
-        if (threadIdx.x != 0) return;
-        p.sum_x2 = a; p.sum_err2 = b; p.sum_abs_err = c; p.max_abs_err = m;
-        p.n_saturated = n0; p.n_zero_flush = n1; p.n_nonfinite = n2;
-    } else {
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        if (lane == 0) {
-            s_d[wave][0] = a; s_d[wave][1] = b; s_d[wave][2] = c; s_m[wave] = m;
-            s_c[wave][0] = n0; s_c[wave][1] = n1; s_c[wave][2] = n2;
-        }
-        __syncthreads();
-        if (threadIdx.x != 0) return;
-        p.sum_x2 = s_d[0][0]; p.sum_err2 = s_d[0][1]; p.sum_abs_err = s_d[0][2]; p.max_abs_err = s_m[0];
-        p.n_saturated = s_c[0][0]; p.n_zero_flush = s_c[0][1]; p.n_nonfinite = s_c[0][2];
-#pragma unroll
-        for (int k = 1; k < NWAVES; ++k) {
-            p.sum_x2 += s_d[k][0]; p.sum_err2 += s_d[k][1]; p.sum_abs_err += s_d[k][2];
-            p.max_abs_err = __builtin_fmaxf(p.max_abs_err, s_m[k]);
-            p.n_saturated += s_c[k][0]; p.n_zero_flush += s_c[k][1]; p.n_nonfinite += s_c[k][2];
-        }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (NWAVES > 1 && lane == 0) {
+        s_d[wave][0] = a; s_d[wave][1] = b; s_d[wave][2] = c; s_m[wave] = m;
+        s_c[wave][0] = n0; s_c[wave][1] = n1; s_c[wave][2] = n2;
     }
-    p.pad[0] = p.pad[1] = 0;
-    out[blockIdx.x] = p;
+    if (NWAVES > 1) __syncthreads();
+    if (threadIdx.x == 0) {
+        Partial p;
+        if (NWAVES == 1) {
+            p.sum_x2 = a; p.sum_err2 = b; p.sum_abs_err = c; p.max_abs_err = m;
+            p.n_saturated = n0; p.n_zero_flush = n1; p.n_nonfinite = n2;
+        } else {
+            p.sum_x2 = s_d[0][0]; p.sum_err2 = s_d[0][1]; p.sum_abs_err = s_d[0][2]; p.max_abs_err = s_m[0];
+            p.n_saturated = s_c[0][0]; p.n_zero_flush = s_c[0][1]; p.n_nonfinite = s_c[0][2];
+#pragma unroll
+            for (int k = 1; k < NWAVES; ++k) {
+                p.sum_x2 += s_d[k][0]; p.sum_err2 += s_d[k][1]; p.sum_abs_err += s_d[k][2];
+                p.max_abs_err = __builtin_fmaxf(p.max_abs_err, s_m[k]);
+                p.n_saturated += s_c[k][0]; p.n_zero_flush += s_c[k][1]; p.n_nonfinite += s_c[k][2];
+            }
+        }
+        uint64_t* q = reinterpret_cast<uint64_t*>(sink.partials + blockIdx.x);
+        const uint64_t r0 = __hip_atomic_exchange(q + 0, __builtin_bit_cast(uint64_t, p.sum_x2), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t r1 = __hip_atomic_exchange(q + 1, __builtin_bit_cast(uint64_t, p.sum_err2), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t r2 = __hip_atomic_exchange(q + 2, __builtin_bit_cast(uint64_t, p.sum_abs_err), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t r3 = __hip_atomic_exchange(q + 3, (uint64_t)as_u(p.max_abs_err) | ((uint64_t)p.n_saturated << 32),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t r4 = __hip_atomic_exchange(q + 4, (uint64_t)p.n_zero_flush | ((uint64_t)p.n_nonfinite << 32),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The old values are consumed here, so the exchanges have returned
+        // (been performed) before the ticket below is taken.
+        asm volatile("" ::"v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(r4) : "memory");
+        const uint32_t tk = __hip_atomic_fetch_add(sink.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = tk == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last != 0) fold_partials<NWAVES * 64>(sink, (int)gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -534,8 +710,14 @@ template <> struct Fmt<F_E5M2> {
     static constexpr double qmid = 57344.0 + 0x1p-9;
 };
 template <> struct Fmt<F_MXFP4> { static constexpr float qmax = 6.f; };
-template <> struct Fmt<F_NVFP4> { static constexpr float qmax = 6.f; };
-template <> struct Fmt<F_INT4> { static constexpr float qmax = 7.f; };
+template <> struct Fmt<F_NVFP4> {
+    static constexpr float qmax = 6.f;
+    static constexpr double qmid = 6.0 + 0x1p-22;
+};
+template <> struct Fmt<F_INT4> {
+    static constexpr float qmax = 7.f;
+    static constexpr double qmid = 7.0 + 0x1p-22;
+};
 template <> struct Fmt<F_INT4ZP> { static constexpr float qmax = 15.f; };   // codes 0..15
 
 // Saturation in the x domain: for s > 0 and the correctly rounded v = x / s,
@@ -793,7 +975,7 @@ struct RowArgs {
     float* scales;
     void* xhat;
     int xhat_dtype;
-    Partial* partials;
+    StatsSink sink;
 };
 
 template <int IN, int CPT, int NT>
@@ -1017,7 +1199,7 @@ __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
         }
         if (STATS) st.fold();
     }
-    if (STATS) write_partial<NT / 64>(st, a.partials);
+    if (STATS) write_partial<NT / 64>(st, a.sink);
 }
 
 // Rows longer than 2048 chunks: absmax pass, then a second
@@ -1070,7 +1252,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
             if (STATS) st.fold();
         }
     }
-    if (STATS) write_partial<kThreads / 64>(st, a.partials);
+    if (STATS) write_partial<kThreads / 64>(st, a.sink);
 }
 
 // ---------------------------------------------------------------------------
@@ -1098,7 +1280,9 @@ struct FlatArgs {
     void* xhat;
     int xhat_dtype;
     const TensorInfo* info;  // per-tensor INT8/FP8 and NVFP4: absmax pre-pass result
-    Partial* partials;
+    const float* static_amax;  // static scaling: the caller's absmax instead of info
+    float* scale_out;        // static scaling: where the per-tensor scale (or s_g) goes
+    StatsSink sink;
     uint32_t rule;           // R_* scale-rule bits (MXFP4 exponent, NVFP4 block-scale rounding)
     uint8_t* shifts;         // asymmetric INT4: packed 4-bit shifts
 };
@@ -1123,13 +1307,26 @@ __device__ __forceinline__ uint32_t unit_absmax(const Chunk<IN>& ch, bool& nonfi
     return bits;
 }
 
-// Flushed elements of a chunk with nibble codes w: nonzero inputs (8 for a
-// lane with data unless some lane of the wave holds an exact zero) minus
-// nonzero codes.
-template <int IN>
-__device__ __forceinline__ void count_flush_nibbles(Stats& st, const Chunk<IN>& ch, bool valid, bool chunk_zero, uint32_t w) {
-    const uint32_t nzx = __ballot(chunk_zero) != 0 ? ch.nonzero_count() : (valid ? 8u : 0u);
-    st.count_flush(nzx, nonzero_nibbles(w));
+// Flushed elements of a lane's chunks from its codes: every valid element
+// is taken as a nonzero input, minus the nonzero codes (nz, accumulated per
+// chunk); exact zero inputs are taken out by uncount_zero_inputs in the
+// waves that hold one.
+__device__ __forceinline__ void add_flushed(Stats& st, uint32_t nvalid, uint32_t nz) { st.lzf += 8u * nvalid - nz; }
+
+// The chunks of a lane are cast one after another: pinned() hands out an
+// opaque copy of a chunk (nothing that reads it can move above this point)
+// and pin_sums() closes a chunk's statistics (nothing it feeds can move
+// below).  Empty asm statements keep their program order, so the compiler
+// cannot interleave the chunks, and each chunk's registers are released
+// before the next one starts.
+template <int IN> __device__ __forceinline__ Chunk<IN> pinned(const Chunk<IN>& ch) {
+    Chunk<IN> c = ch;
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(c.w) / 4); ++k) asm volatile("" : "+v"(c.w[k]));
+    return c;
+}
+__device__ __forceinline__ void pin_sums(Stats& st, uint32_t& nz) {
+    asm volatile("" : "+v"(st.fx2), "+v"(st.fe2), "+v"(st.fae), "+v"(st.mae), "+v"(nz));
 }
 
 // Absmax over chunks [k0, k0 + K) of the lane: FP32 bits of the finite
@@ -1196,7 +1393,13 @@ __device__ __forceinline__ int mx_exponent(uint32_t bits, uint32_t rule) {
 // MXFP4: one block of 32 = the lane's 4 chunks.  E8M0 = clamp(E + 127, 0, 254)
 // with E from mx_exponent.  g0 is the lane's first chunk (a multiple of 4),
 // nvalid its chunks with data (0 or 4: the row length is a multiple of 32).
-template <int IN, bool STATS>
+// The wave takes the fast body when every block of the wave is finite with
+// its absmax in the FP32 statistics range: branch-free over the 4 chunks,
+// with saturated elements and exact zeros counted first, in separate passes,
+// by the waves that can hold them.  Otherwise every lane of the wave takes
+// the general body: element by element from x in rolled loops (NaN codes
+// patched, FP64 statistics), few registers for a rare case.
+template <int IN, bool STATS, bool XHAT>
 __device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
                                               const FlatArgs& a, Stats& st) {
     bool nonfinite, zero;
@@ -1210,47 +1413,69 @@ __device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksP
         E = E < 0 ? 0 : (E > 254 ? 254 : E);
     }
     const float sc = E ? as_f((uint32_t)E << 23) : as_f(0x00400000u);   // 2^(E-127), exact
-    const bool valid = nvalid != 0;
-    if (valid) static_cast<uint8_t*>(a.scales)[g0 >> 2] = (uint8_t)E;
-    // Saturation test without the quotient: |x / 2^(E-127)| > 6 exactly
-    // when |x| > 6 * 2^(E-127) (both sides are exact near 6).
+    if (nvalid != 0) static_cast<uint8_t*>(a.scales)[g0 >> 2] = (uint8_t)E;
+    // Saturation without the quotient: |x / 2^(E-127)| > 6 exactly when
+    // |x| > 6 * 2^(E-127) (both sides exact near 6).
     const float thr = 6.0f * sc;
-    const bool slow = __ballot(nonfinite || !stat_range(as_f(bits))) != 0;
-    const bool sat = __ballot(as_f(bits) > thr) != 0;
-    uint32_t wq[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float x[8], v[8], h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = ch[k].get(i);
-        uint32_t w = 0;
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], sc, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
-        if (nonfinite) {
-            // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (__builtin_isnan(x[i])) w &= ~(0xFu << (4 * i));
-        }
-        const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
-        const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
-        const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
-        const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
-        h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
-        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + k) * kChunk, h);
+    if (__ballot(nonfinite || !stat_range(as_f(bits))) == 0) {
         if (STATS) {
-            if (!slow) {
-                st.add8_fast<IN, true, false>(ch[k], sat, x, v, h, thr);
-                count_flush_nibbles<IN>(st, ch[k], valid, zero, w);
-            } else {
-                st.add8_slow(x, x, h, thr);
+            if (__ballot(as_f(bits) > thr) != 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) count_above<IN>(st, ch[k], thr);
+            }
+            if (__ballot(zero) != 0) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) uncount_zero_inputs<IN>(st, ch[k], nvalid != 0);
             }
         }
-        wq[k] = w;
+        uint32_t nz = 0, wq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const Chunk<IN> cc = pinned(ch[k]);
+            float x[8], h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = cc.get(i);
+            uint32_t w = 0;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], sc, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], sc, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], sc, 3);
+            const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+            const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+            const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+            const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+            h[0] = p0.x; h[1] = p0.y; h[2] = p1.x; h[3] = p1.y; h[4] = p2.x; h[5] = p2.y; h[6] = p3.x; h[7] = p3.y;
+            if (STATS) {
+                sums8<IN>(st, cc, x, h);
+                nz += nonzero_nibbles(w);
+                pin_sums(st, nz);
+            }
+            if (XHAT && nvalid != 0) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + k) * kChunk, h);
+            wq[k] = w;
+        }
+        store_words4(a.codes, g0, nvalid, wq);
+        if (STATS) add_flushed(st, nvalid, nz);
+    } else {
+        uint32_t* codes32 = reinterpret_cast<uint32_t*>(a.codes);
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            const bool valid = (uint32_t)c < nvalid;
+            const int64_t e0 = valid ? a.geo.elem(g0 + c) : 0;
+            uint32_t w = 0;
+#pragma unroll 1
+            for (int i = 0; i < 8; ++i) {
+                const float x = valid ? load_elem<IN>(a.geo.x, e0 + i) : 0.f;
+                // NaN has no E2M1 code: it maps to +0 (the convert would give +-6).
+                uint32_t code = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, x, 0.f, sc, 0) & 0xFu;
+                if (__builtin_isnan(x)) code = 0u;
+                const float h = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, sc, 0)[0];
+                w |= code << (4 * i);
+                if (STATS) st.add1_slow(x, __builtin_fabsf(x) > thr, h);
+                if (XHAT && valid) store_xhat1(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk + i, h);
+            }
+            if (valid) __builtin_nontemporal_store(w, codes32 + g0 + c);
+        }
     }
-    store_words4(a.codes, g0, nvalid, wq);
 }
 
 // Smallest E4M3 code whose value is >= t (t >= 0, finite), capped at 448.
@@ -1311,10 +1536,13 @@ __device__ __forceinline__ uint32_t nv_block_code(float A, const NvConst& k) {
 }
 
 // NVFP4: blocks of 16 = 2 chunks; the lane holds blocks (0, 1) and (2, 3) of
-// its chunks.  The wave takes the fast path when every lane's blocks are
-// finite with scales in the fast range; the slow path (correctly rounded
-// division, patches) is exact for every lane.
-template <int IN, bool STATS>
+// its chunks.  The wave takes the fast body when every lane's blocks are
+// finite with scales in the fast range (branch-free over the 4 chunks;
+// saturated elements and exact zeros counted first, in separate passes, by
+// the waves that can hold them); otherwise the general body, element by
+// element from x in rolled loops (correctly rounded division, patches,
+// FP64 statistics), which is exact for every lane.
+template <int IN, bool STATS, bool XHAT>
 __device__ __forceinline__ void quant_lane_nv(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
                                               const NvConst& k, const FlatArgs& a, Stats& st) {
     bool nonfinite[2], zero[2];
@@ -1339,65 +1567,89 @@ __device__ __forceinline__ void quant_lane_nv(const Chunk<IN> (&ch)[kTileChunksP
     uint8_t* sc8 = static_cast<uint8_t*>(a.scales) + (g0 >> 1);
     if (nvalid == 4) *reinterpret_cast<uint16_t*>(sc8) = (uint16_t)(sb[0] | (sb[1] << 8));
     else if (nvalid >= 2) *sc8 = (uint8_t)sb[0];
-    bool fast = true, satl = false;
+    bool fast = true;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        fast = fast && !nonfinite[b] && s_nv[b] >= kTinyScale && stat_range(as_f(bits[b]));
-        satl = satl || can_saturate(as_f(bits[b]), s_nv[b], 6.f);
-    }
-    const bool all_fast = __ballot(!fast) == 0;
-    const bool sat = __ballot(satl) != 0;
-    uint32_t wq[4];
+    for (int b = 0; b < 2; ++b) fast = fast && !nonfinite[b] && s_nv[b] >= kTinyScale && stat_range(as_f(bits[b]));
+    if (__ballot(!fast) == 0) {
+        if (STATS) {
+            if (__ballot(can_saturate(as_f(bits[0]), s_nv[0], 6.f) || can_saturate(as_f(bits[1]), s_nv[1], 6.f)) != 0) {
+                const float T0 = sat_threshold<F_NVFP4>(s_nv[0]), T1 = sat_threshold<F_NVFP4>(s_nv[1]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float s = s_nv[c >> 1], yy = y[c >> 1];
-        const bool valid = (uint32_t)c < nvalid;
-        float x[8], v[8], h[8];
+                for (int c = 0; c < 4; ++c) count_above<IN>(st, ch[c], c < 2 ? T0 : T1);
+            }
+            if (__ballot(zero[0] || zero[1]) != 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = ch[c].get(i);
-        uint32_t w;
-        if (all_fast) {
+                for (int c = 0; c < 4; ++c) uncount_zero_inputs<IN>(st, ch[c], (uint32_t)c < nvalid);
+            }
+        }
+        uint32_t nz = 0, wq[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = markstein(x[i], s, yy);
-            w = fp4_pack8(v);
+        for (int c = 0; c < 4; ++c) {
+            const Chunk<IN> cc = pinned(ch[c]);
+            const float s = s_nv[c >> 1], yy = y[c >> 1];
+            float x[8], v[8], h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = cc.get(i);
+                v[i] = markstein(x[i], s, yy);
+            }
+            const uint32_t w = fp4_pack8(v);
             fp4_unpack8(w, s, h);
             if (STATS) {
-                st.add8_fast<IN, false, false>(ch[c], sat, x, v, h, 6.f);
-                count_flush_nibbles<IN>(st, ch[c], valid, zero[c >> 1], w);
+                sums8<IN>(st, cc, x, h);
+                nz += nonzero_nibbles(w);
+                pin_sums(st, nz);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (s == 0.f) ? 0.f : x[i] / s;
-            w = fp4_pack8(v);
-            if (s == 0.f) w = 0u;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (__builtin_isnan(v[i])) w &= ~(0xFu << (4 * i));
-            fp4_unpack8(w, s, h);
-            if (STATS) st.add8_slow(x, v, h, 6.f);
+            if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+            wq[c] = w;
         }
-        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
-        wq[c] = w;
+        store_words4(a.codes, g0, nvalid, wq);
+        if (STATS) add_flushed(st, nvalid, nz);
+    } else {
+        uint32_t* codes32 = reinterpret_cast<uint32_t*>(a.codes);
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            const bool valid = (uint32_t)c < nvalid;
+            const float s = c < 2 ? s_nv[0] : s_nv[1];
+            const int64_t e0 = valid ? a.geo.elem(g0 + c) : 0;
+            uint32_t w = 0;
+#pragma unroll 1
+            for (int i = 0; i < 8; ++i) {
+                const float x = valid ? load_elem<IN>(a.geo.x, e0 + i) : 0.f;
+                const float v = (s == 0.f) ? 0.f : x / s;
+                uint32_t code = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0, v, 0.f, 1.0f, 0) & 0xFu;
+                if (s == 0.f || __builtin_isnan(v)) code = 0u;
+                const float h = s * __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
+                w |= code << (4 * i);
+                if (STATS) st.add1_slow(x, __builtin_fabsf(v) > 6.f, h);
+                if (XHAT && valid) store_xhat1(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk + i, h);
+            }
+            if (valid) __builtin_nontemporal_store(w, codes32 + g0 + c);
+        }
     }
-    store_words4(a.codes, g0, nvalid, wq);
 }
 
 // 8 INT4 codes from t = v + 1.5 * 2^23 (the low nibble of each t is the
-// two's-complement code): nibble pairs in the low byte, then bytes gathered.
+// two's-complement code, or the unsigned code of the asymmetric format):
+// the low bytes of the even and of the odd elements are gathered into one
+// word each, then the odd nibbles are shifted up and merged with one bit
+// select (element 2j in bits 3:0 of byte j, element 2j+1 in bits 7:4).
 __device__ __forceinline__ uint32_t int4_pack8(const float (&t)[8]) {
-    uint32_t p[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) p[k] = (as_u(t[2 * k + 1]) << 4) | (as_u(t[2 * k]) & 0xFu);
-    const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0c0c0400u);   // bytes {p0.b0, p1.b0, 0, 0}
-    const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x0c0c0400u);
-    return lo | (hi << 16);
+    const uint32_t e = __builtin_amdgcn_perm(as_u(t[2]), as_u(t[0]), 0x0c0c0400u) |
+                       (__builtin_amdgcn_perm(as_u(t[6]), as_u(t[4]), 0x0c0c0400u) << 16);
+    const uint32_t o = __builtin_amdgcn_perm(as_u(t[3]), as_u(t[1]), 0x0c0c0400u) |
+                       (__builtin_amdgcn_perm(as_u(t[7]), as_u(t[5]), 0x0c0c0400u) << 16);
+    return (e & 0x0F0F0F0Fu) | ((o << 4) & 0xF0F0F0F0u);
 }
 
 // INT4: groups of 128 = 16 chunks = 4 lanes; FP16 scale fp16(A / 7), saturated.
 // rtab[f] = RN(1 / (1 + f / 1024)): the reciprocal of a normal FP16 scale
 // 2^e (1 + f / 1024) is rtab[f] * 2^-e exactly (a power-of-two scaling of a
-// normal binary32).
-template <int IN, bool STATS>
+// normal binary32).  Fast body when every group of the wave is finite with
+// a normal, unsaturated scale (saturated elements, |x| > T with T from
+// sat_threshold, and exact zeros counted first in separate passes);
+// otherwise the general body, element by element from x in rolled loops.
+template <int IN, bool STATS, bool XHAT>
 __device__ __forceinline__ void quant_lane_int4(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0, uint32_t nvalid,
                                                 const float* rtab, const FlatArgs& a, Stats& st) {
     bool nonfinite_l, zero;
@@ -1419,49 +1671,66 @@ __device__ __forceinline__ void quant_lane_int4(const Chunk<IN> (&ch)[kTileChunk
     // fast: finite inputs and a normal, unsaturated FP16 scale keep |x/sf| < 7.5
     // (and put A = 7 sf inside the FP32 statistics range)
     const bool fast = !nonfinite && sf >= 0x1p-14f && s32 <= 65504.f;
-    const bool all_fast = __ballot(!fast) == 0;
-    const bool sat = __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0;
-    const int ex = (int)((s16 >> 10) & 0x1Fu) - 15;
-    const float y = all_fast ? __builtin_amdgcn_ldexpf(rtab[s16 & 0x3FFu], -ex) : 0.f;
-    // x^ = sf * q = fma(sf, t, -sf * kMagic): sf * kMagic and sf * q are
-    // exact (11 + 2 and 11 + 3 significant bits), so the fma is exact.
-    const float sfm = sf * kMagic;
-    uint32_t wq[4];
+    if (__ballot(!fast) == 0) {
+        if (STATS) {
+            if (__ballot(can_saturate(as_f(bits), sf, 7.f)) != 0) {
+                const float T = sat_threshold<F_INT4>(sf);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const bool valid = (uint32_t)c < nvalid;
-        float x[8], v[8], h[8];
+                for (int c = 0; c < 4; ++c) count_above<IN>(st, ch[c], T);
+            }
+            if (__ballot(zero) != 0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = ch[c].get(i);
-        uint32_t w = 0;
-        if (all_fast) {
-            float t[8];
+                for (int c = 0; c < 4; ++c) uncount_zero_inputs<IN>(st, ch[c], (uint32_t)c < nvalid);
+            }
+        }
+        const int ex = (int)((s16 >> 10) & 0x1Fu) - 15;
+        const float y = __builtin_amdgcn_ldexpf(rtab[s16 & 0x3FFu], -ex);
+        // x^ = sf * q = fma(sf, t, -sf * kMagic): sf * kMagic and sf * q are
+        // exact (11 + 2 and 11 + 3 significant bits), so the fma is exact.
+        const float sfm = sf * kMagic;
+        uint32_t nz = 0, wq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const Chunk<IN> cc = pinned(ch[c]);
+            float x[8], t[8], h[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                v[i] = markstein(x[i], sf, y);
-                t[i] = v[i] + kMagic;
+                x[i] = cc.get(i);
+                t[i] = markstein(x[i], sf, y) + kMagic;   // |v| <= 7.5: kMagic + RNE(v)
                 h[i] = __builtin_fmaf(sf, t[i], -sfm);
             }
-            w = int4_pack8(t);
+            const uint32_t w = int4_pack8(t);
             if (STATS) {
-                st.add8_fast<IN, false, false>(ch[c], sat, x, v, h, 7.f);
-                count_flush_nibbles<IN>(st, ch[c], valid, zero, w);
+                sums8<IN>(st, cc, x, h);
+                nz += nonzero_nibbles(w);
+                pin_sums(st, nz);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                v[i] = (sf == 0.f) ? 0.f : x[i] / sf;
-                const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v[i]), -7.f), 7.f);
-                const int qi = __builtin_isnan(v[i]) ? 0 : (int)q;   // via int: a zero code is +0
-                w |= ((uint32_t)qi & 0xFu) << (4 * i);
-                h[i] = sf * (float)qi;
-            }
-            if (STATS) st.add8_slow(x, v, h, 7.f);
+            if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+            wq[c] = w;
         }
-        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
-        wq[c] = w;
+        store_words4(a.codes, g0, nvalid, wq);
+        if (STATS) add_flushed(st, nvalid, nz);
+    } else {
+        uint32_t* codes32 = reinterpret_cast<uint32_t*>(a.codes);
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            const bool valid = (uint32_t)c < nvalid;
+            const int64_t e0 = valid ? a.geo.elem(g0 + c) : 0;
+            uint32_t w = 0;
+#pragma unroll 1
+            for (int i = 0; i < 8; ++i) {
+                const float x = valid ? load_elem<IN>(a.geo.x, e0 + i) : 0.f;
+                const float v = (sf == 0.f) ? 0.f : x / sf;
+                const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(v), -7.f), 7.f);
+                const int qi = __builtin_isnan(v) ? 0 : (int)q;   // via int: a zero code is +0
+                const float h = sf * (float)qi;
+                w |= ((uint32_t)qi & 0xFu) << (4 * i);
+                if (STATS) st.add1_slow(x, __builtin_fabsf(v) > 7.f, h);
+                if (XHAT && valid) store_xhat1(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk + i, h);
+            }
+            if (valid) __builtin_nontemporal_store(w, codes32 + g0 + c);
+        }
     }
-    store_words4(a.codes, g0, nvalid, wq);
 }
 
 // Signed range over the finite elements of the lane's chunks (the rare path
@@ -1485,6 +1754,41 @@ __device__ __forceinline__ void lane_range_finite(const Chunk<IN> (&ch)[kTileChu
     neg = as_u(nlo) & 0x7FFFFFFFu;
 }
 
+// The x-domain bound of RN(x / s) > q for an integer 0 <= q <= 15 and a
+// scale s > 0: RN(x / s) > q exactly when x > RD((q + u) * s), with u half
+// an ulp of q (q's significand is even, so the midpoint above q rounds down
+// to q), and u = 2^-150 for q = 0 (the tie at half the smallest subnormal
+// rounds to +0).  The FP64 product is exact (at most 25 + 24 bits).
+__device__ __forceinline__ float above_int(int q, float s) {
+    const double u = q == 0 ? 0x1p-150 : __builtin_ldexp(1.0, (31 - __clz(q)) - 24);
+    return rd_to_float(((double)q + u) * (double)s);
+}
+
+// Elements of a chunk beyond the asymmetric grid: x > thi (positive side) or
+// -x > tlo (negative side), compared on the integer images of an opaque
+// copy of the raw words (signed for the positive side, where negative
+// inputs compare below every bound; unsigned with the sign bit set for the
+// negative side, where positive inputs compare below).  For BF16 the bounds
+// are truncated to BF16, which keeps the comparisons exact.
+template <int IN>
+__device__ __forceinline__ void count_outside(Stats& st, const Chunk<IN>& ch, float thi, float tlo) {
+    const uint32_t hb = as_u(thi), lb = as_u(tlo);
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(ch.w) / 4); ++k) {
+        uint32_t w = ch.w[k];
+        asm volatile("" : "+v"(w));
+        if (IN == D_BF16) {
+            const int ph = (int)(hb >> 16);
+            const uint32_t nl = 0x8000u | (lb >> 16);
+            const int w0 = (int)(int16_t)(w & 0xFFFFu), w1 = (int)(int16_t)(w >> 16);
+            st.nsat += __popcll(__ballot(w0 > ph || (w & 0xFFFFu) > nl));
+            st.nsat += __popcll(__ballot(w1 > ph || (w >> 16) > nl));
+        } else {
+            st.nsat += __popcll(__ballot((int)w > (int)hb || w > (0x80000000u | lb)));
+        }
+    }
+}
+
 // Asymmetric INT4 (the Triton post, Puzzle 12: x^ = sc * (w - sh) with
 // unsigned 4-bit w and sh; the min-max encoder).  Groups of 128 = 16 chunks
 // = 4 lanes.  Over the group's finite elements lo = min(0, min x) and
@@ -1495,9 +1799,10 @@ __device__ __forceinline__ void lane_range_finite(const Chunk<IN> (&ch)[kTileChu
 // which give the same code (checked on the CPU over random FP32 ranges and
 // every BF16 input of random BF16 ranges).  A code equal to sh is exactly a
 // zero x^, so flushed elements are counted from w ^ sh.  Saturated elements
-// (x / sc above 15 - sh or below -sh) sit at the ends of a group's range;
-// only waves where some group's hi or lo crosses are compared per element.
-template <int IN, bool STATS>
+// (x / sc above 15 - sh or below -sh) are counted in the x domain
+// (above_int), in a separate pass by the waves where some group's hi or lo
+// crosses its bound.
+template <int IN, bool STATS, bool XHAT>
 __device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0,
                                                   uint32_t nvalid, const FlatArgs& a, Stats& st) {
     uint32_t p = 0, n = 0, mn = Chunk<IN>::kMagInit;
@@ -1527,73 +1832,82 @@ __device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChu
         if ((g0 & 31u) == 0) a.shifts[g0 >> 5] = (uint8_t)(sh | (sh_next << 4));
     }
     const bool fast = !nonfinite && sc >= kTinyScale && stat_range(__builtin_fmaxf(hi, nlo));
-    const bool all_fast = __ballot(!fast) == 0;
-    const float thi = (float)(15 - sh), tlo = (float)(-sh);
-    const uint32_t shrep = (uint32_t)sh * 0x11111111u;
-    const float y = all_fast ? 1.0f / sc : 0.f;
-    const bool sat = all_fast && __ballot(markstein(hi, sc, y) > thi || markstein(-nlo, sc, y) < tlo) != 0;
-    // Fast path codes in the magic-number domain: (v + kMagic) is kMagic +
-    // RNE(v) (ties to an even q, as the rounding happens before the shift),
-    // adding sh is exact, and clamping to kMagic + [0, 15] leaves kMagic + w,
-    // whose low nibble is w; x^ = sc * (t - (kMagic + sh)) with an exact
-    // difference.
-    const float shf = (float)sh, magic_sh = kMagic + shf, wtop = kMagic + 15.f;
-    uint32_t wq[4];
+    if (__ballot(!fast) == 0) {
+        if (STATS) {
+            const float thi = above_int(15 - sh, sc), tlo = above_int(sh, sc);
+            if (__ballot(hi > thi || nlo > tlo) != 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const bool valid = (uint32_t)c < nvalid;
-        float x[8], h[8];
-        uint32_t w = 0;
-        if (all_fast) {
-            float v[8], t[8];
+                for (int c = 0; c < 4; ++c) count_outside<IN>(st, ch[c], thi, tlo);
+            }
+            if (__ballot(zero) != 0) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) uncount_zero_inputs<IN>(st, ch[c], (uint32_t)c < nvalid);
+            }
+        }
+        const float y = 1.0f / sc;
+        const uint32_t shrep = (uint32_t)sh * 0x11111111u;
+        // Codes in the magic-number domain: (v + kMagic) is kMagic + RNE(v)
+        // (ties to an even q, as the rounding happens before the shift),
+        // adding sh is exact, and clamping to kMagic + [0, 15] leaves
+        // kMagic + w, whose low nibble is w; x^ = sc * (t - (kMagic + sh))
+        // with an exact difference.
+        const float shf = (float)sh, magic_sh = kMagic + shf, wtop = kMagic + 15.f;
+        uint32_t nz = 0, wq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const Chunk<IN> cc = pinned(ch[c]);
+            float x[8], t[8], h[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                x[i] = ch[c].get(i);
-                v[i] = markstein(x[i], sc, y);
-                t[i] = __builtin_amdgcn_fmed3f((v[i] + kMagic) + shf, kMagic, wtop);   // finite here
+                x[i] = cc.get(i);
+                t[i] = __builtin_amdgcn_fmed3f((markstein(x[i], sc, y) + kMagic) + shf, kMagic, wtop);
                 h[i] = sc * (t[i] - magic_sh);
             }
-            w = int4_pack8(t);
+            const uint32_t w = int4_pack8(t);
             if (STATS) {
-                st.add8_fast<IN, false, false>(ch[c], false, x, v, h, 0.f);
-                if (sat) {
-                    float th = thi;
-                    asm volatile("" : "+v"(th));   // keep the compares inside this branch
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) st.nsat += __popcll(__ballot(v[i] > th || v[i] < tlo));
-                }
-                const uint32_t nzx = __ballot(zero) != 0 ? ch[c].nonzero_count() : (valid ? 8u : 0u);
-                st.count_flush(nzx, nonzero_nibbles_full(w ^ shrep));   // w != sh: a nonzero x^
+                sums8<IN>(st, cc, x, h);
+                nz += nonzero_nibbles_full(w ^ shrep);   // w != sh: a nonzero x^
+                pin_sums(st, nz);
             }
-        } else {
-            bool sv[8];
-#pragma unroll
+            if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+            wq[c] = w;
+        }
+        store_words4(a.codes, g0, nvalid, wq);
+        if (STATS) add_flushed(st, nvalid, nz);
+    } else {
+        const float vhi = (float)(15 - sh), vlo = (float)(-sh);
+        uint32_t* codes32 = reinterpret_cast<uint32_t*>(a.codes);
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            const bool valid = (uint32_t)c < nvalid;
+            const int64_t e0 = valid ? a.geo.elem(g0 + c) : 0;
+            uint32_t w = 0;
+#pragma unroll 1
             for (int i = 0; i < 8; ++i) {
-                x[i] = ch[c].get(i);
+                const float x = valid ? load_elem<IN>(a.geo.x, e0 + i) : 0.f;
                 float v = 0.f;
                 int wi = sh;
                 if (sc != 0.f) {
-                    v = x[i] / sc;
+                    v = x / sc;
                     if (!__builtin_isnan(v))
                         wi = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(v) + (float)sh, 0.f), 15.f);
                 }
-                sv[i] = v > thi || v < tlo;
-                h[i] = sc * (float)(wi - sh);
+                const float h = sc * (float)(wi - sh);
                 w |= (uint32_t)wi << (4 * i);
+                if (STATS) st.add1_slow(x, v > vhi || v < vlo, h);
+                if (XHAT && valid) store_xhat1(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk + i, h);
             }
-            if (STATS) st.add8_slow_flags(x, sv, h);
+            if (valid) __builtin_nontemporal_store(w, codes32 + g0 + c);
         }
-        if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
-        wq[c] = w;
     }
-    store_words4(a.codes, g0, nvalid, wq);
 }
 
 // ---------------------------------------------------------------------------
 // Flat tiles.  A workgroup iteration covers kTileChunks = 1024 consecutive
-// chunks; lane l of wave w owns the 4 consecutive chunks 256 w + 4 l + k of
-// the tile (32 elements: one MXFP4 block, two NVFP4 blocks, a quarter of an
-// INT4 group).  The HBM -> LDS copies keep each instruction on 1 KiB of
+// chunks; for the block formats lane l of wave w owns the 4 consecutive
+// chunks 256 w + 4 l + k of the tile (32 elements: one MXFP4 block, two
+// NVFP4 blocks, a quarter of an INT4 group), for INT8 / FP8 per tensor the
+// chunks 256 w + 64 k + l (FlatOwn).  The HBM -> LDS copies keep each instruction on 1 KiB of
 // consecutive input: lane i of copy j fetches 16-byte word 64 j + unswz(i)
 // of the wave's region, so word o lands in column swz(o mod 64) of row
 // o / 64; a lane's reads of its own words then fall in distinct banks within
@@ -1611,14 +1925,25 @@ struct FlatConst {
     const float* rtab;
 };
 
+// Chunk ownership within a tile.  The block formats give lane l of wave w
+// the 4 consecutive chunks 256 w + 4 l + k (whole blocks per lane or lane
+// group).  INT8 / FP8 per tensor have no blocks: lane l owns chunks
+// 256 w + 64 k + l, so the 8-byte code stores (and x^ stores) of a wave
+// cover consecutive bytes, as in the per-row kernels.
+template <int FMT> struct FlatOwn {
+    static constexpr bool kInterleaved = FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2;
+    static constexpr uint32_t kStride = kInterleaved ? 64u : 1u;   // chunk k of the lane is g0 + kStride * k
+};
+
 // One tile's worth of the lane's chunks (wd: its 16-byte words from LDS).
 // FULL: every chunk of the tile holds data (no per-chunk validity selects).
+// XHAT: the x^ output is written (a separate instantiation).
 // CHECK (per-tensor INT8 / FP8 with a caller-supplied absmax): nothing is
 // known of the data, so each wave takes the fast cast only when its inputs
 // are finite, within the absmax (no clamping beyond the rounding of s) and
 // not all below the FP32 statistics range; the exact-zero flag is the
 // wave's own.
-template <int IN, int FMT, bool STATS, bool FULL, bool CHECK>
+template <int IN, int FMT, bool STATS, bool FULL, bool CHECK, bool XHAT>
 __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread * ChunkWords<IN>::n], uint32_t g0,
                                           uint32_t nchunks, const FlatConst& k, const FlatArgs& a, Stats& st) {
     constexpr int W = ChunkWords<IN>::n;
@@ -1626,18 +1951,21 @@ __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread *
     Chunk<IN> ch[kTileChunksPerThread];
 #pragma unroll
     for (int c = 0; c < kTileChunksPerThread; ++c) {
-        if (FULL || (uint32_t)c < nvalid) ch[c].set(&wd[c * W], 1);
+        const bool valid = FlatOwn<FMT>::kInterleaved ? (FULL || g0 + FlatOwn<FMT>::kStride * c < nchunks)
+                                                      : (FULL || (uint32_t)c < nvalid);
+        if (valid) ch[c].set(&wd[c * W], 1);
         else ch[c].zero();
     }
     if (FMT == F_MXFP4) {
-        quant_lane_mx<IN, STATS>(ch, g0, nvalid, a, st);
+        quant_lane_mx<IN, STATS, XHAT>(ch, g0, nvalid, a, st);
     } else if (FMT == F_NVFP4) {
-        quant_lane_nv<IN, STATS>(ch, g0, nvalid, k.nk, a, st);
+        quant_lane_nv<IN, STATS, XHAT>(ch, g0, nvalid, k.nk, a, st);
     } else if (FMT == F_INT4) {
-        quant_lane_int4<IN, STATS>(ch, g0, nvalid, k.rtab, a, st);
+        quant_lane_int4<IN, STATS, XHAT>(ch, g0, nvalid, k.rtab, a, st);
     } else if (FMT == F_INT4ZP) {
-        quant_lane_int4zp<IN, STATS>(ch, g0, nvalid, a, st);
+        quant_lane_int4zp<IN, STATS, XHAT>(ch, g0, nvalid, a, st);
     } else {
+        // INT8 / FP8 per tensor: the scale is the tensor's, the flags wave-uniform.
         bool fast = k.fast, zeros = k.zeros;
         if (CHECK) {
             bool nonfinite, zero;
@@ -1645,32 +1973,89 @@ __device__ __forceinline__ void flat_lane(const u4v (&wd)[kTileChunksPerThread *
             fast = fast && __ballot(nonfinite || m > k.amax_bits) == 0 && __ballot(m >= as_u(kStatLo)) != 0;
             zeros = __ballot(zero) != 0;
         }
+        if (fast) {
+            // one branch-free body; saturated elements (tensors whose absmax
+            // saturates) and exact zeros (waves holding one) counted first
+            if (STATS && k.sat) {
 #pragma unroll
-        for (int c = 0; c < kTileChunksPerThread; ++c) {
-            const bool valid = FULL || (uint32_t)c < nvalid;
-            float h[8];
-            quant_chunk_uniform<IN, FMT, STATS>(ch[c], k.s, k.y, fast, k.sat, k.T, zeros, valid,
-                                                a.codes + (int64_t)(g0 + c) * kChunk, h, st);
-            if (a.xhat && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+                for (int c = 0; c < kTileChunksPerThread; ++c) count_above<IN>(st, ch[c], k.T);
+            }
+            if (STATS && zeros) {
+#pragma unroll
+                for (int c = 0; c < kTileChunksPerThread; ++c)
+                    uncount_zero_inputs<IN>(st, ch[c], FULL || g0 + FlatOwn<FMT>::kStride * c < nchunks);
+            }
+#pragma unroll
+            for (int c = 0; c < kTileChunksPerThread; ++c) {
+                const uint32_t g = g0 + FlatOwn<FMT>::kStride * c;
+                const bool valid = FULL || g < nchunks;
+                float h[8];
+                quant_chunk_fast_t<IN, FMT, STATS, false, false>(pinned(ch[c]), k.s, k.y, k.T, valid,
+                                                                 a.codes + (int64_t)g * kChunk, h, st);
+                if (STATS) {
+                    uint32_t none = 0;
+                    pin_sums(st, none);
+                }
+                if (XHAT && valid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)g * kChunk, h);
+            }
+        } else {
+            // element by element from x in rolled loops (correctly rounded
+            // division, clamps, NaN codes, FP64 statistics)
+            constexpr float Q = Fmt<FMT>::qmax;
+#pragma unroll 1
+            for (int c = 0; c < kTileChunksPerThread; ++c) {
+                const uint32_t g = g0 + FlatOwn<FMT>::kStride * c;
+                const bool valid = FULL || g < nchunks;
+                const int64_t e0 = valid ? a.geo.elem(g) : 0;
+                uint32_t w0 = 0, w1 = 0;
+#pragma unroll 1
+                for (int i = 0; i < 8; ++i) {
+                    const float x = valid ? load_elem<IN>(a.geo.x, e0 + i) : 0.f;
+                    float v, h;
+                    const uint32_t code = cast1_slow<FMT>(x, k.s, v, h);
+                    if (i < 4) w0 |= code << (8 * i);
+                    else w1 |= code << (8 * (i - 4));
+                    if (STATS) st.add1_slow(x, __builtin_fabsf(v) > Q, h);
+                    if (XHAT && valid) store_xhat1(a.xhat, a.xhat_dtype, (int64_t)g * kChunk + i, h);
+                }
+                if (valid) {
+                    const u2v o = {w0, w1};
+                    __builtin_nontemporal_store(o, reinterpret_cast<u2v*>(a.codes + (int64_t)g * kChunk));
+                }
+            }
         }
     }
 }
 
-template <int IN, int FMT, bool STATS, bool CHECK>
+template <int IN, int FMT, bool STATS, bool CHECK, bool XHAT>
 __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     constexpr int W = ChunkWords<IN>::n;
     constexpr int NW = kTileChunksPerThread * W;      // 16-byte words per lane = copies per wave and tile
     static_assert(kTileChunksPerThread == 4, "lane layout assumes 4 chunks per lane");
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
-    // Per-tensor quantities from the absmax pre-pass (uniform over the grid).
+    // Per-tensor quantities (uniform over the grid): from the absmax pre-pass,
+    // or for static scaling from the caller's absmax.  A NaN, negative or
+    // infinite one is taken as 0 and -0 as +0; nothing is known of the data
+    // then (the per-tensor INT8 / FP8 kernel checks it per wave), so the
+    // exact-zero flag is set.
     float s = 0.f, y = 0.f, T = 0.f;
     bool fast = false, sat = true, zeros = true;
+    TensorInfo inf = {0u, 0u, 0.f, 0u};
     if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2 || FMT == F_NVFP4) {
-        s = a.info->scale;
-        zeros = a.info->zeros != 0;
-        const float alpha = as_f(a.info->amax_bits);
-        fast = a.info->nonfinite == 0 && stat_range(alpha);
+        if (a.static_amax) {
+            float am = *a.static_amax;
+            am = (am >= 0.f && am <= 0x1.fffffep127f) ? __builtin_fabsf(am) : 0.f;
+            constexpr float qdiv = FMT == F_INT8 ? 127.f : FMT == F_E4M3 ? 448.f : FMT == F_E5M2 ? 57344.f : 2688.f;
+            inf.amax_bits = as_u(am); inf.nonfinite = 0u; inf.scale = am / qdiv; inf.zeros = 1u;
+            if (blockIdx.x == 0 && threadIdx.x == 0) *a.scale_out = inf.scale;
+        } else {
+            inf = *a.info;
+        }
+        s = inf.scale;
+        zeros = inf.zeros != 0;
+        const float alpha = as_f(inf.amax_bits);
+        fast = inf.nonfinite == 0 && stat_range(alpha);
         if constexpr (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) {
             if (fast) {
                 y = 1.0f / s;
@@ -1730,32 +2115,50 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     if (blockIdx.x < ntiles) stage_tile(blockIdx.x);
     FlatConst fk;
     fk.s = s; fk.y = y; fk.T = T; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
-    fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? a.info->amax_bits : 0u;
+    fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? inf.amax_bits : 0u;
     const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const uint32_t g0 = tile * kTileChunks + 256u * wave + 4u * lane;   // the lane's first chunk
+        // the lane's first chunk, and its words of the wave's region in LDS
+        const uint32_t g0 = tile * kTileChunks + 256u * wave + (FlatOwn<FMT>::kInterleaved ? lane : 4u * lane);
         wait_staged();
         u4v wd[NW];
 #pragma unroll
         for (int k = 0; k < NW; ++k) {
-            const uint32_t ow = NW * lane + k;
+            const uint32_t ow = FlatOwn<FMT>::kInterleaved ? W * (64u * (k / W) + lane) + k % W : NW * lane + k;
             wd[k] = stage[ow >> 6][64 * wave + swz(ow & 63u)];
         }
         wait_lds_reads();
         if (tile + gridDim.x < ntiles) stage_tile(tile + gridDim.x);
-        if (tile < full_tiles) flat_lane<IN, FMT, STATS, true, CHECK>(wd, g0, a.geo.nchunks, fk, a, st);
-        else flat_lane<IN, FMT, STATS, false, CHECK>(wd, g0, a.geo.nchunks, fk, a, st);
+        if (tile < full_tiles) flat_lane<IN, FMT, STATS, true, CHECK, XHAT>(wd, g0, a.geo.nchunks, fk, a, st);
+        else flat_lane<IN, FMT, STATS, false, CHECK, XHAT>(wd, g0, a.geo.nchunks, fk, a, st);
         if (STATS) st.fold();
     }
-    if (STATS) write_partial<kThreads / 64>(st, a.partials);
+    if (STATS) write_partial<kThreads / 64>(st, a.sink);
 }
 
 // ---------------------------------------------------------------------------
 // Absmax pre-pass (per-tensor formats, the NVFP4 global scale, iq_amax).
 // ---------------------------------------------------------------------------
+// The result of the pre-pass and where it goes: the tensor header (info),
+// the per-tensor scale alpha / qdiv or the NVFP4 global scale amax / 2688
+// (scale_out), and the absmax itself (amax_out); each may be null.
+struct AmaxSink {
+    uint32_t* partials;   // two words per workgroup: absmax bits, flags
+    uint32_t* ticket;     // zero when the launch starts; zero again when it ends
+    float qdiv;           // 0: no scale
+    TensorInfo* info;
+    float* scale_out;
+    float* amax_out;
+};
+
+// Each workgroup reduces its tiles to (absmax over finite elements, flags:
+// 1 non-finite seen, 2 exact zero seen), publishes them with one
+// device-scope atomic exchange and takes a ticket; the last one folds all
+// partials (max and OR, order-free) and writes the results.
 template <int IN>
-__global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* partials) {
+__global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) {
     __shared__ uint32_t s_red[2][kThreads / 64][2];
+    __shared__ uint32_t s_last;
     const uint32_t ntiles = (geo.nchunks + kTileChunks - 1) / kTileChunks;
     uint32_t m = 0, raw = 0, mn = 0xFFFFFFFFu;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -1781,118 +2184,49 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, uint32_t* parti
     const uint32_t bits = block_max_or<kThreads / 64>(m, Chunk<IN>::absmax_bits(raw) >= kNonFinite, nonfinite, s_red[0]);
     block_max_or<kThreads / 64>(0u, Chunk<IN>::has_zero(mn), zeros, s_red[1]);
     if (threadIdx.x == 0) {
-        partials[2 * blockIdx.x] = bits;
-        partials[2 * blockIdx.x + 1] = (nonfinite ? 1u : 0u) | (zeros ? 2u : 0u);
-    }
-}
-
-// Fold the absmax partials; derive the per-tensor scale (alpha / qmax) or the
-// NVFP4 global scale (amax / 2688); write them where the caller wants them.
-__global__ __launch_bounds__(kThreads) void k_amax_finalize(const uint32_t* partials, int n, float qdiv,
-                                                            TensorInfo* info, float* scale_out, float* amax_out) {
-    __shared__ uint32_t s_red[2][kThreads / 64][2];
-    uint32_t m = 0, f = 0;
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-        m = umax(m, partials[2 * i]);
-        f |= partials[2 * i + 1];
-    }
-    bool nonfinite, zeros;
-    m = block_max_or<kThreads / 64>(m, (f & 1u) != 0, nonfinite, s_red[0]);
-    block_max_or<kThreads / 64>(0u, (f & 2u) != 0, zeros, s_red[1]);
-    if (threadIdx.x == 0) {
-        const float s = qdiv > 0.f ? as_f(m) / qdiv : 0.f;
-        if (info) {
-            TensorInfo t;
-            t.amax_bits = m; t.nonfinite = nonfinite ? 1u : 0u; t.scale = s; t.zeros = zeros ? 1u : 0u;
-            *info = t;
-        }
-        if (scale_out) *scale_out = s;
-        if (amax_out) *amax_out = as_f(m);
-    }
-}
-
-// Static scaling: the per-tensor absmax comes from the caller.  A NaN,
-// negative or infinite value is taken as 0 and -0 as +0; the scale follows
-// as in k_amax_finalize.  Nothing is known of the data (the quantize kernel
-// checks it per wave), so the exact-zero flag is set.
-__global__ __launch_bounds__(64) void k_static_info(const float* amax_in, float qdiv, TensorInfo* info,
-                                                     float* scale_out) {
-    if (threadIdx.x == 0) {
-        float a = *amax_in;
-        a = (a >= 0.f && a <= 0x1.fffffep127f) ? __builtin_fabsf(a) : 0.f;
-        const float s = a / qdiv;
-        TensorInfo t;
-        t.amax_bits = as_u(a); t.nonfinite = 0u; t.scale = s; t.zeros = 1u;
-        *info = t;
-        *scale_out = s;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Statistics finalize: one workgroup, fixed summation order.
-// ---------------------------------------------------------------------------
-struct StatsOut {   // mirrors iq_stats
-    uint64_t n, n_zero_flush, n_saturated, n_nonfinite;
-    double sum_x2, sum_err2, sum_abs_err;
-    float max_abs_err;
-    uint32_t reserved;
-};
-
-constexpr int kFinThreads = 256;
-constexpr int kFinPer = kMaxGrid / kFinThreads;   // partials per thread
-
-// Sum over the 64 lanes with a fixed butterfly (the same order on every run).
-template <typename T> __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-// Thread t folds partials t, t + 256, ... in that order (all loads issued
-// before the first add), then lanes and waves combine in a fixed pattern.
-__global__ __launch_bounds__(kFinThreads) void k_stats_finalize(const Partial* p, int n, uint64_t nelem, StatsOut* out) {
-    __shared__ double s_d[kFinThreads / 64][3];
-    __shared__ float s_m[kFinThreads / 64];
-    __shared__ uint64_t s_c[kFinThreads / 64][3];
-    const int t = threadIdx.x;
-    Partial q[kFinPer];
-#pragma unroll
-    for (int k = 0; k < kFinPer; ++k) {
-        const int i = t + k * kFinThreads;
-        if (i < n) q[k] = p[i];
-        else q[k] = Partial{};
-    }
-    double a = 0.0, b = 0.0, c = 0.0;
-    float m = 0.f;
-    uint64_t c0 = 0, c1 = 0, c2 = 0;
-#pragma unroll
-    for (int k = 0; k < kFinPer; ++k) {
-        a += q[k].sum_x2; b += q[k].sum_err2; c += q[k].sum_abs_err;
-        m = __builtin_fmaxf(m, q[k].max_abs_err);
-        c0 += q[k].n_saturated; c1 += q[k].n_zero_flush; c2 += q[k].n_nonfinite;
-    }
-    a = wave_sum(a); b = wave_sum(b); c = wave_sum(c);
-    c0 = wave_sum(c0); c1 = wave_sum(c1); c2 = wave_sum(c2);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
-    const int w = t >> 6;
-    if ((t & 63) == 0) {
-        s_d[w][0] = a; s_d[w][1] = b; s_d[w][2] = c; s_m[w] = m;
-        s_c[w][0] = c0; s_c[w][1] = c1; s_c[w][2] = c2;
+        const uint64_t word = (uint64_t)bits | ((uint64_t)((nonfinite ? 1u : 0u) | (zeros ? 2u : 0u)) << 32);
+        const uint64_t old = __hip_atomic_exchange(reinterpret_cast<uint64_t*>(sink.partials) + blockIdx.x, word,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(old) : "memory");   // performed before the ticket
+        const uint32_t tk = __hip_atomic_fetch_add(sink.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = tk == gridDim.x - 1 ? 1u : 0u;
     }
     __syncthreads();
-    if (t == 0) {
-        StatsOut o;
-        o.n = nelem;
-        o.sum_x2 = s_d[0][0]; o.sum_err2 = s_d[0][1]; o.sum_abs_err = s_d[0][2]; o.max_abs_err = s_m[0];
-        o.n_saturated = s_c[0][0]; o.n_zero_flush = s_c[0][1]; o.n_nonfinite = s_c[0][2];
+    if (s_last == 0) return;
+    uint32_t fm = 0, ff = 0;
+    uint64_t w[kMaxGrid / kThreads];   // every load issued before the first use
 #pragma unroll
-        for (int k = 1; k < kFinThreads / 64; ++k) {   // waves in order
-            o.sum_x2 += s_d[k][0]; o.sum_err2 += s_d[k][1]; o.sum_abs_err += s_d[k][2];
-            o.max_abs_err = __builtin_fmaxf(o.max_abs_err, s_m[k]);
-            o.n_saturated += s_c[k][0]; o.n_zero_flush += s_c[k][1]; o.n_nonfinite += s_c[k][2];
+    for (int k = 0; k < kMaxGrid / kThreads; ++k) {
+        const int i = (int)threadIdx.x + k * kThreads;
+        w[k] = __hip_atomic_load(reinterpret_cast<const uint64_t*>(sink.partials) + (i < (int)gridDim.x ? i : 0),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxGrid / kThreads; ++k) {
+        if ((int)threadIdx.x + k * kThreads >= (int)gridDim.x) continue;
+        fm = umax(fm, (uint32_t)w[k]);
+        ff |= (uint32_t)(w[k] >> 32);
+    }
+    bool any_nonfinite, any_zero;
+    fm = block_max_or<kThreads / 64>(fm, (ff & 1u) != 0, any_nonfinite, s_red[0]);
+    block_max_or<kThreads / 64>(0u, (ff & 2u) != 0, any_zero, s_red[1]);
+    if (threadIdx.x == 0) {
+        const float sc = sink.qdiv > 0.f ? as_f(fm) / sink.qdiv : 0.f;
+        if (sink.info) {
+            TensorInfo t;
+            t.amax_bits = fm; t.nonfinite = any_nonfinite ? 1u : 0u; t.scale = sc; t.zeros = any_zero ? 1u : 0u;
+            *sink.info = t;
         }
-        o.reserved = 0;
+        if (sink.scale_out) *sink.scale_out = sc;
+        if (sink.amax_out) *sink.amax_out = as_f(fm);
+        __hip_atomic_store(sink.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Statistics of an empty tensor: n = 0 and every sum zero.
+__global__ __launch_bounds__(64) void k_empty_stats(StatsOut* out) {
+    if (threadIdx.x == 0) {
+        StatsOut o = {};
         *out = o;
     }
 }
@@ -1988,8 +2322,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant(DeqArgs a) {
 // an integer in [-15, 15], exact in BF16, so v_mfma_f32_16x16x32_bf16 forms
 // exact products of it and the BF16 activations, summed in FP32; each group's
 // sum is scaled by sc and added with one fma.
-// From 33 tokens on a workgroup computes a 128 x 64 WN tile of z with 2 WN
-// waves of 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per group the activations
+// From 33 tokens on a workgroup computes a 128-row tile of z: 64 tokens with
+// four waves of 64 x 32 (33 to 64 tokens), 128 tokens with four waves of
+// 64 x 64, or 256 tokens with eight (4 x 4 MFMA tiles of 16 x 16 per 64 x 64
+// wave tile); launch_zp_gemm picks the width.  Per group the activations
 // and codes of the next group load into registers during the MFMAs (direct
 // global-to-LDS copies were the bottleneck), then the activations are
 // written and the weights dequantized into LDS, WN threads per row.  Both
@@ -3006,12 +3342,13 @@ template <int NT = kThreads, typename K> int grid_for(K kernel, uint64_t units) 
 
 uint32_t tiles_of(uint32_t nchunks) { return (nchunks + kTileChunks - 1) / kTileChunks; }
 
-// With x^ requested the partial-row instantiation serves every row length.
+// With x^ requested the partial-row instantiation with statistics serves
+// every row length (without a statistics output its partials go unread).
 template <int IN, int FMT, int CPT, int NT, bool STATS>
 void launch_row_k(const RowArgs& r, int& grid, hipStream_t s) {
     if (r.xhat) {
-        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, false, true, STATS>, (uint64_t)r.rows);
-        k_quant_row<IN, FMT, CPT, NT, false, true, STATS><<<grid, NT, 0, s>>>(r);
+        grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, false, true, true>, (uint64_t)r.rows);
+        k_quant_row<IN, FMT, CPT, NT, false, true, true><<<grid, NT, 0, s>>>(r);
     } else if (r.cpr == CPT * NT) {
         grid = grid_for<NT>(k_quant_row<IN, FMT, CPT, NT, true, false, STATS>, (uint64_t)r.rows);
         k_quant_row<IN, FMT, CPT, NT, true, false, STATS><<<grid, NT, 0, s>>>(r);
@@ -3047,22 +3384,29 @@ hipError_t launch_row(const RowArgs& r, bool stats, int& grid, hipStream_t s) {
     return stats ? launch_row_t<IN, FMT, true>(r, grid, s) : launch_row_t<IN, FMT, false>(r, grid, s);
 }
 
-template <int IN, int FMT, bool STATS, bool CHECK>
+template <int IN, int FMT, bool STATS, bool CHECK, bool XHAT>
 hipError_t launch_flat_one(const FlatArgs& f, int& grid, hipStream_t s) {
-    grid = grid_for(k_quant_flat<IN, FMT, STATS, CHECK>, tiles_of(f.geo.nchunks));
-    k_quant_flat<IN, FMT, STATS, CHECK><<<grid, kThreads, 0, s>>>(f);
+    grid = grid_for(k_quant_flat<IN, FMT, STATS, CHECK, XHAT>, tiles_of(f.geo.nchunks));
+    k_quant_flat<IN, FMT, STATS, CHECK, XHAT><<<grid, kThreads, 0, s>>>(f);
     return hipGetLastError();
 }
 
 // check: per-tensor INT8 / FP8 with a caller-supplied absmax (the other
-// formats decide per block and need no data checks).
+// formats decide per block and need no data checks).  With x^ requested the
+// instantiation with statistics serves (without a statistics output its
+// partials go unread).
+template <int IN, int FMT, bool CHECK>
+hipError_t launch_flat_c(const FlatArgs& f, bool stats, int& grid, hipStream_t s) {
+    if (f.xhat) return launch_flat_one<IN, FMT, true, CHECK, true>(f, grid, s);
+    return stats ? launch_flat_one<IN, FMT, true, CHECK, false>(f, grid, s)
+                 : launch_flat_one<IN, FMT, false, CHECK, false>(f, grid, s);
+}
+
 template <int IN, int FMT>
 hipError_t launch_flat(const FlatArgs& f, bool stats, bool check, int& grid, hipStream_t s) {
     constexpr bool kUniform = FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2;
-    if (kUniform && check)
-        return stats ? launch_flat_one<IN, FMT, true, kUniform>(f, grid, s)
-                     : launch_flat_one<IN, FMT, false, kUniform>(f, grid, s);
-    return stats ? launch_flat_one<IN, FMT, true, false>(f, grid, s) : launch_flat_one<IN, FMT, false, false>(f, grid, s);
+    if (kUniform && check) return launch_flat_c<IN, FMT, kUniform>(f, stats, grid, s);
+    return launch_flat_c<IN, FMT, false>(f, stats, grid, s);
 }
 
 template <int IN>
@@ -3087,22 +3431,21 @@ hipError_t launch_row_fmt(int fmt, const RowArgs& r, bool stats, int& grid, hipS
     }
 }
 
+// The absmax pre-pass in one launch (its last workgroup writes the results);
+// an empty tensor takes one workgroup, which writes zeros.
 hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, float qdiv, TensorInfo* info,
                             float* scale_out, float* amax_out, hipStream_t s) {
-    uint32_t* part = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxOff);
-    int grid = 0;
-    if (geo.nchunks) {
-        if (in_dtype == D_BF16) {
-            grid = grid_for(k_amax<D_BF16>, tiles_of(geo.nchunks));
-            k_amax<D_BF16><<<grid, kThreads, 0, s>>>(geo, part);
-        } else {
-            grid = grid_for(k_amax<D_F32>, tiles_of(geo.nchunks));
-            k_amax<D_F32><<<grid, kThreads, 0, s>>>(geo, part);
-        }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    AmaxSink k;
+    k.partials = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxOff);
+    k.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxTicketOff);
+    k.qdiv = qdiv; k.info = info; k.scale_out = scale_out; k.amax_out = amax_out;
+    if (in_dtype == D_BF16) {
+        const int grid = grid_for(k_amax<D_BF16>, tiles_of(geo.nchunks));
+        k_amax<D_BF16><<<grid, kThreads, 0, s>>>(geo, k);
+    } else {
+        const int grid = grid_for(k_amax<D_F32>, tiles_of(geo.nchunks));
+        k_amax<D_F32><<<grid, kThreads, 0, s>>>(geo, k);
     }
-    k_amax_finalize<<<1, kThreads, 0, s>>>(part, geo.nchunks ? grid : 0, qdiv, info, scale_out, amax_out);
     return hipGetLastError();
 }
 
@@ -3111,49 +3454,54 @@ hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, float q
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
     char* ws = static_cast<char*>(q.workspace);
-    Partial* partials = reinterpret_cast<Partial*>(ws + Workspace::kPartialOff);
     TensorInfo* info = reinterpret_cast<TensorInfo*>(ws + Workspace::kInfoOff);
     const bool stats = q.stats != nullptr;
     const int64_t nelem = q.rows * q.cols;
+    StatsSink sink;
+    sink.partials = reinterpret_cast<Partial*>(ws + Workspace::kPartialOff);
+    sink.ticket = reinterpret_cast<uint32_t*>(ws + Workspace::kStatsTicketOff);
+    sink.out = static_cast<StatsOut*>(q.stats);
+    sink.nelem = (uint64_t)nelem;
     int grid = 0;
+    bool stats_written = false;   // a quantize kernel with statistics ran (its last workgroup wrote them)
     hipError_t e = hipSuccess;
 
     if (q.gran == G_ROW) {
         RowArgs r;
         r.x = q.x; r.ld = q.ld; r.rows = (int32_t)q.rows; r.cpr = (int32_t)(q.cols / kChunk);
         r.codes = static_cast<uint8_t*>(q.codes); r.scales = static_cast<float*>(q.scales);
-        r.xhat = q.xhat; r.xhat_dtype = q.xhat_dtype; r.partials = partials;
+        r.xhat = q.xhat; r.xhat_dtype = q.xhat_dtype; r.sink = sink;
         if (nelem) {
             e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, stats, grid, s)
                                      : launch_row_fmt<D_F32>(q.fmt, r, stats, grid, s);
+            stats_written = true;
         }
     } else {
         FlatArgs f;
         f.geo = make_geom(q.x, q.rows, q.cols, q.ld);
         f.codes = static_cast<uint8_t*>(q.codes); f.scales = q.scales; f.global_scale = q.global_scale;
-        f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.info = info; f.partials = partials;
+        f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.info = info; f.sink = sink;
         f.rule = q.rule;
         f.shifts = q.shifts;
-        if (q.gran == G_TENSOR || q.fmt == F_NVFP4) {
-            float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
-            float* scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);
-            if (q.static_amax) {
-                k_static_info<<<1, 64, 0, s>>>(q.static_amax, qdiv, info, scale_out);
-                e = hipGetLastError();
-            } else {
-                e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, scale_out, nullptr, s);
-            }
+        f.static_amax = q.static_amax;
+        f.scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);
+        if ((q.gran == G_TENSOR || q.fmt == F_NVFP4) && !q.static_amax) {
+            const float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
+            e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, f.scale_out, nullptr, s);
             if (e != hipSuccess) return e;
         }
         const bool check = q.static_amax != nullptr;
-        if (nelem) {
+        // static scaling launches even an empty tensor: its one workgroup
+        // writes the scale derived from the caller's absmax
+        if (nelem || q.static_amax) {
             e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, stats, check, grid, s)
                                      : launch_flat_fmt<D_F32>(q.fmt, f, stats, check, grid, s);
+            stats_written = true;
         }
     }
     if (e != hipSuccess) return e;
-    if (stats) {
-        k_stats_finalize<<<1, kFinThreads, 0, s>>>(partials, grid, (uint64_t)nelem, static_cast<StatsOut*>(q.stats));
+    if (stats && !stats_written) {
+        k_empty_stats<<<1, 64, 0, s>>>(static_cast<StatsOut*>(q.stats));
         e = hipGetLastError();
     }
     return e;

@@ -22,7 +22,8 @@ constexpr int kTileChunksPerThread = 4;
 constexpr int kTileChunks = kThreads * kTileChunksPerThread;  // chunks per workgroup iteration
 constexpr int kMaxGrid = 2048;       // workgroups of the persistent streaming kernels
 
-// Per-workgroup partial statistics, reduced by the finalize kernel in a fixed order.
+// Per-workgroup partial statistics, folded in a fixed order by the workgroup
+// of the launch that finishes last.
 struct alignas(16) Partial {
     double sum_x2, sum_err2, sum_abs_err;
     float max_abs_err;
@@ -31,7 +32,7 @@ struct alignas(16) Partial {
 };
 static_assert(sizeof(Partial) == 48, "partial layout");
 
-// Workspace header written by the absmax finalize kernel.
+// Workspace header written by the absmax pre-pass.
 struct alignas(16) TensorInfo {
     uint32_t amax_bits;   // absmax over finite elements (bits of a non-negative float)
     uint32_t nonfinite;   // nonzero if any element is NaN or +-Inf
@@ -39,8 +40,14 @@ struct alignas(16) TensorInfo {
     uint32_t zeros;       // nonzero if any element is an exact zero
 };
 
+// Workspace layout.  The two tickets count the workgroups of a launch that
+// have published their partials; the last one folds them and sets its
+// ticket back to zero, so a zero-filled workspace stays ready for the next
+// call.
 struct Workspace {
     static constexpr size_t kInfoOff = 0;
+    static constexpr size_t kStatsTicketOff = 128;                           // uint32
+    static constexpr size_t kAmaxTicketOff = 132;                            // uint32
     static constexpr size_t kAmaxOff = 256;                                  // uint2 per workgroup
     static constexpr size_t kPartialOff = kAmaxOff + sizeof(uint32_t) * 2 * kMaxGrid;
     static constexpr size_t kBytes = kPartialOff + sizeof(Partial) * kMaxGrid;

@@ -1,0 +1,230 @@
+/*
+ * division_check.c -- CPU proof of the quotient arithmetic of the GPU fast
+ * paths (test infrastructure; neither the library nor the oracle uses it).
+ *
+ * The method computes v = x / s as one correctly rounded binary32 division
+ * (post "浅谈低精度浮点数", section "FP8": x^ = s * round(x / s)).  The GPU
+ * kernels reach that quotient without a division instruction:
+ *   - a constant divisor Q (scales alpha / 127, / 448, / 57344; block
+ *     maxima A / 6 and A / 7) by one correction step from RN(1/Q):
+ *       q0 = a * r;  e = fma(-Q, q0, a);  q = fma(e, r, q0)
+ *   - a unit's scale s by the correction step from y = RN(1/s):
+ *       q0 = x * y;  r = fma(s, q0, -x);  v = fma(-r, y, q0)
+ *     where, for the INT4 FP16 scales, y comes from a 1024-entry table of
+ *     RN(1 / (1 + f/1024)) scaled by 2^-e.
+ * This program restates that arithmetic in C (binary32, explicit fmaf, no
+ * contraction) and compares it bit for bit with the correctly rounded C
+ * division over the domains the kernels use it on.  A quotient below 2^-20
+ * may differ (every code grid rounds it to a signed zero): there the check
+ * is that the corrected value stays below 2^-19 with the same sign.
+ *
+ * Usage: division_check <check>   with <check> one of
+ *   divconst     every finite binary32 a >= 0 (the kernels divide absolute
+ *                maxima only) against a / Q, Q in {6, 7, 127, 448, 57344}:
+ *                any difference where the quotient is normal counts, and
+ *                for Q = 7 and 127 any difference at all
+ *   row_bf16     per-row INT8 / E4M3 / E5M2: every BF16 absmax alpha in
+ *                [2^-40, 2^60], s = alpha / Q, every BF16 x with |x| <= alpha
+ *   int4_fp16    every normal FP16 scale sf: the table reciprocal equals
+ *                RN(1/sf), and every BF16 x with |x| <= 7.5 sf
+ *   nvfp4        64 seeded global maxima G, s_g = G / 2688, every E4M3 block
+ *                code c: s = s_g * value(c), every BF16 x with |x| <= 6.5 s;
+ *                and the block-scale quotient (A/6) / s_g for every BF16
+ *                A <= G
+ *   random_f32   10^8 seeded binary32 pairs per Q with |x| <= alpha
+ * It prints "<check> <pairs checked> <mismatches>" per line; exit status 0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+static inline float fb(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static inline uint32_t bf(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* The empty asm statements keep gcc from folding a negation into an fma
+ * (-fma(a, b, c) -> fma(-a, b, -c)), which changes the sign of exact zeros;
+ * the GPU code is compiled as written. */
+#define KEEP(v) __asm__("" : "+x"(v))
+
+static inline float corrected_quotient(float x, float s, float y) {
+    float q0 = x * y;
+    KEEP(q0);
+    float r = fmaf(s, q0, -x);
+    KEEP(r);
+    return fmaf(-r, y, q0);
+}
+
+/* Called on a >= 0 only, where no zero changes sign: no barriers, so the
+ * exhaustive loop vectorizes. */
+static inline float const_quotient(float a, float Q, float r) {
+    const float q0 = a * r;
+    const float e = fmaf(-Q, q0, a);
+    return fmaf(e, r, q0);
+}
+
+/* 1 if the corrected quotient vm is acceptable for the true quotient v. */
+static inline int quotient_ok(float vm, float v) {
+    if (bf(vm) == bf(v)) return 1;
+    return fabsf(v) < 0x1p-20f && fabsf(vm) < 0x1p-19f && signbit(vm) == signbit(v);
+}
+
+static float e4m3_value(uint32_t c) {   /* positive E4M3 codes 1 .. 0x7E */
+    const uint32_t e = c >> 3, m = c & 7u;
+    return e ? ldexpf((float)(8 + m), (int)e - 7 - 3) : ldexpf((float)m, -9);
+}
+
+static void divconst(void) {
+    const float Qs[5] = {6.f, 7.f, 127.f, 448.f, 57344.f};
+    for (int qi = 0; qi < 5; ++qi) {
+        const float Q = Qs[qi], r = 1.0f / Q;
+        const int strict = Q == 7.f || Q == 127.f;
+        uint64_t bad = 0, n = 0;
+#pragma omp parallel for reduction(+ : bad, n) schedule(static)
+        for (int64_t hi = 0; hi < 32768; ++hi) {   /* a >= 0: every caller passes an absolute maximum */
+            if ((((uint32_t)hi << 16) & 0x7F800000u) == 0x7F800000u) continue;   /* Inf, NaN */
+            uint32_t b = 0;
+            for (uint32_t lo = 0; lo < 65536; ++lo) {
+                const float a = fb(((uint32_t)hi << 16) | lo);
+                const float q = a / Q, qc = const_quotient(a, Q, r);
+                b += (bf(q) != bf(qc)) & (strict | (fabsf(q) >= 0x1p-126f));
+            }
+            bad += b;
+            n += 65536;
+        }
+        printf("divconst_%g %llu %llu\n", (double)Q, (unsigned long long)n, (unsigned long long)bad);
+    }
+}
+
+/* every BF16 x with |x| <= lim (both signs) against scale s, reciprocal y */
+static void sweep_bf16(float s, float y, float lim, uint64_t* n, uint64_t* bad) {
+    for (uint32_t b = 0; b < 0x7F80u; ++b) {
+        const float xa = fb(b << 16);
+        if (xa > lim) break;
+        for (int sg = 0; sg < 2; ++sg) {
+            const float x = sg ? -xa : xa;
+            ++*n;
+            if (!quotient_ok(corrected_quotient(x, s, y), x / s)) ++*bad;
+        }
+    }
+}
+
+static void row_bf16(void) {
+    const float Qs[3] = {127.f, 448.f, 57344.f};
+    const uint32_t lo = bf(0x1p-40f) >> 16, hi = bf(0x1p60f) >> 16;
+    for (int qi = 0; qi < 3; ++qi) {
+        const float Q = Qs[qi];
+        uint64_t bad = 0, n = 0;
+#pragma omp parallel for reduction(+ : bad, n) schedule(dynamic, 16)
+        for (int64_t a = lo; a <= (int64_t)hi; ++a) {
+            const float alpha = fb((uint32_t)a << 16);
+            const float s = alpha / Q, y = 1.0f / s;
+            uint64_t nn = 0, bb = 0;
+            sweep_bf16(s, y, alpha, &nn, &bb);
+            n += nn;
+            bad += bb;
+        }
+        printf("row_bf16_%g %llu %llu\n", (double)Q, (unsigned long long)n, (unsigned long long)bad);
+    }
+}
+
+static void int4_fp16(void) {
+    float rtab[1024];
+    for (int f = 0; f < 1024; ++f) rtab[f] = 1.0f / (1.0f + (float)f * 0x1p-10f);
+    uint64_t bad = 0, n = 0, bad_tab = 0;
+#pragma omp parallel for reduction(+ : bad, n, bad_tab) schedule(dynamic, 64)
+    for (int64_t h = 0x0400; h <= 0x7BFF; ++h) {
+        const int ex = (int)((h >> 10) & 0x1F) - 15;
+        const float sf = ldexpf(1.0f + (float)(h & 0x3FF) * 0x1p-10f, ex);
+        const float y = ldexpf(rtab[h & 0x3FF], -ex);
+        if (bf(y) != bf(1.0f / sf)) ++bad_tab;
+        uint64_t nn = 0, bb = 0;
+        sweep_bf16(sf, y, 7.5f * sf, &nn, &bb);
+        n += nn;
+        bad += bb;
+    }
+    printf("int4_fp16_table 30720 %llu\n", (unsigned long long)bad_tab);
+    printf("int4_fp16 %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+}
+
+static uint64_t splitmix(uint64_t* s) {
+    uint64_t z = (*s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+static void nvfp4(void) {
+    uint64_t seed = 0x6E7646700001ull;
+    float G[64];
+    for (int i = 0; i < 64; ++i) {          /* positive normal BF16 maxima over the whole range */
+        const uint32_t b = 0x0080u + (uint32_t)(splitmix(&seed) % (0x7F7Fu - 0x0080u));
+        G[i] = fb(b << 16);
+    }
+    uint64_t bad = 0, n = 0, bad_t = 0, n_t = 0;
+#pragma omp parallel for reduction(+ : bad, n, bad_t, n_t) schedule(dynamic, 1) collapse(2)
+    for (int gi = 0; gi < 64; ++gi) {
+        for (int c = 1; c <= 0x7E; ++c) {
+            const float s_g = G[gi] / 2688.0f;
+            const float s = s_g * e4m3_value((uint32_t)c);
+            if (s < 0x1p-64f || !(s > 0.f)) continue;        /* tiny scales: the division path */
+            const float y = 1.0f / s;
+            uint64_t nn = 0, bb = 0;
+            sweep_bf16(s, y, 6.5f * s, &nn, &bb);
+            n += nn;
+            bad += bb;
+            if (c == 1) {                               /* block-scale quotient (A/6)/s_g, A <= G */
+                const float y_g = 1.0f / s_g;
+                for (uint32_t b = 1; b < 0x7F80u; ++b) {
+                    const float A = fb(b << 16);
+                    if (A > G[gi]) break;
+                    const float t1 = A / 6.0f, t = t1 / s_g;
+                    if (!(t1 >= 0x1p-100f && t >= 0x1p-100f && t <= 0x1p120f)) continue;
+                    ++n_t;
+                    if (bf(corrected_quotient(t1, s_g, y_g)) != bf(t)) ++bad_t;
+                }
+            }
+        }
+    }
+    printf("nvfp4_block_scale %llu %llu\n", (unsigned long long)n_t, (unsigned long long)bad_t);
+    printf("nvfp4 %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+}
+
+static void random_f32(void) {
+    const float Qs[5] = {127.f, 448.f, 57344.f, 6.f, 7.f};
+    for (int qi = 0; qi < 5; ++qi) {
+        const float Q = Qs[qi];
+        uint64_t bad = 0, n = 0;
+#pragma omp parallel for reduction(+ : bad, n) schedule(static)
+        for (int64_t blk = 0; blk < 1000; ++blk) {
+            uint64_t seed = 0x5EED0000ull * (uint64_t)(qi + 1) + (uint64_t)blk;
+            for (int i = 0; i < 100000; ++i) {
+                const uint64_t r = splitmix(&seed);
+                /* alpha: exponent in [-40, 60], random significand */
+                const int ea = -40 + (int)(r % 101);
+                const float alpha = ldexpf(1.0f + (float)((r >> 8) & 0x7FFFFF) * 0x1p-23f, ea);
+                const float s = alpha / Q, y = 1.0f / s;
+                /* x: |x| <= alpha, magnitude spread over 60 binades below alpha */
+                const uint64_t r2 = splitmix(&seed);
+                float x = ldexpf(1.0f + (float)(r2 & 0x7FFFFF) * 0x1p-23f, ea - (int)((r2 >> 32) % 61));
+                if (x > alpha) x = alpha;
+                if (r2 >> 63) x = -x;
+                ++n;
+                if (!quotient_ok(corrected_quotient(x, s, y), x / s)) ++bad;
+            }
+        }
+        printf("random_f32_%g %llu %llu\n", (double)Q, (unsigned long long)n, (unsigned long long)bad);
+    }
+}
+
+int main(int argc, char** argv) {
+    if (argc != 2) return 2;
+    if (!strcmp(argv[1], "divconst")) divconst();
+    else if (!strcmp(argv[1], "row_bf16")) row_bf16();
+    else if (!strcmp(argv[1], "int4_fp16")) int4_fp16();
+    else if (!strcmp(argv[1], "nvfp4")) nvfp4();
+    else if (!strcmp(argv[1], "random_f32")) random_f32();
+    else return 2;
+    return 0;
+}

@@ -66,7 +66,7 @@ int main(void) {
 
 
 def test_version_and_status_strings(iq):
-    assert iq.iq_abi_version() == 1
+    assert iq.iq_abi_version() == 2
     for s in range(5):
         assert iq.iq_status_str(s)
     assert "unknown" in iq.iq_status_str(99)

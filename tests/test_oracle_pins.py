@@ -10,6 +10,7 @@ Pages: Lorn blog, post "æµ…è°ˆä½Žç²¾åº¦æµ®ç‚¹æ•°" (sections "IEEE 754 æ ‡å‡†æµ®ç
 """
 import math
 import struct
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -619,6 +620,105 @@ def test_p11_int4_bound_and_nibbles(O, S):
     for i in range(8):
         nib = (words >> (4 * i)) & 0xF
         assert np.array_equal(nib, (q[:, i::8].astype(np.int64) & 0xF))
+
+
+# ---- P11: the INT4 FP16 group scale on FP16 rounding boundaries -------------------
+def rne_grid(v: Fraction, mbits: int, emin: int) -> Fraction:
+    """The binary floating-point value nearest to the rational v >= 0 with
+    mbits fraction bits and smallest normal exponent emin (a fixed spacing
+    2^(emin - mbits) below it), ties to the even significand; unbounded above."""
+    if v == 0:
+        return Fraction(0)
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - mbits)
+    n = v / ulp
+    k = n.numerator // n.denominator
+    rem = n - k
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    return k * ulp
+
+
+def fp16_bits_of(v: Fraction) -> int:
+    """IEEE binary16 bit pattern of a non-negative value on the binary16 grid."""
+    if v < Fraction(2) ** -14:
+        return int(v / Fraction(2) ** -24)
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    return ((e + 15) << 10) | int((v / Fraction(2) ** e - 1) * 1024)
+
+
+def int4_scale_expected(A: float) -> int:
+    """s = A/7 as the method states it: one binary32 quotient (exact rational,
+    rounded to nearest even), then binary16 by round to nearest even,
+    saturating at the largest finite binary16 value 65504."""
+    s32 = rne_grid(Fraction(A) / 7, 23, -126)
+    s16 = rne_grid(s32, 10, -14)
+    return 0x7BFF if s16 > 65504 else fp16_bits_of(s16)
+
+
+def test_p11_int4_fp16_scale_ties_exact():
+    """Self-check of the exact-rational helpers on printed binary16 facts."""
+    assert fp16_bits_of(Fraction(1)) == 0x3C00 and fp16_bits_of(Fraction(65504)) == 0x7BFF
+    assert fp16_bits_of(Fraction(2) ** -24) == 0x0001 and fp16_bits_of(Fraction(2) ** -14) == 0x0400
+    assert rne_grid(Fraction(2049, 2048), 10, -14) == 1                          # tie, even below
+    assert rne_grid(Fraction(2051, 2048), 10, -14) == Fraction(1026, 1024)        # tie, even above
+    assert rne_grid(Fraction(1, 3), 23, -126) == Fraction(bits_f32(0x3EAAAAAB))
+
+
+def test_p11_int4_fp16_scale_rounding(O):
+    """Groups whose maximum A puts A/7 on a binary16 midpoint m (A = 7m, exact
+    in binary32) and on the binary32 values next to 7m: the stored FP16 scale
+    is fp16(fl32(A/7)) with ties to even and saturation at 65504."""
+    ulp16 = lambda h: Fraction(2) ** -24 if h < 0x0400 else Fraction(2) ** (((h >> 10) - 15) - 10)
+    val16 = lambda h: Fraction(fp16_value(h))
+    mids = [val16(h) + ulp16(h) / 2 for h in (0x3C00, 0x3C01, 0x0400, 0x03FF, 0x5000, 0x1234, 0x2F01, 0x7BFE,
+                                              0x7BFF, 0x0000, 0x0001, 0x0002)]
+    As, want = [], []
+    for m in mids:
+        a0 = float(7 * m)
+        assert Fraction(a0) == 7 * m                     # 7m is exact in binary32 (m has <= 12 bits)
+        for a in (np.nextafter(np.float32(a0), np.float32(0)), np.float32(a0), np.nextafter(np.float32(a0),
+                                                                                              np.float32(np.inf))):
+            As.append(float(a))
+            want.append(int4_scale_expected(float(a)))
+    x = np.zeros((len(As), 128), dtype=np.float32)
+    for i, a in enumerate(As):
+        x[i] = np.linspace(0.0, a, 128, dtype=np.float32)
+        x[i, 37] = np.float32(a)
+        x[i] = np.minimum(x[i], np.float32(a))
+    r = O.quantize(x, "int4", "block")
+    got = r["scales"].view(np.uint16)[:, 0].astype(int)
+    assert got.tolist() == want, [(hex(g), hex(w)) for g, w in zip(got, want) if g != w]
+    # the cases really sit on the boundaries: every tie (A = 7m) goes to the
+    # even code, some down and some up, and 65520 saturates where a plain
+    # binary16 cast would give Inf
+    ties = want[1::3]
+    assert all(t % 2 == 0 for i, t in enumerate(ties) if i != 8)   # 8: the saturating tie
+    assert any(Fraction(fp16_value(t)) < m for t, m in zip(ties, mids) if t != 0x7BFF)
+    assert any(Fraction(fp16_value(t)) > m for t, m in zip(ties, mids))
+    assert want[3 * 8 + 1] == 0x7BFF and rne_grid(mids[8], 10, -14) > 65504
+    # planted mistakes this pin catches: a product with RN(1/7), ties away
+    # from zero, and an unsaturated binary16 cast
+    a32 = np.array(As, dtype=np.float32)
+    mult = (a32 * np.float32(1.0 / 7.0)).astype(np.float16).view(np.uint16).astype(int)
+    assert (mult != np.array(want)).any()
+    assert np.isinf((a32 / np.float32(7.0)).astype(np.float16)).any()
+    away = [fp16_bits_of(min(rne_grid(Fraction(a) / 7, 23, -126) + Fraction(1, 2 ** 60), Fraction(65504)))
+            for a in As]
+    away = [0x7BFF if a > 0x7BFF else a for a in away]
+    assert away != want
+
+
+def fp16_value(h: int) -> float:
+    return float(np.array([h], dtype=np.uint16).view(np.float16)[0])
 
 
 # ---- P15: asymmetric INT4 of Puzzle 12 (decoder printed, encoder read) ------------

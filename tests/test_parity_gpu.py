@@ -49,13 +49,15 @@ def S():
     return synth
 
 
-def run_gpu(iq, x_np, fmt, gran, cols=None, xhat="f32", flags=0):
+def run_gpu(iq, x_np, fmt, gran, cols=None, xhat="f32", flags=0, stats=True, x_dev=None):
+    """One iq_quantize call; stats=False passes no statistics buffer (the
+    statistics-free kernels), x_dev an input already on the device."""
     import torch
-    x = to_device(x_np)
+    x = to_device(x_np) if x_dev is None else x_dev
     if cols is not None:
         x = x[:, :cols]
     xdt = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[xhat]
-    q = iq.quantize(x, fmt, gran, xhat_dtype=xdt, flags=flags)
+    q = iq.quantize(x, fmt, gran, xhat_dtype=xdt, flags=flags, stats=stats)
     torch.cuda.synchronize()
     out = {"codes": q.codes.cpu().numpy(), "scales": q.scales.cpu().numpy(), "stats": q.stats(), "q": q}
     if q.global_scale is not None:
@@ -83,7 +85,8 @@ def compare(g, r, fmt, what, O=None, S=None, xhat="f32"):
         if xhat == "bf16":
             want = S.f32_to_bf16_bits(want)
         assert_bits_equal(g["xhat"], want, f"{what} xhat")
-    assert_stats_match(g["stats"], r["stats"], what)
+    if g["stats"] is not None:
+        assert_stats_match(g["stats"], r["stats"], what)
 
 
 def oracle_ref(O, x_np, fmt, gran, cols=None, want_xhat=True, flags=0):
@@ -99,6 +102,9 @@ SHAPES = [
     (33, 1024, 1056),      # padded rows (ld > cols), power-of-two chunks per row
     (13, 384, 400),        # padded rows, non-power-of-two chunks per row
     (1, 8192, None),
+    (6, 2048, None),       # per-row: one wave, 4 chunks per lane
+    (9, 16384, None),      # per-row: 8 chunks per lane (the stream's row length)
+    (4, 12288, 12296),     # per-row: 8 chunks per lane, partial, padded rows
 ]
 
 
@@ -108,16 +114,22 @@ def make_input(S, dtype, rows, cols, ld, seed):
     return w
 
 
+@pytest.mark.parametrize("stats", [True, False], ids=["stats", "nostats"])
 @pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
 @pytest.mark.parametrize("fmt,gran", ALL)
-def test_parity_shapes(iq, O, S, fmt, gran, dtype):
+def test_parity_shapes(iq, O, S, fmt, gran, dtype, stats):
+    """Every row-kernel width (1, 2, 4 chunks per lane on one wave; 2, 4, 8 on
+    four; the two-pass kernel), full and partial flat tiles, padded rows,
+    with and without the statistics, with and without x^."""
     for i, (rows, cols, ld) in enumerate(SHAPES):
         if not fits(O, fmt, gran, cols):
             continue
         x = make_input(S, dtype, rows, cols, ld, seed=100 + i)
-        g = run_gpu(iq, x, fmt, gran, cols=cols if ld else None)
         r = oracle_ref(O, x, fmt, gran, cols=cols if ld else None)
-        compare(g, r, fmt, f"{fmt}/{gran}/{'bf16' if dtype else 'f32'} {rows}x{cols} ld={ld}", O)
+        for xhat in ("f32", None):
+            g = run_gpu(iq, x, fmt, gran, cols=cols if ld else None, xhat=xhat, stats=stats)
+            compare(g, r, fmt, f"{fmt}/{gran}/{'bf16' if dtype else 'f32'} {rows}x{cols} ld={ld} stats={stats} "
+                               f"xhat={xhat}", O)
 
 
 @pytest.mark.parametrize("fmt,gran", ALL)
@@ -256,26 +268,53 @@ def test_determinism(iq, S):
 
 
 # ---- dequantize (separate call) -------------------------------------------------
-@pytest.mark.parametrize("fmt,gran", ALL)
-def test_dequantize_parity(iq, O, S, fmt, gran):
+def dev_raw(a):
+    """Upload an array's raw bytes (codes, scales, shifts) as a device tensor
+    of the same element size."""
     import torch
-    x = make_input(S, 1, 48, 2048, None, seed=11)
-    q = iq.quantize(x_dev := to_device(x), fmt, gran, xhat_dtype=torch.float32)
-    for dt, odt in ((torch.float32, O.F32), (torch.bfloat16, O.BF16)):
+    a = np.ascontiguousarray(a)
+    view = {1: np.uint8, 2: np.int16, 4: np.float32}[a.dtype.itemsize]
+    return torch.from_numpy(a.view(view)).to("cuda:0")
+
+
+def oracle_quantized(iq, r, fmt, gran, rows, cols):
+    """The oracle's codes and scales as the binding's Quantized (device copies)."""
+    gs = dev_raw(r["global_scale"]) if fmt == "nvfp4" else None
+    sh = dev_raw(r["shifts"]) if fmt == "int4zp" else None
+    return iq.Quantized(dev_raw(r["codes"]), dev_raw(r["scales"]), gs, None, None, fmt, gran, rows, cols, sh)
+
+
+def check_dequantize(iq, O, S, x, fmt, gran, what, flags=0):
+    """GPU dequantize of the oracle's codes and scales: FP32 equals the
+    oracle's x^ (the fused x^ of the quantizer), BF16 its RNE."""
+    import torch
+    rows, cols = x.shape
+    r = O.quantize(x, fmt, gran, flags=flags, want_xhat=True, threads=THREADS)
+    q = oracle_quantized(iq, r, fmt, gran, rows, cols)
+    for dt in (torch.float32, torch.bfloat16):
         d = iq.dequantize(q, dt)
         torch.cuda.synchronize()
-        codes = q.codes.cpu().numpy()
-        scales = q.scales.cpu().numpy()
-        if scales.dtype == np.int16:
-            scales = scales.view(np.uint16)
-        gs = q.global_scale.cpu().numpy() if q.global_scale is not None else None
-        sh = q.shifts.cpu().numpy() if q.shifts is not None else None
-        want = O.dequantize(codes, scales, fmt, gran, x.shape[0], x.shape[1], gs, odt, shifts=sh)
         got = d.cpu().numpy() if dt == torch.float32 else d.cpu().view(torch.int16).numpy().view(np.uint16)
-        assert_bits_equal(got, want, f"{fmt}/{gran} dequantize {dt}")
-        if dt == torch.float32:
-            assert_bits_equal(got, q.xhat.cpu().numpy(), f"{fmt}/{gran} dequantize vs quantize x^")
-    del x_dev
+        want = r["xhat"] if dt == torch.float32 else S.f32_to_bf16_bits(r["xhat"])
+        assert_bits_equal(got, want, f"{what} dequantize {dt}")
+        del d
+    del q
+
+
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_dequantize_parity(iq, O, S, fmt, gran):
+    """Power-of-two (2048 columns) and non-power-of-two (768 columns: 96
+    chunks per row) row lengths."""
+    for i, cols in enumerate((2048, 768)):
+        x = make_input(S, 1, 48, cols, None, seed=11 + i)
+        check_dequantize(iq, O, S, x, fmt, gran, f"{fmt}/{gran} 48x{cols}")
+
+
+@pytest.mark.parametrize("cfg,fmt,gran", [("c1", "int8", "tensor"), ("c1", "e4m3", "tensor"), ("c2", "e4m3", "row"),
+                                          ("c2", "e5m2", "row"), ("c3", "mxfp4", "block"), ("c4", "nvfp4", "block"),
+                                          ("c5", "int4", "block"), ("c5", "int4zp", "block")])
+def test_dequantize_full_size(iq, O, S, cfg, fmt, gran):
+    check_dequantize(iq, O, S, S.make(cfg), fmt, gran, f"{cfg} {fmt}/{gran} full size")
 
 
 def test_amax(iq, O, S):
@@ -306,6 +345,43 @@ def test_bf16_division_sweep(iq, O, S, fmt):
     assert_bits_equal(g["codes"], r["codes"], f"{fmt} sweep codes")
     assert_bits_equal(g["scales"], r["scales"], f"{fmt} sweep scales")
     assert_stats_match(g["stats"], r["stats"], f"{fmt} sweep")
+
+
+def division_rows_8192(step=8):
+    """Rows of exactly 8192 BF16 columns for every `step`-th normal BF16
+    absmax alpha: each row starts with alpha and holds BF16 values of
+    magnitude <= alpha (both signs, zeros included); the values of one alpha
+    fill as many rows as they need, the last one padded with +0."""
+    alphas = np.arange(0x0080, 0x7F80, step, dtype=np.uint32)
+    per = 8191
+    counts = [(2 * (int(a) + 1) + per - 1) // per for a in alphas]
+    x = np.zeros((sum(counts), 8192), np.uint16)
+    r = 0
+    for a, nrows in zip(alphas, counts):
+        mags = np.arange(int(a) + 1, dtype=np.uint32)
+        vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        body = np.zeros(nrows * per, np.uint16)
+        body[:vals.size] = vals
+        x[r:r + nrows, 0] = a
+        x[r:r + nrows, 1:] = body.reshape(nrows, per)
+        r += nrows
+    return x
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "int8"])
+def test_bf16_division_sweep_8192(iq, O, S, fmt):
+    """Every 8th normal BF16 absmax with every BF16 input at or below it,
+    in rows of 8192 columns: the per-row kernel the bench times (4 chunks
+    per lane, full rows, no x^) and its scale derivation, with and without
+    statistics, and the x^-writing kernel."""
+    x = division_rows_8192()
+    xd = to_device(x)
+    r = O.quantize(x, fmt, "row", want_xhat=True, threads=THREADS)
+    for xhat, stats in ((None, True), (None, False), ("f32", True)):
+        g = run_gpu(iq, None, fmt, "row", xhat=xhat, stats=stats, x_dev=xd)
+        compare(g, r, fmt, f"{fmt} 8192-column sweep stats={stats} xhat={xhat}")
+        del g
+    del xd
 
 
 @pytest.mark.parametrize("fmt,flags", [("int4", 0), ("nvfp4", 0), ("mxfp4", 0), ("nvfp4", 4), ("mxfp4", 1),
@@ -341,42 +417,38 @@ FULL = [("c1", "int8", "tensor", 0), ("c1", "e4m3", "tensor", 0), ("c2", "e4m3",
 
 @pytest.mark.parametrize("cfg,fmt,gran,flags", FULL)
 def test_full_size_workloads(iq, O, S, cfg, fmt, gran, flags):
+    """The kernels the bench times (no x^) with statistics on and off, and
+    the x^-writing kernels, element by element against the oracle."""
     x = S.make(cfg)
-    g = run_gpu(iq, x, fmt, gran, xhat=None, flags=flags)
-    r = O.quantize(x, fmt, gran, flags=flags, want_xhat=False, threads=THREADS)
-    compare(g, r, fmt, f"{cfg} {fmt}/{gran} flags={flags} full size", O)
-
-
-def test_stream_sampled_rows(iq, O, S):
-    """The 2 GiB streaming workload: every format on the GPU at full size,
-    oracle on sampled rows (given the oracle's own tensor absmax)."""
-    import torch
-    x = S.make("stream")
     xd = to_device(x)
-    rows = x.shape[0]
-    sample = np.unique(np.concatenate([[0, 1, rows - 1], np.random.default_rng(1).integers(0, rows, 24)]))
-    G = O.amax(x)
-    for fmt, gran in S.WORKLOADS["stream"].formats:
-        q = iq.quantize(xd, fmt, gran, stats=True)
-        torch.cuda.synchronize()
-        codes = q.codes.cpu().numpy()
-        scales = q.scales.cpu().numpy()
-        if scales.dtype == np.int16:
-            scales = scales.view(np.uint16)
-        st = q.stats()
-        assert st["n"] == x.size and st["n_nonfinite"] == 0
-        for r0 in sample:
-            ref = O.quantize_rows(np.ascontiguousarray(x[r0:r0 + 1]), fmt, gran, 0, 1, G)
-            assert_bits_equal(codes[r0:r0 + 1], ref["codes"], f"stream {fmt}/{gran} row {r0} codes")
-            if gran == "row":
-                assert_bits_equal(scales[r0:r0 + 1], ref["scales"], f"stream {fmt} row {r0} scale")
-            elif gran == "tensor":
-                assert_bits_equal(scales, np.array([np.float32(G) / np.float32(O.QMAX[fmt])], np.float32),
-                                  f"stream {fmt} tensor scale")
-            else:
-                assert_bits_equal(scales[r0:r0 + 1], ref["scales"], f"stream {fmt} row {r0} scales")
-        del q
+    r = O.quantize(x, fmt, gran, flags=flags, want_xhat=True, threads=THREADS)
+    for xhat, stats in ((None, True), (None, False), ("f32", True)):
+        g = run_gpu(iq, None, fmt, gran, xhat=xhat, flags=flags, stats=stats, x_dev=xd)
+        compare(g, r, fmt, f"{cfg} {fmt}/{gran} flags={flags} full size stats={stats} xhat={xhat}", O)
+        del g
     del xd
+
+
+@pytest.fixture(scope="module")
+def stream_input(S):
+    """The 2 GiB streaming workload, on the host and the device."""
+    x = S.make("stream")
+    yield x, to_device(x)
+
+
+@pytest.mark.parametrize("fmt,gran", [("int8", "tensor"), ("e4m3", "tensor"), ("e4m3", "row"), ("e5m2", "row"),
+                                      ("mxfp4", "block"), ("nvfp4", "block"), ("int4", "block")])
+def test_stream_every_row(iq, O, S, stream_input, fmt, gran):
+    """The 2 GiB streaming workload in every format: every code and scale and
+    the statistics against the oracle over the whole tensor; the call
+    without statistics gives the same codes and scales."""
+    x, xd = stream_input
+    r = O.quantize(x, fmt, gran, want_xhat=False, threads=THREADS)
+    for stats in (True, False):
+        g = run_gpu(iq, None, fmt, gran, xhat=None, stats=stats, x_dev=xd)
+        compare(g, r, fmt, f"stream {fmt}/{gran} stats={stats}")
+        del g
+    del r
 
 
 # ---- graph capture: replays match eager calls -------------------------------------
@@ -410,10 +482,11 @@ def test_graph_replay_matches_eager(iq, S, fmt, gran):
 
 @pytest.mark.parametrize("n1", [1, 24, 64, 100, 256])
 def test_gemm_repeat_bit_identical(iq, O, S, n1):
-    """Every consumer path returns the same bits on every call: the INT4
-    k split (atomic adds, direct at 64 tokens and row by row at 100), the
-    W4A16 and FP4 64-row tiles and the few-token kernels, on a 1024-row
-    grid over five calls with other work between them."""
+    """Every consumer path returns the same bits on every call, on a
+    1024-row grid over five calls with other work between them: the INT4
+    k split (atomic adds: the 64-token tile adding directly at 64 tokens,
+    the 128-token tile row by row at 100, the 256-token tile directly at
+    256), the W4A16 and FP4 64-row tiles and the few-token kernels."""
     import torch
     n0, K = 1024, 1024
     rzp = O.quantize((S.bf16_to_f32(S.make("c5", nrows=n0))[:, :K]).copy(), "int4zp", "block")
@@ -930,12 +1003,14 @@ def c5_int4zp(O, S):
     return O.quantize(S.make("c5"), "int4zp", "block", want_xhat=False, threads=THREADS)
 
 
-@pytest.mark.parametrize("n1", [1, 16, 50, 64, 256, 384, 2048])
+@pytest.mark.parametrize("n1", [1, 16, 50, 64, 100, 256, 384, 2048])
 def test_zp_gemm_full_size_sampled(iq, O, S, c5_int4zp, n1):
-    """The c5 weights against n1 tokens of BF16 activations (the few-token
-    kernel, the 128-token tile with k split in halves, added row by row at
-    50 tokens and directly at 64, and the 128- and 256-token tiles whole);
-    rows sampled for the oracle."""
+    """The c5 weights against n1 tokens of BF16 activations; rows sampled
+    for the oracle.  At 28672 rows the kernels are: the few-token kernel
+    (1, 16); the 64-token tile with k split in halves, adding row by row at
+    50 tokens and directly at 64; the 128-token tile with the k split,
+    adding row by row (100, not a multiple of 16); the 128- and 256-token
+    tiles whole (256, 384, 2048)."""
     import torch
     r = c5_int4zp
     n0, K = 28672, 8192
