@@ -530,15 +530,17 @@ __device__ __forceinline__ bool can_saturate(float A, float s, float Q) { return
 
 // ---------------------------------------------------------------------------
 // Statistics across workgroups.  Every workgroup of a launch reduces its own
-// statistics to one partial, publishes it and takes a ticket; the workgroup
-// that draws the last ticket folds all partials, in a fixed order, into the
-// output and sets the ticket back to zero.
+// statistics to one partial, publishes it and counts its arrival; the last
+// workgroup to arrive folds all partials, in a fixed order, into the output.
 //   Publishing uses device-scope atomic exchanges, whose results the
 //   workgroup waits for: an exchange has been performed at device scope
 //   when its old value returns, so every partial is in place before its
-//   ticket is taken.  The ticket is a device-scope atomic add, and the
-//   folding workgroup reads the partials with device-scope atomic loads
-//   after its own ticket returned, i.e. after every other ticket.
+//   arrival is counted.  Arrivals are device-scope atomic adds on counters
+//   of 64 workgroups each, then on one launch-wide counter (a single
+//   counter taking every workgroup's add serializes them: about 7 ns each,
+//   15 us on a 2048-workgroup launch whose workgroups all end together).
+//   The folding workgroup reads the partials with device-scope atomic
+//   loads after its own arrival returned, i.e. after every other one.
 //   No cache writeback of the whole L2 is needed, which a release fence per
 //   workgroup would cost.
 // ---------------------------------------------------------------------------
@@ -551,7 +553,7 @@ struct StatsOut {   // mirrors iq_stats
 
 struct StatsSink {
     Partial* partials;   // one slot per workgroup
-    uint32_t* ticket;    // zero when the launch starts; zero again when it ends
+    uint32_t* ticket;    // arrival counters (kTicketBytes): zero at the start and at the end
     StatsOut* out;       // may be null: the partials of an x^ call without statistics
     uint64_t nelem;
 };
@@ -561,6 +563,23 @@ template <typename T> __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return v;
+}
+
+// Arrival of one workgroup (one thread), after its partial has been
+// performed at device scope: true for the last workgroup of the launch.
+// Counters: [0] the launch, [kTicketStride * (1 + g)] group g.  Device-scope
+// atomics are performed at one point in a single order, so the last arrival
+// sees every partial published before any arrival it follows.
+__device__ bool arrive_last(uint32_t* tickets) {
+    const uint32_t n = gridDim.x, g = blockIdx.x / kTicketGroup;
+    const uint32_t left = n - g * kTicketGroup, gsize = left < (uint32_t)kTicketGroup ? left : (uint32_t)kTicketGroup;
+    uint32_t* gc = tickets + kTicketStride * (1 + g);
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gsize - 1) return false;
+    __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ngroups = (n + kTicketGroup - 1) / kTicketGroup;
+    if (__hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ngroups - 1) return false;
+    __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 // Fold the n published partials (all NT threads of the last workgroup):
@@ -624,7 +643,6 @@ __device__ void fold_partials(const StatsSink& sink, int n) {
         }
         o.reserved = 0;
         if (sink.out) *sink.out = o;
-        __hip_atomic_store(sink.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -684,8 +702,7 @@ __device__ void write_partial(Stats& st, const StatsSink& sink) {
         // The old values are consumed here, so the exchanges have returned
         // (been performed) before the ticket below is taken.
         asm volatile("" ::"v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(r4) : "memory");
-        const uint32_t tk = __hip_atomic_fetch_add(sink.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = tk == gridDim.x - 1 ? 1u : 0u;
+        s_last = arrive_last(sink.ticket) ? 1u : 0u;
     }
     __syncthreads();
     if (s_last != 0) fold_partials<NWAVES * 64>(sink, (int)gridDim.x);
@@ -2144,7 +2161,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
 // (scale_out), and the absmax itself (amax_out); each may be null.
 struct AmaxSink {
     uint32_t* partials;   // two words per workgroup: absmax bits, flags
-    uint32_t* ticket;     // zero when the launch starts; zero again when it ends
+    uint32_t* ticket;     // arrival counters (kTicketBytes): zero at the start and at the end
     float qdiv;           // 0: no scale
     TensorInfo* info;
     float* scale_out;
@@ -2153,7 +2170,7 @@ struct AmaxSink {
 
 // Each workgroup reduces its tiles to (absmax over finite elements, flags:
 // 1 non-finite seen, 2 exact zero seen), publishes them with one
-// device-scope atomic exchange and takes a ticket; the last one folds all
+// device-scope atomic exchange and counts its arrival; the last one folds all
 // partials (max and OR, order-free) and writes the results.
 template <int IN>
 __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) {
@@ -2188,8 +2205,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) 
         const uint64_t old = __hip_atomic_exchange(reinterpret_cast<uint64_t*>(sink.partials) + blockIdx.x, word,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("" ::"v"(old) : "memory");   // performed before the ticket
-        const uint32_t tk = __hip_atomic_fetch_add(sink.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = tk == gridDim.x - 1 ? 1u : 0u;
+        s_last = arrive_last(sink.ticket) ? 1u : 0u;
     }
     __syncthreads();
     if (s_last == 0) return;
@@ -2219,7 +2235,6 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) 
         }
         if (sink.scale_out) *sink.scale_out = sc;
         if (sink.amax_out) *sink.amax_out = as_f(fm);
-        __hip_atomic_store(sink.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -40,15 +40,23 @@ struct alignas(16) TensorInfo {
     uint32_t zeros;       // nonzero if any element is an exact zero
 };
 
-// Workspace layout.  The two tickets count the workgroups of a launch that
-// have published their partials; the last one folds them and sets its
-// ticket back to zero, so a zero-filled workspace stays ready for the next
+// Arrival counters of one launch: workgroups count on their group's counter
+// (kTicketGroup workgroups per group), the last of each group on the
+// launch-wide counter, so no counter takes more than kTicketGroup atomics.
+// Counters sit kTicketStride uint32 apart (separate 64-byte lines).
+constexpr int kTicketGroup = 64;
+constexpr int kTicketStride = 16;
+constexpr size_t kTicketBytes = sizeof(uint32_t) * kTicketStride * (1 + kMaxGrid / kTicketGroup);
+
+// Workspace layout.  The last workgroup of a launch folds the partials and
+// sets every counter it used back to zero (each group's last arrival resets
+// its group counter), so a zero-filled workspace stays ready for the next
 // call.
 struct Workspace {
     static constexpr size_t kInfoOff = 0;
-    static constexpr size_t kStatsTicketOff = 128;                           // uint32
-    static constexpr size_t kAmaxTicketOff = 132;                            // uint32
-    static constexpr size_t kAmaxOff = 256;                                  // uint2 per workgroup
+    static constexpr size_t kStatsTicketOff = 256;                           // kTicketBytes
+    static constexpr size_t kAmaxTicketOff = kStatsTicketOff + kTicketBytes;  // kTicketBytes
+    static constexpr size_t kAmaxOff = kAmaxTicketOff + kTicketBytes;        // uint2 per workgroup
     static constexpr size_t kPartialOff = kAmaxOff + sizeof(uint32_t) * 2 * kMaxGrid;
     static constexpr size_t kBytes = kPartialOff + sizeof(Partial) * kMaxGrid;
 };
