@@ -143,6 +143,27 @@ iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales
                       void* workspace, hipStream_t stream);
 
 /*
+ * iq_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments and results, with the library's own
+ * workspace in place of the caller's.
+ *   The workspace is one device array per GPU of 128 KiB (IQ_NOALLOC_SCRATCH_BYTES),
+ *   zero-filled when the library loads and held until the process ends; the
+ *   call rejects a descriptor whose workspace would not fit it
+ *   (IQ_EUNSUPPORTED; every descriptor iq_quantize accepts fits).
+ *   No hipMalloc, hipFree or other allocating call is made.  The first call
+ *   on a device resolves the array's address on that device (make one call
+ *   before capturing a graph); a failure to resolve it returns IQ_EHIP.
+ *   Every call on a GPU shares that GPU's array, and each call leaves it
+ *   ready for the next: calls that may overlap on one GPU (other streams,
+ *   other host threads) race and must be serialized by the caller.
+ */
+#define IQ_NOALLOC_SCRATCH_BYTES (128u * 1024u)
+iq_status iq_quantize_noalloc(const iq_desc* d, const void* x, void* codes, void* scales,
+                              float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype,
+                              hipStream_t stream);
+
+/*
  * Dequantize: x^ = s * decode(q), bit-identical to the x^ of iq_quantize.
  * Sections "FP8" (x^ = s * round(x / s): the code's value times the scale)
  * and "FP4 / MXFP4 / NVFP4" (MXFP4: E2M1 value times 2^(E - 127); NVFP4:

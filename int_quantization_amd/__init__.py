@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.iq_workspace_bytes.restype, L.iq_workspace_bytes.argtypes = S, [D]
     L.iq_quantize.restype = ctypes.c_int
     L.iq_quantize.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.iq_quantize_noalloc.restype = ctypes.c_int
+    L.iq_quantize_noalloc.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P]
     L.iq_quantize_static.restype = ctypes.c_int
     L.iq_quantize_static.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_int32, P, P]
     L.iq_quantize_zp.restype = ctypes.c_int
@@ -120,6 +122,13 @@ def iq_quantize(d: IQDesc, x: int, codes: int, scales: int, global_scale: int | 
     """Raw call with integer device addresses; returns the iq_status."""
     return load_library().iq_quantize(ctypes.byref(d), x, codes, scales, global_scale, stats, xhat,
                                       xhat_dtype, workspace, stream)
+
+
+def iq_quantize_noalloc(d: IQDesc, x: int, codes: int, scales: int, global_scale: int | None, stats: int | None,
+                        xhat: int | None, xhat_dtype: int, stream: int | None) -> int:
+    """Raw call with integer device addresses; the library's own workspace."""
+    return load_library().iq_quantize_noalloc(ctypes.byref(d), x, codes, scales, global_scale, stats, xhat,
+                                              xhat_dtype, stream)
 
 
 def iq_quantize_static(d: IQDesc, x: int, amax_in: int, codes: int, scales: int, global_scale: int | None,

@@ -40,6 +40,8 @@ bool flags_valid(const iq_desc* d) {
     }
 }
 
+static_assert(iqk::kScratchBytes == IQ_NOALLOC_SCRATCH_BYTES, "the held workspace is the size the header states");
+
 static_assert(iqk::R_MX_NEAREST == IQ_FLAG_MX_ROUND_NEAREST && iqk::R_MX_UP == IQ_FLAG_MX_ROUND_UP &&
                   iqk::R_NV_RNE == IQ_FLAG_NV_SCALE_RNE,
               "rule bits are the public flag values");
@@ -210,6 +212,18 @@ iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales
     if (d && d->fmt == IQ_INT4_ZP) return IQ_EINVAL;   // shifts have no slot here: iq_quantize_zp
     return quantize_impl(d, x, nullptr, codes, scales, global_scale, nullptr, stats, xhat, xhat_dtype, workspace,
                          stream);
+}
+
+iq_status iq_quantize_noalloc(const iq_desc* d, const void* x, void* codes, void* scales, float* global_scale,
+                              iq_stats* stats, void* xhat, int32_t xhat_dtype, hipStream_t stream) {
+    if (d && d->fmt == IQ_INT4_ZP) return IQ_EINVAL;
+    // every argument is checked before the first HIP call
+    iq_status st = check_quantize(d, x, codes, scales, global_scale, nullptr, stats, xhat, xhat_dtype);
+    if (st != IQ_OK) return st;
+    if (iq_workspace_bytes(d) > iqk::kScratchBytes) return IQ_EUNSUPPORTED;   // beyond the held workspace
+    void* ws = nullptr;
+    if (iqk::scratch_workspace(&ws) != hipSuccess) return IQ_EHIP;
+    return quantize_impl(d, x, nullptr, codes, scales, global_scale, nullptr, stats, xhat, xhat_dtype, ws, stream);
 }
 
 iq_status iq_quantize_zp(const iq_desc* d, const void* x, void* codes, float* scales, uint8_t* shifts,

@@ -3692,4 +3692,32 @@ hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, con
     return launch_amax_pass(in_dtype, geo, workspace, 0.f, nullptr, nullptr, amax_out, stream);
 }
 
+// ---------------------------------------------------------------------------
+// The library's own workspace, for callers that cannot allocate: one
+// file-scope device array per GPU (zero-filled when the code object loads,
+// held until the process ends).  Host code never uses the array's name as
+// an address: the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and is cached here.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static_assert(Workspace::kBytes <= kScratchBytes, "the workspace layout fits the scratch array");
+
+hipError_t scratch_workspace(void** out) {
+    static std::mutex mu;
+    static std::unordered_map<int, void*> addr;   // device -> address of its scratch array
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        it = addr.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
+
 }  // namespace iqk

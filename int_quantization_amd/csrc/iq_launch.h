@@ -128,4 +128,9 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t stream);
 hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, const void* x,
                        float* amax_out, void* workspace, hipStream_t stream);
 
+// The library-held workspace of the current device (kScratchBytes, zero at
+// load, tickets left at zero by every call): its device address.
+constexpr size_t kScratchBytes = 128 * 1024;
+hipError_t scratch_workspace(void** device_address);
+
 }  // namespace iqk
