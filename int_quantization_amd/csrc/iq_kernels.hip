@@ -245,6 +245,13 @@ __device__ __forceinline__ void wait_staged() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     asm volatile("" ::: "memory");
 }
+// vmcnt(N): every copy but the N most recently issued memory operations of
+// the wave has landed (the counter drains in issue order).
+template <int N> __device__ __forceinline__ void wait_staged_keep() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void wait_lds_reads() {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     asm volatile("" ::: "memory");
@@ -313,8 +320,11 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Max over the NWAVES waves of a workgroup (one LDS slot per wave beyond the
-// first).  Every thread returns the result; red must not be reused by the
-// next call before all threads passed this one (callers alternate two slots).
+// first).  Every thread returns the result.  A slot may be written again
+// only after a barrier that every thread reaches after its reads of the
+// slot, i.e. the barrier of a call on another slot: the row loops alternate
+// two slots between rows and give the re-reduction of a row holding Inf or
+// NaN a third one.
 // Max of m and OR of the per-lane flag f over the workgroup (two LDS words
 // per wave beyond the first), with the same slot discipline as block_max.
 template <int NWAVES>
@@ -1024,6 +1034,11 @@ __device__ __forceinline__ void unstage_row(const RowStage<IN, CPT, NT>& st, con
     }
 }
 
+// Rows in flight per workgroup of the per-row kernels: two LDS buffers for
+// FULL BF16 rows of 8 chunks per lane, one elsewhere.
+template <int IN, int CPT, bool FULL>
+constexpr int kRowDepth = FULL && IN == D_BF16 && CPT >= 8 ? 2 : 1;
+
 // Row scale and flags, uniform over the workgroup (sat: over the wave).
 struct RowScale {
     float s, y, T;   // T: saturation threshold in the x domain
@@ -1031,7 +1046,7 @@ struct RowScale {
 };
 
 template <int IN, int FMT, int CPT, int NT>
-__device__ __forceinline__ RowScale row_scale(const Chunk<IN> (&ch)[CPT], uint32_t (&red)[2][NT / 64][2],
+__device__ __forceinline__ RowScale row_scale(const Chunk<IN> (&ch)[CPT], uint32_t (&red)[3][NT / 64][2],
                                               int parity) {
     constexpr float Q = Fmt<FMT>::qmax;
     uint32_t wm[CPT], wn[CPT];
@@ -1053,7 +1068,7 @@ __device__ __forceinline__ RowScale row_scale(const Chunk<IN> (&ch)[CPT], uint32
 #pragma unroll
         for (int j = 0; j < CPT; ++j) f = umax(f, ch[j].absmax_finite());
         bool unused;
-        bits = block_max_or<NT / 64>(f, false, unused, red[parity ^ 1]);
+        bits = block_max_or<NT / 64>(f, false, unused, red[2]);
     }
     const float alpha = as_f(bits);
     RowScale r;
@@ -1191,21 +1206,33 @@ __device__ __forceinline__ void quant_row_fast(const Chunk<IN> (&ch)[CPT], const
 // instantiation, so the other one carries no x^ code).
 template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS>
 __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
-    __shared__ uint32_t s_red[2][NT / 64][2];
-    __shared__ RowStage<IN, CPT, NT> stage;
+    // Rows in flight per workgroup (LDS buffers).
+    constexpr int DEPTH = kRowDepth<IN, CPT, FULL>;
+    __shared__ uint32_t s_red[3][NT / 64][2];
+    __shared__ RowStage<IN, CPT, NT> stage[DEPTH];
     Stats st;
     const int32_t G = gridDim.x;
     const int64_t cols = (int64_t)a.cpr * kChunk;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int parity = 0;
+    int parity = 0, b = 0;
     int32_t row = blockIdx.x;
-    if (row < a.rows) stage_row<IN, CPT, NT, FULL>(stage, a, row, wave);
-    for (; row < a.rows; row += G, parity ^= 1) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (row + d * G < a.rows) stage_row<IN, CPT, NT, FULL>(stage[d], a, row + d * G, wave);
+    for (; row < a.rows; row += G, parity ^= 1, b = DEPTH > 1 ? b ^ 1 : 0) {
         Chunk<IN> ch[CPT];
-        wait_staged();
-        unstage_row<IN, CPT, NT, FULL>(stage, a, ch);
+        // With two buffers the copies of the next row (CPT * words per chunk
+        // of them, all issued: FULL rows) were issued after this row's and
+        // may stay in flight: the counter drains in issue order.
+        if constexpr (DEPTH > 1) {
+            if (row + G < a.rows) wait_staged_keep<CPT * ChunkWords<IN>::n>();
+            else wait_staged();
+        } else {
+            wait_staged();
+        }
+        unstage_row<IN, CPT, NT, FULL>(stage[b], a, ch);
         wait_lds_reads();
-        if (row + G < a.rows) stage_row<IN, CPT, NT, FULL>(stage, a, row + G, wave);
+        if (row + DEPTH * G < a.rows) stage_row<IN, CPT, NT, FULL>(stage[b], a, row + DEPTH * G, wave);
         const auto r = row_scale<IN, FMT, CPT, NT>(ch, s_red, parity);
         if (threadIdx.x == 0) a.scales[row] = r.s;
         uint8_t* crow = a.codes + (int64_t)row * cols;
@@ -1224,7 +1251,7 @@ __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
 template <int IN, int FMT, bool STATS>
 __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
     constexpr float Q = Fmt<FMT>::qmax;
-    __shared__ uint32_t s_red[2][kThreads / 64];
+    __shared__ uint32_t s_red[3][kThreads / 64];
     const int tid = threadIdx.x;
     const int64_t cols = (int64_t)a.cpr * kChunk;
     Stats st;
@@ -1246,7 +1273,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row_long(RowArgs a) {
                 ch.load(a.x, base + (int64_t)c * kChunk);
                 f = umax(f, ch.absmax_finite());
             }
-            bits = block_max<kThreads / 64>(f, s_red[parity ^ 1]);
+            bits = block_max<kThreads / 64>(f, s_red[2]);
         }
         const float alpha = as_f(bits);
         const float s = alpha / Q;
@@ -2104,12 +2131,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
         for (int f = threadIdx.x; f < 1024; f += kThreads) s_rtab[f] = 1.0f / (1.0f + (float)f * 0x1p-10f);
         __syncthreads();
     }
-    __shared__ Stage<NW> stage;
+    // Tiles in flight per workgroup (LDS buffers): two for BF16 INT4 and
+    // NVFP4, one elsewhere (measured: the second buffer slows the MXFP4 and
+    // per-tensor kernels with statistics; FP32 tiles are twice as large).
+    constexpr int DEPTH = IN == D_BF16 && (FMT == F_INT4 || FMT == F_NVFP4) ? 2 : 1;
+    __shared__ Stage<NW> stage[DEPTH];
     const uint32_t lane = threadIdx.x & 63u;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t dlane = unswz(lane);
     const uint32_t esize = IN == D_BF16 ? 2u : 4u;
-    auto stage_tile = [&](uint32_t tile) {
+    auto stage_tile = [&](uint32_t tile, Stage<NW>& buf) {
         const uint32_t base = tile * kTileChunks + 256u * wave;
         if (a.geo.contiguous) {
             // word ow of the wave's region is the (base * W + ow)-th 16-byte word of x
@@ -2117,7 +2148,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
 #pragma unroll
             for (int j = 0; j < NW; ++j) {
                 const uint32_t ow = 64u * j + dlane;
-                if (base + ow / W < a.geo.nchunks) dma_word(wp + ow * 16u, &stage[j][64 * wave]);
+                if (base + ow / W < a.geo.nchunks) dma_word(wp + ow * 16u, &buf[j][64 * wave]);
             }
         } else {
 #pragma unroll
@@ -2125,27 +2156,40 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
                 const uint32_t ow = 64u * j + dlane;                // word of the wave's region
                 const uint32_t c = base + ow / W;
                 if (c < a.geo.nchunks)
-                    dma_word(static_cast<const char*>(a.geo.x) + a.geo.elem(c) * esize + 16u * (ow % W), &stage[j][64 * wave]);
+                    dma_word(static_cast<const char*>(a.geo.x) + a.geo.elem(c) * esize + 16u * (ow % W), &buf[j][64 * wave]);
             }
         }
     };
-    if (blockIdx.x < ntiles) stage_tile(blockIdx.x);
+    const uint32_t G = gridDim.x;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (blockIdx.x + d * G < ntiles) stage_tile(blockIdx.x + d * G, stage[d]);
     FlatConst fk;
     fk.s = s; fk.y = y; fk.T = T; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
     fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? inf.amax_bits : 0u;
     const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int b = 0;
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += G, b = DEPTH > 1 ? b ^ 1 : 0) {
         // the lane's first chunk, and its words of the wave's region in LDS
         const uint32_t g0 = tile * kTileChunks + 256u * wave + (FlatOwn<FMT>::kInterleaved ? lane : 4u * lane);
-        wait_staged();
+        // This tile's copies have landed once at most the NW copies of the
+        // next tile, issued after them, are outstanding (memory operations
+        // of a wave complete in issue order); a next tile that is not full
+        // may have been issued with fewer copies: then wait for all.
+        if constexpr (DEPTH > 1) {
+            if (tile + G < full_tiles) wait_staged_keep<NW>();
+            else wait_staged();
+        } else {
+            wait_staged();
+        }
         u4v wd[NW];
 #pragma unroll
         for (int k = 0; k < NW; ++k) {
             const uint32_t ow = FlatOwn<FMT>::kInterleaved ? W * (64u * (k / W) + lane) + k % W : NW * lane + k;
-            wd[k] = stage[ow >> 6][64 * wave + swz(ow & 63u)];
+            wd[k] = stage[b][ow >> 6][64 * wave + swz(ow & 63u)];
         }
         wait_lds_reads();
-        if (tile + gridDim.x < ntiles) stage_tile(tile + gridDim.x);
+        if (tile + DEPTH * G < ntiles) stage_tile(tile + DEPTH * G, stage[b]);
         if (tile < full_tiles) flat_lane<IN, FMT, STATS, true, CHECK, XHAT>(wd, g0, a.geo.nchunks, fk, a, st);
         else flat_lane<IN, FMT, STATS, false, CHECK, XHAT>(wd, g0, a.geo.nchunks, fk, a, st);
         if (STATS) st.fold();
