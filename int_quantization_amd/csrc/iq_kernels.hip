@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 #include <unordered_map>
 
 #include "iq_launch.h"
@@ -772,7 +773,7 @@ __device__ __forceinline__ float markstein(float x, float s, float y) {
 
 // a / Q for a constant Q by the same correction with the compile-time
 // reciprocal RN(1/Q).  Checked against the correctly rounded quotient for
-// every finite binary32 a: equal for Q = 7 and 127 everywhere, and for
+// every finite binary32 a: equal for Q = 7, 15 and 127 everywhere, and for
 // Q = 6, 448, 2688 and 57344 whenever the quotient is a normal number (the
 // only differences have subnormal quotients); callers take the division
 // for quotients below kMarksteinMin.
@@ -1462,23 +1463,25 @@ __device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksP
     // |x| > 6 * 2^(E-127) (both sides exact near 6).
     const float thr = 6.0f * sc;
     if (__ballot(nonfinite || !stat_range(as_f(bits))) == 0) {
-        if (STATS) {
-            if (__ballot(as_f(bits) > thr) != 0) {
+        if (STATS && __ballot(zero) != 0) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) count_above<IN>(st, ch[k], thr);
-            }
-            if (__ballot(zero) != 0) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) uncount_zero_inputs<IN>(st, ch[k], nvalid != 0);
-            }
+            for (int k = 0; k < 4; ++k) uncount_zero_inputs<IN>(st, ch[k], nvalid != 0);
         }
         uint32_t nz = 0, wq[4];
+        // Saturated elements are counted with the cast in the waves where
+        // some block can saturate (with the floor rule A / 2^(E-127) lies in
+        // [4, 8): most blocks can).
+        auto body = [&](auto count_sat) {
+          constexpr bool SAT = decltype(count_sat)::value;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < 4; ++k) {
             const Chunk<IN> cc = pinned(ch[k]);
             float x[8], h[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = cc.get(i);
+            for (int i = 0; i < 8; ++i) {
+                x[i] = cc.get(i);
+                if (STATS && SAT) st.nsat += __popcll(__ballot(__builtin_fabsf(x[i]) > thr));
+            }
             uint32_t w = 0;
             w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], sc, 0);
             w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], sc, 1);
@@ -1496,7 +1499,10 @@ __device__ __forceinline__ void quant_lane_mx(const Chunk<IN> (&ch)[kTileChunksP
             }
             if (XHAT && nvalid != 0) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + k) * kChunk, h);
             wq[k] = w;
-        }
+          }
+        };
+        if (STATS && __ballot(as_f(bits) > thr) != 0) body(std::true_type{});
+        else body(std::false_type{});
         store_words4(a.codes, g0, nvalid, wq);
         if (STATS) add_flushed(st, nvalid, nz);
     } else {
@@ -1716,16 +1722,9 @@ __device__ __forceinline__ void quant_lane_int4(const Chunk<IN> (&ch)[kTileChunk
     // (and put A = 7 sf inside the FP32 statistics range)
     const bool fast = !nonfinite && sf >= 0x1p-14f && s32 <= 65504.f;
     if (__ballot(!fast) == 0) {
-        if (STATS) {
-            if (__ballot(can_saturate(as_f(bits), sf, 7.f)) != 0) {
-                const float T = sat_threshold<F_INT4>(sf);
+        if (STATS && __ballot(zero) != 0) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) count_above<IN>(st, ch[c], T);
-            }
-            if (__ballot(zero) != 0) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) uncount_zero_inputs<IN>(st, ch[c], (uint32_t)c < nvalid);
-            }
+            for (int c = 0; c < 4; ++c) uncount_zero_inputs<IN>(st, ch[c], (uint32_t)c < nvalid);
         }
         const int ex = (int)((s16 >> 10) & 0x1Fu) - 15;
         const float y = __builtin_amdgcn_ldexpf(rtab[s16 & 0x3FFu], -ex);
@@ -1733,25 +1732,35 @@ __device__ __forceinline__ void quant_lane_int4(const Chunk<IN> (&ch)[kTileChunk
         // exact (11 + 2 and 11 + 3 significant bits), so the fma is exact.
         const float sfm = sf * kMagic;
         uint32_t nz = 0, wq[4];
+        // Saturated elements, |v| > 7, counted from the quotient (the
+        // division there) in the waves where some group can saturate: the
+        // FP16 rounding of A / 7 puts A / sf above 7 in about half of them.
+        auto body = [&](auto count_sat) {
+            constexpr bool SAT = decltype(count_sat)::value;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const Chunk<IN> cc = pinned(ch[c]);
-            float x[8], t[8], h[8];
+            for (int c = 0; c < 4; ++c) {
+                const Chunk<IN> cc = pinned(ch[c]);
+                float x[8], t[8], h[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                x[i] = cc.get(i);
-                t[i] = markstein(x[i], sf, y) + kMagic;   // |v| <= 7.5: kMagic + RNE(v)
-                h[i] = __builtin_fmaf(sf, t[i], -sfm);
+                for (int i = 0; i < 8; ++i) {
+                    x[i] = cc.get(i);
+                    const float v = markstein(x[i], sf, y);
+                    if (STATS && SAT) st.nsat += __popcll(__ballot(__builtin_fabsf(v) > 7.f));
+                    t[i] = v + kMagic;   // |v| <= 7.5: kMagic + RNE(v)
+                    h[i] = __builtin_fmaf(sf, t[i], -sfm);
+                }
+                const uint32_t w = int4_pack8(t);
+                if (STATS) {
+                    sums8<IN>(st, cc, x, h);
+                    nz += nonzero_nibbles(w);
+                    pin_sums(st, nz);
+                }
+                if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+                wq[c] = w;
             }
-            const uint32_t w = int4_pack8(t);
-            if (STATS) {
-                sums8<IN>(st, cc, x, h);
-                nz += nonzero_nibbles(w);
-                pin_sums(st, nz);
-            }
-            if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
-            wq[c] = w;
-        }
+        };
+        if (STATS && __ballot(can_saturate(as_f(bits), sf, 7.f)) != 0) body(std::true_type{});
+        else body(std::false_type{});
         store_words4(a.codes, g0, nvalid, wq);
         if (STATS) add_flushed(st, nvalid, nz);
     } else {
@@ -1840,12 +1849,11 @@ __device__ __forceinline__ void count_outside(Stats& st, const Chunk<IN>& ch, fl
 // overflows); sh = RNE(-lo / sc) clamped to [0, 15];
 // w = clamp(RNE(x / sc) + sh, 0, 15).  x / sc takes the correction step with
 // y = RN(1 / sc): it equals the division except for quotients below 2^-20,
-// which give the same code (checked on the CPU over random FP32 ranges and
-// every BF16 input of random BF16 ranges).  A code equal to sh is exactly a
-// zero x^, so flushed elements are counted from w ^ sh.  Saturated elements
-// (x / sc above 15 - sh or below -sh) are counted in the x domain
-// (above_int), in a separate pass by the waves where some group's hi or lo
-// crosses its bound.
+// which give the same code (checked on the CPU for every BF16 input of
+// seeded BF16 group ranges).  A code equal to sh is exactly a zero x^, so
+// flushed elements are counted from w ^ sh.  Saturated elements (x / sc
+// above 15 - sh or below -sh) are counted from the quotient where both
+// bounds are at least 1 in magnitude, else in the x domain (above_int).
 template <int IN, bool STATS, bool XHAT>
 __device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChunksPerThread], uint32_t g0,
                                                   uint32_t nvalid, const FlatArgs& a, Stats& st) {
@@ -1866,56 +1874,84 @@ __device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChu
         if (nonfinite) { pos = fp; neg = fn; }
     }
     const float hi = as_f(pos), nlo = as_f(neg);          // lo = -nlo
-    float sc = (hi + nlo) / 15.0f;                        // (hi - lo) / 15
-    sc = sc > 0x1.fffffep127f ? 0x1.fffffep127f : sc;
+    // (hi - lo) / 15: the constant-divisor correction is the division for
+    // every finite span >= 0; an infinite span gives the largest float.
+    const float span = hi + nlo;
+    const float sc = span <= 0x1.fffffep127f ? div_const<15>(span) : 0x1.fffffep127f;
+    const bool fast = !nonfinite && sc >= kTinyScale && stat_range(__builtin_fmaxf(hi, nlo));
+    const bool wave_fast = __ballot(!fast) == 0;
+    const float y = wave_fast ? 1.0f / sc : 0.f;
+    // sh = RNE(nlo / sc) clamped to [0, 15]; on the fast path the corrected
+    // quotient gives the same shift (checked on the CPU over seeded BF16
+    // group ranges)
     int sh = 0;
-    if (sc != 0.f) sh = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(nlo / sc), 0.f), 15.f);
-    const int sh_next = __shfl_down(sh, 4);               // the next group's shift (4 lanes on)
+    if (wave_fast) sh = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(markstein(nlo, sc, y)), 0.f), 15.f);
+    else if (sc != 0.f) sh = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(nlo / sc), 0.f), 15.f);
+    // the next group's shift, 4 lanes on (within the lane's row of 16; only
+    // lanes 8k, whose next group is lanes 8k + 4 .. 8k + 7, use it)
+    const int sh_next = __builtin_amdgcn_update_dpp(0, sh, 0x104, 0xF, 0xF, false);
     if (nvalid != 0) {
         if ((g0 & 15u) == 0) static_cast<float*>(a.scales)[g0 >> 4] = sc;
         if ((g0 & 31u) == 0) a.shifts[g0 >> 5] = (uint8_t)(sh | (sh_next << 4));
     }
-    const bool fast = !nonfinite && sc >= kTinyScale && stat_range(__builtin_fmaxf(hi, nlo));
-    if (__ballot(!fast) == 0) {
+    if (wave_fast) {
+        // With 1 <= sh <= 14 in every group of the wave both bounds of the
+        // grid, 15 - sh and -sh, are at least 1 in magnitude, where the
+        // corrected quotient is the division: saturated elements are then
+        // counted from it, v outside [-sh, 15 - sh] (about half the groups
+        // hold one: hi / sc = 15 - sh + (sh - nlo / sc)).  A zero bound
+        // (sh = 0 or 15) decides at the underflow threshold: there the
+        // elements are compared with the exact x-domain bounds (above_int).
+        const bool inner = __ballot(sh == 0 || sh == 15) == 0;
         if (STATS) {
-            const float thi = above_int(15 - sh, sc), tlo = above_int(sh, sc);
-            if (__ballot(hi > thi || nlo > tlo) != 0) {
+            if (!inner) {
+                const float thi = above_int(15 - sh, sc), tlo = above_int(sh, sc);
+                if (__ballot(hi > thi || nlo > tlo) != 0) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) count_outside<IN>(st, ch[c], thi, tlo);
+                    for (int c = 0; c < 4; ++c) count_outside<IN>(st, ch[c], thi, tlo);
+                }
             }
             if (__ballot(zero) != 0) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) uncount_zero_inputs<IN>(st, ch[c], (uint32_t)c < nvalid);
             }
         }
-        const float y = 1.0f / sc;
         const uint32_t shrep = (uint32_t)sh * 0x11111111u;
-        // Codes in the magic-number domain: (v + kMagic) is kMagic + RNE(v)
-        // (ties to an even q, as the rounding happens before the shift),
-        // adding sh is exact, and clamping to kMagic + [0, 15] leaves
-        // kMagic + w, whose low nibble is w; x^ = sc * (t - (kMagic + sh))
-        // with an exact difference.
-        const float shf = (float)sh, magic_sh = kMagic + shf, wtop = kMagic + 15.f;
+        // Codes in the magic-number domain: v is clamped to [-sh, 15 - sh]
+        // first (integer bounds, so rounding the clamped value equals
+        // clamping the rounded one), (vc + kMagic) is kMagic + RNE(vc) (ties
+        // to an even q, as the rounding happens before the shift) and adding
+        // sh is exact, leaving kMagic + w, whose low nibble is w;
+        // x^ = sc * (t - (kMagic + sh)) with an exact difference.
+        const float shf = (float)sh, magic_sh = kMagic + shf, vlo = -shf, vhi = 15.f - shf;
         uint32_t nz = 0, wq[4];
+        auto body = [&](auto count_v) {
+            constexpr bool COUNT_V = decltype(count_v)::value;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const Chunk<IN> cc = pinned(ch[c]);
-            float x[8], t[8], h[8];
+            for (int c = 0; c < 4; ++c) {
+                const Chunk<IN> cc = pinned(ch[c]);
+                float x[8], t[8], h[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                x[i] = cc.get(i);
-                t[i] = __builtin_amdgcn_fmed3f((markstein(x[i], sc, y) + kMagic) + shf, kMagic, wtop);
-                h[i] = sc * (t[i] - magic_sh);
+                for (int i = 0; i < 8; ++i) {
+                    x[i] = cc.get(i);
+                    const float v = markstein(x[i], sc, y);
+                    const float vc = __builtin_amdgcn_fmed3f(v, vlo, vhi);
+                    if (STATS && COUNT_V) st.nsat += __popcll(__ballot(vc != v));
+                    t[i] = (vc + kMagic) + shf;
+                    h[i] = sc * (t[i] - magic_sh);
+                }
+                const uint32_t w = int4_pack8(t);
+                if (STATS) {
+                    sums8<IN>(st, cc, x, h);
+                    nz += nonzero_nibbles_full(w ^ shrep);   // w != sh: a nonzero x^
+                    pin_sums(st, nz);
+                }
+                if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
+                wq[c] = w;
             }
-            const uint32_t w = int4_pack8(t);
-            if (STATS) {
-                sums8<IN>(st, cc, x, h);
-                nz += nonzero_nibbles_full(w ^ shrep);   // w != sh: a nonzero x^
-                pin_sums(st, nz);
-            }
-            if (XHAT && (uint32_t)c < nvalid) store_xhat(a.xhat, a.xhat_dtype, (int64_t)(g0 + c) * kChunk, h);
-            wq[c] = w;
-        }
+        };
+        if (inner) body(std::true_type{});
+        else body(std::false_type{});
         store_words4(a.codes, g0, nvalid, wq);
         if (STATS) add_flushed(st, nvalid, nz);
     } else {

@@ -20,9 +20,9 @@
  *
  * Usage: division_check <check>   with <check> one of
  *   divconst     every finite binary32 a >= 0 (the kernels divide absolute
- *                maxima only) against a / Q, Q in {6, 7, 127, 448, 57344}:
+ *                maxima only) against a / Q, Q in {6, 7, 15, 127, 448, 57344}:
  *                any difference where the quotient is normal counts, and
- *                for Q = 7 and 127 any difference at all
+ *                for Q = 7, 15 and 127 any difference at all
  *   row_bf16     per-row INT8 / E4M3 / E5M2: every BF16 absmax alpha in
  *                [2^-40, 2^60], s = alpha / Q, every BF16 x with |x| <= alpha
  *   int4_fp16    every normal FP16 scale sf: the table reciprocal equals
@@ -32,6 +32,8 @@
  *                and the block-scale quotient (A/6) / s_g for every BF16
  *                A <= G
  *   random_f32   10^8 seeded binary32 pairs per Q with |x| <= alpha
+ *   int4zp       asymmetric INT4: 32768 seeded BF16 group ranges, the scale
+ *                span / 15, the shift quotient and every BF16 x in range
  * It prints "<check> <pairs checked> <mismatches>" per line; exit status 0.
  */
 #include <math.h>
@@ -76,10 +78,10 @@ static float e4m3_value(uint32_t c) {   /* positive E4M3 codes 1 .. 0x7E */
 }
 
 static void divconst(void) {
-    const float Qs[5] = {6.f, 7.f, 127.f, 448.f, 57344.f};
-    for (int qi = 0; qi < 5; ++qi) {
+    const float Qs[6] = {6.f, 7.f, 15.f, 127.f, 448.f, 57344.f};
+    for (int qi = 0; qi < 6; ++qi) {
         const float Q = Qs[qi], r = 1.0f / Q;
-        const int strict = Q == 7.f || Q == 127.f;
+        const int strict = Q == 7.f || Q == 15.f || Q == 127.f;
         uint64_t bad = 0, n = 0;
 #pragma omp parallel for reduction(+ : bad, n) schedule(static)
         for (int64_t hi = 0; hi < 32768; ++hi) {   /* a >= 0: every caller passes an absolute maximum */
@@ -191,6 +193,55 @@ static void nvfp4(void) {
     printf("nvfp4 %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
 }
 
+/* Asymmetric INT4 groups: span = hi + nlo (hi = max(0, max x), nlo =
+ * -min(0, min x), BF16 magnitudes), sc = span / 15 by the constant-divisor
+ * correction, y = RN(1 / sc).  Seeded pairs (hi, nlo), one within 24
+ * binades of the other, max(hi, nlo) in the fast range [2^-40, 2^60] and
+ * sc >= 2^-64, one in four one-sided:
+ * sc against the division, the shift RNE(nlo / sc) clamped to [0, 15]
+ * from the corrected quotient against the division's, and the corrected
+ * quotient of every BF16 x in [-nlo, hi]. */
+static void int4zp(void) {
+    uint64_t bad = 0, n = 0, bad_sc = 0, bad_sh = 0, groups = 0;
+    const float lo_lim = 0x1p-40f, hi_lim = 0x1p60f;
+    const uint32_t blo = bf(lo_lim) >> 16, bhi = bf(hi_lim) >> 16;
+#pragma omp parallel for reduction(+ : bad, n, bad_sc, bad_sh, groups) schedule(dynamic, 4)
+    for (int64_t pi = 0; pi < 32768; ++pi) {
+        uint64_t seed = 0x7A70000000ull + (uint64_t)pi * 0x10001ull;
+        const uint64_t r = splitmix(&seed);
+        /* hi anywhere in the fast range, nlo within 24 binades of it */
+        uint32_t hb = blo + (uint32_t)(r % (bhi - blo + 1));
+        int32_t nbs = (int32_t)hb + (int32_t)((r >> 24) % (48u * 128u)) - 24 * 128;
+        uint32_t nb = nbs < 0x0080 ? 0x0080u : nbs > 0x7F7F ? 0x7F7Fu : (uint32_t)nbs;
+        if ((r >> 61) == 0) hb = 0;          /* one-sided groups */
+        else if ((r >> 61) == 1) nb = 0;
+        if ((r >> 56) & 1) { const uint32_t t = hb; hb = nb; nb = t; }
+        const float hi = fb(hb << 16), nlo = fb(nb << 16), m = hi > nlo ? hi : nlo;
+        if (!(m >= lo_lim && m <= hi_lim)) continue;
+        const float span = hi + nlo;
+        const float sc = span / 15.0f;
+        if (bf(const_quotient(span, 15.0f, 1.0f / 15.0f)) != bf(sc)) ++bad_sc;
+        if (!(sc >= 0x1p-64f)) continue;
+        ++groups;
+        const float y = 1.0f / sc;
+        const float shd = fminf(fmaxf(rintf(nlo / sc), 0.f), 15.f);
+        const float shm = fminf(fmaxf(rintf(corrected_quotient(nlo, sc, y)), 0.f), 15.f);
+        if (bf(shd) != bf(shm)) ++bad_sh;
+        uint64_t nn = 0, bb = 0;
+        for (uint32_t b = 0; b < 0x7F80u; ++b) {
+            const float xa = fb(b << 16);
+            if (xa > hi && xa > nlo) break;
+            if (xa <= hi) { ++nn; if (!quotient_ok(corrected_quotient(xa, sc, y), xa / sc)) ++bb; }
+            if (xa <= nlo) { ++nn; if (!quotient_ok(corrected_quotient(-xa, sc, y), -xa / sc)) ++bb; }
+        }
+        n += nn;
+        bad += bb;
+    }
+    printf("int4zp_scale %llu %llu\n", (unsigned long long)groups, (unsigned long long)bad_sc);
+    printf("int4zp_shift %llu %llu\n", (unsigned long long)groups, (unsigned long long)bad_sh);
+    printf("int4zp %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+}
+
 static void random_f32(void) {
     const float Qs[5] = {127.f, 448.f, 57344.f, 6.f, 7.f};
     for (int qi = 0; qi < 5; ++qi) {
@@ -225,6 +276,7 @@ int main(int argc, char** argv) {
     else if (!strcmp(argv[1], "int4_fp16")) int4_fp16();
     else if (!strcmp(argv[1], "nvfp4")) nvfp4();
     else if (!strcmp(argv[1], "random_f32")) random_f32();
+    else if (!strcmp(argv[1], "int4zp")) int4zp();
     else return 2;
     return 0;
 }

@@ -38,10 +38,11 @@ def run(checker, what):
 
 
 def test_constant_divisors_exhaustive(checker):
-    """alpha / 127, / 448, / 57344 and A / 6, A / 7 for every finite binary32
-    value >= 0."""
+    """alpha / 127, / 448, / 57344, A / 6, A / 7 and the asymmetric INT4
+    span / 15 for every finite binary32 value >= 0."""
     res = run(checker, "divconst")
-    assert set(res) == {"divconst_6", "divconst_7", "divconst_127", "divconst_448", "divconst_57344"}
+    assert set(res) == {"divconst_6", "divconst_7", "divconst_15", "divconst_127", "divconst_448",
+                        "divconst_57344"}
     for name, (n, bad) in res.items():
         assert n == 0x7F800000, name          # every non-negative finite binary32 pattern
         assert bad == 0, f"{name}: {bad} quotients differ from the division"
@@ -78,3 +79,16 @@ def test_random_fp32_pairs(checker):
     assert len(res) == 5
     for name, (n, bad) in res.items():
         assert n == 10 ** 8 and bad == 0, name
+
+
+def test_int4zp_groups(checker):
+    """Asymmetric INT4 (Triton post, Puzzle 12): the group scale span / 15
+    by the constant-divisor correction, the shift RNE(nlo / sc) from the
+    corrected quotient, and the corrected quotient of every BF16 x of the
+    group's range, over seeded group ranges."""
+    res = run(checker, "int4zp")
+    groups, bad = res["int4zp_scale"]
+    assert groups > 20000 and bad == 0
+    assert res["int4zp_shift"] == (groups, 0)
+    n, bad = res["int4zp"]
+    assert n > 5e8 and bad == 0
