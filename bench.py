@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="profiling aid: run one call type in a loop (e.g. stream:e4m3:row, c2:e4m3:row, "
-                         "c4:nvfp4:block:static, c5:int4:block:nostats, ceiling, zp_gemm:16, mx_gemm:2048)")
+                         "c4:nvfp4:block:static, c5:int4:block:nostats, ceiling, copy, zp_gemm:16, mx_gemm:2048)")
     ap.add_argument("--reps", type=int, default=30, help="timed graph replays per breakdown entry")
     return ap.parse_args()
 
@@ -543,6 +543,21 @@ def only(args):
         res, _ = ceiling(reps=3)
         print(json.dumps({"ceiling": res}), flush=True)
         return
+    if args.only == "copy":
+        # the calibration kernel of the HBM counters: a 1 GiB copy (reads 1 GiB, writes 1 GiB)
+        lib = ctypes.CDLL(os.path.join(ROOT, "int_quantization_amd", "libiq_bench.so"))
+        lib.iqb_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+        n = 1 << 30
+        src = torch.empty(n // 4, dtype=torch.float32, device="cuda:0").normal_()
+        dst = torch.empty(n // 4, dtype=torch.float32, device="cuda:0")
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(args.warmup + args.steps):
+            assert lib.iqb_stream(2, 4, 1, src.data_ptr(), dst.data_ptr(), n, 4096, cs) == 0
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "calls": args.warmup + args.steps}),
+              flush=True)
+        return
     if args.only.startswith(("zp_gemm:", "mx_gemm:", "mxw_gemm:")):
         import int_quantization_amd as iq
         from synth import synth
@@ -571,10 +586,19 @@ def only(args):
     rest = [r for r in rest if r != "nostats"]
     var = rest[0] if rest else ""
     W = Workload(name, [(fmt, gran, var)], nsets=1 if name == "stream" else NSETS)
-    for s in range(args.warmup + args.steps):
-        W.quant(fmt, gran, s % W.nsets, var, stats=stats)
+    # the calls are replayed from a graph, as the per-format timings replay them
+    n = 2 * W.nsets if W.nsets > 1 else 2
+
+    def q():
+        for k in range(n):
+            W.quant(fmt, gran, k % W.nsets, var, stats=stats)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q()
+    for _ in range(args.warmup + args.steps):
+        g.replay()
     torch.cuda.synchronize()
-    print(json.dumps({"only": args.only, "calls": args.warmup + args.steps}), flush=True)
+    print(json.dumps({"only": args.only, "calls": n * (args.warmup + args.steps)}), flush=True)
 
 
 def main():

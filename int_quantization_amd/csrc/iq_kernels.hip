@@ -1917,12 +1917,13 @@ __device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChu
             }
         }
         const uint32_t shrep = (uint32_t)sh * 0x11111111u;
-        // Codes in the magic-number domain: v is clamped to [-sh, 15 - sh]
-        // first (integer bounds, so rounding the clamped value equals
-        // clamping the rounded one), (vc + kMagic) is kMagic + RNE(vc) (ties
-        // to an even q, as the rounding happens before the shift) and adding
-        // sh is exact, leaving kMagic + w, whose low nibble is w;
-        // x^ = sc * (t - (kMagic + sh)) with an exact difference.
+        // v is clamped to [-sh, 15 - sh] first (integer bounds, so rounding
+        // the clamped value equals clamping the rounded one) and rounded to
+        // q = RNE(vc) (ties to an even q, as the rounding happens before the
+        // shift); t = q + (kMagic + sh) is exact and holds w in its low
+        // nibble, and x^ = sc * q.  A q that rounds from a small negative vc
+        // is -0: the x^ output takes q = (vc + kMagic) - kMagic, +0 there as
+        // in x^ = sc * (w - sh); the statistics need no sign of zero.
         const float shf = (float)sh, magic_sh = kMagic + shf, vlo = -shf, vhi = 15.f - shf;
         uint32_t nz = 0, wq[4];
         auto body = [&](auto count_v) {
@@ -1937,8 +1938,9 @@ __device__ __forceinline__ void quant_lane_int4zp(const Chunk<IN> (&ch)[kTileChu
                     const float v = markstein(x[i], sc, y);
                     const float vc = __builtin_amdgcn_fmed3f(v, vlo, vhi);
                     if (STATS && COUNT_V) st.nsat += __popcll(__ballot(vc != v));
-                    t[i] = (vc + kMagic) + shf;
-                    h[i] = sc * (t[i] - magic_sh);
+                    const float q = XHAT ? (vc + kMagic) - kMagic : __builtin_rintf(vc);
+                    t[i] = q + magic_sh;
+                    h[i] = sc * q;
                 }
                 const uint32_t w = int4_pack8(t);
                 if (STATS) {
