@@ -34,6 +34,9 @@
  *   random_f32   10^8 seeded binary32 pairs per Q with |x| <= alpha
  *   int4zp       asymmetric INT4: 32768 seeded BF16 group ranges, the scale
  *                span / 15, the shift quotient and every BF16 x in range
+ *   a7_double_rounding  the INT4 FP16 scale: rounding A / 7 to binary32
+ *                first gives the same binary16 as one rounding, for every
+ *                finite binary32 A up to the binary16 range
  * It prints "<check> <pairs checked> <mismatches>" per line; exit status 0.
  */
 #include <math.h>
@@ -242,6 +245,39 @@ static void int4zp(void) {
     printf("int4zp %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
 }
 
+/* The INT4 scale rounds A / 7 to binary32 first, then to binary16 (RNE).
+ * Every finite binary32 A whose quotient is within the binary16 range:
+ * fp16(fl32(A / 7)) against the single rounding fp16(A / 7), taken from
+ * the binary64 quotient (53 bits: its own rounding cannot reach a binary16
+ * midpoint).  f16 rounds a non-negative double to binary16, exactly. */
+static double f16_of(double v) {
+    if (v == 0) return 0;
+    int e;
+    frexp(v, &e);
+    e -= 1;
+    if (e < -14) e = -14;
+    const double ulp = ldexp(1.0, e - 10);
+    return nearbyint(v / ulp) * ulp;
+}
+
+static void a7_double_rounding(void) {
+    uint64_t bad = 0, n = 0;
+#pragma omp parallel for reduction(+ : bad, n) schedule(static)
+    for (int64_t hi = 0; hi < 0x7F80; ++hi) {
+        for (uint32_t lo = 0; lo < 65536; ++lo) {
+            float A = fb(((uint32_t)hi << 16) | lo);
+            KEEP(A);
+            float q32 = A / 7.0f;
+            KEEP(q32);
+            const double q64 = (double)A / 7.0;
+            if (q64 > 65520.0) continue;   /* beyond it the scale saturates at 65504 */
+            ++n;
+            if (f16_of((double)q32) != f16_of(q64)) ++bad;
+        }
+    }
+    printf("a7_double_rounding %llu %llu\n", (unsigned long long)n, (unsigned long long)bad);
+}
+
 static void random_f32(void) {
     const float Qs[5] = {127.f, 448.f, 57344.f, 6.f, 7.f};
     for (int qi = 0; qi < 5; ++qi) {
@@ -277,6 +313,7 @@ int main(int argc, char** argv) {
     else if (!strcmp(argv[1], "nvfp4")) nvfp4();
     else if (!strcmp(argv[1], "random_f32")) random_f32();
     else if (!strcmp(argv[1], "int4zp")) int4zp();
+    else if (!strcmp(argv[1], "a7_double_rounding")) a7_double_rounding();
     else return 2;
     return 0;
 }

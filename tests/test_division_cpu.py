@@ -92,3 +92,13 @@ def test_int4zp_groups(checker):
     assert res["int4zp_shift"] == (groups, 0)
     n, bad = res["int4zp"]
     assert n > 5e8 and bad == 0
+
+
+def test_int4_scale_double_rounding(checker):
+    """The INT4 scale is fp16(fl32(A / 7)) (post "浅谈低精度浮点数", section
+    "FP4 / MXFP4 / NVFP4": s = A / 7 kept in FP16).  Rounding the quotient
+    to binary32 first never changes the binary16 result: every finite
+    binary32 A up to the binary16 range gives the same code as one rounding
+    of the exact quotient."""
+    n, bad = run(checker, "a7_double_rounding")["a7_double_rounding"]
+    assert n > 1e9 and bad == 0
