@@ -1036,9 +1036,10 @@ __device__ __forceinline__ void unstage_row(const RowStage<IN, CPT, NT>& st, con
 }
 
 // Rows in flight per workgroup of the per-row kernels: two LDS buffers for
-// FULL BF16 rows of 8 chunks per lane, one elsewhere.
-template <int IN, int CPT, bool FULL>
-constexpr int kRowDepth = FULL && IN == D_BF16 && CPT >= 8 ? 2 : 1;
+// FULL BF16 rows of 2048 chunks (16384 columns, 8 waves of 4 chunks per
+// lane), one elsewhere.
+template <int IN, int CPT, int NT, bool FULL>
+constexpr int kRowDepth = FULL && IN == D_BF16 && CPT * NT >= 2048 ? 2 : 1;
 
 // Row scale and flags, uniform over the workgroup (sat: over the wave).
 struct RowScale {
@@ -1208,7 +1209,7 @@ __device__ __forceinline__ void quant_row_fast(const Chunk<IN> (&ch)[CPT], const
 template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS>
 __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
     // Rows in flight per workgroup (LDS buffers).
-    constexpr int DEPTH = kRowDepth<IN, CPT, FULL>;
+    constexpr int DEPTH = kRowDepth<IN, CPT, NT, FULL>;
     __shared__ uint32_t s_red[3][NT / 64][2];
     __shared__ RowStage<IN, CPT, NT> stage[DEPTH];
     Stats st;
@@ -3456,10 +3457,12 @@ void launch_row_k(const RowArgs& r, int& grid, hipStream_t s) {
 }
 
 // Rows of up to 256 chunks take a one-wave workgroup (no cross-wave
-// reduction); longer rows four waves (up to 8 chunks per lane), beyond that
-// the two-pass kernel.  At 1024 chunks per row four waves with 4 chunks per
-// lane measure faster than one wave with 16 (whose 200 VGPRs halve the
-// resident waves).
+// reduction); rows of up to 1024 chunks four waves, rows of up to 2048
+// eight waves, with at most 4 chunks per lane; beyond that the two-pass
+// kernel.  At 1024 chunks per row four waves with 4 chunks per lane measure
+// faster than one wave with 16 (whose 200 VGPRs halve the resident waves),
+// and at 2048 eight waves with 4 faster than four with 8 (about 200 VGPRs,
+// 2 waves per SIMD against 8).
 template <int IN, int FMT, bool STATS>
 hipError_t launch_row_t(const RowArgs& r, int& grid, hipStream_t s) {
     const int cpr = r.cpr;
@@ -3468,7 +3471,7 @@ hipError_t launch_row_t(const RowArgs& r, int& grid, hipStream_t s) {
     else if (cpr <= 256) launch_row_k<IN, FMT, 4, 64, STATS>(r, grid, s);
     else if (cpr <= 512) launch_row_k<IN, FMT, 2, kThreads, STATS>(r, grid, s);
     else if (cpr <= 1024) launch_row_k<IN, FMT, 4, kThreads, STATS>(r, grid, s);
-    else if (cpr <= 2048) launch_row_k<IN, FMT, 8, kThreads, STATS>(r, grid, s);
+    else if (cpr <= 2048) launch_row_k<IN, FMT, 4, 512, STATS>(r, grid, s);   // 8 waves per row
     else {
         grid = grid_for(k_quant_row_long<IN, FMT, STATS>, (uint64_t)r.rows);
         k_quant_row_long<IN, FMT, STATS><<<grid, kThreads, 0, s>>>(r);
