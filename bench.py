@@ -635,7 +635,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": r["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(r["GBps"] / HBM_PEAK_GBS, 4), "traffic": read_traffic("stream_e4m3_row"),
                 "kernel": "iq_quantize E4M3 per row with statistics on the stream: one launch of "
-                          "k_quant_row<BF16, E4M3, 8 chunks per lane, 256 threads, full rows, statistics> "
+                          "k_quant_row<BF16, E4M3, 4 chunks per lane, 512 threads, full rows, statistics> "
                           "(the statistics fold runs inside it)",
                 "bytes_per_launch": per_format[rk]["bytes"], "avg_launch_us": r["us"],
                 "timing": "HIP events on the launch stream around replays of a graph of 2 calls; median"}
