@@ -3788,20 +3788,22 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 static_assert(Workspace::kBytes <= kScratchBytes, "the workspace layout fits the scratch array");
 
 hipError_t scratch_workspace(void** out) {
+    constexpr int kMaxDevices = 64;
     static std::mutex mu;
-    static std::unordered_map<int, void*> addr;   // device -> address of its scratch array
+    static void* addr[kMaxDevices] = {};   // device -> address of its scratch array (no host allocation)
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lk(mu);
-    auto it = addr.find(dev);
-    if (it == addr.end()) {
+    if (addr[dev] == nullptr) {
         void* ptr = nullptr;
         e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-        if (e != hipSuccess || ptr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
-        it = addr.emplace(dev, ptr).first;
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = ptr;
     }
-    *out = it->second;
+    *out = addr[dev];
     return hipSuccess;
 }
 
