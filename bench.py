@@ -604,7 +604,7 @@ def only(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on one MI355X)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (one MI355X per run)",
               file=sys.stderr)
         sys.exit(2)
     import torch
