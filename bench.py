@@ -18,7 +18,8 @@ Also reported:
               grid sweep: the practical HBM ceilings of this chip;
   per_format  every workload (c1-c5 and the stream), each format with
               statistics on and off: median, p10 and p90 over repeated
-              graph replays, GB/s, fractions of 8 TB/s, of the copy ceiling
+              graph replays (after about 40 ms of untimed replays, so that
+              the clocks have settled under load), GB/s, fractions of 8 TB/s, of the copy ceiling
               and of the matching read:write ceiling; moved-bytes GB/s for
               the calls with an absmax pre-pass; the dequantize call;
   roofline    the dominant kernel of the step against the HBM peak;
@@ -30,6 +31,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -63,7 +65,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-format workloads and the GEMMs")
     ap.add_argument("--no-gemm", action="store_true", help="skip the dequantize-GEMM consumers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,18 +123,29 @@ def backlog():
     torch.cuda._sleep(2_000_000)
 
 
-def time_graph(body, reps):
+def time_graph(body, reps, warm_ms=40.0):
     """Capture body() in a graph, replay it `reps` times with HIP events on
-    the current stream around each replay; returns per-replay milliseconds."""
+    the current stream around each replay; returns per-replay milliseconds.
+    Untimed replays worth about warm_ms of device time run first: after an
+    idle gap the first tens of milliseconds of heavy load run slower than
+    the steady state (the clocks settle under the power limit), and the
+    timings are of the steady state."""
     import torch
     s = torch.cuda.current_stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         body()
     g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    g.replay()
+    b.record(s)
     torch.cuda.synchronize()
+    nwarm = min(1000, max(1, math.ceil(warm_ms / max(a.elapsed_time(b), 1e-3))))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     backlog()
+    for _ in range(nwarm):
+        g.replay()
     for a, b in evs:
         a.record(s)
         g.replay()
@@ -638,7 +651,8 @@ def main():
                           "k_quant_row<BF16, E4M3, 4 chunks per lane, 512 threads, full rows, statistics> "
                           "(the statistics fold runs inside it)",
                 "bytes_per_launch": per_format[rk]["bytes"], "avg_launch_us": r["us"],
-                "timing": "HIP events on the launch stream around replays of a graph of 2 calls; median"}
+                "timing": "HIP events on the launch stream around replays of a graph of 2 calls, after "
+                          "about 40 ms of untimed replays; median"}
 
     extra = {}
     if ceil:
