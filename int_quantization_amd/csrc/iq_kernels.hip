@@ -1326,9 +1326,10 @@ struct FlatArgs {
     float* global_scale;
     void* xhat;
     int xhat_dtype;
-    const TensorInfo* info;  // per-tensor INT8/FP8 and NVFP4: absmax pre-pass result
-    const float* static_amax;  // static scaling: the caller's absmax instead of info
-    float* scale_out;        // static scaling: where the per-tensor scale (or s_g) goes
+    const uint64_t* amax_words;  // per-tensor INT8/FP8 and NVFP4: one word per pre-pass workgroup
+    int32_t amax_nwords;         //   (absmax bits | flags << 32, flags 1 non-finite, 2 exact zero)
+    const float* static_amax;    // static scaling: the caller's absmax instead of the pre-pass
+    float* scale_out;            // where the per-tensor scale (or s_g) goes
     StatsSink sink;
     uint32_t rule;           // R_* scale-rule bits (MXFP4 exponent, NVFP4 block-scale rounding)
     uint8_t* shifts;         // asymmetric INT4: packed 4-bit shifts
@@ -2118,28 +2119,76 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     static_assert(kTileChunksPerThread == 4, "lane layout assumes 4 chunks per lane");
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
-    // Per-tensor quantities (uniform over the grid): from the absmax pre-pass,
-    // or for static scaling from the caller's absmax.  A NaN, negative or
-    // infinite one is taken as 0 and -0 as +0; nothing is known of the data
-    // then (the per-tensor INT8 / FP8 kernel checks it per wave), so the
-    // exact-zero flag is set.
+    // Tiles in flight per workgroup (LDS buffers): two for BF16 INT4 and
+    // NVFP4, one elsewhere (measured: the second buffer slows the MXFP4 and
+    // per-tensor kernels with statistics; FP32 tiles are twice as large).
+    constexpr int DEPTH = IN == D_BF16 && (FMT == F_INT4 || FMT == F_NVFP4) ? 2 : 1;
+    __shared__ Stage<NW> stage[DEPTH];
+    const uint32_t lane = threadIdx.x & 63u;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t dlane = unswz(lane);
+    const uint32_t esize = IN == D_BF16 ? 2u : 4u;
+    auto stage_tile = [&](uint32_t tile, Stage<NW>& buf) {
+        const uint32_t base = tile * kTileChunks + 256u * wave;
+        if (a.geo.contiguous) {
+            // word ow of the wave's region is the (base * W + ow)-th 16-byte word of x
+            const char* wp = static_cast<const char*>(a.geo.x) + (size_t)base * W * 16u;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t ow = 64u * j + dlane;
+                if (base + ow / W < a.geo.nchunks) dma_word(wp + ow * 16u, &buf[j][64 * wave]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t ow = 64u * j + dlane;                // word of the wave's region
+                const uint32_t c = base + ow / W;
+                if (c < a.geo.nchunks)
+                    dma_word(static_cast<const char*>(a.geo.x) + a.geo.elem(c) * esize + 16u * (ow % W), &buf[j][64 * wave]);
+            }
+        }
+    };
+    const uint32_t G = gridDim.x;
+    // Per-tensor quantities (uniform over the grid): from the caller's absmax
+    // (static scaling) or from the pre-pass's per-workgroup words, folded
+    // here by every workgroup.  A NaN,
+    // negative or infinite caller absmax is taken as 0 and -0 as +0; nothing
+    // is known of the data then (the per-tensor INT8 / FP8 kernel checks it
+    // per wave), so the exact-zero flag is set.
     float s = 0.f, y = 0.f, T = 0.f;
     bool fast = false, sat = true, zeros = true;
-    TensorInfo inf = {0u, 0u, 0.f, 0u};
+    uint32_t amax_bits = 0u;
     if (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2 || FMT == F_NVFP4) {
+        constexpr float qdiv = FMT == F_INT8 ? 127.f : FMT == F_E4M3 ? 448.f : FMT == F_E5M2 ? 57344.f : 2688.f;
+        bool nonfinite = false;
         if (a.static_amax) {
             float am = *a.static_amax;
             am = (am >= 0.f && am <= 0x1.fffffep127f) ? __builtin_fabsf(am) : 0.f;
-            constexpr float qdiv = FMT == F_INT8 ? 127.f : FMT == F_E4M3 ? 448.f : FMT == F_E5M2 ? 57344.f : 2688.f;
-            inf.amax_bits = as_u(am); inf.nonfinite = 0u; inf.scale = am / qdiv; inf.zeros = 1u;
-            if (blockIdx.x == 0 && threadIdx.x == 0) *a.scale_out = inf.scale;
+            amax_bits = as_u(am);
         } else {
-            inf = *a.info;
+            __shared__ uint32_t s_pre[2][kThreads / 64][2];
+            // Plain loads: the words were stored by the previous kernel on the
+            // stream, and every workgroup reads the same 16 KB, so they are
+            // served from L2 after the first.  All issued before the first use.
+            uint64_t w[kMaxGrid / kThreads];
+#pragma unroll
+            for (int k = 0; k < kMaxGrid / kThreads; ++k) {
+                const int i = (int)threadIdx.x + k * kThreads;
+                w[k] = i < a.amax_nwords ? a.amax_words[i] : 0u;
+            }
+            uint32_t m = 0u, fl = 0u;
+#pragma unroll
+            for (int k = 0; k < kMaxGrid / kThreads; ++k) {
+                m = umax(m, (uint32_t)w[k]);
+                fl |= (uint32_t)(w[k] >> 32);
+            }
+            amax_bits = block_max_or<kThreads / 64>(m, (fl & 1u) != 0, nonfinite, s_pre[0]);
+            block_max_or<kThreads / 64>(0u, (fl & 2u) != 0, zeros, s_pre[1]);
         }
-        s = inf.scale;
-        zeros = inf.zeros != 0;
-        const float alpha = as_f(inf.amax_bits);
-        fast = inf.nonfinite == 0 && stat_range(alpha);
+        s = as_f(amax_bits) / qdiv;
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.scale_out = s;
+        const float alpha = as_f(amax_bits);
+        fast = !nonfinite && stat_range(alpha);
         if constexpr (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) {
             if (fast) {
                 y = 1.0f / s;
@@ -2171,42 +2220,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
         for (int f = threadIdx.x; f < 1024; f += kThreads) s_rtab[f] = 1.0f / (1.0f + (float)f * 0x1p-10f);
         __syncthreads();
     }
-    // Tiles in flight per workgroup (LDS buffers): two for BF16 INT4 and
-    // NVFP4, one elsewhere (measured: the second buffer slows the MXFP4 and
-    // per-tensor kernels with statistics; FP32 tiles are twice as large).
-    constexpr int DEPTH = IN == D_BF16 && (FMT == F_INT4 || FMT == F_NVFP4) ? 2 : 1;
-    __shared__ Stage<NW> stage[DEPTH];
-    const uint32_t lane = threadIdx.x & 63u;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t dlane = unswz(lane);
-    const uint32_t esize = IN == D_BF16 ? 2u : 4u;
-    auto stage_tile = [&](uint32_t tile, Stage<NW>& buf) {
-        const uint32_t base = tile * kTileChunks + 256u * wave;
-        if (a.geo.contiguous) {
-            // word ow of the wave's region is the (base * W + ow)-th 16-byte word of x
-            const char* wp = static_cast<const char*>(a.geo.x) + (size_t)base * W * 16u;
-#pragma unroll
-            for (int j = 0; j < NW; ++j) {
-                const uint32_t ow = 64u * j + dlane;
-                if (base + ow / W < a.geo.nchunks) dma_word(wp + ow * 16u, &buf[j][64 * wave]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NW; ++j) {
-                const uint32_t ow = 64u * j + dlane;                // word of the wave's region
-                const uint32_t c = base + ow / W;
-                if (c < a.geo.nchunks)
-                    dma_word(static_cast<const char*>(a.geo.x) + a.geo.elem(c) * esize + 16u * (ow % W), &buf[j][64 * wave]);
-            }
-        }
-    };
-    const uint32_t G = gridDim.x;
+    // The first tiles are copied only now: issued before the prologue above,
+    // the compiler's waits in the loop below came out differently (measured on
+    // BF16 65536 x 16384 NVFP4: 10 us slower with statistics, 24 us faster
+    // without).
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
         if (blockIdx.x + d * G < ntiles) stage_tile(blockIdx.x + d * G, stage[d]);
     FlatConst fk;
     fk.s = s; fk.y = y; fk.T = T; fk.fast = fast; fk.sat = sat; fk.zeros = zeros; fk.nk = nk; fk.rtab = s_rtab;
-    fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? inf.amax_bits : 0u;
+    fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? amax_bits : 0u;
     const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
     int b = 0;
     for (uint32_t tile = blockIdx.x; tile < ntiles; tile += G, b = DEPTH > 1 ? b ^ 1 : 0) {
@@ -2247,16 +2270,18 @@ struct AmaxSink {
     uint32_t* partials;   // two words per workgroup: absmax bits, flags
     uint32_t* ticket;     // arrival counters (kTicketBytes): zero at the start and at the end
     float qdiv;           // 0: no scale
-    TensorInfo* info;
     float* scale_out;
     float* amax_out;
 };
 
 // Each workgroup reduces its tiles to (absmax over finite elements, flags:
-// 1 non-finite seen, 2 exact zero seen), publishes them with one
-// device-scope atomic exchange and counts its arrival; the last one folds all
-// partials (max and OR, order-free) and writes the results.
-template <int IN>
+// 1 non-finite seen, 2 exact zero seen) in one word.  As the pre-pass of a
+// quantize call (FOLD false) it stores the word and ends: the cast kernel,
+// next on the stream, folds the words in each of its workgroups.  With FOLD
+// (the absmax call, and empty tensors) the word is published with one
+// device-scope atomic exchange and the workgroup counts its arrival; the
+// last one folds all words (max and OR, order-free) and writes the results.
+template <int IN, bool FOLD>
 __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) {
     __shared__ uint32_t s_red[2][kThreads / 64][2];
     __shared__ uint32_t s_last;
@@ -2284,8 +2309,13 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) 
     bool nonfinite, zeros;
     const uint32_t bits = block_max_or<kThreads / 64>(m, Chunk<IN>::absmax_bits(raw) >= kNonFinite, nonfinite, s_red[0]);
     block_max_or<kThreads / 64>(0u, Chunk<IN>::has_zero(mn), zeros, s_red[1]);
+    const uint64_t word = (uint64_t)bits | ((uint64_t)((nonfinite ? 1u : 0u) | (zeros ? 2u : 0u)) << 32);
+    if (!FOLD) {
+        // The cast kernel launched next on the stream folds the words itself.
+        if (threadIdx.x == 0) reinterpret_cast<uint64_t*>(sink.partials)[blockIdx.x] = word;
+        return;
+    }
     if (threadIdx.x == 0) {
-        const uint64_t word = (uint64_t)bits | ((uint64_t)((nonfinite ? 1u : 0u) | (zeros ? 2u : 0u)) << 32);
         const uint64_t old = __hip_atomic_exchange(reinterpret_cast<uint64_t*>(sink.partials) + blockIdx.x, word,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("" ::"v"(old) : "memory");   // performed before the ticket
@@ -2311,13 +2341,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(FlatGeom geo, AmaxSink sink) 
     fm = block_max_or<kThreads / 64>(fm, (ff & 1u) != 0, any_nonfinite, s_red[0]);
     block_max_or<kThreads / 64>(0u, (ff & 2u) != 0, any_zero, s_red[1]);
     if (threadIdx.x == 0) {
-        const float sc = sink.qdiv > 0.f ? as_f(fm) / sink.qdiv : 0.f;
-        if (sink.info) {
-            TensorInfo t;
-            t.amax_bits = fm; t.nonfinite = any_nonfinite ? 1u : 0u; t.scale = sc; t.zeros = any_zero ? 1u : 0u;
-            *sink.info = t;
-        }
-        if (sink.scale_out) *sink.scale_out = sc;
+        if (sink.scale_out) *sink.scale_out = sink.qdiv > 0.f ? as_f(fm) / sink.qdiv : 0.f;
         if (sink.amax_out) *sink.amax_out = as_f(fm);
     }
 }
@@ -3543,21 +3567,31 @@ hipError_t launch_row_fmt(int fmt, const RowArgs& r, bool stats, int& grid, hipS
     }
 }
 
-// The absmax pre-pass in one launch (its last workgroup writes the results);
-// an empty tensor takes one workgroup, which writes zeros.
-hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, float qdiv, TensorInfo* info,
-                            float* scale_out, float* amax_out, hipStream_t s) {
+// The absmax pass in one launch.  fold: its last workgroup writes the
+// results (an empty tensor takes one workgroup, which writes zeros);
+// otherwise each workgroup leaves its word at Workspace::kAmaxOff for the
+// cast kernel, and *grid_out is the number of words.
+template <int IN>
+void launch_amax_k(const FlatGeom& geo, const AmaxSink& k, bool fold, int& grid, hipStream_t s) {
+    if (fold) {
+        grid = grid_for(k_amax<IN, true>, tiles_of(geo.nchunks));
+        k_amax<IN, true><<<grid, kThreads, 0, s>>>(geo, k);
+    } else {
+        grid = grid_for(k_amax<IN, false>, tiles_of(geo.nchunks));
+        k_amax<IN, false><<<grid, kThreads, 0, s>>>(geo, k);
+    }
+}
+
+hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, bool fold, float qdiv, float* scale_out,
+                            float* amax_out, int* grid_out, hipStream_t s) {
     AmaxSink k;
     k.partials = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxOff);
     k.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + Workspace::kAmaxTicketOff);
-    k.qdiv = qdiv; k.info = info; k.scale_out = scale_out; k.amax_out = amax_out;
-    if (in_dtype == D_BF16) {
-        const int grid = grid_for(k_amax<D_BF16>, tiles_of(geo.nchunks));
-        k_amax<D_BF16><<<grid, kThreads, 0, s>>>(geo, k);
-    } else {
-        const int grid = grid_for(k_amax<D_F32>, tiles_of(geo.nchunks));
-        k_amax<D_F32><<<grid, kThreads, 0, s>>>(geo, k);
-    }
+    k.qdiv = qdiv; k.scale_out = scale_out; k.amax_out = amax_out;
+    int grid = 0;
+    if (in_dtype == D_BF16) launch_amax_k<D_BF16>(geo, k, fold, grid, s);
+    else launch_amax_k<D_F32>(geo, k, fold, grid, s);
+    if (grid_out) *grid_out = grid;
     return hipGetLastError();
 }
 
@@ -3566,7 +3600,6 @@ hipError_t launch_amax_pass(int in_dtype, const FlatGeom& geo, void* ws, float q
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
     char* ws = static_cast<char*>(q.workspace);
-    TensorInfo* info = reinterpret_cast<TensorInfo*>(ws + Workspace::kInfoOff);
     const bool stats = q.stats != nullptr;
     const int64_t nelem = q.rows * q.cols;
     StatsSink sink;
@@ -3592,14 +3625,18 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         FlatArgs f;
         f.geo = make_geom(q.x, q.rows, q.cols, q.ld);
         f.codes = static_cast<uint8_t*>(q.codes); f.scales = q.scales; f.global_scale = q.global_scale;
-        f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.info = info; f.sink = sink;
+        f.xhat = q.xhat; f.xhat_dtype = q.xhat_dtype; f.sink = sink;
+        f.amax_words = reinterpret_cast<const uint64_t*>(ws + Workspace::kAmaxOff);
+        f.amax_nwords = 0;
         f.rule = q.rule;
         f.shifts = q.shifts;
         f.static_amax = q.static_amax;
         f.scale_out = q.fmt == F_NVFP4 ? q.global_scale : static_cast<float*>(q.scales);
         if ((q.gran == G_TENSOR || q.fmt == F_NVFP4) && !q.static_amax) {
+            // A non-empty tensor's cast kernel folds the pre-pass words itself;
+            // an empty one has no cast kernel, so its pre-pass writes the scale.
             const float qdiv = q.fmt == F_INT8 ? 127.f : q.fmt == F_E4M3 ? 448.f : q.fmt == F_E5M2 ? 57344.f : 2688.f;
-            e = launch_amax_pass(q.in_dtype, f.geo, ws, qdiv, info, f.scale_out, nullptr, s);
+            e = launch_amax_pass(q.in_dtype, f.geo, ws, nelem == 0, qdiv, f.scale_out, nullptr, &f.amax_nwords, s);
             if (e != hipSuccess) return e;
         }
         const bool check = q.static_amax != nullptr;
@@ -3786,7 +3823,7 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
 hipError_t launch_amax(int in_dtype, int64_t rows, int64_t cols, int64_t ld, const void* x, float* amax_out,
                        void* workspace, hipStream_t stream) {
     FlatGeom geo = make_geom(x, rows, cols, ld);
-    return launch_amax_pass(in_dtype, geo, workspace, 0.f, nullptr, nullptr, amax_out, stream);
+    return launch_amax_pass(in_dtype, geo, workspace, true, 0.f, nullptr, amax_out, nullptr, stream);
 }
 
 // ---------------------------------------------------------------------------

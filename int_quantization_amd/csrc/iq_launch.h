@@ -32,14 +32,6 @@ struct alignas(16) Partial {
 };
 static_assert(sizeof(Partial) == 48, "partial layout");
 
-// Workspace header written by the absmax pre-pass.
-struct alignas(16) TensorInfo {
-    uint32_t amax_bits;   // absmax over finite elements (bits of a non-negative float)
-    uint32_t nonfinite;   // nonzero if any element is NaN or +-Inf
-    float scale;          // per-tensor scale (INT8/FP8) or NVFP4 global scale s_g
-    uint32_t zeros;       // nonzero if any element is an exact zero
-};
-
 // Arrival counters of one launch: workgroups count on their group's counter
 // (kTicketGroup workgroups per group), the last of each group on the
 // launch-wide counter, so no counter takes more than kTicketGroup atomics.
@@ -53,8 +45,7 @@ constexpr size_t kTicketBytes = sizeof(uint32_t) * kTicketStride * (1 + kMaxGrid
 // its group counter), so a zero-filled workspace stays ready for the next
 // call.
 struct Workspace {
-    static constexpr size_t kInfoOff = 0;
-    static constexpr size_t kStatsTicketOff = 256;                           // kTicketBytes
+    static constexpr size_t kStatsTicketOff = 0;                             // kTicketBytes
     static constexpr size_t kAmaxTicketOff = kStatsTicketOff + kTicketBytes;  // kTicketBytes
     static constexpr size_t kAmaxOff = kAmaxTicketOff + kTicketBytes;        // uint2 per workgroup
     static constexpr size_t kPartialOff = kAmaxOff + sizeof(uint32_t) * 2 * kMaxGrid;
