@@ -2119,10 +2119,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     static_assert(kTileChunksPerThread == 4, "lane layout assumes 4 chunks per lane");
     Stats st;
     const uint32_t ntiles = (a.geo.nchunks + kTileChunks - 1) / kTileChunks;
-    // Tiles in flight per workgroup (LDS buffers): two for BF16 INT4 and
-    // NVFP4, one elsewhere (measured: the second buffer slows the MXFP4 and
-    // per-tensor kernels with statistics; FP32 tiles are twice as large).
-    constexpr int DEPTH = IN == D_BF16 && (FMT == F_INT4 || FMT == F_NVFP4) ? 2 : 1;
+    // Tiles in flight per workgroup (LDS buffers): for BF16 INT4 and NVFP4
+    // two with statistics and three without, one elsewhere.  Measured on BF16
+    // 65536 x 16384: without statistics a third buffer takes INT4 from 491 to
+    // 459 us (28672 x 8192: 105 -> 99 us), with statistics it costs 10 us (the
+    // statistics kernels are bound by their VALU work, and 48 KB of LDS per
+    // workgroup leaves 3 resident instead of 4); a second buffer slows the
+    // MXFP4 and per-tensor kernels with statistics (513 -> 538 and 914 ->
+    // 966 us).  FP32 tiles are twice as large.
+    constexpr int DEPTH = IN == D_BF16 && (FMT == F_INT4 || FMT == F_NVFP4) ? (STATS ? 2 : 3) : 1;
     __shared__ Stage<NW> stage[DEPTH];
     const uint32_t lane = threadIdx.x & 63u;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2232,15 +2237,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     fk.amax_bits = (FMT == F_INT8 || FMT == F_E4M3 || FMT == F_E5M2) ? amax_bits : 0u;
     const uint32_t full_tiles = a.geo.nchunks / kTileChunks;
     int b = 0;
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += G, b = DEPTH > 1 ? b ^ 1 : 0) {
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += G, b = b + 1 < DEPTH ? b + 1 : 0) {
         // the lane's first chunk, and its words of the wave's region in LDS
         const uint32_t g0 = tile * kTileChunks + 256u * wave + (FlatOwn<FMT>::kInterleaved ? lane : 4u * lane);
-        // This tile's copies have landed once at most the NW copies of the
-        // next tile, issued after them, are outstanding (memory operations
-        // of a wave complete in issue order); a next tile that is not full
-        // may have been issued with fewer copies: then wait for all.
+        // This tile's copies have landed once at most the (DEPTH - 1) * NW
+        // copies of the next tiles, issued after them, are outstanding
+        // (memory operations of a wave complete in issue order); a next tile
+        // that is not full may have been issued with fewer copies: then wait
+        // for all.
         if constexpr (DEPTH > 1) {
-            if (tile + G < full_tiles) wait_staged_keep<NW>();
+            if (tile + (DEPTH - 1) * G < full_tiles) wait_staged_keep<(DEPTH - 1) * NW>();
             else wait_staged();
         } else {
             wait_staged();
