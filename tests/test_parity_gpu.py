@@ -429,6 +429,26 @@ def test_full_size_workloads(iq, O, S, cfg, fmt, gran, flags):
     del xd
 
 
+FLAT = [f for f in ALL if f[1] != "row"]
+
+
+@pytest.mark.parametrize("fmt,gran", FLAT)
+def test_many_tiles_ragged(iq, O, S, fmt, gran):
+    """The flat kernels with many tiles per workgroup and a ragged last
+    tile (BF16 2500 x 8448: 2578 full tiles of 1024 chunks and one of 128),
+    so the persistent loop runs its in-flight buffers down to a partial
+    tile: with and without statistics, and with x^."""
+    x = make_input(S, 1, 2500, 8448, None, seed=77)
+    assert (2500 * 8448 // 8) % 1024 == 128
+    xd = to_device(x)
+    r = oracle_ref(O, x, fmt, gran)
+    for xhat, stats in ((None, True), (None, False), ("f32", False)):
+        g = run_gpu(iq, None, fmt, gran, xhat=xhat, stats=stats, x_dev=xd)
+        compare(g, r, fmt, f"{fmt}/{gran} 2500x8448 stats={stats} xhat={xhat}", O)
+        del g
+    del xd
+
+
 @pytest.fixture(scope="module")
 def stream_input(S):
     """The 2 GiB streaming workload, on the host and the device."""
