@@ -134,9 +134,9 @@ size_t iq_workspace_bytes(const iq_desc* d);
  *                    before its first use (e.g. hipMemset once, or torch.zeros);
  *                    every call leaves it ready for the next one.  The
  *                    workgroups of a call count themselves on it to decide
- *                    which one folds the partial statistics (and the
- *                    per-tensor absmax), so concurrent calls need separate
- *                    workspaces
+ *                    which one folds the partial statistics, and the absmax
+ *                    pre-pass leaves its per-workgroup maxima there for the
+ *                    cast, so concurrent calls need separate workspaces
  */
 iq_status iq_quantize(const iq_desc* d, const void* x, void* codes, void* scales,
                       float* global_scale, iq_stats* stats, void* xhat, int32_t xhat_dtype,
