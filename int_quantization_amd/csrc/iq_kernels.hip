@@ -2156,7 +2156,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
     const uint32_t G = gridDim.x;
     // Per-tensor quantities (uniform over the grid): from the caller's absmax
     // (static scaling) or from the pre-pass's per-workgroup words, folded
-    // here by every workgroup.  A NaN,
+    // here by every workgroup; workgroup 0 writes the scale.  A NaN,
     // negative or infinite caller absmax is taken as 0 and -0 as +0; nothing
     // is known of the data then (the per-tensor INT8 / FP8 kernel checks it
     // per wave), so the exact-zero flag is set.
@@ -2273,7 +2273,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_flat(FlatArgs a) {
 // the per-tensor scale alpha / qdiv or the NVFP4 global scale amax / 2688
 // (scale_out), and the absmax itself (amax_out); each may be null.
 struct AmaxSink {
-    uint32_t* partials;   // two words per workgroup: absmax bits, flags
+    uint32_t* partials;   // one 64-bit word per workgroup: absmax bits | flags << 32
     uint32_t* ticket;     // arrival counters (kTicketBytes): zero at the start and at the end
     float qdiv;           // 0: no scale
     float* scale_out;
