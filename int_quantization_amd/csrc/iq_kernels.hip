@@ -2482,16 +2482,18 @@ typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 // Tile (jb, nb) of GEMM work item idx.  The items of one XCD are
 // consecutive, and the workgroups that XCD holds at once run consecutive
-// items: walking kTileGroupJ weight-row tiles of a token tile before the
-// next token tile makes them share both operands in that XCD's L2, where
-// row-major order (every token tile of one weight-row tile first) streams
-// the whole activation matrix past each pair of weight tiles.  FP4 GEMM
-// 14336 x 4096 x 8192 tokens: 459 -> 396 us (groups of 4, 8 and 16 weight
-// tiles: 403, 400 and 396 us); unchanged up to 256 tokens.
-constexpr uint32_t kTileGroupJ = 16;
+// items: walking GJ weight-row tiles of a token tile before the next token
+// tile makes them share both operands in that XCD's L2, where row-major
+// order (every token tile of one weight-row tile first) streams the whole
+// activation matrix past each pair of weight tiles.  Measured at 2048 / 8192
+// tokens against row-major order: FP4 GEMM (GJ 8) 116 -> 109 / 470 -> 390
+// us, MXFP4 x BF16 (GJ 16) 292 -> 279 / 1160 -> 965 us, asymmetric INT4
+// (GJ 16) 1210 -> 1151 / 5195 -> 5004 us; groups of 32 and 64 were slower
+// for all three.  Unchanged up to 256 tokens.
+template <uint32_t GJ>
 __device__ __forceinline__ void gemm_tile_of(uint32_t idx, uint32_t tiles_j, uint32_t tiles_n, int& jb, int& nb) {
-    const uint32_t gsize = kTileGroupJ * tiles_n, grp = idx / gsize, first = grp * kTileGroupJ;
-    const uint32_t gj = min(tiles_j - first, kTileGroupJ), in = idx - grp * gsize;
+    const uint32_t gsize = GJ * tiles_n, grp = idx / gsize, first = grp * GJ;
+    const uint32_t gj = min(tiles_j - first, GJ), in = idx - grp * gsize;
     jb = (int)(first + in % gj);
     nb = (int)(in / gj);
 }
@@ -2754,7 +2756,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_zp_gemm(ZpGemmArgs a) {
     const uint32_t tile = idx / (uint32_t)a.ksplit;
     const int half = (int)(idx % (uint32_t)a.ksplit);
     int jb, nb;
-    gemm_tile_of(tile, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
+    gemm_tile_of<16>(tile, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
     const int j0 = jb * kGemmTile, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -2927,7 +2929,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
     int jb, nb;
-    gemm_tile_of(idx, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
+    gemm_tile_of<8>(idx, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
     const int j0 = jb * TM, t0 = nb * TN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -3219,7 +3221,7 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
     int jb, nb;
-    gemm_tile_of(idx, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
+    gemm_tile_of<16>(idx, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
     const int j0 = jb * TM, t0 = nb * kTN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
