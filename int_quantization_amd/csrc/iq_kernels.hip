@@ -1005,6 +1005,11 @@ struct RowArgs {
     void* xhat;
     int xhat_dtype;
     StatsSink sink;
+    // per-tensor scale over rows of the tensor (TENSOR): the absmax
+    // pre-pass's words and where the tensor's scale goes
+    const uint64_t* amax_words;
+    int32_t amax_nwords;
+    float* scale_out;
 };
 
 template <int IN, int CPT, int NT>
@@ -1204,16 +1209,54 @@ __device__ __forceinline__ void quant_row_fast(const Chunk<IN> (&ch)[CPT], const
     }
 }
 
+// The scale of a whole tensor quantized over rows of it (per-tensor INT8 /
+// FP8 on a contiguous tensor): every workgroup folds the absmax pre-pass's
+// per-workgroup words (maximum and OR) and derives what the per-tensor flat
+// kernel derives from them: s = alpha / Q, the FP32 fast path for a finite
+// tensor with alpha in the statistics range, saturation possible when alpha
+// exceeds T, exact zeros as flagged.  Workgroup 0 writes the scale.
+template <int FMT, int NT>
+__device__ __forceinline__ RowScale tensor_row_scale(const RowArgs& a) {
+    __shared__ uint32_t s_pre[2][NT / 64][2];
+    uint64_t w[kMaxGrid / NT];   // every load issued before the first use
+#pragma unroll
+    for (int k = 0; k < kMaxGrid / NT; ++k) {
+        const int i = (int)threadIdx.x + k * NT;
+        w[k] = i < a.amax_nwords ? a.amax_words[i] : 0u;
+    }
+    uint32_t m = 0u, fl = 0u;
+#pragma unroll
+    for (int k = 0; k < kMaxGrid / NT; ++k) {
+        m = umax(m, (uint32_t)w[k]);
+        fl |= (uint32_t)(w[k] >> 32);
+    }
+    bool nonfinite, zeros;
+    const uint32_t bits = block_max_or<NT / 64>(m, (fl & 1u) != 0, nonfinite, s_pre[0]);
+    block_max_or<NT / 64>(0u, (fl & 2u) != 0, zeros, s_pre[1]);
+    const float alpha = as_f(bits);
+    RowScale r;
+    r.s = alpha / Fmt<FMT>::qmax;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.scale_out = r.s;
+    r.fast = !nonfinite && stat_range(alpha);
+    r.y = r.fast ? 1.0f / r.s : 0.f;
+    r.T = r.fast ? sat_threshold<FMT>(r.s) : 0.f;
+    r.sat = !r.fast || alpha > r.T;
+    r.zeros = zeros;
+    return r;
+}
+
 // Per-row INT8 / FP8: the next row streams into LDS while the current one
 // is reduced, cast and stored.  XHAT: the x^ output is requested (a separate
 // instantiation, so the other one carries no x^ code).
-template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS>
+template <int IN, int FMT, int CPT, int NT, bool FULL, bool XHAT, bool STATS, bool TENSOR = false>
 __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
     // Rows in flight per workgroup (LDS buffers).
     constexpr int DEPTH = kRowDepth<IN, CPT, NT, FULL>;
     __shared__ uint32_t s_red[3][NT / 64][2];
     __shared__ RowStage<IN, CPT, NT> stage[DEPTH];
     Stats st;
+    RowScale rt{};
+    if constexpr (TENSOR) rt = tensor_row_scale<FMT, NT>(a);
     const int32_t G = gridDim.x;
     const int64_t cols = (int64_t)a.cpr * kChunk;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1236,8 +1279,19 @@ __global__ __launch_bounds__(NT) void k_quant_row(RowArgs a) {
         unstage_row<IN, CPT, NT, FULL>(stage[b], a, ch);
         wait_lds_reads();
         if (row + DEPTH * G < a.rows) stage_row<IN, CPT, NT, FULL>(stage[b], a, row + DEPTH * G, wave);
-        const auto r = row_scale<IN, FMT, CPT, NT>(ch, s_red, parity);
-        if (threadIdx.x == 0) a.scales[row] = r.s;
+        RowScale r;
+        if constexpr (TENSOR) {
+            r = rt;
+            // Keep the workgroup's waves on one row, as the per-row reduction
+            // does: waves left to drift onto different rows issue their
+            // copies interleaved with other rows' (BF16 65536 x 16384
+            // per-tensor INT8: 655 us for this kernel without the barrier,
+            // about 568 with it).
+            lds_barrier();
+        } else {
+            r = row_scale<IN, FMT, CPT, NT>(ch, s_red, parity);
+            if (threadIdx.x == 0) a.scales[row] = r.s;
+        }
         uint8_t* crow = a.codes + (int64_t)row * cols;
         if (r.fast) {
             quant_row_fast<IN, FMT, CPT, NT, FULL, XHAT, STATS>(ch, a, row, r, crow, st);
@@ -3552,6 +3606,28 @@ hipError_t launch_row(const RowArgs& r, bool stats, int& grid, hipStream_t s) {
     return stats ? launch_row_t<IN, FMT, true>(r, grid, s) : launch_row_t<IN, FMT, false>(r, grid, s);
 }
 
+// Per-tensor INT8 / FP8 of a contiguous BF16 tensor whose size is a multiple
+// of kTensorRowCols, as rows of that many elements under the tensor's
+// scale: the per-row kernel's staging (two rows of 32 KB in flight per
+// workgroup of eight waves, the waves kept on one row) moves the tensor
+// faster than the flat kernel (BF16 65536 x 16384 INT8 per tensor, the
+// whole call with its absmax pre-pass: 911 -> 875 us with statistics,
+// 887 -> 858 us without).
+constexpr int64_t kTensorRowCols = 16384;
+template <int FMT, bool STATS>
+hipError_t launch_row_tensor_k(const RowArgs& r, int& grid, hipStream_t s) {
+    grid = grid_for_rows<512>(k_quant_row<D_BF16, FMT, 4, 512, true, false, STATS, true>, (uint64_t)r.rows);
+    k_quant_row<D_BF16, FMT, 4, 512, true, false, STATS, true><<<grid, 512, 0, s>>>(r);
+    return hipGetLastError();
+}
+hipError_t launch_row_tensor(int fmt, const RowArgs& r, bool stats, int& grid, hipStream_t s) {
+    switch (fmt) {
+    case F_INT8: return stats ? launch_row_tensor_k<F_INT8, true>(r, grid, s) : launch_row_tensor_k<F_INT8, false>(r, grid, s);
+    case F_E4M3: return stats ? launch_row_tensor_k<F_E4M3, true>(r, grid, s) : launch_row_tensor_k<F_E4M3, false>(r, grid, s);
+    default: return stats ? launch_row_tensor_k<F_E5M2, true>(r, grid, s) : launch_row_tensor_k<F_E5M2, false>(r, grid, s);
+    }
+}
+
 template <int IN, int FMT, bool STATS, bool CHECK, bool XHAT>
 hipError_t launch_flat_one(const FlatArgs& f, int& grid, hipStream_t s) {
     grid = grid_for(k_quant_flat<IN, FMT, STATS, CHECK, XHAT>, tiles_of(f.geo.nchunks));
@@ -3648,6 +3724,7 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
         r.x = q.x; r.ld = q.ld; r.rows = (int32_t)q.rows; r.cpr = (int32_t)(q.cols / kChunk);
         r.codes = static_cast<uint8_t*>(q.codes); r.scales = static_cast<float*>(q.scales);
         r.xhat = q.xhat; r.xhat_dtype = q.xhat_dtype; r.sink = sink;
+        r.amax_words = nullptr; r.amax_nwords = 0; r.scale_out = nullptr;
         if (nelem) {
             e = q.in_dtype == D_BF16 ? launch_row_fmt<D_BF16>(q.fmt, r, stats, grid, s)
                                      : launch_row_fmt<D_F32>(q.fmt, r, stats, grid, s);
@@ -3672,9 +3749,22 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t s) {
             if (e != hipSuccess) return e;
         }
         const bool check = q.static_amax != nullptr;
-        // static scaling launches even an empty tensor: its one workgroup
-        // writes the scale derived from the caller's absmax
-        if (nelem || q.static_amax) {
+        // per tensor, measured scale, contiguous BF16 in whole rows of
+        // kTensorRowCols, no x^: the per-row kernel under the tensor's scale
+        const bool tensor_rows = q.gran == G_TENSOR && q.in_dtype == D_BF16 && !q.static_amax && !q.xhat &&
+                                 q.ld == q.cols && nelem > 0 && nelem % kTensorRowCols == 0;
+        if (tensor_rows) {
+            RowArgs r;
+            r.x = q.x; r.ld = kTensorRowCols;
+            r.rows = (int32_t)(nelem / kTensorRowCols); r.cpr = (int32_t)(kTensorRowCols / kChunk);
+            r.codes = static_cast<uint8_t*>(q.codes); r.scales = nullptr;
+            r.xhat = nullptr; r.xhat_dtype = 0; r.sink = sink;
+            r.amax_words = f.amax_words; r.amax_nwords = f.amax_nwords; r.scale_out = f.scale_out;
+            e = launch_row_tensor(q.fmt, r, stats, grid, s);
+            stats_written = true;
+        } else if (nelem || q.static_amax) {
+            // static scaling launches even an empty tensor: its one workgroup
+            // writes the scale derived from the caller's absmax
             e = q.in_dtype == D_BF16 ? launch_flat_fmt<D_BF16>(q.fmt, f, stats, check, grid, s)
                                      : launch_flat_fmt<D_F32>(q.fmt, f, stats, check, grid, s);
             stats_written = true;

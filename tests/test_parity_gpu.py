@@ -432,6 +432,45 @@ def test_full_size_workloads(iq, O, S, cfg, fmt, gran, flags):
 FLAT = [f for f in ALL if f[1] != "row"]
 
 
+def saturating_alpha(fmt):
+    """A BF16 absmax alpha whose per-tensor scale s = RN(alpha / Q) puts
+    RN(alpha / s) above Q, so the elements equal to alpha saturate."""
+    Q = {"int8": 127.0, "e4m3": 448.0, "e5m2": 57344.0}[fmt]
+    for bits in range(0x4000, 0x4800):                  # BF16 values in [2, 2^17)
+        a = np.float32(np.array([bits << 16], np.uint32).view(np.float32)[0])
+        s = np.float32(a / np.float32(Q))
+        if np.float32(a / s) > np.float32(Q):
+            return a
+    raise AssertionError("no saturating absmax found")
+
+
+@pytest.mark.parametrize("fmt", ["int8", "e4m3", "e5m2"])
+def test_tensor_rows_special_and_saturating(iq, O, S, fmt):
+    """Per-tensor INT8 / FP8 of BF16 tensors of 16384 elements, which the
+    library quantizes as rows of 16384 under the tensor's scale: the special
+    values (NaN and +-Inf send the whole tensor to the general path), the
+    rows without the non-finite and huge ones (zeros, subnormals and tiny
+    values on the fast path), and a tensor whose absmax saturates under its
+    own scale (two elements at +-alpha), each against the oracle."""
+    x = bf16_special_matrix(S, rows=32, cols=512)
+    assert x.size % 16384 == 0
+    # without the non-finite and the huge rows: the fast path, with exact zeros, -0, subnormals and tiny values
+    finite = np.concatenate([np.delete(x, [4, 5, 6, 7, 8, 9], axis=0), S.fill(6, 512, 1, sigma=1.0, seed=9)], axis=0)
+    alpha = saturating_alpha(fmt)
+    sat = S.fill(2, 16384, 1, sigma=float(alpha) / 8, seed=10)
+    abits = int(np.array([alpha], np.float32).view(np.uint32)[0] >> 16)
+    mag = sat & 0x7FFF
+    sat[mag > abits] = (sat[mag > abits] & 0x8000) | abits   # clip to |x| <= alpha
+    sat[0, 7] = abits
+    sat[1, 9000] = abits | 0x8000
+    for k, xc in enumerate((x, finite, sat)):
+        g = run_gpu(iq, np.ascontiguousarray(xc), fmt, "tensor", xhat=None)
+        r = oracle_ref(O, np.ascontiguousarray(xc), fmt, "tensor")
+        compare(g, r, fmt, f"{fmt}/tensor rows case {k}", O)
+        if k == 2:
+            assert r["stats"]["n_saturated"] >= 2
+
+
 @pytest.mark.parametrize("fmt,gran", FLAT)
 def test_many_tiles_ragged(iq, O, S, fmt, gran):
     """The flat kernels with many tiles per workgroup and a ragged last
