@@ -132,6 +132,83 @@ def test_parity_shapes(iq, O, S, fmt, gran, dtype, stats):
                                f"xhat={xhat}", O)
 
 
+def sweep_shapes(O, fmt, gran, seed, n=20):
+    """n legal (rows, cols, ld, stats, xhat) drawn from a seeded generator:
+    row lengths log-uniform from one chunk (or block) to 65536 columns, up to
+    about 2 M elements, padded rows (ld > cols) about a third of the time,
+    statistics and x^ on or off; per-tensor adds contiguous shapes whose
+    element count is a multiple of 16384 (the per-tensor kernel over rows of
+    16384), without x^, which that kernel requires."""
+    rng = np.random.default_rng(seed)
+    step = 256 if fmt == "int4zp" else max(8, O.block_size(fmt, gran) or 8)
+    out = []
+    for _ in range(n):
+        cols = max(step, int(np.exp(rng.uniform(np.log(step), np.log(65536)))) // step * step)
+        rows = int(rng.integers(1, max(2, min(400, 2_000_000 // cols)) + 1))
+        ld = cols + 8 * int(rng.integers(1, 9)) if rng.random() < 0.35 else None
+        out.append((rows, cols, ld, bool(rng.random() < 0.7), [None, "f32", "bf16"][int(rng.integers(0, 3))]))
+    if gran == "tensor":
+        for rows, cols in ((2, 8192), (3, 16384), (1, 65536), (int(rng.integers(2, 40)) * 4, 4096)):
+            out.append((rows, cols, None, bool(rng.random() < 0.7), None))
+    return out
+
+
+@pytest.mark.parametrize("dtype", [1, 0], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fmt,gran", ALL)
+def test_parity_random_shapes(iq, O, S, fmt, gran, dtype):
+    """A seeded sweep across the kernel selection: every drawn shape, with
+    its statistics and x^ choice, against the oracle bit for bit; the
+    standalone dequantize of every third contiguous shape as well."""
+    seed = 7000 + 10 * ALL.index((fmt, gran)) + dtype
+    for i, (rows, cols, ld, stats, xhat) in enumerate(sweep_shapes(O, fmt, gran, seed)):
+        x = make_input(S, dtype, rows, cols, ld, seed=seed * 100 + i)
+        what = f"{fmt}/{gran}/{'bf16' if dtype else 'f32'} {rows}x{cols} ld={ld} (seed {seed}, case {i})"
+        r = oracle_ref(O, x, fmt, gran, cols=cols if ld else None, want_xhat=xhat is not None)
+        g = run_gpu(iq, x, fmt, gran, cols=cols if ld else None, xhat=xhat, stats=stats)
+        compare(g, r, fmt, f"{what} stats={stats} xhat={xhat}", O, S, xhat=xhat or "f32")
+        if ld is None and i % 3 == 0:
+            check_dequantize(iq, O, S, x, fmt, gran, what)
+
+
+def gemm_shapes(seed, k_step, n=12, max_macs=60e6):
+    """n seeded (n0, K, n1): n0 up to 384 weight rows, K a multiple of k_step
+    up to 4096, n1 log-uniform from 1 to 1200 tokens (the few-token, tiled,
+    k-split and ragged-tile paths); n0 is drawn below max_macs / (K n1), to
+    bound the oracle's time."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        K = k_step * int(rng.integers(1, 4096 // k_step + 1))
+        n1 = int(np.exp(rng.uniform(0.0, np.log(1200.0))))
+        top = min(384, int(max_macs // (K * n1)))
+        if top >= 1:
+            out.append((int(rng.integers(1, top + 1)), K, n1))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["zp", "mx", "mxw"])
+def test_gemm_random_shapes(iq, O, S, kind):
+    """The three consumers over seeded shapes, each against the oracle's
+    exact sum within the FP32 bound."""
+    seed = {"zp": 8100, "mx": 8200, "mxw": 8300}[kind]
+    shapes = gemm_shapes(seed, 256 if kind == "zp" else 128, max_macs=20e6 if kind == "mx" else 60e6)
+    for i, (n0, K, n1) in enumerate(shapes):
+        what = f"{kind} {n0}x{K}x{n1} (seed {seed}, case {i})"
+        if kind == "zp":
+            zp_gemm_case(iq, O, S, n0, K, n1, seed=seed + i)
+            continue
+        if kind == "mxw":
+            z, zr, zabs = mxw_case(iq, O, S, n0, K, n1, seed=seed + i)
+        else:
+            rw = mx_operand(O, S, n0, K, seed=seed + i, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+            ra = mx_operand(O, S, n1, K, seed=seed + 50 + i, sigma=1.0, outlier_axis=S.AXIS_COLS)
+            z = iq.mx_gemm(mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, n1, K)).cpu().numpy().astype(np.float64)
+            zr, zabs = O.mx_gemm(rw["codes"], rw["scales"], ra["codes"], ra["scales"])
+        bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+        err = np.abs(z - zr)
+        assert np.all(err <= bound), f"{what}: max err/bound {np.max(err / bound):.3g}"
+
+
 @pytest.mark.parametrize("fmt,gran", ALL)
 def test_parity_bf16_xhat(iq, O, S, fmt, gran):
     x = make_input(S, 1, 64, 4096, None, seed=7)
