@@ -541,7 +541,10 @@ def mx_gemm_breakdown(args):
         mx[f"n1={n1}"] = gemm_entry(us, b, fl, MFMA_FP4_PEAK_TFS, "k_mx_gemv" if n1 <= 64 else "k_mx_gemm")
         us = summarize(time_graph(bodyw, args.reps), n, 1)["mean_us"]
         b = G.n0 * (G.K // 2 + G.K // 32) + n1 * G.K * 2 + G.n0 * n1 * 4
-        mxw[f"n1={n1}"] = gemm_entry(us, b, fl, MFMA_BF16_PEAK_TFS, "k_mxw_gemv" if n1 <= 64 else "k_mxw_gemm")
+        # 256 x 256 tiles once the c3 weights' 112 rows of 128 x 256 tiles need
+        # more than one round of the 256 CUs' resident workgroups (n1 > 512)
+        kname = "k_mxw_gemv" if n1 <= 64 else "k_mxw_gemm_wide" if n1 > 512 else "k_mxw_gemm"
+        mxw[f"n1={n1}"] = gemm_entry(us, b, fl, MFMA_BF16_PEAK_TFS, kname)
         del x, qa, outs
     del G
     torch.cuda.empty_cache()

@@ -3362,6 +3362,108 @@ __global__ __launch_bounds__(128 * WN) void k_mxw_gemm(MxwGemmArgs a) {
         }
 }
 
+// Large grids: 256 x 256 tiles, 8 waves of 64 weight rows x 128 tokens (two
+// waves per SIMD), double-buffered in k steps of 64.  A step reads 0.375 KB
+// of LDS fragments per MFMA against 0.5 for the 64 x 64 wave tiles above,
+// and with the LDS writes the tile's LDS time per step falls to about its
+// MFMA time.  Rows of a step are 128 bytes (8 slots of 16, slot s of row r at
+// s ^ (r & 7)); two tiles of 64 KB.  Step k + 1 is written to the other tile
+// while step k's MFMAs run, and step k + 2 loads into registers; one
+// LDS-only barrier per step.  Every thread also dequantizes one 32-code
+// block per step (weight row t / 2, block t % 2).  Measured on the c3
+// weights (14336 x 4096) against the 128 x 256 tiles: 141 -> 112 us at 1024
+// tokens, 279 -> 224 us at 2048, 967 -> 836 us at 8192; the 128 x 256 tile
+// double-buffered the same way gained 0-2.5%.
+__global__ __launch_bounds__(512) void k_mxw_gemm_wide(MxwGemmArgs a) {
+    constexpr int kTN = 256, TM = 256, WT = 2, NB = 8;
+    __shared__ u4v sA[2][TM * 8], sB[2][kTN * 8];
+    const uint32_t b = blockIdx.x;
+    const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
+    if (idx >= a.tiles) return;
+    int jb, nb;
+    gemm_tile_of<16>(idx, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
+    const int j0 = jb * TM, t0 = nb * kTN;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WT, wn = wave % WT;
+    const int nks = a.K / 64;
+    const int ldc = a.K / 2, lds_ = a.K / 32;
+    f4v acc[4][NB];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    const int xr0 = t >> 3, xs = t & 7;
+    const uint16_t* gx[4];
+    int lx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = xr0 + 64 * i;
+        gx[i] = a.x + (int64_t)min(t0 + row, a.n1 - 1) * a.K + xs * 8;
+        lx[i] = row * 8 + (xs ^ (row & 7));
+    }
+    const int dr = t >> 1, dp = t & 1;
+    const int64_t dj = min(j0 + dr, a.n0 - 1);
+    const u4v* gc = reinterpret_cast<const u4v*>(a.codes + dj * ldc + dp * 16);
+    const uint8_t* gs = a.scales + dj * lds_ + dp;
+    u4v rx[4], rc = {};
+    uint32_t rs = 0;
+    auto load_step = [&](int ks) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rx[i] = *reinterpret_cast<const u4v*>(gx[i] + ks * 64);
+        rc = gc[ks * 2];
+        rs = gs[ks * 2];
+    };
+    auto store_step = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sB[buf][lx[i]] = rx[i];
+        const float sc = e8m0_scale(rs);
+        const uint32_t cw[4] = {rc.x, rc.y, rc.z, rc.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sA[buf][dr * 8 + ((dp * 4 + q) ^ (dr & 7))] = mx_bf16x8(cw[q], sc, rs == 255u);
+    };
+    load_step(0);
+    store_step(0);
+    if (nks > 1) load_step(1);
+    for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        lds_barrier();                        // step ks is in LDS; step ks - 1's tile is free
+        if (ks + 1 < nks) store_step(buf ^ 1);
+        if (ks + 2 < nks) load_step(ks + 2);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int slot = 4 * s + (lane >> 4);
+            bf8v af[4], bfr[NB];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int r = wm * 64 + mt * 16 + (lane & 15);
+                af[mt] = __builtin_bit_cast(bf8v, sA[buf][r * 8 + (slot ^ (r & 7))]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NB; ++nt) {
+                const int r = wn * (kTN / WT) + nt * 16 + (lane & 15);
+                bfr[nt] = __builtin_bit_cast(bf8v, sB[buf][r * 8 + (slot ^ (r & 7))]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NB; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
+#pragma unroll
+            for (int nt = 0; nt < NB; ++nt) {
+                const int tok = t0 + wn * (kTN / WT) + nt * 16 + (lane & 15);
+                if (j < a.n0 && tok < a.n1) a.z[(int64_t)j * a.n1 + tok] = acc[mt][nt][i];
+            }
+        }
+}
+
 // Few tokens (n1 <= 64): the asymmetric INT4 consumer's register-only kernel
 // with this dequantization.  Lane l holds weight row 16 f + l % 16 and, for
 // MFMA step q of 128-deep step g, k = 128 g + 32 (l / 16) + 8 q .. + 8: one
@@ -3931,12 +4033,22 @@ hipError_t launch_mxw_gemm(const MxwGemmLaunch& g, hipStream_t s) {
     a.tiles_n = (int32_t)((g.n1 + 64 * wn - 1) / (64 * wn));
     // (a grid of 256-token tiles small enough to want a k split always has
     // 128 x 128 tiles few enough for this form, so no split is needed)
+    // 256 x 256 tiles where the 128 x 256 tiles would take more than one
+    // round of resident workgroups (c3 weights: from 768 tokens; at 384-512
+    // tokens the wide tiles measured 105 against 71 us)
+    const bool wide = wn == 4 && (int64_t)a.tiles_j * a.tiles_n > resident_slots(
+                                     reinterpret_cast<const void*>(k_mxw_gemm<4, 128>), 512);
+    if (wide) {
+        a.tiles_j = (int32_t)((g.n0 + 255) / 256);
+        a.tiles_n = (int32_t)((g.n1 + 255) / 256);
+    }
     const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
     if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
     a.tiles = (uint32_t)tiles;
     a.per_xcd = (int32_t)((tiles + 7) / 8);
     const unsigned grid = (unsigned)(8 * (int64_t)a.per_xcd);
-    if (wn == 4) k_mxw_gemm<4, 128><<<grid, 256 * 2, 0, s>>>(a);
+    if (wide) k_mxw_gemm_wide<<<grid, 512, 0, s>>>(a);
+    else if (wn == 4) k_mxw_gemm<4, 128><<<grid, 256 * 2, 0, s>>>(a);
     else if (tm == 64) k_mxw_gemm<2, 64><<<grid, 256, 0, s>>>(a);
     else k_mxw_gemm<2, 128><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();

@@ -1269,7 +1269,9 @@ def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
 
 
 # n1 <= 64: the few-token kernel (1, 2 or 4 token tiles); 65 .. 255: 128-token
-# tiles; from 256: 256-token tiles.  Odd step counts (K / 128) included.  The
+# tiles; from 256: 256-token tiles (256 x 256 where the 128 x 256 tiles exceed
+# one round of resident workgroups, which no case here does; see the sampled
+# tests).  Odd step counts (K / 128) included.  The
 # tiled cases' grids are small, so k is split in halves (one step each for
 # K = 256, 1 and 2 steps for K = 384), except for K = 128 (one step).
 @pytest.mark.parametrize("n0,K,n1", [(128, 256, 128), (200, 512, 75), (257, 384, 129), (40, 512, 300),
@@ -1283,6 +1285,43 @@ def test_mxw_gemm_parity(iq, O, S, n0, K, n1):
     err = np.abs(z - zr)
     assert np.all(err <= bound), f"{n0}x{K}x{n1}: max err/bound {np.max(err / bound):.3g}"
     assert np.abs(zr).max() > 0 and np.max(err / bound) < 0.05
+
+
+def test_mxw_gemm_wide_tiles_sampled(iq, O, S):
+    """More 128 x 256 tiles than one round of resident workgroups (33 x 9
+    here) take 256 x 256 tiles: a ragged 4100 x 384 x 2100 product, the last
+    weight row with a NaN block scale, on sampled rows (both ends of the
+    ragged last row tile among them) against the oracle; a second call and
+    two replays of a captured call return the same bits."""
+    import torch
+    n0, K, n1 = 4100, 384, 2100
+    rw = mx_operand(O, S, n0, K, seed=77, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    rw["scales"][n0 - 1, 2] = 255
+    rng = np.random.default_rng(78)
+    x = S.f32_to_bf16_bits(rng.standard_normal((n1, K)).astype(np.float32))
+    qw, xd = mx_gpu(iq, rw, n0, K), to_device(x)
+    z = iq.mxw_gemm(qw, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(iq.mxw_gemm(qw, xd).view(torch.int32), z.view(torch.int32))
+    out = torch.empty_like(z)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iq.mxw_gemm(qw, xd, out=out)
+    for rep in range(2):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), z.view(torch.int32)), rep
+    rows = np.unique(np.concatenate([np.arange(0, n0, 97), [1, 255, 256, 3839, 3840, 4095, 4096, n0 - 2, n0 - 1]]))
+    zs = z[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    zr, zabs = O.mxw_gemm(np.ascontiguousarray(rw["codes"][rows]), np.ascontiguousarray(rw["scales"][rows]), x)
+    assert np.isnan(zr[-1]).all() and np.array_equal(np.isnan(zs), np.isnan(zr))
+    fin = np.isfinite(zr)
+    bound = (K + 2) * 2.0 ** -24 * zabs[fin] + 1e-30
+    err = np.abs(zs[fin] - zr[fin])
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    assert np.max(err / bound) < 0.05
 
 
 @pytest.mark.parametrize("n1", [24, 300])
