@@ -538,7 +538,9 @@ def mx_gemm_breakdown(args):
         us = summarize(time_graph(body, args.reps), n, 1)["mean_us"]
         b = (G.n0 + n1) * (G.K // 2 + G.K // 32) + G.n0 * n1 * 4
         fl = 2.0 * G.n0 * G.K * n1
-        mx[f"n1={n1}"] = gemm_entry(us, b, fl, MFMA_FP4_PEAK_TFS, "k_mx_gemv" if n1 <= 64 else "k_mx_gemm")
+        # LDS-DMA 256 x 256 tiles from 1024 tokens (the c3 weights give 224 or more)
+        kname = "k_mx_gemv" if n1 <= 64 else "k_mx_gemm_dma" if n1 >= 1024 else "k_mx_gemm"
+        mx[f"n1={n1}"] = gemm_entry(us, b, fl, MFMA_FP4_PEAK_TFS, kname)
         us = summarize(time_graph(bodyw, args.reps), n, 1)["mean_us"]
         b = G.n0 * (G.K // 2 + G.K // 32) + n1 * G.K * 2 + G.n0 * n1 * 4
         # 256 x 256 tiles once the c3 weights' 112 rows of 128 x 256 tiles need

@@ -2942,8 +2942,9 @@ __global__ __launch_bounds__(64 * NW, 2) void k_zp_gemm(ZpGemmArgs a) {
 // 32-bit word of 4 E8M0 bytes per row) are staged through registers into a
 // double-buffered LDS tile: step k + 2 loads into registers while step k
 // computes, and is written to LDS during step k + 1 after that step's
-// operands have been read.  (Direct global-to-LDS copies measured about 3x
-// slower here.)  One LDS-only barrier per step: it must not wait for the
+// operands have been read.  (Direct global-to-LDS copies of these half-line
+// rows measured about 3x slower; k_mx_gemm_dma below copies whole lines.)
+// One LDS-only barrier per step: it must not wait for the
 // register loads in flight.  Code rows are 4 slots of 16 bytes, slot s of
 // row r at s ^ ((r >> 1) & 3), so the 8 lanes of each read phase hit 8
 // distinct 16-byte bank groups.  Rows past n0 and tokens past n1 read a clamped valid
@@ -3079,6 +3080,118 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
 #pragma unroll
             for (int nt = 0; nt < NB; ++nt) {
                 const int tok = t0 + wn * (TN / WT) + nt * 16 + (lane & 15);
+                if (j < a.n0 && tok < a.n1) __builtin_nontemporal_store(acc[mt][nt][i], a.z + (int64_t)j * a.n1 + tok);
+            }
+        }
+}
+
+// Large products with the operand copies done by LDS DMA
+// (global_load_lds): 256 x 256 tiles of 8 waves, 64 weight rows x 128
+// tokens each (two waves per SIMD).  A stage is a pair of k steps, 128 code
+// bytes per row: each 8 lanes of a DMA instruction fetch one row's whole
+// 128-byte line, where the register-staged kernel fetched half lines (64
+// bytes per row and step), which cost four L2 requests per 128 bytes against
+// one.  No registers hold the copies.  The LDS row is 8 slots of 16 bytes,
+// logical slot ls (step ls / 4, k block ls % 4) at ls ^ (r & 7); a lane's
+// DMA word goes to a fixed LDS slot, so each lane fetches the logical slot
+// that belongs there.  Scale words: 2 per row and pair (8 E8M0 bytes), read
+// back as single bytes.  Two LDS stages (68 KB each): the copy of pair p + 1
+// is issued after the barrier that opens pair p and lands during its MFMAs.
+// With an odd step count the last pair's second step repeats the last step
+// (in-bounds) and is not computed.
+__global__ __launch_bounds__(512) void k_mx_gemm_dma(MxGemmArgs a) {
+    constexpr int TM = 256, TN = 256, WT = 2, NB = 8;
+    __shared__ u4v sW[2][TM * 8], sA[2][TN * 8];
+    __shared__ uint32_t sWs[2][TM * 2], sAs[2][TN * 2];
+    const uint32_t b = blockIdx.x;
+    const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
+    if (idx >= a.tiles) return;
+    int jb, nb;
+    gemm_tile_of<8>(idx, (uint32_t)a.tiles_j, (uint32_t)a.tiles_n, jb, nb);
+    const int j0 = jb * TM, t0 = nb * TN;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WT, wn = wave % WT;
+    const int nks = a.K / 128, np = (nks + 1) / 2;
+    const int64_t cstride = a.K / 2, sstride = a.K / 32;
+    // DMA lanes: instruction i of this wave covers rows 8 (4 wave + i) ..
+    // + 7 of each operand; lane l takes row + (l >> 3), LDS slot l & 7,
+    // which holds logical slot ls = (l & 7) ^ ((l >> 3) & 7)
+    const int ls = (lane & 7) ^ ((lane >> 3) & 7), lhalf = ls >> 2, lkb = (ls & 3) * 16;
+    const uint8_t* gw[4];
+    const uint8_t* gx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * wave + i) + (lane >> 3);
+        gw[i] = a.codes_w + (int64_t)min(j0 + row, a.n0 - 1) * cstride + lkb;
+        gx[i] = a.codes_a + (int64_t)min(t0 + row, a.n1 - 1) * cstride + lkb;
+    }
+    // scale lanes: row 32 wave + (l >> 1), word l & 1 of the pair
+    const int srow = 32 * wave + (lane >> 1), sword = lane & 1;
+    const uint8_t* gsw = a.scales_w + (int64_t)min(j0 + srow, a.n0 - 1) * sstride;
+    const uint8_t* gsx = a.scales_a + (int64_t)min(t0 + srow, a.n1 - 1) * sstride;
+    auto issue = [&](int p, int buf) {
+        const int64_t off = (int64_t)min(2 * p + lhalf, nks - 1) * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(gw[i] + off, (lds_void*)&sW[buf][(4 * wave + i) * 64], 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(gx[i] + off, (lds_void*)&sA[buf][(4 * wave + i) * 64], 16, 0, 0);
+        const int64_t soff = (int64_t)min(2 * p + sword, nks - 1) * 4;
+        __builtin_amdgcn_global_load_lds(gsw + soff, (lds_void*)&sWs[buf][wave * 64], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(gsx + soff, (lds_void*)&sAs[buf][wave * 64], 4, 0, 0);
+    };
+    const int kb = lane >> 4;
+    f4v acc[4][NB];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
+    issue(0, 0);
+    for (int p = 0; p < np; ++p) {
+        const int buf = p & 1;
+        wait_staged();                        // this wave's copies of pair p have landed
+        lds_barrier();                        // every wave's have; pair p - 1's tile is free
+        if (p + 1 < np) issue(p + 1, buf ^ 1);
+        const uint8_t* bw = reinterpret_cast<const uint8_t*>(sWs[buf]);
+        const uint8_t* ba = reinterpret_cast<const uint8_t*>(sAs[buf]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if (s == 1 && 2 * p + 1 >= nks) break;   // uniform: odd step count
+            const int lsl = 4 * s + kb;
+            v8i af[4], bf[NB];
+            int sa[4], sb[NB];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = wm * 64 + m * 16 + (lane & 15);
+                const u4v c = sW[buf][r * 8 + (lsl ^ (r & 7))];
+                af[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+                sa[m] = bw[r * 8 + lsl];
+            }
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                const int r = wn * 128 + m * 16 + (lane & 15);
+                const u4v c = sA[buf][r * 8 + (lsl ^ (r & 7))];
+                bf[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+                sb[m] = ba[r * 8 + lsl];
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NB; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], bf[nt], acc[mt][nt], 4, 4, 0,
+                                                                                   sa[mt], 0, sb[nt]);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + wm * 64 + mt * 16 + 4 * (lane >> 4) + i;
+#pragma unroll
+            for (int nt = 0; nt < NB; ++nt) {
+                const int tok = t0 + wn * 128 + nt * 16 + (lane & 15);
                 if (j < a.n0 && tok < a.n1) __builtin_nontemporal_store(acc[mt][nt][i], a.z + (int64_t)j * a.n1 + tok);
             }
         }
@@ -3984,6 +4097,20 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
         if (nt == 1) k_mx_gemv<1><<<grid, kThreads, 0, s>>>(a);
         else if (nt == 2) k_mx_gemv<2><<<grid, kThreads, 0, s>>>(a);
         else k_mx_gemv<4><<<grid, kThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    // 256 x 256 tiles with LDS DMA copies from 1024 tokens, where they fill at
+    // least half of the CUs (one workgroup per CU: 136 KB of LDS); on the c3
+    // weights 1024 / 2048 tokens 56.0 -> 52.0 / 106.7 -> 101.5 us, unchanged
+    // from 4096 (200 / 390 us)
+    if (g.n1 >= 1024 && ((g.n0 + 255) / 256) * ((g.n1 + 255) / 256) >= 128) {
+        a.tiles_j = (int32_t)((g.n0 + 255) / 256);
+        a.tiles_n = (int32_t)((g.n1 + 255) / 256);
+        const int64_t tiles = (int64_t)a.tiles_j * a.tiles_n;
+        if (tiles > kMaxGemmTiles) return hipErrorInvalidConfiguration;   // beyond one launch's grid
+        a.tiles = (uint32_t)tiles;
+        a.per_xcd = (int32_t)((tiles + 7) / 8);
+        k_mx_gemm_dma<<<(unsigned)(8 * (int64_t)a.per_xcd), 512, 0, s>>>(a);
         return hipGetLastError();
     }
     const int tn = g.n1 >= 1024 ? 256 : 128;

@@ -1256,6 +1256,33 @@ def test_mx_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
     assert np.max(err / bound) < 0.05
 
 
+def test_mx_gemm_dma_tiles_sampled(iq, O, S):
+    """From 1024 tokens, grids of at least 128 tiles of 256 x 256 copy their
+    operands by LDS DMA in pairs of k steps: a ragged 2100 x 384 x 3600
+    product (9 x 15 tiles; three steps, so the last pair has one), the last
+    token with a NaN block scale, on sampled rows against the oracle; a
+    second call returns the same bits."""
+    import torch
+    n0, K, n1 = 2100, 384, 3600
+    rw = mx_operand(O, S, n0, K, seed=91, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+    ra = mx_operand(O, S, n1, K, seed=92, sigma=1.0, outlier_axis=S.AXIS_COLS)
+    ra["scales"][n1 - 1, 1] = 255
+    qw, qa = mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, n1, K)
+    z = iq.mx_gemm(qw, qa)
+    torch.cuda.synchronize()
+    assert torch.equal(iq.mx_gemm(qw, qa).view(torch.int32), z.view(torch.int32))
+    rows = np.unique(np.concatenate([np.arange(0, n0, 53), [1, 255, 256, 2047, 2048, n0 - 2, n0 - 1]]))
+    zs = z[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    zr, zabs = O.mx_gemm(np.ascontiguousarray(rw["codes"][rows]), np.ascontiguousarray(rw["scales"][rows]),
+                         ra["codes"], ra["scales"])
+    assert np.isnan(zr[:, -1]).all() and np.array_equal(np.isnan(zs), np.isnan(zr))
+    fin = np.isfinite(zr)
+    bound = (K + 2) * 2.0 ** -24 * zabs[fin] + 1e-30
+    err = np.abs(zs[fin] - zr[fin])
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+    assert np.max(err / bound) < 0.05
+
+
 # ---- MXFP4 weights against BF16 activations (W4A16) ---------------------------------
 def mxw_case(iq, O, S, n0, K, n1, seed, nan_row=None):
     rw = mx_operand(O, S, n0, K, seed=seed, sigma=0.02, outlier_axis=S.AXIS_ROWS)
