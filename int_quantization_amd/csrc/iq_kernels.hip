@@ -3098,11 +3098,19 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxGemmArgs a) {
 // back as single bytes.  Two LDS stages (68 KB each): the copy of pair p + 1
 // is issued after the barrier that opens pair p and lands during its MFMAs.
 // With an odd step count the last pair's second step repeats the last step
-// (in-bounds) and is not computed.
+// (in-bounds) and is not computed.  The two stages are separate LDS objects
+// and the pair loop is unrolled by two, so that every read and every copy
+// names its stage statically: with one array indexed by the stage the
+// compiler waited for the next pair's copies before each LDS read
+// (vmcnt(0)), which serialized copy and compute (c3 weights at 2048 / 8192
+// tokens: 101.5 / 387 us that way, 94.3 / 348 us this way).
+struct MxPairBuf {
+    u4v w[256 * 8], a[256 * 8];
+    uint32_t sw[256 * 2], sa[256 * 2];
+};
 __global__ __launch_bounds__(512) void k_mx_gemm_dma(MxGemmArgs a) {
     constexpr int TM = 256, TN = 256, WT = 2, NB = 8;
-    __shared__ u4v sW[2][TM * 8], sA[2][TN * 8];
-    __shared__ uint32_t sWs[2][TM * 2], sAs[2][TN * 2];
+    __shared__ MxPairBuf P0, P1;
     const uint32_t b = blockIdx.x;
     const uint32_t idx = (b & 7u) * (uint32_t)a.per_xcd + (b >> 3);
     if (idx >= a.tiles) return;
@@ -3130,17 +3138,17 @@ __global__ __launch_bounds__(512) void k_mx_gemm_dma(MxGemmArgs a) {
     const int srow = 32 * wave + (lane >> 1), sword = lane & 1;
     const uint8_t* gsw = a.scales_w + (int64_t)min(j0 + srow, a.n0 - 1) * sstride;
     const uint8_t* gsx = a.scales_a + (int64_t)min(t0 + srow, a.n1 - 1) * sstride;
-    auto issue = [&](int p, int buf) {
+    auto issue = [&](int p, MxPairBuf& d) {
         const int64_t off = (int64_t)min(2 * p + lhalf, nks - 1) * 64;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(gw[i] + off, (lds_void*)&sW[buf][(4 * wave + i) * 64], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gw[i] + off, (lds_void*)&d.w[(4 * wave + i) * 64], 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(gx[i] + off, (lds_void*)&sA[buf][(4 * wave + i) * 64], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gx[i] + off, (lds_void*)&d.a[(4 * wave + i) * 64], 16, 0, 0);
         const int64_t soff = (int64_t)min(2 * p + sword, nks - 1) * 4;
-        __builtin_amdgcn_global_load_lds(gsw + soff, (lds_void*)&sWs[buf][wave * 64], 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(gsx + soff, (lds_void*)&sAs[buf][wave * 64], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(gsw + soff, (lds_void*)&d.sw[wave * 64], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(gsx + soff, (lds_void*)&d.sa[wave * 64], 4, 0, 0);
     };
     const int kb = lane >> 4;
     f4v acc[4][NB];
@@ -3148,14 +3156,12 @@ __global__ __launch_bounds__(512) void k_mx_gemm_dma(MxGemmArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NB; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-    issue(0, 0);
-    for (int p = 0; p < np; ++p) {
-        const int buf = p & 1;
+    auto pair = [&](int p, const MxPairBuf& cur, MxPairBuf& nxt) {
         wait_staged();                        // this wave's copies of pair p have landed
         lds_barrier();                        // every wave's have; pair p - 1's tile is free
-        if (p + 1 < np) issue(p + 1, buf ^ 1);
-        const uint8_t* bw = reinterpret_cast<const uint8_t*>(sWs[buf]);
-        const uint8_t* ba = reinterpret_cast<const uint8_t*>(sAs[buf]);
+        if (p + 1 < np) issue(p + 1, nxt);
+        const uint8_t* bw = reinterpret_cast<const uint8_t*>(cur.sw);
+        const uint8_t* ba = reinterpret_cast<const uint8_t*>(cur.sa);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             if (s == 1 && 2 * p + 1 >= nks) break;   // uniform: odd step count
@@ -3165,14 +3171,14 @@ __global__ __launch_bounds__(512) void k_mx_gemm_dma(MxGemmArgs a) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = wm * 64 + m * 16 + (lane & 15);
-                const u4v c = sW[buf][r * 8 + (lsl ^ (r & 7))];
+                const u4v c = cur.w[r * 8 + (lsl ^ (r & 7))];
                 af[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
                 sa[m] = bw[r * 8 + lsl];
             }
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
                 const int r = wn * 128 + m * 16 + (lane & 15);
-                const u4v c = sA[buf][r * 8 + (lsl ^ (r & 7))];
+                const u4v c = cur.a[r * 8 + (lsl ^ (r & 7))];
                 bf[m] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
                 sb[m] = ba[r * 8 + lsl];
             }
@@ -3183,6 +3189,11 @@ __global__ __launch_bounds__(512) void k_mx_gemm_dma(MxGemmArgs a) {
                     acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mt], bf[nt], acc[mt][nt], 4, 4, 0,
                                                                                    sa[mt], 0, sb[nt]);
         }
+    };
+    issue(0, P0);
+    for (int p = 0; p < np; p += 2) {
+        pair(p, P0, P1);
+        if (p + 1 < np) pair(p + 1, P1, P0);
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -4101,8 +4112,8 @@ hipError_t launch_mx_gemm(const MxGemmLaunch& g, hipStream_t s) {
     }
     // 256 x 256 tiles with LDS DMA copies from 1024 tokens, where they fill at
     // least half of the CUs (one workgroup per CU: 136 KB of LDS); on the c3
-    // weights 1024 / 2048 tokens 56.0 -> 52.0 / 106.7 -> 101.5 us, unchanged
-    // from 4096 (200 / 390 us)
+    // weights against the 128 x 256 tiles: 1024 / 2048 / 4096 / 8192 tokens
+    // 56.0 / 106.7 / 200 / 390 -> 47.4 / 94.3 / 183 / 348 us
     if (g.n1 >= 1024 && ((g.n0 + 255) / 256) * ((g.n1 + 255) / 256) >= 128) {
         a.tiles_j = (int32_t)((g.n0 + 255) / 256);
         a.tiles_n = (int32_t)((g.n1 + 255) / 256);
