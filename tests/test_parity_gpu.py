@@ -1256,6 +1256,37 @@ def test_mx_gemm_full_size_sampled(iq, O, S, c3_mxfp4, n1):
     assert np.max(err / bound) < 0.05
 
 
+@pytest.mark.parametrize("kind", ["mx", "mxw"])
+def test_gemm_large_grid_random_shapes(iq, O, S, kind):
+    """Seeded ragged shapes large enough for the 256 x 256 kernels (LDS DMA
+    for the FP4 GEMM, the wide W4A16 tile): 4100 to 6000 weight rows and
+    2100 to 4096 tokens (at least 153 tiles of 256 x 256 and 297 of
+    128 x 256), K a multiple of 128 up to 768 (odd step counts included);
+    24 sampled weight rows per case, among them the last one, against the
+    oracle."""
+    import torch
+    rng = np.random.default_rng(8400 if kind == "mx" else 8500)
+    for case in range(4):
+        n0 = int(rng.integers(4100, 6000))
+        n1 = int(rng.integers(2100, 4097))
+        K = 128 * int(rng.integers(1, 7))
+        rw = mx_operand(O, S, n0, K, seed=8600 + case, sigma=0.02, outlier_axis=S.AXIS_ROWS)
+        if kind == "mx":
+            ra = mx_operand(O, S, n1, K, seed=8700 + case, sigma=1.0, outlier_axis=S.AXIS_COLS)
+            z = iq.mx_gemm(mx_gpu(iq, rw, n0, K), mx_gpu(iq, ra, n1, K))
+        else:
+            x = S.f32_to_bf16_bits(np.random.default_rng(8800 + case).standard_normal((n1, K)).astype(np.float32))
+            z = iq.mxw_gemm(mx_gpu(iq, rw, n0, K), to_device(x))
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([rng.choice(n0, 22, replace=False), [0, n0 - 1]]))
+        zs = z[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        wc, ws = np.ascontiguousarray(rw["codes"][rows]), np.ascontiguousarray(rw["scales"][rows])
+        zr, zabs = O.mx_gemm(wc, ws, ra["codes"], ra["scales"]) if kind == "mx" else O.mxw_gemm(wc, ws, x)
+        bound = (K + 2) * 2.0 ** -24 * zabs + 1e-30
+        err = np.abs(zs - zr)
+        assert np.all(err <= bound), f"{kind} {n0}x{K}x{n1} (case {case}): max err/bound {np.max(err / bound):.3g}"
+
+
 def test_mx_gemm_dma_tiles_sampled(iq, O, S):
     """From 1024 tokens, grids of at least 128 tiles of 256 x 256 copy their
     operands by LDS DMA in pairs of k steps: a ragged 2100 x 384 x 3600
